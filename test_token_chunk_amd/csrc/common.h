@@ -1,0 +1,85 @@
+// Shared device/host helpers of the HIP path (gfx950).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <cmath>
+
+// bf16 storage: raw 16-bit pattern, converted explicitly (round to nearest even).
+struct bf16 {
+  uint16_t x;
+};
+
+__host__ __device__ __forceinline__ float bf2f(bf16 v) {
+  uint32_t u = (uint32_t)v.x << 16;
+  float f;
+  __builtin_memcpy(&f, &u, 4);
+  return f;
+}
+
+__host__ __device__ __forceinline__ bf16 f2bf(float f) {
+  uint32_t u;
+  __builtin_memcpy(&u, &f, 4);
+  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return bf16{(uint16_t)((u >> 16) | 0x40)};  // NaN
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return bf16{(uint16_t)(u >> 16)};
+}
+
+template <typename T>
+__host__ __device__ __forceinline__ float to_f(const T& v);
+template <>
+__host__ __device__ __forceinline__ float to_f<float>(const float& v) {
+  return v;
+}
+template <>
+__host__ __device__ __forceinline__ float to_f<bf16>(const bf16& v) {
+  return bf2f(v);
+}
+
+template <typename T>
+__host__ __device__ __forceinline__ T from_f(float f);
+template <>
+__host__ __device__ __forceinline__ float from_f<float>(float f) {
+  return f;
+}
+template <>
+__host__ __device__ __forceinline__ bf16 from_f<bf16>(float f) {
+  return f2bf(f);
+}
+
+__device__ __forceinline__ float warp_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ __forceinline__ float warp_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// block-wide sum for blockDim.x a multiple of 64 (<= 1024); sh holds >= 16 floats
+__device__ __forceinline__ float block_sum(float v, float* sh) {
+  v = warp_sum(v);
+  int w = threadIdx.x >> 6, l = threadIdx.x & 63, nw = blockDim.x >> 6;
+  __syncthreads();
+  if (l == 0) sh[w] = v;
+  __syncthreads();
+  float t = 0.f;
+  for (int i = 0; i < nw; ++i) t += sh[i];
+  return t;
+}
+
+__device__ __forceinline__ float block_max(float v, float* sh) {
+  v = warp_max(v);
+  int w = threadIdx.x >> 6, l = threadIdx.x & 63, nw = blockDim.x >> 6;
+  __syncthreads();
+  if (l == 0) sh[w] = v;
+  __syncthreads();
+  float t = -INFINITY;
+  for (int i = 0; i < nw; ++i) t = fmaxf(t, sh[i]);
+  return t;
+}
+
+static inline unsigned cdiv(int64_t a, int64_t b) { return (unsigned)((a + b - 1) / b); }

@@ -1,0 +1,945 @@
+// Host engine of the TTT-E2E inner loop and the C ABI (include/ttt.h).
+//
+// Per chunk of b tokens (page "TTT-E2E 如何让大模型边用边学", §4.4): forward
+// with the sliding window over the key/value rings, mean next-token
+// cross-entropy, backward into the MLPs of the last n_fast blocks only (keys
+// and values of earlier chunks are constants, same page §8 Q1), one SGD step
+// on fp32 master weights, then the next chunk.
+//
+// Exact reordering used here: blocks 0 .. l0-1 and the attention half of
+// block l0 (l0 = L - n_fast) never see the fast weights, so their forward for
+// up to `lookahead` consecutive chunks runs as one large batch before the
+// per-chunk loop over the upper blocks.  Every row of every kernel computes
+// the same values as it would chunk by chunk.
+#include <string.h>
+
+#include <algorithm>
+#include <cmath>
+#include <string>
+#include <vector>
+
+#include "kernels.h"
+#include "ttt.h"
+
+hipError_t refresh_shadows(const float* master, int rows, int cols, int batch, int64_t sm, void* sh, int64_t ssh,
+                           void* shT, int64_t sshT, int is_bf16, hipStream_t s);
+
+namespace {
+
+ttt_alloc_fn g_alloc = nullptr;
+ttt_free_fn g_free = nullptr;
+void* g_user = nullptr;
+thread_local std::string g_create_err;
+
+enum Mode { FULL = 0, ATTN_ONLY = 1, MLP_ONLY = 2 };
+
+struct LayerW {
+  float* attn_norm = nullptr;
+  float* mlp_norm = nullptr;
+  void* wqkv = nullptr;   // [3d][d]
+  void* wo = nullptr;     // [d][d]
+  void* wgu = nullptr;    // [2f][d]  (frozen blocks)
+  void* wd = nullptr;     // [d][f]   (frozen blocks)
+  void* wqkvT = nullptr;  // [d][3d]  (blocks above l0)
+  void* woT = nullptr;    // [d][d]   (blocks above l0)
+  void* kr = nullptr;     // ring K [B][H][R][hd]
+  void* vr = nullptr;     // ring V [B][H][R][hd]
+  void* vtr = nullptr;    // ring V^T [B][H][hd][R]
+};
+
+struct FastW {
+  float* master = nullptr;  // [B][ W_gate f*d | W_up f*d | W_down d*f ] fp32
+  void* wgu = nullptr;      // [B][2f][d]  shadow (T)
+  void* wguT = nullptr;     // [B][d][2f]
+  void* wd = nullptr;       // [B][d][f]
+  void* wdT = nullptr;      // [B][f][d]
+};
+
+struct TopActs {
+  float *h_in = nullptr, *rstd1 = nullptr, *h_mid = nullptr, *rstd2 = nullptr, *lse = nullptr;
+  void *q = nullptr, *qt = nullptr, *o = nullptr, *mT = nullptr, *zg = nullptr, *zu = nullptr, *actT = nullptr;
+};
+
+}  // namespace
+
+struct ttt_ctx {
+  ttt_config cfg;
+  int L, d, H, hd, f, V, k, b, Lq, l0, B, R, G;
+  bool bf16;
+  size_t es;  // element size of T
+  bool mfma = true;
+  hipStream_t stream = nullptr;
+  ttt_free_fn free_fn = nullptr;
+  void* free_user = nullptr;
+  std::vector<void*> allocs;
+  bool alloc_failed = false;
+
+  std::vector<LayerW> lw;
+  std::vector<FastW> fw;
+  std::vector<TopActs> acts;
+  void *embed = nullptr, *lm_head = nullptr, *lm_headT = nullptr;
+  float* final_norm = nullptr;
+  float *cos_t = nullptr, *sin_t = nullptr;
+  float* fast_init = nullptr;  // [Lq][3fd]
+
+  // work buffers
+  float *hb = nullptr, *qkvb = nullptr, *rstd_tmp = nullptr;
+  void *ub = nullptr, *qb = nullptr, *ob = nullptr, *actb = nullptr;
+  float *htop = nullptr, *rstdf = nullptr, *logits = nullptr, *loss_tok = nullptr;
+  void *hf = nullptr, *dlogits = nullptr;
+  int* nvalid = nullptr;
+  float *dh = nullptr, *tmpf = nullptr, *dq = nullptr, *dk = nullptr, *dv = nullptr, *dvec = nullptr;
+  void *dyN = nullptr, *dyT = nullptr, *dz = nullptr, *dzT = nullptr, *dhT = nullptr, *dO = nullptr, *dqkv = nullptr;
+  int* err_dev = nullptr;
+  int32_t* d_tok = nullptr;
+  int64_t d_tok_cap = 0;
+  float* d_loss = nullptr;
+  int64_t d_loss_cap = 0;
+
+  int64_t pos = 0;
+  bool poisoned = false;
+  std::string err;
+  float* pending_loss = nullptr;  // device losses of async work, checked by ttt_sync
+  int64_t pending_n = 0;
+
+  void* alloc(size_t bytes) {
+    if (bytes == 0) bytes = 256;
+    void* p = nullptr;
+    if (g_alloc) {
+      p = g_alloc(bytes, g_user);
+    } else if (hipMalloc(&p, bytes) != hipSuccess) {
+      p = nullptr;
+    }
+    if (!p) {
+      alloc_failed = true;
+      return nullptr;
+    }
+    allocs.push_back(p);
+    return p;
+  }
+  void release_all() {
+    for (void* p : allocs) {
+      if (free_fn)
+        free_fn(p, free_user);
+      else
+        (void)hipFree(p);
+    }
+    allocs.clear();
+  }
+};
+
+namespace {
+
+int fail(ttt_ctx* c, int code, const std::string& msg) {
+  c->err = msg;
+  if (code == TTT_EDEVICE || code == TTT_ENONFINITE || code == TTT_ENOMEM) c->poisoned = true;
+  return code;
+}
+
+#define CK(expr)                                                                                   \
+  do {                                                                                             \
+    hipError_t e_ = (expr);                                                                        \
+    if (e_ != hipSuccess) return fail(c, TTT_EDEVICE, std::string(#expr) + ": " + hipGetErrorString(e_)); \
+  } while (0)
+
+// ------------------------------------------------------------------ dispatch
+
+template <typename T>
+struct Ops;
+
+template <>
+struct Ops<float> {
+  static hipError_t gemm(ttt_ctx* c, const GemmArgs& g) { return gemm_simt_f32(g, c->stream); }
+  static hipError_t fwd(ttt_ctx* c, const AttnArgs& a) { return swa_fwd_simt<float>(a, c->stream); }
+  static hipError_t bwd(ttt_ctx* c, const AttnBwdArgs& a) { return swa_bwd_simt<float>(a, c->stream); }
+};
+
+template <>
+struct Ops<bf16> {
+  static hipError_t gemm(ttt_ctx* c, const GemmArgs& g) {
+    if (c->mfma) return gemm_mfma_bf16(g, c->stream);
+    return gemm_simt_bf16(g, c->stream);
+  }
+  static hipError_t fwd(ttt_ctx* c, const AttnArgs& a) {
+    if (c->mfma) return swa_fwd_mfma(a, c->stream);
+    return swa_fwd_simt<bf16>(a, c->stream);
+  }
+  static hipError_t bwd(ttt_ctx* c, const AttnBwdArgs& a) {
+    if (c->mfma) return swa_bwd_mfma(a, c->stream);
+    return swa_bwd_simt<bf16>(a, c->stream);
+  }
+};
+
+GemmArgs mk(const void* A, int64_t lda, const void* B, int64_t ldb, int M, int N, int K) {
+  GemmArgs g;
+  g.A = A;
+  g.lda = lda;
+  g.B = B;
+  g.ldb = ldb;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  return g;
+}
+
+template <typename T>
+T* tp(void* p, int64_t off = 0) {
+  return (T*)p + off;
+}
+
+// forward of block l over n tokens per row at positions [p0, p0+n); h is the
+// fp32 residual stream [B*n][d], updated in place.
+template <typename T>
+int layer_fwd(ttt_ctx* c, int l, float* h, int n, int64_t p0, int mode, TopActs* sv) {
+  const int B = c->B, d = c->d, f = c->f;
+  const int64_t M = (int64_t)B * n;
+  const LayerW& w = c->lw[l];
+  if (mode != MLP_ONLY) {
+    if (sv) CK(hipMemcpyAsync(sv->h_in, h, M * d * 4, hipMemcpyDeviceToDevice, c->stream));
+    CK(rmsnorm_fwd<T>(h, M, d, w.attn_norm, (float)c->cfg.rms_eps, tp<T>(c->ub), sv ? sv->rstd1 : c->rstd_tmp,
+                      (T*)nullptr, n, 0, c->stream));
+    GemmArgs g = mk(c->ub, d, w.wqkv, d, (int)M, 3 * d, d);
+    g.e.kind = EPI_F32;
+    g.e.c = c->qkvb;
+    g.e.ldc = 3 * d;
+    CK(Ops<T>::gemm(c, g));
+    RopeRing rr;
+    rr.cos_t = c->cos_t;
+    rr.sin_t = c->sin_t;
+    rr.pos0 = p0;
+    rr.n = n;
+    rr.H = c->H;
+    rr.hd = c->hd;
+    rr.R = c->R;
+    rr.q = sv ? sv->q : c->qb;
+    rr.qt = sv ? sv->qt : nullptr;
+    rr.kr = w.kr;
+    rr.vr = w.vr;
+    rr.vtr = w.vtr;
+    CK(rope_qkv_f32in(c->qkvb, B, rr, c->bf16 ? 1 : 0, c->stream));
+    AttnArgs a;
+    a.q = rr.q;
+    a.kr = w.kr;
+    a.vr = w.vr;
+    a.vtr = w.vtr;
+    a.o = sv ? sv->o : c->ob;
+    a.lse = sv ? sv->lse : nullptr;
+    a.B = B;
+    a.H = c->H;
+    a.hd = c->hd;
+    a.n = n;
+    a.R = c->R;
+    a.window = c->k;
+    a.pos0 = p0;
+    CK(Ops<T>::fwd(c, a));
+    GemmArgs go = mk(a.o, d, w.wo, d, (int)M, d, d);
+    go.e.kind = EPI_ADD_F32;
+    go.e.c = h;
+    go.e.ldc = d;
+    CK(Ops<T>::gemm(c, go));
+    if (mode == ATTN_ONLY) return TTT_OK;
+  }
+  if (sv) CK(hipMemcpyAsync(sv->h_mid, h, M * d * 4, hipMemcpyDeviceToDevice, c->stream));
+  CK(rmsnorm_fwd<T>(h, M, d, w.mlp_norm, (float)c->cfg.rms_eps, tp<T>(c->ub), sv ? sv->rstd2 : c->rstd_tmp,
+                    sv ? tp<T>(sv->mT) : (T*)nullptr, n, c->b, c->stream));
+  if (l >= c->l0) {
+    const FastW& fw = c->fw[l - c->l0];
+    GemmArgs g = mk(c->ub, d, fw.wgu, d, n, f, d);
+    g.batch = B;
+    g.sA = (int64_t)n * d;
+    g.sB = 2LL * f * d;
+    g.dual_off = f;
+    g.e.kind = EPI_SWIGLU;
+    g.e.c = c->actb;
+    g.e.ldc = f;
+    g.e.sc = (int64_t)n * f;
+    if (sv) {
+      g.e.zg = sv->zg;
+      g.e.zu = sv->zu;
+      g.e.ldz = f;
+      g.e.sz = (int64_t)n * f;
+      g.e.t = sv->actT;
+      g.e.ldt = c->b;
+      g.e.st = (int64_t)f * c->b;
+    }
+    CK(Ops<T>::gemm(c, g));
+    GemmArgs gd = mk(c->actb, f, fw.wd, f, n, d, f);
+    gd.batch = B;
+    gd.sA = (int64_t)n * f;
+    gd.sB = (int64_t)d * f;
+    gd.e.kind = EPI_ADD_F32;
+    gd.e.c = h;
+    gd.e.ldc = d;
+    gd.e.sc = (int64_t)n * d;
+    CK(Ops<T>::gemm(c, gd));
+  } else {
+    GemmArgs g = mk(c->ub, d, w.wgu, d, (int)M, f, d);
+    g.dual_off = f;
+    g.e.kind = EPI_SWIGLU;
+    g.e.c = c->actb;
+    g.e.ldc = f;
+    CK(Ops<T>::gemm(c, g));
+    GemmArgs gd = mk(c->actb, f, w.wd, f, (int)M, d, f);
+    gd.e.kind = EPI_ADD_F32;
+    gd.e.c = h;
+    gd.e.ldc = d;
+    CK(Ops<T>::gemm(c, gd));
+  }
+  return TTT_OK;
+}
+
+// fast-weight-independent forward of g tokens per row: blocks 0..l0-1 and the
+// attention half of block l0; leaves h' of block l0 in c->hb ([B][g][d]).
+template <typename T>
+int bottom_pass(ttt_ctx* c, const int32_t* tok, int64_t ld, int g, int64_t p0) {
+  CK(embed_gather_ld<T>(tok, ld, c->B, g, tp<T>(c->embed), c->d, c->V, c->hb, c->err_dev, c->stream));
+  for (int l = 0; l < c->l0; ++l) {
+    int rc = layer_fwd<T>(c, l, c->hb, g, p0, FULL, nullptr);
+    if (rc) return rc;
+  }
+  return layer_fwd<T>(c, c->l0, c->hb, g, p0, ATTN_ONLY, nullptr);
+}
+
+// upper blocks of one chunk: forward, loss, backward, SGD.  hsrc: h' of block
+// l0 for this chunk (row r at hsrc + r*hsrc_bs).
+template <typename T>
+int top_chunk(ttt_ctx* c, const int32_t* tgt, int64_t ld, const float* hsrc, int64_t hsrc_bs, int n, int64_t p0,
+              float* loss_dev) {
+  const int B = c->B, d = c->d, f = c->f, V = c->V, b = c->b;
+  const int64_t M = (int64_t)B * n;
+  CK(copy_rows(hsrc, hsrc_bs, c->htop, B, n, d, c->stream));
+  int rc = layer_fwd<T>(c, c->l0, c->htop, n, p0, MLP_ONLY, &c->acts[0]);
+  if (rc) return rc;
+  for (int j = 1; j < c->Lq; ++j) {
+    rc = layer_fwd<T>(c, c->l0 + j, c->htop, n, p0, FULL, &c->acts[j]);
+    if (rc) return rc;
+  }
+  CK(rmsnorm_fwd<T>(c->htop, M, d, c->final_norm, (float)c->cfg.rms_eps, tp<T>(c->hf), c->rstdf, (T*)nullptr, n, 0,
+                    c->stream));
+  GemmArgs gl = mk(c->hf, d, c->lm_head, d, (int)M, V, d);
+  gl.e.kind = EPI_F32;
+  gl.e.c = c->logits;
+  gl.e.ldc = V;
+  CK(Ops<T>::gemm(c, gl));
+  CK(count_valid_ld(tgt, ld, B, n, c->nvalid, c->stream));
+  CK(ce_rows_ld<T>(c->logits, M, V, tgt, ld, c->nvalid, n, c->loss_tok, tp<T>(c->dlogits), c->err_dev, c->stream));
+  CK(reduce_loss(c->loss_tok, c->nvalid, B, n, loss_dev, c->stream));
+
+  // backward
+  GemmArgs gx = mk(c->dlogits, V, c->lm_headT, V, (int)M, d, V);
+  gx.e.kind = EPI_F32;
+  gx.e.c = c->tmpf;
+  gx.e.ldc = d;
+  CK(Ops<T>::gemm(c, gx));
+  CK(rmsnorm_bwd<T>(c->htop, c->rstdf, M, d, c->final_norm, c->tmpf, nullptr, c->dh, (T*)nullptr, c->stream));
+  const float lr = c->cfg.lr;
+  const int64_t fsz = 3LL * f * d;
+  for (int j = c->Lq - 1; j >= 0; --j) {
+    const int l = c->l0 + j;
+    TopActs& a = c->acts[j];
+    FastW& w = c->fw[j];
+    CK(convert_rows<T>(c->dh, M, d, tp<T>(c->dyN), tp<T>(c->dyT), n, b, c->stream));
+    // d act = dy W_down  ->  dz_g, dz_u
+    GemmArgs g1 = mk(c->dyN, d, w.wdT, d, n, f, d);
+    g1.batch = B;
+    g1.sA = (int64_t)n * d;
+    g1.sB = (int64_t)f * d;
+    g1.e.kind = EPI_SWIGLU_BWD;
+    g1.e.zg = a.zg;
+    g1.e.zu = a.zu;
+    g1.e.ldz = f;
+    g1.e.sz = (int64_t)n * f;
+    g1.e.c = c->dz;
+    g1.e.ldc = 2 * f;
+    g1.e.sc = (int64_t)n * 2 * f;
+    g1.e.t = c->dzT;
+    g1.e.ldt = b;
+    g1.e.st = 2LL * f * b;
+    g1.e.f = f;
+    CK(Ops<T>::gemm(c, g1));
+    // dW_down = dy^T act, fused SGD step on W_down
+    GemmArgs g2 = mk(c->dyT, b, a.actT, b, d, f, n);
+    g2.batch = B;
+    g2.sA = (int64_t)d * b;
+    g2.sB = (int64_t)f * b;
+    g2.e.kind = EPI_SGD;
+    g2.e.master = w.master + 2LL * f * d;
+    g2.e.ldm = f;
+    g2.e.sm = fsz;
+    g2.e.sh = w.wd;
+    g2.e.ldsh = f;
+    g2.e.ssh = (int64_t)d * f;
+    g2.e.shT = w.wdT;
+    g2.e.ldshT = d;
+    g2.e.sshT = (int64_t)f * d;
+    g2.e.lr = lr;
+    CK(Ops<T>::gemm(c, g2));
+    if (j > 0) {  // dm = dz_g W_gate + dz_u W_up  (before W_gate/W_up change)
+      GemmArgs g3 = mk(c->dz, 2 * f, w.wguT, 2 * f, n, d, 2 * f);
+      g3.batch = B;
+      g3.sA = (int64_t)n * 2 * f;
+      g3.sB = 2LL * d * f;
+      g3.e.kind = EPI_F32;
+      g3.e.c = c->tmpf;
+      g3.e.ldc = d;
+      g3.e.sc = (int64_t)n * d;
+      CK(Ops<T>::gemm(c, g3));
+    }
+    // [dW_gate; dW_up] = dz^T m, fused SGD step
+    GemmArgs g4 = mk(c->dzT, b, a.mT, b, 2 * f, d, n);
+    g4.batch = B;
+    g4.sA = 2LL * f * b;
+    g4.sB = (int64_t)d * b;
+    g4.e.kind = EPI_SGD;
+    g4.e.master = w.master;
+    g4.e.ldm = d;
+    g4.e.sm = fsz;
+    g4.e.sh = w.wgu;
+    g4.e.ldsh = d;
+    g4.e.ssh = 2LL * f * d;
+    g4.e.shT = w.wguT;
+    g4.e.ldshT = 2 * f;
+    g4.e.sshT = 2LL * d * f;
+    g4.e.lr = lr;
+    CK(Ops<T>::gemm(c, g4));
+    if (j == 0) break;
+    const LayerW& lw = c->lw[l];
+    // through the MLP norm and the residual: dh <- d h_mid
+    CK(rmsnorm_bwd<T>(a.h_mid, a.rstd2, M, d, lw.mlp_norm, c->tmpf, c->dh, c->dh, tp<T>(c->dhT), c->stream));
+    // attention output projection
+    GemmArgs g5 = mk(c->dhT, d, lw.woT, d, (int)M, d, d);
+    g5.e.kind = EPI_T;
+    g5.e.c = c->dO;
+    g5.e.ldc = d;
+    CK(Ops<T>::gemm(c, g5));
+    AttnBwdArgs ab;
+    ab.q = a.q;
+    ab.qt = a.qt;
+    ab.kr = lw.kr;
+    ab.vr = lw.vr;
+    ab.vtr = lw.vtr;
+    ab.o = a.o;
+    ab.dout = c->dO;
+    ab.lse = a.lse;
+    ab.dvec = c->dvec;
+    ab.dq = c->dq;
+    ab.dk = c->dk;
+    ab.dv = c->dv;
+    ab.B = B;
+    ab.H = c->H;
+    ab.hd = c->hd;
+    ab.n = n;
+    ab.R = c->R;
+    ab.window = c->k;
+    ab.pos0 = p0;
+    CK(Ops<T>::bwd(c, ab));
+    CK(rope_bwd_pack<T>(c->dq, c->dk, c->dv, c->cos_t, c->sin_t, p0, B, n, c->H, c->hd, tp<T>(c->dqkv), c->stream));
+    GemmArgs g6 = mk(c->dqkv, 3 * d, lw.wqkvT, 3 * d, (int)M, d, 3 * d);
+    g6.e.kind = EPI_F32;
+    g6.e.c = c->tmpf;
+    g6.e.ldc = d;
+    CK(Ops<T>::gemm(c, g6));
+    CK(rmsnorm_bwd<T>(a.h_in, a.rstd1, M, d, lw.attn_norm, c->tmpf, c->dh, c->dh, (T*)nullptr, c->stream));
+  }
+  return TTT_OK;
+}
+
+// the chunk loop over n_tokens tokens per row, starting at c->pos
+template <typename T>
+int run_tokens(ttt_ctx* c, const int32_t* tok, const int32_t* tgt, int64_t ld, int64_t n_tokens, float* loss_dev) {
+  int64_t done = 0, ci = 0;
+  const int64_t gmax = (int64_t)c->G * c->b;
+  while (done < n_tokens) {
+    int g = (int)std::min<int64_t>(n_tokens - done, gmax);
+    int rc = bottom_pass<T>(c, tok + done, ld, g, c->pos + done);
+    if (rc) return rc;
+    for (int cs = 0; cs < g; cs += c->b) {
+      int n = std::min(c->b, g - cs);
+      rc = top_chunk<T>(c, tgt + done + cs, ld, c->hb + (int64_t)cs * c->d, (int64_t)g * c->d, n, c->pos + done + cs,
+                        loss_dev + ci * c->B);
+      if (rc) return rc;
+      ++ci;
+    }
+    done += g;
+  }
+  c->pos += n_tokens;
+  return TTT_OK;
+}
+
+// one greedy decode step: input tok[r*ld], output arg-max to tok[r*ld + 1]
+template <typename T>
+int decode_step(ttt_ctx* c, int32_t* tok, int64_t ld) {
+  const int B = c->B, d = c->d;
+  CK(embed_gather_ld<T>(tok, ld, B, 1, tp<T>(c->embed), d, c->V, c->hb, c->err_dev, c->stream));
+  for (int l = 0; l < c->L; ++l) {
+    int rc = layer_fwd<T>(c, l, c->hb, 1, c->pos, FULL, nullptr);
+    if (rc) return rc;
+  }
+  CK(rmsnorm_fwd<T>(c->hb, B, d, c->final_norm, (float)c->cfg.rms_eps, tp<T>(c->hf), c->rstd_tmp, (T*)nullptr, 1, 0,
+                    c->stream));
+  GemmArgs gl = mk(c->hf, d, c->lm_head, d, B, c->V, d);
+  gl.e.kind = EPI_F32;
+  gl.e.c = c->logits;
+  gl.e.ldc = c->V;
+  CK(Ops<T>::gemm(c, gl));
+  CK(argmax_rows_ld(c->logits, B, c->V, tok + 1, ld, nullptr, 0, c->stream));
+  c->pos += 1;
+  return TTT_OK;
+}
+
+int ensure_tok(ttt_ctx* c, int64_t n) {
+  if (n <= c->d_tok_cap) return TTT_OK;
+  void* p = c->alloc((size_t)n * 4);
+  if (!p) return fail(c, TTT_ENOMEM, "token buffer allocation failed");
+  c->d_tok = (int32_t*)p;
+  c->d_tok_cap = n;
+  return TTT_OK;
+}
+
+int ensure_loss(ttt_ctx* c, int64_t n) {
+  if (n <= c->d_loss_cap) return TTT_OK;
+  void* p = c->alloc((size_t)n * 4);
+  if (!p) return fail(c, TTT_ENOMEM, "loss buffer allocation failed");
+  c->d_loss = (float*)p;
+  c->d_loss_cap = n;
+  return TTT_OK;
+}
+
+int check_ids(const ttt_ctx* c, const int32_t* x, int64_t cnt, bool allow_ignore) {
+  for (int64_t i = 0; i < cnt; ++i) {
+    if (x[i] >= c->V) return 0;
+    if (x[i] < 0 && !(allow_ignore && x[i] == -1)) return 0;
+  }
+  return 1;
+}
+
+int sync_and_check(ttt_ctx* c, const float* dloss, int64_t nloss, float* host_copy) {
+  std::vector<float> tmp;
+  if (dloss && nloss > 0) {
+    tmp.resize(nloss);
+    CK(hipMemcpyAsync(tmp.data(), dloss, nloss * 4, hipMemcpyDeviceToHost, c->stream));
+  }
+  int herr = 0;
+  CK(hipMemcpyAsync(&herr, c->err_dev, 4, hipMemcpyDeviceToHost, c->stream));
+  CK(hipStreamSynchronize(c->stream));
+  if (herr) {
+    c->poisoned = true;
+    return fail(c, TTT_EINVAL, "token id out of range in device input");
+  }
+  for (int64_t i = 0; i < nloss; ++i)
+    if (!std::isfinite(tmp[i])) return fail(c, TTT_ENONFINITE, "non-finite chunk loss");
+  if (host_copy && nloss > 0) memcpy(host_copy, tmp.data(), nloss * 4);
+  return TTT_OK;
+}
+
+int run_dispatch(ttt_ctx* c, const int32_t* tok, const int32_t* tgt, int64_t ld, int64_t n, float* loss_dev) {
+  return c->bf16 ? run_tokens<bf16>(c, tok, tgt, ld, n, loss_dev) : run_tokens<float>(c, tok, tgt, ld, n, loss_dev);
+}
+
+int decode_dispatch(ttt_ctx* c, int32_t* tok, int64_t ld) {
+  return c->bf16 ? decode_step<bf16>(c, tok, ld) : decode_step<float>(c, tok, ld);
+}
+
+// host fp32 -> device T
+int upload(ttt_ctx* c, void* dst, const float* src, int64_t cnt) {
+  if (!c->bf16) {
+    CK(hipMemcpy(dst, src, cnt * 4, hipMemcpyHostToDevice));
+    return TTT_OK;
+  }
+  std::vector<bf16> tmp(cnt);
+  for (int64_t i = 0; i < cnt; ++i) tmp[i] = f2bf(src[i]);
+  CK(hipMemcpy(dst, tmp.data(), cnt * 2, hipMemcpyHostToDevice));
+  return TTT_OK;
+}
+
+// host fp32 [rows][cols] -> device T transposed [cols][rows]
+int upload_t(ttt_ctx* c, void* dst, const float* src, int64_t rows, int64_t cols) {
+  std::vector<float> t(rows * cols);
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t q = 0; q < cols; ++q) t[q * rows + r] = src[r * cols + q];
+  return upload(c, dst, t.data(), rows * cols);
+}
+
+int build(ttt_ctx* c, const ttt_weights* w) {
+  const int L = c->L, d = c->d, f = c->f, V = c->V, B = c->B, H = c->H, hd = c->hd, b = c->b, R = c->R;
+  const size_t es = c->es;
+  const int64_t rows_bot = (int64_t)B * c->G * b, rows_top = (int64_t)B * b;
+#define AL(ptr, bytes)                                                           \
+  do {                                                                           \
+    (ptr) = (decltype(ptr))c->alloc((size_t)(bytes));                            \
+    if (!(ptr)) return fail(c, TTT_ENOMEM, "device allocation failed: " #ptr);  \
+  } while (0)
+  AL(c->embed, (int64_t)V * d * es);
+  AL(c->lm_head, (int64_t)V * d * es);
+  AL(c->lm_headT, (int64_t)V * d * es);
+  AL(c->final_norm, d * 4);
+  int rc;
+  if ((rc = upload(c, c->embed, w->embed, (int64_t)V * d))) return rc;
+  if ((rc = upload(c, c->lm_head, w->lm_head, (int64_t)V * d))) return rc;
+  if ((rc = upload_t(c, c->lm_headT, w->lm_head, V, d))) return rc;
+  CK(hipMemcpy(c->final_norm, w->final_norm, d * 4, hipMemcpyHostToDevice));
+  c->lw.resize(L);
+  const int64_t ring = (int64_t)B * H * R * hd * es;
+  std::vector<float> qkv((size_t)3 * d * d);
+  for (int l = 0; l < L; ++l) {
+    LayerW& lw = c->lw[l];
+    AL(lw.attn_norm, d * 4);
+    AL(lw.mlp_norm, d * 4);
+    CK(hipMemcpy(lw.attn_norm, w->attn_norm[l], d * 4, hipMemcpyHostToDevice));
+    CK(hipMemcpy(lw.mlp_norm, w->mlp_norm[l], d * 4, hipMemcpyHostToDevice));
+    memcpy(qkv.data(), w->wq[l], (size_t)d * d * 4);
+    memcpy(qkv.data() + (size_t)d * d, w->wk[l], (size_t)d * d * 4);
+    memcpy(qkv.data() + 2 * (size_t)d * d, w->wv[l], (size_t)d * d * 4);
+    AL(lw.wqkv, 3LL * d * d * es);
+    AL(lw.wo, (int64_t)d * d * es);
+    if ((rc = upload(c, lw.wqkv, qkv.data(), 3LL * d * d))) return rc;
+    if ((rc = upload(c, lw.wo, w->wo[l], (int64_t)d * d))) return rc;
+    if (l > c->l0) {
+      AL(lw.wqkvT, 3LL * d * d * es);
+      AL(lw.woT, (int64_t)d * d * es);
+      if ((rc = upload_t(c, lw.wqkvT, qkv.data(), 3LL * d, d))) return rc;
+      if ((rc = upload_t(c, lw.woT, w->wo[l], d, d))) return rc;
+    }
+    if (l < c->l0) {
+      AL(lw.wgu, 2LL * f * d * es);
+      AL(lw.wd, (int64_t)d * f * es);
+      if ((rc = upload(c, lw.wgu, w->w_gate[l], (int64_t)f * d))) return rc;
+      if ((rc = upload(c, (char*)lw.wgu + (int64_t)f * d * es, w->w_up[l], (int64_t)f * d))) return rc;
+      if ((rc = upload(c, lw.wd, w->w_down[l], (int64_t)d * f))) return rc;
+    }
+    AL(lw.kr, ring);
+    AL(lw.vr, ring);
+    AL(lw.vtr, ring);
+    CK(hipMemset(lw.kr, 0, ring));
+    CK(hipMemset(lw.vr, 0, ring));
+    CK(hipMemset(lw.vtr, 0, ring));
+  }
+  // fast weights: fp32 masters per row plus T shadows in both layouts
+  const int64_t fsz = 3LL * f * d;
+  AL(c->fast_init, fsz * c->Lq * 4);
+  c->fw.resize(c->Lq);
+  for (int j = 0; j < c->Lq; ++j) {
+    int l = c->l0 + j;
+    float* init = c->fast_init + j * fsz;
+    CK(hipMemcpy(init, w->w_gate[l], (size_t)f * d * 4, hipMemcpyHostToDevice));
+    CK(hipMemcpy(init + (int64_t)f * d, w->w_up[l], (size_t)f * d * 4, hipMemcpyHostToDevice));
+    CK(hipMemcpy(init + 2LL * f * d, w->w_down[l], (size_t)d * f * 4, hipMemcpyHostToDevice));
+    FastW& fw = c->fw[j];
+    AL(fw.master, fsz * B * 4);
+    AL(fw.wgu, 2LL * f * d * B * es);
+    AL(fw.wguT, 2LL * f * d * B * es);
+    AL(fw.wd, (int64_t)d * f * B * es);
+    AL(fw.wdT, (int64_t)d * f * B * es);
+  }
+  // RoPE table in fp64 on the host, stored fp32: angle = pos * theta^(-2i/hd)
+  const int half = hd / 2;
+  const int64_t P = c->cfg.max_positions;
+  {
+    std::vector<float> cs((size_t)P * half), sn((size_t)P * half);
+    std::vector<double> inv(half);
+    for (int i = 0; i < half; ++i) inv[i] = std::pow(c->cfg.rope_theta, -2.0 * i / hd);
+    for (int64_t p = 0; p < P; ++p)
+      for (int i = 0; i < half; ++i) {
+        double a = (double)p * inv[i];
+        cs[(size_t)p * half + i] = (float)std::cos(a);
+        sn[(size_t)p * half + i] = (float)std::sin(a);
+      }
+    AL(c->cos_t, P * half * 4);
+    AL(c->sin_t, P * half * 4);
+    CK(hipMemcpy(c->cos_t, cs.data(), (size_t)P * half * 4, hipMemcpyHostToDevice));
+    CK(hipMemcpy(c->sin_t, sn.data(), (size_t)P * half * 4, hipMemcpyHostToDevice));
+  }
+  // work buffers
+  AL(c->hb, rows_bot * d * 4);
+  AL(c->qkvb, rows_bot * 3 * d * 4);
+  AL(c->rstd_tmp, rows_bot * 4);
+  AL(c->ub, rows_bot * d * es);
+  AL(c->qb, rows_bot * d * es);
+  AL(c->ob, rows_bot * d * es);
+  AL(c->actb, rows_bot * f * es);
+  AL(c->htop, rows_top * d * 4);
+  AL(c->rstdf, rows_top * 4);
+  AL(c->logits, rows_top * V * 4);
+  AL(c->loss_tok, rows_top * 4);
+  AL(c->hf, rows_top * d * es);
+  AL(c->dlogits, rows_top * V * es);
+  AL(c->nvalid, B * 4);
+  AL(c->dh, rows_top * d * 4);
+  AL(c->tmpf, rows_top * d * 4);
+  AL(c->dq, rows_top * d * 4);
+  AL(c->dk, rows_top * d * 4);
+  AL(c->dv, rows_top * d * 4);
+  AL(c->dvec, rows_top * H * 4);
+  AL(c->dyN, rows_top * d * es);
+  AL(c->dyT, rows_top * d * es);
+  AL(c->dz, rows_top * 2 * f * es);
+  AL(c->dzT, rows_top * 2 * f * es);
+  AL(c->dhT, rows_top * d * es);
+  AL(c->dO, rows_top * d * es);
+  AL(c->dqkv, rows_top * 3 * d * es);
+  AL(c->err_dev, 256);
+  CK(hipMemset(c->err_dev, 0, 4));
+  c->acts.resize(c->Lq);
+  for (int j = 0; j < c->Lq; ++j) {
+    TopActs& a = c->acts[j];
+    AL(a.h_in, rows_top * d * 4);
+    AL(a.h_mid, rows_top * d * 4);
+    AL(a.rstd1, rows_top * 4);
+    AL(a.rstd2, rows_top * 4);
+    AL(a.lse, rows_top * H * 4);
+    AL(a.q, rows_top * d * es);
+    AL(a.qt, rows_top * d * es);
+    AL(a.o, rows_top * d * es);
+    AL(a.mT, rows_top * d * es);
+    AL(a.zg, rows_top * f * es);
+    AL(a.zu, rows_top * f * es);
+    AL(a.actT, rows_top * f * es);
+  }
+#undef AL
+  return TTT_OK;
+}
+
+int reset_state(ttt_ctx* c) {
+  const int64_t fsz = 3LL * c->f * c->d;
+  for (int j = 0; j < c->Lq; ++j) {
+    FastW& fw = c->fw[j];
+    for (int r = 0; r < c->B; ++r)
+      CK(hipMemcpyAsync(fw.master + r * fsz, c->fast_init + j * fsz, fsz * 4, hipMemcpyDeviceToDevice, c->stream));
+    CK(refresh_shadows(fw.master, 2 * c->f, c->d, c->B, fsz, fw.wgu, 2LL * c->f * c->d, fw.wguT, 2LL * c->f * c->d,
+                       c->bf16, c->stream));
+    CK(refresh_shadows(fw.master + 2LL * c->f * c->d, c->d, c->f, c->B, fsz, fw.wd, (int64_t)c->d * c->f, fw.wdT,
+                       (int64_t)c->d * c->f, c->bf16, c->stream));
+  }
+  const int64_t ring = (int64_t)c->B * c->H * c->R * c->hd * c->es;
+  for (int l = 0; l < c->L; ++l) {
+    CK(hipMemsetAsync(c->lw[l].kr, 0, ring, c->stream));
+    CK(hipMemsetAsync(c->lw[l].vr, 0, ring, c->stream));
+    CK(hipMemsetAsync(c->lw[l].vtr, 0, ring, c->stream));
+  }
+  CK(hipMemsetAsync(c->err_dev, 0, 4, c->stream));
+  CK(hipStreamSynchronize(c->stream));
+  c->pos = 0;
+  c->poisoned = false;
+  c->pending_loss = nullptr;
+  c->pending_n = 0;
+  return TTT_OK;
+}
+
+}  // namespace
+
+// ====================================================================== C ABI
+
+extern "C" {
+
+int ttt_set_allocator(ttt_alloc_fn alloc, ttt_free_fn free_fn, void* user) {
+  if ((alloc == nullptr) != (free_fn == nullptr)) return TTT_EINVAL;
+  g_alloc = alloc;
+  g_free = free_fn;
+  g_user = user;
+  return TTT_OK;
+}
+
+const char* ttt_last_error(const ttt_ctx* ctx) { return ctx ? ctx->err.c_str() : g_create_err.c_str(); }
+
+int ttt_create(const ttt_config* cfg, const ttt_weights* w, void* hip_stream, ttt_ctx** out) {
+  g_create_err.clear();
+  if (!cfg || !w || !out) {
+    g_create_err = "NULL argument";
+    return TTT_EINVAL;
+  }
+  *out = nullptr;
+  ttt_config c0 = *cfg;
+  if (c0.n_fast == 0) c0.n_fast = std::max(1, c0.n_layers / 4);
+  if (c0.lookahead <= 0) c0.lookahead = 8;
+  auto bad = [&](const char* m) {
+    g_create_err = m;
+    return TTT_EINVAL;
+  };
+  if (c0.n_layers <= 0 || c0.d_model <= 0 || c0.n_heads <= 0 || c0.d_ff <= 0 || c0.vocab <= 0 || c0.batch <= 0)
+    return bad("sizes must be positive");
+  if (c0.d_model % c0.n_heads) return bad("d_model must be a multiple of n_heads");
+  int hd = c0.d_model / c0.n_heads;
+  if (hd % 2 || hd > 128) return bad("head_dim must be even and at most 128");
+  if (c0.chunk <= 0 || c0.window < c0.chunk) return bad("window must be >= chunk >= 1");
+  if (c0.n_fast < 1 || c0.n_fast > c0.n_layers) return bad("n_fast out of range");
+  if (c0.dtype != TTT_F32 && c0.dtype != TTT_BF16) return bad("dtype must be TTT_F32 or TTT_BF16");
+  if (c0.max_positions <= 0) return bad("max_positions must be positive");
+  if (!(c0.rope_theta > 0) || !(c0.rms_eps >= 0) || !std::isfinite(c0.lr)) return bad("bad theta/eps/lr");
+  if (!w->embed || !w->final_norm || !w->lm_head || !w->attn_norm || !w->wq || !w->wk || !w->wv || !w->wo ||
+      !w->mlp_norm || !w->w_gate || !w->w_up || !w->w_down)
+    return bad("NULL weight pointer");
+  for (int l = 0; l < c0.n_layers; ++l)
+    if (!w->attn_norm[l] || !w->wq[l] || !w->wk[l] || !w->wv[l] || !w->wo[l] || !w->mlp_norm[l] || !w->w_gate[l] ||
+        !w->w_up[l] || !w->w_down[l])
+      return bad("NULL per-layer weight pointer");
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || ndev == 0) {
+    g_create_err = "no HIP device";
+    return TTT_ENODEV;
+  }
+  int dev = 0;
+  hipDeviceProp_t prop;
+  if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess ||
+      strncmp(prop.gcnArchName, "gfx950", 6) != 0) {
+    g_create_err = "device is not gfx950";
+    return TTT_ENODEV;
+  }
+  ttt_ctx* c = new ttt_ctx();
+  c->cfg = c0;
+  c->L = c0.n_layers;
+  c->d = c0.d_model;
+  c->H = c0.n_heads;
+  c->hd = hd;
+  c->f = c0.d_ff;
+  c->V = c0.vocab;
+  c->k = c0.window;
+  c->b = c0.chunk;
+  c->Lq = c0.n_fast;
+  c->l0 = c0.n_layers - c0.n_fast;
+  c->B = c0.batch;
+  c->G = c0.lookahead;
+  c->R = c0.window + c0.lookahead * c0.chunk;
+  c->bf16 = c0.dtype == TTT_BF16;
+  c->es = c->bf16 ? 2 : 4;
+  c->stream = (hipStream_t)hip_stream;
+  c->free_fn = g_free;
+  c->free_user = g_user;
+  const char* simt = getenv("TTT_SIMT");
+  c->mfma = !(simt && simt[0] == '1');
+  int rc = build(c, w);
+  if (rc == TTT_OK) rc = reset_state(c);
+  if (rc != TTT_OK) {
+    g_create_err = c->err;
+    c->release_all();
+    delete c;
+    return rc;
+  }
+  *out = c;
+  return TTT_OK;
+}
+
+void ttt_destroy(ttt_ctx* c) {
+  if (!c) return;
+  (void)hipStreamSynchronize(c->stream);
+  c->release_all();
+  delete c;
+}
+
+int64_t ttt_position(const ttt_ctx* c) { return c ? c->pos : -1; }
+
+int ttt_reset(ttt_ctx* c) {
+  if (!c) return TTT_EINVAL;
+  return reset_state(c);
+}
+
+int ttt_prefill(ttt_ctx* c, const int32_t* tokens, const int32_t* targets, int64_t n_tokens, float* losses) {
+  if (!c) return TTT_EINVAL;
+  if (c->poisoned) return fail(c, TTT_ESTATE, "context poisoned; call ttt_reset");
+  if (!tokens || !targets || n_tokens <= 0) return fail(c, TTT_EINVAL, "NULL tokens/targets or n_tokens <= 0");
+  if (c->pos + n_tokens > c->cfg.max_positions) return fail(c, TTT_EINVAL, "beyond max_positions");
+  const int64_t cnt = (int64_t)c->B * n_tokens;
+  if (!check_ids(c, tokens, cnt, false)) return fail(c, TTT_EINVAL, "token id out of range");
+  if (!check_ids(c, targets, cnt, true)) return fail(c, TTT_EINVAL, "target id out of range");
+  const int64_t nch = (n_tokens + c->b - 1) / c->b;
+  int rc;
+  if ((rc = ensure_tok(c, 2 * cnt))) return rc;
+  if ((rc = ensure_loss(c, nch * c->B))) return rc;
+  CK(hipMemcpyAsync(c->d_tok, tokens, cnt * 4, hipMemcpyHostToDevice, c->stream));
+  CK(hipMemcpyAsync(c->d_tok + cnt, targets, cnt * 4, hipMemcpyHostToDevice, c->stream));
+  rc = run_dispatch(c, c->d_tok, c->d_tok + cnt, n_tokens, n_tokens, c->d_loss);
+  if (rc) return rc;
+  std::vector<float> tmp(nch * c->B);
+  rc = sync_and_check(c, c->d_loss, nch * c->B, tmp.data());
+  if (rc) return rc;
+  if (losses)
+    for (int64_t ch = 0; ch < nch; ++ch)
+      for (int r = 0; r < c->B; ++r) losses[(int64_t)r * nch + ch] = tmp[ch * c->B + r];
+  return TTT_OK;
+}
+
+int ttt_prefill_chunk(ttt_ctx* c, const int32_t* tokens, const int32_t* targets, int32_t n, float* loss_out) {
+  if (!c) return TTT_EINVAL;
+  if (n <= 0 || n > c->b) return fail(c, TTT_EINVAL, "n must be in 1..chunk");
+  return ttt_prefill(c, tokens, targets, n, loss_out);
+}
+
+int ttt_prefill_device(ttt_ctx* c, const int32_t* d_tokens, const int32_t* d_targets, int64_t n_tokens,
+                       float* d_losses) {
+  if (!c) return TTT_EINVAL;
+  if (c->poisoned) return fail(c, TTT_ESTATE, "context poisoned; call ttt_reset");
+  if (!d_tokens || !d_targets || n_tokens <= 0) return fail(c, TTT_EINVAL, "NULL tokens/targets or n_tokens <= 0");
+  if (c->pos + n_tokens > c->cfg.max_positions) return fail(c, TTT_EINVAL, "beyond max_positions");
+  const int64_t nch = (n_tokens + c->b - 1) / c->b;
+  if (!d_losses) {
+    int rc = ensure_loss(c, nch * c->B);
+    if (rc) return rc;
+    d_losses = c->d_loss;
+  }
+  int rc = run_dispatch(c, d_tokens, d_targets, n_tokens, n_tokens, d_losses);
+  if (rc) return rc;
+  c->pending_loss = d_losses;
+  c->pending_n = nch * c->B;
+  return TTT_OK;
+}
+
+int ttt_sync(ttt_ctx* c) {
+  if (!c) return TTT_EINVAL;
+  if (c->poisoned) return fail(c, TTT_ESTATE, "context poisoned; call ttt_reset");
+  int rc = sync_and_check(c, c->pending_loss, c->pending_n, nullptr);
+  c->pending_loss = nullptr;
+  c->pending_n = 0;
+  return rc;
+}
+
+int ttt_generate(ttt_ctx* c, const int32_t* first_input, int32_t n_new, int32_t update_every, int32_t* out_tokens,
+                 float* update_losses) {
+  if (!c) return TTT_EINVAL;
+  if (c->poisoned) return fail(c, TTT_ESTATE, "context poisoned; call ttt_reset");
+  if (!first_input || !out_tokens || n_new < 0) return fail(c, TTT_EINVAL, "bad generate arguments");
+  if (update_every < 1 || update_every > c->b) return fail(c, TTT_EINVAL, "update_every must be in 1..chunk");
+  if (c->pos + n_new > c->cfg.max_positions) return fail(c, TTT_EINVAL, "beyond max_positions");
+  if (!check_ids(c, first_input, c->B, false)) return fail(c, TTT_EINVAL, "first_input id out of range");
+  if (n_new == 0) return TTT_OK;
+  const int64_t ld = (int64_t)n_new + 1;
+  const int nu = n_new / update_every;
+  int rc;
+  if ((rc = ensure_tok(c, ld * c->B))) return rc;
+  if ((rc = ensure_loss(c, (int64_t)std::max(nu, 1) * c->B))) return rc;
+  CK(hipMemcpy2DAsync(c->d_tok, ld * 4, first_input, 4, 4, c->B, hipMemcpyHostToDevice, c->stream));
+  int upd = 0;
+  for (int j = 0; j < n_new; ++j) {
+    rc = decode_dispatch(c, c->d_tok + j, ld);
+    if (rc) return rc;
+    if ((j + 1) % update_every == 0) {
+      const int j0 = j + 1 - update_every;
+      c->pos -= update_every;
+      rc = run_dispatch(c, c->d_tok + j0, c->d_tok + j0 + 1, ld, update_every, c->d_loss + (int64_t)upd * c->B);
+      if (rc) return rc;
+      ++upd;
+    }
+  }
+  std::vector<float> tmp((size_t)std::max(nu, 1) * c->B);
+  rc = sync_and_check(c, c->d_loss, (int64_t)nu * c->B, tmp.data());
+  if (rc) return rc;
+  std::vector<int32_t> all((size_t)ld * c->B);
+  CK(hipMemcpy(all.data(), c->d_tok, ld * c->B * 4, hipMemcpyDeviceToHost));
+  for (int r = 0; r < c->B; ++r)
+    for (int j = 0; j < n_new; ++j) out_tokens[(int64_t)r * n_new + j] = all[(size_t)r * ld + j + 1];
+  if (update_losses)
+    for (int u = 0; u < nu; ++u)
+      for (int r = 0; r < c->B; ++r) update_losses[(int64_t)r * nu + u] = tmp[(size_t)u * c->B + r];
+  return TTT_OK;
+}
+
+int ttt_get_fast_weights(ttt_ctx* c, int32_t row, float* dst, int64_t n_floats) {
+  if (!c) return TTT_EINVAL;
+  if (!dst || row < 0 || row >= c->B) return fail(c, TTT_EINVAL, "bad row or NULL dst");
+  const int64_t fsz = 3LL * c->f * c->d;
+  if (n_floats != fsz * c->Lq) return fail(c, TTT_EINVAL, "n_floats must be 3*d*f*n_fast");
+  CK(hipStreamSynchronize(c->stream));
+  for (int j = 0; j < c->Lq; ++j)
+    CK(hipMemcpy(dst + j * fsz, c->fw[j].master + row * fsz, fsz * 4, hipMemcpyDeviceToHost));
+  return TTT_OK;
+}
+
+}  // extern "C"

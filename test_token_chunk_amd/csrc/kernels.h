@@ -1,0 +1,137 @@
+// Kernel launchers of the HIP path (gfx950).  All pointers are device pointers;
+// every launcher enqueues on `s` and returns the launch status.
+#pragma once
+#include "common.h"
+
+// ------------------------------------------------------------------ GEMM
+// C[b][m][n] = sum_k A[b][m][k] * B[b][n][k]   (both operands K-contiguous,
+// i.e. y = x W^T with W stored [out, in]), fp32 accumulation, then an
+// epilogue applied per output element.
+enum EpiKind {
+  EPI_F32 = 0,     // c (fp32) = acc
+  EPI_T = 1,       // c (T) = acc
+  EPI_ADD_F32 = 2, // c (fp32) += acc           (residual stream)
+  EPI_SWIGLU = 3,  // dual: act = silu(acc_g) * acc_u -> c (T); zg, zu (T) and act^T (T) optional
+  EPI_SWIGLU_BWD = 4, // acc = d act: dz_g, dz_u -> c = dz (T, [m][2f]) and dz^T (T, [2f][ldt])
+  EPI_SGD = 5,     // acc = gradient: master (fp32) -= lr * acc; shadow (T) and shadow^T (T) refreshed
+  EPI_QKV_ROPE = 6 // acc = [q|k|v] row: RoPE of q, k; q -> c, k,v -> rings (see RopeRing)
+};
+
+struct RopeRing {
+  const float* cos_t;  // [max_pos][hd/2]
+  const float* sin_t;
+  int64_t pos0;        // absolute position of local row 0 (same for every batch row)
+  int n;               // tokens per batch row in this call
+  int H, hd, R;        // heads, head dim, ring slots
+  void* q;             // [B][H][n][hd] T (rotated queries)
+  void* qt;            // [B][H][hd][n] T or null
+  void* kr;            // ring K [B][H][R][hd] T
+  void* vr;            // ring V [B][H][R][hd] T
+  void* vtr;           // ring V^T [B][H][hd][R] T
+};
+
+struct Epi {
+  int kind = EPI_F32;
+  void* c = nullptr;
+  int64_t ldc = 0, sc = 0;  // row stride and batch stride of c
+  // SWIGLU / SWIGLU_BWD extras
+  void* zg = nullptr;
+  void* zu = nullptr;
+  int64_t ldz = 0, sz = 0;
+  void* t = nullptr;  // transposed output ([n][ldt] per batch)
+  int64_t ldt = 0, st = 0;
+  int f = 0;
+  // SGD extras
+  float* master = nullptr;
+  int64_t ldm = 0, sm = 0;
+  void* sh = nullptr;
+  int64_t ldsh = 0, ssh = 0;
+  void* shT = nullptr;
+  int64_t ldshT = 0, sshT = 0;
+  float lr = 0.f;
+  RopeRing rr;
+};
+
+struct GemmArgs {
+  const void* A = nullptr;
+  int64_t lda = 0, sA = 0;
+  const void* B = nullptr;
+  int64_t ldb = 0, sB = 0;
+  int M = 0, N = 0, K = 0, batch = 1;
+  int64_t dual_off = 0;  // EPI_SWIGLU: the "up" operand starts dual_off rows after the "gate" rows
+  Epi e;
+};
+
+hipError_t gemm_simt_f32(const GemmArgs& g, hipStream_t s);   // fp32 operands
+hipError_t gemm_simt_bf16(const GemmArgs& g, hipStream_t s);  // bf16 operands, SIMT
+hipError_t gemm_mfma_bf16(const GemmArgs& g, hipStream_t s);  // bf16 operands, MFMA
+
+// ------------------------------------------------------------------ elementwise
+// Token arrays are [B][ld] int32 (row stride ld); activations are [B*n][d] rows.
+template <typename T>
+hipError_t embed_gather_ld(const int32_t* ids, int64_t ld, int B, int n, const T* E, int d, int V, float* h,
+                           int* err, hipStream_t s);
+// y = g * x / sqrt(mean(x^2) + eps) as T (optional), rstd (optional), transposed copy yT [B][d][ldT] (optional)
+template <typename T>
+hipError_t rmsnorm_fwd(const float* x, int64_t M, int d, const float* g, float eps, T* y, float* rstd, T* yT,
+                       int rows_per_batch, int64_t ldT, hipStream_t s);
+// out = resid + RMSNorm-backward(dy) (resid may be null, out may alias resid); outT: T copy of out (optional)
+template <typename T>
+hipError_t rmsnorm_bwd(const float* x, const float* rstd, int64_t M, int d, const float* g, const float* dy,
+                       const float* resid, float* out, T* outT, hipStream_t s);
+// fp32 [B*n][d] -> T copy [B*n][d] (optional) and transposed T [B][d][ldT] (optional)
+template <typename T>
+hipError_t convert_rows(const float* x, int64_t M, int d, T* y, T* yT, int rows_per_batch, int64_t ldT,
+                        hipStream_t s);
+hipError_t count_valid_ld(const int32_t* tgt, int64_t ld, int B, int n, int* nvalid, hipStream_t s);
+// cross-entropy of full logit rows: loss_tok[m] and dlogits = (softmax - onehot) / nvalid (T)
+template <typename T>
+hipError_t ce_rows_ld(const float* logits, int64_t M, int V, const int32_t* tgt, int64_t ld, const int* nvalid,
+                      int rows_per_batch, float* loss_tok, T* dlogits, int* err, hipStream_t s);
+hipError_t reduce_loss(const float* loss_tok, const int* nvalid, int B, int n, float* loss_out, hipStream_t s);
+hipError_t argmax_rows_ld(const float* logits, int B, int V, int32_t* out, int64_t ld_out, int32_t* out2,
+                          int64_t ld_out2, hipStream_t s);
+hipError_t copy_rows(const float* src, int64_t src_batch_stride, float* dst, int B, int n, int d, hipStream_t s);
+
+// ------------------------------------------------------------------ attention
+struct AttnArgs {
+  const void* q;    // [B][H][n][hd] rotated queries
+  const void* kr;   // ring K [B][H][R][hd]
+  const void* vr;   // ring V [B][H][R][hd]
+  const void* vtr;  // ring V^T [B][H][hd][R]
+  void* o;          // [B*n][H*hd] output (T)
+  float* lse;       // [B][H][n] or null
+  int B, H, hd, n, R, window;
+  int64_t pos0;     // absolute position of query 0
+};
+template <typename T>
+hipError_t swa_fwd_simt(const AttnArgs& a, hipStream_t s);
+hipError_t swa_fwd_mfma(const AttnArgs& a, hipStream_t s);  // bf16
+
+struct AttnBwdArgs {
+  const void* q;    // [B][H][n][hd]
+  const void* qt;   // [B][H][hd][n]
+  const void* kr;   // ring K
+  const void* vr;   // ring V
+  const void* vtr;  // ring V^T
+  const void* o;    // [B*n][H*hd] forward output (T)
+  const void* dout; // [B*n][H*hd] gradient of the output (T)
+  const float* lse; // [B][H][n]
+  float* dvec;      // [B][H][n] scratch: rowsum(dO * O)
+  float* dq;        // [B*n][H*hd] fp32 (rotated frame)
+  float* dk;        // [B*n][H*hd] fp32 (rotated frame), in-chunk keys only
+  float* dv;        // [B*n][H*hd] fp32
+  int B, H, hd, n, R, window;
+  int64_t pos0;
+};
+template <typename T>
+hipError_t swa_bwd_simt(const AttnBwdArgs& a, hipStream_t s);
+hipError_t swa_bwd_mfma(const AttnBwdArgs& a, hipStream_t s);  // bf16
+
+// RoPE of q, k from a fp32 [B*n][3d] projection; q -> rr.q (and rr.qt), k, v -> rings
+hipError_t rope_qkv_f32in(const float* qkv, int B, const RopeRing& rr, int is_bf16, hipStream_t s);
+
+// RoPE backward of dq, dk (fp32, rotated frame) and packing [dq | dk | dv] into T [B*n][3d]
+template <typename T>
+hipError_t rope_bwd_pack(const float* dq, const float* dk, const float* dv, const float* cos_t, const float* sin_t,
+                         int64_t pos0, int B, int n, int H, int hd, T* dqkv, hipStream_t s);

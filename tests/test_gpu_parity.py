@@ -1,0 +1,179 @@
+"""HIP path vs the fp64 oracle, through the C ABI, on seeded synthetic inputs.
+
+Tolerances (per chunk loss: relative; fast weights: max|W_gpu - W_ref| over
+max|W_ref| per tensor, and the same for the update dW = W_T - W_0):
+fp32 path 1e-5 / 1e-4, bf16 path 2e-2 / 3e-2.
+"""
+import numpy as np
+import pytest
+
+from oracle import Oracle
+from tests.cfgs import TOY, cfg as mkcfg
+from test_token_chunk_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": (1e-5, 1e-4), "bf16": (2e-2, 3e-2)}
+
+
+def _ctx(c, w, max_pos, **over):
+    import torch
+    from test_token_chunk_amd import TTTConfig, TTTContext
+    assert torch.cuda.is_available()
+    tc = TTTConfig.from_dict(vars(c), max_positions=max_pos, **over)
+    return TTTContext(tc, w)
+
+
+def _shape(c):
+    return synth.Shape(c.n_layers, c.d_model, c.n_heads, c.d_ff, c.vocab)
+
+
+def _w0(w, c):
+    return [(w["w_gate"][l], w["w_up"][l], w["w_down"][l]) for l in range(c.n_layers - c.n_fast, c.n_layers)]
+
+
+def compare_fast(gpu_fast, ref_fast, w0, tol, label=""):
+    worst_w, worst_d = 0.0, 0.0
+    for j, (g, r, z) in enumerate(zip(gpu_fast, ref_fast, w0)):
+        for a in range(3):
+            ew = np.max(np.abs(g[a] - r[a])) / np.max(np.abs(r[a]))
+            dr = r[a] - z[a]
+            ed = np.max(np.abs((g[a] - z[a]) - dr)) / max(np.max(np.abs(dr)), 1e-30)
+            worst_w, worst_d = max(worst_w, ew), max(worst_d, ed)
+    print(f"{label} fast-weight rel err {worst_w:.3e}, update rel err {worst_d:.3e}")
+    assert worst_w <= tol, (worst_w, label)
+    assert worst_d <= tol, (worst_d, label)
+
+
+def run_pair(c, T, dist="uniform", tok_seed=1, targets_mask=None, **over):
+    bf = c.dtype == "bf16"
+    w = synth.weights(_shape(c), bf16=bf)
+    seq = synth.tokens(c.batch, T + 1, c.vocab, dist, seed=tok_seed)
+    tg = seq[:, 1:].copy()
+    if targets_mask is not None:
+        tg[targets_mask] = -1
+    o = Oracle(c, w, T + 8)
+    ref = []
+    for s in range(0, T, c.chunk):
+        e = min(T, s + c.chunk)
+        ref.append(o.prefill_chunk(seq[:, s:e], tg[:, s:e]))
+    ref = np.stack(ref, axis=1)
+    ctx = _ctx(c, w, T + 8, **over)
+    got = ctx.prefill(seq[:, :T], tg)
+    return w, o, ctx, ref, got
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_toy_full_sequence_parity(dtype):
+    """The toy workload (4 layers, d=128, T=1024, k=256, b=64, 16 chunks, the
+    ring wraps) against the oracle: every chunk loss and the final fast weights."""
+    c = mkcfg(**dict(TOY, dtype=dtype))
+    print(f"case toy {dtype}", flush=True)
+    w, o, ctx, ref, got = run_pair(c, 1024)
+    tl, tw = TOL[dtype]
+    rel = np.max(np.abs(got - ref) / np.abs(ref))
+    print(f"toy {dtype}: max loss rel err {rel:.3e}")
+    assert rel <= tl
+    compare_fast(ctx.fast_weights(0), o.get_fast(0), _w0(w, c), tw, f"toy {dtype}")
+
+
+def test_toy_more_fast_blocks_and_ragged_tail():
+    """Two fast blocks (attention backward exercised), window 96 not a
+    multiple of the chunk 40, T=300 (ragged last chunk), some targets ignored."""
+    c = mkcfg(**dict(TOY, n_fast=2, window=96, chunk=40, lr=3e-2))
+    print("case ragged f32", flush=True)
+    mask = np.zeros((1, 300), dtype=bool)
+    mask[0, ::7] = True
+    w, o, ctx, ref, got = run_pair(c, 300, targets_mask=mask)
+    rel = np.max(np.abs(got - ref) / np.abs(ref))
+    print(f"ragged: loss rel err {rel:.3e}")
+    assert rel <= 1e-5
+    compare_fast(ctx.fast_weights(0), o.get_fast(0), _w0(w, c), 1e-4, "ragged f32")
+
+
+def test_batch_rows_are_independent():
+    """B=3 rows on the GPU give each row's own single-row result."""
+    c3 = mkcfg(**dict(TOY, batch=3, n_fast=2))
+    w = synth.weights(_shape(c3), bf16=False)
+    seq = synth.tokens(3, 257, c3.vocab, "uniform", seed=5)
+    ctx3 = _ctx(c3, w, 300)
+    l3 = ctx3.prefill_seq(seq)
+    c1 = mkcfg(**dict(TOY, batch=1, n_fast=2))
+    for r in (0, 2):
+        ctx1 = _ctx(c1, w, 300)
+        l1 = ctx1.prefill_seq(seq[r:r + 1])
+        np.testing.assert_allclose(l3[r], l1[0], rtol=1e-6)
+        np.testing.assert_allclose(ctx3.fast_weights_flat(r), ctx1.fast_weights_flat(0), rtol=0, atol=1e-7)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_lookahead_is_exact(dtype):
+    """Running the frozen lower blocks one chunk at a time or eight at a time
+    gives bit-identical losses and fast weights."""
+    c = mkcfg(**dict(TOY, dtype=dtype, n_fast=2))
+    w = synth.weights(_shape(c), bf16=dtype == "bf16")
+    seq = synth.tokens(1, 641, c.vocab, "uniform", seed=9)
+    a = _ctx(c, w, 700, lookahead=1)
+    b = _ctx(c, w, 700, lookahead=8)
+    la, lb = a.prefill_seq(seq), b.prefill_seq(seq)
+    assert np.array_equal(la, lb)
+    assert np.array_equal(a.fast_weights_flat(), b.fast_weights_flat())
+
+
+def test_chunk_calls_equal_sequence_call_and_reset():
+    c = mkcfg(**dict(TOY, n_fast=2))
+    w = synth.weights(_shape(c), bf16=False)
+    seq = synth.tokens(1, 201, c.vocab, "uniform", seed=4)
+    a = _ctx(c, w, 256)
+    la = a.prefill_seq(seq)
+    b = _ctx(c, w, 256)
+    lb = [b.prefill_chunk(seq[:, s:min(200, s + 64)], seq[:, s + 1:min(200, s + 64) + 1])[0] for s in range(0, 200, 64)]
+    np.testing.assert_array_equal(la[0], np.array(lb, dtype=np.float32))
+    assert b.position == 200
+    b.reset()
+    assert b.position == 0
+    lc = b.prefill_seq(seq)
+    np.testing.assert_array_equal(la, lc)
+
+
+def test_device_entry_point_matches_host_entry_point():
+    import torch
+    c = mkcfg(**dict(TOY, n_fast=2))
+    w = synth.weights(_shape(c), bf16=False)
+    seq = synth.tokens(1, 321, c.vocab, "uniform", seed=6)
+    a = _ctx(c, w, 400)
+    la = a.prefill_seq(seq)
+    b = _ctx(c, w, 400)
+    dt = torch.tensor(seq[:, :320], dtype=torch.int32, device="cuda")
+    dg = torch.tensor(seq[:, 1:], dtype=torch.int32, device="cuda")
+    dl = torch.zeros(5, 1, dtype=torch.float32, device="cuda")
+    b.prefill_device(dt, dg, dl)
+    b.sync()
+    np.testing.assert_array_equal(la[0], dl[:, 0].cpu().numpy())
+
+
+def test_generate_teacher_forced_against_oracle():
+    """Greedy decode with an update every b generated tokens: replaying the
+    GPU's tokens in the oracle, each GPU token's logit is within tolerance of
+    the oracle's maximum, ids agree wherever the oracle's top-2 margin is
+    clear, and the update losses match."""
+    c = mkcfg(**dict(TOY, n_fast=2))
+    w = synth.weights(_shape(c), bf16=False)
+    T, n_new = 256, 160
+    seq = synth.tokens(1, T + 1, c.vocab, "uniform", seed=8)
+    ctx = _ctx(c, w, T + n_new + 8)
+    ctx.prefill_seq(seq)
+    toks, upd = ctx.generate(seq[:, T], n_new, 64)
+    o = Oracle(c, w, T + n_new + 8)
+    o.prefill(seq)
+    ot, oupd, logits = o.generate(seq[:, T], n_new, 64, forced=toks, want_logits=True)
+    lg = logits[0]
+    top = lg.max(axis=1)
+    chosen = lg[np.arange(n_new), toks[0]]
+    tol = 1e-4 * np.max(np.abs(lg))
+    assert np.all(top - chosen <= tol)
+    srt = np.sort(lg, axis=1)
+    clear = (srt[:, -1] - srt[:, -2]) > tol
+    assert np.array_equal(lg.argmax(axis=1)[clear], toks[0][clear])
+    np.testing.assert_allclose(upd, oupd, rtol=1e-5)
+    compare_fast(ctx.fast_weights(0), o.get_fast(0), _w0(w, c), 1e-4, "decode f32")
