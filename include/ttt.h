@@ -155,6 +155,17 @@ int ttt_reset(ttt_ctx* ctx);
 /* Current absolute position of every row (rows advance together). */
 int64_t ttt_position(const ttt_ctx* ctx);
 
+/* Kernel timing (tracing): while enabled, every launch of the classes below
+ * is bracketed by HIP events on the context's stream.  ttt_profile_enable
+ * clears earlier records; ttt_profile_read synchronizes and returns, per
+ * class, the summed device time (ms), the launch count and the algorithmic
+ * FLOPs of those launches (matmul = 2 M N K; attention = 4 * head_dim per
+ * visible query-key pair, plus 4 * head_dim per in-chunk pair in backward).
+ * Classes: 0 GEMM, 1 sliding-window attention forward, 2 its backward. */
+enum { TTT_PROF_GEMM = 0, TTT_PROF_SWA_FWD = 1, TTT_PROF_SWA_BWD = 2, TTT_PROF_CLASSES = 3 };
+int ttt_profile_enable(ttt_ctx* ctx, int32_t on);
+int ttt_profile_read(ttt_ctx* ctx, int32_t n_classes, double* ms, int64_t* counts, double* flops);
+
 void ttt_destroy(ttt_ctx* ctx);
 
 /* Message of the last error of `ctx`, or of the calling thread's last failed

@@ -1,0 +1,45 @@
+/*
+ * ttt_kernels.h -- kernel-level entry points of the MI355X TTT-E2E library,
+ * for unit tests and micro-benchmarks of single kernels.  All pointers are
+ * DEVICE pointers owned by the caller; every call is asynchronous on
+ * `stream` (hipStream_t, may be NULL) and returns 0 or a negative TTT_E* code
+ * (include/ttt.h) for a bad argument or a launch failure.  dtype is TTT_F32
+ * (fp32 operands, SIMT kernels) or TTT_BF16 (bf16 operands, matrix cores).
+ */
+#ifndef TTT_KERNELS_H
+#define TTT_KERNELS_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* C[m][n] = sum_k A[m][k] * B[n][k]  (y = x W^T with W stored [out, in]);
+ * A [M][lda], B [N][ldb] row-major in dtype, C fp32 [M][ldc]. */
+int tttk_gemm(int dtype, const void* A, int64_t lda, const void* B, int64_t ldb, float* C, int64_t ldc, int32_t M,
+              int32_t N, int32_t K, void* stream);
+
+/* Sliding-window attention of n queries per (row, head) at absolute
+ * positions pos0 .. pos0+n-1 over the key/value ring (page "TTT-E2E 如何让大模型
+ * 边用边学", §4.2: the key/value cache holds only the window): query t sees
+ * keys t-window < s <= t, s >= 0, key s at ring slot s mod R.
+ * q [B][H][n][hd] (rotated), kr, vr [B][H][R][hd], vtr [B][H][hd][R] (V
+ * transposed), o [B*n][H*hd], lse [B][H][n] fp32 (natural log) or NULL.
+ * Scale 1/sqrt(hd). */
+int tttk_swa_fwd(int dtype, const void* q, const void* kr, const void* vr, const void* vtr, void* o, float* lse,
+                 int32_t B, int32_t H, int32_t hd, int32_t n, int32_t R, int32_t window, int64_t pos0, void* stream);
+
+/* Backward of tttk_swa_fwd for a chunk whose keys are ring slots of
+ * positions pos0 .. pos0+n-1; keys before pos0 are constants (same page,
+ * §8 Q1).  qt [B][H][hd][n] (q transposed), o, dout [B*n][H*hd] in dtype,
+ * lse from the forward, dvec scratch [B][H][n]; outputs dq, dk, dv fp32
+ * [B*n][H*hd] (dk, dv for the chunk's own keys only). */
+int tttk_swa_bwd(int dtype, const void* q, const void* qt, const void* kr, const void* vr, const void* vtr,
+                 const void* o, const void* dout, const float* lse, float* dvec, float* dq, float* dk, float* dv,
+                 int32_t B, int32_t H, int32_t hd, int32_t n, int32_t R, int32_t window, int64_t pos0, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

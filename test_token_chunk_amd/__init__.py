@@ -23,7 +23,9 @@ _NAMES = {-1: "TTT_EINVAL", -2: "TTT_ENOMEM", -3: "TTT_EDEVICE", -4: "TTT_ESTATE
 
 # every symbol include/ttt.h declares
 EXPORTS = ("ttt_set_allocator", "ttt_create", "ttt_prefill_chunk", "ttt_prefill", "ttt_prefill_device", "ttt_sync",
-           "ttt_generate", "ttt_get_fast_weights", "ttt_reset", "ttt_position", "ttt_destroy", "ttt_last_error")
+           "ttt_generate", "ttt_get_fast_weights", "ttt_reset", "ttt_position", "ttt_destroy", "ttt_last_error",
+           "ttt_profile_enable", "ttt_profile_read")
+PROFILE_CLASSES = ("gemm", "swa_fwd", "swa_bwd")
 
 
 class TTTError(RuntimeError):
@@ -78,6 +80,8 @@ def load_library():
     lib.ttt_position.restype = i64
     lib.ttt_destroy.argtypes = [vp]
     lib.ttt_destroy.restype = None
+    lib.ttt_profile_enable.argtypes = [vp, i32]
+    lib.ttt_profile_read.argtypes = [vp, i32, vp, vp, vp]
     lib.ttt_last_error.argtypes = [vp]
     lib.ttt_last_error.restype = ctypes.c_char_p
     _lib = lib
@@ -255,3 +259,85 @@ class TTTContext:
 
     def reset(self):
         self._check(self._lib.ttt_reset(self._h))
+
+    def profile_begin(self):
+        """Start timing every GEMM / attention launch with HIP events."""
+        self._check(self._lib.ttt_profile_enable(self._h, 1))
+        return True
+
+    def profile_end(self, _token=None) -> dict:
+        """Stop timing; {class: {"ms", "count", "flops"}} since profile_begin."""
+        n = len(PROFILE_CLASSES)
+        ms = np.zeros(n, dtype=np.float64)
+        cnt = np.zeros(n, dtype=np.int64)
+        fl = np.zeros(n, dtype=np.float64)
+        self._check(self._lib.ttt_profile_read(self._h, n, ms.ctypes.data, cnt.ctypes.data, fl.ctypes.data))
+        self._check(self._lib.ttt_profile_enable(self._h, 0))
+        return {name: {"ms": float(ms[i]), "count": int(cnt[i]), "flops": float(fl[i])}
+                for i, name in enumerate(PROFILE_CLASSES) if cnt[i] > 0}
+
+
+# ---------------------------------------------------------------- kernel level
+KERNEL_EXPORTS = ("tttk_gemm", "tttk_swa_fwd", "tttk_swa_bwd")
+
+
+def _klib():
+    lib = load_library()
+    if not getattr(lib, "_k_ready", False):
+        vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+        lib.tttk_gemm.argtypes = [ctypes.c_int, vp, i64, vp, i64, vp, i64, i32, i32, i32, vp]
+        lib.tttk_swa_fwd.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i64, vp]
+        lib.tttk_swa_bwd.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                     i32, i32, i32, i32, i32, i32, i64, vp]
+        lib._k_ready = True
+    return lib
+
+
+def _dt(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return TTT_BF16
+    if t.dtype == torch.float32:
+        return TTT_F32
+    raise TypeError(t.dtype)
+
+
+def _p(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _stream():
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def gemm(A, B, C=None):
+    """C (fp32) = A @ B.T for CUDA tensors A [M,K], B [N,K] (bf16 or fp32, row-major)."""
+    import torch
+    M, K = A.shape
+    N = B.shape[0]
+    if C is None:
+        C = torch.empty(M, N, dtype=torch.float32, device=A.device)
+    rc = _klib().tttk_gemm(_dt(A), _p(A), A.stride(0), _p(B), B.stride(0), _p(C), C.stride(0), M, N, K, _stream())
+    if rc:
+        raise TTTError(rc, "tttk_gemm")
+    return C
+
+
+def swa_fwd(q, kr, vr, vtr, o, lse, pos0: int, window: int):
+    """Kernel-level sliding-window attention (see include/ttt_kernels.h)."""
+    B, H, n, hd = q.shape
+    R = kr.shape[2]
+    rc = _klib().tttk_swa_fwd(_dt(q), _p(q), _p(kr), _p(vr), _p(vtr), _p(o), _p(lse), B, H, hd, n, R, window, pos0,
+                              _stream())
+    if rc:
+        raise TTTError(rc, "tttk_swa_fwd")
+
+
+def swa_bwd(q, qt, kr, vr, vtr, o, dout, lse, dvec, dq, dk, dv, pos0: int, window: int):
+    B, H, n, hd = q.shape
+    R = kr.shape[2]
+    rc = _klib().tttk_swa_bwd(_dt(q), _p(q), _p(qt), _p(kr), _p(vr), _p(vtr), _p(o), _p(dout), _p(lse), _p(dvec),
+                              _p(dq), _p(dk), _p(dv), B, H, hd, n, R, window, pos0, _stream())
+    if rc:
+        raise TTTError(rc, "tttk_swa_bwd")

@@ -102,6 +102,17 @@ struct ttt_ctx {
   float* pending_loss = nullptr;  // device losses of async work, checked by ttt_sync
   int64_t pending_n = 0;
 
+  // per-kernel-class device time (HIP events around each launch) while profiling is on
+  bool prof = false;
+  std::vector<hipEvent_t> ev_pool;
+  size_t ev_used = 0;
+  struct ProfRec {
+    int cls;
+    double flops;
+    hipEvent_t a, b;
+  };
+  std::vector<ProfRec> prof_recs;
+
   void* alloc(size_t bytes) {
     if (bytes == 0) bytes = 256;
     void* p = nullptr;
@@ -142,31 +153,78 @@ int fail(ttt_ctx* c, int code, const std::string& msg) {
     if (e_ != hipSuccess) return fail(c, TTT_EDEVICE, std::string(#expr) + ": " + hipGetErrorString(e_)); \
   } while (0)
 
+// ------------------------------------------------------------------ profiling
+enum { PC_GEMM = 0, PC_SWA_FWD = 1, PC_SWA_BWD = 2, PC_CE = 3, PC_N = 4 };
+
+hipEvent_t next_event(ttt_ctx* c) {
+  if (c->ev_used == c->ev_pool.size()) {
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    c->ev_pool.push_back(e);
+  }
+  return c->ev_pool[c->ev_used++];
+}
+
+// run `launch` (returns hipError_t); with profiling on, bracket it with events
+template <typename F>
+hipError_t timed(ttt_ctx* c, int cls, double flops, F&& launch) {
+  if (!c->prof) return launch();
+  hipEvent_t a = next_event(c), b = next_event(c);
+  if (!a || !b) return hipErrorOutOfMemory;
+  hipError_t e = hipEventRecord(a, c->stream);
+  if (e != hipSuccess) return e;
+  e = launch();
+  if (e != hipSuccess) return e;
+  e = hipEventRecord(b, c->stream);
+  c->prof_recs.push_back({cls, flops, a, b});
+  return e;
+}
+
+double attn_pairs(const ttt_ctx* c, int n, int64_t p0) {
+  double s = 0;
+  for (int t = 0; t < n; ++t) s += (double)std::min<int64_t>(c->k, p0 + t + 1);
+  return s;
+}
+
 // ------------------------------------------------------------------ dispatch
 
 template <typename T>
 struct Ops;
 
+double gemm_flops(const GemmArgs& g) {
+  return 2.0 * g.M * g.N * g.K * g.batch * (g.e.kind == EPI_SWIGLU ? 2 : 1);
+}
+
 template <>
 struct Ops<float> {
-  static hipError_t gemm(ttt_ctx* c, const GemmArgs& g) { return gemm_simt_f32(g, c->stream); }
-  static hipError_t fwd(ttt_ctx* c, const AttnArgs& a) { return swa_fwd_simt<float>(a, c->stream); }
-  static hipError_t bwd(ttt_ctx* c, const AttnBwdArgs& a) { return swa_bwd_simt<float>(a, c->stream); }
+  static hipError_t gemm(ttt_ctx* c, const GemmArgs& g) {
+    return timed(c, PC_GEMM, gemm_flops(g), [&] { return gemm_simt_f32(g, c->stream); });
+  }
+  static hipError_t fwd(ttt_ctx* c, const AttnArgs& a) {
+    double fl = 4.0 * a.hd * a.H * a.B * attn_pairs(c, a.n, a.pos0);
+    return timed(c, PC_SWA_FWD, fl, [&] { return swa_fwd_simt<float>(a, c->stream); });
+  }
+  static hipError_t bwd(ttt_ctx* c, const AttnBwdArgs& a) {
+    double fl = 4.0 * a.hd * a.H * a.B * (attn_pairs(c, a.n, a.pos0) + 0.5 * a.n * (a.n + 1.0));
+    return timed(c, PC_SWA_BWD, fl, [&] { return swa_bwd_simt<float>(a, c->stream); });
+  }
 };
 
 template <>
 struct Ops<bf16> {
   static hipError_t gemm(ttt_ctx* c, const GemmArgs& g) {
-    if (c->mfma) return gemm_mfma_bf16(g, c->stream);
-    return gemm_simt_bf16(g, c->stream);
+    return timed(c, PC_GEMM, gemm_flops(g),
+                 [&] { return c->mfma ? gemm_mfma_bf16(g, c->stream) : gemm_simt_bf16(g, c->stream); });
   }
   static hipError_t fwd(ttt_ctx* c, const AttnArgs& a) {
-    if (c->mfma) return swa_fwd_mfma(a, c->stream);
-    return swa_fwd_simt<bf16>(a, c->stream);
+    double fl = 4.0 * a.hd * a.H * a.B * attn_pairs(c, a.n, a.pos0);
+    return timed(c, PC_SWA_FWD, fl,
+                 [&] { return c->mfma ? swa_fwd_mfma(a, c->stream) : swa_fwd_simt<bf16>(a, c->stream); });
   }
   static hipError_t bwd(ttt_ctx* c, const AttnBwdArgs& a) {
-    if (c->mfma) return swa_bwd_mfma(a, c->stream);
-    return swa_bwd_simt<bf16>(a, c->stream);
+    double fl = 4.0 * a.hd * a.H * a.B * (attn_pairs(c, a.n, a.pos0) + 0.5 * a.n * (a.n + 1.0));
+    return timed(c, PC_SWA_BWD, fl,
+                 [&] { return c->mfma ? swa_bwd_mfma(a, c->stream) : swa_bwd_simt<bf16>(a, c->stream); });
   }
 };
 
@@ -818,9 +876,38 @@ int ttt_create(const ttt_config* cfg, const ttt_weights* w, void* hip_stream, tt
   return TTT_OK;
 }
 
+int ttt_profile_enable(ttt_ctx* c, int32_t on) {
+  if (!c) return TTT_EINVAL;
+  CK(hipStreamSynchronize(c->stream));
+  c->prof = on != 0;
+  c->prof_recs.clear();
+  c->ev_used = 0;
+  return TTT_OK;
+}
+
+int ttt_profile_read(ttt_ctx* c, int32_t n_classes, double* ms, int64_t* counts, double* flops) {
+  if (!c || n_classes < 0 || (n_classes > 0 && (!ms || !counts || !flops))) return TTT_EINVAL;
+  CK(hipStreamSynchronize(c->stream));
+  for (int i = 0; i < n_classes; ++i) {
+    ms[i] = 0;
+    counts[i] = 0;
+    flops[i] = 0;
+  }
+  for (const auto& r : c->prof_recs) {
+    if (r.cls >= n_classes) continue;
+    float t = 0.f;
+    CK(hipEventElapsedTime(&t, r.a, r.b));
+    ms[r.cls] += t;
+    counts[r.cls] += 1;
+    flops[r.cls] += r.flops;
+  }
+  return TTT_OK;
+}
+
 void ttt_destroy(ttt_ctx* c) {
   if (!c) return;
   (void)hipStreamSynchronize(c->stream);
+  for (hipEvent_t e : c->ev_pool) (void)hipEventDestroy(e);
   c->release_all();
   delete c;
 }

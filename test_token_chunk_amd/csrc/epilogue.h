@@ -11,9 +11,9 @@ __device__ __forceinline__ float epi_exp(float x) {
     return __expf(x);
 }
 
-template <typename T>
-__device__ __forceinline__ void epi_apply(const Epi& e, int bz, int m, int n, float acc) {
-  switch (e.kind) {
+template <typename T, int KIND>
+__device__ __forceinline__ void epi_apply_k(const Epi& e, int bz, int m, int n, float acc) {
+  switch (KIND) {
     case EPI_F32:
       ((float*)e.c)[bz * e.sc + (int64_t)m * e.ldc + n] = acc;
       break;
@@ -52,6 +52,18 @@ __device__ __forceinline__ void epi_apply(const Epi& e, int bz, int m, int n, fl
     }
     default:
       break;
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void epi_apply(const Epi& e, int bz, int m, int n, float acc) {
+  switch (e.kind) {
+    case EPI_F32: epi_apply_k<T, EPI_F32>(e, bz, m, n, acc); break;
+    case EPI_T: epi_apply_k<T, EPI_T>(e, bz, m, n, acc); break;
+    case EPI_ADD_F32: epi_apply_k<T, EPI_ADD_F32>(e, bz, m, n, acc); break;
+    case EPI_SWIGLU_BWD: epi_apply_k<T, EPI_SWIGLU_BWD>(e, bz, m, n, acc); break;
+    case EPI_SGD: epi_apply_k<T, EPI_SGD>(e, bz, m, n, acc); break;
+    default: break;
   }
 }
 
