@@ -143,7 +143,8 @@ def main():
         flops_per_launch = st["flops"] / max(st["count"], 1)
         avg_s = st["ms"] / max(st["count"], 1) / 1e3
         achieved = flops_per_launch / avg_s / 1e12
-        roof = {"kernel": name, "bound": "mfma", "achieved": round(achieved, 1), "peak": peak / 1e12,
+        from test_token_chunk_amd import PROFILE_KERNELS
+        roof = {"kernel": name, "symbol": PROFILE_KERNELS.get(name, name), "bound": "mfma", "achieved": round(achieved, 1), "peak": peak / 1e12,
                 "unit": "TFLOP/s", "frac": round(achieved / (peak / 1e12), 4), "traffic": None,
                 "avg_launch_us": round(avg_s * 1e6, 2), "launches_per_step": st["count"] // args.steps}
     out = {

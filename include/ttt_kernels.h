@@ -15,10 +15,15 @@
 extern "C" {
 #endif
 
+/* Every call takes an optional fp32 workspace (ws, ws_floats; NULL/0 for none): with
+ * one, launches whose grid would under-fill the GPU split their reduction dimension
+ * (K of a GEMM, the key range of attention) over more blocks and sum the parts in a
+ * fixed order afterwards.  Calls that share a workspace must not overlap. */
+
 /* C[m][n] = sum_k A[m][k] * B[n][k]  (y = x W^T with W stored [out, in]);
  * A [M][lda], B [N][ldb] row-major in dtype, C fp32 [M][ldc]. */
 int tttk_gemm(int dtype, const void* A, int64_t lda, const void* B, int64_t ldb, float* C, int64_t ldc, int32_t M,
-              int32_t N, int32_t K, void* stream);
+              int32_t N, int32_t K, float* ws, int64_t ws_floats, void* stream);
 
 /* Sliding-window attention of n queries per (row, head) at absolute
  * positions pos0 .. pos0+n-1 over the key/value ring (page "TTT-E2E 如何让大模型
@@ -28,7 +33,8 @@ int tttk_gemm(int dtype, const void* A, int64_t lda, const void* B, int64_t ldb,
  * transposed), o [B*n][H*hd], lse [B][H][n] fp32 (natural log) or NULL.
  * Scale 1/sqrt(hd). */
 int tttk_swa_fwd(int dtype, const void* q, const void* kr, const void* vr, const void* vtr, void* o, float* lse,
-                 int32_t B, int32_t H, int32_t hd, int32_t n, int32_t R, int32_t window, int64_t pos0, void* stream);
+                 int32_t B, int32_t H, int32_t hd, int32_t n, int32_t R, int32_t window, int64_t pos0, float* ws,
+                 int64_t ws_floats, void* stream);
 
 /* Backward of tttk_swa_fwd for a chunk whose keys are ring slots of
  * positions pos0 .. pos0+n-1; keys before pos0 are constants (same page,
@@ -37,7 +43,8 @@ int tttk_swa_fwd(int dtype, const void* q, const void* kr, const void* vr, const
  * [B*n][H*hd] (dk, dv for the chunk's own keys only). */
 int tttk_swa_bwd(int dtype, const void* q, const void* qt, const void* kr, const void* vr, const void* vtr,
                  const void* o, const void* dout, const float* lse, float* dvec, float* dq, float* dk, float* dv,
-                 int32_t B, int32_t H, int32_t hd, int32_t n, int32_t R, int32_t window, int64_t pos0, void* stream);
+                 int32_t B, int32_t H, int32_t hd, int32_t n, int32_t R, int32_t window, int64_t pos0, float* ws,
+                 int64_t ws_floats, void* stream);
 
 #ifdef __cplusplus
 }

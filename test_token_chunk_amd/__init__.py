@@ -25,7 +25,13 @@ _NAMES = {-1: "TTT_EINVAL", -2: "TTT_ENOMEM", -3: "TTT_EDEVICE", -4: "TTT_ESTATE
 EXPORTS = ("ttt_set_allocator", "ttt_create", "ttt_prefill_chunk", "ttt_prefill", "ttt_prefill_device", "ttt_sync",
            "ttt_generate", "ttt_get_fast_weights", "ttt_reset", "ttt_position", "ttt_destroy", "ttt_last_error",
            "ttt_profile_enable", "ttt_profile_read")
-PROFILE_CLASSES = ("gemm", "swa_fwd", "swa_bwd")
+PROFILE_CLASSES = ("gemm_f32out", "gemm_bf16out", "gemm_resid", "gemm_swiglu", "gemm_swiglu_bwd", "gemm_sgd",
+                   "swa_fwd", "swa_bwd")
+# kernel symbol of each class (as rocprofv3 names it), for the roofline cross-check
+PROFILE_KERNELS = {"gemm_f32out": "k_gemm_mfma<*, false, 0>", "gemm_bf16out": "k_gemm_mfma<*, false, 1>",
+                   "gemm_resid": "k_gemm_mfma<*, false, 2>", "gemm_swiglu": "k_gemm_mfma<*, true, 3>",
+                   "gemm_swiglu_bwd": "k_gemm_mfma<*, false, 4>", "gemm_sgd": "k_gemm_mfma<*, false, 5>",
+                   "swa_fwd": "k_swa_fwd<hd>", "swa_bwd": "k_dvec + k_swa_dq<hd> + k_swa_dkv<hd>"}
 
 
 class TTTError(RuntimeError):
@@ -285,10 +291,11 @@ def _klib():
     lib = load_library()
     if not getattr(lib, "_k_ready", False):
         vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
-        lib.tttk_gemm.argtypes = [ctypes.c_int, vp, i64, vp, i64, vp, i64, i32, i32, i32, vp]
-        lib.tttk_swa_fwd.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i64, vp]
+        lib.tttk_gemm.argtypes = [ctypes.c_int, vp, i64, vp, i64, vp, i64, i32, i32, i32, vp, i64, vp]
+        lib.tttk_swa_fwd.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i64, vp, i64,
+                                     vp]
         lib.tttk_swa_bwd.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
-                                     i32, i32, i32, i32, i32, i32, i64, vp]
+                                     i32, i32, i32, i32, i32, i32, i64, vp, i64, vp]
         lib._k_ready = True
     return lib
 
@@ -311,33 +318,38 @@ def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
-def gemm(A, B, C=None):
-    """C (fp32) = A @ B.T for CUDA tensors A [M,K], B [N,K] (bf16 or fp32, row-major)."""
+def _ws(ws):
+    return (_p(ws), ws.numel()) if ws is not None else (None, 0)
+
+
+def gemm(A, B, C=None, ws=None):
+    """C (fp32) = A @ B.T for CUDA tensors A [M,K], B [N,K] (bf16 or fp32, row-major); ws: fp32 workspace."""
     import torch
     M, K = A.shape
     N = B.shape[0]
     if C is None:
         C = torch.empty(M, N, dtype=torch.float32, device=A.device)
-    rc = _klib().tttk_gemm(_dt(A), _p(A), A.stride(0), _p(B), B.stride(0), _p(C), C.stride(0), M, N, K, _stream())
+    rc = _klib().tttk_gemm(_dt(A), _p(A), A.stride(0), _p(B), B.stride(0), _p(C), C.stride(0), M, N, K, *_ws(ws),
+                           _stream())
     if rc:
         raise TTTError(rc, "tttk_gemm")
     return C
 
 
-def swa_fwd(q, kr, vr, vtr, o, lse, pos0: int, window: int):
+def swa_fwd(q, kr, vr, vtr, o, lse, pos0: int, window: int, ws=None):
     """Kernel-level sliding-window attention (see include/ttt_kernels.h)."""
     B, H, n, hd = q.shape
     R = kr.shape[2]
     rc = _klib().tttk_swa_fwd(_dt(q), _p(q), _p(kr), _p(vr), _p(vtr), _p(o), _p(lse), B, H, hd, n, R, window, pos0,
-                              _stream())
+                              *_ws(ws), _stream())
     if rc:
         raise TTTError(rc, "tttk_swa_fwd")
 
 
-def swa_bwd(q, qt, kr, vr, vtr, o, dout, lse, dvec, dq, dk, dv, pos0: int, window: int):
+def swa_bwd(q, qt, kr, vr, vtr, o, dout, lse, dvec, dq, dk, dv, pos0: int, window: int, ws=None):
     B, H, n, hd = q.shape
     R = kr.shape[2]
     rc = _klib().tttk_swa_bwd(_dt(q), _p(q), _p(qt), _p(kr), _p(vr), _p(vtr), _p(o), _p(dout), _p(lse), _p(dvec),
-                              _p(dq), _p(dk), _p(dv), B, H, hd, n, R, window, pos0, _stream())
+                              _p(dq), _p(dk), _p(dv), B, H, hd, n, R, window, pos0, *_ws(ws), _stream())
     if rc:
         raise TTTError(rc, "tttk_swa_bwd")

@@ -11,7 +11,11 @@
 // MFMA's k index is permuted so that k-slot e of lane group g (= l/32) of
 // the 16-key step h is key 16h + 8(e/4) + 4g + e%4, which is exactly the C
 // register 8h + e of S^T.  V^T tiles come from the transposed value ring.
+#include <algorithm>
+
 #include "kernels.h"
+
+hipError_t swa_dvec_bf16(const AttnBwdArgs& a, hipStream_t s);
 
 namespace {
 
@@ -30,22 +34,31 @@ struct FwdSmem {
   bf16 vt[2][HD][KT + 8];  // V^T tile, row = head dim
 };
 
+// two floats -> packed bf16 pair, round to nearest even (one v_cvt_pk_bf16_f32 on gfx950)
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pk2(float a, float b) {
-  return (uint32_t)f2bf(a).x | ((uint32_t)f2bf(b).x << 16);
+  bf16x2 v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
-template <int HD>
-__global__ __launch_bounds__(256) void k_swa_fwd(AttnArgs a) {
+// SPLIT: blockIdx.z = b * S + split; the block covers only its share of the key tiles
+// and writes unnormalized O, the running max (raw score units) and the exp-sum to the
+// workspace: O [S][B][H][n][hd], m [S][B][H][n], l [S][B][H][n].
+template <int HD, int NW, bool SPLIT = false>
+__global__ __launch_bounds__(NW * 64) void k_swa_fwd(AttnArgs a, int S) {
+  constexpr int NT = NW * 64;  // threads per block
+  constexpr int BQ = NW * QW;  // queries per block
   constexpr int KS = HD / 16;               // MFMA k-steps over the head dim
   constexpr int HM = HD / 32;               // 32-row tiles of the head dim
-  constexpr int KCH = KT * HD / 8 / 256;    // 16-byte chunks of the K tile per thread
-  constexpr int VCH = HD * KT / 8 / 256;    // same for the V^T tile
-  static_assert(KCH <= 4 && VCH <= 4 && KT * HD % 2048 == 0, "tile staging covers HD <= 128");
+  constexpr int KCH = (KT * HD / 8 + NT - 1) / NT;  // 16-byte chunks of the K tile per thread
+  constexpr int VCH = (HD * KT / 8 + NT - 1) / NT;  // same for the V^T tile
+  static_assert(KCH <= 4 && VCH <= 4, "tile staging covers HD <= 128");
   extern __shared__ __align__(16) unsigned char smem_raw[];
   FwdSmem<HD>& sm = *reinterpret_cast<FwdSmem<HD>*>(smem_raw);
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int b = blockIdx.z, h = blockIdx.y;
+  const int b = SPLIT ? blockIdx.z / S : blockIdx.z, h = blockIdx.y;
+  const int sp = SPLIT ? blockIdx.z % S : 0;
   const int64_t bh = (int64_t)b * a.H + h;
   const int R = a.R;
   const int t0 = blockIdx.x * BQ;               // first local query of the block
@@ -53,6 +66,9 @@ __global__ __launch_bounds__(256) void k_swa_fwd(AttnArgs a) {
   const bool qok = tq < a.n;
   const int64_t qpos = a.pos0 + tq;
   const int g = lane >> 5;
+  const int tw0 = t0 + wid * QW;                  // first query of this wave
+  const bool wfull = tw0 + QW <= a.n;             // all 32 queries of the wave exist
+  const int64_t wpos_lo = a.pos0 + tw0, wpos_hi = wpos_lo + QW - 1;
 
   const bf16* Kr = (const bf16*)a.kr + bh * R * HD;
   const bf16* Vt = (const bf16*)a.vtr + bh * HD * R;
@@ -78,7 +94,10 @@ __global__ __launch_bounds__(256) void k_swa_fwd(AttnArgs a) {
   const int64_t kbeg = max((int64_t)0, a.pos0 + t0 - a.window + 1);
   const int64_t kend = a.pos0 + tlast;
   const int64_t ktile0 = (kbeg / KT) * KT;
-  const int ntiles = (int)((kend - ktile0) / KT) + 1;
+  const int ntiles_all = (int)((kend - ktile0) / KT) + 1;
+  const int per = SPLIT ? (ntiles_all + S - 1) / S : ntiles_all;
+  const int it_beg = SPLIT ? min(ntiles_all, sp * per) : 0;
+  const int ntiles = SPLIT ? min(ntiles_all, it_beg + per) : ntiles_all;  // loop end
 
   // global -> register staging of the next tile (named registers: at most 4 + 4 chunks)
   uint4 rk0, rk1, rk2, rk3, rv0, rv1, rv2, rv3;
@@ -88,13 +107,13 @@ __global__ __launch_bounds__(256) void k_swa_fwd(AttnArgs a) {
   // tiles and R % 8 == 0 keep every 8-key group inside the ring)
 #define LOADK(i, dst)                                                              \
   if constexpr (KCH > i) {                                                         \
-    const int c = tid + i * 256, r = c / (HD / 8), col = (c % (HD / 8)) * 8;       \
-    dst = *(const uint4*)(Kr + (int64_t)((slot0 + r) % R) * HD + col);            \
+    const int c = tid + i * NT, r = c / (HD / 8), col = (c % (HD / 8)) * 8;        \
+    if (c < KT * HD / 8) dst = *(const uint4*)(Kr + (int64_t)((slot0 + r) % R) * HD + col); \
   }
 #define LOADV(i, dst)                                                              \
   if constexpr (VCH > i) {                                                         \
-    const int c = tid + i * 256, r = c / (KT / 8), col = (c % (KT / 8)) * 8;       \
-    dst = *(const uint4*)(Vt + (int64_t)r * R + (slot0 + col) % R);               \
+    const int c = tid + i * NT, r = c / (KT / 8), col = (c % (KT / 8)) * 8;        \
+    if (c < KT * HD / 8) dst = *(const uint4*)(Vt + (int64_t)r * R + (slot0 + col) % R); \
   }
 #define LOAD_TILE(it_)                                                             \
   {                                                                                \
@@ -104,13 +123,13 @@ __global__ __launch_bounds__(256) void k_swa_fwd(AttnArgs a) {
   }
 #define STK(i, src)                                                                \
   if constexpr (KCH > i) {                                                         \
-    const int c = tid + i * 256, r = c / (HD / 8), col = (c % (HD / 8)) * 8;       \
-    *(uint4*)&sm.k[buf][r][col] = src;                                             \
+    const int c = tid + i * NT, r = c / (HD / 8), col = (c % (HD / 8)) * 8;        \
+    if (c < KT * HD / 8) *(uint4*)&sm.k[buf][r][col] = src;                        \
   }
 #define STV(i, src)                                                                \
   if constexpr (VCH > i) {                                                         \
-    const int c = tid + i * 256, r = c / (KT / 8), col = (c % (KT / 8)) * 8;       \
-    *(uint4*)&sm.vt[buf][r][col] = src;                                            \
+    const int c = tid + i * NT, r = c / (KT / 8), col = (c % (KT / 8)) * 8;        \
+    if (c < KT * HD / 8) *(uint4*)&sm.vt[buf][r][col] = src;                       \
   }
 #define STORE_TILE(buf_)                                                           \
   {                                                                                \
@@ -125,10 +144,12 @@ __global__ __launch_bounds__(256) void k_swa_fwd(AttnArgs a) {
   float mrun = -INFINITY, lrun = 0.f;
   const float sl2 = 1.4426950408889634f / sqrtf((float)HD);  // log2(e) / sqrt(hd)
 
-  LOAD_TILE(0)
-  STORE_TILE(0)
+  if (it_beg < ntiles) {
+    LOAD_TILE(it_beg)
+    STORE_TILE(it_beg & 1)
+  }
   __syncthreads();
-  for (int it = 0; it < ntiles; ++it) {
+  for (int it = it_beg; it < ntiles; ++it) {
     const int cur = it & 1;
     if (it + 1 < ntiles) LOAD_TILE(it + 1)
     const int64_t kp0 = ktile0 + (int64_t)it * KT;
@@ -147,31 +168,34 @@ __global__ __launch_bounds__(256) void k_swa_fwd(AttnArgs a) {
       SSTEP(0, q0) SSTEP(1, q1) SSTEP(2, q2) SSTEP(3, q3) SSTEP(4, q4) SSTEP(5, q5) SSTEP(6, q6) SSTEP(7, q7)
 #undef SSTEP
     }
-    // mask + scale; register 4j+i of half mt holds key kp0 + 32 mt + 8 j + 4 g + i.
-    // Visible: qpos - window < key <= qpos, i.e. lo < off <= hi with off = key - kp0.
-    const int64_t hi64 = qpos - kp0, lo64 = qpos - a.window - kp0;
-    const int hi = qok ? (int)min<int64_t>(max<int64_t>(hi64, -1), 64) : -1;
-    const int lo = (int)min<int64_t>(max<int64_t>(lo64, -2), 64);
+    // register 4j+i of half mt holds key kp0 + 32 mt + 8 j + 4 g + i.  Visible keys:
+    // qpos - window < key <= qpos.  Only tiles that cut a window edge for some query of
+    // this wave (or waves with out-of-range queries) need the per-element mask.
+    const bool full = wfull && kp0 >= wpos_hi - a.window + 1 && kp0 + KT - 1 <= wpos_lo;
+    if (!full) {
+      const int64_t hi64 = qpos - kp0, lo64 = qpos - a.window - kp0;
+      const int hi = qok ? (int)min<int64_t>(max<int64_t>(hi64, -1), 64) : -1;
+      const int lo = (int)min<int64_t>(max<int64_t>(lo64, -2), 64);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int off = 8 * (r >> 2) + 4 * g + (r & 3);
+        if (!(off <= hi && off > lo)) s0[r] = -INFINITY;
+        if (!(off + 32 <= hi && off + 32 > lo)) s1[r] = -INFINITY;
+      }
+    }
     float tmax = -INFINITY;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int off = 8 * (r >> 2) + 4 * g + (r & 3);
-      float v0 = (off <= hi && off > lo) ? s0[r] * sl2 : -INFINITY;
-      float v1 = (off + 32 <= hi && off + 32 > lo) ? s1[r] * sl2 : -INFINITY;
-      s0[r] = v0;
-      s1[r] = v1;
-      tmax = fmaxf(tmax, fmaxf(v0, v1));
-    }
+    for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, fmaxf(s0[r], s1[r]));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    const float mnew = fmaxf(mrun, tmax);
-    const float msafe = mnew == -INFINITY ? 0.f : mnew;
-    const float corr = exp2f(mrun - msafe);
+    const float mnew = fmaxf(mrun, tmax);  // raw score units
+    const float nb = mnew == -INFINITY ? 0.f : -mnew * sl2;
+    const float corr = exp2f(fmaf(mrun, sl2, nb));
     float psum = 0.f;
     uint32_t pa[8], pb[8];
 #pragma unroll
     for (int r = 0; r < 16; r += 2) {
-      float p0 = exp2f(s0[r] - msafe), p1 = exp2f(s0[r + 1] - msafe);
-      float q0 = exp2f(s1[r] - msafe), q1 = exp2f(s1[r + 1] - msafe);
+      float p0 = exp2f(fmaf(s0[r], sl2, nb)), p1 = exp2f(fmaf(s0[r + 1], sl2, nb));
+      float q0 = exp2f(fmaf(s1[r], sl2, nb)), q1 = exp2f(fmaf(s1[r + 1], sl2, nb));
       psum += (p0 + p1) + (q0 + q1);
       pa[r >> 1] = pk2(p0, p1);
       pb[r >> 1] = pk2(q0, q1);
@@ -179,8 +203,10 @@ __global__ __launch_bounds__(256) void k_swa_fwd(AttnArgs a) {
     psum += __shfl_xor(psum, 32, 64);
     lrun = lrun * corr + psum;
     mrun = mnew;
+    if (__any(corr != 1.f)) {
 #pragma unroll
-    for (int i = 0; i < HM; ++i) o[i] *= corr;
+      for (int i = 0; i < HM; ++i) o[i] *= corr;
+    }
     // O^T += V^T P^T, four 16-key steps (keys 0-15, 16-31 of each half)
     const bf16x8 pf[4] = {__builtin_bit_cast(bf16x8, make_uint4(pa[0], pa[1], pa[2], pa[3])),
                           __builtin_bit_cast(bf16x8, make_uint4(pa[4], pa[5], pa[6], pa[7])),
@@ -209,6 +235,24 @@ __global__ __launch_bounds__(256) void k_swa_fwd(AttnArgs a) {
 #undef STV
 #undef STORE_TILE
   if (!qok) return;
+  if constexpr (SPLIT) {
+    const int64_t row = ((int64_t)sp * a.B * a.H + bh) * a.n + tq;  // [S][B][H][n]
+    float* po = a.ws + row * HD;
+    float* pm = a.ws + (int64_t)S * a.B * a.H * a.n * HD;
+    float* pl = pm + (int64_t)S * a.B * a.H * a.n;
+#pragma unroll
+    for (int hm = 0; hm < HM; ++hm)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d0 = hm * 32 + 8 * j + 4 * g;
+        *(float4*)(po + d0) = make_float4(o[hm][4 * j], o[hm][4 * j + 1], o[hm][4 * j + 2], o[hm][4 * j + 3]);
+      }
+    if (g == 0) {
+      pm[row] = mrun;
+      pl[row] = lrun;
+    }
+    return;
+  }
   const float inv = 1.f / lrun;
   bf16* out = (bf16*)a.o + ((int64_t)b * a.n + tq) * ((int64_t)a.H * HD) + (int64_t)h * HD;
 #pragma unroll
@@ -220,12 +264,35 @@ __global__ __launch_bounds__(256) void k_swa_fwd(AttnArgs a) {
                            pk2(o[hm][4 * j + 2] * inv, o[hm][4 * j + 3] * inv));
       *(uint2*)(out + d0) = w;
     }
-  if (a.lse && g == 0) a.lse[bh * a.n + tq] = (mrun + log2f(lrun)) * 0.6931471805599453f;
+  if (a.lse && g == 0) a.lse[bh * a.n + tq] = mrun * (sl2 * 0.6931471805599453f) + logf(lrun);
 }
 
-template <int HD>
-hipError_t launch_fwd(const AttnArgs& a, hipStream_t s) {
-  auto kern = k_swa_fwd<HD>;
+// merge the key-range parts of a split forward: O = sum_s w_s O_s / sum_s w_s l_s with
+// w_s = 2^((m_s - max m) * sl2); grid (n, H, B), one thread per head dim
+__global__ void k_swa_combine(AttnArgs a, int S) {
+  const int t = blockIdx.x, h = blockIdx.y, b = blockIdx.z, hd = a.hd;
+  const int64_t bh = (int64_t)b * a.H + h;
+  const int64_t plane = (int64_t)a.B * a.H * a.n;
+  const float* pm = a.ws + (int64_t)S * plane * hd;
+  const float* pl = pm + (int64_t)S * plane;
+  const float sl2 = 1.4426950408889634f / sqrtf((float)hd);
+  float M = -INFINITY;
+  for (int sidx = 0; sidx < S; ++sidx) M = fmaxf(M, pm[sidx * plane + bh * a.n + t]);
+  float L = 0.f, acc = 0.f;
+  for (int sidx = 0; sidx < S; ++sidx) {
+    const int64_t row = sidx * plane + bh * a.n + t;
+    const float w = pm[row] == -INFINITY ? 0.f : exp2f((pm[row] - M) * sl2);
+    L += w * pl[row];
+    if ((int)threadIdx.x < hd) acc += w * a.ws[row * hd + threadIdx.x];
+  }
+  if ((int)threadIdx.x < hd)
+    ((bf16*)a.o)[((int64_t)b * a.n + t) * ((int64_t)a.H * hd) + (int64_t)h * hd + threadIdx.x] = f2bf(acc / L);
+  if (a.lse && threadIdx.x == 0) a.lse[bh * a.n + t] = M * (sl2 * 0.6931471805599453f) + logf(L);
+}
+
+template <int HD, int NW, bool SPLIT>
+hipError_t launch_fwd_nw(const AttnArgs& a, int S, hipStream_t s) {
+  auto kern = k_swa_fwd<HD, NW, SPLIT>;
   size_t shm = sizeof(FwdSmem<HD>);
   static bool attr = false;
   if (!attr) {
@@ -233,8 +300,397 @@ hipError_t launch_fwd(const AttnArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
     attr = true;
   }
+  dim3 grid(cdiv(a.n, NW * QW), a.H, a.B * S);
+  hipLaunchKernelGGL(kern, grid, dim3(NW * 64), shm, s, a, S);
+  if (SPLIT) hipLaunchKernelGGL(k_swa_combine, dim3(a.n, a.H, a.B), dim3(HD), 0, s, a, S);
+  return hipGetLastError();
+}
+
+// 8 waves (256 queries) per block when there are enough query blocks to fill the chip,
+// else 4 waves (128 queries)
+// how many key-range parts give a grid of >= ~2 blocks per CU (1 when no workspace)
+int attn_splits(int64_t blocks, int64_t ntiles, int64_t need_per_split, const float* ws, int64_t ws_floats) {
+  if (!ws || blocks >= 384) return 1;
+  int S = (int)std::min<int64_t>(8, (512 + blocks - 1) / blocks);
+  S = (int)std::min<int64_t>(S, std::max<int64_t>(1, ntiles / 8));
+  while (S > 1 && S * need_per_split > ws_floats) --S;
+  return S;
+}
+
+template <int HD>
+hipError_t launch_fwd(const AttnArgs& a, hipStream_t s) {
+  const int64_t blocks8 = (int64_t)cdiv(a.n, 8 * QW) * a.H * a.B;
+  if (blocks8 >= 512) return launch_fwd_nw<HD, 8, false>(a, 1, s);
+  const int64_t blocks4 = (int64_t)cdiv(a.n, 4 * QW) * a.H * a.B;
+  const int64_t ntiles = (std::min<int64_t>(a.window, a.pos0 + 1) + 4 * QW) / KT + 1;
+  const int S = attn_splits(blocks4, ntiles, (int64_t)a.B * a.H * a.n * (HD + 2), a.ws, a.ws_floats);
+  if (S > 1) return launch_fwd_nw<HD, 4, true>(a, S, s);
+  return launch_fwd_nw<HD, 4, false>(a, 1, s);
+}
+
+
+// ---------------------------------------------------------------- backward
+//
+// dQ kernel: per wave 32 queries, loop over the 64-key tiles of the window
+// (cached keys included, as constants).  S^T = K Q^T and dP^T = V dO^T put
+// one query per lane; dS^T = P^T (dP^T - D) then feeds dQ^T += K^T dS^T from
+// registers with the same permuted k index as the forward's P V product.
+// K^T is produced in LDS by a transposing store of the K tile.
+template <int HD>
+struct DqSmem {
+  bf16 k[KT][HD + 8];
+  bf16 v[KT][HD + 8];
+  bf16 kt[HD][KT + 8];
+};
+
+// SPLIT: blockIdx.z = b * S + split over the key tiles; partial dq to ws[S][B*n][H*hd]
+template <int HD, bool SPLIT = false>
+__global__ __launch_bounds__(256) void k_swa_dq(AttnBwdArgs a, int S) {
+  constexpr int KS = HD / 16, HM = HD / 32;
+  constexpr int KCH = KT * HD / 8 / 256;
+  static_assert(KCH <= 4, "tile staging covers HD <= 128");
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  DqSmem<HD>& sm = *reinterpret_cast<DqSmem<HD>*>(smem_raw);
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, g = lane >> 5;
+  const int b = SPLIT ? blockIdx.z / S : blockIdx.z, h = blockIdx.y;
+  const int sp = SPLIT ? blockIdx.z % S : 0;
+  const int64_t bh = (int64_t)b * a.H + h;
+  const int R = a.R, d = a.H * HD;
+  const int t0 = blockIdx.x * BQ;
+  const int tq = t0 + wid * QW + (lane & 31);
+  const bool qok = tq < a.n;
+  const int64_t qpos = a.pos0 + tq;
+  const bf16* Kr = (const bf16*)a.kr + bh * R * HD;
+  const bf16* Vr = (const bf16*)a.vr + bh * R * HD;
+
+  bf16x8 q0, q1, q2, q3, q4, q5, q6, q7, e0, e1, e2, e3, e4, e5, e6, e7;
+  {
+    const bf16* q = (const bf16*)a.q + (bh * a.n + (qok ? tq : 0)) * HD + g * 8;
+    const bf16* dO = (const bf16*)a.dout + ((int64_t)b * a.n + (qok ? tq : 0)) * d + (int64_t)h * HD + g * 8;
+    auto ld8 = [&](const bf16* p, int ks) {
+      uint4 v = qok ? *(const uint4*)(p + ks * 16) : make_uint4(0, 0, 0, 0);
+      return __builtin_bit_cast(bf16x8, v);
+    };
+    q0 = ld8(q, 0); q1 = ld8(q, 1); e0 = ld8(dO, 0); e1 = ld8(dO, 1);
+    if constexpr (KS > 2) { q2 = ld8(q, 2); q3 = ld8(q, 3); e2 = ld8(dO, 2); e3 = ld8(dO, 3); }
+    if constexpr (KS > 4) { q4 = ld8(q, 4); q5 = ld8(q, 5); e4 = ld8(dO, 4); e5 = ld8(dO, 5); }
+    if constexpr (KS > 6) { q6 = ld8(q, 6); q7 = ld8(q, 7); e6 = ld8(dO, 6); e7 = ld8(dO, 7); }
+  }
+  const float LOG2E = 1.4426950408889634f;
+  const float sl2 = LOG2E / sqrtf((float)HD);
+  const float lse2 = qok ? a.lse[bh * a.n + tq] * LOG2E : 0.f;
+  const float Dq = qok ? a.dvec[bh * a.n + tq] : 0.f;
+
+  const int tlast = min(t0 + BQ, a.n) - 1;
+  const int64_t kbeg = max((int64_t)0, a.pos0 + t0 - a.window + 1);
+  const int64_t kend = a.pos0 + tlast;
+  const int64_t ktile0 = (kbeg / KT) * KT;
+  const int ntiles_all = (int)((kend - ktile0) / KT) + 1;
+  const int per = SPLIT ? (ntiles_all + S - 1) / S : ntiles_all;
+  const int it_beg = SPLIT ? min(ntiles_all, sp * per) : 0;
+  const int ntiles = SPLIT ? min(ntiles_all, it_beg + per) : ntiles_all;
+  const int sbase = (int)(ktile0 % R);
+
+  f32x16 acc[HM];
+#pragma unroll
+  for (int i = 0; i < HM; ++i) acc[i] = f32x16{};
+
+  for (int it = it_beg; it < ntiles; ++it) {
+    const int slot0 = (sbase + it * KT) % R;
+    const int64_t kp0 = ktile0 + (int64_t)it * KT;
+    // stage K (both layouts) and V
+    uint4 rk0, rk1, rk2, rk3, rv0, rv1, rv2, rv3;
+#define LD(i, dk, dv)                                                                    \
+  if constexpr (KCH > i) {                                                               \
+    const int c = tid + i * 256, r = c / (HD / 8), col = (c % (HD / 8)) * 8;             \
+    const int64_t off = (int64_t)((slot0 + r) % R) * HD + col;                           \
+    dk = *(const uint4*)(Kr + off);                                                      \
+    dv = *(const uint4*)(Vr + off);                                                      \
+  }
+    LD(0, rk0, rv0) LD(1, rk1, rv1) LD(2, rk2, rv2) LD(3, rk3, rv3)
+#undef LD
+    __syncthreads();  // previous tile fully consumed
+#define ST(i, sk, sv)                                                                    \
+  if constexpr (KCH > i) {                                                               \
+    const int c = tid + i * 256, r = c / (HD / 8), col = (c % (HD / 8)) * 8;             \
+    *(uint4*)&sm.k[r][col] = sk;                                                         \
+    *(uint4*)&sm.v[r][col] = sv;                                                         \
+    const uint16_t* e = (const uint16_t*)&sk;                                            \
+    _Pragma("unroll") for (int x = 0; x < 8; ++x) sm.kt[col + x][r].x = e[x];             \
+  }
+    ST(0, rk0, rv0) ST(1, rk1, rv1) ST(2, rk2, rv2) ST(3, rk3, rv3)
+#undef ST
+    __syncthreads();
+    f32x16 s0 = f32x16{}, s1 = f32x16{}, p0 = f32x16{}, p1 = f32x16{};
+    {
+      const bf16* k0p = &sm.k[(lane & 31)][g * 8];
+      const bf16* k1p = &sm.k[32 + (lane & 31)][g * 8];
+      const bf16* v0p = &sm.v[(lane & 31)][g * 8];
+      const bf16* v1p = &sm.v[32 + (lane & 31)][g * 8];
+#define SSTEP(ks, qv, ev)                                                                          \
+  if constexpr (KS > ks) {                                                                         \
+    s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(k0p + ks * 16), qv, s0, 0, 0, 0); \
+    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(k1p + ks * 16), qv, s1, 0, 0, 0); \
+    p0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(v0p + ks * 16), ev, p0, 0, 0, 0); \
+    p1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(v1p + ks * 16), ev, p1, 0, 0, 0); \
+  }
+      SSTEP(0, q0, e0) SSTEP(1, q1, e1) SSTEP(2, q2, e2) SSTEP(3, q3, e3)
+      SSTEP(4, q4, e4) SSTEP(5, q5, e5) SSTEP(6, q6, e6) SSTEP(7, q7, e7)
+#undef SSTEP
+    }
+    const int64_t hi64 = qpos - kp0, lo64 = qpos - a.window - kp0;
+    const int hi = qok ? (int)min<int64_t>(max<int64_t>(hi64, -1), 64) : -1;
+    const int lo = (int)min<int64_t>(max<int64_t>(lo64, -2), 64);
+    uint32_t da[8], db[8];
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      const int off = 8 * (r >> 2) + 4 * g + (r & 3);
+      float x0 = (off <= hi && off > lo) ? exp2f(s0[r] * sl2 - lse2) * (p0[r] - Dq) : 0.f;
+      float x1 = (off + 1 <= hi && off + 1 > lo) ? exp2f(s0[r + 1] * sl2 - lse2) * (p0[r + 1] - Dq) : 0.f;
+      float y0 = (off + 32 <= hi && off + 32 > lo) ? exp2f(s1[r] * sl2 - lse2) * (p1[r] - Dq) : 0.f;
+      float y1 = (off + 33 <= hi && off + 33 > lo) ? exp2f(s1[r + 1] * sl2 - lse2) * (p1[r + 1] - Dq) : 0.f;
+      da[r >> 1] = pk2(x0, x1);
+      db[r >> 1] = pk2(y0, y1);
+    }
+    const bf16x8 dsf[4] = {__builtin_bit_cast(bf16x8, make_uint4(da[0], da[1], da[2], da[3])),
+                           __builtin_bit_cast(bf16x8, make_uint4(da[4], da[5], da[6], da[7])),
+                           __builtin_bit_cast(bf16x8, make_uint4(db[0], db[1], db[2], db[3])),
+                           __builtin_bit_cast(bf16x8, make_uint4(db[4], db[5], db[6], db[7]))};
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const int kc = st * 16 + 4 * g;
+#pragma unroll
+      for (int hm = 0; hm < HM; ++hm) {
+        const bf16* row = &sm.kt[hm * 32 + (lane & 31)][0];
+        uint2 lo2 = *(const uint2*)(row + kc);
+        uint2 hi2 = *(const uint2*)(row + kc + 8);
+        bf16x8 kf = __builtin_bit_cast(bf16x8, make_uint4(lo2.x, lo2.y, hi2.x, hi2.y));
+        acc[hm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, dsf[st], acc[hm], 0, 0, 0);
+      }
+    }
+  }
+  if (!qok) return;
+  const float sc = 1.f / sqrtf((float)HD);
+  float* out = (SPLIT ? a.ws + (int64_t)sp * a.B * a.n * d : a.dq) + ((int64_t)b * a.n + tq) * d + (int64_t)h * HD;
+#pragma unroll
+  for (int hm = 0; hm < HM; ++hm)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int d0 = hm * 32 + 8 * j + 4 * g;
+      *(float4*)(out + d0) = make_float4(acc[hm][4 * j] * sc, acc[hm][4 * j + 1] * sc, acc[hm][4 * j + 2] * sc,
+                                         acc[hm][4 * j + 3] * sc);
+    }
+}
+
+// dK/dV kernel for the chunk's own keys (keys before pos0 are constants and get
+// nothing): per wave 32 keys, loop over 64-query tiles of the chunk.  S = Q K^T
+// and dP = dO V^T put one key per lane; dV^T += dO^T P and dK^T += Q^T dS with
+// the permuted k index over queries.  Q^T and dO^T come from transposing LDS stores.
+template <int HD>
+struct DkvSmem {
+  bf16 q[KT][HD + 8];
+  bf16 o[KT][HD + 8];   // dO
+  bf16 qt[HD][KT + 8];
+  bf16 ot[HD][KT + 8];  // dO^T
+  float lse2[KT];
+  float dd[KT];
+};
+
+template <int HD>
+__global__ __launch_bounds__(256) void k_swa_dkv(AttnBwdArgs a) {
+  constexpr int KS = HD / 16, HM = HD / 32;
+  constexpr int KCH = KT * HD / 8 / 256;
+  static_assert(KCH <= 4, "tile staging covers HD <= 128");
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  DkvSmem<HD>& sm = *reinterpret_cast<DkvSmem<HD>*>(smem_raw);
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, g = lane >> 5;
+  const int b = blockIdx.z, h = blockIdx.y;
+  const int64_t bh = (int64_t)b * a.H + h;
+  const int R = a.R, d = a.H * HD;
+  const int s0blk = blockIdx.x * BQ;
+  const int sk = s0blk + wid * QW + (lane & 31);  // this lane's key (chunk-local)
+  const bool kok = sk < a.n;
+  const float LOG2E = 1.4426950408889634f;
+  const float sl2 = LOG2E / sqrtf((float)HD);
+
+  bf16x8 k0, k1, k2, k3, k4, k5, k6, k7, v0, v1, v2, v3, v4, v5, v6, v7;
+  {
+    const int slot = (int)((a.pos0 + (kok ? sk : 0)) % R);
+    const bf16* kp = (const bf16*)a.kr + (bh * R + slot) * HD + g * 8;
+    const bf16* vp = (const bf16*)a.vr + (bh * R + slot) * HD + g * 8;
+    auto ld8 = [&](const bf16* p, int ks) {
+      uint4 v = kok ? *(const uint4*)(p + ks * 16) : make_uint4(0, 0, 0, 0);
+      return __builtin_bit_cast(bf16x8, v);
+    };
+    k0 = ld8(kp, 0); k1 = ld8(kp, 1); v0 = ld8(vp, 0); v1 = ld8(vp, 1);
+    if constexpr (KS > 2) { k2 = ld8(kp, 2); k3 = ld8(kp, 3); v2 = ld8(vp, 2); v3 = ld8(vp, 3); }
+    if constexpr (KS > 4) { k4 = ld8(kp, 4); k5 = ld8(kp, 5); v4 = ld8(vp, 4); v5 = ld8(vp, 5); }
+    if constexpr (KS > 6) { k6 = ld8(kp, 6); k7 = ld8(kp, 7); v6 = ld8(vp, 6); v7 = ld8(vp, 7); }
+  }
+  f32x16 dk[HM], dv[HM];
+#pragma unroll
+  for (int i = 0; i < HM; ++i) {
+    dk[i] = f32x16{};
+    dv[i] = f32x16{};
+  }
+  // queries t >= first key of the block, up to the end of the chunk
+  const int tbeg = (s0blk / KT) * KT;
+  const int qb = blockIdx.x * BQ;
+  (void)qb;
+  for (int tq0 = tbeg; tq0 < a.n; tq0 += KT) {
+    uint4 rq0, rq1, rq2, rq3, ro0, ro1, ro2, ro3;
+#define LD(i, dq_, do_)                                                                     \
+  if constexpr (KCH > i) {                                                                  \
+    const int c = tid + i * 256, r = c / (HD / 8), col = (c % (HD / 8)) * 8;                \
+    const int t = tq0 + r;                                                                  \
+    if (t < a.n) {                                                                          \
+      dq_ = *(const uint4*)((const bf16*)a.q + (bh * a.n + t) * HD + col);                  \
+      do_ = *(const uint4*)((const bf16*)a.dout + ((int64_t)b * a.n + t) * d + (int64_t)h * HD + col); \
+    } else {                                                                                \
+      dq_ = make_uint4(0, 0, 0, 0);                                                         \
+      do_ = make_uint4(0, 0, 0, 0);                                                         \
+    }                                                                                       \
+  }
+    LD(0, rq0, ro0) LD(1, rq1, ro1) LD(2, rq2, ro2) LD(3, rq3, ro3)
+#undef LD
+    __syncthreads();
+#define ST(i, sq, so)                                                                       \
+  if constexpr (KCH > i) {                                                                  \
+    const int c = tid + i * 256, r = c / (HD / 8), col = (c % (HD / 8)) * 8;                \
+    *(uint4*)&sm.q[r][col] = sq;                                                            \
+    *(uint4*)&sm.o[r][col] = so;                                                            \
+    const uint16_t* eq = (const uint16_t*)&sq;                                              \
+    const uint16_t* eo = (const uint16_t*)&so;                                              \
+    _Pragma("unroll") for (int x = 0; x < 8; ++x) {                                         \
+      sm.qt[col + x][r].x = eq[x];                                                          \
+      sm.ot[col + x][r].x = eo[x];                                                          \
+    }                                                                                       \
+  }
+    ST(0, rq0, ro0) ST(1, rq1, ro1) ST(2, rq2, ro2) ST(3, rq3, ro3)
+#undef ST
+    if (tid < KT) {
+      const int t = tq0 + tid;
+      sm.lse2[tid] = t < a.n ? a.lse[bh * a.n + t] * LOG2E : 0.f;
+      sm.dd[tid] = t < a.n ? a.dvec[bh * a.n + t] : 0.f;
+    }
+    __syncthreads();
+    f32x16 s0 = f32x16{}, s1 = f32x16{}, p0 = f32x16{}, p1 = f32x16{};
+    {
+      const bf16* q0p = &sm.q[(lane & 31)][g * 8];
+      const bf16* q1p = &sm.q[32 + (lane & 31)][g * 8];
+      const bf16* o0p = &sm.o[(lane & 31)][g * 8];
+      const bf16* o1p = &sm.o[32 + (lane & 31)][g * 8];
+#define SSTEP(ks, kv, vv)                                                                          \
+  if constexpr (KS > ks) {                                                                         \
+    s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(q0p + ks * 16), kv, s0, 0, 0, 0); \
+    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(q1p + ks * 16), kv, s1, 0, 0, 0); \
+    p0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(o0p + ks * 16), vv, p0, 0, 0, 0); \
+    p1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(o1p + ks * 16), vv, p1, 0, 0, 0); \
+  }
+      SSTEP(0, k0, v0) SSTEP(1, k1, v1) SSTEP(2, k2, v2) SSTEP(3, k3, v3)
+      SSTEP(4, k4, v4) SSTEP(5, k5, v5) SSTEP(6, k6, v6) SSTEP(7, k7, v7)
+#undef SSTEP
+    }
+    // rows = queries tq0 + 32 half + 8 j + 4 g + i; visible iff sk <= t < n and t - sk < window
+    uint32_t pa[8], pb[8], da[8], db[8];
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      float pv[4], dsv[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int rr = r + (u & 1);
+        const int row = (u >> 1) * 32 + 8 * (rr >> 2) + 4 * g + (rr & 3);
+        const int t = tq0 + row;
+        const bool ok = kok && t < a.n && t >= sk && t - sk < a.window;
+        const float sv = (u >> 1) ? s1[rr] : s0[rr];
+        const float dpv = (u >> 1) ? p1[rr] : p0[rr];
+        const float p = ok ? exp2f(sv * sl2 - sm.lse2[row]) : 0.f;
+        pv[u] = p;
+        dsv[u] = p * (dpv - sm.dd[row]);
+      }
+      pa[r >> 1] = pk2(pv[0], pv[1]);
+      pb[r >> 1] = pk2(pv[2], pv[3]);
+      da[r >> 1] = pk2(dsv[0], dsv[1]);
+      db[r >> 1] = pk2(dsv[2], dsv[3]);
+    }
+    const bf16x8 pf[4] = {__builtin_bit_cast(bf16x8, make_uint4(pa[0], pa[1], pa[2], pa[3])),
+                          __builtin_bit_cast(bf16x8, make_uint4(pa[4], pa[5], pa[6], pa[7])),
+                          __builtin_bit_cast(bf16x8, make_uint4(pb[0], pb[1], pb[2], pb[3])),
+                          __builtin_bit_cast(bf16x8, make_uint4(pb[4], pb[5], pb[6], pb[7]))};
+    const bf16x8 dsf[4] = {__builtin_bit_cast(bf16x8, make_uint4(da[0], da[1], da[2], da[3])),
+                           __builtin_bit_cast(bf16x8, make_uint4(da[4], da[5], da[6], da[7])),
+                           __builtin_bit_cast(bf16x8, make_uint4(db[0], db[1], db[2], db[3])),
+                           __builtin_bit_cast(bf16x8, make_uint4(db[4], db[5], db[6], db[7]))};
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const int kc = st * 16 + 4 * g;
+#pragma unroll
+      for (int hm = 0; hm < HM; ++hm) {
+        const bf16* orow = &sm.ot[hm * 32 + (lane & 31)][0];
+        const bf16* qrow = &sm.qt[hm * 32 + (lane & 31)][0];
+        uint2 ol = *(const uint2*)(orow + kc), oh = *(const uint2*)(orow + kc + 8);
+        uint2 ql = *(const uint2*)(qrow + kc), qh = *(const uint2*)(qrow + kc + 8);
+        bf16x8 of = __builtin_bit_cast(bf16x8, make_uint4(ol.x, ol.y, oh.x, oh.y));
+        bf16x8 qf = __builtin_bit_cast(bf16x8, make_uint4(ql.x, ql.y, qh.x, qh.y));
+        dv[hm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(of, pf[st], dv[hm], 0, 0, 0);
+        dk[hm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf, dsf[st], dk[hm], 0, 0, 0);
+      }
+    }
+  }
+  if (!kok) return;
+  const float sc = 1.f / sqrtf((float)HD);
+  float* ok_ = a.dk + ((int64_t)b * a.n + sk) * d + (int64_t)h * HD;
+  float* ov_ = a.dv + ((int64_t)b * a.n + sk) * d + (int64_t)h * HD;
+#pragma unroll
+  for (int hm = 0; hm < HM; ++hm)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int d0 = hm * 32 + 8 * j + 4 * g;
+      *(float4*)(ok_ + d0) = make_float4(dk[hm][4 * j] * sc, dk[hm][4 * j + 1] * sc, dk[hm][4 * j + 2] * sc,
+                                         dk[hm][4 * j + 3] * sc);
+      *(float4*)(ov_ + d0) = make_float4(dv[hm][4 * j], dv[hm][4 * j + 1], dv[hm][4 * j + 2], dv[hm][4 * j + 3]);
+    }
+}
+
+template <typename Smem, typename K>
+hipError_t set_lds(K kern) {
+  return hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(Smem));
+}
+
+// dq = sum over the key-range parts, in order
+__global__ void k_dq_reduce(const float* ws, int S, int64_t total, float* dq) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+    float acc = 0.f;
+    for (int sidx = 0; sidx < S; ++sidx) acc += ws[sidx * total + i];
+    dq[i] = acc;
+  }
+}
+
+template <int HD>
+hipError_t launch_bwd(const AttnBwdArgs& a, hipStream_t s) {
+  static bool attr = false;
+  if (!attr) {
+    hipError_t e = set_lds<DqSmem<HD>>(k_swa_dq<HD, false>);
+    if (e == hipSuccess) e = set_lds<DqSmem<HD>>(k_swa_dq<HD, true>);
+    if (e == hipSuccess) e = set_lds<DkvSmem<HD>>(k_swa_dkv<HD>);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  hipError_t e = swa_dvec_bf16(a, s);
+  if (e != hipSuccess) return e;
+  const int64_t blocks = (int64_t)cdiv(a.n, BQ) * a.H * a.B;
+  const int64_t ntiles = (std::min<int64_t>(a.window, a.pos0 + 1) + BQ) / KT + 1;
+  const int64_t total = (int64_t)a.B * a.n * a.H * HD;
+  const int S = attn_splits(blocks, ntiles, total, a.ws, a.ws_floats);
+  if (S > 1) {
+    hipLaunchKernelGGL((k_swa_dq<HD, true>), dim3(cdiv(a.n, BQ), a.H, a.B * S), dim3(256), sizeof(DqSmem<HD>), s, a, S);
+    hipLaunchKernelGGL(k_dq_reduce, dim3((unsigned)std::min<int64_t>(cdiv(total, 256), 4096)), dim3(256), 0, s, a.ws,
+                       S, total, a.dq);
+  } else {
+    hipLaunchKernelGGL((k_swa_dq<HD, false>), dim3(cdiv(a.n, BQ), a.H, a.B), dim3(256), sizeof(DqSmem<HD>), s, a, 1);
+  }
   dim3 grid(cdiv(a.n, BQ), a.H, a.B);
-  hipLaunchKernelGGL(kern, grid, dim3(256), shm, s, a);
+  hipLaunchKernelGGL(k_swa_dkv<HD>, grid, dim3(256), sizeof(DkvSmem<HD>), s, a);
   return hipGetLastError();
 }
 
@@ -253,4 +709,14 @@ hipError_t swa_fwd_mfma(const AttnArgs& a, hipStream_t s) {
   }
 }
 
-hipError_t swa_bwd_mfma(const AttnBwdArgs& a, hipStream_t s) { return swa_bwd_simt<bf16>(a, s); }
+hipError_t swa_bwd_mfma(const AttnBwdArgs& a, hipStream_t s) {
+  if (a.n == 0) return hipSuccess;
+  if (a.window < a.n) return swa_bwd_simt<bf16>(a, s);
+  switch (a.hd) {
+    case 32: return launch_bwd<32>(a, s);
+    case 64: return launch_bwd<64>(a, s);
+    case 96: return launch_bwd<96>(a, s);
+    case 128: return launch_bwd<128>(a, s);
+    default: return swa_bwd_simt<bf16>(a, s);
+  }
+}

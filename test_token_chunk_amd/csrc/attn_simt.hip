@@ -205,6 +205,11 @@ hipError_t swa_bwd_simt(const AttnBwdArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+hipError_t swa_dvec_bf16(const AttnBwdArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_dvec<bf16>, dim3(a.n, a.H, a.B), dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+
 template hipError_t swa_fwd_simt<float>(const AttnArgs&, hipStream_t);
 template hipError_t swa_fwd_simt<bf16>(const AttnArgs&, hipStream_t);
 template hipError_t swa_bwd_simt<float>(const AttnBwdArgs&, hipStream_t);

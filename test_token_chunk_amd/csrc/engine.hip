@@ -91,6 +91,8 @@ struct ttt_ctx {
   float *dh = nullptr, *tmpf = nullptr, *dq = nullptr, *dk = nullptr, *dv = nullptr, *dvec = nullptr;
   void *dyN = nullptr, *dyT = nullptr, *dz = nullptr, *dzT = nullptr, *dhT = nullptr, *dO = nullptr, *dqkv = nullptr;
   int* err_dev = nullptr;
+  float* ws = nullptr;  // split-K / split-key workspace (used by one launch at a time)
+  int64_t ws_floats = 0;
   int32_t* d_tok = nullptr;
   int64_t d_tok_cap = 0;
   float* d_loss = nullptr;
@@ -154,7 +156,8 @@ int fail(ttt_ctx* c, int code, const std::string& msg) {
   } while (0)
 
 // ------------------------------------------------------------------ profiling
-enum { PC_GEMM = 0, PC_SWA_FWD = 1, PC_SWA_BWD = 2, PC_CE = 3, PC_N = 4 };
+// GEMM classes follow the epilogue kind (EPI_F32 .. EPI_SGD), then attention
+enum { PC_SWA_FWD = 6, PC_SWA_BWD = 7, PC_N = 8 };
 
 hipEvent_t next_event(ttt_ctx* c) {
   if (c->ev_used == c->ev_pool.size()) {
@@ -198,7 +201,7 @@ double gemm_flops(const GemmArgs& g) {
 template <>
 struct Ops<float> {
   static hipError_t gemm(ttt_ctx* c, const GemmArgs& g) {
-    return timed(c, PC_GEMM, gemm_flops(g), [&] { return gemm_simt_f32(g, c->stream); });
+    return timed(c, g.e.kind, gemm_flops(g), [&] { return gemm_simt_f32(g, c->stream); });
   }
   static hipError_t fwd(ttt_ctx* c, const AttnArgs& a) {
     double fl = 4.0 * a.hd * a.H * a.B * attn_pairs(c, a.n, a.pos0);
@@ -210,18 +213,28 @@ struct Ops<float> {
   }
 };
 
+// the bf16 kernels may use the context's workspace to split under-filled grids
 template <>
 struct Ops<bf16> {
-  static hipError_t gemm(ttt_ctx* c, const GemmArgs& g) {
-    return timed(c, PC_GEMM, gemm_flops(g),
+  static hipError_t gemm(ttt_ctx* c, const GemmArgs& g0) {
+    GemmArgs g = g0;
+    g.ws = c->ws;
+    g.ws_floats = c->ws_floats;
+    return timed(c, g.e.kind, gemm_flops(g),
                  [&] { return c->mfma ? gemm_mfma_bf16(g, c->stream) : gemm_simt_bf16(g, c->stream); });
   }
-  static hipError_t fwd(ttt_ctx* c, const AttnArgs& a) {
+  static hipError_t fwd(ttt_ctx* c, const AttnArgs& a0) {
+    AttnArgs a = a0;
+    a.ws = c->ws;
+    a.ws_floats = c->ws_floats;
     double fl = 4.0 * a.hd * a.H * a.B * attn_pairs(c, a.n, a.pos0);
     return timed(c, PC_SWA_FWD, fl,
                  [&] { return c->mfma ? swa_fwd_mfma(a, c->stream) : swa_fwd_simt<bf16>(a, c->stream); });
   }
-  static hipError_t bwd(ttt_ctx* c, const AttnBwdArgs& a) {
+  static hipError_t bwd(ttt_ctx* c, const AttnBwdArgs& a0) {
+    AttnBwdArgs a = a0;
+    a.ws = c->ws;
+    a.ws_floats = c->ws_floats;
     double fl = 4.0 * a.hd * a.H * a.B * (attn_pairs(c, a.n, a.pos0) + 0.5 * a.n * (a.n + 1.0));
     return timed(c, PC_SWA_BWD, fl,
                  [&] { return c->mfma ? swa_bwd_mfma(a, c->stream) : swa_bwd_simt<bf16>(a, c->stream); });
@@ -736,6 +749,8 @@ int build(ttt_ctx* c, const ttt_weights* w) {
   AL(c->dO, rows_top * d * es);
   AL(c->dqkv, rows_top * 3 * d * es);
   AL(c->err_dev, 256);
+  c->ws_floats = 8 * rows_top * (int64_t)(d + 2 * H);
+  AL(c->ws, c->ws_floats * 4);
   CK(hipMemset(c->err_dev, 0, 4));
   c->acts.resize(c->Lq);
   for (int j = 0; j < c->Lq; ++j) {

@@ -11,6 +11,8 @@
 // MFMA 32x32x16 bf16 lane layout (checked on the device): lane l holds
 // A[row l%32][k 8*(l/32) .. +7], B[col l%32][k 8*(l/32) .. +7], and
 // C[row 8j + 4*(l/32) + i][col l%32] in acc[4j + i].
+#include <algorithm>
+
 #include "epilogue.h"
 
 namespace {
@@ -43,7 +45,7 @@ __device__ __forceinline__ uint4 ldg16_tail(const bf16* p, int valid) {
   return make_uint4(pair(q, 0, valid), pair(q, 2, valid), pair(q, 4, valid), pair(q, 6, valid));
 }
 
-template <int BM, int BN, int WM, int WN, bool DUAL, int EK>
+template <int BM, int BN, int WM, int WN, bool DUAL, int EK, bool SPLIT = false>
 __global__ __launch_bounds__(256) void k_gemm_mfma(GemmArgs g) {
   constexpr int TM = WM / 32, TN = WN / 32;        // MFMA tiles per wave
   constexpr int A_CH = BM * BK / 8 / 256;          // 16-byte chunks per thread
@@ -51,31 +53,37 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(GemmArgs g) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   Smem<BM, BN, DUAL>& sm = *reinterpret_cast<Smem<BM, BN, DUAL>*>(smem_raw);
 
-  const int bz = blockIdx.z;
+  // SPLIT: blockIdx.z = batch * S + split; split covers K range [split*Ks, (split+1)*Ks)
+  // (S and Ks travel in e.ldt / e.st) and writes fp32 partials to ws[split][batch][M][N].
+  const int S = SPLIT ? (int)g.e.ldt : 1;
+  const int bz = SPLIT ? blockIdx.z / S : blockIdx.z;
+  const int split = SPLIT ? blockIdx.z % S : 0;
+  const int kbeg = SPLIT ? split * (int)g.e.st : 0;
+  const int kend = SPLIT ? min(g.K, kbeg + (int)g.e.st) : g.K;
   const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
   const bf16* A = (const bf16*)g.A + bz * g.sA;
   const bf16* B = (const bf16*)g.B + bz * g.sB;
   const bf16* U = DUAL ? B + g.dual_off * g.ldb : nullptr;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wm0 = (wid >> 1) * WM, wn0 = (wid & 1) * WN;
-  const int nk = (g.K + BK - 1) / BK;
+  const int nk = (kend - kbeg + BK - 1) / BK;
 
   uint4 ra[A_CH], rb[B_CH], ru[DUAL ? B_CH : 1];
   auto load = [&](int kt) {
-    const int k0 = kt * BK;
+    const int k0 = kbeg + kt * BK;
 #pragma unroll
     for (int i = 0; i < A_CH; ++i) {
       int c = tid + i * 256, r = c >> 3, kc = (c & 7) * 8;
       int gm = m0 + r, gk = k0 + kc;
-      ra[i] = (gm < g.M) ? ldg16_tail(A + (int64_t)gm * g.lda + gk, g.K - gk) : make_uint4(0, 0, 0, 0);
+      ra[i] = (gm < g.M) ? ldg16_tail(A + (int64_t)gm * g.lda + gk, kend - gk) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < B_CH; ++i) {
       int c = tid + i * 256, r = c >> 3, kc = (c & 7) * 8;
       int gn = n0 + r, gk = k0 + kc;
-      rb[i] = (gn < g.N) ? ldg16_tail(B + (int64_t)gn * g.ldb + gk, g.K - gk) : make_uint4(0, 0, 0, 0);
+      rb[i] = (gn < g.N) ? ldg16_tail(B + (int64_t)gn * g.ldb + gk, kend - gk) : make_uint4(0, 0, 0, 0);
       if constexpr (DUAL)
-        ru[i] = (gn < g.N) ? ldg16_tail(U + (int64_t)gn * g.ldb + gk, g.K - gk) : make_uint4(0, 0, 0, 0);
+        ru[i] = (gn < g.N) ? ldg16_tail(U + (int64_t)gn * g.ldb + gk, kend - gk) : make_uint4(0, 0, 0, 0);
     }
   };
   auto store = [&](int buf) {
@@ -131,27 +139,102 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(GemmArgs g) {
     __syncthreads();
   }
 
-  // epilogue: C[row 8q + 4*(l/32) + i][col l%32] = acc[4q + i]
+  // epilogue: C[row 8q + 4*(l/32) + i][col l%32] = acc[4q + i].
+  // Outputs stored transposed ([n][m]: the refreshed W^T shadow of the fused SGD step,
+  // act^T, dz^T) are staged through LDS and written as 16-byte row segments.
+  constexpr bool TR = (EK == EPI_SGD) || (EK == EPI_SWIGLU_BWD) || DUAL;
+  constexpr int TLD = BM + 8;
+  bf16* tr0 = reinterpret_cast<bf16*>(smem_raw);  // [BN][TLD]
+  bf16* tr1 = tr0 + BN * TLD;                     // second tile (dz_u^T)
+  static_assert(!TR || (EK == EPI_SWIGLU_BWD ? 2 : 1) * BN * TLD * 2 <= (int)sizeof(Smem<BM, BN, DUAL>),
+                "transpose staging fits in the operand buffers");
+  const bool want_t = TR && (EK != EPI_SWIGLU || g.e.t != nullptr);
   const int hi = lane >> 5;
+  const Epi& e = g.e;
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-      const int n = n0 + wn0 + j * 32 + lr;
-      if (n >= g.N) continue;
+      const int nl = wn0 + j * 32 + lr, n = n0 + nl;
 #pragma unroll
       for (int q = 0; q < 4; ++q)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int m = m0 + wm0 + i * 32 + 8 * q + 4 * hi + r;
-          if (m < g.M) {
-            if constexpr (DUAL)
-              epi_apply2<bf16>(g.e, bz, m, n, acc[i][j][4 * q + r], accu[i][j][4 * q + r]);
-            else
-              epi_apply_k<bf16, EK>(g.e, bz, m, n, acc[i][j][4 * q + r]);
+          const int ml = wm0 + i * 32 + 8 * q + 4 * hi + r, m = m0 + ml;
+          const bool in = m < g.M && n < g.N;
+          const float x = acc[i][j][4 * q + r];
+          if constexpr (DUAL) {
+            const float u = accu[i][j][4 * q + r];
+            const float act = x / (1.f + __expf(-x)) * u;
+            if (in) {
+              ((bf16*)e.c)[bz * e.sc + (int64_t)m * e.ldc + n] = f2bf(act);
+              if (e.zg) {
+                ((bf16*)e.zg)[bz * e.sz + (int64_t)m * e.ldz + n] = f2bf(x);
+                ((bf16*)e.zu)[bz * e.sz + (int64_t)m * e.ldz + n] = f2bf(u);
+              }
+            }
+            tr0[nl * TLD + ml] = f2bf(act);
+          } else if constexpr (EK == EPI_SGD) {
+            if (in) {
+              float* p = e.master + bz * e.sm + (int64_t)m * e.ldm + n;
+              const float w = *p - e.lr * x;
+              *p = w;
+              ((bf16*)e.sh)[bz * e.ssh + (int64_t)m * e.ldsh + n] = f2bf(w);
+              tr0[nl * TLD + ml] = f2bf(w);
+            }
+          } else if constexpr (EK == EPI_SWIGLU_BWD) {
+            if (in) {
+              const float zg = bf2f(((const bf16*)e.zg)[bz * e.sz + (int64_t)m * e.ldz + n]);
+              const float zu = bf2f(((const bf16*)e.zu)[bz * e.sz + (int64_t)m * e.ldz + n]);
+              const float sg = 1.f / (1.f + __expf(-zg));
+              const float dzu = x * zg * sg;
+              const float dzg = x * zu * sg * (1.f + zg * (1.f - sg));
+              bf16* c = (bf16*)e.c + bz * e.sc + (int64_t)m * e.ldc;
+              c[n] = f2bf(dzg);
+              c[e.f + n] = f2bf(dzu);
+              tr0[nl * TLD + ml] = f2bf(dzg);
+              tr1[nl * TLD + ml] = f2bf(dzu);
+            }
+          } else if constexpr (SPLIT) {
+            if (in) g.ws[(((int64_t)split * (gridDim.z / S) + bz) * g.M + m) * g.N + n] = x;
+          } else {
+            if (in) epi_apply_k<bf16, EK>(e, bz, m, n, x);
           }
         }
     }
+  if constexpr (TR) {
+    if (!want_t) return;
+    __syncthreads();
+    // tile rows nl (output rows n0+nl) hold BM consecutive m values
+    bf16* dst0;
+    bf16* dst1 = nullptr;
+    int64_t ld;
+    if constexpr (EK == EPI_SGD) {
+      dst0 = (bf16*)e.shT + bz * e.sshT;
+      ld = e.ldshT;
+    } else {
+      dst0 = (bf16*)e.t + bz * e.st;
+      ld = e.ldt;
+      if constexpr (EK == EPI_SWIGLU_BWD) dst1 = dst0 + (int64_t)e.f * e.ldt;
+    }
+    const bool vec = (ld % 8) == 0 && (((uintptr_t)dst0) & 15) == 0;
+    constexpr int CH = BM / 8;  // 16-byte chunks per tile row
+    for (int cidx = tid; cidx < BN * CH; cidx += 256) {
+      const int nl = cidx / CH, ml = (cidx % CH) * 8;
+      const int n = n0 + nl, m = m0 + ml;
+      if (n >= g.N || m >= g.M) continue;
+#pragma unroll
+      for (int t = 0; t < (EK == EPI_SWIGLU_BWD ? 2 : 1); ++t) {
+        const bf16* srow = (t ? tr1 : tr0) + nl * TLD + ml;
+        bf16* drow = (t ? dst1 : dst0) + (int64_t)n * ld + m;
+        if (vec && m + 8 <= g.M) {
+          *(uint4*)drow = *(const uint4*)srow;
+        } else {
+          for (int x = 0; x < 8 && m + x < g.M; ++x) drow[x] = srow[x];
+        }
+      }
+    }
+  }
 }
 
 template <int BM, int BN, int WM, int WN, bool DUAL, int EK>
@@ -169,6 +252,45 @@ hipError_t launch(const GemmArgs& g, hipStream_t s) {
   return hipGetLastError();
 }
 
+// out = epilogue(sum_s ws[s]) for the split-K parts; the sum runs over s in order
+template <int EK>
+__global__ void k_splitk_reduce(GemmArgs g, int S) {
+  const int64_t per = (int64_t)g.M * g.N;
+  const int64_t total = per * g.batch;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+    float acc = 0.f;
+    for (int sidx = 0; sidx < S; ++sidx) acc += g.ws[sidx * total + i];
+    const int bz = (int)(i / per);
+    const int64_t r = i % per;
+    epi_apply_k<bf16, EK>(g.e, bz, (int)(r / g.N), (int)(r % g.N), acc);
+  }
+}
+
+hipError_t launch_splitk(const GemmArgs& g0, int S, int Ks, hipStream_t s) {
+  GemmArgs g = g0;
+  g.e.ldt = S;   // carried to the kernel
+  g.e.st = Ks;
+  auto kern = k_gemm_mfma<128, 128, 64, 64, false, EPI_F32, true>;
+  static bool attr_set = false;
+  const size_t shm = sizeof(Smem<128, 128, false>);
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  dim3 grid(cdiv(g.N, 128), cdiv(g.M, 128), g.batch * S);
+  hipLaunchKernelGGL(kern, grid, dim3(256), shm, s, g);
+  const int64_t total = (int64_t)g.batch * g.M * g.N;
+  dim3 rg((unsigned)std::min<int64_t>(cdiv(total, 256), 4096));
+  switch (g0.e.kind) {
+    case EPI_F32: hipLaunchKernelGGL(k_splitk_reduce<EPI_F32>, rg, dim3(256), 0, s, g0, S); break;
+    case EPI_T: hipLaunchKernelGGL(k_splitk_reduce<EPI_T>, rg, dim3(256), 0, s, g0, S); break;
+    case EPI_ADD_F32: hipLaunchKernelGGL(k_splitk_reduce<EPI_ADD_F32>, rg, dim3(256), 0, s, g0, S); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
 }  // namespace
@@ -179,6 +301,18 @@ hipError_t gemm_mfma_bf16(const GemmArgs& g, hipStream_t s) {
   bool ok = aligned16(g.A) && aligned16(g.B) && g.lda % 8 == 0 && g.ldb % 8 == 0 && g.sA % 8 == 0 &&
             g.sB % 8 == 0 && (g.dual_off * g.ldb) % 8 == 0 && g.K >= 1;
   if (!ok) return gemm_simt_bf16(g, s);
+  // Small grids with a long K (the N = d GEMMs of the per-chunk upper blocks) split K
+  // over several blocks into an fp32 workspace, then one pass sums the parts in a
+  // fixed order and applies the epilogue.
+  const int64_t tiles = (int64_t)cdiv(g.M, 128) * cdiv(g.N, 128) * g.batch;
+  if (g.ws && tiles < 384 && g.K >= 1024 &&
+      (g.e.kind == EPI_F32 || g.e.kind == EPI_T || g.e.kind == EPI_ADD_F32)) {
+    int S = (int)std::min<int64_t>(8, (640 + tiles - 1) / tiles);
+    S = std::min(S, g.K / 256);
+    const int Ks = (int)cdiv(cdiv(g.K, S), BK) * BK;
+    S = (int)cdiv(g.K, Ks);
+    if (S >= 2 && (int64_t)S * g.batch * g.M * g.N <= g.ws_floats) return launch_splitk(g, S, Ks, s);
+  }
   switch (g.e.kind) {
     case EPI_SWIGLU: return launch<128, 128, 64, 64, true, EPI_SWIGLU>(g, s);
     case EPI_F32: return launch<128, 128, 64, 64, false, EPI_F32>(g, s);

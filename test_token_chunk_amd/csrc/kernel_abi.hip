@@ -6,8 +6,8 @@
 static int code(hipError_t e) { return e == hipSuccess ? TTT_OK : (e == hipErrorInvalidValue ? TTT_EINVAL : TTT_EDEVICE); }
 
 extern "C" int tttk_gemm(int dtype, const void* A, int64_t lda, const void* B, int64_t ldb, float* C, int64_t ldc,
-                         int32_t M, int32_t N, int32_t K, void* stream) {
-  if (!A || !B || !C || M < 0 || N < 0 || K < 1 || lda < K || ldb < K || ldc < N) return TTT_EINVAL;
+                         int32_t M, int32_t N, int32_t K, float* ws, int64_t ws_floats, void* stream) {
+  if (!A || !B || !C || M < 0 || N < 0 || K < 1 || lda < K || ldb < K || ldc < N || ws_floats < 0) return TTT_EINVAL;
   GemmArgs g;
   g.A = A;
   g.lda = lda;
@@ -19,6 +19,8 @@ extern "C" int tttk_gemm(int dtype, const void* A, int64_t lda, const void* B, i
   g.e.kind = EPI_F32;
   g.e.c = C;
   g.e.ldc = ldc;
+  g.ws = ws;
+  g.ws_floats = ws ? ws_floats : 0;
   if (dtype == TTT_F32) return code(gemm_simt_f32(g, (hipStream_t)stream));
   if (dtype == TTT_BF16) return code(gemm_mfma_bf16(g, (hipStream_t)stream));
   return TTT_EINVAL;
@@ -26,11 +28,11 @@ extern "C" int tttk_gemm(int dtype, const void* A, int64_t lda, const void* B, i
 
 extern "C" int tttk_swa_fwd(int dtype, const void* q, const void* kr, const void* vr, const void* vtr, void* o,
                             float* lse, int32_t B, int32_t H, int32_t hd, int32_t n, int32_t R, int32_t window,
-                            int64_t pos0, void* stream) {
+                            int64_t pos0, float* ws, int64_t ws_floats, void* stream) {
   if (!q || !kr || !vr || !vtr || !o || B < 1 || H < 1 || hd < 2 || hd % 2 || hd > 128 || n < 0 || window < 1 ||
       pos0 < 0 || R < window + n - 1)
     return TTT_EINVAL;
-  AttnArgs a{q, kr, vr, vtr, o, lse, B, H, hd, n, R, window, pos0};
+  AttnArgs a{q, kr, vr, vtr, o, lse, B, H, hd, n, R, window, pos0, ws, ws ? ws_floats : 0};
   if (dtype == TTT_F32) return code(swa_fwd_simt<float>(a, (hipStream_t)stream));
   if (dtype == TTT_BF16) return code(swa_fwd_mfma(a, (hipStream_t)stream));
   return TTT_EINVAL;
@@ -39,11 +41,12 @@ extern "C" int tttk_swa_fwd(int dtype, const void* q, const void* kr, const void
 extern "C" int tttk_swa_bwd(int dtype, const void* q, const void* qt, const void* kr, const void* vr, const void* vtr,
                             const void* o, const void* dout, const float* lse, float* dvec, float* dq, float* dk,
                             float* dv, int32_t B, int32_t H, int32_t hd, int32_t n, int32_t R, int32_t window,
-                            int64_t pos0, void* stream) {
+                            int64_t pos0, float* ws, int64_t ws_floats, void* stream) {
   if (!q || !qt || !kr || !vr || !vtr || !o || !dout || !lse || !dvec || !dq || !dk || !dv || B < 1 || H < 1 ||
       hd < 2 || hd % 2 || hd > 128 || n < 0 || window < n || pos0 < 0 || R < window + n - 1)
     return TTT_EINVAL;
-  AttnBwdArgs a{q, qt, kr, vr, vtr, o, dout, lse, dvec, dq, dk, dv, B, H, hd, n, R, window, pos0};
+  AttnBwdArgs a{q, qt, kr, vr, vtr, o, dout, lse, dvec, dq, dk, dv, B, H, hd, n, R, window, pos0, ws,
+                ws ? ws_floats : 0};
   if (dtype == TTT_F32) return code(swa_bwd_simt<float>(a, (hipStream_t)stream));
   if (dtype == TTT_BF16) return code(swa_bwd_mfma(a, (hipStream_t)stream));
   return TTT_EINVAL;

@@ -60,6 +60,8 @@ struct GemmArgs {
   int M = 0, N = 0, K = 0, batch = 1;
   int64_t dual_off = 0;  // EPI_SWIGLU: the "up" operand starts dual_off rows after the "gate" rows
   Epi e;
+  float* ws = nullptr;    // optional fp32 workspace: lets small-grid GEMMs split K (EPI_F32/EPI_T/EPI_ADD_F32)
+  int64_t ws_floats = 0;
 };
 
 hipError_t gemm_simt_f32(const GemmArgs& g, hipStream_t s);   // fp32 operands
@@ -103,6 +105,8 @@ struct AttnArgs {
   float* lse;       // [B][H][n] or null
   int B, H, hd, n, R, window;
   int64_t pos0;     // absolute position of query 0
+  float* ws = nullptr;  // optional fp32 workspace: lets small grids split the key range
+  int64_t ws_floats = 0;
 };
 template <typename T>
 hipError_t swa_fwd_simt(const AttnArgs& a, hipStream_t s);
@@ -123,6 +127,8 @@ struct AttnBwdArgs {
   float* dv;        // [B*n][H*hd] fp32
   int B, H, hd, n, R, window;
   int64_t pos0;
+  float* ws = nullptr;  // optional fp32 workspace: lets small grids split the key range of dq
+  int64_t ws_floats = 0;
 };
 template <typename T>
 hipError_t swa_bwd_simt(const AttnBwdArgs& a, hipStream_t s);

@@ -19,19 +19,25 @@ def _torch():
 
 
 GEMM_SHAPES = [(128, 128, 64), (300, 200, 72), (1, 512, 128), (1000, 384, 40), (257, 129, 1000), (64, 96, 8),
-               (1024, 2560, 256)]
+               (1024, 2560, 256), (1000, 384, 4100), (256, 640, 2056)]
 
 
+def _workspace(torch, use):
+    return torch.zeros(1 << 24, dtype=torch.float32, device="cuda") if use else None
+
+
+@pytest.mark.parametrize("use_ws", [False, True])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
-def test_gemm_matches_fp64(dtype, M, N, K):
+def test_gemm_matches_fp64(dtype, M, N, K, use_ws):
+    """bf16 with a workspace also covers the split-K path (small grids, K >= 1024)."""
     torch = _torch()
     from test_token_chunk_amd import gemm
     g = torch.Generator(device="cpu").manual_seed(M * 7 + N * 3 + K)
     dt = torch.bfloat16 if dtype == "bf16" else torch.float32
     A = torch.randn(M, K, generator=g).to(dt)
     B = torch.randn(N, K, generator=g).to(dt)
-    C = gemm(A.cuda(), B.cuda())
+    C = gemm(A.cuda(), B.cuda(), ws=_workspace(torch, use_ws))
     torch.cuda.synchronize()
     ref = A.double().numpy() @ B.double().numpy().T
     err = np.max(np.abs(C.cpu().numpy() - ref)) / max(np.max(np.abs(ref)), 1e-30)
@@ -77,9 +83,11 @@ ATTN_CASES = [
 ]
 
 
+@pytest.mark.parametrize("use_ws", [False, True])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("B,H,hd,n,window,pos0,R", ATTN_CASES)
-def test_swa_fwd_matches_fp64(dtype, B, H, hd, n, window, pos0, R):
+def test_swa_fwd_matches_fp64(dtype, B, H, hd, n, window, pos0, R, use_ws):
+    """bf16 with a workspace also covers the split key range (small grids, long windows)."""
     torch = _torch()
     from test_token_chunk_amd import swa_fwd
     dt = torch.bfloat16 if dtype == "bf16" else torch.float32
@@ -87,7 +95,7 @@ def test_swa_fwd_matches_fp64(dtype, B, H, hd, n, window, pos0, R):
     vtr = vr.transpose(2, 3).contiguous()
     o = torch.empty(B * n, H * hd, dtype=dt, device="cuda")
     lse = torch.empty(B, H, n, dtype=torch.float32, device="cuda")
-    swa_fwd(q.cuda(), kr.cuda(), vr.cuda(), vtr.cuda(), o, lse, pos0, window)
+    swa_fwd(q.cuda(), kr.cuda(), vr.cuda(), vtr.cuda(), o, lse, pos0, window, ws=_workspace(torch, use_ws))
     torch.cuda.synchronize()
     O, L = ref_attention(q.double().numpy(), kr.double().numpy(), vr.double().numpy(), pos0, window)
     got = o.float().cpu().numpy().reshape(B, n, H, hd).transpose(0, 2, 1, 3)
@@ -150,10 +158,11 @@ def ref_attention_bwd(q, kr, vr, dO, pos0, window):
     return dq, dk, dv
 
 
+@pytest.mark.parametrize("use_ws", [False, True])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("B,H,hd,n,window,pos0,R", [(1, 2, 32, 64, 256, 1000, 320), (2, 2, 64, 100, 130, 517, 256),
-                                                    (1, 2, 128, 130, 200, 331, 336)])
-def test_swa_bwd_matches_fp64(dtype, B, H, hd, n, window, pos0, R):
+                                                    (1, 2, 128, 130, 200, 331, 336), (1, 2, 128, 200, 1536, 3000, 1736)])
+def test_swa_bwd_matches_fp64(dtype, B, H, hd, n, window, pos0, R, use_ws):
     torch = _torch()
     from test_token_chunk_amd import swa_bwd, swa_fwd
     dt = torch.bfloat16 if dtype == "bf16" else torch.float32
@@ -162,13 +171,14 @@ def test_swa_bwd_matches_fp64(dtype, B, H, hd, n, window, pos0, R):
     cu = lambda x: x.contiguous().cuda()
     o = torch.empty(B * n, H * hd, dtype=dt, device="cuda")
     lse = torch.empty(B, H, n, dtype=torch.float32, device="cuda")
-    swa_fwd(cu(q), cu(kr), cu(vr), cu(vr.transpose(2, 3)), o, lse, pos0, window)
+    ws = _workspace(torch, use_ws)
+    swa_fwd(cu(q), cu(kr), cu(vr), cu(vr.transpose(2, 3)), o, lse, pos0, window, ws=ws)
     dq = torch.empty(B * n, H * hd, dtype=torch.float32, device="cuda")
     dk = torch.empty_like(dq)
     dv = torch.empty_like(dq)
     dvec = torch.empty(B, H, n, dtype=torch.float32, device="cuda")
     swa_bwd(cu(q), cu(q.transpose(2, 3)), cu(kr), cu(vr), cu(vr.transpose(2, 3)), o, cu(dO.reshape(B * n, H * hd)),
-            lse, dvec, dq, dk, dv, pos0, window)
+            lse, dvec, dq, dk, dv, pos0, window, ws=ws)
     torch.cuda.synchronize()
     rq, rk, rv = ref_attention_bwd(q.double().numpy(), kr.double().numpy(), vr.double().numpy(),
                                    dO.double().numpy().transpose(0, 2, 1, 3), pos0, window)
