@@ -321,10 +321,9 @@ template <int HD>
 hipError_t launch_fwd(const AttnArgs& a, hipStream_t s) {
   const int64_t blocks8 = (int64_t)cdiv(a.n, 8 * QW) * a.H * a.B;
   if (blocks8 >= 512) return launch_fwd_nw<HD, 8, false>(a, 1, s);
-  const int64_t blocks4 = (int64_t)cdiv(a.n, 4 * QW) * a.H * a.B;
-  const int64_t ntiles = (std::min<int64_t>(a.window, a.pos0 + 1) + 4 * QW) / KT + 1;
-  const int S = attn_splits(blocks4, ntiles, (int64_t)a.B * a.H * a.n * (HD + 2), a.ws, a.ws_floats);
-  if (S > 1) return launch_fwd_nw<HD, 4, true>(a, S, s);
+  const int64_t ntiles = (std::min<int64_t>(a.window, a.pos0 + 1) + 8 * QW) / KT + 1;
+  const int S = attn_splits(blocks8, ntiles, (int64_t)a.B * a.H * a.n * (HD + 2), a.ws, a.ws_floats);
+  if (S > 1) return launch_fwd_nw<HD, 8, true>(a, S, s);
   return launch_fwd_nw<HD, 4, false>(a, 1, s);
 }
 
@@ -338,16 +337,17 @@ hipError_t launch_fwd(const AttnArgs& a, hipStream_t s) {
 // K^T is produced in LDS by a transposing store of the K tile.
 template <int HD>
 struct DqSmem {
-  bf16 k[KT][HD + 8];
-  bf16 v[KT][HD + 8];
-  bf16 kt[HD][KT + 8];
+  bf16 k[2][KT][HD + 8];
+  bf16 v[2][KT][HD + 8];
+  bf16 kt[2][HD][KT + 8];
 };
 
 // SPLIT: blockIdx.z = b * S + split over the key tiles; partial dq to ws[S][B*n][H*hd]
-template <int HD, bool SPLIT = false>
-__global__ __launch_bounds__(256) void k_swa_dq(AttnBwdArgs a, int S) {
+template <int HD, int NW, bool SPLIT>
+__global__ __launch_bounds__(NW * 64) void k_swa_dq(AttnBwdArgs a, int S) {
+  constexpr int NT = NW * 64, BQn = NW * QW;
   constexpr int KS = HD / 16, HM = HD / 32;
-  constexpr int KCH = KT * HD / 8 / 256;
+  constexpr int KCH = (KT * HD / 8 + NT - 1) / NT;
   static_assert(KCH <= 4, "tile staging covers HD <= 128");
   extern __shared__ __align__(16) unsigned char smem_raw[];
   DqSmem<HD>& sm = *reinterpret_cast<DqSmem<HD>*>(smem_raw);
@@ -356,10 +356,13 @@ __global__ __launch_bounds__(256) void k_swa_dq(AttnBwdArgs a, int S) {
   const int sp = SPLIT ? blockIdx.z % S : 0;
   const int64_t bh = (int64_t)b * a.H + h;
   const int R = a.R, d = a.H * HD;
-  const int t0 = blockIdx.x * BQ;
+  const int t0 = blockIdx.x * BQn;
   const int tq = t0 + wid * QW + (lane & 31);
   const bool qok = tq < a.n;
   const int64_t qpos = a.pos0 + tq;
+  const int tw0 = t0 + wid * QW;
+  const bool wfull = tw0 + QW <= a.n;
+  const int64_t wpos_lo = a.pos0 + tw0, wpos_hi = wpos_lo + QW - 1;
   const bf16* Kr = (const bf16*)a.kr + bh * R * HD;
   const bf16* Vr = (const bf16*)a.vr + bh * R * HD;
 
@@ -378,10 +381,10 @@ __global__ __launch_bounds__(256) void k_swa_dq(AttnBwdArgs a, int S) {
   }
   const float LOG2E = 1.4426950408889634f;
   const float sl2 = LOG2E / sqrtf((float)HD);
-  const float lse2 = qok ? a.lse[bh * a.n + tq] * LOG2E : 0.f;
+  const float nlse2 = qok ? -a.lse[bh * a.n + tq] * LOG2E : 0.f;
   const float Dq = qok ? a.dvec[bh * a.n + tq] : 0.f;
 
-  const int tlast = min(t0 + BQ, a.n) - 1;
+  const int tlast = min(t0 + BQn, a.n) - 1;
   const int64_t kbeg = max((int64_t)0, a.pos0 + t0 - a.window + 1);
   const int64_t kend = a.pos0 + tlast;
   const int64_t ktile0 = (kbeg / KT) * KT;
@@ -395,38 +398,58 @@ __global__ __launch_bounds__(256) void k_swa_dq(AttnBwdArgs a, int S) {
 #pragma unroll
   for (int i = 0; i < HM; ++i) acc[i] = f32x16{};
 
-  for (int it = it_beg; it < ntiles; ++it) {
-    const int slot0 = (sbase + it * KT) % R;
-    const int64_t kp0 = ktile0 + (int64_t)it * KT;
-    // stage K (both layouts) and V
-    uint4 rk0, rk1, rk2, rk3, rv0, rv1, rv2, rv3;
+  uint4 rk0, rk1, rk2, rk3, rv0, rv1, rv2, rv3;
 #define LD(i, dk, dv)                                                                    \
   if constexpr (KCH > i) {                                                               \
-    const int c = tid + i * 256, r = c / (HD / 8), col = (c % (HD / 8)) * 8;             \
-    const int64_t off = (int64_t)((slot0 + r) % R) * HD + col;                           \
-    dk = *(const uint4*)(Kr + off);                                                      \
-    dv = *(const uint4*)(Vr + off);                                                      \
+    const int c = tid + i * NT, r = c / (HD / 8), col = (c % (HD / 8)) * 8;              \
+    if (c < KT * HD / 8) {                                                               \
+      const int64_t off = (int64_t)((slot0 + r) % R) * HD + col;                         \
+      dk = *(const uint4*)(Kr + off);                                                    \
+      dv = *(const uint4*)(Vr + off);                                                    \
+    }                                                                                    \
   }
-    LD(0, rk0, rv0) LD(1, rk1, rv1) LD(2, rk2, rv2) LD(3, rk3, rv3)
-#undef LD
-    __syncthreads();  // previous tile fully consumed
+#define LOAD_TILE(it_)                                                                   \
+  {                                                                                      \
+    const int slot0 = (sbase + (it_) * KT) % R;                                          \
+    LD(0, rk0, rv0) LD(1, rk1, rv1) LD(2, rk2, rv2) LD(3, rk3, rv3)                      \
+  }
 #define ST(i, sk, sv)                                                                    \
   if constexpr (KCH > i) {                                                               \
-    const int c = tid + i * 256, r = c / (HD / 8), col = (c % (HD / 8)) * 8;             \
-    *(uint4*)&sm.k[r][col] = sk;                                                         \
-    *(uint4*)&sm.v[r][col] = sv;                                                         \
-    const uint16_t* e = (const uint16_t*)&sk;                                            \
-    _Pragma("unroll") for (int x = 0; x < 8; ++x) sm.kt[col + x][r].x = e[x];             \
+    const int c = tid + i * NT, r = c / (HD / 8), col = (c % (HD / 8)) * 8;              \
+    if (c < KT * HD / 8) {                                                               \
+      *(uint4*)&sm.k[buf][r][col] = sk;                                                  \
+      *(uint4*)&sm.v[buf][r][col] = sv;                                                  \
+      const uint32_t w0 = sk.x, w1 = sk.y, w2 = sk.z, w3 = sk.w;                         \
+      sm.kt[buf][col + 0][r].x = (uint16_t)w0;                                           \
+      sm.kt[buf][col + 1][r].x = (uint16_t)(w0 >> 16);                                   \
+      sm.kt[buf][col + 2][r].x = (uint16_t)w1;                                           \
+      sm.kt[buf][col + 3][r].x = (uint16_t)(w1 >> 16);                                   \
+      sm.kt[buf][col + 4][r].x = (uint16_t)w2;                                           \
+      sm.kt[buf][col + 5][r].x = (uint16_t)(w2 >> 16);                                   \
+      sm.kt[buf][col + 6][r].x = (uint16_t)w3;                                           \
+      sm.kt[buf][col + 7][r].x = (uint16_t)(w3 >> 16);                                   \
+    }                                                                                    \
   }
-    ST(0, rk0, rv0) ST(1, rk1, rv1) ST(2, rk2, rv2) ST(3, rk3, rv3)
-#undef ST
-    __syncthreads();
+#define STORE_TILE(buf_)                                                                 \
+  {                                                                                      \
+    const int buf = (buf_);                                                              \
+    ST(0, rk0, rv0) ST(1, rk1, rv1) ST(2, rk2, rv2) ST(3, rk3, rv3)                      \
+  }
+  if (it_beg < ntiles) {
+    LOAD_TILE(it_beg)
+    STORE_TILE(it_beg & 1)
+  }
+  __syncthreads();
+  for (int it = it_beg; it < ntiles; ++it) {
+    const int cur = it & 1;
+    if (it + 1 < ntiles) LOAD_TILE(it + 1)
+    const int64_t kp0 = ktile0 + (int64_t)it * KT;
     f32x16 s0 = f32x16{}, s1 = f32x16{}, p0 = f32x16{}, p1 = f32x16{};
     {
-      const bf16* k0p = &sm.k[(lane & 31)][g * 8];
-      const bf16* k1p = &sm.k[32 + (lane & 31)][g * 8];
-      const bf16* v0p = &sm.v[(lane & 31)][g * 8];
-      const bf16* v1p = &sm.v[32 + (lane & 31)][g * 8];
+      const bf16* k0p = &sm.k[cur][(lane & 31)][g * 8];
+      const bf16* k1p = &sm.k[cur][32 + (lane & 31)][g * 8];
+      const bf16* v0p = &sm.v[cur][(lane & 31)][g * 8];
+      const bf16* v1p = &sm.v[cur][32 + (lane & 31)][g * 8];
 #define SSTEP(ks, qv, ev)                                                                          \
   if constexpr (KS > ks) {                                                                         \
     s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(k0p + ks * 16), qv, s0, 0, 0, 0); \
@@ -438,17 +461,26 @@ __global__ __launch_bounds__(256) void k_swa_dq(AttnBwdArgs a, int S) {
       SSTEP(4, q4, e4) SSTEP(5, q5, e5) SSTEP(6, q6, e6) SSTEP(7, q7, e7)
 #undef SSTEP
     }
-    const int64_t hi64 = qpos - kp0, lo64 = qpos - a.window - kp0;
-    const int hi = qok ? (int)min<int64_t>(max<int64_t>(hi64, -1), 64) : -1;
-    const int lo = (int)min<int64_t>(max<int64_t>(lo64, -2), 64);
+    // masked keys get score -inf (p = 0); only tiles that cut a window edge need it
+    const bool full = wfull && kp0 >= wpos_hi - a.window + 1 && kp0 + KT - 1 <= wpos_lo;
+    if (!full) {
+      const int64_t hi64 = qpos - kp0, lo64 = qpos - a.window - kp0;
+      const int hi = qok ? (int)min<int64_t>(max<int64_t>(hi64, -1), 64) : -1;
+      const int lo = (int)min<int64_t>(max<int64_t>(lo64, -2), 64);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int off = 8 * (r >> 2) + 4 * g + (r & 3);
+        if (!(off <= hi && off > lo)) s0[r] = -INFINITY;
+        if (!(off + 32 <= hi && off + 32 > lo)) s1[r] = -INFINITY;
+      }
+    }
     uint32_t da[8], db[8];
 #pragma unroll
     for (int r = 0; r < 16; r += 2) {
-      const int off = 8 * (r >> 2) + 4 * g + (r & 3);
-      float x0 = (off <= hi && off > lo) ? exp2f(s0[r] * sl2 - lse2) * (p0[r] - Dq) : 0.f;
-      float x1 = (off + 1 <= hi && off + 1 > lo) ? exp2f(s0[r + 1] * sl2 - lse2) * (p0[r + 1] - Dq) : 0.f;
-      float y0 = (off + 32 <= hi && off + 32 > lo) ? exp2f(s1[r] * sl2 - lse2) * (p1[r] - Dq) : 0.f;
-      float y1 = (off + 33 <= hi && off + 33 > lo) ? exp2f(s1[r + 1] * sl2 - lse2) * (p1[r + 1] - Dq) : 0.f;
+      const float x0 = exp2f(fmaf(s0[r], sl2, nlse2)) * (p0[r] - Dq);
+      const float x1 = exp2f(fmaf(s0[r + 1], sl2, nlse2)) * (p0[r + 1] - Dq);
+      const float y0 = exp2f(fmaf(s1[r], sl2, nlse2)) * (p1[r] - Dq);
+      const float y1 = exp2f(fmaf(s1[r + 1], sl2, nlse2)) * (p1[r + 1] - Dq);
       da[r >> 1] = pk2(x0, x1);
       db[r >> 1] = pk2(y0, y1);
     }
@@ -461,14 +493,20 @@ __global__ __launch_bounds__(256) void k_swa_dq(AttnBwdArgs a, int S) {
       const int kc = st * 16 + 4 * g;
 #pragma unroll
       for (int hm = 0; hm < HM; ++hm) {
-        const bf16* row = &sm.kt[hm * 32 + (lane & 31)][0];
+        const bf16* row = &sm.kt[cur][hm * 32 + (lane & 31)][0];
         uint2 lo2 = *(const uint2*)(row + kc);
         uint2 hi2 = *(const uint2*)(row + kc + 8);
         bf16x8 kf = __builtin_bit_cast(bf16x8, make_uint4(lo2.x, lo2.y, hi2.x, hi2.y));
         acc[hm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, dsf[st], acc[hm], 0, 0, 0);
       }
     }
+    if (it + 1 < ntiles) STORE_TILE((it + 1) & 1)
+    __syncthreads();
   }
+#undef LD
+#undef LOAD_TILE
+#undef ST
+#undef STORE_TILE
   if (!qok) return;
   const float sc = 1.f / sqrtf((float)HD);
   float* out = (SPLIT ? a.ws + (int64_t)sp * a.B * a.n * d : a.dq) + ((int64_t)b * a.n + tq) * d + (int64_t)h * HD;
@@ -666,28 +704,41 @@ __global__ void k_dq_reduce(const float* ws, int S, int64_t total, float* dq) {
   }
 }
 
+template <int HD, int NW, bool SPLIT>
+hipError_t launch_dq(const AttnBwdArgs& a, int S, hipStream_t s) {
+  static bool attr = false;
+  if (!attr) {
+    hipError_t e = set_lds<DqSmem<HD>>(k_swa_dq<HD, NW, SPLIT>);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  hipLaunchKernelGGL((k_swa_dq<HD, NW, SPLIT>), dim3(cdiv(a.n, NW * QW), a.H, a.B * S), dim3(NW * 64),
+                     sizeof(DqSmem<HD>), s, a, S);
+  return hipGetLastError();
+}
+
 template <int HD>
 hipError_t launch_bwd(const AttnBwdArgs& a, hipStream_t s) {
   static bool attr = false;
   if (!attr) {
-    hipError_t e = set_lds<DqSmem<HD>>(k_swa_dq<HD, false>);
-    if (e == hipSuccess) e = set_lds<DqSmem<HD>>(k_swa_dq<HD, true>);
-    if (e == hipSuccess) e = set_lds<DkvSmem<HD>>(k_swa_dkv<HD>);
+    hipError_t e = set_lds<DkvSmem<HD>>(k_swa_dkv<HD>);
     if (e != hipSuccess) return e;
     attr = true;
   }
   hipError_t e = swa_dvec_bf16(a, s);
   if (e != hipSuccess) return e;
-  const int64_t blocks = (int64_t)cdiv(a.n, BQ) * a.H * a.B;
-  const int64_t ntiles = (std::min<int64_t>(a.window, a.pos0 + 1) + BQ) / KT + 1;
+  const int64_t blocks8 = (int64_t)cdiv(a.n, 8 * QW) * a.H * a.B;
+  const int64_t ntiles = (std::min<int64_t>(a.window, a.pos0 + 1) + 8 * QW) / KT + 1;
   const int64_t total = (int64_t)a.B * a.n * a.H * HD;
-  const int S = attn_splits(blocks, ntiles, total, a.ws, a.ws_floats);
+  const int S = attn_splits(blocks8, ntiles, total, a.ws, a.ws_floats);
   if (S > 1) {
-    hipLaunchKernelGGL((k_swa_dq<HD, true>), dim3(cdiv(a.n, BQ), a.H, a.B * S), dim3(256), sizeof(DqSmem<HD>), s, a, S);
+    e = launch_dq<HD, 8, true>(a, S, s);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_dq_reduce, dim3((unsigned)std::min<int64_t>(cdiv(total, 256), 4096)), dim3(256), 0, s, a.ws,
                        S, total, a.dq);
   } else {
-    hipLaunchKernelGGL((k_swa_dq<HD, false>), dim3(cdiv(a.n, BQ), a.H, a.B), dim3(256), sizeof(DqSmem<HD>), s, a, 1);
+    e = launch_dq<HD, 8, false>(a, 1, s);
+    if (e != hipSuccess) return e;
   }
   dim3 grid(cdiv(a.n, BQ), a.H, a.B);
   hipLaunchKernelGGL(k_swa_dkv<HD>, grid, dim3(256), sizeof(DkvSmem<HD>), s, a);

@@ -69,8 +69,26 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(GemmArgs g) {
   const int nk = (kend - kbeg + BK - 1) / BK;
 
   uint4 ra[A_CH], rb[B_CH], ru[DUAL ? B_CH : 1];
+  // Interior tiles (the common case) load with straight-line 16-byte loads; only tiles
+  // that cross M, N or the end of K take the guarded path (a block-uniform branch, so
+  // the fast path has no per-load control flow or waits between loads).
+  const bool interior_mn = m0 + BM <= g.M && n0 + BN <= g.N;
   auto load = [&](int kt) {
     const int k0 = kbeg + kt * BK;
+    if (interior_mn && k0 + BK <= kend) {
+#pragma unroll
+      for (int i = 0; i < A_CH; ++i) {
+        const int c = tid + i * 256, r = c >> 3, kc = (c & 7) * 8;
+        ra[i] = *(const uint4*)(A + (int64_t)(m0 + r) * g.lda + k0 + kc);
+      }
+#pragma unroll
+      for (int i = 0; i < B_CH; ++i) {
+        const int c = tid + i * 256, r = c >> 3, kc = (c & 7) * 8;
+        rb[i] = *(const uint4*)(B + (int64_t)(n0 + r) * g.ldb + k0 + kc);
+        if constexpr (DUAL) ru[i] = *(const uint4*)(U + (int64_t)(n0 + r) * g.ldb + k0 + kc);
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < A_CH; ++i) {
       int c = tid + i * 256, r = c >> 3, kc = (c & 7) * 8;
