@@ -161,13 +161,15 @@ int64_t ttt_position(const ttt_ctx* ctx);
  * class, the summed device time (ms), the launch count and the algorithmic
  * FLOPs of those launches (matmul = 2 M N K; attention = 4 * head_dim per
  * visible query-key pair, plus 4 * head_dim per in-chunk pair in backward).
- * Classes: GEMMs by epilogue -- 0 fp32 output, 1 bf16 output, 2 residual add,
- * 3 SwiGLU (gate and up), 4 SwiGLU backward, 5 weight gradient with the fused
- * SGD step -- then 6 sliding-window attention forward, 7 its backward. */
+ * Classes: GEMMs without a K split by epilogue -- 0 fp32 output, 1 bf16 output,
+ * 2 residual add, 3 SwiGLU (gate and up), 4 SwiGLU backward, 5 weight gradient
+ * with the fused SGD step (one kernel each) -- 6 K-split GEMMs (kernel + ordered
+ * sum), 7 sliding-window attention forward (one kernel), 8 the same with a split
+ * key range (kernel + merge), 9 attention backward (all its kernels). */
 enum {
   TTT_PROF_GEMM_F32 = 0, TTT_PROF_GEMM_BF16 = 1, TTT_PROF_GEMM_RESID = 2, TTT_PROF_GEMM_SWIGLU = 3,
-  TTT_PROF_GEMM_SWIGLU_BWD = 4, TTT_PROF_GEMM_SGD = 5, TTT_PROF_SWA_FWD = 6, TTT_PROF_SWA_BWD = 7,
-  TTT_PROF_CLASSES = 8
+  TTT_PROF_GEMM_SWIGLU_BWD = 4, TTT_PROF_GEMM_SGD = 5, TTT_PROF_GEMM_SPLITK = 6, TTT_PROF_SWA_FWD = 7,
+  TTT_PROF_SWA_FWD_SPLIT = 8, TTT_PROF_SWA_BWD = 9, TTT_PROF_CLASSES = 10
 };
 int ttt_profile_enable(ttt_ctx* ctx, int32_t on);
 int ttt_profile_read(ttt_ctx* ctx, int32_t n_classes, double* ms, int64_t* counts, double* flops);

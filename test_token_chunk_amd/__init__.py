@@ -26,12 +26,20 @@ EXPORTS = ("ttt_set_allocator", "ttt_create", "ttt_prefill_chunk", "ttt_prefill"
            "ttt_generate", "ttt_get_fast_weights", "ttt_reset", "ttt_position", "ttt_destroy", "ttt_last_error",
            "ttt_profile_enable", "ttt_profile_read")
 PROFILE_CLASSES = ("gemm_f32out", "gemm_bf16out", "gemm_resid", "gemm_swiglu", "gemm_swiglu_bwd", "gemm_sgd",
-                   "swa_fwd", "swa_bwd")
-# kernel symbol of each class (as rocprofv3 names it), for the roofline cross-check
-PROFILE_KERNELS = {"gemm_f32out": "k_gemm_mfma<*, false, 0>", "gemm_bf16out": "k_gemm_mfma<*, false, 1>",
-                   "gemm_resid": "k_gemm_mfma<*, false, 2>", "gemm_swiglu": "k_gemm_mfma<*, true, 3>",
-                   "gemm_swiglu_bwd": "k_gemm_mfma<*, false, 4>", "gemm_sgd": "k_gemm_mfma<*, false, 5>",
-                   "swa_fwd": "k_swa_fwd<hd>", "swa_bwd": "k_dvec + k_swa_dq<hd> + k_swa_dkv<hd>"}
+                   "gemm_splitk", "swa_fwd", "swa_fwd_split", "swa_bwd")
+# kernels behind each class (rocprofv3 names); classes marked single=True are one kernel
+PROFILE_KERNELS = {
+    "gemm_f32out": ("k_gemm_mfma<128, 128, 64, 64, false, 0, false>", True),
+    "gemm_bf16out": ("k_gemm_mfma<128, 128, 64, 64, false, 1, false>", True),
+    "gemm_resid": ("k_gemm_mfma<128, 128, 64, 64, false, 2, false>", True),
+    "gemm_swiglu": ("k_gemm_mfma<128, 128, 64, 64, true, 3, false>", True),
+    "gemm_swiglu_bwd": ("k_gemm_mfma<128, 128, 64, 64, false, 4, false>", True),
+    "gemm_sgd": ("k_gemm_mfma<128, 128, 64, 64, false, 5, false>", True),
+    "gemm_splitk": ("k_gemm_mfma<128, 128, 64, 64, false, 0, true> + k_splitk_reduce<*>", False),
+    "swa_fwd": ("k_swa_fwd<hd, 8, false>", True),
+    "swa_fwd_split": ("k_swa_fwd<hd, 8, true> + k_swa_combine", False),
+    "swa_bwd": ("k_dvec + k_swa_dq<hd, 8, *> (+ k_dq_reduce) + k_swa_dkv<hd>", False),
+}
 
 
 class TTTError(RuntimeError):

@@ -324,7 +324,7 @@ hipError_t launch_fwd(const AttnArgs& a, hipStream_t s) {
   const int64_t ntiles = (std::min<int64_t>(a.window, a.pos0 + 1) + 8 * QW) / KT + 1;
   const int S = attn_splits(blocks8, ntiles, (int64_t)a.B * a.H * a.n * (HD + 2), a.ws, a.ws_floats);
   if (S > 1) return launch_fwd_nw<HD, 8, true>(a, S, s);
-  return launch_fwd_nw<HD, 4, false>(a, 1, s);
+  return launch_fwd_nw<HD, 8, false>(a, 1, s);
 }
 
 
@@ -746,6 +746,15 @@ hipError_t launch_bwd(const AttnBwdArgs& a, hipStream_t s) {
 }
 
 }  // namespace
+
+// key-range parts the forward would use for this call (1: single kernel)
+int swa_fwd_mfma_splits(const AttnArgs& a) {
+  if (a.n == 0 || a.R % 8 != 0 || (a.hd != 32 && a.hd != 64 && a.hd != 96 && a.hd != 128)) return 1;
+  const int64_t blocks8 = (int64_t)cdiv(a.n, 8 * QW) * a.H * a.B;
+  if (blocks8 >= 512) return 1;
+  const int64_t ntiles = (std::min<int64_t>(a.window, a.pos0 + 1) + 8 * QW) / KT + 1;
+  return attn_splits(blocks8, ntiles, (int64_t)a.B * a.H * a.n * (a.hd + 2), a.ws, a.ws_floats);
+}
 
 hipError_t swa_fwd_mfma(const AttnArgs& a, hipStream_t s) {
   if (a.n == 0) return hipSuccess;

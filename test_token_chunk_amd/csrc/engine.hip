@@ -156,8 +156,10 @@ int fail(ttt_ctx* c, int code, const std::string& msg) {
   } while (0)
 
 // ------------------------------------------------------------------ profiling
-// GEMM classes follow the epilogue kind (EPI_F32 .. EPI_SGD), then attention
-enum { PC_SWA_FWD = 6, PC_SWA_BWD = 7, PC_N = 8 };
+// Classes: GEMMs without split by epilogue kind (EPI_F32 .. EPI_SGD; one kernel each),
+// split-K GEMMs (kernel + ordered reduce), attention forward (one kernel), split-key
+// attention forward (kernel + combine), attention backward (dvec + dq + dk/dv)
+enum { PC_GEMM_SPLITK = 6, PC_SWA_FWD = 7, PC_SWA_FWD_SPLIT = 8, PC_SWA_BWD = 9, PC_N = 10 };
 
 hipEvent_t next_event(ttt_ctx* c) {
   if (c->ev_used == c->ev_pool.size()) {
@@ -220,7 +222,8 @@ struct Ops<bf16> {
     GemmArgs g = g0;
     g.ws = c->ws;
     g.ws_floats = c->ws_floats;
-    return timed(c, g.e.kind, gemm_flops(g),
+    const int cls = (c->mfma && gemm_mfma_splits(g, nullptr) > 1) ? PC_GEMM_SPLITK : g.e.kind;
+    return timed(c, cls, gemm_flops(g),
                  [&] { return c->mfma ? gemm_mfma_bf16(g, c->stream) : gemm_simt_bf16(g, c->stream); });
   }
   static hipError_t fwd(ttt_ctx* c, const AttnArgs& a0) {
@@ -228,7 +231,8 @@ struct Ops<bf16> {
     a.ws = c->ws;
     a.ws_floats = c->ws_floats;
     double fl = 4.0 * a.hd * a.H * a.B * attn_pairs(c, a.n, a.pos0);
-    return timed(c, PC_SWA_FWD, fl,
+    const int cls = (c->mfma && swa_fwd_mfma_splits(a) > 1) ? PC_SWA_FWD_SPLIT : PC_SWA_FWD;
+    return timed(c, cls, fl,
                  [&] { return c->mfma ? swa_fwd_mfma(a, c->stream) : swa_fwd_simt<bf16>(a, c->stream); });
   }
   static hipError_t bwd(ttt_ctx* c, const AttnBwdArgs& a0) {

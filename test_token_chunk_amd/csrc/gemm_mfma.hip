@@ -313,6 +313,21 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
 }  // namespace
 
+// split-K parts for this GEMM (1: no split); see gemm_mfma_bf16
+int gemm_mfma_splits(const GemmArgs& g, int* ks_out) {
+  const int64_t tiles = (int64_t)cdiv(g.M, 128) * cdiv(g.N, 128) * g.batch;
+  if (!(g.ws && tiles < 384 && g.K >= 1024 &&
+        (g.e.kind == EPI_F32 || g.e.kind == EPI_T || g.e.kind == EPI_ADD_F32)))
+    return 1;
+  int S = (int)std::min<int64_t>(8, (640 + tiles - 1) / tiles);
+  S = std::min(S, g.K / 256);
+  const int Ks = (int)cdiv(cdiv(g.K, S), BK) * BK;
+  S = (int)cdiv(g.K, Ks);
+  if (S < 2 || (int64_t)S * g.batch * g.M * g.N > g.ws_floats) return 1;
+  if (ks_out) *ks_out = Ks;
+  return S;
+}
+
 hipError_t gemm_mfma_bf16(const GemmArgs& g, hipStream_t s) {
   if (g.M <= 0 || g.N <= 0 || g.batch <= 0) return hipSuccess;
   // 16-byte vector loads need 8-element aligned rows and batch strides
@@ -322,15 +337,9 @@ hipError_t gemm_mfma_bf16(const GemmArgs& g, hipStream_t s) {
   // Small grids with a long K (the N = d GEMMs of the per-chunk upper blocks) split K
   // over several blocks into an fp32 workspace, then one pass sums the parts in a
   // fixed order and applies the epilogue.
-  const int64_t tiles = (int64_t)cdiv(g.M, 128) * cdiv(g.N, 128) * g.batch;
-  if (g.ws && tiles < 384 && g.K >= 1024 &&
-      (g.e.kind == EPI_F32 || g.e.kind == EPI_T || g.e.kind == EPI_ADD_F32)) {
-    int S = (int)std::min<int64_t>(8, (640 + tiles - 1) / tiles);
-    S = std::min(S, g.K / 256);
-    const int Ks = (int)cdiv(cdiv(g.K, S), BK) * BK;
-    S = (int)cdiv(g.K, Ks);
-    if (S >= 2 && (int64_t)S * g.batch * g.M * g.N <= g.ws_floats) return launch_splitk(g, S, Ks, s);
-  }
+  int Ks = 0;
+  const int S = gemm_mfma_splits(g, &Ks);
+  if (S > 1) return launch_splitk(g, S, Ks, s);
   switch (g.e.kind) {
     case EPI_SWIGLU: return launch<128, 128, 64, 64, true, EPI_SWIGLU>(g, s);
     case EPI_F32: return launch<128, 128, 64, 64, false, EPI_F32>(g, s);

@@ -67,6 +67,7 @@ struct GemmArgs {
 hipError_t gemm_simt_f32(const GemmArgs& g, hipStream_t s);   // fp32 operands
 hipError_t gemm_simt_bf16(const GemmArgs& g, hipStream_t s);  // bf16 operands, SIMT
 hipError_t gemm_mfma_bf16(const GemmArgs& g, hipStream_t s);  // bf16 operands, MFMA
+int gemm_mfma_splits(const GemmArgs& g, int* ks_out);          // split-K parts gemm_mfma_bf16 would use
 
 // ------------------------------------------------------------------ elementwise
 // Token arrays are [B][ld] int32 (row stride ld); activations are [B*n][d] rows.
@@ -111,6 +112,7 @@ struct AttnArgs {
 template <typename T>
 hipError_t swa_fwd_simt(const AttnArgs& a, hipStream_t s);
 hipError_t swa_fwd_mfma(const AttnArgs& a, hipStream_t s);  // bf16
+int swa_fwd_mfma_splits(const AttnArgs& a);                  // key-range parts it would use
 
 struct AttnBwdArgs {
   const void* q;    // [B][H][n][hd]
