@@ -32,7 +32,7 @@ PROFILE_KERNELS = {
     "gemm_f32out": ("k_gemm_mfma<128, 128, 64, 64, false, 0, false>", True),
     "gemm_bf16out": ("k_gemm_mfma<128, 128, 64, 64, false, 1, false>", True),
     "gemm_resid": ("k_gemm_mfma<128, 128, 64, 64, false, 2, false>", True),
-    "gemm_swiglu": ("k_gemm_mfma<128, 128, 64, 64, true, 3, false>", True),
+    "gemm_swiglu": ("k_gemm_mfma<128, 128, 64, 64, false, 7, false>", True),
     "gemm_swiglu_bwd": ("k_gemm_mfma<128, 128, 64, 64, false, 4, false>", True),
     "gemm_sgd": ("k_gemm_mfma<128, 128, 64, 64, false, 5, false>", True),
     "gemm_splitk": ("k_gemm_mfma<128, 128, 64, 64, false, 0, true> + k_splitk_reduce<*>", False),

@@ -226,7 +226,7 @@ __global__ void k_rope_bwd_pack(const float* dq, const float* dk, const float* d
 // shadow copies of fp32 master weights: sh = T(master) [rows][cols], shT = T(master)^T [cols][rows]
 template <typename T>
 __global__ void k_shadow(const float* master, int rows, int cols, int64_t sm, T* sh, int64_t ssh, T* shT,
-                         int64_t sshT) {
+                         int64_t sshT, int64_t il_f) {
   __shared__ float tile[32][33];
   int bz = blockIdx.z;
   int r0 = blockIdx.y * 32, c0 = blockIdx.x * 32;
@@ -236,7 +236,7 @@ __global__ void k_shadow(const float* master, int rows, int cols, int64_t sm, T*
     if (r < rows && q < cols) {
       float v = src[(int64_t)r * cols + q];
       tile[i][threadIdx.x] = v;
-      sh[bz * ssh + (int64_t)r * cols + q] = from_f<T>(v);
+      sh[bz * ssh + (il_f ? swiglu_il_row(r, il_f) : (int64_t)r) * cols + q] = from_f<T>(v);
     }
   }
   __syncthreads();
@@ -333,13 +333,14 @@ hipError_t rope_bwd_pack(const float* dq, const float* dk, const float* dv, cons
 }
 
 hipError_t refresh_shadows(const float* master, int rows, int cols, int batch, int64_t sm, void* sh, int64_t ssh,
-                           void* shT, int64_t sshT, int is_bf16, hipStream_t s) {
+                           void* shT, int64_t sshT, int is_bf16, int64_t il_f, hipStream_t s) {
   dim3 grid(cdiv(cols, 32), cdiv(rows, 32), batch), block(32, 8);
   if (is_bf16)
-    hipLaunchKernelGGL(k_shadow<bf16>, grid, block, 0, s, master, rows, cols, sm, (bf16*)sh, ssh, (bf16*)shT, sshT);
+    hipLaunchKernelGGL(k_shadow<bf16>, grid, block, 0, s, master, rows, cols, sm, (bf16*)sh, ssh, (bf16*)shT, sshT,
+                       il_f);
   else
     hipLaunchKernelGGL(k_shadow<float>, grid, block, 0, s, master, rows, cols, sm, (float*)sh, ssh, (float*)shT,
-                       sshT);
+                       sshT, il_f);
   return hipGetLastError();
 }
 

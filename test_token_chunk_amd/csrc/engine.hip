@@ -22,7 +22,7 @@
 #include "ttt.h"
 
 hipError_t refresh_shadows(const float* master, int rows, int cols, int batch, int64_t sm, void* sh, int64_t ssh,
-                           void* shT, int64_t sshT, int is_bf16, hipStream_t s);
+                           void* shT, int64_t sshT, int is_bf16, int64_t il_f, hipStream_t s);
 
 namespace {
 
@@ -68,6 +68,7 @@ struct ttt_ctx {
   bool bf16;
   size_t es;  // element size of T
   bool mfma = true;
+  bool il = false;  // gate/up rows interleaved for the single-operand SwiGLU GEMM (bf16 matrix-core path)
   hipStream_t stream = nullptr;
   ttt_free_fn free_fn = nullptr;
   void* free_user = nullptr;
@@ -222,7 +223,8 @@ struct Ops<bf16> {
     GemmArgs g = g0;
     g.ws = c->ws;
     g.ws_floats = c->ws_floats;
-    const int cls = (c->mfma && gemm_mfma_splits(g, nullptr) > 1) ? PC_GEMM_SPLITK : g.e.kind;
+    const int kind_cls = g.e.kind == EPI_SWIGLU_IL ? (int)EPI_SWIGLU : g.e.kind;  // one SwiGLU class
+    const int cls = (c->mfma && gemm_mfma_splits(g, nullptr) > 1) ? PC_GEMM_SPLITK : kind_cls;
     return timed(c, cls, gemm_flops(g),
                  [&] { return c->mfma ? gemm_mfma_bf16(g, c->stream) : gemm_simt_bf16(g, c->stream); });
   }
@@ -319,12 +321,12 @@ int layer_fwd(ttt_ctx* c, int l, float* h, int n, int64_t p0, int mode, TopActs*
                     sv ? tp<T>(sv->mT) : (T*)nullptr, n, c->b, c->stream));
   if (l >= c->l0) {
     const FastW& fw = c->fw[l - c->l0];
-    GemmArgs g = mk(c->ub, d, fw.wgu, d, n, f, d);
+    GemmArgs g = mk(c->ub, d, fw.wgu, d, n, c->il ? 2 * f : f, d);
     g.batch = B;
     g.sA = (int64_t)n * d;
     g.sB = 2LL * f * d;
-    g.dual_off = f;
-    g.e.kind = EPI_SWIGLU;
+    g.dual_off = c->il ? 0 : f;
+    g.e.kind = c->il ? EPI_SWIGLU_IL : EPI_SWIGLU;
     g.e.c = c->actb;
     g.e.ldc = f;
     g.e.sc = (int64_t)n * f;
@@ -348,9 +350,9 @@ int layer_fwd(ttt_ctx* c, int l, float* h, int n, int64_t p0, int mode, TopActs*
     gd.e.sc = (int64_t)n * d;
     CK(Ops<T>::gemm(c, gd));
   } else {
-    GemmArgs g = mk(c->ub, d, w.wgu, d, (int)M, f, d);
-    g.dual_off = f;
-    g.e.kind = EPI_SWIGLU;
+    GemmArgs g = mk(c->ub, d, w.wgu, d, (int)M, c->il ? 2 * f : f, d);
+    g.dual_off = c->il ? 0 : f;
+    g.e.kind = c->il ? EPI_SWIGLU_IL : EPI_SWIGLU;
     g.e.c = c->actb;
     g.e.ldc = f;
     CK(Ops<T>::gemm(c, g));
@@ -476,6 +478,7 @@ int top_chunk(ttt_ctx* c, const int32_t* tgt, int64_t ld, const float* hsrc, int
     g4.e.ldshT = 2 * f;
     g4.e.sshT = 2LL * d * f;
     g4.e.lr = lr;
+    g4.e.il_f = c->il ? f : 0;
     CK(Ops<T>::gemm(c, g4));
     if (j == 0) break;
     const LayerW& lw = c->lw[l];
@@ -678,8 +681,17 @@ int build(ttt_ctx* c, const ttt_weights* w) {
     if (l < c->l0) {
       AL(lw.wgu, 2LL * f * d * es);
       AL(lw.wd, (int64_t)d * f * es);
-      if ((rc = upload(c, lw.wgu, w->w_gate[l], (int64_t)f * d))) return rc;
-      if ((rc = upload(c, (char*)lw.wgu + (int64_t)f * d * es, w->w_up[l], (int64_t)f * d))) return rc;
+      if (c->il) {  // [W_gate; W_up] rows placed at swiglu_il_row
+        std::vector<float> gu((size_t)2 * f * d);
+        for (int64_t r = 0; r < 2LL * f; ++r) {
+          const float* src = r < f ? w->w_gate[l] + r * d : w->w_up[l] + (r - f) * d;
+          memcpy(gu.data() + swiglu_il_row(r, f) * d, src, (size_t)d * 4);
+        }
+        if ((rc = upload(c, lw.wgu, gu.data(), 2LL * f * d))) return rc;
+      } else {
+        if ((rc = upload(c, lw.wgu, w->w_gate[l], (int64_t)f * d))) return rc;
+        if ((rc = upload(c, (char*)lw.wgu + (int64_t)f * d * es, w->w_up[l], (int64_t)f * d))) return rc;
+      }
       if ((rc = upload(c, lw.wd, w->w_down[l], (int64_t)d * f))) return rc;
     }
     AL(lw.kr, ring);
@@ -783,9 +795,9 @@ int reset_state(ttt_ctx* c) {
     for (int r = 0; r < c->B; ++r)
       CK(hipMemcpyAsync(fw.master + r * fsz, c->fast_init + j * fsz, fsz * 4, hipMemcpyDeviceToDevice, c->stream));
     CK(refresh_shadows(fw.master, 2 * c->f, c->d, c->B, fsz, fw.wgu, 2LL * c->f * c->d, fw.wguT, 2LL * c->f * c->d,
-                       c->bf16, c->stream));
+                       c->bf16, c->il ? c->f : 0, c->stream));
     CK(refresh_shadows(fw.master + 2LL * c->f * c->d, c->d, c->f, c->B, fsz, fw.wd, (int64_t)c->d * c->f, fw.wdT,
-                       (int64_t)c->d * c->f, c->bf16, c->stream));
+                       (int64_t)c->d * c->f, c->bf16, 0, c->stream));
   }
   const int64_t ring = (int64_t)c->B * c->H * c->R * c->hd * c->es;
   for (int l = 0; l < c->L; ++l) {
@@ -883,6 +895,7 @@ int ttt_create(const ttt_config* cfg, const ttt_weights* w, void* hip_stream, tt
   c->free_user = g_user;
   const char* simt = getenv("TTT_SIMT");
   c->mfma = !(simt && simt[0] == '1');
+  c->il = c->bf16 && c->mfma && c0.d_ff % 32 == 0 && c0.d_model % 8 == 0;
   int rc = build(c, w);
   if (rc == TTT_OK) rc = reset_state(c);
   if (rc != TTT_OK) {

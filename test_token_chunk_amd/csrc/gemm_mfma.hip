@@ -160,15 +160,66 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(GemmArgs g) {
   // epilogue: C[row 8q + 4*(l/32) + i][col l%32] = acc[4q + i].
   // Outputs stored transposed ([n][m]: the refreshed W^T shadow of the fused SGD step,
   // act^T, dz^T) are staged through LDS and written as 16-byte row segments.
-  constexpr bool TR = (EK == EPI_SGD) || (EK == EPI_SWIGLU_BWD) || DUAL;
+  constexpr bool TR = (EK == EPI_SGD) || (EK == EPI_SWIGLU_BWD) || DUAL || (EK == EPI_SWIGLU_IL);
+  static_assert(EK != EPI_SWIGLU_IL || TN == 2, "interleaved SwiGLU pairs the two 32-column halves of a wave");
   constexpr int TLD = BM + 8;
   bf16* tr0 = reinterpret_cast<bf16*>(smem_raw);  // [BN][TLD]
   bf16* tr1 = tr0 + BN * TLD;                     // second tile (dz_u^T)
   static_assert(!TR || (EK == EPI_SWIGLU_BWD ? 2 : 1) * BN * TLD * 2 <= (int)sizeof(Smem<BM, BN, DUAL>),
                 "transpose staging fits in the operand buffers");
-  const bool want_t = TR && (EK != EPI_SWIGLU || g.e.t != nullptr);
+  const bool want_t = TR && ((EK != EPI_SWIGLU && EK != EPI_SWIGLU_IL) || g.e.t != nullptr);
   const int hi = lane >> 5;
   const Epi& e = g.e;
+  // Epilogues that read memory (fp32 master, residual stream, saved z_g/z_u) first load
+  // every element of the lane into registers, then compute and store: interleaving a
+  // load with the stores of earlier elements would serialize each element on a full
+  // memory round trip (the stores may alias the loads).
+  constexpr bool READS = (EK == EPI_SGD) || (EK == EPI_ADD_F32);
+  constexpr int NE = TM * TN * 16;
+  float pre0[READS ? NE : 1];
+  if constexpr (READS) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int n = n0 + wn0 + j * 32 + lr;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int m = m0 + wm0 + i * 32 + 8 * q + 4 * hi + r;
+            const int idx = (i * TN + j) * 16 + 4 * q + r;
+            const bool in = m < g.M && n < g.N;
+            if constexpr (EK == EPI_SGD) {
+              pre0[idx] = in ? e.master[bz * e.sm + (int64_t)m * e.ldm + n] : 0.f;
+            } else {
+              pre0[idx] = in ? ((const float*)e.c)[bz * e.sc + (int64_t)m * e.ldc + n] : 0.f;
+            }
+          }
+      }
+  }
+  if constexpr (EK == EPI_SWIGLU_IL) {
+    // lane holds gate column (j = 0) and up column (j = 1) of hidden unit fi
+    const int fl = wn0 / 2 + lr, fi = n0 / 2 + fl;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int ml = wm0 + i * 32 + 8 * q + 4 * hi + r, m = m0 + ml;
+          const float x = acc[i][0][4 * q + r], u = acc[i][1][4 * q + r];
+          const float act = x / (1.f + __expf(-x)) * u;
+          if (m < g.M && 2 * fi < g.N) {
+            ((bf16*)e.c)[bz * e.sc + (int64_t)m * e.ldc + fi] = f2bf(act);
+            if (e.zg) {
+              ((bf16*)e.zg)[bz * e.sz + (int64_t)m * e.ldz + fi] = f2bf(x);
+              ((bf16*)e.zu)[bz * e.sz + (int64_t)m * e.ldz + fi] = f2bf(u);
+            }
+          }
+          tr0[fl * TLD + ml] = f2bf(act);
+        }
+  } else
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -179,6 +230,7 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(GemmArgs g) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int ml = wm0 + i * 32 + 8 * q + 4 * hi + r, m = m0 + ml;
+          const int idx = (i * TN + j) * 16 + 4 * q + r;
           const bool in = m < g.M && n < g.N;
           const float x = acc[i][j][4 * q + r];
           if constexpr (DUAL) {
@@ -194,10 +246,10 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(GemmArgs g) {
             tr0[nl * TLD + ml] = f2bf(act);
           } else if constexpr (EK == EPI_SGD) {
             if (in) {
-              float* p = e.master + bz * e.sm + (int64_t)m * e.ldm + n;
-              const float w = *p - e.lr * x;
-              *p = w;
-              ((bf16*)e.sh)[bz * e.ssh + (int64_t)m * e.ldsh + n] = f2bf(w);
+              const float w = pre0[idx] - e.lr * x;
+              e.master[bz * e.sm + (int64_t)m * e.ldm + n] = w;
+              const int64_t shrow = e.il_f ? swiglu_il_row(m, e.il_f) : m;
+              ((bf16*)e.sh)[bz * e.ssh + shrow * e.ldsh + n] = f2bf(w);
               tr0[nl * TLD + ml] = f2bf(w);
             }
           } else if constexpr (EK == EPI_SWIGLU_BWD) {
@@ -213,6 +265,8 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(GemmArgs g) {
               tr0[nl * TLD + ml] = f2bf(dzg);
               tr1[nl * TLD + ml] = f2bf(dzu);
             }
+          } else if constexpr (EK == EPI_ADD_F32) {
+            if (in) ((float*)e.c)[bz * e.sc + (int64_t)m * e.ldc + n] = pre0[idx] + x;
           } else if constexpr (SPLIT) {
             if (in) g.ws[(((int64_t)split * (gridDim.z / S) + bz) * g.M + m) * g.N + n] = x;
           } else {
@@ -237,10 +291,13 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(GemmArgs g) {
     }
     const bool vec = (ld % 8) == 0 && (((uintptr_t)dst0) & 15) == 0;
     constexpr int CH = BM / 8;  // 16-byte chunks per tile row
-    for (int cidx = tid; cidx < BN * CH; cidx += 256) {
+    constexpr int ROWS = EK == EPI_SWIGLU_IL ? BN / 2 : BN;
+    const int row0 = EK == EPI_SWIGLU_IL ? n0 / 2 : n0;
+    const int nrows = EK == EPI_SWIGLU_IL ? g.N / 2 : g.N;
+    for (int cidx = tid; cidx < ROWS * CH; cidx += 256) {
       const int nl = cidx / CH, ml = (cidx % CH) * 8;
-      const int n = n0 + nl, m = m0 + ml;
-      if (n >= g.N || m >= g.M) continue;
+      const int n = row0 + nl, m = m0 + ml;
+      if (n >= nrows || m >= g.M) continue;
 #pragma unroll
       for (int t = 0; t < (EK == EPI_SWIGLU_BWD ? 2 : 1); ++t) {
         const bf16* srow = (t ? tr1 : tr0) + nl * TLD + ml;
@@ -333,7 +390,8 @@ hipError_t gemm_mfma_bf16(const GemmArgs& g, hipStream_t s) {
   // 16-byte vector loads need 8-element aligned rows and batch strides
   bool ok = aligned16(g.A) && aligned16(g.B) && g.lda % 8 == 0 && g.ldb % 8 == 0 && g.sA % 8 == 0 &&
             g.sB % 8 == 0 && (g.dual_off * g.ldb) % 8 == 0 && g.K >= 1;
-  if (!ok) return gemm_simt_bf16(g, s);
+  if (!ok) return g.e.kind == EPI_SWIGLU_IL ? hipErrorInvalidValue : gemm_simt_bf16(g, s);
+  if (g.e.kind == EPI_SWIGLU_IL && (g.N % 64 != 0)) return hipErrorInvalidValue;
   // Small grids with a long K (the N = d GEMMs of the per-chunk upper blocks) split K
   // over several blocks into an fp32 workspace, then one pass sums the parts in a
   // fixed order and applies the epilogue.
@@ -342,6 +400,7 @@ hipError_t gemm_mfma_bf16(const GemmArgs& g, hipStream_t s) {
   if (S > 1) return launch_splitk(g, S, Ks, s);
   switch (g.e.kind) {
     case EPI_SWIGLU: return launch<128, 128, 64, 64, true, EPI_SWIGLU>(g, s);
+    case EPI_SWIGLU_IL: return launch<128, 128, 64, 64, false, EPI_SWIGLU_IL>(g, s);
     case EPI_F32: return launch<128, 128, 64, 64, false, EPI_F32>(g, s);
     case EPI_T: return launch<128, 128, 64, 64, false, EPI_T>(g, s);
     case EPI_ADD_F32: return launch<128, 128, 64, 64, false, EPI_ADD_F32>(g, s);

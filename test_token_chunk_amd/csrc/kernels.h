@@ -14,8 +14,17 @@ enum EpiKind {
   EPI_SWIGLU = 3,  // dual: act = silu(acc_g) * acc_u -> c (T); zg, zu (T) and act^T (T) optional
   EPI_SWIGLU_BWD = 4, // acc = d act: dz_g, dz_u -> c = dz (T, [m][2f]) and dz^T (T, [2f][ldt])
   EPI_SGD = 5,     // acc = gradient: master (fp32) -= lr * acc; shadow (T) and shadow^T (T) refreshed
-  EPI_QKV_ROPE = 6 // acc = [q|k|v] row: RoPE of q, k; q -> c, k,v -> rings (see RopeRing)
+  EPI_QKV_ROPE = 6, // acc = [q|k|v] row: RoPE of q, k; q -> c, k,v -> rings (see RopeRing)
+  EPI_SWIGLU_IL = 7 // single operand with gate/up rows interleaved in groups of 32 (see swiglu_il_row):
+                    // columns 64g..64g+31 are gate rows 32g.., 64g+32..64g+63 the matching up rows;
+                    // outputs as EPI_SWIGLU with N = 2f (act, z_g, z_u [m][f], act^T)
 };
+
+// row of the interleaved [gate; up] weight that holds row r (< 2f) of the stacked [W_gate; W_up]
+__host__ __device__ inline int64_t swiglu_il_row(int64_t r, int64_t f) {
+  const int64_t u = r >= f ? 1 : 0, rr = r - u * f;
+  return 64 * (rr / 32) + 32 * u + rr % 32;
+}
 
 struct RopeRing {
   const float* cos_t;  // [max_pos][hd/2]
@@ -49,6 +58,7 @@ struct Epi {
   void* shT = nullptr;
   int64_t ldshT = 0, sshT = 0;
   float lr = 0.f;
+  int64_t il_f = 0;  // EPI_SGD: > 0 writes the row-major shadow with gate/up rows interleaved (f = il_f)
   RopeRing rr;
 };
 
