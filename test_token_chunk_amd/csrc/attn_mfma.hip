@@ -534,15 +534,17 @@ struct DkvSmem {
   float dd[KT];
 };
 
+// P > 1: blockIdx.z = b * P + part; the block covers part `part` of its key block's query
+// tiles and writes partial dK / dV to ws[part] / ws[P + part] (each [B*n][H*hd]).
 template <int HD>
-__global__ __launch_bounds__(256) void k_swa_dkv(AttnBwdArgs a) {
+__global__ __launch_bounds__(256) void k_swa_dkv(AttnBwdArgs a, int P) {
   constexpr int KS = HD / 16, HM = HD / 32;
   constexpr int KCH = KT * HD / 8 / 256;
   static_assert(KCH <= 4, "tile staging covers HD <= 128");
   extern __shared__ __align__(16) unsigned char smem_raw[];
   DkvSmem<HD>& sm = *reinterpret_cast<DkvSmem<HD>*>(smem_raw);
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, g = lane >> 5;
-  const int b = blockIdx.z, h = blockIdx.y;
+  const int b = blockIdx.z / P, h = blockIdx.y, part = blockIdx.z % P;
   const int64_t bh = (int64_t)b * a.H + h;
   const int R = a.R, d = a.H * HD;
   const int s0blk = blockIdx.x * BQ;
@@ -571,11 +573,13 @@ __global__ __launch_bounds__(256) void k_swa_dkv(AttnBwdArgs a) {
     dk[i] = f32x16{};
     dv[i] = f32x16{};
   }
-  // queries t >= first key of the block, up to the end of the chunk
-  const int tbeg = (s0blk / KT) * KT;
-  const int qb = blockIdx.x * BQ;
-  (void)qb;
-  for (int tq0 = tbeg; tq0 < a.n; tq0 += KT) {
+  // queries t >= first key of the block, up to the end of the chunk; part `part` of them
+  const int tfirst = (s0blk / KT) * KT;
+  const int ntq = (a.n - tfirst + KT - 1) / KT;
+  const int per = (ntq + P - 1) / P;
+  const int tbeg = tfirst + part * per * KT;
+  const int tstop = min(a.n, tfirst + (part + 1) * per * KT);
+  for (int tq0 = tbeg; tq0 < tstop; tq0 += KT) {
     uint4 rq0, rq1, rq2, rq3, ro0, ro1, ro2, ro3;
 #define LD(i, dq_, do_)                                                                     \
   if constexpr (KCH > i) {                                                                  \
@@ -677,8 +681,9 @@ __global__ __launch_bounds__(256) void k_swa_dkv(AttnBwdArgs a) {
   }
   if (!kok) return;
   const float sc = 1.f / sqrtf((float)HD);
-  float* ok_ = a.dk + ((int64_t)b * a.n + sk) * d + (int64_t)h * HD;
-  float* ov_ = a.dv + ((int64_t)b * a.n + sk) * d + (int64_t)h * HD;
+  const int64_t plane = (int64_t)a.B * a.n * d;
+  float* ok_ = (P > 1 ? a.ws + part * plane : a.dk) + ((int64_t)b * a.n + sk) * d + (int64_t)h * HD;
+  float* ov_ = (P > 1 ? a.ws + (P + part) * plane : a.dv) + ((int64_t)b * a.n + sk) * d + (int64_t)h * HD;
 #pragma unroll
   for (int hm = 0; hm < HM; ++hm)
 #pragma unroll
@@ -693,6 +698,19 @@ __global__ __launch_bounds__(256) void k_swa_dkv(AttnBwdArgs a) {
 template <typename Smem, typename K>
 hipError_t set_lds(K kern) {
   return hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(Smem));
+}
+
+// dk = sum_p ws[p], dv = sum_p ws[P + p], in order
+__global__ void k_dkv_reduce(const float* ws, int P, int64_t total, float* dk, float* dv) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+    float sk = 0.f, sv = 0.f;
+    for (int p = 0; p < P; ++p) {
+      sk += ws[p * total + i];
+      sv += ws[(P + p) * total + i];
+    }
+    dk[i] = sk;
+    dv[i] = sv;
+  }
 }
 
 // dq = sum over the key-range parts, in order
@@ -740,8 +758,18 @@ hipError_t launch_bwd(const AttnBwdArgs& a, hipStream_t s) {
     e = launch_dq<HD, 8, false>(a, 1, s);
     if (e != hipSuccess) return e;
   }
-  dim3 grid(cdiv(a.n, BQ), a.H, a.B);
-  hipLaunchKernelGGL(k_swa_dkv<HD>, grid, dim3(256), sizeof(DkvSmem<HD>), s, a);
+  // dK/dV: split each key block's query range when the grid is small (ordered sum after)
+  const int64_t kblocks = (int64_t)cdiv(a.n, BQ) * a.H * a.B;
+  int P = 1;
+  if (a.ws && kblocks < 384) {
+    P = (int)std::min<int64_t>(4, (512 + kblocks - 1) / kblocks);
+    P = std::min(P, (int)cdiv(a.n, KT));
+    while (P > 1 && 2LL * P * total > a.ws_floats) --P;
+  }
+  hipLaunchKernelGGL(k_swa_dkv<HD>, dim3(cdiv(a.n, BQ), a.H, a.B * P), dim3(256), sizeof(DkvSmem<HD>), s, a, P);
+  if (P > 1)
+    hipLaunchKernelGGL(k_dkv_reduce, dim3((unsigned)std::min<int64_t>(cdiv(total, 256), 4096)), dim3(256), 0, s,
+                       a.ws, P, total, a.dk, a.dv);
   return hipGetLastError();
 }
 

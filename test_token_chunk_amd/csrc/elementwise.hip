@@ -159,40 +159,61 @@ __global__ void k_copy_rows(const float* src, int64_t sbs, float* dst, int n, in
 
 // RoPE (rotate-half pairs (i, i+hd/2)) of q and k from a fp32 [B*n][3d] projection,
 // and the write of rotated keys and values into the window ring at slot = pos mod R.
+// One block handles 64 consecutive tokens of one (row, head); the transposed outputs
+// (V^T ring, optional q^T) go through LDS so that each of their rows is written as 64
+// consecutive tokens.
+constexpr int RT = 64;  // tokens per block
 template <typename T>
-__global__ void k_rope_qkv(const float* qkv, RopeRing rr) {
-  int64_t m = blockIdx.x;
-  int h = blockIdx.y;
-  int b = (int)(m / rr.n), t = (int)(m % rr.n);
-  int hd = rr.hd, half = hd / 2, d = rr.H * hd;
-  int64_t pos = rr.pos0 + t;
-  int slot = (int)(pos % rr.R);
-  const float* row = qkv + m * 3 * d + h * hd;
-  int64_t bh = (int64_t)b * rr.H + h;
-  T* q = (T*)rr.q + (bh * rr.n + t) * hd;
-  T* kr = (T*)rr.kr + (bh * rr.R + slot) * hd;
-  T* vr = (T*)rr.vr + (bh * rr.R + slot) * hd;
-  T* vtr = (T*)rr.vtr + bh * hd * rr.R + slot;
-  T* qt = rr.qt ? (T*)rr.qt + bh * hd * rr.n + t : nullptr;
-  for (int i = threadIdx.x; i < half; i += blockDim.x) {
-    float c = rr.cos_t[pos * half + i], s = rr.sin_t[pos * half + i];
+__global__ __launch_bounds__(256) void k_rope_qkv(const float* __restrict__ qkv, RopeRing rr) {
+  __shared__ T vt[128][RT + 2];  // [dim][token]
+  __shared__ T qs[128][RT + 2];
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int t0 = blockIdx.x * RT;
+  const int hd = rr.hd, half = hd / 2, d = rr.H * hd;
+  const int nt = min(RT, rr.n - t0);
+  const int64_t bh = (int64_t)b * rr.H + h;
+  T* Q = (T*)rr.q;
+  T* Kr = (T*)rr.kr;
+  T* Vr = (T*)rr.vr;
+  // rotated q, k and plain v: thread -> (token, pair) over 64 x hd/2
+  for (int e = threadIdx.x; e < RT * half; e += blockDim.x) {
+    const int tt = e / half, i = e % half;
+    if (tt >= nt) continue;
+    const int t = t0 + tt;
+    const int64_t pos = rr.pos0 + t;
+    const int slot = (int)(pos % rr.R);
+    const float* row = qkv + ((int64_t)b * rr.n + t) * 3 * d + h * hd;
+    const float c = rr.cos_t[pos * half + i], s = rr.sin_t[pos * half + i];
     float a = row[i], bb = row[i + half];
-    float q0 = a * c - bb * s, q1 = bb * c + a * s;
-    q[i] = from_f<T>(q0);
-    q[i + half] = from_f<T>(q1);
-    if (qt) {
-      qt[(int64_t)i * rr.n] = from_f<T>(q0);
-      qt[(int64_t)(i + half) * rr.n] = from_f<T>(q1);
-    }
+    const float q0 = a * c - bb * s, q1 = bb * c + a * s;
+    T* qrow = Q + (bh * rr.n + t) * hd;
+    qrow[i] = from_f<T>(q0);
+    qrow[i + half] = from_f<T>(q1);
+    qs[i][tt] = from_f<T>(q0);
+    qs[i + half][tt] = from_f<T>(q1);
     a = row[d + i];
     bb = row[d + i + half];
-    kr[i] = from_f<T>(a * c - bb * s);
-    kr[i + half] = from_f<T>(bb * c + a * s);
-    float v0 = row[2 * d + i], v1 = row[2 * d + i + half];
-    vr[i] = from_f<T>(v0);
-    vr[i + half] = from_f<T>(v1);
-    vtr[(int64_t)i * rr.R] = from_f<T>(v0);
-    vtr[(int64_t)(i + half) * rr.R] = from_f<T>(v1);
+    T* krow = Kr + (bh * rr.R + slot) * hd;
+    krow[i] = from_f<T>(a * c - bb * s);
+    krow[i + half] = from_f<T>(bb * c + a * s);
+    const float v0 = row[2 * d + i], v1 = row[2 * d + i + half];
+    T* vrow = Vr + (bh * rr.R + slot) * hd;
+    vrow[i] = from_f<T>(v0);
+    vrow[i + half] = from_f<T>(v1);
+    vt[i][tt] = from_f<T>(v0);
+    vt[i + half][tt] = from_f<T>(v1);
+  }
+  __syncthreads();
+  // V^T ring rows: [dim][slot], consecutive tokens -> consecutive slots (mod R)
+  T* Vt = (T*)rr.vtr + bh * hd * rr.R;
+  T* Qt = rr.qt ? (T*)rr.qt + bh * hd * rr.n : nullptr;
+  for (int e = threadIdx.x; e < hd * RT; e += blockDim.x) {
+    const int dim = e / RT, tt = e % RT;
+    if (tt >= nt) continue;
+    const int t = t0 + tt;
+    const int slot = (int)((rr.pos0 + t) % rr.R);
+    Vt[(int64_t)dim * rr.R + slot] = vt[dim][tt];
+    if (Qt) Qt[(int64_t)dim * rr.n + t] = qs[dim][tt];
   }
 }
 
@@ -313,12 +334,12 @@ hipError_t copy_rows(const float* src, int64_t src_batch_stride, float* dst, int
 
 hipError_t rope_qkv_f32in(const float* qkv, int B, const RopeRing& rr, int is_bf16, hipStream_t s) {
   if (B * rr.n == 0) return hipSuccess;
-  dim3 grid(B * rr.n, rr.H);
-  int th = rr.hd / 2 >= 64 ? 64 : 32;
+  if (rr.hd > 128) return hipErrorInvalidValue;
+  dim3 grid(cdiv(rr.n, RT), rr.H, B);
   if (is_bf16)
-    hipLaunchKernelGGL(k_rope_qkv<bf16>, grid, dim3(th), 0, s, qkv, rr);
+    hipLaunchKernelGGL(k_rope_qkv<bf16>, grid, dim3(256), 0, s, qkv, rr);
   else
-    hipLaunchKernelGGL(k_rope_qkv<float>, grid, dim3(th), 0, s, qkv, rr);
+    hipLaunchKernelGGL(k_rope_qkv<float>, grid, dim3(256), 0, s, qkv, rr);
   return hipGetLastError();
 }
 
