@@ -16,6 +16,7 @@
 #include <algorithm>
 #include <cmath>
 #include <string>
+#include <type_traits>
 #include <vector>
 
 #include "kernels.h"
@@ -70,6 +71,9 @@ struct ttt_ctx {
   bool mfma = true;
   bool il = false;  // gate/up rows interleaved for the single-operand SwiGLU GEMM (bf16 matrix-core path)
   hipStream_t stream = nullptr;
+  // second stream for the fused-SGD weight-gradient GEMMs, which only the next chunk depends on
+  hipStream_t side = nullptr;
+  hipEvent_t ev_m2s = nullptr, ev_s2m = nullptr;
   ttt_free_fn free_fn = nullptr;
   void* free_user = nullptr;
   std::vector<void*> allocs;
@@ -90,7 +94,8 @@ struct ttt_ctx {
   void *hf = nullptr, *dlogits = nullptr;
   int* nvalid = nullptr;
   float *dh = nullptr, *tmpf = nullptr, *dq = nullptr, *dk = nullptr, *dv = nullptr, *dvec = nullptr;
-  void *dyN = nullptr, *dyT = nullptr, *dz = nullptr, *dzT = nullptr, *dhT = nullptr, *dO = nullptr, *dqkv = nullptr;
+  void *dyN = nullptr, *dz = nullptr, *dhT = nullptr, *dO = nullptr, *dqkv = nullptr;
+  std::vector<void*> dyT, dzT;  // per fast block: inputs of its weight-gradient GEMMs (side stream)
   int* err_dev = nullptr;
   float* ws = nullptr;  // split-K / split-key workspace (used by one launch at a time)
   int64_t ws_floats = 0;
@@ -173,15 +178,15 @@ hipEvent_t next_event(ttt_ctx* c) {
 
 // run `launch` (returns hipError_t); with profiling on, bracket it with events
 template <typename F>
-hipError_t timed(ttt_ctx* c, int cls, double flops, F&& launch) {
+hipError_t timed(ttt_ctx* c, int cls, double flops, hipStream_t st, F&& launch) {
   if (!c->prof) return launch();
   hipEvent_t a = next_event(c), b = next_event(c);
   if (!a || !b) return hipErrorOutOfMemory;
-  hipError_t e = hipEventRecord(a, c->stream);
+  hipError_t e = hipEventRecord(a, st);
   if (e != hipSuccess) return e;
   e = launch();
   if (e != hipSuccess) return e;
-  e = hipEventRecord(b, c->stream);
+  e = hipEventRecord(b, st);
   c->prof_recs.push_back({cls, flops, a, b});
   return e;
 }
@@ -203,30 +208,33 @@ double gemm_flops(const GemmArgs& g) {
 
 template <>
 struct Ops<float> {
-  static hipError_t gemm(ttt_ctx* c, const GemmArgs& g) {
-    return timed(c, g.e.kind, gemm_flops(g), [&] { return gemm_simt_f32(g, c->stream); });
+  static hipError_t gemm(ttt_ctx* c, const GemmArgs& g, hipStream_t st = nullptr) {
+    if (!st) st = c->stream;
+    return timed(c, g.e.kind, gemm_flops(g), st, [&] { return gemm_simt_f32(g, st); });
   }
   static hipError_t fwd(ttt_ctx* c, const AttnArgs& a) {
     double fl = 4.0 * a.hd * a.H * a.B * attn_pairs(c, a.n, a.pos0);
-    return timed(c, PC_SWA_FWD, fl, [&] { return swa_fwd_simt<float>(a, c->stream); });
+    return timed(c, PC_SWA_FWD, fl, c->stream, [&] { return swa_fwd_simt<float>(a, c->stream); });
   }
   static hipError_t bwd(ttt_ctx* c, const AttnBwdArgs& a) {
     double fl = 4.0 * a.hd * a.H * a.B * (attn_pairs(c, a.n, a.pos0) + 0.5 * a.n * (a.n + 1.0));
-    return timed(c, PC_SWA_BWD, fl, [&] { return swa_bwd_simt<float>(a, c->stream); });
+    return timed(c, PC_SWA_BWD, fl, c->stream, [&] { return swa_bwd_simt<float>(a, c->stream); });
   }
 };
 
 // the bf16 kernels may use the context's workspace to split under-filled grids
 template <>
 struct Ops<bf16> {
-  static hipError_t gemm(ttt_ctx* c, const GemmArgs& g0) {
+  // st: the side stream (no workspace there: the split workspace belongs to the main stream)
+  static hipError_t gemm(ttt_ctx* c, const GemmArgs& g0, hipStream_t st = nullptr) {
     GemmArgs g = g0;
-    g.ws = c->ws;
-    g.ws_floats = c->ws_floats;
+    g.ws = st ? nullptr : c->ws;
+    g.ws_floats = st ? 0 : c->ws_floats;
+    if (!st) st = c->stream;
     const int kind_cls = g.e.kind == EPI_SWIGLU_IL ? (int)EPI_SWIGLU : g.e.kind;  // one SwiGLU class
     const int cls = (c->mfma && gemm_mfma_splits(g, nullptr) > 1) ? PC_GEMM_SPLITK : kind_cls;
-    return timed(c, cls, gemm_flops(g),
-                 [&] { return c->mfma ? gemm_mfma_bf16(g, c->stream) : gemm_simt_bf16(g, c->stream); });
+    return timed(c, cls, gemm_flops(g), st,
+                 [&] { return c->mfma ? gemm_mfma_bf16(g, st) : gemm_simt_bf16(g, st); });
   }
   static hipError_t fwd(ttt_ctx* c, const AttnArgs& a0) {
     AttnArgs a = a0;
@@ -234,7 +242,7 @@ struct Ops<bf16> {
     a.ws_floats = c->ws_floats;
     double fl = 4.0 * a.hd * a.H * a.B * attn_pairs(c, a.n, a.pos0);
     const int cls = (c->mfma && swa_fwd_mfma_splits(a) > 1) ? PC_SWA_FWD_SPLIT : PC_SWA_FWD;
-    return timed(c, cls, fl,
+    return timed(c, cls, fl, c->stream,
                  [&] { return c->mfma ? swa_fwd_mfma(a, c->stream) : swa_fwd_simt<bf16>(a, c->stream); });
   }
   static hipError_t bwd(ttt_ctx* c, const AttnBwdArgs& a0) {
@@ -242,7 +250,7 @@ struct Ops<bf16> {
     a.ws = c->ws;
     a.ws_floats = c->ws_floats;
     double fl = 4.0 * a.hd * a.H * a.B * (attn_pairs(c, a.n, a.pos0) + 0.5 * a.n * (a.n + 1.0));
-    return timed(c, PC_SWA_BWD, fl,
+    return timed(c, PC_SWA_BWD, fl, c->stream,
                  [&] { return c->mfma ? swa_bwd_mfma(a, c->stream) : swa_bwd_simt<bf16>(a, c->stream); });
   }
 };
@@ -415,7 +423,9 @@ int top_chunk(ttt_ctx* c, const int32_t* tgt, int64_t ld, const float* hsrc, int
     const int l = c->l0 + j;
     TopActs& a = c->acts[j];
     FastW& w = c->fw[j];
-    CK(convert_rows<T>(c->dh, M, d, tp<T>(c->dyN), tp<T>(c->dyT), n, b, c->stream));
+    void* dyT = c->dyT[j];
+    void* dzT = c->dzT[j];
+    CK(convert_rows<T>(c->dh, M, d, tp<T>(c->dyN), tp<T>(dyT), n, b, c->stream));
     // d act = dy W_down  ->  dz_g, dz_u
     GemmArgs g1 = mk(c->dyN, d, w.wdT, d, n, f, d);
     g1.batch = B;
@@ -429,13 +439,30 @@ int top_chunk(ttt_ctx* c, const int32_t* tgt, int64_t ld, const float* hsrc, int
     g1.e.c = c->dz;
     g1.e.ldc = 2 * f;
     g1.e.sc = (int64_t)n * 2 * f;
-    g1.e.t = c->dzT;
+    g1.e.t = dzT;
     g1.e.ldt = b;
     g1.e.st = 2LL * f * b;
     g1.e.f = f;
     CK(Ops<T>::gemm(c, g1));
+    if (j > 0) {  // dm = dz_g W_gate + dz_u W_up  (before W_gate/W_up change)
+      GemmArgs g3 = mk(c->dz, 2 * f, w.wguT, 2 * f, n, d, 2 * f);
+      g3.batch = B;
+      g3.sA = (int64_t)n * 2 * f;
+      g3.sB = 2LL * d * f;
+      g3.e.kind = EPI_F32;
+      g3.e.c = c->tmpf;
+      g3.e.ldc = d;
+      g3.e.sc = (int64_t)n * d;
+      CK(Ops<T>::gemm(c, g3));
+    }
+    // The weight gradients of this block with the fused SGD step run on the side stream,
+    // overlapping the rest of the backward: their inputs (dy^T, dz^T of this block, act^T,
+    // m^T) stay untouched until the next chunk, and the GEMMs above that read the old
+    // W_down^T and W_gu^T have been enqueued before them.
+    CK(hipEventRecord(c->ev_m2s, c->stream));
+    CK(hipStreamWaitEvent(c->side, c->ev_m2s, 0));
     // dW_down = dy^T act, fused SGD step on W_down
-    GemmArgs g2 = mk(c->dyT, b, a.actT, b, d, f, n);
+    GemmArgs g2 = mk(dyT, b, a.actT, b, d, f, n);
     g2.batch = B;
     g2.sA = (int64_t)d * b;
     g2.sB = (int64_t)f * b;
@@ -450,20 +477,9 @@ int top_chunk(ttt_ctx* c, const int32_t* tgt, int64_t ld, const float* hsrc, int
     g2.e.ldshT = d;
     g2.e.sshT = (int64_t)f * d;
     g2.e.lr = lr;
-    CK(Ops<T>::gemm(c, g2));
-    if (j > 0) {  // dm = dz_g W_gate + dz_u W_up  (before W_gate/W_up change)
-      GemmArgs g3 = mk(c->dz, 2 * f, w.wguT, 2 * f, n, d, 2 * f);
-      g3.batch = B;
-      g3.sA = (int64_t)n * 2 * f;
-      g3.sB = 2LL * d * f;
-      g3.e.kind = EPI_F32;
-      g3.e.c = c->tmpf;
-      g3.e.ldc = d;
-      g3.e.sc = (int64_t)n * d;
-      CK(Ops<T>::gemm(c, g3));
-    }
+    CK(Ops<T>::gemm(c, g2, c->side));
     // [dW_gate; dW_up] = dz^T m, fused SGD step
-    GemmArgs g4 = mk(c->dzT, b, a.mT, b, 2 * f, d, n);
+    GemmArgs g4 = mk(dzT, b, a.mT, b, 2 * f, d, n);
     g4.batch = B;
     g4.sA = 2LL * f * b;
     g4.sB = (int64_t)d * b;
@@ -479,7 +495,7 @@ int top_chunk(ttt_ctx* c, const int32_t* tgt, int64_t ld, const float* hsrc, int
     g4.e.sshT = 2LL * d * f;
     g4.e.lr = lr;
     g4.e.il_f = c->il ? f : 0;
-    CK(Ops<T>::gemm(c, g4));
+    CK(Ops<T>::gemm(c, g4, c->side));
     if (j == 0) break;
     const LayerW& lw = c->lw[l];
     // through the MLP norm and the residual: dh <- d h_mid
@@ -519,6 +535,9 @@ int top_chunk(ttt_ctx* c, const int32_t* tgt, int64_t ld, const float* hsrc, int
     CK(Ops<T>::gemm(c, g6));
     CK(rmsnorm_bwd<T>(a.h_in, a.rstd1, M, d, lw.attn_norm, c->tmpf, c->dh, c->dh, (T*)nullptr, c->stream));
   }
+  // the next chunk reads the updated fast weights and rewrites the saved activations
+  CK(hipEventRecord(c->ev_s2m, c->side));
+  CK(hipStreamWaitEvent(c->stream, c->ev_s2m, 0));
   return TTT_OK;
 }
 
@@ -644,7 +663,7 @@ int build(ttt_ctx* c, const ttt_weights* w) {
   const int64_t rows_bot = (int64_t)B * c->G * b, rows_top = (int64_t)B * b;
 #define AL(ptr, bytes)                                                           \
   do {                                                                           \
-    (ptr) = (decltype(ptr))c->alloc((size_t)(bytes));                            \
+    (ptr) = (std::remove_reference_t<decltype(ptr)>)c->alloc((size_t)(bytes));   \
     if (!(ptr)) return fail(c, TTT_ENOMEM, "device allocation failed: " #ptr);  \
   } while (0)
   AL(c->embed, (int64_t)V * d * es);
@@ -758,9 +777,13 @@ int build(ttt_ctx* c, const ttt_weights* w) {
   AL(c->dv, rows_top * d * 4);
   AL(c->dvec, rows_top * H * 4);
   AL(c->dyN, rows_top * d * es);
-  AL(c->dyT, rows_top * d * es);
+  c->dyT.resize(c->Lq);
+  c->dzT.resize(c->Lq);
+  for (int j = 0; j < c->Lq; ++j) {
+    AL(c->dyT[j], rows_top * d * es);
+    AL(c->dzT[j], rows_top * 2 * f * es);
+  }
   AL(c->dz, rows_top * 2 * f * es);
-  AL(c->dzT, rows_top * 2 * f * es);
   AL(c->dhT, rows_top * d * es);
   AL(c->dO, rows_top * d * es);
   AL(c->dqkv, rows_top * 3 * d * es);
@@ -896,11 +919,22 @@ int ttt_create(const ttt_config* cfg, const ttt_weights* w, void* hip_stream, tt
   const char* simt = getenv("TTT_SIMT");
   c->mfma = !(simt && simt[0] == '1');
   c->il = c->bf16 && c->mfma && c0.d_ff % 32 == 0 && c0.d_model % 8 == 0;
+  if (hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking) != hipSuccess ||
+      hipEventCreateWithFlags(&c->ev_m2s, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&c->ev_s2m, hipEventDisableTiming) != hipSuccess) {
+    g_create_err = "stream/event creation failed";
+    if (c->side) (void)hipStreamDestroy(c->side);
+    delete c;
+    return TTT_EDEVICE;
+  }
   int rc = build(c, w);
   if (rc == TTT_OK) rc = reset_state(c);
   if (rc != TTT_OK) {
     g_create_err = c->err;
     c->release_all();
+    (void)hipEventDestroy(c->ev_m2s);
+    (void)hipEventDestroy(c->ev_s2m);
+    (void)hipStreamDestroy(c->side);
     delete c;
     return rc;
   }
@@ -940,6 +974,10 @@ void ttt_destroy(ttt_ctx* c) {
   if (!c) return;
   (void)hipStreamSynchronize(c->stream);
   for (hipEvent_t e : c->ev_pool) (void)hipEventDestroy(e);
+  (void)hipStreamSynchronize(c->side);
+  (void)hipEventDestroy(c->ev_m2s);
+  (void)hipEventDestroy(c->ev_s2m);
+  (void)hipStreamDestroy(c->side);
   c->release_all();
   delete c;
 }

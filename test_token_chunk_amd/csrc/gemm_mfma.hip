@@ -45,119 +45,15 @@ __device__ __forceinline__ uint4 ldg16_tail(const bf16* p, int valid) {
   return make_uint4(pair(q, 0, valid), pair(q, 2, valid), pair(q, 4, valid), pair(q, 6, valid));
 }
 
-template <int BM, int BN, int WM, int WN, bool DUAL, int EK, bool SPLIT = false>
-__global__ __launch_bounds__(256) void k_gemm_mfma(GemmArgs g) {
-  constexpr int TM = WM / 32, TN = WN / 32;        // MFMA tiles per wave
-  constexpr int A_CH = BM * BK / 8 / 256;          // 16-byte chunks per thread
-  constexpr int B_CH = BN * BK / 8 / 256;
-  extern __shared__ __align__(16) unsigned char smem_raw[];
-  Smem<BM, BN, DUAL>& sm = *reinterpret_cast<Smem<BM, BN, DUAL>*>(smem_raw);
-
-  // SPLIT: blockIdx.z = batch * S + split; split covers K range [split*Ks, (split+1)*Ks)
-  // (S and Ks travel in e.ldt / e.st) and writes fp32 partials to ws[split][batch][M][N].
-  const int S = SPLIT ? (int)g.e.ldt : 1;
-  const int bz = SPLIT ? blockIdx.z / S : blockIdx.z;
-  const int split = SPLIT ? blockIdx.z % S : 0;
-  const int kbeg = SPLIT ? split * (int)g.e.st : 0;
-  const int kend = SPLIT ? min(g.K, kbeg + (int)g.e.st) : g.K;
-  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
-  const bf16* A = (const bf16*)g.A + bz * g.sA;
-  const bf16* B = (const bf16*)g.B + bz * g.sB;
-  const bf16* U = DUAL ? B + g.dual_off * g.ldb : nullptr;
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int wm0 = (wid >> 1) * WM, wn0 = (wid & 1) * WN;
-  const int nk = (kend - kbeg + BK - 1) / BK;
-
-  uint4 ra[A_CH], rb[B_CH], ru[DUAL ? B_CH : 1];
-  // Interior tiles (the common case) load with straight-line 16-byte loads; only tiles
-  // that cross M, N or the end of K take the guarded path (a block-uniform branch, so
-  // the fast path has no per-load control flow or waits between loads).
-  const bool interior_mn = m0 + BM <= g.M && n0 + BN <= g.N;
-  auto load = [&](int kt) {
-    const int k0 = kbeg + kt * BK;
-    if (interior_mn && k0 + BK <= kend) {
-#pragma unroll
-      for (int i = 0; i < A_CH; ++i) {
-        const int c = tid + i * 256, r = c >> 3, kc = (c & 7) * 8;
-        ra[i] = *(const uint4*)(A + (int64_t)(m0 + r) * g.lda + k0 + kc);
-      }
-#pragma unroll
-      for (int i = 0; i < B_CH; ++i) {
-        const int c = tid + i * 256, r = c >> 3, kc = (c & 7) * 8;
-        rb[i] = *(const uint4*)(B + (int64_t)(n0 + r) * g.ldb + k0 + kc);
-        if constexpr (DUAL) ru[i] = *(const uint4*)(U + (int64_t)(n0 + r) * g.ldb + k0 + kc);
-      }
-      return;
-    }
-#pragma unroll
-    for (int i = 0; i < A_CH; ++i) {
-      int c = tid + i * 256, r = c >> 3, kc = (c & 7) * 8;
-      int gm = m0 + r, gk = k0 + kc;
-      ra[i] = (gm < g.M) ? ldg16_tail(A + (int64_t)gm * g.lda + gk, kend - gk) : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < B_CH; ++i) {
-      int c = tid + i * 256, r = c >> 3, kc = (c & 7) * 8;
-      int gn = n0 + r, gk = k0 + kc;
-      rb[i] = (gn < g.N) ? ldg16_tail(B + (int64_t)gn * g.ldb + gk, kend - gk) : make_uint4(0, 0, 0, 0);
-      if constexpr (DUAL)
-        ru[i] = (gn < g.N) ? ldg16_tail(U + (int64_t)gn * g.ldb + gk, kend - gk) : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto store = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < A_CH; ++i) {
-      int c = tid + i * 256, r = c >> 3, kc = (c & 7) * 8;
-      *(uint4*)&sm.a[buf][r][kc] = ra[i];
-    }
-#pragma unroll
-    for (int i = 0; i < B_CH; ++i) {
-      int c = tid + i * 256, r = c >> 3, kc = (c & 7) * 8;
-      *(uint4*)&sm.b[buf][r][kc] = rb[i];
-      if constexpr (DUAL) *(uint4*)&sm.u[buf][r][kc] = ru[i];
-    }
-  };
-
-  f32x16 acc[TM][TN];
-  f32x16 accu[DUAL ? TM : 1][DUAL ? TN : 1];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      acc[i][j] = f32x16{};
-      if constexpr (DUAL) accu[i][j] = f32x16{};
-    }
-
-  load(0);
-  store(0);
-  __syncthreads();
-  const int lr = lane & 31, lk = (lane >> 5) * 8;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) load(kt + 1);
-#pragma unroll
-    for (int kk = 0; kk < BK; kk += 16) {
-      bf16x8 af[TM], bfr[TN], uf[DUAL ? TN : 1];
-#pragma unroll
-      for (int i = 0; i < TM; ++i) af[i] = *(const bf16x8*)&sm.a[cur][wm0 + i * 32 + lr][kk + lk];
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        bfr[j] = *(const bf16x8*)&sm.b[cur][wn0 + j * 32 + lr][kk + lk];
-        if constexpr (DUAL) uf[j] = *(const bf16x8*)&sm.u[cur][wn0 + j * 32 + lr][kk + lk];
-      }
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-          if constexpr (DUAL) accu[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], uf[j], accu[i][j], 0, 0, 0);
-        }
-    }
-    if (kt + 1 < nk) store(cur ^ 1);
-    __syncthreads();
-  }
-
-  // epilogue: C[row 8q + 4*(l/32) + i][col l%32] = acc[4q + i].
+// Epilogue shared by the GEMM main loops: C[row 8q + 4*(l/32) + i][col l%32] = acc[4q + i]
+// of each 32 x 32 tile.  smem_raw (free once the main loop has ended with a barrier) stages
+// outputs that are stored transposed.
+template <int BM, int BN, int WM, int WN, bool DUAL, int EK, bool SPLIT, int TM = WM / 32, int TN = WN / 32>
+__device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, f32x16 (&acc)[TM][TN],
+                                              f32x16 (&accu)[DUAL ? TM : 1][DUAL ? TN : 1],
+                                              unsigned char* smem_raw, int m0, int n0, int wm0, int wn0, int tid,
+                                              int bz, int split, int S) {
+  const int lane = tid & 63, lr = lane & 31;
   // Outputs stored transposed ([n][m]: the refreshed W^T shadow of the fused SGD step,
   // act^T, dz^T) are staged through LDS and written as 16-byte row segments.
   constexpr bool TR = (EK == EPI_SGD) || (EK == EPI_SWIGLU_BWD) || DUAL || (EK == EPI_SWIGLU_IL);
@@ -312,6 +208,244 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(GemmArgs g) {
   }
 }
 
+template <int BM, int BN, int WM, int WN, bool DUAL, int EK, bool SPLIT = false>
+__global__ __launch_bounds__(256) void k_gemm_mfma(GemmArgs g) {
+  constexpr int TM = WM / 32, TN = WN / 32;        // MFMA tiles per wave
+  constexpr int A_CH = BM * BK / 8 / 256;          // 16-byte chunks per thread
+  constexpr int B_CH = BN * BK / 8 / 256;
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  Smem<BM, BN, DUAL>& sm = *reinterpret_cast<Smem<BM, BN, DUAL>*>(smem_raw);
+
+  // SPLIT: blockIdx.z = batch * S + split; split covers K range [split*Ks, (split+1)*Ks)
+  // (S and Ks travel in e.ldt / e.st) and writes fp32 partials to ws[split][batch][M][N].
+  const int S = SPLIT ? (int)g.e.ldt : 1;
+  const int bz = SPLIT ? blockIdx.z / S : blockIdx.z;
+  const int split = SPLIT ? blockIdx.z % S : 0;
+  const int kbeg = SPLIT ? split * (int)g.e.st : 0;
+  const int kend = SPLIT ? min(g.K, kbeg + (int)g.e.st) : g.K;
+  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+  const bf16* A = (const bf16*)g.A + bz * g.sA;
+  const bf16* B = (const bf16*)g.B + bz * g.sB;
+  const bf16* U = DUAL ? B + g.dual_off * g.ldb : nullptr;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int wm0 = (wid >> 1) * WM, wn0 = (wid & 1) * WN;
+  const int nk = (kend - kbeg + BK - 1) / BK;
+
+  uint4 ra[A_CH], rb[B_CH], ru[DUAL ? B_CH : 1];
+  // Interior tiles (the common case) load with straight-line 16-byte loads; only tiles
+  // that cross M, N or the end of K take the guarded path (a block-uniform branch, so
+  // the fast path has no per-load control flow or waits between loads).
+  const bool interior_mn = m0 + BM <= g.M && n0 + BN <= g.N;
+  auto load = [&](int kt) {
+    const int k0 = kbeg + kt * BK;
+    if (interior_mn && k0 + BK <= kend) {
+#pragma unroll
+      for (int i = 0; i < A_CH; ++i) {
+        const int c = tid + i * 256, r = c >> 3, kc = (c & 7) * 8;
+        ra[i] = *(const uint4*)(A + (int64_t)(m0 + r) * g.lda + k0 + kc);
+      }
+#pragma unroll
+      for (int i = 0; i < B_CH; ++i) {
+        const int c = tid + i * 256, r = c >> 3, kc = (c & 7) * 8;
+        rb[i] = *(const uint4*)(B + (int64_t)(n0 + r) * g.ldb + k0 + kc);
+        if constexpr (DUAL) ru[i] = *(const uint4*)(U + (int64_t)(n0 + r) * g.ldb + k0 + kc);
+      }
+      return;
+    }
+#pragma unroll
+    for (int i = 0; i < A_CH; ++i) {
+      int c = tid + i * 256, r = c >> 3, kc = (c & 7) * 8;
+      int gm = m0 + r, gk = k0 + kc;
+      ra[i] = (gm < g.M) ? ldg16_tail(A + (int64_t)gm * g.lda + gk, kend - gk) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < B_CH; ++i) {
+      int c = tid + i * 256, r = c >> 3, kc = (c & 7) * 8;
+      int gn = n0 + r, gk = k0 + kc;
+      rb[i] = (gn < g.N) ? ldg16_tail(B + (int64_t)gn * g.ldb + gk, kend - gk) : make_uint4(0, 0, 0, 0);
+      if constexpr (DUAL)
+        ru[i] = (gn < g.N) ? ldg16_tail(U + (int64_t)gn * g.ldb + gk, kend - gk) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < A_CH; ++i) {
+      int c = tid + i * 256, r = c >> 3, kc = (c & 7) * 8;
+      *(uint4*)&sm.a[buf][r][kc] = ra[i];
+    }
+#pragma unroll
+    for (int i = 0; i < B_CH; ++i) {
+      int c = tid + i * 256, r = c >> 3, kc = (c & 7) * 8;
+      *(uint4*)&sm.b[buf][r][kc] = rb[i];
+      if constexpr (DUAL) *(uint4*)&sm.u[buf][r][kc] = ru[i];
+    }
+  };
+
+  f32x16 acc[TM][TN];
+  f32x16 accu[DUAL ? TM : 1][DUAL ? TN : 1];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      acc[i][j] = f32x16{};
+      if constexpr (DUAL) accu[i][j] = f32x16{};
+    }
+
+  load(0);
+  store(0);
+  __syncthreads();
+  const int lr = lane & 31, lk = (lane >> 5) * 8;
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) load(kt + 1);
+#pragma unroll
+    for (int kk = 0; kk < BK; kk += 16) {
+      bf16x8 af[TM], bfr[TN], uf[DUAL ? TN : 1];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) af[i] = *(const bf16x8*)&sm.a[cur][wm0 + i * 32 + lr][kk + lk];
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        bfr[j] = *(const bf16x8*)&sm.b[cur][wn0 + j * 32 + lr][kk + lk];
+        if constexpr (DUAL) uf[j] = *(const bf16x8*)&sm.u[cur][wn0 + j * 32 + lr][kk + lk];
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+          if constexpr (DUAL) accu[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], uf[j], accu[i][j], 0, 0, 0);
+        }
+    }
+    if (kt + 1 < nk) store(cur ^ 1);
+    __syncthreads();
+  }
+
+  gemm_epilogue<BM, BN, WM, WN, DUAL, EK, SPLIT>(g, acc, accu, smem_raw, m0, n0, wm0, wn0, tid, bz, split, S);
+}
+
+
+// ------------------------------------------------------------------ direct-to-LDS main loop
+// Same tile (128 x 128, K step 64, 4 waves of 64 x 64) with the operand tiles copied
+// straight from global memory into LDS (global_load_lds_dwordx4: lane L of a wave writes
+// 16 bytes at the wave's LDS address + 16 L) through a ring of STAGES buffers, so loads run
+// STAGES-1 K steps ahead without staging registers.  LDS rows are 128 bytes with the
+// 16-byte chunks XOR-swizzled by (row & 7), which keeps the operand reads of a wave on
+// distinct banks.  Requires M, N multiples of 128 and a K range that is a multiple of 64.
+#define LDSP(p) ((void __attribute__((address_space(3)))*)(p))
+// wait until at most n vector-memory operations are outstanding and all LDS operations are
+// done (gfx9 s_waitcnt: vmcnt in bits 15:14 and 3:0, expcnt 6:4, lgkmcnt 11:8)
+#define WAIT_VM_LDS(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4))
+
+constexpr int DL_TILE_BYTES = (128 + 128) * BK * 2;  // one stage: A and B tiles
+
+template <int EK, int STAGES, bool SPLIT>
+__global__ __launch_bounds__(256) void k_gemm_dl(GemmArgs g) {
+  constexpr int BM = 128, BN = 128, WM = 64, WN = 64, TM = 2, TN = 2;
+  constexpr int LPT = (BM + BN) * BK * 2 / 16 / 256;  // 16-byte loads per thread per tile
+  static_assert(STAGES >= 2 && STAGES <= 4, "pipeline depth");
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  const int S = SPLIT ? (int)g.e.ldt : 1;
+  const int bz = SPLIT ? blockIdx.z / S : blockIdx.z;
+  const int split = SPLIT ? blockIdx.z % S : 0;
+  const int kbeg = SPLIT ? split * (int)g.e.st : 0;
+  const int kend = SPLIT ? min(g.K, kbeg + (int)g.e.st) : g.K;
+  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+  const bf16* A = (const bf16*)g.A + bz * g.sA;
+  const bf16* B = (const bf16*)g.B + bz * g.sB;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int wm0 = (wid >> 1) * WM, wn0 = (wid & 1) * WN;
+  const int nk = (kend - kbeg) / BK;
+
+  auto issue = [&](int kt) {
+    unsigned char* base = smem_raw + (kt % STAGES) * DL_TILE_BYTES;
+    const int k0 = kbeg + kt * BK;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int blk = wid * 4 + i;          // 8-row block of the tile (1 KB)
+      const int r = blk * 8 + (lane >> 3);  // tile row of this lane
+      const int c = (lane & 7) ^ (r & 7);   // logical chunk that lands at physical chunk lane & 7
+      __builtin_amdgcn_global_load_lds(A + (int64_t)(m0 + r) * g.lda + k0 + c * 8, LDSP(base + blk * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(B + (int64_t)(n0 + r) * g.ldb + k0 + c * 8,
+                                       LDSP(base + BM * BK * 2 + blk * 1024), 16, 0, 0);
+    }
+  };
+
+  f32x16 acc[TM][TN];
+  f32x16 accu[1][1];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
+
+  const int lr = lane & 31, lk = (lane >> 5) * 8, sw = lr & 7;
+  for (int st = 0; st < STAGES - 1 && st < nk; ++st) issue(st);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int later = min(STAGES - 2, nk - 1 - kt);  // tiles issued after tile kt
+    if (later >= 2)
+      WAIT_VM_LDS(2 * LPT);
+    else if (later == 1)
+      WAIT_VM_LDS(LPT);
+    else
+      WAIT_VM_LDS(0);
+    __builtin_amdgcn_s_barrier();  // tile kt is in LDS for all waves; stage of tile kt-1 is free
+    if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1);
+    const unsigned char* a_base = smem_raw + (kt % STAGES) * DL_TILE_BYTES;
+    const unsigned char* b_base = a_base + BM * BK * 2;
+#pragma unroll
+    for (int kk = 0; kk < BK; kk += 16) {
+      const int p = (((kk + lk) >> 3) ^ sw) << 4;  // physical byte offset of the logical chunk
+      bf16x8 af[TM], bfr[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) af[i] = *(const bf16x8*)(a_base + (wm0 + i * 32 + lr) * 128 + p);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) bfr[j] = *(const bf16x8*)(b_base + (wn0 + j * 32 + lr) * 128 + p);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+  }
+  WAIT_VM_LDS(0);
+  __builtin_amdgcn_s_barrier();  // every wave is done with the operand buffers
+  gemm_epilogue<BM, BN, WM, WN, false, EK, SPLIT>(g, acc, accu, smem_raw, m0, n0, wm0, wn0, tid, bz, split, S);
+}
+
+template <int EK, bool SPLIT, int STAGES>
+hipError_t launch_dl_st(const GemmArgs& g, int S, hipStream_t s) {
+  auto kern = k_gemm_dl<EK, STAGES, SPLIT>;
+  const size_t shm = std::max<size_t>(STAGES * DL_TILE_BYTES, sizeof(Smem<128, 128, false>));
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  dim3 grid(cdiv(g.N, 128), cdiv(g.M, 128), g.batch * S);
+  hipLaunchKernelGGL(kern, grid, dim3(256), shm, s, g);
+  return hipGetLastError();
+}
+
+template <int EK, bool SPLIT>
+hipError_t launch_dl(const GemmArgs& g, int S, hipStream_t s) {
+  static int stages = -1;
+  if (stages < 0) {
+    const char* e = getenv("TTT_GEMM_STAGES");
+    stages = e ? atoi(e) : 2;
+  }
+  if (stages == 4) return launch_dl_st<EK, SPLIT, 4>(g, S, s);
+  if (stages == 3) return launch_dl_st<EK, SPLIT, 3>(g, S, s);
+  return launch_dl_st<EK, SPLIT, 2>(g, S, s);
+}
+
+// shapes the direct-to-LDS loop takes
+bool dl_ok(const GemmArgs& g, int Ks) {
+  const char* off = getenv("TTT_GEMM_NO_DL");
+  if (off && off[0] == '1') return false;
+  return g.M % 128 == 0 && g.N % 128 == 0 && g.K % BK == 0 && Ks % BK == 0 && g.lda % 8 == 0 && g.ldb % 8 == 0 &&
+         g.e.kind != EPI_SWIGLU;
+}
+
 template <int BM, int BN, int WM, int WN, bool DUAL, int EK>
 hipError_t launch(const GemmArgs& g, hipStream_t s) {
   auto kern = k_gemm_mfma<BM, BN, WM, WN, DUAL, EK>;
@@ -345,16 +479,21 @@ hipError_t launch_splitk(const GemmArgs& g0, int S, int Ks, hipStream_t s) {
   GemmArgs g = g0;
   g.e.ldt = S;   // carried to the kernel
   g.e.st = Ks;
-  auto kern = k_gemm_mfma<128, 128, 64, 64, false, EPI_F32, true>;
-  static bool attr_set = false;
-  const size_t shm = sizeof(Smem<128, 128, false>);
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+  if (dl_ok(g, Ks)) {
+    hipError_t e = launch_dl<EPI_F32, true>(g, S, s);
     if (e != hipSuccess) return e;
-    attr_set = true;
+  } else {
+    auto kern = k_gemm_mfma<128, 128, 64, 64, false, EPI_F32, true>;
+    static bool attr_set = false;
+    const size_t shm = sizeof(Smem<128, 128, false>);
+    if (!attr_set) {
+      hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+      if (e != hipSuccess) return e;
+      attr_set = true;
+    }
+    dim3 grid(cdiv(g.N, 128), cdiv(g.M, 128), g.batch * S);
+    hipLaunchKernelGGL(kern, grid, dim3(256), shm, s, g);
   }
-  dim3 grid(cdiv(g.N, 128), cdiv(g.M, 128), g.batch * S);
-  hipLaunchKernelGGL(kern, grid, dim3(256), shm, s, g);
   const int64_t total = (int64_t)g.batch * g.M * g.N;
   dim3 rg((unsigned)std::min<int64_t>(cdiv(total, 256), 4096));
   switch (g0.e.kind) {
@@ -398,6 +537,18 @@ hipError_t gemm_mfma_bf16(const GemmArgs& g, hipStream_t s) {
   int Ks = 0;
   const int S = gemm_mfma_splits(g, &Ks);
   if (S > 1) return launch_splitk(g, S, Ks, s);
+  if (dl_ok(g, g.K)) {
+    switch (g.e.kind) {
+      case EPI_SWIGLU_IL: return launch_dl<EPI_SWIGLU_IL, false>(g, 1, s);
+      case EPI_F32: return launch_dl<EPI_F32, false>(g, 1, s);
+      case EPI_T: return launch_dl<EPI_T, false>(g, 1, s);
+      // EPI_ADD_F32 stays on the register-staged loop: its two-phase epilogue needs many
+      // registers and the lower occupancy costs more than the direct loads gain
+      case EPI_SWIGLU_BWD: return launch_dl<EPI_SWIGLU_BWD, false>(g, 1, s);
+      case EPI_SGD: return launch_dl<EPI_SGD, false>(g, 1, s);
+      default: break;
+    }
+  }
   switch (g.e.kind) {
     case EPI_SWIGLU: return launch<128, 128, 64, 64, true, EPI_SWIGLU>(g, s);
     case EPI_SWIGLU_IL: return launch<128, 128, 64, 64, false, EPI_SWIGLU_IL>(g, s);
