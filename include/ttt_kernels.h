@@ -40,11 +40,14 @@ int tttk_swa_fwd(int dtype, const void* q, const void* kr, const void* vr, const
  * positions pos0 .. pos0+n-1; keys before pos0 are constants (same page,
  * §8 Q1).  qt [B][H][hd][n] (q transposed), o, dout [B*n][H*hd] in dtype,
  * lse from the forward, dvec scratch [B][H][n]; outputs dq, dk, dv fp32
- * [B*n][H*hd] (dk, dv for the chunk's own keys only). */
+ * [B*n][H*hd] (dk, dv for the chunk's own keys only).  Optional (may be NULL):
+ * ktr, the ring of keys transposed [B][H][hd][R], and dot, a scratch of
+ * B*n*H*hd elements of dtype for dout transposed; with both (and n % 8 == 0)
+ * the matrix-core kernels read transposed tiles instead of transposing in LDS. */
 int tttk_swa_bwd(int dtype, const void* q, const void* qt, const void* kr, const void* vr, const void* vtr,
-                 const void* o, const void* dout, const float* lse, float* dvec, float* dq, float* dk, float* dv,
-                 int32_t B, int32_t H, int32_t hd, int32_t n, int32_t R, int32_t window, int64_t pos0, float* ws,
-                 int64_t ws_floats, void* stream);
+                 const void* ktr, const void* o, const void* dout, const float* lse, float* dvec, float* dq, float* dk,
+                 float* dv, void* dot, int32_t B, int32_t H, int32_t hd, int32_t n, int32_t R, int32_t window,
+                 int64_t pos0, float* ws, int64_t ws_floats, void* stream);
 
 #ifdef __cplusplus
 }

@@ -302,7 +302,7 @@ def _klib():
         lib.tttk_gemm.argtypes = [ctypes.c_int, vp, i64, vp, i64, vp, i64, i32, i32, i32, vp, i64, vp]
         lib.tttk_swa_fwd.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i64, vp, i64,
                                      vp]
-        lib.tttk_swa_bwd.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+        lib.tttk_swa_bwd.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                      i32, i32, i32, i32, i32, i32, i64, vp, i64, vp]
         lib._k_ready = True
     return lib
@@ -354,10 +354,12 @@ def swa_fwd(q, kr, vr, vtr, o, lse, pos0: int, window: int, ws=None):
         raise TTTError(rc, "tttk_swa_fwd")
 
 
-def swa_bwd(q, qt, kr, vr, vtr, o, dout, lse, dvec, dq, dk, dv, pos0: int, window: int, ws=None):
+def swa_bwd(q, qt, kr, vr, vtr, o, dout, lse, dvec, dq, dk, dv, pos0: int, window: int, ws=None, ktr=None,
+            dot=None):
     B, H, n, hd = q.shape
     R = kr.shape[2]
-    rc = _klib().tttk_swa_bwd(_dt(q), _p(q), _p(qt), _p(kr), _p(vr), _p(vtr), _p(o), _p(dout), _p(lse), _p(dvec),
-                              _p(dq), _p(dk), _p(dv), B, H, hd, n, R, window, pos0, *_ws(ws), _stream())
+    rc = _klib().tttk_swa_bwd(_dt(q), _p(q), _p(qt), _p(kr), _p(vr), _p(vtr), _p(ktr), _p(o), _p(dout), _p(lse),
+                              _p(dvec), _p(dq), _p(dk), _p(dv), _p(dot), B, H, hd, n, R, window, pos0, *_ws(ws),
+                              _stream())
     if rc:
         raise TTTError(rc, "tttk_swa_bwd")

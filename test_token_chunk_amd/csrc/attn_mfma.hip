@@ -334,6 +334,7 @@ hipError_t launch_fwd(const AttnArgs& a, hipStream_t s) {
 // (cached keys included, as constants).  S^T = K Q^T and dP^T = V dO^T put
 // one query per lane; dS^T = P^T (dP^T - D) then feeds dQ^T += K^T dS^T from
 // registers with the same permuted k index as the forward's P V product.
+// TR: K^T tiles are 16-byte copies from the transposed key ring; otherwise
 // K^T is produced in LDS by a transposing store of the K tile.
 template <int HD>
 struct DqSmem {
@@ -343,7 +344,7 @@ struct DqSmem {
 };
 
 // SPLIT: blockIdx.z = b * S + split over the key tiles; partial dq to ws[S][B*n][H*hd]
-template <int HD, int NW, bool SPLIT>
+template <int HD, int NW, bool SPLIT, bool TR>
 __global__ __launch_bounds__(NW * 64) void k_swa_dq(AttnBwdArgs a, int S) {
   constexpr int NT = NW * 64, BQn = NW * QW;
   constexpr int KS = HD / 16, HM = HD / 32;
@@ -365,6 +366,7 @@ __global__ __launch_bounds__(NW * 64) void k_swa_dq(AttnBwdArgs a, int S) {
   const int64_t wpos_lo = a.pos0 + tw0, wpos_hi = wpos_lo + QW - 1;
   const bf16* Kr = (const bf16*)a.kr + bh * R * HD;
   const bf16* Vr = (const bf16*)a.vr + bh * R * HD;
+  const bf16* Kt = TR ? (const bf16*)a.ktr + bh * HD * R : nullptr;
 
   bf16x8 q0, q1, q2, q3, q4, q5, q6, q7, e0, e1, e2, e3, e4, e5, e6, e7;
   {
@@ -398,42 +400,50 @@ __global__ __launch_bounds__(NW * 64) void k_swa_dq(AttnBwdArgs a, int S) {
 #pragma unroll
   for (int i = 0; i < HM; ++i) acc[i] = f32x16{};
 
-  uint4 rk0, rk1, rk2, rk3, rv0, rv1, rv2, rv3;
-#define LD(i, dk, dv)                                                                    \
+  uint4 rk0, rk1, rk2, rk3, rv0, rv1, rv2, rv3, rt0, rt1, rt2, rt3;
+  // K^T chunk c (TR): head-dim row c / 8, keys (c % 8) * 8 .. +7 -- contiguous, since
+  // tiles start at multiples of 64 positions and R % 8 == 0
+#define LD(i, dk, dv, dt)                                                                \
   if constexpr (KCH > i) {                                                               \
     const int c = tid + i * NT, r = c / (HD / 8), col = (c % (HD / 8)) * 8;              \
     if (c < KT * HD / 8) {                                                               \
       const int64_t off = (int64_t)((slot0 + r) % R) * HD + col;                         \
       dk = *(const uint4*)(Kr + off);                                                    \
       dv = *(const uint4*)(Vr + off);                                                    \
+      if constexpr (TR)                                                                  \
+        dt = *(const uint4*)(Kt + (int64_t)(c / (KT / 8)) * R + (slot0 + (c % (KT / 8)) * 8) % R); \
     }                                                                                    \
   }
 #define LOAD_TILE(it_)                                                                   \
   {                                                                                      \
     const int slot0 = (sbase + (it_) * KT) % R;                                          \
-    LD(0, rk0, rv0) LD(1, rk1, rv1) LD(2, rk2, rv2) LD(3, rk3, rv3)                      \
+    LD(0, rk0, rv0, rt0) LD(1, rk1, rv1, rt1) LD(2, rk2, rv2, rt2) LD(3, rk3, rv3, rt3)  \
   }
-#define ST(i, sk, sv)                                                                    \
+#define ST(i, sk, sv, st_)                                                               \
   if constexpr (KCH > i) {                                                               \
     const int c = tid + i * NT, r = c / (HD / 8), col = (c % (HD / 8)) * 8;              \
     if (c < KT * HD / 8) {                                                               \
       *(uint4*)&sm.k[buf][r][col] = sk;                                                  \
       *(uint4*)&sm.v[buf][r][col] = sv;                                                  \
-      const uint32_t w0 = sk.x, w1 = sk.y, w2 = sk.z, w3 = sk.w;                         \
-      sm.kt[buf][col + 0][r].x = (uint16_t)w0;                                           \
-      sm.kt[buf][col + 1][r].x = (uint16_t)(w0 >> 16);                                   \
-      sm.kt[buf][col + 2][r].x = (uint16_t)w1;                                           \
-      sm.kt[buf][col + 3][r].x = (uint16_t)(w1 >> 16);                                   \
-      sm.kt[buf][col + 4][r].x = (uint16_t)w2;                                           \
-      sm.kt[buf][col + 5][r].x = (uint16_t)(w2 >> 16);                                   \
-      sm.kt[buf][col + 6][r].x = (uint16_t)w3;                                           \
-      sm.kt[buf][col + 7][r].x = (uint16_t)(w3 >> 16);                                   \
+      if constexpr (TR) {                                                                \
+        *(uint4*)&sm.kt[buf][c / (KT / 8)][(c % (KT / 8)) * 8] = st_;                    \
+      } else {                                                                           \
+        const uint32_t w0 = sk.x, w1 = sk.y, w2 = sk.z, w3 = sk.w;                       \
+        sm.kt[buf][col + 0][r].x = (uint16_t)w0;                                         \
+        sm.kt[buf][col + 1][r].x = (uint16_t)(w0 >> 16);                                 \
+        sm.kt[buf][col + 2][r].x = (uint16_t)w1;                                         \
+        sm.kt[buf][col + 3][r].x = (uint16_t)(w1 >> 16);                                 \
+        sm.kt[buf][col + 4][r].x = (uint16_t)w2;                                         \
+        sm.kt[buf][col + 5][r].x = (uint16_t)(w2 >> 16);                                 \
+        sm.kt[buf][col + 6][r].x = (uint16_t)w3;                                         \
+        sm.kt[buf][col + 7][r].x = (uint16_t)(w3 >> 16);                                 \
+      }                                                                                  \
     }                                                                                    \
   }
 #define STORE_TILE(buf_)                                                                 \
   {                                                                                      \
     const int buf = (buf_);                                                              \
-    ST(0, rk0, rv0) ST(1, rk1, rv1) ST(2, rk2, rv2) ST(3, rk3, rv3)                      \
+    ST(0, rk0, rv0, rt0) ST(1, rk1, rv1, rt1) ST(2, rk2, rv2, rt2) ST(3, rk3, rv3, rt3)  \
   }
   if (it_beg < ntiles) {
     LOAD_TILE(it_beg)
@@ -444,60 +454,52 @@ __global__ __launch_bounds__(NW * 64) void k_swa_dq(AttnBwdArgs a, int S) {
     const int cur = it & 1;
     if (it + 1 < ntiles) LOAD_TILE(it + 1)
     const int64_t kp0 = ktile0 + (int64_t)it * KT;
-    f32x16 s0 = f32x16{}, s1 = f32x16{}, p0 = f32x16{}, p1 = f32x16{};
-    {
-      const bf16* k0p = &sm.k[cur][(lane & 31)][g * 8];
-      const bf16* k1p = &sm.k[cur][32 + (lane & 31)][g * 8];
-      const bf16* v0p = &sm.v[cur][(lane & 31)][g * 8];
-      const bf16* v1p = &sm.v[cur][32 + (lane & 31)][g * 8];
+    // masked keys get score -inf (p = 0); only tiles that cut a window edge need it
+    const bool full = wfull && kp0 >= wpos_hi - a.window + 1 && kp0 + KT - 1 <= wpos_lo;
+    const int64_t hi64 = qpos - kp0, lo64 = qpos - a.window - kp0;
+    const int hi = qok ? (int)min<int64_t>(max<int64_t>(hi64, -1), 64) : -1;
+    const int lo = (int)min<int64_t>(max<int64_t>(lo64, -2), 64);
+    // the 64-key tile in two halves of 32 keys (keeps the score registers to one half)
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      f32x16 s0 = f32x16{}, p0 = f32x16{};
+      const bf16* k0p = &sm.k[cur][hf * 32 + (lane & 31)][g * 8];
+      const bf16* v0p = &sm.v[cur][hf * 32 + (lane & 31)][g * 8];
 #define SSTEP(ks, qv, ev)                                                                          \
   if constexpr (KS > ks) {                                                                         \
     s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(k0p + ks * 16), qv, s0, 0, 0, 0); \
-    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(k1p + ks * 16), qv, s1, 0, 0, 0); \
     p0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(v0p + ks * 16), ev, p0, 0, 0, 0); \
-    p1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(v1p + ks * 16), ev, p1, 0, 0, 0); \
   }
       SSTEP(0, q0, e0) SSTEP(1, q1, e1) SSTEP(2, q2, e2) SSTEP(3, q3, e3)
       SSTEP(4, q4, e4) SSTEP(5, q5, e5) SSTEP(6, q6, e6) SSTEP(7, q7, e7)
 #undef SSTEP
-    }
-    // masked keys get score -inf (p = 0); only tiles that cut a window edge need it
-    const bool full = wfull && kp0 >= wpos_hi - a.window + 1 && kp0 + KT - 1 <= wpos_lo;
-    if (!full) {
-      const int64_t hi64 = qpos - kp0, lo64 = qpos - a.window - kp0;
-      const int hi = qok ? (int)min<int64_t>(max<int64_t>(hi64, -1), 64) : -1;
-      const int lo = (int)min<int64_t>(max<int64_t>(lo64, -2), 64);
+      if (!full) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int off = 8 * (r >> 2) + 4 * g + (r & 3);
-        if (!(off <= hi && off > lo)) s0[r] = -INFINITY;
-        if (!(off + 32 <= hi && off + 32 > lo)) s1[r] = -INFINITY;
+        for (int r = 0; r < 16; ++r) {
+          const int off = hf * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+          if (!(off <= hi && off > lo)) s0[r] = -INFINITY;
+        }
       }
-    }
-    uint32_t da[8], db[8];
+      uint32_t da[8];
 #pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-      const float x0 = exp2f(fmaf(s0[r], sl2, nlse2)) * (p0[r] - Dq);
-      const float x1 = exp2f(fmaf(s0[r + 1], sl2, nlse2)) * (p0[r + 1] - Dq);
-      const float y0 = exp2f(fmaf(s1[r], sl2, nlse2)) * (p1[r] - Dq);
-      const float y1 = exp2f(fmaf(s1[r + 1], sl2, nlse2)) * (p1[r + 1] - Dq);
-      da[r >> 1] = pk2(x0, x1);
-      db[r >> 1] = pk2(y0, y1);
-    }
-    const bf16x8 dsf[4] = {__builtin_bit_cast(bf16x8, make_uint4(da[0], da[1], da[2], da[3])),
-                           __builtin_bit_cast(bf16x8, make_uint4(da[4], da[5], da[6], da[7])),
-                           __builtin_bit_cast(bf16x8, make_uint4(db[0], db[1], db[2], db[3])),
-                           __builtin_bit_cast(bf16x8, make_uint4(db[4], db[5], db[6], db[7]))};
+      for (int r = 0; r < 16; r += 2) {
+        const float x0 = exp2f(fmaf(s0[r], sl2, nlse2)) * (p0[r] - Dq);
+        const float x1 = exp2f(fmaf(s0[r + 1], sl2, nlse2)) * (p0[r + 1] - Dq);
+        da[r >> 1] = pk2(x0, x1);
+      }
+      const bf16x8 ds0 = __builtin_bit_cast(bf16x8, make_uint4(da[0], da[1], da[2], da[3]));
+      const bf16x8 ds1 = __builtin_bit_cast(bf16x8, make_uint4(da[4], da[5], da[6], da[7]));
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      const int kc = st * 16 + 4 * g;
+      for (int st = 0; st < 2; ++st) {
+        const int kc = hf * 32 + st * 16 + 4 * g;
 #pragma unroll
-      for (int hm = 0; hm < HM; ++hm) {
-        const bf16* row = &sm.kt[cur][hm * 32 + (lane & 31)][0];
-        uint2 lo2 = *(const uint2*)(row + kc);
-        uint2 hi2 = *(const uint2*)(row + kc + 8);
-        bf16x8 kf = __builtin_bit_cast(bf16x8, make_uint4(lo2.x, lo2.y, hi2.x, hi2.y));
-        acc[hm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, dsf[st], acc[hm], 0, 0, 0);
+        for (int hm = 0; hm < HM; ++hm) {
+          const bf16* row = &sm.kt[cur][hm * 32 + (lane & 31)][0];
+          uint2 lo2 = *(const uint2*)(row + kc);
+          uint2 hi2 = *(const uint2*)(row + kc + 8);
+          bf16x8 kf = __builtin_bit_cast(bf16x8, make_uint4(lo2.x, lo2.y, hi2.x, hi2.y));
+          acc[hm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, st ? ds1 : ds0, acc[hm], 0, 0, 0);
+        }
       }
     }
     if (it + 1 < ntiles) STORE_TILE((it + 1) & 1)
@@ -523,7 +525,9 @@ __global__ __launch_bounds__(NW * 64) void k_swa_dq(AttnBwdArgs a, int S) {
 // dK/dV kernel for the chunk's own keys (keys before pos0 are constants and get
 // nothing): per wave 32 keys, loop over 64-query tiles of the chunk.  S = Q K^T
 // and dP = dO V^T put one key per lane; dV^T += dO^T P and dK^T += Q^T dS with
-// the permuted k index over queries.  Q^T and dO^T come from transposing LDS stores.
+// the permuted k index over queries.  TR: Q^T and dO^T tiles are 16-byte copies
+// of the transposed rows [B][H][hd][n] (n % 8 == 0); otherwise they come from
+// transposing LDS stores.
 template <int HD>
 struct DkvSmem {
   bf16 q[KT][HD + 8];
@@ -536,7 +540,7 @@ struct DkvSmem {
 
 // P > 1: blockIdx.z = b * P + part; the block covers part `part` of its key block's query
 // tiles and writes partial dK / dV to ws[part] / ws[P + part] (each [B*n][H*hd]).
-template <int HD>
+template <int HD, bool TR>
 __global__ __launch_bounds__(256) void k_swa_dkv(AttnBwdArgs a, int P) {
   constexpr int KS = HD / 16, HM = HD / 32;
   constexpr int KCH = KT * HD / 8 / 256;
@@ -580,8 +584,9 @@ __global__ __launch_bounds__(256) void k_swa_dkv(AttnBwdArgs a, int P) {
   const int tbeg = tfirst + part * per * KT;
   const int tstop = min(a.n, tfirst + (part + 1) * per * KT);
   for (int tq0 = tbeg; tq0 < tstop; tq0 += KT) {
-    uint4 rq0, rq1, rq2, rq3, ro0, ro1, ro2, ro3;
-#define LD(i, dq_, do_)                                                                     \
+    uint4 rq0, rq1, rq2, rq3, ro0, ro1, ro2, ro3, tq_0, tq_1, tq_2, tq_3, to_0, to_1, to_2, to_3;
+    // Q^T / dO^T chunk c (TR): head-dim row c / 8, queries (c % 8) * 8 .. +7
+#define LD(i, dq_, do_, tq_, to_)                                                           \
   if constexpr (KCH > i) {                                                                  \
     const int c = tid + i * 256, r = c / (HD / 8), col = (c % (HD / 8)) * 8;                \
     const int t = tq0 + r;                                                                  \
@@ -592,23 +597,39 @@ __global__ __launch_bounds__(256) void k_swa_dkv(AttnBwdArgs a, int P) {
       dq_ = make_uint4(0, 0, 0, 0);                                                         \
       do_ = make_uint4(0, 0, 0, 0);                                                         \
     }                                                                                       \
+    if constexpr (TR) {                                                                     \
+      const int tt = tq0 + (c % (KT / 8)) * 8;                                              \
+      const int64_t toff = (bh * HD + c / (KT / 8)) * a.n + tt;                             \
+      if (tt < a.n) {                                                                       \
+        tq_ = *(const uint4*)((const bf16*)a.qt + toff);                                    \
+        to_ = *(const uint4*)((const bf16*)a.dot + toff);                                   \
+      } else {                                                                              \
+        tq_ = make_uint4(0, 0, 0, 0);                                                       \
+        to_ = make_uint4(0, 0, 0, 0);                                                       \
+      }                                                                                     \
+    }                                                                                       \
   }
-    LD(0, rq0, ro0) LD(1, rq1, ro1) LD(2, rq2, ro2) LD(3, rq3, ro3)
+    LD(0, rq0, ro0, tq_0, to_0) LD(1, rq1, ro1, tq_1, to_1) LD(2, rq2, ro2, tq_2, to_2) LD(3, rq3, ro3, tq_3, to_3)
 #undef LD
     __syncthreads();
-#define ST(i, sq, so)                                                                       \
+#define ST(i, sq, so, tq_, to_)                                                             \
   if constexpr (KCH > i) {                                                                  \
     const int c = tid + i * 256, r = c / (HD / 8), col = (c % (HD / 8)) * 8;                \
     *(uint4*)&sm.q[r][col] = sq;                                                            \
     *(uint4*)&sm.o[r][col] = so;                                                            \
-    const uint16_t* eq = (const uint16_t*)&sq;                                              \
-    const uint16_t* eo = (const uint16_t*)&so;                                              \
-    _Pragma("unroll") for (int x = 0; x < 8; ++x) {                                         \
-      sm.qt[col + x][r].x = eq[x];                                                          \
-      sm.ot[col + x][r].x = eo[x];                                                          \
+    if constexpr (TR) {                                                                     \
+      *(uint4*)&sm.qt[c / (KT / 8)][(c % (KT / 8)) * 8] = tq_;                              \
+      *(uint4*)&sm.ot[c / (KT / 8)][(c % (KT / 8)) * 8] = to_;                              \
+    } else {                                                                                \
+      const uint16_t* eq = (const uint16_t*)&sq;                                            \
+      const uint16_t* eo = (const uint16_t*)&so;                                            \
+      _Pragma("unroll") for (int x = 0; x < 8; ++x) {                                       \
+        sm.qt[col + x][r].x = eq[x];                                                        \
+        sm.ot[col + x][r].x = eo[x];                                                        \
+      }                                                                                     \
     }                                                                                       \
   }
-    ST(0, rq0, ro0) ST(1, rq1, ro1) ST(2, rq2, ro2) ST(3, rq3, ro3)
+    ST(0, rq0, ro0, tq_0, to_0) ST(1, rq1, ro1, tq_1, to_1) ST(2, rq2, ro2, tq_2, to_2) ST(3, rq3, ro3, tq_3, to_3)
 #undef ST
     if (tid < KT) {
       const int t = tq0 + tid;
@@ -616,66 +637,56 @@ __global__ __launch_bounds__(256) void k_swa_dkv(AttnBwdArgs a, int P) {
       sm.dd[tid] = t < a.n ? a.dvec[bh * a.n + t] : 0.f;
     }
     __syncthreads();
-    f32x16 s0 = f32x16{}, s1 = f32x16{}, p0 = f32x16{}, p1 = f32x16{};
-    {
-      const bf16* q0p = &sm.q[(lane & 31)][g * 8];
-      const bf16* q1p = &sm.q[32 + (lane & 31)][g * 8];
-      const bf16* o0p = &sm.o[(lane & 31)][g * 8];
-      const bf16* o1p = &sm.o[32 + (lane & 31)][g * 8];
+    // the 64-query tile in two halves of 32 queries (keeps the score registers to one half)
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      f32x16 s0 = f32x16{}, p0 = f32x16{};
+      const bf16* q0p = &sm.q[hf * 32 + (lane & 31)][g * 8];
+      const bf16* o0p = &sm.o[hf * 32 + (lane & 31)][g * 8];
 #define SSTEP(ks, kv, vv)                                                                          \
   if constexpr (KS > ks) {                                                                         \
     s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(q0p + ks * 16), kv, s0, 0, 0, 0); \
-    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(q1p + ks * 16), kv, s1, 0, 0, 0); \
     p0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(o0p + ks * 16), vv, p0, 0, 0, 0); \
-    p1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(o1p + ks * 16), vv, p1, 0, 0, 0); \
   }
       SSTEP(0, k0, v0) SSTEP(1, k1, v1) SSTEP(2, k2, v2) SSTEP(3, k3, v3)
       SSTEP(4, k4, v4) SSTEP(5, k5, v5) SSTEP(6, k6, v6) SSTEP(7, k7, v7)
 #undef SSTEP
-    }
-    // rows = queries tq0 + 32 half + 8 j + 4 g + i; visible iff sk <= t < n and t - sk < window
-    uint32_t pa[8], pb[8], da[8], db[8];
+      // rows = queries tq0 + 32 hf + 8 j + 4 g + i; visible iff sk <= t < n and t - sk < window
+      uint32_t pa[8], da[8];
 #pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-      float pv[4], dsv[4];
+      for (int r = 0; r < 16; r += 2) {
+        float pv[2], dsv[2];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int rr = r + (u & 1);
-        const int row = (u >> 1) * 32 + 8 * (rr >> 2) + 4 * g + (rr & 3);
-        const int t = tq0 + row;
-        const bool ok = kok && t < a.n && t >= sk && t - sk < a.window;
-        const float sv = (u >> 1) ? s1[rr] : s0[rr];
-        const float dpv = (u >> 1) ? p1[rr] : p0[rr];
-        const float p = ok ? exp2f(sv * sl2 - sm.lse2[row]) : 0.f;
-        pv[u] = p;
-        dsv[u] = p * (dpv - sm.dd[row]);
+        for (int u = 0; u < 2; ++u) {
+          const int rr = r + u;
+          const int row = hf * 32 + 8 * (rr >> 2) + 4 * g + (rr & 3);
+          const int t = tq0 + row;
+          const bool ok = kok && t < a.n && t >= sk && t - sk < a.window;
+          const float p = ok ? exp2f(s0[rr] * sl2 - sm.lse2[row]) : 0.f;
+          pv[u] = p;
+          dsv[u] = p * (p0[rr] - sm.dd[row]);
+        }
+        pa[r >> 1] = pk2(pv[0], pv[1]);
+        da[r >> 1] = pk2(dsv[0], dsv[1]);
       }
-      pa[r >> 1] = pk2(pv[0], pv[1]);
-      pb[r >> 1] = pk2(pv[2], pv[3]);
-      da[r >> 1] = pk2(dsv[0], dsv[1]);
-      db[r >> 1] = pk2(dsv[2], dsv[3]);
-    }
-    const bf16x8 pf[4] = {__builtin_bit_cast(bf16x8, make_uint4(pa[0], pa[1], pa[2], pa[3])),
-                          __builtin_bit_cast(bf16x8, make_uint4(pa[4], pa[5], pa[6], pa[7])),
-                          __builtin_bit_cast(bf16x8, make_uint4(pb[0], pb[1], pb[2], pb[3])),
-                          __builtin_bit_cast(bf16x8, make_uint4(pb[4], pb[5], pb[6], pb[7]))};
-    const bf16x8 dsf[4] = {__builtin_bit_cast(bf16x8, make_uint4(da[0], da[1], da[2], da[3])),
-                           __builtin_bit_cast(bf16x8, make_uint4(da[4], da[5], da[6], da[7])),
-                           __builtin_bit_cast(bf16x8, make_uint4(db[0], db[1], db[2], db[3])),
-                           __builtin_bit_cast(bf16x8, make_uint4(db[4], db[5], db[6], db[7]))};
+      const bf16x8 pf0 = __builtin_bit_cast(bf16x8, make_uint4(pa[0], pa[1], pa[2], pa[3]));
+      const bf16x8 pf1 = __builtin_bit_cast(bf16x8, make_uint4(pa[4], pa[5], pa[6], pa[7]));
+      const bf16x8 df0 = __builtin_bit_cast(bf16x8, make_uint4(da[0], da[1], da[2], da[3]));
+      const bf16x8 df1 = __builtin_bit_cast(bf16x8, make_uint4(da[4], da[5], da[6], da[7]));
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      const int kc = st * 16 + 4 * g;
+      for (int st = 0; st < 2; ++st) {
+        const int kc = hf * 32 + st * 16 + 4 * g;
 #pragma unroll
-      for (int hm = 0; hm < HM; ++hm) {
-        const bf16* orow = &sm.ot[hm * 32 + (lane & 31)][0];
-        const bf16* qrow = &sm.qt[hm * 32 + (lane & 31)][0];
-        uint2 ol = *(const uint2*)(orow + kc), oh = *(const uint2*)(orow + kc + 8);
-        uint2 ql = *(const uint2*)(qrow + kc), qh = *(const uint2*)(qrow + kc + 8);
-        bf16x8 of = __builtin_bit_cast(bf16x8, make_uint4(ol.x, ol.y, oh.x, oh.y));
-        bf16x8 qf = __builtin_bit_cast(bf16x8, make_uint4(ql.x, ql.y, qh.x, qh.y));
-        dv[hm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(of, pf[st], dv[hm], 0, 0, 0);
-        dk[hm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf, dsf[st], dk[hm], 0, 0, 0);
+        for (int hm = 0; hm < HM; ++hm) {
+          const bf16* orow = &sm.ot[hm * 32 + (lane & 31)][0];
+          const bf16* qrow = &sm.qt[hm * 32 + (lane & 31)][0];
+          uint2 ol = *(const uint2*)(orow + kc), oh = *(const uint2*)(orow + kc + 8);
+          uint2 ql = *(const uint2*)(qrow + kc), qh = *(const uint2*)(qrow + kc + 8);
+          bf16x8 of = __builtin_bit_cast(bf16x8, make_uint4(ol.x, ol.y, oh.x, oh.y));
+          bf16x8 qf = __builtin_bit_cast(bf16x8, make_uint4(ql.x, ql.y, qh.x, qh.y));
+          dv[hm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(of, st ? pf1 : pf0, dv[hm], 0, 0, 0);
+          dk[hm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf, st ? df1 : df0, dk[hm], 0, 0, 0);
+        }
       }
     }
   }
@@ -722,40 +733,71 @@ __global__ void k_dq_reduce(const float* ws, int S, int64_t total, float* dq) {
   }
 }
 
-template <int HD, int NW, bool SPLIT>
+// dO [B*n][H*hd] -> dO^T [B][H][hd][n], 64 x 64 tiles through LDS
+__global__ __launch_bounds__(256) void k_heads_transpose(const bf16* __restrict__ x, bf16* __restrict__ xt, int n,
+                                                         int H, int hd) {
+  __shared__ uint16_t tile[64][66];
+  const int d = H * hd, t0 = blockIdx.x * 64, c0 = blockIdx.y * 64, b = blockIdx.z;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int r = ty; r < 64; r += 4) {
+    const int t = t0 + r, c = c0 + tx;
+    tile[r][tx] = (t < n && c < d) ? x[((int64_t)b * n + t) * d + c].x : (uint16_t)0;
+  }
+  __syncthreads();
+  for (int r = ty; r < 64; r += 4) {
+    const int c = c0 + r, t = t0 + tx;
+    if (c < d && t < n) xt[((int64_t)b * d + c) * n + t].x = tile[tx][r];
+  }
+}
+
+template <int HD, int NW, bool SPLIT, bool TR>
 hipError_t launch_dq(const AttnBwdArgs& a, int S, hipStream_t s) {
   static bool attr = false;
   if (!attr) {
-    hipError_t e = set_lds<DqSmem<HD>>(k_swa_dq<HD, NW, SPLIT>);
+    hipError_t e = set_lds<DqSmem<HD>>(k_swa_dq<HD, NW, SPLIT, TR>);
     if (e != hipSuccess) return e;
     attr = true;
   }
-  hipLaunchKernelGGL((k_swa_dq<HD, NW, SPLIT>), dim3(cdiv(a.n, NW * QW), a.H, a.B * S), dim3(NW * 64),
+  hipLaunchKernelGGL((k_swa_dq<HD, NW, SPLIT, TR>), dim3(cdiv(a.n, NW * QW), a.H, a.B * S), dim3(NW * 64),
                      sizeof(DqSmem<HD>), s, a, S);
+  return hipGetLastError();
+}
+
+template <int HD, bool TR>
+hipError_t launch_dkv(const AttnBwdArgs& a, int P, hipStream_t s) {
+  static bool attr = false;
+  if (!attr) {
+    hipError_t e = set_lds<DkvSmem<HD>>(k_swa_dkv<HD, TR>);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  hipLaunchKernelGGL((k_swa_dkv<HD, TR>), dim3(cdiv(a.n, BQ), a.H, a.B * P), dim3(256), sizeof(DkvSmem<HD>), s, a,
+                     P);
   return hipGetLastError();
 }
 
 template <int HD>
 hipError_t launch_bwd(const AttnBwdArgs& a, hipStream_t s) {
-  static bool attr = false;
-  if (!attr) {
-    hipError_t e = set_lds<DkvSmem<HD>>(k_swa_dkv<HD>);
-    if (e != hipSuccess) return e;
-    attr = true;
-  }
   hipError_t e = swa_dvec_bf16(a, s);
   if (e != hipSuccess) return e;
+  // transposed tiles are read with 16-byte copies when the caller provides the
+  // transposed key ring and a dO^T scratch, 8-key groups stay inside the ring
+  // (R % 8 == 0) and 8-query groups inside the chunk (n % 8 == 0)
+  const bool tr = a.ktr && a.dot && a.R % 8 == 0 && a.n % 8 == 0;
+  if (tr)
+    hipLaunchKernelGGL(k_heads_transpose, dim3(cdiv(a.n, 64), cdiv(a.H * HD, 64), a.B), dim3(256), 0, s,
+                       (const bf16*)a.dout, (bf16*)a.dot, a.n, a.H, HD);
   const int64_t blocks8 = (int64_t)cdiv(a.n, 8 * QW) * a.H * a.B;
   const int64_t ntiles = (std::min<int64_t>(a.window, a.pos0 + 1) + 8 * QW) / KT + 1;
   const int64_t total = (int64_t)a.B * a.n * a.H * HD;
   const int S = attn_splits(blocks8, ntiles, total, a.ws, a.ws_floats);
   if (S > 1) {
-    e = launch_dq<HD, 8, true>(a, S, s);
+    e = tr ? launch_dq<HD, 8, true, true>(a, S, s) : launch_dq<HD, 8, true, false>(a, S, s);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_dq_reduce, dim3((unsigned)std::min<int64_t>(cdiv(total, 256), 4096)), dim3(256), 0, s, a.ws,
                        S, total, a.dq);
   } else {
-    e = launch_dq<HD, 8, false>(a, 1, s);
+    e = tr ? launch_dq<HD, 8, false, true>(a, 1, s) : launch_dq<HD, 8, false, false>(a, 1, s);
     if (e != hipSuccess) return e;
   }
   // dK/dV: split each key block's query range when the grid is small (ordered sum after)
@@ -766,7 +808,8 @@ hipError_t launch_bwd(const AttnBwdArgs& a, hipStream_t s) {
     P = std::min(P, (int)cdiv(a.n, KT));
     while (P > 1 && 2LL * P * total > a.ws_floats) --P;
   }
-  hipLaunchKernelGGL(k_swa_dkv<HD>, dim3(cdiv(a.n, BQ), a.H, a.B * P), dim3(256), sizeof(DkvSmem<HD>), s, a, P);
+  e = tr ? launch_dkv<HD, true>(a, P, s) : launch_dkv<HD, false>(a, P, s);
+  if (e != hipSuccess) return e;
   if (P > 1)
     hipLaunchKernelGGL(k_dkv_reduce, dim3((unsigned)std::min<int64_t>(cdiv(total, 256), 4096)), dim3(256), 0, s,
                        a.ws, P, total, a.dk, a.dv);

@@ -167,6 +167,8 @@ template <typename T>
 __global__ __launch_bounds__(256) void k_rope_qkv(const float* __restrict__ qkv, RopeRing rr) {
   __shared__ T vt[128][RT + 2];  // [dim][token]
   __shared__ T qs[128][RT + 2];
+  constexpr bool KTR = sizeof(T) == 2;  // transposed key ring (bf16 contexts only)
+  __shared__ T ks[KTR ? 128 : 1][RT + 2];
   const int h = blockIdx.y, b = blockIdx.z;
   const int t0 = blockIdx.x * RT;
   const int hd = rr.hd, half = hd / 2, d = rr.H * hd;
@@ -194,8 +196,13 @@ __global__ __launch_bounds__(256) void k_rope_qkv(const float* __restrict__ qkv,
     a = row[d + i];
     bb = row[d + i + half];
     T* krow = Kr + (bh * rr.R + slot) * hd;
-    krow[i] = from_f<T>(a * c - bb * s);
-    krow[i + half] = from_f<T>(bb * c + a * s);
+    const T k0 = from_f<T>(a * c - bb * s), k1 = from_f<T>(bb * c + a * s);
+    krow[i] = k0;
+    krow[i + half] = k1;
+    if constexpr (KTR) {
+      ks[i][tt] = k0;
+      ks[i + half][tt] = k1;
+    }
     const float v0 = row[2 * d + i], v1 = row[2 * d + i + half];
     T* vrow = Vr + (bh * rr.R + slot) * hd;
     vrow[i] = from_f<T>(v0);
@@ -204,8 +211,9 @@ __global__ __launch_bounds__(256) void k_rope_qkv(const float* __restrict__ qkv,
     vt[i + half][tt] = from_f<T>(v1);
   }
   __syncthreads();
-  // V^T ring rows: [dim][slot], consecutive tokens -> consecutive slots (mod R)
+  // V^T (and K^T) ring rows: [dim][slot], consecutive tokens -> consecutive slots (mod R)
   T* Vt = (T*)rr.vtr + bh * hd * rr.R;
+  T* Kt = (KTR && rr.ktr) ? (T*)rr.ktr + bh * hd * rr.R : nullptr;
   T* Qt = rr.qt ? (T*)rr.qt + bh * hd * rr.n : nullptr;
   for (int e = threadIdx.x; e < hd * RT; e += blockDim.x) {
     const int dim = e / RT, tt = e % RT;
@@ -213,6 +221,8 @@ __global__ __launch_bounds__(256) void k_rope_qkv(const float* __restrict__ qkv,
     const int t = t0 + tt;
     const int slot = (int)((rr.pos0 + t) % rr.R);
     Vt[(int64_t)dim * rr.R + slot] = vt[dim][tt];
+    if constexpr (KTR)
+      if (Kt) Kt[(int64_t)dim * rr.R + slot] = ks[dim][tt];
     if (Qt) Qt[(int64_t)dim * rr.n + t] = qs[dim][tt];
   }
 }

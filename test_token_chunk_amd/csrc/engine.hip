@@ -46,6 +46,7 @@ struct LayerW {
   void* kr = nullptr;     // ring K [B][H][R][hd]
   void* vr = nullptr;     // ring V [B][H][R][hd]
   void* vtr = nullptr;    // ring V^T [B][H][hd][R]
+  void* ktr = nullptr;    // ring K^T [B][H][hd][R] (bf16 blocks whose attention runs backward)
 };
 
 struct FastW {
@@ -94,7 +95,7 @@ struct ttt_ctx {
   void *hf = nullptr, *dlogits = nullptr;
   int* nvalid = nullptr;
   float *dh = nullptr, *tmpf = nullptr, *dq = nullptr, *dk = nullptr, *dv = nullptr, *dvec = nullptr;
-  void *dyN = nullptr, *dz = nullptr, *dhT = nullptr, *dO = nullptr, *dqkv = nullptr;
+  void *dyN = nullptr, *dz = nullptr, *dhT = nullptr, *dO = nullptr, *dOT = nullptr, *dqkv = nullptr;
   std::vector<void*> dyT, dzT;  // per fast block: inputs of its weight-gradient GEMMs (side stream)
   int* err_dev = nullptr;
   float* ws = nullptr;  // split-K / split-key workspace (used by one launch at a time)
@@ -301,6 +302,7 @@ int layer_fwd(ttt_ctx* c, int l, float* h, int n, int64_t p0, int mode, TopActs*
     rr.kr = w.kr;
     rr.vr = w.vr;
     rr.vtr = w.vtr;
+    rr.ktr = w.ktr;
     CK(rope_qkv_f32in(c->qkvb, B, rr, c->bf16 ? 1 : 0, c->stream));
     AttnArgs a;
     a.q = rr.q;
@@ -512,6 +514,8 @@ int top_chunk(ttt_ctx* c, const int32_t* tgt, int64_t ld, const float* hsrc, int
     ab.kr = lw.kr;
     ab.vr = lw.vr;
     ab.vtr = lw.vtr;
+    ab.ktr = lw.ktr;
+    ab.dot = c->dOT;
     ab.o = a.o;
     ab.dout = c->dO;
     ab.lse = a.lse;
@@ -719,6 +723,10 @@ int build(ttt_ctx* c, const ttt_weights* w) {
     CK(hipMemset(lw.kr, 0, ring));
     CK(hipMemset(lw.vr, 0, ring));
     CK(hipMemset(lw.vtr, 0, ring));
+    if (c->bf16 && l > c->l0) {
+      AL(lw.ktr, ring);
+      CK(hipMemset(lw.ktr, 0, ring));
+    }
   }
   // fast weights: fp32 masters per row plus T shadows in both layouts
   const int64_t fsz = 3LL * f * d;
@@ -786,6 +794,7 @@ int build(ttt_ctx* c, const ttt_weights* w) {
   AL(c->dz, rows_top * 2 * f * es);
   AL(c->dhT, rows_top * d * es);
   AL(c->dO, rows_top * d * es);
+  if (c->bf16) AL(c->dOT, rows_top * d * es);
   AL(c->dqkv, rows_top * 3 * d * es);
   AL(c->err_dev, 256);
   c->ws_floats = 8 * rows_top * (int64_t)(d + 2 * H);
@@ -827,6 +836,7 @@ int reset_state(ttt_ctx* c) {
     CK(hipMemsetAsync(c->lw[l].kr, 0, ring, c->stream));
     CK(hipMemsetAsync(c->lw[l].vr, 0, ring, c->stream));
     CK(hipMemsetAsync(c->lw[l].vtr, 0, ring, c->stream));
+    if (c->lw[l].ktr) CK(hipMemsetAsync(c->lw[l].ktr, 0, ring, c->stream));
   }
   CK(hipMemsetAsync(c->err_dev, 0, 4, c->stream));
   CK(hipStreamSynchronize(c->stream));

@@ -39,13 +39,13 @@ extern "C" int tttk_swa_fwd(int dtype, const void* q, const void* kr, const void
 }
 
 extern "C" int tttk_swa_bwd(int dtype, const void* q, const void* qt, const void* kr, const void* vr, const void* vtr,
-                            const void* o, const void* dout, const float* lse, float* dvec, float* dq, float* dk,
-                            float* dv, int32_t B, int32_t H, int32_t hd, int32_t n, int32_t R, int32_t window,
-                            int64_t pos0, float* ws, int64_t ws_floats, void* stream) {
+                            const void* ktr, const void* o, const void* dout, const float* lse, float* dvec, float* dq,
+                            float* dk, float* dv, void* dot, int32_t B, int32_t H, int32_t hd, int32_t n, int32_t R,
+                            int32_t window, int64_t pos0, float* ws, int64_t ws_floats, void* stream) {
   if (!q || !qt || !kr || !vr || !vtr || !o || !dout || !lse || !dvec || !dq || !dk || !dv || B < 1 || H < 1 ||
       hd < 2 || hd % 2 || hd > 128 || n < 0 || window < n || pos0 < 0 || R < window + n - 1)
     return TTT_EINVAL;
-  AttnBwdArgs a{q, qt, kr, vr, vtr, o, dout, lse, dvec, dq, dk, dv, B, H, hd, n, R, window, pos0, ws,
+  AttnBwdArgs a{q, qt, kr, vr, vtr, ktr, o, dout, lse, dvec, dq, dk, dv, dot, B, H, hd, n, R, window, pos0, ws,
                 ws ? ws_floats : 0};
   if (dtype == TTT_F32) return code(swa_bwd_simt<float>(a, (hipStream_t)stream));
   if (dtype == TTT_BF16) return code(swa_bwd_mfma(a, (hipStream_t)stream));

@@ -37,6 +37,7 @@ struct RopeRing {
   void* kr;            // ring K [B][H][R][hd] T
   void* vr;            // ring V [B][H][R][hd] T
   void* vtr;           // ring V^T [B][H][hd][R] T
+  void* ktr = nullptr; // ring K^T [B][H][hd][R] T, or null (needed only where the backward runs)
 };
 
 struct Epi {
@@ -130,6 +131,7 @@ struct AttnBwdArgs {
   const void* kr;   // ring K
   const void* vr;   // ring V
   const void* vtr;  // ring V^T
+  const void* ktr;  // ring K^T [B][H][hd][R] or null (then K^T tiles are transposed in LDS)
   const void* o;    // [B*n][H*hd] forward output (T)
   const void* dout; // [B*n][H*hd] gradient of the output (T)
   const float* lse; // [B][H][n]
@@ -137,6 +139,7 @@ struct AttnBwdArgs {
   float* dq;        // [B*n][H*hd] fp32 (rotated frame)
   float* dk;        // [B*n][H*hd] fp32 (rotated frame), in-chunk keys only
   float* dv;        // [B*n][H*hd] fp32
+  void* dot;        // scratch for dO^T [B][H][hd][n] (T), or null (then dO^T is transposed in LDS)
   int B, H, hd, n, R, window;
   int64_t pos0;
   float* ws = nullptr;  // optional fp32 workspace: lets small grids split the key range of dq

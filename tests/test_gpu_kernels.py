@@ -158,12 +158,17 @@ def ref_attention_bwd(q, kr, vr, dO, pos0, window):
     return dq, dk, dv
 
 
+@pytest.mark.parametrize("tr", [False, True])
 @pytest.mark.parametrize("use_ws", [False, True])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("B,H,hd,n,window,pos0,R", [(1, 2, 32, 64, 256, 1000, 320), (2, 2, 64, 100, 130, 517, 256),
-                                                    (1, 2, 128, 130, 200, 331, 336), (1, 2, 128, 200, 1536, 3000, 1736)])
-def test_swa_bwd_matches_fp64(dtype, B, H, hd, n, window, pos0, R, use_ws):
+                                                    (1, 2, 128, 130, 200, 331, 336), (1, 2, 128, 200, 1536, 3000, 1736),
+                                                    (2, 3, 96, 136, 300, 4000, 440)])
+def test_swa_bwd_matches_fp64(dtype, B, H, hd, n, window, pos0, R, use_ws, tr):
+    """tr: the transposed key ring and a dO^T scratch are passed (16-byte tile copies when n % 8 == 0)."""
     torch = _torch()
+    if tr and dtype == "f32":
+        pytest.skip("transposed operands only feed the bf16 matrix-core path")
     from test_token_chunk_amd import swa_bwd, swa_fwd
     dt = torch.bfloat16 if dtype == "bf16" else torch.float32
     q, kr, vr = ring_inputs(torch, B, H, hd, n, R, window, pos0, dt, seed=3)
@@ -177,8 +182,10 @@ def test_swa_bwd_matches_fp64(dtype, B, H, hd, n, window, pos0, R, use_ws):
     dk = torch.empty_like(dq)
     dv = torch.empty_like(dq)
     dvec = torch.empty(B, H, n, dtype=torch.float32, device="cuda")
+    ktr = cu(kr.transpose(2, 3)) if tr else None
+    dot = torch.full((B * n * H * hd,), float("nan"), dtype=dt, device="cuda") if tr else None
     swa_bwd(cu(q), cu(q.transpose(2, 3)), cu(kr), cu(vr), cu(vr.transpose(2, 3)), o, cu(dO.reshape(B * n, H * hd)),
-            lse, dvec, dq, dk, dv, pos0, window, ws=ws)
+            lse, dvec, dq, dk, dv, pos0, window, ws=ws, ktr=ktr, dot=dot)
     torch.cuda.synchronize()
     rq, rk, rv = ref_attention_bwd(q.double().numpy(), kr.double().numpy(), vr.double().numpy(),
                                    dO.double().numpy().transpose(0, 2, 1, 3), pos0, window)
