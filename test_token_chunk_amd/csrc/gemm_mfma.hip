@@ -57,7 +57,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, f32x16 (&acc)[T
   // Outputs stored transposed ([n][m]: the refreshed W^T shadow of the fused SGD step,
   // act^T, dz^T) are staged through LDS and written as 16-byte row segments.
   constexpr bool TR = (EK == EPI_SGD) || (EK == EPI_SWIGLU_BWD) || DUAL || (EK == EPI_SWIGLU_IL);
-  static_assert(EK != EPI_SWIGLU_IL || TN == 2, "interleaved SwiGLU pairs the two 32-column halves of a wave");
+  static_assert(EK != EPI_SWIGLU_IL || TN % 2 == 0, "interleaved SwiGLU pairs 32-column halves of a wave");
   constexpr int TLD = BM + 8;
   bf16* tr0 = reinterpret_cast<bf16*>(smem_raw);  // [BN][TLD]
   bf16* tr1 = tr0 + BN * TLD;                     // second tile (dz_u^T)
@@ -66,16 +66,40 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, f32x16 (&acc)[T
   const bool want_t = TR && ((EK != EPI_SWIGLU && EK != EPI_SWIGLU_IL) || g.e.t != nullptr);
   const int hi = lane >> 5;
   const Epi& e = g.e;
-  // Epilogues that read memory (fp32 master, residual stream, saved z_g/z_u) first load
-  // every element of the lane into registers, then compute and store: interleaving a
-  // load with the stores of earlier elements would serialize each element on a full
-  // memory round trip (the stores may alias the loads).
+  // Epilogues that read memory (fp32 master, residual stream) first load every element of
+  // a 32-row group of the wave into registers, then compute and store: interleaving a load
+  // with the stores of earlier elements would serialize each element on a full memory
+  // round trip (the stores may alias the loads).
   constexpr bool READS = (EK == EPI_SGD) || (EK == EPI_ADD_F32);
-  constexpr int NE = TM * TN * 16;
-  float pre0[READS ? NE : 1];
-  if constexpr (READS) {
+  if constexpr (EK == EPI_SWIGLU_IL) {
+    // lane holds gate column (j = 2p) and up column (j = 2p + 1) of hidden unit fi
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+    for (int jp = 0; jp < TN / 2; ++jp) {
+      const int fl = wn0 / 2 + jp * 32 + lr, fi = n0 / 2 + fl;
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int ml = wm0 + i * 32 + 8 * q + 4 * hi + r, m = m0 + ml;
+            const float x = acc[i][2 * jp][4 * q + r], u = acc[i][2 * jp + 1][4 * q + r];
+            const float act = x / (1.f + __expf(-x)) * u;
+            if (m < g.M && 2 * fi < g.N) {
+              ((bf16*)e.c)[bz * e.sc + (int64_t)m * e.ldc + fi] = f2bf(act);
+              if (e.zg) {
+                ((bf16*)e.zg)[bz * e.sz + (int64_t)m * e.ldz + fi] = f2bf(x);
+                ((bf16*)e.zu)[bz * e.sz + (int64_t)m * e.ldz + fi] = f2bf(u);
+              }
+            }
+            tr0[fl * TLD + ml] = f2bf(act);
+          }
+    }
+  } else
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    float pre0[READS ? TN * 16 : 1];
+    if constexpr (READS) {
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
         const int n = n0 + wn0 + j * 32 + lr;
@@ -84,40 +108,17 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, f32x16 (&acc)[T
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int m = m0 + wm0 + i * 32 + 8 * q + 4 * hi + r;
-            const int idx = (i * TN + j) * 16 + 4 * q + r;
             const bool in = m < g.M && n < g.N;
+            float v = 0.f;
             if constexpr (EK == EPI_SGD) {
-              pre0[idx] = in ? e.master[bz * e.sm + (int64_t)m * e.ldm + n] : 0.f;
+              if (in) v = e.master[bz * e.sm + (int64_t)m * e.ldm + n];
             } else {
-              pre0[idx] = in ? ((const float*)e.c)[bz * e.sc + (int64_t)m * e.ldc + n] : 0.f;
+              if (in) v = ((const float*)e.c)[bz * e.sc + (int64_t)m * e.ldc + n];
             }
+            pre0[j * 16 + 4 * q + r] = v;
           }
       }
-  }
-  if constexpr (EK == EPI_SWIGLU_IL) {
-    // lane holds gate column (j = 0) and up column (j = 1) of hidden unit fi
-    const int fl = wn0 / 2 + lr, fi = n0 / 2 + fl;
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int ml = wm0 + i * 32 + 8 * q + 4 * hi + r, m = m0 + ml;
-          const float x = acc[i][0][4 * q + r], u = acc[i][1][4 * q + r];
-          const float act = x / (1.f + __expf(-x)) * u;
-          if (m < g.M && 2 * fi < g.N) {
-            ((bf16*)e.c)[bz * e.sc + (int64_t)m * e.ldc + fi] = f2bf(act);
-            if (e.zg) {
-              ((bf16*)e.zg)[bz * e.sz + (int64_t)m * e.ldz + fi] = f2bf(x);
-              ((bf16*)e.zu)[bz * e.sz + (int64_t)m * e.ldz + fi] = f2bf(u);
-            }
-          }
-          tr0[fl * TLD + ml] = f2bf(act);
-        }
-  } else
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
+    }
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       const int nl = wn0 + j * 32 + lr, n = n0 + nl;
@@ -126,7 +127,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, f32x16 (&acc)[T
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int ml = wm0 + i * 32 + 8 * q + 4 * hi + r, m = m0 + ml;
-          const int idx = (i * TN + j) * 16 + 4 * q + r;
+          const int idx = j * 16 + 4 * q + r;
           const bool in = m < g.M && n < g.N;
           const float x = acc[i][j][4 * q + r];
           if constexpr (DUAL) {
@@ -164,12 +165,13 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, f32x16 (&acc)[T
           } else if constexpr (EK == EPI_ADD_F32) {
             if (in) ((float*)e.c)[bz * e.sc + (int64_t)m * e.ldc + n] = pre0[idx] + x;
           } else if constexpr (SPLIT) {
-            if (in) g.ws[(((int64_t)split * (gridDim.z / S) + bz) * g.M + m) * g.N + n] = x;
+            if (in) g.ws[(((int64_t)split * g.batch + bz) * g.M + m) * g.N + n] = x;
           } else {
             if (in) epi_apply_k<bf16, EK>(e, bz, m, n, x);
           }
         }
     }
+  }
   if constexpr (TR) {
     if (!want_t) return;
     __syncthreads();
@@ -411,6 +413,306 @@ __global__ __launch_bounds__(256) void k_gemm_dl(GemmArgs g) {
   gemm_epilogue<BM, BN, WM, WN, false, EK, SPLIT>(g, acc, accu, smem_raw, m0, n0, wm0, wn0, tid, bz, split, S);
 }
 
+// ------------------------------------------------------------------ wide tiles
+// BM x 256 block tile, 8 waves in a 2 x 4 grid, each wave (BM/2) x 64 = (BM/64) x 2 MFMA
+// tiles; one block (two waves per SIMD) per CU.  Two configurations:
+//   BM = 256: K steps of 32 through a ring of 4 stages (32 KB each), wave tile 128 x 64;
+//   BM = 128: K steps of 64 through a ring of 3 stages (48 KB each), wave tile 64 x 64.
+// A wave tile of 128 x 64 reads 0.75 KB of operands from LDS per MFMA instead of the
+// 1 KB of a 64 x 64 one; on CDNA4 the 64 x 64 tile is bound by LDS bandwidth.
+//
+// Operands go straight from global memory to LDS (global_load_lds), a step WST - 2 steps
+// ahead of its use.  LDS rows hold one K step of one operand row (64 or 128 bytes) with the
+// 16-byte chunks XOR-swizzled by (row / 4) % 4 or (row / 2) % 8, which puts the 16 rows read
+// by a quarter-wave on distinct banks.  Inside a step the fragments of the next 16-deep
+// slice are read while the MFMAs of the current one run, across the step boundary too:
+// the barrier that publishes step kt + 1 sits inside step kt.
+//
+// The MFMA takes the B fragment as its first operand, so a lane's accumulators hold one
+// output row m and four consecutive columns n per 4-register group: the epilogues store
+// 16-byte (fp32) or 8-byte (bf16) row segments.
+//
+// XCD-aware tile order: workgroups are dispatched round-robin over the 8 XCDs, each with
+// its own L2.  Block b (1-D grid of 8 * per blocks) takes logical tile (b % 8) * per + b / 8,
+// so every XCD walks a contiguous range of logical tiles; logical tiles run down groups of
+// up to 8 row tiles before moving to the next column, so the tiles an XCD has in flight
+// form a compact rectangle whose operand panels are shared in its L2.
+// Requires M % BM == 0, N % 256 == 0 and a K range that is a multiple of the K step.
+template <int BM>
+struct WideCfg {
+  static constexpr int BK = BM == 256 ? 32 : 64;     // K step
+  static constexpr int ST = BM == 256 ? 4 : 3;       // ring stages
+  static constexpr int RB = BK * 2;                  // LDS row bytes
+  static constexpr int SBYTES = (BM + 256) * RB;     // one stage
+  static constexpr int LPT = (BM + 256) * RB / 1024 / 8;  // 1 KB DMA blocks per wave per step
+};
+
+template <int BM, int EK>
+constexpr size_t wide_lds_bytes() {
+  const size_t ops = (size_t)WideCfg<BM>::ST * WideCfg<BM>::SBYTES;
+  const bool tr = EK == EPI_SGD || EK == EPI_SWIGLU_IL;
+  const size_t trb = tr ? (size_t)256 * (BM + 8) * 2 : 0;
+  return ops > trb ? ops : trb;
+}
+
+template <int BK>
+__device__ __forceinline__ int wide_swz(int row) {
+  return BK == 32 ? (row >> 2) & 3 : (row >> 1) & 7;
+}
+
+// Epilogue of the wide tiles: lane holds C[m][n .. n+3] with m = m0 + wm0 + 32 i + (l % 32),
+// n = n0 + wn0 + 32 j + 8 q + 4 (l / 32) in acc[i][j][4q .. 4q+3].
+template <int BM, int EK, bool SPLIT, int TM, int TN>
+__device__ __forceinline__ void wide_epilogue(const GemmArgs& g, f32x16 (&acc)[TM][TN], unsigned char* smem_raw,
+                                              int m0, int n0, int wm0, int wn0, int tid, int bz, int split) {
+  constexpr int BN = 256, NT = 512;
+  const int lane = tid & 63, lr = lane & 31, hi = lane >> 5;
+  const Epi& e = g.e;
+  constexpr bool TR = EK == EPI_SGD || EK == EPI_SWIGLU_IL;
+  constexpr int TLD = BM + 8;
+  bf16* tr0 = reinterpret_cast<bf16*>(smem_raw);  // [BN][TLD] (IL: [BN/2][TLD])
+  auto pk4 = [](float a, float b, float c, float d) {
+    return make_uint2((uint32_t)f2bf(a).x | ((uint32_t)f2bf(b).x << 16),
+                      (uint32_t)f2bf(c).x | ((uint32_t)f2bf(d).x << 16));
+  };
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int ml = wm0 + i * 32 + lr, m = m0 + ml;
+    if constexpr (EK == EPI_SWIGLU_IL) {
+      static_assert(TN == 2, "gate and up halves of one 64-column group");
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int fl = wn0 / 2 + 8 * q + 4 * hi, fi = n0 / 2 + fl;
+        float x[4], u[4], a[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          x[r] = acc[i][0][4 * q + r];
+          u[r] = acc[i][1][4 * q + r];
+          a[r] = x[r] / (1.f + __expf(-x[r])) * u[r];
+          tr0[(fl + r) * TLD + ml] = f2bf(a[r]);
+        }
+        *(uint2*)((bf16*)e.c + bz * e.sc + (int64_t)m * e.ldc + fi) = pk4(a[0], a[1], a[2], a[3]);
+        if (e.zg) {
+          *(uint2*)((bf16*)e.zg + bz * e.sz + (int64_t)m * e.ldz + fi) = pk4(x[0], x[1], x[2], x[3]);
+          *(uint2*)((bf16*)e.zu + bz * e.sz + (int64_t)m * e.ldz + fi) = pk4(u[0], u[1], u[2], u[3]);
+        }
+      }
+    } else {
+      // epilogues that read memory load the row group first (stores could alias the loads)
+      constexpr bool READS = EK == EPI_SGD || EK == EPI_ADD_F32;
+      float4 pre[READS ? TN * 4 : 1];
+      if constexpr (READS) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int n = n0 + wn0 + j * 32 + 8 * q + 4 * hi;
+            pre[j * 4 + q] = EK == EPI_SGD ? *(const float4*)(e.master + bz * e.sm + (int64_t)m * e.ldm + n)
+                                           : *(const float4*)((const float*)e.c + bz * e.sc + (int64_t)m * e.ldc + n);
+          }
+      }
+      const int64_t shrow = (EK == EPI_SGD && e.il_f) ? swiglu_il_row(m, e.il_f) : m;
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int nl = wn0 + j * 32 + 8 * q + 4 * hi, n = n0 + nl;
+          const float v0 = acc[i][j][4 * q], v1 = acc[i][j][4 * q + 1], v2 = acc[i][j][4 * q + 2],
+                      v3 = acc[i][j][4 * q + 3];
+          if constexpr (SPLIT) {
+            *(float4*)(g.ws + (((int64_t)split * g.batch + bz) * g.M + m) * g.N + n) = make_float4(v0, v1, v2, v3);
+          } else if constexpr (EK == EPI_F32) {
+            *(float4*)((float*)e.c + bz * e.sc + (int64_t)m * e.ldc + n) = make_float4(v0, v1, v2, v3);
+          } else if constexpr (EK == EPI_T) {
+            *(uint2*)((bf16*)e.c + bz * e.sc + (int64_t)m * e.ldc + n) = pk4(v0, v1, v2, v3);
+          } else if constexpr (EK == EPI_ADD_F32) {
+            const float4 p = pre[j * 4 + q];
+            *(float4*)((float*)e.c + bz * e.sc + (int64_t)m * e.ldc + n) =
+                make_float4(p.x + v0, p.y + v1, p.z + v2, p.w + v3);
+          } else if constexpr (EK == EPI_SGD) {
+            const float4 p = pre[j * 4 + q];
+            const float w0 = p.x - e.lr * v0, w1 = p.y - e.lr * v1, w2 = p.z - e.lr * v2, w3 = p.w - e.lr * v3;
+            *(float4*)(e.master + bz * e.sm + (int64_t)m * e.ldm + n) = make_float4(w0, w1, w2, w3);
+            *(uint2*)((bf16*)e.sh + bz * e.ssh + shrow * e.ldsh + n) = pk4(w0, w1, w2, w3);
+            tr0[(nl + 0) * TLD + ml] = f2bf(w0);
+            tr0[(nl + 1) * TLD + ml] = f2bf(w1);
+            tr0[(nl + 2) * TLD + ml] = f2bf(w2);
+            tr0[(nl + 3) * TLD + ml] = f2bf(w3);
+          }
+        }
+    }
+  }
+  if constexpr (TR) {
+    if (EK == EPI_SWIGLU_IL && e.t == nullptr) return;
+    __syncthreads();
+    // tile rows (output rows of the transposed matrix) hold BM consecutive m values
+    bf16* dst = EK == EPI_SGD ? (bf16*)e.shT + bz * e.sshT : (bf16*)e.t + bz * e.st;
+    const int64_t ld = EK == EPI_SGD ? e.ldshT : e.ldt;
+    constexpr int CH = BM / 8;
+    constexpr int ROWS = EK == EPI_SWIGLU_IL ? BN / 2 : BN;
+    const int row0 = EK == EPI_SWIGLU_IL ? n0 / 2 : n0;
+    for (int c = tid; c < ROWS * CH; c += NT) {
+      const int rl = c / CH, ml = (c % CH) * 8;
+      *(uint4*)(dst + (int64_t)(row0 + rl) * ld + m0 + ml) = *(const uint4*)(tr0 + rl * TLD + ml);
+    }
+  }
+}
+
+template <int BM, int EK, bool SPLIT>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_gemm_wide(GemmArgs g) {
+  using C = WideCfg<BM>;
+  constexpr int BN = 256, BK = C::BK, WST = C::ST, RB = C::RB, SBYTES = C::SBYTES, LPT = C::LPT;
+  constexpr int WM = BM / 2, WN = 64, TM = WM / 32, TN = WN / 32;
+  constexpr int RPB = 1024 / RB, CPR = RB / 16, NH = BK / 16;
+  constexpr int ABYTES = BM * RB, ABLK = BM / RPB / 8, BBLK = BN / RPB / 8;
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  const int S = SPLIT ? (int)g.e.ldt : 1;
+  const int tiles_m = g.M / BM, tiles_n = g.N / BN, tiles = tiles_m * tiles_n;
+  const int per = gridDim.x / 8;
+  const int t = (blockIdx.x % 8) * per + blockIdx.x / 8;
+  if (t >= tiles * g.batch * S) return;  // padding block of the last XCD range (uniform, before any barrier)
+  const int zz = t / tiles, r = t % tiles;
+  const int GM = min(8, tiles_m);
+  const int grp = r / (GM * tiles_n), first_m = grp * GM, gm = min(tiles_m - first_m, GM);
+  const int rr = r - grp * GM * tiles_n;
+  const int m0 = (first_m + rr % gm) * BM, n0 = (rr / gm) * BN;
+  const int bz = SPLIT ? zz / S : zz;
+  const int split = SPLIT ? zz % S : 0;
+  const int kbeg = SPLIT ? split * (int)g.e.st : 0;
+  const int kend = SPLIT ? min(g.K, kbeg + (int)g.e.st) : g.K;
+  const bf16* A = (const bf16*)g.A + bz * g.sA;
+  const bf16* B = (const bf16*)g.B + bz * g.sB;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int wm0 = (wid >> 2) * WM, wn0 = (wid & 3) * WN;
+  const int nk = (kend - kbeg) / BK;
+  // 1 KB DMA block = RPB rows; lane L lands at row L / CPR, physical chunk L % CPR and
+  // fetches the logical chunk the swizzle puts there.  Wave w copies A blocks
+  // [w ABLK, (w+1) ABLK) and B blocks [w BBLK, (w+1) BBLK).
+  const int lrow = lane / CPR, lpc = lane % CPR;
+  const int arow = wid * ABLK * RPB + lrow, brow = wid * BBLK * RPB + lrow;
+  const bf16* Ag = A + (int64_t)(m0 + arow) * g.lda;
+  const bf16* Bg = B + (int64_t)(n0 + brow) * g.ldb;
+
+  auto issue = [&](int kt) {
+    unsigned char* base = smem_raw + (kt % WST) * SBYTES;
+    const int k0 = kbeg + kt * BK;
+#pragma unroll
+    for (int i = 0; i < ABLK; ++i) {
+      const int lc = lpc ^ wide_swz<BK>(arow + i * RPB);
+      __builtin_amdgcn_global_load_lds(Ag + (int64_t)(i * RPB) * g.lda + k0 + lc * 8,
+                                       LDSP(base + (wid * ABLK + i) * 1024), 16, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < BBLK; ++i) {
+      const int lc = lpc ^ wide_swz<BK>(brow + i * RPB);
+      __builtin_amdgcn_global_load_lds(Bg + (int64_t)(i * RPB) * g.ldb + k0 + lc * 8,
+                                       LDSP(base + ABYTES + (wid * BBLK + i) * 1024), 16, 0, 0);
+    }
+  };
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
+
+  const int lr = lane & 31, lk = lane >> 5, sw = wide_swz<BK>(lr);
+  const int a_off = (wm0 + lr) * RB, b_off = ABYTES + (wn0 + lr) * RB;
+  bf16x8 f0a[TM], f0b[TN], f1a[TM], f1b[TN];
+  // fragments of 16-deep slice h of step kt: logical chunk 2h + lk of the row
+#define FRAGS(fa, fb, kt, h)                                                                   \
+  {                                                                                            \
+    const unsigned char* sb = smem_raw + ((kt) % WST) * SBYTES;                                \
+    const int p = ((2 * (h) + lk) ^ sw) << 4;                                                  \
+    _Pragma("unroll") for (int i = 0; i < TM; ++i) fa[i] = *(const bf16x8*)(sb + a_off + i * 32 * RB + p); \
+    _Pragma("unroll") for (int j = 0; j < TN; ++j) fb[j] = *(const bf16x8*)(sb + b_off + j * 32 * RB + p); \
+  }
+#define MFMA_ROWS(fa, fb, i0, i1)                                                              \
+  _Pragma("unroll") for (int i = (i0); i < (i1); ++i)                                          \
+    _Pragma("unroll") for (int j = 0; j < TN; ++j)                                             \
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+#define SB() __builtin_amdgcn_sched_barrier(0)
+  // waits until at most `later` steps of DMA are outstanding (later <= 2 here)
+#define WAIT_STEPS(later)                                                                      \
+  {                                                                                            \
+    if ((later) >= 2) WAIT_VM_LDS(2 * LPT);                                                    \
+    else if ((later) == 1) WAIT_VM_LDS(LPT);                                                   \
+    else WAIT_VM_LDS(0);                                                                       \
+  }
+  static_assert(WST - 2 <= 2 && WST >= 3, "ring depth");
+
+  // prologue: steps 0 .. WST-2 in flight, step 0 published, its first slice in registers
+  for (int st = 0; st < WST - 1 && st < nk; ++st) issue(st);
+  if (nk > 0) {
+    WAIT_STEPS(min(WST - 2, nk - 1));
+    __builtin_amdgcn_s_barrier();
+    FRAGS(f0a, f0b, 0, 0)
+  }
+  SB();
+  for (int kt = 0; kt < nk; ++kt) {
+    // invariant: f0 holds slice 0 of step kt; step kt is published; every wave has finished
+    // reading step kt - 1
+    const bool more = kt + 1 < nk;
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+      if ((h & 1) == 0) {
+        MFMA_ROWS(f0a, f0b, 0, 1)
+        SB();
+        if (h + 1 < NH) FRAGS(f1a, f1b, kt, h + 1)
+        SB();
+        if (h == NH - 2 && more) {
+          // publish step kt + 1 (issued WST - 2 steps ago) for every wave; the barrier also
+          // tells that every wave is past its reads of step kt - 1, whose stage is reused next
+          WAIT_STEPS(min(WST - 3, nk - 2 - kt));
+          __builtin_amdgcn_s_barrier();
+          if (kt + WST - 1 < nk) issue(kt + WST - 1);
+        }
+        SB();
+        MFMA_ROWS(f0a, f0b, 1, TM)
+        SB();
+      } else {
+        MFMA_ROWS(f1a, f1b, 0, 1)
+        SB();
+        if (h + 1 < NH) {
+          FRAGS(f0a, f0b, kt, h + 1)
+        } else if (more) {
+          FRAGS(f0a, f0b, kt + 1, 0)
+        }
+        SB();
+        MFMA_ROWS(f1a, f1b, 1, TM)
+        SB();
+      }
+    }
+  }
+#undef FRAGS
+#undef MFMA_ROWS
+#undef SB
+#undef WAIT_STEPS
+  WAIT_VM_LDS(0);
+  __syncthreads();  // every wave is done with the operand buffers
+  wide_epilogue<BM, EK, SPLIT, TM, TN>(g, acc, smem_raw, m0, n0, wm0, wn0, tid, bz, split);
+}
+
+template <int BM, int EK, bool SPLIT>
+hipError_t launch_wide(const GemmArgs& g, int S, hipStream_t s) {
+  auto kern = k_gemm_wide<BM, EK, SPLIT>;
+  constexpr size_t shm = wide_lds_bytes<BM, EK>();
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int64_t tiles = (int64_t)(g.M / BM) * (g.N / 256) * g.batch * S;
+  hipLaunchKernelGGL(kern, dim3((unsigned)(8 * cdiv(tiles, 8))), dim3(512), shm, s, g);
+  return hipGetLastError();
+}
+
+template <int EK>
+hipError_t launch_wide_bm(const GemmArgs& g, int bm, hipStream_t s) {
+  return bm == 256 ? launch_wide<256, EK, false>(g, 1, s) : launch_wide<128, EK, false>(g, 1, s);
+}
+
 template <int EK, bool SPLIT, int STAGES>
 hipError_t launch_dl_st(const GemmArgs& g, int S, hipStream_t s) {
   auto kern = k_gemm_dl<EK, STAGES, SPLIT>;
@@ -475,11 +777,14 @@ __global__ void k_splitk_reduce(GemmArgs g, int S) {
   }
 }
 
-hipError_t launch_splitk(const GemmArgs& g0, int S, int Ks, hipStream_t s) {
+hipError_t launch_splitk(const GemmArgs& g0, int S, int Ks, bool wide, hipStream_t s) {
   GemmArgs g = g0;
   g.e.ldt = S;   // carried to the kernel
   g.e.st = Ks;
-  if (dl_ok(g, Ks)) {
+  if (wide) {
+    hipError_t e = launch_wide<128, EPI_F32, true>(g, S, s);
+    if (e != hipSuccess) return e;
+  } else if (dl_ok(g, Ks)) {
     hipError_t e = launch_dl<EPI_F32, true>(g, S, s);
     if (e != hipSuccess) return e;
   } else {
@@ -509,19 +814,81 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
 }  // namespace
 
-// split-K parts for this GEMM (1: no split); see gemm_mfma_bf16
-int gemm_mfma_splits(const GemmArgs& g, int* ks_out) {
+namespace {
+
+// Which main loop runs a GEMM, with how many K parts.
+//   kern 3 / 2: wide tiles with BM = 256 / 128; 1: 128 x 128 direct-to-LDS; 0: 128 x 128
+//   register-staged (any shape).
+// Small grids with a long K (the N = d GEMMs of the per-chunk upper blocks) split K over
+// several blocks into an fp32 workspace; one pass then sums the parts in a fixed order and
+// applies the epilogue.
+struct GemmPlan {
+  int kern, S, Ks;
+};
+
+bool al(const void* p, int bytes) { return ((uintptr_t)p % bytes) == 0; }
+
+bool wide_ok(const GemmArgs& g) {
+  static int off = -1;
+  if (off < 0) {
+    const char* e = getenv("TTT_GEMM_NO_WIDE");
+    off = e && e[0] == '1';
+  }
+  if (off) return false;
+  if (!(g.M % 128 == 0 && g.N % 256 == 0 && g.K % 64 == 0 && g.lda % 8 == 0 && g.ldb % 8 == 0)) return false;
+  // the epilogues store 4-element row segments (and 8-element transposed segments)
+  const Epi& e = g.e;
+  switch (e.kind) {
+    case EPI_F32:
+    case EPI_ADD_F32: return e.ldc % 4 == 0 && e.sc % 4 == 0 && al(e.c, 16);
+    case EPI_T: return e.ldc % 4 == 0 && e.sc % 4 == 0 && al(e.c, 8);
+    case EPI_SWIGLU_IL:
+      return e.ldc % 4 == 0 && e.sc % 4 == 0 && al(e.c, 8) &&
+             (!e.zg || (e.ldz % 4 == 0 && e.sz % 4 == 0 && al(e.zg, 8) && al(e.zu, 8))) &&
+             (!e.t || (e.ldt % 8 == 0 && e.st % 8 == 0 && al(e.t, 16)));
+    case EPI_SGD:
+      return e.ldm % 4 == 0 && e.sm % 4 == 0 && al(e.master, 16) && e.ldsh % 4 == 0 && e.ssh % 4 == 0 &&
+             al(e.sh, 8) && e.ldshT % 8 == 0 && e.sshT % 8 == 0 && al(e.shT, 16);
+    default: return false;
+  }
+}
+
+GemmPlan gemm_plan(const GemmArgs& g) {
+  const bool splittable = g.e.kind == EPI_F32 || g.e.kind == EPI_T || g.e.kind == EPI_ADD_F32;
+  if (wide_ok(g)) {
+    const int64_t t128 = (int64_t)(g.M / 128) * (g.N / 256) * g.batch;
+    const int64_t t256 = g.M % 256 == 0 ? (int64_t)(g.M / 256) * (g.N / 256) * g.batch : 0;
+    if (g.ws && splittable && t128 < 192 && g.K >= 1024 && al(g.ws, 16)) {
+      int S = (int)std::min<int64_t>(8, std::max<int64_t>(2, 256 / t128));
+      S = std::min(S, g.K / 256);
+      const int Ks = (int)cdiv(cdiv(g.K, S), 64) * 64;
+      S = (int)cdiv(g.K, Ks);
+      if (S >= 2 && (int64_t)S * g.batch * g.M * g.N <= g.ws_floats) return {2, S, Ks};
+    }
+    // one block per CU: rounds of 256 tiles; a 128-row tile costs a little over half a 256-row one
+    const double c256 = t256 ? (double)cdiv(t256, 256) : 1e30;
+    const double c128 = 0.55 * (double)cdiv(t128, 256);
+    return {c256 <= c128 ? 3 : 2, 1, g.K};
+  }
   const int64_t tiles = (int64_t)cdiv(g.M, 128) * cdiv(g.N, 128) * g.batch;
-  if (!(g.ws && tiles < 384 && g.K >= 1024 &&
-        (g.e.kind == EPI_F32 || g.e.kind == EPI_T || g.e.kind == EPI_ADD_F32)))
-    return 1;
-  int S = (int)std::min<int64_t>(8, (640 + tiles - 1) / tiles);
-  S = std::min(S, g.K / 256);
-  const int Ks = (int)cdiv(cdiv(g.K, S), BK) * BK;
-  S = (int)cdiv(g.K, Ks);
-  if (S < 2 || (int64_t)S * g.batch * g.M * g.N > g.ws_floats) return 1;
-  if (ks_out) *ks_out = Ks;
-  return S;
+  if (g.ws && tiles < 384 && g.K >= 1024 && splittable) {
+    int S = (int)std::min<int64_t>(8, (640 + tiles - 1) / tiles);
+    S = std::min(S, g.K / 256);
+    const int Ks = (int)cdiv(cdiv(g.K, S), BK) * BK;
+    S = (int)cdiv(g.K, Ks);
+    if (S >= 2 && (int64_t)S * g.batch * g.M * g.N <= g.ws_floats) return {dl_ok(g, Ks) ? 1 : 0, S, Ks};
+  }
+  return {dl_ok(g, g.K) ? 1 : 0, 1, g.K};
+}
+
+}  // namespace
+
+// split-K parts for this GEMM (1: no split)
+int gemm_mfma_splits(const GemmArgs& g, int* ks_out) {
+  if (g.M <= 0 || g.N <= 0 || g.batch <= 0) return 1;
+  const GemmPlan p = gemm_plan(g);
+  if (ks_out) *ks_out = p.Ks;
+  return p.S;
 }
 
 hipError_t gemm_mfma_bf16(const GemmArgs& g, hipStream_t s) {
@@ -531,13 +898,20 @@ hipError_t gemm_mfma_bf16(const GemmArgs& g, hipStream_t s) {
             g.sB % 8 == 0 && (g.dual_off * g.ldb) % 8 == 0 && g.K >= 1;
   if (!ok) return g.e.kind == EPI_SWIGLU_IL ? hipErrorInvalidValue : gemm_simt_bf16(g, s);
   if (g.e.kind == EPI_SWIGLU_IL && (g.N % 64 != 0)) return hipErrorInvalidValue;
-  // Small grids with a long K (the N = d GEMMs of the per-chunk upper blocks) split K
-  // over several blocks into an fp32 workspace, then one pass sums the parts in a
-  // fixed order and applies the epilogue.
-  int Ks = 0;
-  const int S = gemm_mfma_splits(g, &Ks);
-  if (S > 1) return launch_splitk(g, S, Ks, s);
-  if (dl_ok(g, g.K)) {
+  const GemmPlan p = gemm_plan(g);
+  if (p.S > 1) return launch_splitk(g, p.S, p.Ks, p.kern >= 2, s);
+  if (p.kern >= 2) {
+    const int bm = p.kern == 3 ? 256 : 128;
+    switch (g.e.kind) {
+      case EPI_SWIGLU_IL: return launch_wide_bm<EPI_SWIGLU_IL>(g, bm, s);
+      case EPI_F32: return launch_wide_bm<EPI_F32>(g, bm, s);
+      case EPI_T: return launch_wide_bm<EPI_T>(g, bm, s);
+      case EPI_ADD_F32: return launch_wide_bm<EPI_ADD_F32>(g, bm, s);
+      case EPI_SGD: return launch_wide_bm<EPI_SGD>(g, bm, s);
+      default: break;
+    }
+  }
+  if (p.kern == 1) {
     switch (g.e.kind) {
       case EPI_SWIGLU_IL: return launch_dl<EPI_SWIGLU_IL, false>(g, 1, s);
       case EPI_F32: return launch_dl<EPI_F32, false>(g, 1, s);

@@ -26,3 +26,9 @@ M760_T = 32768
 M3B = dict(n_layers=32, d_model=2560, n_heads=20, d_ff=6912, vocab=32000, window=8192, chunk=1024, n_fast=8,
            batch=1, rope_theta=1e7, rms_eps=1e-5, lr=1e-3, dtype="bf16")
 M3B_T = 131072
+
+# matrix-core tile coverage: every GEMM of the engine meets the wide-tile shape rules
+# (rows % 128, columns % 256, K % 64), and the per-chunk N = d GEMMs with K >= 1024 split K
+MID = dict(n_layers=4, d_model=256, n_heads=2, d_ff=1024, vocab=1024, window=256, chunk=128, n_fast=2, batch=1,
+           rope_theta=1e4, rms_eps=1e-5, lr=1e-2, dtype="bf16")
+MID_T = 680

@@ -19,7 +19,9 @@ def _torch():
 
 
 GEMM_SHAPES = [(128, 128, 64), (300, 200, 72), (1, 512, 128), (1000, 384, 40), (257, 129, 1000), (64, 96, 8),
-               (1024, 2560, 256), (1000, 384, 4100), (256, 640, 2056)]
+               (1024, 2560, 256), (1000, 384, 4100), (256, 640, 2056),
+               # wide tiles: 128-row (small grid), 128-row split K, 256-row (large grid)
+               (512, 512, 256), (512, 1024, 2048), (4096, 4096, 256)]
 
 
 def _workspace(torch, use):

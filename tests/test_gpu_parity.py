@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 
 from oracle import Oracle
-from tests.cfgs import TOY, cfg as mkcfg
+from tests.cfgs import MID, MID_T, TOY, cfg as mkcfg
 from test_token_chunk_amd import synth
 
 pytestmark = pytest.mark.gpu
@@ -75,6 +75,21 @@ def test_toy_full_sequence_parity(dtype):
     print(f"toy {dtype}: max loss rel err {rel:.3e}")
     assert rel <= tl
     compare_fast(ctx.fast_weights(0), o.get_fast(0), _w0(w, c), tw, f"toy {dtype}")
+
+
+@pytest.mark.parametrize("lookahead", [1, 4])
+def test_mid_matrix_core_tiles_parity(lookahead):
+    """d=256, f=1024, V=1024, b=128: every GEMM of the bf16 path takes the wide-tile
+    matrix-core loop (residual-add, SwiGLU, fused-SGD and transposed epilogues, and the
+    split-K sum of the per-chunk N = d products); 6 chunks, the last one ragged."""
+    c = mkcfg(**MID)
+    print(f"case mid lookahead {lookahead}", flush=True)
+    w, o, ctx, ref, got = run_pair(c, MID_T, dist="zipf", lookahead=lookahead)
+    tl, tw = TOL["bf16"]
+    rel = np.max(np.abs(got - ref) / np.abs(ref))
+    print(f"mid: max loss rel err {rel:.3e}")
+    assert rel <= tl
+    compare_fast(ctx.fast_weights(0), o.get_fast(0), _w0(w, c), tw, "mid")
 
 
 def test_toy_more_fast_blocks_and_ragged_tail():
