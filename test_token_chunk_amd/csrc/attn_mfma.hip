@@ -733,20 +733,27 @@ __global__ void k_dq_reduce(const float* ws, int S, int64_t total, float* dq) {
   }
 }
 
-// dO [B*n][H*hd] -> dO^T [B][H][hd][n], 64 x 64 tiles through LDS
+// dO [B*n][H*hd] -> dO^T [B][H][hd][n], 64 x 64 tiles through LDS with 16-byte global
+// loads and stores (H*hd % 8 == 0 and n % 8 == 0)
 __global__ __launch_bounds__(256) void k_heads_transpose(const bf16* __restrict__ x, bf16* __restrict__ xt, int n,
                                                          int H, int hd) {
-  __shared__ uint16_t tile[64][66];
+  __shared__ __align__(16) uint16_t tile[64][72];  // [token][column]
   const int d = H * hd, t0 = blockIdx.x * 64, c0 = blockIdx.y * 64, b = blockIdx.z;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int r = ty; r < 64; r += 4) {
-    const int t = t0 + r, c = c0 + tx;
-    tile[r][tx] = (t < n && c < d) ? x[((int64_t)b * n + t) * d + c].x : (uint16_t)0;
+  for (int e = threadIdx.x; e < 64 * 8; e += 256) {
+    const int r = e >> 3, ch = (e & 7) * 8, t = t0 + r, c = c0 + ch;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (t < n && c < d) v = *(const uint4*)(x + ((int64_t)b * n + t) * d + c);
+    *(uint4*)&tile[r][ch] = v;
   }
   __syncthreads();
-  for (int r = ty; r < 64; r += 4) {
-    const int c = c0 + r, t = t0 + tx;
-    if (c < d && t < n) xt[((int64_t)b * d + c) * n + t].x = tile[tx][r];
+  for (int e = threadIdx.x; e < 64 * 8; e += 256) {
+    const int cr = e >> 3, tch = (e & 7) * 8, c = c0 + cr, t = t0 + tch;
+    if (c < d && t < n) {
+      uint32_t w[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) w[k] = (uint32_t)tile[tch + 2 * k][cr] | ((uint32_t)tile[tch + 2 * k + 1][cr] << 16);
+      *(uint4*)(xt + ((int64_t)b * d + c) * n + t) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
   }
 }
 
@@ -783,7 +790,7 @@ hipError_t launch_bwd(const AttnBwdArgs& a, hipStream_t s) {
   // transposed tiles are read with 16-byte copies when the caller provides the
   // transposed key ring and a dO^T scratch, 8-key groups stay inside the ring
   // (R % 8 == 0) and 8-query groups inside the chunk (n % 8 == 0)
-  const bool tr = a.ktr && a.dot && a.R % 8 == 0 && a.n % 8 == 0;
+  const bool tr = a.ktr && a.dot && a.R % 8 == 0 && a.n % 8 == 0 && (a.H * HD) % 8 == 0;
   if (tr)
     hipLaunchKernelGGL(k_heads_transpose, dim3(cdiv(a.n, 64), cdiv(a.H * HD, 64), a.B), dim3(256), 0, s,
                        (const bf16*)a.dout, (bf16*)a.dot, a.n, a.H, HD);

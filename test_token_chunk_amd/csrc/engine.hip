@@ -70,6 +70,7 @@ struct ttt_ctx {
   bool bf16;
   size_t es;  // element size of T
   bool mfma = true;
+  bool overlap = true;  // weight-gradient GEMMs on the side stream (TTT_NO_SIDE=1: on the main stream)
   bool il = false;  // gate/up rows interleaved for the single-operand SwiGLU GEMM (bf16 matrix-core path)
   hipStream_t stream = nullptr;
   // second stream for the fused-SGD weight-gradient GEMMs, which only the next chunk depends on
@@ -461,8 +462,11 @@ int top_chunk(ttt_ctx* c, const int32_t* tgt, int64_t ld, const float* hsrc, int
     // overlapping the rest of the backward: their inputs (dy^T, dz^T of this block, act^T,
     // m^T) stay untouched until the next chunk, and the GEMMs above that read the old
     // W_down^T and W_gu^T have been enqueued before them.
-    CK(hipEventRecord(c->ev_m2s, c->stream));
-    CK(hipStreamWaitEvent(c->side, c->ev_m2s, 0));
+    hipStream_t sg = c->overlap ? c->side : c->stream;
+    if (c->overlap) {
+      CK(hipEventRecord(c->ev_m2s, c->stream));
+      CK(hipStreamWaitEvent(c->side, c->ev_m2s, 0));
+    }
     // dW_down = dy^T act, fused SGD step on W_down
     GemmArgs g2 = mk(dyT, b, a.actT, b, d, f, n);
     g2.batch = B;
@@ -479,7 +483,7 @@ int top_chunk(ttt_ctx* c, const int32_t* tgt, int64_t ld, const float* hsrc, int
     g2.e.ldshT = d;
     g2.e.sshT = (int64_t)f * d;
     g2.e.lr = lr;
-    CK(Ops<T>::gemm(c, g2, c->side));
+    CK(Ops<T>::gemm(c, g2, sg));
     // [dW_gate; dW_up] = dz^T m, fused SGD step
     GemmArgs g4 = mk(dzT, b, a.mT, b, 2 * f, d, n);
     g4.batch = B;
@@ -497,7 +501,7 @@ int top_chunk(ttt_ctx* c, const int32_t* tgt, int64_t ld, const float* hsrc, int
     g4.e.sshT = 2LL * d * f;
     g4.e.lr = lr;
     g4.e.il_f = c->il ? f : 0;
-    CK(Ops<T>::gemm(c, g4, c->side));
+    CK(Ops<T>::gemm(c, g4, sg));
     if (j == 0) break;
     const LayerW& lw = c->lw[l];
     // through the MLP norm and the residual: dh <- d h_mid
@@ -540,8 +544,10 @@ int top_chunk(ttt_ctx* c, const int32_t* tgt, int64_t ld, const float* hsrc, int
     CK(rmsnorm_bwd<T>(a.h_in, a.rstd1, M, d, lw.attn_norm, c->tmpf, c->dh, c->dh, (T*)nullptr, c->stream));
   }
   // the next chunk reads the updated fast weights and rewrites the saved activations
-  CK(hipEventRecord(c->ev_s2m, c->side));
-  CK(hipStreamWaitEvent(c->stream, c->ev_s2m, 0));
+  if (c->overlap) {
+    CK(hipEventRecord(c->ev_s2m, c->side));
+    CK(hipStreamWaitEvent(c->stream, c->ev_s2m, 0));
+  }
   return TTT_OK;
 }
 
@@ -928,6 +934,8 @@ int ttt_create(const ttt_config* cfg, const ttt_weights* w, void* hip_stream, tt
   c->free_user = g_user;
   const char* simt = getenv("TTT_SIMT");
   c->mfma = !(simt && simt[0] == '1');
+  const char* noside = getenv("TTT_NO_SIDE");
+  c->overlap = !(noside && noside[0] == '1');
   c->il = c->bf16 && c->mfma && c0.d_ff % 32 == 0 && c0.d_model % 8 == 0;
   if (hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking) != hipSuccess ||
       hipEventCreateWithFlags(&c->ev_m2s, hipEventDisableTiming) != hipSuccess ||
