@@ -83,6 +83,7 @@ def main():
     ap.add_argument("--config", default="3b", choices=sorted(CONFIGS))
     ap.add_argument("--tokens", type=int, default=0, help="override T (tokens per row)")
     ap.add_argument("--cpu-sample", type=int, default=32, help="oracle sample size in tokens (0 = skip)")
+    ap.add_argument("--lookahead", type=int, default=0, help="chunks per batched lower-block pass (0 = library default)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for {args.gpus}); the inner loop of one sequence is "
@@ -102,7 +103,7 @@ def main():
     w = synth.weights(synth.Shape(c["n_layers"], c["d_model"], c["n_heads"], c["d_ff"], c["vocab"]),
                       bf16=c["dtype"] == "bf16")
     seq = synth.tokens(1, T + 1, c["vocab"], dist)
-    cfg = TTTConfig(batch=1, max_positions=T + 8, **c)
+    cfg = TTTConfig(batch=1, max_positions=T + 8, lookahead=args.lookahead, **c)
     ctx = TTTContext(cfg, w)
     d_tok = torch.tensor(seq[:, :T], dtype=torch.int32, device="cuda")
     d_tgt = torch.tensor(seq[:, 1:], dtype=torch.int32, device="cuda")

@@ -63,7 +63,8 @@ typedef struct {
   int32_t batch;      /* B independent rows */
   int32_t dtype;      /* TTT_F32: fp32 everywhere; TTT_BF16: bf16 weights/activations, fp32 accumulate,
                          fp32 residual stream and fp32 master copy of the fast weights */
-  int32_t lookahead;  /* chunks whose frozen lower blocks run as one batch (0 = default) */
+  int32_t lookahead;  /* chunks whose frozen lower blocks run as one batch (0 = default: 32, at most
+                         ceil(max_positions / chunk)); costs (window + lookahead * chunk) ring slots */
   int32_t reserved_;
   int64_t max_positions; /* largest absolute position + 1 that will be processed (RoPE table size) */
   double rope_theta;  /* RoPE base; rotate-half pairing (i, i + head_dim/2) */

@@ -878,7 +878,12 @@ int ttt_create(const ttt_config* cfg, const ttt_weights* w, void* hip_stream, tt
   *out = nullptr;
   ttt_config c0 = *cfg;
   if (c0.n_fast == 0) c0.n_fast = std::max(1, c0.n_layers / 4);
-  if (c0.lookahead <= 0) c0.lookahead = 8;
+  // default: 32 chunks per batched lower-block pass (large GEMM and attention grids fill the
+  // 256 CUs in whole rounds), no more than the positions the context will see
+  if (c0.lookahead <= 0 && c0.chunk > 0) {
+    const int64_t need = c0.max_positions > 0 ? (c0.max_positions + c0.chunk - 1) / c0.chunk : 32;
+    c0.lookahead = (int32_t)std::max<int64_t>(1, std::min<int64_t>(32, need));
+  }
   auto bad = [&](const char* m) {
     g_create_err = m;
     return TTT_EINVAL;
