@@ -42,7 +42,7 @@ __device__ __forceinline__ uint32_t pk2(float a, float b) {
 }
 
 // SPLIT: blockIdx.z = b * S + split; the block covers only its share of the key tiles
-// and writes unnormalized O, the running max (raw score units) and the exp-sum to the
+// and writes unnormalized O, the reference max (raw score units) and the exp-sum to the
 // workspace: O [S][B][H][n][hd], m [S][B][H][n], l [S][B][H][n].
 template <int HD, int NW, bool SPLIT = false>
 __global__ __launch_bounds__(NW * 64) void k_swa_fwd(AttnArgs a, int S) {
@@ -141,8 +141,9 @@ __global__ __launch_bounds__(NW * 64) void k_swa_fwd(AttnArgs a, int S) {
   f32x16 o[HM];
 #pragma unroll
   for (int i = 0; i < HM; ++i) o[i] = f32x16{};
-  float mrun = -INFINITY, lrun = 0.f;
+  float mref = -INFINITY, lrun = 0.f;  // reference max (log2 units), this lane's row sum
   const float sl2 = 1.4426950408889634f / sqrtf((float)HD);  // log2(e) / sqrt(hd)
+  const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
 
   if (it_beg < ntiles) {
     LOAD_TILE(it_beg)
@@ -174,8 +175,8 @@ __global__ __launch_bounds__(NW * 64) void k_swa_fwd(AttnArgs a, int S) {
     const bool full = wfull && kp0 >= wpos_hi - a.window + 1 && kp0 + KT - 1 <= wpos_lo;
     if (!full) {
       const int64_t hi64 = qpos - kp0, lo64 = qpos - a.window - kp0;
-      const int hi = qok ? (int)min<int64_t>(max<int64_t>(hi64, -1), 64) : -1;
-      const int lo = (int)min<int64_t>(max<int64_t>(lo64, -2), 64);
+      const int hi = !qok ? -1 : hi64 < -1 ? -1 : hi64 > 64 ? 64 : (int)hi64;
+      const int lo = lo64 < -2 ? -2 : lo64 > 64 ? 64 : (int)lo64;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int off = 8 * (r >> 2) + 4 * g + (r & 3);
@@ -183,30 +184,34 @@ __global__ __launch_bounds__(NW * 64) void k_swa_fwd(AttnArgs a, int S) {
         if (!(off + 32 <= hi && off + 32 > lo)) s1[r] = -INFINITY;
       }
     }
+    // lazy reference max (log2 units): it moves only when the tile's max passes it by more
+    // than 8, so exponentials stay <= 2^8 and O is rarely rescaled (the result does not
+    // depend on the reference); the pair of lanes of a query shares it
     float tmax = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, fmaxf(s0[r], s1[r]));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    const float mnew = fmaxf(mrun, tmax);  // raw score units
-    const float nb = mnew == -INFINITY ? 0.f : -mnew * sl2;
-    const float corr = exp2f(fmaf(mrun, sl2, nb));
+    float corr = 1.f;
+    if (__any(tmax * sl2 > mref + 8.f)) {
+      const float pmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * sl2;
+      const float mnew = pmax > mref + 8.f ? pmax : mref;
+      corr = mnew == mref ? 1.f : exp2f(mref - mnew);
+      mref = mnew;
+#pragma unroll
+      for (int i = 0; i < HM; ++i) o[i] *= corr;
+    }
+    const float nb = mref == -INFINITY ? 0.f : -mref;
+    // row sums: dot products of the bf16 probabilities that feed the PV product, per lane
+    // (the pair's sums are added at the end)
     float psum = 0.f;
     uint32_t pa[8], pb[8];
 #pragma unroll
     for (int r = 0; r < 16; r += 2) {
-      float p0 = exp2f(fmaf(s0[r], sl2, nb)), p1 = exp2f(fmaf(s0[r + 1], sl2, nb));
-      float q0 = exp2f(fmaf(s1[r], sl2, nb)), q1 = exp2f(fmaf(s1[r + 1], sl2, nb));
-      psum += (p0 + p1) + (q0 + q1);
-      pa[r >> 1] = pk2(p0, p1);
-      pb[r >> 1] = pk2(q0, q1);
+      pa[r >> 1] = pk2(exp2f(fmaf(s0[r], sl2, nb)), exp2f(fmaf(s0[r + 1], sl2, nb)));
+      pb[r >> 1] = pk2(exp2f(fmaf(s1[r], sl2, nb)), exp2f(fmaf(s1[r + 1], sl2, nb)));
+      psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pa[r >> 1]), ones, psum, false);
+      psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pb[r >> 1]), ones, psum, false);
     }
-    psum += __shfl_xor(psum, 32, 64);
     lrun = lrun * corr + psum;
-    mrun = mnew;
-    if (__any(corr != 1.f)) {
-#pragma unroll
-      for (int i = 0; i < HM; ++i) o[i] *= corr;
-    }
     // O^T += V^T P^T, four 16-key steps (keys 0-15, 16-31 of each half)
     const bf16x8 pf[4] = {__builtin_bit_cast(bf16x8, make_uint4(pa[0], pa[1], pa[2], pa[3])),
                           __builtin_bit_cast(bf16x8, make_uint4(pa[4], pa[5], pa[6], pa[7])),
@@ -234,6 +239,7 @@ __global__ __launch_bounds__(NW * 64) void k_swa_fwd(AttnArgs a, int S) {
 #undef STK
 #undef STV
 #undef STORE_TILE
+  lrun += __shfl_xor(lrun, 32, 64);
   if (!qok) return;
   if constexpr (SPLIT) {
     const int64_t row = ((int64_t)sp * a.B * a.H + bh) * a.n + tq;  // [S][B][H][n]
@@ -248,7 +254,7 @@ __global__ __launch_bounds__(NW * 64) void k_swa_fwd(AttnArgs a, int S) {
         *(float4*)(po + d0) = make_float4(o[hm][4 * j], o[hm][4 * j + 1], o[hm][4 * j + 2], o[hm][4 * j + 3]);
       }
     if (g == 0) {
-      pm[row] = mrun;
+      pm[row] = mref == -INFINITY ? -INFINITY : mref / sl2;  // raw score units
       pl[row] = lrun;
     }
     return;
@@ -264,7 +270,7 @@ __global__ __launch_bounds__(NW * 64) void k_swa_fwd(AttnArgs a, int S) {
                            pk2(o[hm][4 * j + 2] * inv, o[hm][4 * j + 3] * inv));
       *(uint2*)(out + d0) = w;
     }
-  if (a.lse && g == 0) a.lse[bh * a.n + tq] = mrun * (sl2 * 0.6931471805599453f) + logf(lrun);
+  if (a.lse && g == 0) a.lse[bh * a.n + tq] = (mref + log2f(lrun)) * 0.6931471805599453f;
 }
 
 // merge the key-range parts of a split forward: O = sum_s w_s O_s / sum_s w_s l_s with
@@ -317,12 +323,21 @@ int attn_splits(int64_t blocks, int64_t ntiles, int64_t need_per_split, const fl
   return S;
 }
 
+// key-range parts of the forward: grids of fewer than 128 blocks (one 8-wave block per CU)
+// split the key range so that about one round of blocks covers the chip (needs the workspace)
+int fwd_splits(const AttnArgs& a) {
+  const int64_t blocks = (int64_t)cdiv(a.n, 8 * QW) * a.H * a.B;
+  if (!a.ws || blocks >= 128) return 1;
+  const int64_t ntiles = (std::min<int64_t>(a.window, a.pos0 + 1) + 8 * QW) / KT + 1;
+  int S = (int)std::min<int64_t>(8, 256 / blocks);
+  S = (int)std::min<int64_t>(S, std::max<int64_t>(1, ntiles / 8));
+  while (S > 1 && S * (int64_t)a.B * a.H * a.n * (a.hd + 2) > a.ws_floats) --S;
+  return std::max(S, 1);
+}
+
 template <int HD>
 hipError_t launch_fwd(const AttnArgs& a, hipStream_t s) {
-  const int64_t blocks8 = (int64_t)cdiv(a.n, 8 * QW) * a.H * a.B;
-  if (blocks8 >= 512) return launch_fwd_nw<HD, 8, false>(a, 1, s);
-  const int64_t ntiles = (std::min<int64_t>(a.window, a.pos0 + 1) + 8 * QW) / KT + 1;
-  const int S = attn_splits(blocks8, ntiles, (int64_t)a.B * a.H * a.n * (HD + 2), a.ws, a.ws_floats);
+  const int S = fwd_splits(a);
   if (S > 1) return launch_fwd_nw<HD, 8, true>(a, S, s);
   return launch_fwd_nw<HD, 8, false>(a, 1, s);
 }
@@ -457,8 +472,8 @@ __global__ __launch_bounds__(NW * 64) void k_swa_dq(AttnBwdArgs a, int S) {
     // masked keys get score -inf (p = 0); only tiles that cut a window edge need it
     const bool full = wfull && kp0 >= wpos_hi - a.window + 1 && kp0 + KT - 1 <= wpos_lo;
     const int64_t hi64 = qpos - kp0, lo64 = qpos - a.window - kp0;
-    const int hi = qok ? (int)min<int64_t>(max<int64_t>(hi64, -1), 64) : -1;
-    const int lo = (int)min<int64_t>(max<int64_t>(lo64, -2), 64);
+    const int hi = !qok ? -1 : hi64 < -1 ? -1 : hi64 > 64 ? 64 : (int)hi64;
+    const int lo = lo64 < -2 ? -2 : lo64 > 64 ? 64 : (int)lo64;
     // the 64-key tile in two halves of 32 keys (keeps the score registers to one half)
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
@@ -828,10 +843,7 @@ hipError_t launch_bwd(const AttnBwdArgs& a, hipStream_t s) {
 // key-range parts the forward would use for this call (1: single kernel)
 int swa_fwd_mfma_splits(const AttnArgs& a) {
   if (a.n == 0 || a.R % 8 != 0 || (a.hd != 32 && a.hd != 64 && a.hd != 96 && a.hd != 128)) return 1;
-  const int64_t blocks8 = (int64_t)cdiv(a.n, 8 * QW) * a.H * a.B;
-  if (blocks8 >= 512) return 1;
-  const int64_t ntiles = (std::min<int64_t>(a.window, a.pos0 + 1) + 8 * QW) / KT + 1;
-  return attn_splits(blocks8, ntiles, (int64_t)a.B * a.H * a.n * (a.hd + 2), a.ws, a.ws_floats);
+  return fwd_splits(a);
 }
 
 hipError_t swa_fwd_mfma(const AttnArgs& a, hipStream_t s) {

@@ -83,3 +83,10 @@ __device__ __forceinline__ float block_max(float v, float* sh) {
 }
 
 static inline unsigned cdiv(int64_t a, int64_t b) { return (unsigned)((a + b - 1) / b); }
+
+// LDS pointer for global_load_lds (lane L of a wave writes 16 bytes at the wave's LDS
+// address + 16 L)
+#define LDSP(p) ((void __attribute__((address_space(3)))*)(p))
+// wait until at most n vector-memory operations are outstanding and all LDS operations are
+// done (gfx9 s_waitcnt: vmcnt in bits 15:14 and 3:0, expcnt 6:4, lgkmcnt 11:8)
+#define WAIT_VM_LDS(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4))

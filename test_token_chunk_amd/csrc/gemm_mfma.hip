@@ -333,10 +333,6 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(GemmArgs g) {
 // STAGES-1 K steps ahead without staging registers.  LDS rows are 128 bytes with the
 // 16-byte chunks XOR-swizzled by (row & 7), which keeps the operand reads of a wave on
 // distinct banks.  Requires M, N multiples of 128 and a K range that is a multiple of 64.
-#define LDSP(p) ((void __attribute__((address_space(3)))*)(p))
-// wait until at most n vector-memory operations are outstanding and all LDS operations are
-// done (gfx9 s_waitcnt: vmcnt in bits 15:14 and 3:0, expcnt 6:4, lgkmcnt 11:8)
-#define WAIT_VM_LDS(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4))
 
 constexpr int DL_TILE_BYTES = (128 + 128) * BK * 2;  // one stage: A and B tiles
 
