@@ -28,17 +28,18 @@ EXPORTS = ("ttt_set_allocator", "ttt_create", "ttt_prefill_chunk", "ttt_prefill"
 PROFILE_CLASSES = ("gemm_f32out", "gemm_bf16out", "gemm_resid", "gemm_swiglu", "gemm_swiglu_bwd", "gemm_sgd",
                    "gemm_splitk", "swa_fwd", "swa_fwd_split", "swa_bwd")
 # kernels behind each class (rocprofv3 names); classes marked single=True are one kernel
-PROFILE_KERNELS = {
-    "gemm_f32out": ("k_gemm_mfma<128, 128, 64, 64, false, 0, false>", True),
-    "gemm_bf16out": ("k_gemm_mfma<128, 128, 64, 64, false, 1, false>", True),
-    "gemm_resid": ("k_gemm_mfma<128, 128, 64, 64, false, 2, false>", True),
-    "gemm_swiglu": ("k_gemm_mfma<128, 128, 64, 64, false, 7, false>", True),
-    "gemm_swiglu_bwd": ("k_gemm_mfma<128, 128, 64, 64, false, 4, false>", True),
-    "gemm_sgd": ("k_gemm_mfma<128, 128, 64, 64, false, 5, false>", True),
-    "gemm_splitk": ("k_gemm_mfma<128, 128, 64, 64, false, 0, true> + k_splitk_reduce<*>", False),
+PROFILE_KERNELS = {  # class: (kernels, one kernel per launch)
+    "gemm_f32out": ("k_gemm_wide<256|128, 0, false> (k_gemm_dl / k_gemm_mfma off the wide-tile shapes)", False),
+    "gemm_bf16out": ("k_gemm_wide<256|128, 1, false> (k_gemm_dl / k_gemm_mfma off the wide-tile shapes)", False),
+    "gemm_resid": ("k_gemm_wide<256|128, 2, false> (k_gemm_mfma off the wide-tile shapes)", False),
+    "gemm_swiglu": ("k_gemm_wide<256|128, 7, false> (k_gemm_dl / k_gemm_mfma off the wide-tile shapes)", False),
+    "gemm_swiglu_bwd": ("k_gemm_dl<4, 2, false> (k_gemm_mfma off the 128-aligned shapes)", False),
+    "gemm_sgd": ("k_gemm_wide<256|128, 5, false> on the side stream (overlapped)", False),
+    "gemm_splitk": ("k_gemm_wide<128, 0, true> + k_splitk_reduce<*>", False),
     "swa_fwd": ("k_swa_fwd<hd, 8, false>", True),
     "swa_fwd_split": ("k_swa_fwd<hd, 8, true> + k_swa_combine", False),
-    "swa_bwd": ("k_dvec + k_swa_dq<hd, 8, *> (+ k_dq_reduce) + k_swa_dkv<hd>", False),
+    "swa_bwd": ("k_dvec + k_heads_transpose + k_swa_dq<hd, 8, *> (+ k_dq_reduce) + k_swa_dkv<hd, *> "
+                "(+ k_dkv_reduce)", False),
 }
 
 
