@@ -84,7 +84,18 @@ def main():
     ap.add_argument("--tokens", type=int, default=0, help="override T (tokens per row)")
     ap.add_argument("--cpu-sample", type=int, default=32, help="oracle sample size in tokens (0 = skip)")
     ap.add_argument("--lookahead", type=int, default=0, help="chunks per batched lower-block pass (0 = library default)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 1 GiB device-to-device copy 3 times (reference for HBM byte counters)")
     args = ap.parse_args()
+    if args.copy_calibration:
+        import torch
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": src.numel() * 4, "copy_bytes_written": dst.numel() * 4, "copies": 3}))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for {args.gpus}); the inner loop of one sequence is "
               "sequential over chunks and this build runs on a single MI355X.", file=sys.stderr)
