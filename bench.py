@@ -75,6 +75,23 @@ def cpu_baseline(c: dict, w: dict, seq: np.ndarray, sample_tokens: int) -> dict:
                       f"fp64, {dt:.1f} s"}
 
 
+def measured_traffic(kernel: str, config: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary, or None when
+    there is none for this kernel and workload or the kernel's source changed since it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "k_swa_fwd_3b_hbm_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = dict(line.split(": ", 1) for line in open(path).read().splitlines()
+              if ": " in line and not line.startswith("#"))
+    src = os.path.join(ROOT, kv.get("source", "-"))
+    if kv.get("kernel") != kernel or kv.get("config") != config or not os.path.exists(src):
+        return None
+    if hashlib.sha256(open(src, "rb").read()).hexdigest() != kv.get("source_sha256"):
+        return None
+    return float(kv["traffic_bytes_per_launch"])
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -158,8 +175,10 @@ def main():
         flops_per_launch = st["flops"] / max(st["count"], 1)
         avg_s = st["ms"] / max(st["count"], 1) / 1e3
         achieved = flops_per_launch / avg_s / 1e12
-        roof = {"kernel": PROFILE_KERNELS[name][0], "class": name, "bound": "mfma", "achieved": round(achieved, 1),
-                "peak": peak / 1e12, "unit": "TFLOP/s", "frac": round(achieved / (peak / 1e12), 4), "traffic": None,
+        kname = PROFILE_KERNELS[name][0].replace("hd", str(c["d_model"] // c["n_heads"]))
+        roof = {"kernel": kname, "class": name, "bound": "mfma", "achieved": round(achieved, 1),
+                "peak": peak / 1e12, "unit": "TFLOP/s", "frac": round(achieved / (peak / 1e12), 4),
+                "traffic": measured_traffic(kname, args.config),
                 "avg_launch_us": round(avg_s * 1e6, 2), "launches_per_step": st["count"] // args.steps,
                 "gflop_per_launch": round(flops_per_launch / 1e9, 3)}
     out = {
