@@ -446,8 +446,8 @@ struct WideCfg {
 template <int BM, int EK>
 constexpr size_t wide_lds_bytes() {
   const size_t ops = (size_t)WideCfg<BM>::ST * WideCfg<BM>::SBYTES;
-  const bool tr = EK == EPI_SGD || EK == EPI_SWIGLU_IL;
-  const size_t trb = tr ? (size_t)256 * (BM + 8) * 2 : 0;
+  const int ntr = EK == EPI_SWIGLU_BWD ? 2 : (EK == EPI_SGD || EK == EPI_SWIGLU_IL) ? 1 : 0;
+  const size_t trb = (size_t)ntr * 256 * (BM + 8) * 2;
   return ops > trb ? ops : trb;
 }
 
@@ -464,9 +464,10 @@ __device__ __forceinline__ void wide_epilogue(const GemmArgs& g, f32x16 (&acc)[T
   constexpr int BN = 256, NT = 512;
   const int lane = tid & 63, lr = lane & 31, hi = lane >> 5;
   const Epi& e = g.e;
-  constexpr bool TR = EK == EPI_SGD || EK == EPI_SWIGLU_IL;
+  constexpr bool TR = EK == EPI_SGD || EK == EPI_SWIGLU_IL || EK == EPI_SWIGLU_BWD;
   constexpr int TLD = BM + 8;
   bf16* tr0 = reinterpret_cast<bf16*>(smem_raw);  // [BN][TLD] (IL: [BN/2][TLD])
+  bf16* tr1 = tr0 + BN * TLD;                     // SwiGLU backward: dz_u^T
   auto pk4 = [](float a, float b, float c, float d) {
     return make_uint2((uint32_t)f2bf(a).x | ((uint32_t)f2bf(b).x << 16),
                       (uint32_t)f2bf(c).x | ((uint32_t)f2bf(d).x << 16));
@@ -497,6 +498,17 @@ __device__ __forceinline__ void wide_epilogue(const GemmArgs& g, f32x16 (&acc)[T
       // epilogues that read memory load the row group first (stores could alias the loads)
       constexpr bool READS = EK == EPI_SGD || EK == EPI_ADD_F32;
       float4 pre[READS ? TN * 4 : 1];
+      uint2 zgp[EK == EPI_SWIGLU_BWD ? TN * 4 : 1], zup[EK == EPI_SWIGLU_BWD ? TN * 4 : 1];
+      if constexpr (EK == EPI_SWIGLU_BWD) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int n = n0 + wn0 + j * 32 + 8 * q + 4 * hi;
+            zgp[j * 4 + q] = *(const uint2*)((const bf16*)e.zg + bz * e.sz + (int64_t)m * e.ldz + n);
+            zup[j * 4 + q] = *(const uint2*)((const bf16*)e.zu + bz * e.sz + (int64_t)m * e.ldz + n);
+          }
+      }
       if constexpr (READS) {
 #pragma unroll
         for (int j = 0; j < TN; ++j)
@@ -525,6 +537,26 @@ __device__ __forceinline__ void wide_epilogue(const GemmArgs& g, f32x16 (&acc)[T
             const float4 p = pre[j * 4 + q];
             *(float4*)((float*)e.c + bz * e.sc + (int64_t)m * e.ldc + n) =
                 make_float4(p.x + v0, p.y + v1, p.z + v2, p.w + v3);
+          } else if constexpr (EK == EPI_SWIGLU_BWD) {
+            // dz_g = dact * u * s(1 + g(1 - s)), dz_u = dact * g * s with s = sigmoid(g)
+            const uint2 zg2 = zgp[j * 4 + q], zu2 = zup[j * 4 + q];
+            const float zg[4] = {bf2f(bf16{(uint16_t)zg2.x}), bf2f(bf16{(uint16_t)(zg2.x >> 16)}),
+                                 bf2f(bf16{(uint16_t)zg2.y}), bf2f(bf16{(uint16_t)(zg2.y >> 16)})};
+            const float zu[4] = {bf2f(bf16{(uint16_t)zu2.x}), bf2f(bf16{(uint16_t)(zu2.x >> 16)}),
+                                 bf2f(bf16{(uint16_t)zu2.y}), bf2f(bf16{(uint16_t)(zu2.y >> 16)})};
+            const float x[4] = {v0, v1, v2, v3};
+            float dg[4], du[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const float sg = 1.f / (1.f + __expf(-zg[r]));
+              du[r] = x[r] * zg[r] * sg;
+              dg[r] = x[r] * zu[r] * sg * (1.f + zg[r] * (1.f - sg));
+              tr0[(nl + r) * TLD + ml] = f2bf(dg[r]);
+              tr1[(nl + r) * TLD + ml] = f2bf(du[r]);
+            }
+            bf16* crow = (bf16*)e.c + bz * e.sc + (int64_t)m * e.ldc;
+            *(uint2*)(crow + n) = pk4(dg[0], dg[1], dg[2], dg[3]);
+            *(uint2*)(crow + e.f + n) = pk4(du[0], du[1], du[2], du[3]);
           } else if constexpr (EK == EPI_SGD) {
             const float4 p = pre[j * 4 + q];
             const float w0 = p.x - e.lr * v0, w1 = p.y - e.lr * v1, w2 = p.z - e.lr * v2, w3 = p.w - e.lr * v3;
@@ -550,6 +582,8 @@ __device__ __forceinline__ void wide_epilogue(const GemmArgs& g, f32x16 (&acc)[T
     for (int c = tid; c < ROWS * CH; c += NT) {
       const int rl = c / CH, ml = (c % CH) * 8;
       *(uint4*)(dst + (int64_t)(row0 + rl) * ld + m0 + ml) = *(const uint4*)(tr0 + rl * TLD + ml);
+      if constexpr (EK == EPI_SWIGLU_BWD)
+        *(uint4*)(dst + (int64_t)e.f * ld + (int64_t)(row0 + rl) * ld + m0 + ml) = *(const uint4*)(tr1 + rl * TLD + ml);
     }
   }
 }
@@ -845,6 +879,9 @@ bool wide_ok(const GemmArgs& g) {
     case EPI_SGD:
       return e.ldm % 4 == 0 && e.sm % 4 == 0 && al(e.master, 16) && e.ldsh % 4 == 0 && e.ssh % 4 == 0 &&
              al(e.sh, 8) && e.ldshT % 8 == 0 && e.sshT % 8 == 0 && al(e.shT, 16);
+    case EPI_SWIGLU_BWD:
+      return e.ldc % 4 == 0 && e.sc % 4 == 0 && e.f % 4 == 0 && al(e.c, 8) && e.ldz % 4 == 0 && e.sz % 4 == 0 &&
+             al(e.zg, 8) && al(e.zu, 8) && e.t && e.ldt % 8 == 0 && e.st % 8 == 0 && al(e.t, 16);
     default: return false;
   }
 }
@@ -853,7 +890,9 @@ GemmPlan gemm_plan(const GemmArgs& g) {
   const bool splittable = g.e.kind == EPI_F32 || g.e.kind == EPI_T || g.e.kind == EPI_ADD_F32;
   if (wide_ok(g)) {
     const int64_t t128 = (int64_t)(g.M / 128) * (g.N / 256) * g.batch;
-    const int64_t t256 = g.M % 256 == 0 ? (int64_t)(g.M / 256) * (g.N / 256) * g.batch : 0;
+    // (the SwiGLU backward's two transposed tiles fit beside 128-row tiles only)
+    const int64_t t256 =
+        g.M % 256 == 0 && g.e.kind != EPI_SWIGLU_BWD ? (int64_t)(g.M / 256) * (g.N / 256) * g.batch : 0;
     if (g.ws && splittable && t128 < 192 && g.K >= 1024 && al(g.ws, 16)) {
       int S = (int)std::min<int64_t>(8, std::max<int64_t>(2, 256 / t128));
       S = std::min(S, g.K / 256);
@@ -904,6 +943,7 @@ hipError_t gemm_mfma_bf16(const GemmArgs& g, hipStream_t s) {
       case EPI_T: return launch_wide_bm<EPI_T>(g, bm, s);
       case EPI_ADD_F32: return launch_wide_bm<EPI_ADD_F32>(g, bm, s);
       case EPI_SGD: return launch_wide_bm<EPI_SGD>(g, bm, s);
+      case EPI_SWIGLU_BWD: return launch_wide<128, EPI_SWIGLU_BWD, false>(g, 1, s);
       default: break;
     }
   }

@@ -32,3 +32,10 @@ M3B_T = 131072
 MID = dict(n_layers=4, d_model=256, n_heads=2, d_ff=1024, vocab=1024, window=256, chunk=128, n_fast=2, batch=1,
            rope_theta=1e4, rms_eps=1e-5, lr=1e-2, dtype="bf16")
 MID_T = 680
+
+# d = 1024 (8 heads of 128): the per-chunk N = d products with K >= 1024 -- attention output
+# projection (bf16 output) and its input gradient, down projection (residual add), the
+# d(gate|up) -> d hidden product -- take the K-split path with the fused ordered sum
+MIDK = dict(n_layers=2, d_model=1024, n_heads=8, d_ff=1024, vocab=512, window=256, chunk=128, n_fast=1, batch=1,
+            rope_theta=1e4, rms_eps=1e-5, lr=1e-2, dtype="bf16")
+MIDK_T = 256

@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 
 from oracle import Oracle
-from tests.cfgs import MID, MID_T, TOY, cfg as mkcfg
+from tests.cfgs import MID, MID_T, MIDK, MIDK_T, TOY, cfg as mkcfg
 from test_token_chunk_amd import synth
 
 pytestmark = pytest.mark.gpu
@@ -90,6 +90,18 @@ def test_mid_matrix_core_tiles_parity(lookahead):
     print(f"mid: max loss rel err {rel:.3e}")
     assert rel <= tl
     compare_fast(ctx.fast_weights(0), o.get_fast(0), _w0(w, c), tw, "mid")
+
+
+def test_midk_split_k_epilogues_parity():
+    """d=1024, b=128: the K-split GEMMs with each final epilogue (fp32, bf16, residual add)."""
+    c = mkcfg(**MIDK)
+    print("case midk", flush=True)
+    w, o, ctx, ref, got = run_pair(c, MIDK_T, dist="zipf")
+    tl, tw = TOL["bf16"]
+    rel = np.max(np.abs(got - ref) / np.abs(ref))
+    print(f"midk: max loss rel err {rel:.3e}")
+    assert rel <= tl
+    compare_fast(ctx.fast_weights(0), o.get_fast(0), _w0(w, c), tw, "midk")
 
 
 def test_toy_more_fast_blocks_and_ragged_tail():
