@@ -312,27 +312,21 @@ hipError_t launch_fwd_nw(const AttnArgs& a, int S, hipStream_t s) {
   return hipGetLastError();
 }
 
-// 8 waves (256 queries) per block when there are enough query blocks to fill the chip,
-// else 4 waves (128 queries)
-// how many key-range parts give a grid of >= ~2 blocks per CU (1 when no workspace)
+// parts of a split that give about one round of blocks on the 256 CUs (one 8-wave block per
+// CU): floor(256 / blocks), at most 8, at least 8 key tiles per part, within the workspace
 int attn_splits(int64_t blocks, int64_t ntiles, int64_t need_per_split, const float* ws, int64_t ws_floats) {
-  if (!ws || blocks >= 384) return 1;
-  int S = (int)std::min<int64_t>(8, (512 + blocks - 1) / blocks);
-  S = (int)std::min<int64_t>(S, std::max<int64_t>(1, ntiles / 8));
-  while (S > 1 && S * need_per_split > ws_floats) --S;
-  return S;
-}
-
-// key-range parts of the forward: grids of fewer than 128 blocks (one 8-wave block per CU)
-// split the key range so that about one round of blocks covers the chip (needs the workspace)
-int fwd_splits(const AttnArgs& a) {
-  const int64_t blocks = (int64_t)cdiv(a.n, 8 * QW) * a.H * a.B;
-  if (!a.ws || blocks >= 128) return 1;
-  const int64_t ntiles = (std::min<int64_t>(a.window, a.pos0 + 1) + 8 * QW) / KT + 1;
+  if (!ws || blocks >= 128) return 1;
   int S = (int)std::min<int64_t>(8, 256 / blocks);
   S = (int)std::min<int64_t>(S, std::max<int64_t>(1, ntiles / 8));
-  while (S > 1 && S * (int64_t)a.B * a.H * a.n * (a.hd + 2) > a.ws_floats) --S;
+  while (S > 1 && S * need_per_split > ws_floats) --S;
   return std::max(S, 1);
+}
+
+// key-range parts of the forward
+int fwd_splits(const AttnArgs& a) {
+  const int64_t blocks = (int64_t)cdiv(a.n, 8 * QW) * a.H * a.B;
+  const int64_t ntiles = (std::min<int64_t>(a.window, a.pos0 + 1) + 8 * QW) / KT + 1;
+  return attn_splits(blocks, ntiles, (int64_t)a.B * a.H * a.n * (a.hd + 2), a.ws, a.ws_floats);
 }
 
 template <int HD>
@@ -822,13 +816,20 @@ hipError_t launch_bwd(const AttnBwdArgs& a, hipStream_t s) {
     e = tr ? launch_dq<HD, 8, false, true>(a, 1, s) : launch_dq<HD, 8, false, false>(a, 1, s);
     if (e != hipSuccess) return e;
   }
-  // dK/dV: split each key block's query range when the grid is small (ordered sum after)
+  // dK/dV: split each key block's query range when the grid is small (ordered sum after);
+  // one 4-wave block per CU, so pick the P <= 4 with the fewest rounds of 256 blocks per part
   const int64_t kblocks = (int64_t)cdiv(a.n, BQ) * a.H * a.B;
   int P = 1;
-  if (a.ws && kblocks < 384) {
-    P = (int)std::min<int64_t>(4, (512 + kblocks - 1) / kblocks);
-    P = std::min(P, (int)cdiv(a.n, KT));
-    while (P > 1 && 2LL * P * total > a.ws_floats) --P;
+  if (a.ws && kblocks < 256) {
+    double best = 1e30;
+    for (int p = 1; p <= std::min(4, (int)cdiv(a.n, KT)); ++p) {
+      if (p > 1 && 2LL * p * total > a.ws_floats) break;
+      const double cost = (double)cdiv(kblocks * p, 256) / p;
+      if (cost < best - 1e-9) {
+        best = cost;
+        P = p;
+      }
+    }
   }
   e = tr ? launch_dkv<HD, true>(a, P, s) : launch_dkv<HD, false>(a, P, s);
   if (e != hipSuccess) return e;
