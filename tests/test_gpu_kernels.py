@@ -106,6 +106,41 @@ def test_swa_fwd_matches_fp64(dtype, B, H, hd, n, window, pos0, R, use_ws):
     assert np.max(np.abs(lse.cpu().numpy() - L)) <= (1e-2 if dtype == "bf16" else 1e-5) * np.max(np.abs(L))
 
 
+@pytest.mark.parametrize("trend", ["growing", "shrinking", "spiky"])
+def test_swa_fwd_score_trends(trend):
+    """Scores that grow along the window (the reference max must move many times), shrink
+    (later keys underflow against an early max) or jump by far more than 2^8 at single keys."""
+    torch = _torch()
+    from test_token_chunk_amd import swa_fwd
+    B, H, hd, n, window, pos0, R = 1, 2, 128, 256, 1024, 3000, 1344
+    q, kr, vr = ring_inputs(torch, B, H, hd, n, R, window, pos0, torch.float32, seed=11)
+    pos = torch.arange(R, dtype=torch.float32)
+    # the absolute position of each ring slot over the range the chunk reads
+    slot_pos = torch.zeros(R)
+    for s_ in range(pos0 - window + 1, pos0 + n):
+        slot_pos[s_ % R] = s_
+    rel = (slot_pos - (pos0 - window)) / (window + n)
+    if trend == "growing":
+        scale = 0.5 + 6.0 * rel
+    elif trend == "shrinking":
+        scale = 6.5 - 6.0 * rel
+    else:
+        scale = torch.ones(R)
+        scale[torch.arange(0, R, 97)] = 12.0
+    kr = kr * scale[None, None, :, None]
+    q, kr, vr = q.to(torch.bfloat16), kr.to(torch.bfloat16), vr.to(torch.bfloat16)
+    o = torch.empty(B * n, H * hd, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(B, H, n, dtype=torch.float32, device="cuda")
+    swa_fwd(q.cuda(), kr.cuda(), vr.cuda(), vr.transpose(2, 3).contiguous().cuda(), o, lse, pos0, window,
+            ws=_workspace(torch, True))
+    torch.cuda.synchronize()
+    O, L = ref_attention(q.double().numpy(), kr.double().numpy(), vr.double().numpy(), pos0, window)
+    got = o.float().cpu().numpy().reshape(B, n, H, hd).transpose(0, 2, 1, 3)
+    assert np.all(np.isfinite(got))
+    assert np.max(np.abs(got - O)) <= 2e-2 * np.max(np.abs(O))
+    assert np.max(np.abs(lse.cpu().numpy() - L)) <= 1e-2 * np.max(np.abs(L))
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("hd,n,window,pos0,R", [(128, 256, 8192, 20000, 9216), (32, 64, 256, 960, 320),
                                                  (64, 96, 100, 5, 200)])
