@@ -31,7 +31,7 @@ constexpr int BQ = NW * QW;
 template <int HD>
 struct FwdSmem {
   bf16 k[2][KT][HD + 8];   // K tile, row = key
-  bf16 vt[2][HD][KT + 8];  // V^T tile, row = head dim
+  bf16 vt[3][HD][KT + 8];  // V^T tile, row = head dim (ring of 3: read one and two tiles late)
 };
 
 // two floats -> packed bf16 pair, round to nearest even (one v_cvt_pk_bf16_f32 on gfx950)
@@ -129,11 +129,11 @@ __global__ __launch_bounds__(NW * 64) void k_swa_fwd(AttnArgs a, int S) {
 #define STV(i, src)                                                                \
   if constexpr (VCH > i) {                                                         \
     const int c = tid + i * NT, r = c / (KT / 8), col = (c % (KT / 8)) * 8;        \
-    if (c < KT * HD / 8) *(uint4*)&sm.vt[buf][r][col] = src;                       \
+    if (c < KT * HD / 8) *(uint4*)&sm.vt[vbuf][r][col] = src;                      \
   }
-#define STORE_TILE(buf_)                                                           \
+#define STORE_TILE(buf_, vbuf_)                                                    \
   {                                                                                \
-    const int buf = (buf_);                                                        \
+    const int buf = (buf_), vbuf = (vbuf_);                                        \
     STK(0, rk0) STK(1, rk1) STK(2, rk2) STK(3, rk3)                                \
     STV(0, rv0) STV(1, rv1) STV(2, rv2) STV(3, rv3)                                \
   }
@@ -145,15 +145,42 @@ __global__ __launch_bounds__(NW * 64) void k_swa_fwd(AttnArgs a, int S) {
   const float sl2 = 1.4426950408889634f / sqrtf((float)HD);  // log2(e) / sqrt(hd)
   const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
 
+  // Two wave groups in counter-phase.  The waves of a block move in lockstep between the
+  // per-tile barriers, and the two waves that share a SIMD (w and w + NW/2) are in different
+  // groups: group A runs S^T, softmax, PV for tile it; group B runs PV for tile it-1 (its
+  // probabilities kept in registers), then S^T and softmax for tile it.  So while one wave of
+  // a SIMD works through its softmax on the vector ALUs, the other issues MFMAs.  V^T tiles
+  // live in a ring of 3 (group B reads them one iteration late).
+  const bool late = wid >= NW / 2;
+  uint32_t qa[8], qb[8];  // group B: probabilities of the previous tile
   if (it_beg < ntiles) {
     LOAD_TILE(it_beg)
-    STORE_TILE(it_beg & 1)
+    STORE_TILE(it_beg & 1, it_beg % 3)
   }
   __syncthreads();
+#define PV(vb, PA_, PB_)                                                                             \
+  {                                                                                              \
+    const bf16x8 pf0 = __builtin_bit_cast(bf16x8, make_uint4(PA_[0], PA_[1], PA_[2], PA_[3]));           \
+    const bf16x8 pf1 = __builtin_bit_cast(bf16x8, make_uint4(PA_[4], PA_[5], PA_[6], PA_[7]));           \
+    const bf16x8 pf2 = __builtin_bit_cast(bf16x8, make_uint4(PB_[0], PB_[1], PB_[2], PB_[3]));           \
+    const bf16x8 pf3 = __builtin_bit_cast(bf16x8, make_uint4(PB_[4], PB_[5], PB_[6], PB_[7]));           \
+    _Pragma("unroll") for (int st = 0; st < 4; ++st) {                                           \
+      const int kc = st * 16 + 4 * g;                                                            \
+      const bf16x8 pf = st == 0 ? pf0 : st == 1 ? pf1 : st == 2 ? pf2 : pf3;                     \
+      _Pragma("unroll") for (int hm = 0; hm < HM; ++hm) {                                        \
+        const bf16* vrow = &sm.vt[vb][hm * 32 + (lane & 31)][0];                                 \
+        uint2 lo2 = *(const uint2*)(vrow + kc);                                                  \
+        uint2 hi2 = *(const uint2*)(vrow + kc + 8);                                              \
+        bf16x8 vf = __builtin_bit_cast(bf16x8, make_uint4(lo2.x, lo2.y, hi2.x, hi2.y));          \
+        o[hm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, o[hm], 0, 0, 0);                 \
+      }                                                                                          \
+    }                                                                                            \
+  }
   for (int it = it_beg; it < ntiles; ++it) {
     const int cur = it & 1;
     if (it + 1 < ntiles) LOAD_TILE(it + 1)
     const int64_t kp0 = ktile0 + (int64_t)it * KT;
+    if (late && it > it_beg) PV((it - 1) % 3, qa, qb)
     // S^T for the two 32-key halves of the tile
     f32x16 s0 = f32x16{}, s1 = f32x16{};
     {
@@ -212,26 +239,20 @@ __global__ __launch_bounds__(NW * 64) void k_swa_fwd(AttnArgs a, int S) {
       psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pb[r >> 1]), ones, psum, false);
     }
     lrun = lrun * corr + psum;
-    // O^T += V^T P^T, four 16-key steps (keys 0-15, 16-31 of each half)
-    const bf16x8 pf[4] = {__builtin_bit_cast(bf16x8, make_uint4(pa[0], pa[1], pa[2], pa[3])),
-                          __builtin_bit_cast(bf16x8, make_uint4(pa[4], pa[5], pa[6], pa[7])),
-                          __builtin_bit_cast(bf16x8, make_uint4(pb[0], pb[1], pb[2], pb[3])),
-                          __builtin_bit_cast(bf16x8, make_uint4(pb[4], pb[5], pb[6], pb[7]))};
+    if (late) {
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      const int kc = st * 16 + 4 * g;
-#pragma unroll
-      for (int hm = 0; hm < HM; ++hm) {
-        const bf16* vrow = &sm.vt[cur][hm * 32 + (lane & 31)][0];
-        uint2 lo2 = *(const uint2*)(vrow + kc);
-        uint2 hi2 = *(const uint2*)(vrow + kc + 8);
-        bf16x8 vf = __builtin_bit_cast(bf16x8, make_uint4(lo2.x, lo2.y, hi2.x, hi2.y));
-        o[hm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[st], o[hm], 0, 0, 0);
+      for (int r = 0; r < 8; ++r) {
+        qa[r] = pa[r];
+        qb[r] = pb[r];
       }
+    } else {
+      PV(it % 3, pa, pb)
     }
-    if (it + 1 < ntiles) STORE_TILE(cur ^ 1)
+    if (it + 1 < ntiles) STORE_TILE(cur ^ 1, (it + 1) % 3)
     __syncthreads();
   }
+  if (late && it_beg < ntiles) PV((ntiles - 1) % 3, qa, qb)
+#undef PV
 
 #undef LOADK
 #undef LOADV
