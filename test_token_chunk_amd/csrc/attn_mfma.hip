@@ -296,25 +296,37 @@ __global__ __launch_bounds__(NW * 64) void k_swa_fwd(AttnArgs a, int S) {
 
 // merge the key-range parts of a split forward: O = sum_s w_s O_s / sum_s w_s l_s with
 // w_s = 2^((m_s - max m) * sl2); grid (n, H, B), one thread per head dim
-__global__ void k_swa_combine(AttnArgs a, int S) {
-  const int t = blockIdx.x, h = blockIdx.y, b = blockIdx.z, hd = a.hd;
-  const int64_t bh = (int64_t)b * a.H + h;
+__global__ __launch_bounds__(256) void k_swa_combine(AttnArgs a, int S) {
+  // one wave per (query, head); lane l covers head dims 2l, 2l+1
   const int64_t plane = (int64_t)a.B * a.H * a.n;
+  const int64_t qh = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // (b*H + h)*n + t
+  if (qh >= plane) return;
+  const int lane = threadIdx.x & 63, hd = a.hd;
+  const int64_t bh = qh / a.n;
+  const int t = (int)(qh % a.n), h = (int)(bh % a.H), b = (int)(bh / a.H);
   const float* pm = a.ws + (int64_t)S * plane * hd;
   const float* pl = pm + (int64_t)S * plane;
   const float sl2 = 1.4426950408889634f / sqrtf((float)hd);
   float M = -INFINITY;
-  for (int sidx = 0; sidx < S; ++sidx) M = fmaxf(M, pm[sidx * plane + bh * a.n + t]);
-  float L = 0.f, acc = 0.f;
+  for (int sidx = 0; sidx < S; ++sidx) M = fmaxf(M, pm[sidx * plane + qh]);
+  float L = 0.f;
+  float2 acc = make_float2(0.f, 0.f);
+  const bool act = 2 * lane < hd;
   for (int sidx = 0; sidx < S; ++sidx) {
-    const int64_t row = sidx * plane + bh * a.n + t;
+    const int64_t row = sidx * plane + qh;
     const float w = pm[row] == -INFINITY ? 0.f : exp2f((pm[row] - M) * sl2);
     L += w * pl[row];
-    if ((int)threadIdx.x < hd) acc += w * a.ws[row * hd + threadIdx.x];
+    if (act) {
+      const float2 v = *(const float2*)(a.ws + row * hd + 2 * lane);
+      acc.x += w * v.x;
+      acc.y += w * v.y;
+    }
   }
-  if ((int)threadIdx.x < hd)
-    ((bf16*)a.o)[((int64_t)b * a.n + t) * ((int64_t)a.H * hd) + (int64_t)h * hd + threadIdx.x] = f2bf(acc / L);
-  if (a.lse && threadIdx.x == 0) a.lse[bh * a.n + t] = M * (sl2 * 0.6931471805599453f) + logf(L);
+  if (act) {
+    const uint32_t pkd = (uint32_t)f2bf(acc.x / L).x | ((uint32_t)f2bf(acc.y / L).x << 16);
+    *(uint32_t*)((bf16*)a.o + ((int64_t)b * a.n + t) * ((int64_t)a.H * hd) + (int64_t)h * hd + 2 * lane) = pkd;
+  }
+  if (a.lse && lane == 0) a.lse[qh] = M * (sl2 * 0.6931471805599453f) + logf(L);
 }
 
 template <int HD, int NW, bool SPLIT>
@@ -329,7 +341,7 @@ hipError_t launch_fwd_nw(const AttnArgs& a, int S, hipStream_t s) {
   }
   dim3 grid(cdiv(a.n, NW * QW), a.H, a.B * S);
   hipLaunchKernelGGL(kern, grid, dim3(NW * 64), shm, s, a, S);
-  if (SPLIT) hipLaunchKernelGGL(k_swa_combine, dim3(a.n, a.H, a.B), dim3(HD), 0, s, a, S);
+  if (SPLIT) hipLaunchKernelGGL(k_swa_combine, dim3(cdiv((int64_t)a.B * a.H * a.n, 4)), dim3(256), 0, s, a, S);
   return hipGetLastError();
 }
 
@@ -741,25 +753,32 @@ hipError_t set_lds(K kern) {
   return hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(Smem));
 }
 
-// dk = sum_p ws[p], dv = sum_p ws[P + p], in order
-__global__ void k_dkv_reduce(const float* ws, int P, int64_t total, float* dk, float* dv) {
-  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
-    float sk = 0.f, sv = 0.f;
+// dk = sum_p ws[p], dv = sum_p ws[P + p], in order (4 elements per thread; total % 4 == 0)
+__global__ __launch_bounds__(256) void k_dkv_reduce(const float* ws, int P, int64_t total, float* dk, float* dv) {
+  for (int64_t i = 4 * (blockIdx.x * (int64_t)blockDim.x + threadIdx.x); i < total;
+       i += 4 * (int64_t)gridDim.x * blockDim.x) {
+    float4 sk = make_float4(0.f, 0.f, 0.f, 0.f), sv = sk;
     for (int p = 0; p < P; ++p) {
-      sk += ws[p * total + i];
-      sv += ws[(P + p) * total + i];
+      const float4 a = *(const float4*)(ws + p * total + i);
+      const float4 c = *(const float4*)(ws + (P + p) * total + i);
+      sk.x += a.x; sk.y += a.y; sk.z += a.z; sk.w += a.w;
+      sv.x += c.x; sv.y += c.y; sv.z += c.z; sv.w += c.w;
     }
-    dk[i] = sk;
-    dv[i] = sv;
+    *(float4*)(dk + i) = sk;
+    *(float4*)(dv + i) = sv;
   }
 }
 
-// dq = sum over the key-range parts, in order
-__global__ void k_dq_reduce(const float* ws, int S, int64_t total, float* dq) {
-  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
-    float acc = 0.f;
-    for (int sidx = 0; sidx < S; ++sidx) acc += ws[sidx * total + i];
-    dq[i] = acc;
+// dq = sum over the key-range parts, in order (4 elements per thread; total % 4 == 0)
+__global__ __launch_bounds__(256) void k_dq_reduce(const float* ws, int S, int64_t total, float* dq) {
+  for (int64_t i = 4 * (blockIdx.x * (int64_t)blockDim.x + threadIdx.x); i < total;
+       i += 4 * (int64_t)gridDim.x * blockDim.x) {
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int sidx = 0; sidx < S; ++sidx) {
+      const float4 v = *(const float4*)(ws + sidx * total + i);
+      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    }
+    *(float4*)(dq + i) = acc;
   }
 }
 
@@ -831,8 +850,8 @@ hipError_t launch_bwd(const AttnBwdArgs& a, hipStream_t s) {
   if (S > 1) {
     e = tr ? launch_dq<HD, 8, true, true>(a, S, s) : launch_dq<HD, 8, true, false>(a, S, s);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_dq_reduce, dim3((unsigned)std::min<int64_t>(cdiv(total, 256), 4096)), dim3(256), 0, s, a.ws,
-                       S, total, a.dq);
+    hipLaunchKernelGGL(k_dq_reduce, dim3((unsigned)std::min<int64_t>(cdiv(total / 4, 256), 8192)), dim3(256), 0, s,
+                       a.ws, S, total, a.dq);
   } else {
     e = tr ? launch_dq<HD, 8, false, true>(a, 1, s) : launch_dq<HD, 8, false, false>(a, 1, s);
     if (e != hipSuccess) return e;
@@ -855,7 +874,7 @@ hipError_t launch_bwd(const AttnBwdArgs& a, hipStream_t s) {
   e = tr ? launch_dkv<HD, true>(a, P, s) : launch_dkv<HD, false>(a, P, s);
   if (e != hipSuccess) return e;
   if (P > 1)
-    hipLaunchKernelGGL(k_dkv_reduce, dim3((unsigned)std::min<int64_t>(cdiv(total, 256), 4096)), dim3(256), 0, s,
+    hipLaunchKernelGGL(k_dkv_reduce, dim3((unsigned)std::min<int64_t>(cdiv(total / 4, 256), 8192)), dim3(256), 0, s,
                        a.ws, P, total, a.dk, a.dv);
   return hipGetLastError();
 }

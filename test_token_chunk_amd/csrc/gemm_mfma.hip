@@ -807,6 +807,38 @@ __global__ void k_splitk_reduce(GemmArgs g, int S) {
   }
 }
 
+// the same four elements of a row at a time (N, ldc, the batch stride and c are multiples of
+// four elements / 16 bytes): 16-byte part reads, 16-byte fp32 or 8-byte bf16 stores
+template <int EK>
+__global__ __launch_bounds__(256) void k_splitk_reduce4(GemmArgs g, int S) {
+  const int64_t per = (int64_t)g.M * g.N;
+  const int64_t total = per * g.batch, total4 = total / 4;
+  const Epi& e = g.e;
+  for (int64_t i4 = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i4 < total4; i4 += (int64_t)gridDim.x * blockDim.x) {
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int sidx = 0; sidx < S; ++sidx) {
+      const float4 v = *(const float4*)(g.ws + sidx * total + 4 * i4);
+      acc.x += v.x;
+      acc.y += v.y;
+      acc.z += v.z;
+      acc.w += v.w;
+    }
+    const int64_t i = 4 * i4;
+    const int64_t bz = i / per, r = i % per, m = r / g.N, n = r % g.N;
+    if constexpr (EK == EPI_F32) {
+      *(float4*)((float*)e.c + bz * e.sc + m * e.ldc + n) = acc;
+    } else if constexpr (EK == EPI_T) {
+      const uint2 w = make_uint2((uint32_t)f2bf(acc.x).x | ((uint32_t)f2bf(acc.y).x << 16),
+                                 (uint32_t)f2bf(acc.z).x | ((uint32_t)f2bf(acc.w).x << 16));
+      *(uint2*)((bf16*)e.c + bz * e.sc + m * e.ldc + n) = w;
+    } else {
+      float* c = (float*)e.c + bz * e.sc + m * e.ldc + n;
+      const float4 p = *(const float4*)c;
+      *(float4*)c = make_float4(p.x + acc.x, p.y + acc.y, p.z + acc.z, p.w + acc.w);
+    }
+  }
+}
+
 hipError_t launch_splitk(const GemmArgs& g0, int S, int Ks, bool wide, hipStream_t s) {
   GemmArgs g = g0;
   g.e.ldt = S;   // carried to the kernel
@@ -830,6 +862,18 @@ hipError_t launch_splitk(const GemmArgs& g0, int S, int Ks, bool wide, hipStream
     hipLaunchKernelGGL(kern, grid, dim3(256), shm, s, g);
   }
   const int64_t total = (int64_t)g.batch * g.M * g.N;
+  const bool vec = g.N % 4 == 0 && g.e.ldc % 4 == 0 && g.e.sc % 4 == 0 && ((uintptr_t)g.e.c % 16) == 0 &&
+                   ((uintptr_t)g.ws % 16) == 0;
+  if (vec) {
+    dim3 rg4((unsigned)std::min<int64_t>(cdiv(total / 4, 256), 8192));
+    switch (g0.e.kind) {
+      case EPI_F32: hipLaunchKernelGGL(k_splitk_reduce4<EPI_F32>, rg4, dim3(256), 0, s, g0, S); break;
+      case EPI_T: hipLaunchKernelGGL(k_splitk_reduce4<EPI_T>, rg4, dim3(256), 0, s, g0, S); break;
+      case EPI_ADD_F32: hipLaunchKernelGGL(k_splitk_reduce4<EPI_ADD_F32>, rg4, dim3(256), 0, s, g0, S); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   dim3 rg((unsigned)std::min<int64_t>(cdiv(total, 256), 4096));
   switch (g0.e.kind) {
     case EPI_F32: hipLaunchKernelGGL(k_splitk_reduce<EPI_F32>, rg, dim3(256), 0, s, g0, S); break;
@@ -888,6 +932,9 @@ bool wide_ok(const GemmArgs& g) {
 
 GemmPlan gemm_plan(const GemmArgs& g) {
   const bool splittable = g.e.kind == EPI_F32 || g.e.kind == EPI_T || g.e.kind == EPI_ADD_F32;
+  // short K (the weight gradients over one chunk): the prologue and the epilogue weigh as much as
+  // the main loop, and two 128 x 128 blocks per CU overlap them better than one wide block
+  if (g.K <= 1024 && g.e.kind == EPI_SGD && dl_ok(g, g.K)) return {1, 1, g.K};
   if (wide_ok(g)) {
     const int64_t t128 = (int64_t)(g.M / 128) * (g.N / 256) * g.batch;
     // (the SwiGLU backward's two transposed tiles fit beside 128-row tiles only)
