@@ -156,9 +156,11 @@ int ttt_reset(ttt_ctx* ctx);
 /* Current absolute position of every row (rows advance together). */
 int64_t ttt_position(const ttt_ctx* ctx);
 
-/* Kernel timing (tracing): while enabled, every launch of the classes below
- * is bracketed by HIP events on the context's stream.  ttt_profile_enable
- * clears earlier records; ttt_profile_read synchronizes and returns, per
+/* Kernel timing (tracing): while enabled, every launch of the selected classes
+ * below is bracketed by HIP events on the stream it runs on.  ttt_profile_enable
+ * takes a bit mask (bit i selects class i, -1 all of them, 0 turns timing off;
+ * events cost a little time per launch, so time only what is needed) and clears
+ * earlier records; ttt_profile_read synchronizes and returns, per
  * class, the summed device time (ms), the launch count and the algorithmic
  * FLOPs of those launches (matmul = 2 M N K; attention = 4 * head_dim per
  * visible query-key pair, plus 4 * head_dim per in-chunk pair in backward).

@@ -33,9 +33,10 @@ PROFILE_KERNELS = {  # class: (kernels, one kernel per launch)
     "gemm_bf16out": ("k_gemm_wide<256|128, 1, false> (k_gemm_dl / k_gemm_mfma off the wide-tile shapes)", False),
     "gemm_resid": ("k_gemm_wide<256|128, 2, false> (k_gemm_mfma off the wide-tile shapes)", False),
     "gemm_swiglu": ("k_gemm_wide<256|128, 7, false> (k_gemm_dl / k_gemm_mfma off the wide-tile shapes)", False),
-    "gemm_swiglu_bwd": ("k_gemm_dl<4, 2, false> (k_gemm_mfma off the 128-aligned shapes)", False),
-    "gemm_sgd": ("k_gemm_wide<256|128, 5, false> on the side stream (overlapped)", False),
-    "gemm_splitk": ("k_gemm_wide<128, 0, true> + k_splitk_reduce<*>", False),
+    "gemm_swiglu_bwd": ("k_gemm_wide<128, 4, false> (k_gemm_mfma off the wide-tile shapes)", False),
+    "gemm_sgd": ("k_gemm_dl<*, 5, false> (K <= 1024) / k_gemm_wide<256|128, 5, false> on the side stream "
+                 "(overlapped)", False),
+    "gemm_splitk": ("k_gemm_wide<128, 0, true> + k_splitk_reduce4<0>", False),
     "swa_fwd": ("k_swa_fwd<hd, 8, false>", True),
     "swa_fwd_split": ("k_swa_fwd<hd, 8, true> + k_swa_combine", False),
     "swa_bwd": ("k_dvec + k_heads_transpose + k_swa_dq<hd, 8, *> (+ k_dq_reduce) + k_swa_dkv<hd, *> "
@@ -275,9 +276,10 @@ class TTTContext:
     def reset(self):
         self._check(self._lib.ttt_reset(self._h))
 
-    def profile_begin(self):
-        """Start timing every GEMM / attention launch with HIP events."""
-        self._check(self._lib.ttt_profile_enable(self._h, 1))
+    def profile_begin(self, classes=None):
+        """Start timing the launches of `classes` (names of PROFILE_CLASSES; None = all) with HIP events."""
+        mask = -1 if classes is None else sum(1 << PROFILE_CLASSES.index(k) for k in classes)
+        self._check(self._lib.ttt_profile_enable(self._h, mask))
         return True
 
     def profile_end(self, _token=None) -> dict:

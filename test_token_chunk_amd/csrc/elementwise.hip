@@ -69,6 +69,112 @@ __global__ void k_convert(const float* x, int d, T* y, T* yT, int rpb, int64_t l
   }
 }
 
+// 4 consecutive values -> T: one 16-byte (fp32) or 8-byte (bf16) store
+template <typename T>
+__device__ __forceinline__ void store4(T* p, float a, float b, float c, float d);
+template <>
+__device__ __forceinline__ void store4<float>(float* p, float a, float b, float c, float d) {
+  *(float4*)p = make_float4(a, b, c, d);
+}
+template <>
+__device__ __forceinline__ void store4<bf16>(bf16* p, float a, float b, float c, float d) {
+  *(uint2*)p = make_uint2((uint32_t)f2bf(a).x | ((uint32_t)f2bf(b).x << 16),
+                          (uint32_t)f2bf(c).x | ((uint32_t)f2bf(d).x << 16));
+}
+
+// Vector forms of the row kernels above: one wave per row, 16-byte loads (d % 4 == 0,
+// 16-byte aligned rows); transposed outputs are written by k_transpose_rows afterwards.
+template <typename T>
+__global__ __launch_bounds__(256) void k_rmsnorm_fwd4(const float* x, int64_t M, int d, const float* g, float eps,
+                                                      T* y, float* rstd, float* xcopy) {
+  const int64_t m = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (m >= M) return;
+  const int lane = threadIdx.x & 63, d4 = d / 4;
+  const float4* xr = (const float4*)(x + m * d);
+  float ss = 0.f;
+  for (int i = lane; i < d4; i += 64) {
+    const float4 v = xr[i];
+    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+    if (xcopy) ((float4*)(xcopy + m * d))[i] = v;
+  }
+  ss = warp_sum(ss);
+  const float r = 1.f / sqrtf(ss / (float)d + eps);
+  if (lane == 0 && rstd) rstd[m] = r;
+  for (int i = lane; i < d4; i += 64) {
+    const float4 v = xr[i], w = ((const float4*)g)[i];
+    store4<T>(y + m * d + 4 * i, w.x * v.x * r, w.y * v.y * r, w.z * v.z * r, w.w * v.w * r);
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_rmsnorm_bwd4(const float* x, const float* rstd, int64_t M, int d,
+                                                      const float* g, const float* dy, const float* resid, float* out,
+                                                      T* outT) {
+  const int64_t m = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (m >= M) return;
+  const int lane = threadIdx.x & 63, d4 = d / 4;
+  const float4* xr = (const float4*)(x + m * d);
+  const float4* dr = (const float4*)(dy + m * d);
+  const float4* g4 = (const float4*)g;
+  float dot = 0.f;
+  for (int i = lane; i < d4; i += 64) {
+    const float4 v = xr[i], e = dr[i], w = g4[i];
+    dot += w.x * e.x * v.x + w.y * e.y * v.y + w.z * e.z * v.z + w.w * e.w * v.w;
+  }
+  dot = warp_sum(dot);
+  const float r = rstd[m];
+  const float c = r * r * r * dot / (float)d;
+  for (int i = lane; i < d4; i += 64) {
+    const float4 v = xr[i], e = dr[i], w = g4[i];
+    float4 o = make_float4(r * w.x * e.x - v.x * c, r * w.y * e.y - v.y * c, r * w.z * e.z - v.z * c,
+                           r * w.w * e.w - v.w * c);
+    if (resid) {
+      const float4 q = ((const float4*)(resid + m * d))[i];
+      o.x += q.x;
+      o.y += q.y;
+      o.z += q.z;
+      o.w += q.w;
+    }
+    ((float4*)(out + m * d))[i] = o;
+    if (outT) store4<T>(outT + m * d + 4 * i, o.x, o.y, o.z, o.w);
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_convert4(const float* x, int64_t M, int d, T* y) {
+  const int64_t m = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (m >= M) return;
+  const int lane = threadIdx.x & 63, d4 = d / 4;
+  for (int i = lane; i < d4; i += 64) {
+    const float4 v = ((const float4*)(x + m * d))[i];
+    store4<T>(y + m * d + 4 * i, v.x, v.y, v.z, v.w);
+  }
+}
+
+// y [B][n][d] (bf16) -> yT [B][d][ldt]: yT[b][c][t] = y[b][t][c] for t < n, through a 64 x 64
+// LDS tile, 16-byte loads and stores (d % 8 == 0, n % 8 == 0, ldt % 8 == 0)
+__global__ __launch_bounds__(256) void k_transpose_rows(const bf16* __restrict__ y, bf16* __restrict__ yt, int n,
+                                                        int d, int64_t ldt) {
+  __shared__ __align__(16) uint16_t tile[64][72];  // [token][column]
+  const int t0 = blockIdx.x * 64, c0 = blockIdx.y * 64, b = blockIdx.z;
+  for (int e = threadIdx.x; e < 64 * 8; e += 256) {
+    const int r = e >> 3, ch = (e & 7) * 8, t = t0 + r, c = c0 + ch;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (t < n && c < d) v = *(const uint4*)(y + ((int64_t)b * n + t) * d + c);
+    *(uint4*)&tile[r][ch] = v;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < 64 * 8; e += 256) {
+    const int cr = e >> 3, tch = (e & 7) * 8, c = c0 + cr, t = t0 + tch;
+    if (c < d && t < n) {
+      uint32_t w[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) w[k] = (uint32_t)tile[tch + 2 * k][cr] | ((uint32_t)tile[tch + 2 * k + 1][cr] << 16);
+      *(uint4*)(yt + ((int64_t)b * d + c) * ldt + t) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  }
+}
+
 __global__ void k_count_valid(const int32_t* tgt, int64_t ld, int n, int* nvalid) {
   __shared__ float sh[16];
   int b = blockIdx.x;
@@ -104,6 +210,55 @@ __global__ void k_ce_rows(const float* logits, int V, const int32_t* tgt, int64_
   for (int v = threadIdx.x; v < V; v += blockDim.x) {
     float p = (y >= 0) ? (expf(z[v] - lse) - (v == y ? 1.f : 0.f)) * inv : 0.f;
     dz[v] = from_f<T>(p);
+  }
+}
+
+// Same result for V % 4 == 0 with 16-byte logit loads and one pass fewer: each thread keeps a
+// running (max, sum of exp) over its elements; the block merges them (sum_i s_i e^(m_i - M)).
+template <typename T>
+__global__ __launch_bounds__(512) void k_ce_rows4(const float* logits, int V, const int32_t* tgt, int64_t ld,
+                                                  const int* nvalid, int rpb, float* loss_tok, T* dlogits, int* err) {
+  __shared__ float sh[16];
+  const int64_t m = blockIdx.x;
+  const int b = (int)(m / rpb), t = (int)(m % rpb);
+  int y = tgt[b * ld + t];
+  if (y < -1 || y >= V) {
+    if (threadIdx.x == 0) atomicOr(err, 2);
+    y = -1;
+  }
+  const float4* z4 = (const float4*)(logits + m * V);
+  const int V4 = V / 4;
+  float mx = -INFINITY, se = 0.f;
+  for (int v = threadIdx.x; v < V4; v += blockDim.x) {
+    const float4 z = z4[v];
+    const float zm = fmaxf(fmaxf(z.x, z.y), fmaxf(z.z, z.w));
+    if (zm > mx) {
+      se *= __expf(mx - zm);
+      mx = zm;
+    }
+    se += __expf(z.x - mx) + __expf(z.y - mx) + __expf(z.z - mx) + __expf(z.w - mx);
+  }
+  const float M = block_max(mx, sh);
+  const float ssum = block_sum(mx == -INFINITY ? 0.f : se * __expf(mx - M), sh);
+  const float lse = M + logf(ssum);
+  const int nv = nvalid[b];
+  const float inv = nv > 0 ? 1.f / (float)nv : 0.f;
+  if (threadIdx.x == 0) loss_tok[m] = (y >= 0) ? lse - logits[m * V + y] : 0.f;
+  T* dz = dlogits + m * V;
+  for (int v = threadIdx.x; v < V4; v += blockDim.x) {
+    const float4 z = z4[v];
+    float p[4] = {__expf(z.x - lse), __expf(z.y - lse), __expf(z.z - lse), __expf(z.w - lse)};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if (4 * v + k == y) p[k] -= 1.f;
+      p[k] = (y >= 0) ? p[k] * inv : 0.f;
+    }
+    if constexpr (sizeof(T) == 2) {
+      *(uint2*)(dz + 4 * v) = make_uint2((uint32_t)f2bf(p[0]).x | ((uint32_t)f2bf(p[1]).x << 16),
+                                         (uint32_t)f2bf(p[2]).x | ((uint32_t)f2bf(p[3]).x << 16));
+    } else {
+      *(float4*)(dz + 4 * v) = make_float4(p[0], p[1], p[2], p[3]);
+    }
   }
 }
 
@@ -227,6 +382,148 @@ __global__ __launch_bounds__(256) void k_rope_qkv(const float* __restrict__ qkv,
   }
 }
 
+// Vector form of k_rope_qkv (hd % 8 == 0, 16-byte aligned projection rows and tables):
+// each thread rotates 4 consecutive pairs with 16-byte loads and 8- or 16-byte stores; the
+// transposed rows are written 4 tokens per store where the 4 ring slots are consecutive.
+template <typename T>
+__global__ __launch_bounds__(256) void k_rope_qkv4(const float* __restrict__ qkv, RopeRing rr) {
+  __shared__ T vt[128][RT + 2];  // [dim][token]
+  __shared__ T qs[128][RT + 2];
+  constexpr bool KTR = sizeof(T) == 2;
+  __shared__ T ks[KTR ? 128 : 1][RT + 2];
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int t0 = blockIdx.x * RT;
+  const int hd = rr.hd, half = hd / 2, q4 = half / 4, d = rr.H * hd;
+  const int nt = min(RT, rr.n - t0);
+  const int64_t bh = (int64_t)b * rr.H + h;
+  T* Q = (T*)rr.q;
+  T* Kr = (T*)rr.kr;
+  T* Vr = (T*)rr.vr;
+  for (int e = threadIdx.x; e < RT * q4; e += blockDim.x) {
+    const int tt = e / q4, i = (e % q4) * 4;
+    if (tt >= nt) continue;
+    const int t = t0 + tt;
+    const int64_t pos = rr.pos0 + t;
+    const int slot = (int)(pos % rr.R);
+    const float* row = qkv + ((int64_t)b * rr.n + t) * 3 * d + h * hd;
+    const float4 c = *(const float4*)(rr.cos_t + pos * half + i), sn = *(const float4*)(rr.sin_t + pos * half + i);
+    const float cc[4] = {c.x, c.y, c.z, c.w}, ss[4] = {sn.x, sn.y, sn.z, sn.w};
+    float lo[4], hi[4];
+    // q
+    float4 a = *(const float4*)(row + i), bb = *(const float4*)(row + half + i);
+    float av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {bb.x, bb.y, bb.z, bb.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      lo[j] = av[j] * cc[j] - bv[j] * ss[j];
+      hi[j] = bv[j] * cc[j] + av[j] * ss[j];
+      qs[i + j][tt] = from_f<T>(lo[j]);
+      qs[i + j + half][tt] = from_f<T>(hi[j]);
+    }
+    T* qrow = Q + (bh * rr.n + t) * hd;
+    store4<T>(qrow + i, lo[0], lo[1], lo[2], lo[3]);
+    store4<T>(qrow + half + i, hi[0], hi[1], hi[2], hi[3]);
+    // k
+    a = *(const float4*)(row + d + i);
+    bb = *(const float4*)(row + d + half + i);
+    av[0] = a.x; av[1] = a.y; av[2] = a.z; av[3] = a.w;
+    bv[0] = bb.x; bv[1] = bb.y; bv[2] = bb.z; bv[3] = bb.w;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      lo[j] = av[j] * cc[j] - bv[j] * ss[j];
+      hi[j] = bv[j] * cc[j] + av[j] * ss[j];
+      if constexpr (KTR) {
+        ks[i + j][tt] = from_f<T>(lo[j]);
+        ks[i + j + half][tt] = from_f<T>(hi[j]);
+      }
+    }
+    T* krow = Kr + (bh * rr.R + slot) * hd;
+    store4<T>(krow + i, lo[0], lo[1], lo[2], lo[3]);
+    store4<T>(krow + half + i, hi[0], hi[1], hi[2], hi[3]);
+    // v
+    a = *(const float4*)(row + 2 * d + i);
+    bb = *(const float4*)(row + 2 * d + half + i);
+    T* vrow = Vr + (bh * rr.R + slot) * hd;
+    store4<T>(vrow + i, a.x, a.y, a.z, a.w);
+    store4<T>(vrow + half + i, bb.x, bb.y, bb.z, bb.w);
+    vt[i][tt] = from_f<T>(a.x);
+    vt[i + 1][tt] = from_f<T>(a.y);
+    vt[i + 2][tt] = from_f<T>(a.z);
+    vt[i + 3][tt] = from_f<T>(a.w);
+    vt[i + half][tt] = from_f<T>(bb.x);
+    vt[i + half + 1][tt] = from_f<T>(bb.y);
+    vt[i + half + 2][tt] = from_f<T>(bb.z);
+    vt[i + half + 3][tt] = from_f<T>(bb.w);
+  }
+  __syncthreads();
+  T* Vt = (T*)rr.vtr + bh * hd * rr.R;
+  T* Kt = (KTR && rr.ktr) ? (T*)rr.ktr + bh * hd * rr.R : nullptr;
+  T* Qt = rr.qt ? (T*)rr.qt + bh * hd * rr.n : nullptr;
+  const bool qt4 = rr.n % 4 == 0;
+  for (int e = threadIdx.x; e < hd * (RT / 4); e += blockDim.x) {
+    const int dim = e / (RT / 4), tt = (e % (RT / 4)) * 4;
+    if (tt >= nt) continue;
+    const int t = t0 + tt;
+    const int slot = (int)((rr.pos0 + t) % rr.R);
+    if (tt + 4 <= nt && slot % 4 == 0 && slot + 4 <= rr.R && rr.R % 4 == 0) {
+      store4<T>(Vt + (int64_t)dim * rr.R + slot, to_f<T>(vt[dim][tt]), to_f<T>(vt[dim][tt + 1]),
+                to_f<T>(vt[dim][tt + 2]), to_f<T>(vt[dim][tt + 3]));
+      if constexpr (KTR)
+        if (Kt)
+          store4<T>(Kt + (int64_t)dim * rr.R + slot, to_f<T>(ks[dim][tt]), to_f<T>(ks[dim][tt + 1]),
+                    to_f<T>(ks[dim][tt + 2]), to_f<T>(ks[dim][tt + 3]));
+    } else {
+      for (int u = 0; u < 4 && tt + u < nt; ++u) {
+        const int sl = (int)((rr.pos0 + t + u) % rr.R);
+        Vt[(int64_t)dim * rr.R + sl] = vt[dim][tt + u];
+        if constexpr (KTR)
+          if (Kt) Kt[(int64_t)dim * rr.R + sl] = ks[dim][tt + u];
+      }
+    }
+    if (Qt) {
+      if (qt4 && tt + 4 <= nt) {
+        store4<T>(Qt + (int64_t)dim * rr.n + t, to_f<T>(qs[dim][tt]), to_f<T>(qs[dim][tt + 1]),
+                  to_f<T>(qs[dim][tt + 2]), to_f<T>(qs[dim][tt + 3]));
+      } else {
+        for (int u = 0; u < 4 && tt + u < nt; ++u) Qt[(int64_t)dim * rr.n + t + u] = qs[dim][tt + u];
+      }
+    }
+  }
+}
+
+// vector form of k_rope_bwd_pack: 4 consecutive pairs per thread (hd % 8 == 0, aligned rows)
+template <typename T>
+__global__ __launch_bounds__(256) void k_rope_bwd_pack4(const float* dq, const float* dk, const float* dv,
+                                                        const float* cos_t, const float* sin_t, int64_t pos0,
+                                                        int64_t M, int n, int H, int hd, T* dqkv) {
+  const int half = hd / 2, q4 = half / 4, d = H * hd;
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= M * H * q4) return;
+  const int64_t m = e / (H * q4);
+  const int h = (int)((e / q4) % H), i = (int)(e % q4) * 4;
+  const int64_t pos = pos0 + m % n;
+  const float4 c = *(const float4*)(cos_t + pos * half + i), sn = *(const float4*)(sin_t + pos * half + i);
+  const float cc[4] = {c.x, c.y, c.z, c.w}, ss[4] = {sn.x, sn.y, sn.z, sn.w};
+  T* o = dqkv + m * 3 * d + h * hd;
+  const float* src[2] = {dq + m * d + h * hd, dk + m * d + h * hd};
+#pragma unroll
+  for (int w = 0; w < 2; ++w) {
+    const float4 a = *(const float4*)(src[w] + i), bb = *(const float4*)(src[w] + half + i);
+    const float av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {bb.x, bb.y, bb.z, bb.w};
+    float lo[4], hi[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      lo[j] = av[j] * cc[j] + bv[j] * ss[j];
+      hi[j] = bv[j] * cc[j] - av[j] * ss[j];
+    }
+    store4<T>(o + w * d + i, lo[0], lo[1], lo[2], lo[3]);
+    store4<T>(o + w * d + half + i, hi[0], hi[1], hi[2], hi[3]);
+  }
+  const float* v = dv + m * d + h * hd;
+  const float4 a = *(const float4*)(v + i), bb = *(const float4*)(v + half + i);
+  store4<T>(o + 2 * d + i, a.x, a.y, a.z, a.w);
+  store4<T>(o + 2 * d + half + i, bb.x, bb.y, bb.z, bb.w);
+}
+
 // inverse rotation of dq, dk (gradients w.r.t. rotated q, k) and packing [dq|dk|dv]
 template <typename T>
 __global__ void k_rope_bwd_pack(const float* dq, const float* dk, const float* dv, const float* cos_t,
@@ -289,10 +586,39 @@ hipError_t embed_gather_ld(const int32_t* ids, int64_t ld, int B, int n, const T
   return hipGetLastError();
 }
 
+namespace {
+bool al16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+// the bf16 transposed copy [B][d][ldT] of a row-major [B*rpb][d] bf16 matrix
+template <typename T>
+bool transpose_ok(const T* y, const T* yT, int64_t M, int d, int rpb, int64_t ldT) {
+  return sizeof(T) == 2 && y && rpb > 0 && M % rpb == 0 && rpb % 8 == 0 && ldT % 8 == 0 && d % 8 == 0 && al16(y) &&
+         al16(yT);
+}
+
+template <typename T>
+hipError_t transpose_rows(const T* y, T* yT, int64_t M, int d, int rpb, int64_t ldT, hipStream_t s) {
+  hipLaunchKernelGGL(k_transpose_rows, dim3(cdiv(rpb, 64), cdiv(d, 64), (unsigned)(M / rpb)), dim3(256), 0, s,
+                     (const bf16*)y, (bf16*)yT, rpb, d, ldT);
+  return hipGetLastError();
+}
+}  // namespace
+
 template <typename T>
 hipError_t rmsnorm_fwd(const float* x, int64_t M, int d, const float* g, float eps, T* y, float* rstd, T* yT, int rpb,
-                       int64_t ldT, hipStream_t s) {
+                       int64_t ldT, float* xcopy, hipStream_t s) {
   if (M == 0) return hipSuccess;
+  if (y && d % 4 == 0 && al16(x) && al16(g) && al16(y) && al16(xcopy) &&
+      (!yT || transpose_ok(y, yT, M, d, rpb, ldT))) {
+    hipLaunchKernelGGL(k_rmsnorm_fwd4<T>, dim3(cdiv(M, 4)), dim3(256), 0, s, x, M, d, g, eps, y, rstd, xcopy);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !yT) return e;
+    return transpose_rows(y, yT, M, d, rpb, ldT, s);
+  }
+  if (xcopy) {
+    hipError_t e = hipMemcpyAsync(xcopy, x, (size_t)M * d * 4, hipMemcpyDeviceToDevice, s);
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL(k_rmsnorm_fwd<T>, dim3(M), dim3(row_threads(d)), 0, s, x, d, g, eps, y, rstd, yT, rpb, ldT);
   return hipGetLastError();
 }
@@ -301,6 +627,10 @@ template <typename T>
 hipError_t rmsnorm_bwd(const float* x, const float* rstd, int64_t M, int d, const float* g, const float* dy,
                        const float* resid, float* out, T* outT, hipStream_t s) {
   if (M == 0) return hipSuccess;
+  if (d % 4 == 0 && al16(x) && al16(g) && al16(dy) && al16(resid) && al16(out) && al16(outT)) {
+    hipLaunchKernelGGL(k_rmsnorm_bwd4<T>, dim3(cdiv(M, 4)), dim3(256), 0, s, x, rstd, M, d, g, dy, resid, out, outT);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(k_rmsnorm_bwd<T>, dim3(M), dim3(row_threads(d)), 0, s, x, rstd, d, g, dy, resid, out, outT);
   return hipGetLastError();
 }
@@ -308,6 +638,12 @@ hipError_t rmsnorm_bwd(const float* x, const float* rstd, int64_t M, int d, cons
 template <typename T>
 hipError_t convert_rows(const float* x, int64_t M, int d, T* y, T* yT, int rpb, int64_t ldT, hipStream_t s) {
   if (M == 0) return hipSuccess;
+  if (y && d % 4 == 0 && al16(x) && al16(y) && (!yT || transpose_ok(y, yT, M, d, rpb, ldT))) {
+    hipLaunchKernelGGL(k_convert4<T>, dim3(cdiv(M, 4)), dim3(256), 0, s, x, M, d, y);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !yT) return e;
+    return transpose_rows(y, yT, M, d, rpb, ldT, s);
+  }
   hipLaunchKernelGGL(k_convert<T>, dim3(M), dim3(row_threads(d)), 0, s, x, d, y, yT, rpb, ldT);
   return hipGetLastError();
 }
@@ -321,7 +657,12 @@ template <typename T>
 hipError_t ce_rows_ld(const float* logits, int64_t M, int V, const int32_t* tgt, int64_t ld, const int* nvalid,
                       int rpb, float* loss_tok, T* dlogits, int* err, hipStream_t s) {
   if (M == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_ce_rows<T>, dim3(M), dim3(256), 0, s, logits, V, tgt, ld, nvalid, rpb, loss_tok, dlogits, err);
+  if (V % 4 == 0 && ((uintptr_t)logits % 16) == 0 && ((uintptr_t)dlogits % 16) == 0)
+    hipLaunchKernelGGL(k_ce_rows4<T>, dim3(M), dim3(512), 0, s, logits, V, tgt, ld, nvalid, rpb, loss_tok, dlogits,
+                       err);
+  else
+    hipLaunchKernelGGL(k_ce_rows<T>, dim3(M), dim3(256), 0, s, logits, V, tgt, ld, nvalid, rpb, loss_tok, dlogits,
+                       err);
   return hipGetLastError();
 }
 
@@ -346,10 +687,12 @@ hipError_t rope_qkv_f32in(const float* qkv, int B, const RopeRing& rr, int is_bf
   if (B * rr.n == 0) return hipSuccess;
   if (rr.hd > 128) return hipErrorInvalidValue;
   dim3 grid(cdiv(rr.n, RT), rr.H, B);
+  const bool vec = rr.hd % 8 == 0 && al16(qkv) && al16(rr.cos_t) && al16(rr.sin_t) && al16(rr.q) && al16(rr.kr) &&
+                   al16(rr.vr) && al16(rr.vtr) && al16(rr.ktr) && al16(rr.qt);
   if (is_bf16)
-    hipLaunchKernelGGL(k_rope_qkv<bf16>, grid, dim3(256), 0, s, qkv, rr);
+    hipLaunchKernelGGL(vec ? k_rope_qkv4<bf16> : k_rope_qkv<bf16>, grid, dim3(256), 0, s, qkv, rr);
   else
-    hipLaunchKernelGGL(k_rope_qkv<float>, grid, dim3(256), 0, s, qkv, rr);
+    hipLaunchKernelGGL(vec ? k_rope_qkv4<float> : k_rope_qkv<float>, grid, dim3(256), 0, s, qkv, rr);
   return hipGetLastError();
 }
 
@@ -357,6 +700,12 @@ template <typename T>
 hipError_t rope_bwd_pack(const float* dq, const float* dk, const float* dv, const float* cos_t, const float* sin_t,
                          int64_t pos0, int B, int n, int H, int hd, T* dqkv, hipStream_t s) {
   if (B * n == 0) return hipSuccess;
+  if (hd % 8 == 0 && al16(dq) && al16(dk) && al16(dv) && al16(cos_t) && al16(sin_t) && al16(dqkv)) {
+    const int64_t M = (int64_t)B * n, items = M * H * (hd / 8);
+    hipLaunchKernelGGL(k_rope_bwd_pack4<T>, dim3(cdiv(items, 256)), dim3(256), 0, s, dq, dk, dv, cos_t, sin_t, pos0, M,
+                       n, H, hd, dqkv);
+    return hipGetLastError();
+  }
   int th = hd / 2 >= 64 ? 64 : 32;
   hipLaunchKernelGGL(k_rope_bwd_pack<T>, dim3(B * n, H), dim3(th), 0, s, dq, dk, dv, cos_t, sin_t, pos0, n, H, hd,
                      dqkv);
@@ -379,7 +728,7 @@ hipError_t refresh_shadows(const float* master, int rows, int cols, int batch, i
   template hipError_t embed_gather_ld<T>(const int32_t*, int64_t, int, int, const T*, int, int, float*, int*,       \
                                          hipStream_t);                                                              \
   template hipError_t rmsnorm_fwd<T>(const float*, int64_t, int, const float*, float, T*, float*, T*, int, int64_t, \
-                                     hipStream_t);                                                                  \
+                                     float*, hipStream_t);                                                                  \
   template hipError_t rmsnorm_bwd<T>(const float*, const float*, int64_t, int, const float*, const float*,          \
                                      const float*, float*, T*, hipStream_t);                                        \
   template hipError_t convert_rows<T>(const float*, int64_t, int, T*, T*, int, int64_t, hipStream_t);               \

@@ -113,7 +113,7 @@ struct ttt_ctx {
   int64_t pending_n = 0;
 
   // per-kernel-class device time (HIP events around each launch) while profiling is on
-  bool prof = false;
+  uint32_t prof = 0;  // bit i: time launches of class i
   std::vector<hipEvent_t> ev_pool;
   size_t ev_used = 0;
   struct ProfRec {
@@ -181,7 +181,7 @@ hipEvent_t next_event(ttt_ctx* c) {
 // run `launch` (returns hipError_t); with profiling on, bracket it with events
 template <typename F>
 hipError_t timed(ttt_ctx* c, int cls, double flops, hipStream_t st, F&& launch) {
-  if (!c->prof) return launch();
+  if (!(c->prof & (1u << cls))) return launch();
   hipEvent_t a = next_event(c), b = next_event(c);
   if (!a || !b) return hipErrorOutOfMemory;
   hipError_t e = hipEventRecord(a, st);
@@ -282,9 +282,8 @@ int layer_fwd(ttt_ctx* c, int l, float* h, int n, int64_t p0, int mode, TopActs*
   const int64_t M = (int64_t)B * n;
   const LayerW& w = c->lw[l];
   if (mode != MLP_ONLY) {
-    if (sv) CK(hipMemcpyAsync(sv->h_in, h, M * d * 4, hipMemcpyDeviceToDevice, c->stream));
     CK(rmsnorm_fwd<T>(h, M, d, w.attn_norm, (float)c->cfg.rms_eps, tp<T>(c->ub), sv ? sv->rstd1 : c->rstd_tmp,
-                      (T*)nullptr, n, 0, c->stream));
+                      (T*)nullptr, n, 0, sv ? sv->h_in : nullptr, c->stream));
     GemmArgs g = mk(c->ub, d, w.wqkv, d, (int)M, 3 * d, d);
     g.e.kind = EPI_F32;
     g.e.c = c->qkvb;
@@ -327,9 +326,8 @@ int layer_fwd(ttt_ctx* c, int l, float* h, int n, int64_t p0, int mode, TopActs*
     CK(Ops<T>::gemm(c, go));
     if (mode == ATTN_ONLY) return TTT_OK;
   }
-  if (sv) CK(hipMemcpyAsync(sv->h_mid, h, M * d * 4, hipMemcpyDeviceToDevice, c->stream));
   CK(rmsnorm_fwd<T>(h, M, d, w.mlp_norm, (float)c->cfg.rms_eps, tp<T>(c->ub), sv ? sv->rstd2 : c->rstd_tmp,
-                    sv ? tp<T>(sv->mT) : (T*)nullptr, n, c->b, c->stream));
+                    sv ? tp<T>(sv->mT) : (T*)nullptr, n, c->b, sv ? sv->h_mid : nullptr, c->stream));
   if (l >= c->l0) {
     const FastW& fw = c->fw[l - c->l0];
     GemmArgs g = mk(c->ub, d, fw.wgu, d, n, c->il ? 2 * f : f, d);
@@ -403,7 +401,7 @@ int top_chunk(ttt_ctx* c, const int32_t* tgt, int64_t ld, const float* hsrc, int
     if (rc) return rc;
   }
   CK(rmsnorm_fwd<T>(c->htop, M, d, c->final_norm, (float)c->cfg.rms_eps, tp<T>(c->hf), c->rstdf, (T*)nullptr, n, 0,
-                    c->stream));
+                    nullptr, c->stream));
   GemmArgs gl = mk(c->hf, d, c->lm_head, d, (int)M, V, d);
   gl.e.kind = EPI_F32;
   gl.e.c = c->logits;
@@ -583,7 +581,7 @@ int decode_step(ttt_ctx* c, int32_t* tok, int64_t ld) {
     if (rc) return rc;
   }
   CK(rmsnorm_fwd<T>(c->hb, B, d, c->final_norm, (float)c->cfg.rms_eps, tp<T>(c->hf), c->rstd_tmp, (T*)nullptr, 1, 0,
-                    c->stream));
+                    nullptr, c->stream));
   GemmArgs gl = mk(c->hf, d, c->lm_head, d, B, c->V, d);
   gl.e.kind = EPI_F32;
   gl.e.c = c->logits;
@@ -968,7 +966,7 @@ int ttt_create(const ttt_config* cfg, const ttt_weights* w, void* hip_stream, tt
 int ttt_profile_enable(ttt_ctx* c, int32_t on) {
   if (!c) return TTT_EINVAL;
   CK(hipStreamSynchronize(c->stream));
-  c->prof = on != 0;
+  c->prof = (uint32_t)on & ((1u << PC_N) - 1);
   c->prof_recs.clear();
   c->ev_used = 0;
   return TTT_OK;

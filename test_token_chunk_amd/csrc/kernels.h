@@ -85,10 +85,11 @@ int gemm_mfma_splits(const GemmArgs& g, int* ks_out);          // split-K parts 
 template <typename T>
 hipError_t embed_gather_ld(const int32_t* ids, int64_t ld, int B, int n, const T* E, int d, int V, float* h,
                            int* err, hipStream_t s);
-// y = g * x / sqrt(mean(x^2) + eps) as T (optional), rstd (optional), transposed copy yT [B][d][ldT] (optional)
+// y = g * x / sqrt(mean(x^2) + eps) as T (optional), rstd (optional), transposed copy yT [B][d][ldT] (optional),
+// a copy of x itself (optional)
 template <typename T>
 hipError_t rmsnorm_fwd(const float* x, int64_t M, int d, const float* g, float eps, T* y, float* rstd, T* yT,
-                       int rows_per_batch, int64_t ldT, hipStream_t s);
+                       int rows_per_batch, int64_t ldT, float* xcopy, hipStream_t s);
 // out = resid + RMSNorm-backward(dy) (resid may be null, out may alias resid); outT: T copy of out (optional)
 template <typename T>
 hipError_t rmsnorm_bwd(const float* x, const float* rstd, int64_t M, int d, const float* g, const float* dy,
