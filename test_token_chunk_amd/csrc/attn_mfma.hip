@@ -41,6 +41,16 @@ __device__ __forceinline__ uint32_t pk2(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// 2^x with one v_exp_f32 (results below 2^-126 flush to zero, which no probability here
+// resolves anyway); exp2f adds a denormal-range fix-up of five more instructions
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ring slot s0 + r for a slot s0 < R and an offset 0 <= r < R, without a division
+__device__ __forceinline__ int ring_add(int s0, int r, int R) {
+  const int s = s0 + r;
+  return s >= R ? s - R : s;
+}
+
 // SPLIT: blockIdx.z = b * S + split; the block covers only its share of the key tiles
 // and writes unnormalized O, the reference max (raw score units) and the exp-sum to the
 // workspace: O [S][B][H][n][hd], m [S][B][H][n], l [S][B][H][n].
@@ -108,12 +118,12 @@ __global__ __launch_bounds__(NW * 64) void k_swa_fwd(AttnArgs a, int S) {
 #define LOADK(i, dst)                                                              \
   if constexpr (KCH > i) {                                                         \
     const int c = tid + i * NT, r = c / (HD / 8), col = (c % (HD / 8)) * 8;        \
-    if (c < KT * HD / 8) dst = *(const uint4*)(Kr + (int64_t)((slot0 + r) % R) * HD + col); \
+    if (c < KT * HD / 8) dst = *(const uint4*)(Kr + (int64_t)ring_add(slot0, r, R) * HD + col); \
   }
 #define LOADV(i, dst)                                                              \
   if constexpr (VCH > i) {                                                         \
     const int c = tid + i * NT, r = c / (KT / 8), col = (c % (KT / 8)) * 8;        \
-    if (c < KT * HD / 8) dst = *(const uint4*)(Vt + (int64_t)r * R + (slot0 + col) % R); \
+    if (c < KT * HD / 8) dst = *(const uint4*)(Vt + (int64_t)r * R + ring_add(slot0, col, R)); \
   }
 #define LOAD_TILE(it_)                                                             \
   {                                                                                \
@@ -233,8 +243,8 @@ __global__ __launch_bounds__(NW * 64) void k_swa_fwd(AttnArgs a, int S) {
     uint32_t pa[8], pb[8];
 #pragma unroll
     for (int r = 0; r < 16; r += 2) {
-      pa[r >> 1] = pk2(exp2f(fmaf(s0[r], sl2, nb)), exp2f(fmaf(s0[r + 1], sl2, nb)));
-      pb[r >> 1] = pk2(exp2f(fmaf(s1[r], sl2, nb)), exp2f(fmaf(s1[r + 1], sl2, nb)));
+      pa[r >> 1] = pk2(ex2(fmaf(s0[r], sl2, nb)), ex2(fmaf(s0[r + 1], sl2, nb)));
+      pb[r >> 1] = pk2(ex2(fmaf(s1[r], sl2, nb)), ex2(fmaf(s1[r + 1], sl2, nb)));
       psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pa[r >> 1]), ones, psum, false);
       psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pb[r >> 1]), ones, psum, false);
     }
@@ -449,11 +459,11 @@ __global__ __launch_bounds__(NW * 64) void k_swa_dq(AttnBwdArgs a, int S) {
   if constexpr (KCH > i) {                                                               \
     const int c = tid + i * NT, r = c / (HD / 8), col = (c % (HD / 8)) * 8;              \
     if (c < KT * HD / 8) {                                                               \
-      const int64_t off = (int64_t)((slot0 + r) % R) * HD + col;                         \
+      const int64_t off = (int64_t)ring_add(slot0, r, R) * HD + col;                         \
       dk = *(const uint4*)(Kr + off);                                                    \
       dv = *(const uint4*)(Vr + off);                                                    \
       if constexpr (TR)                                                                  \
-        dt = *(const uint4*)(Kt + (int64_t)(c / (KT / 8)) * R + (slot0 + (c % (KT / 8)) * 8) % R); \
+        dt = *(const uint4*)(Kt + (int64_t)(c / (KT / 8)) * R + ring_add(slot0, (c % (KT / 8)) * 8, R)); \
     }                                                                                    \
   }
 #define LOAD_TILE(it_)                                                                   \
@@ -525,8 +535,8 @@ __global__ __launch_bounds__(NW * 64) void k_swa_dq(AttnBwdArgs a, int S) {
       uint32_t da[8];
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
-        const float x0 = exp2f(fmaf(s0[r], sl2, nlse2)) * (p0[r] - Dq);
-        const float x1 = exp2f(fmaf(s0[r + 1], sl2, nlse2)) * (p0[r + 1] - Dq);
+        const float x0 = ex2(fmaf(s0[r], sl2, nlse2)) * (p0[r] - Dq);
+        const float x1 = ex2(fmaf(s0[r + 1], sl2, nlse2)) * (p0[r + 1] - Dq);
         da[r >> 1] = pk2(x0, x1);
       }
       const bf16x8 ds0 = __builtin_bit_cast(bf16x8, make_uint4(da[0], da[1], da[2], da[3]));
@@ -704,7 +714,7 @@ __global__ __launch_bounds__(256) void k_swa_dkv(AttnBwdArgs a, int P) {
           const int row = hf * 32 + 8 * (rr >> 2) + 4 * g + (rr & 3);
           const int t = tq0 + row;
           const bool ok = kok && t < a.n && t >= sk && t - sk < a.window;
-          const float p = ok ? exp2f(s0[rr] * sl2 - sm.lse2[row]) : 0.f;
+          const float p = ok ? ex2(s0[rr] * sl2 - sm.lse2[row]) : 0.f;
           pv[u] = p;
           dsv[u] = p * (p0[rr] - sm.dd[row]);
         }
