@@ -336,6 +336,63 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(GemmArgs g) {
 
 constexpr int DL_TILE_BYTES = (128 + 128) * BK * 2;  // one stage: A and B tiles
 
+// Fused SGD step of the 128 x 128 loop with the MFMA operands swapped (lane = output row m,
+// four consecutive columns n per register group): the fp32 master values of the tile are
+// loaded into registers before the main loop (their latency hides behind it), then
+// master -= lr * acc is stored as 16-byte row segments, the row-major shadow as 8-byte
+// segments and the transposed shadow through LDS as 16-byte segments.
+__device__ __forceinline__ void dl_sgd_prefetch(const GemmArgs& g, float4 (&pre)[2][2][4], int m0, int n0, int wm0,
+                                                int wn0, int lane, int bz) {
+  const int lr = lane & 31, hi = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int m = m0 + wm0 + i * 32 + lr, n = n0 + wn0 + j * 32 + 8 * q + 4 * hi;
+        pre[i][j][q] = *(const float4*)(g.e.master + bz * g.e.sm + (int64_t)m * g.e.ldm + n);
+      }
+}
+
+__device__ __forceinline__ void dl_sgd_epilogue(const GemmArgs& g, f32x16 (&acc)[2][2], const float4 (&pre)[2][2][4],
+                                                unsigned char* smem_raw, int m0, int n0, int wm0, int wn0, int tid,
+                                                int bz) {
+  constexpr int BM = 128, BN = 128, TLD = BM + 8;
+  const int lane = tid & 63, lr = lane & 31, hi = lane >> 5;
+  const Epi& e = g.e;
+  bf16* tr = reinterpret_cast<bf16*>(smem_raw);  // [BN][TLD]: tile row n holds BM consecutive m
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int ml = wm0 + i * 32 + lr, m = m0 + ml;
+    const int64_t shrow = e.il_f ? swiglu_il_row(m, e.il_f) : m;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int nl = wn0 + j * 32 + 8 * q + 4 * hi, n = n0 + nl;
+        const float4 w = make_float4(pre[i][j][q].x - e.lr * acc[i][j][4 * q], pre[i][j][q].y - e.lr * acc[i][j][4 * q + 1],
+                                     pre[i][j][q].z - e.lr * acc[i][j][4 * q + 2],
+                                     pre[i][j][q].w - e.lr * acc[i][j][4 * q + 3]);
+        *(float4*)(e.master + bz * e.sm + (int64_t)m * e.ldm + n) = w;
+        const bf16 b0 = f2bf(w.x), b1 = f2bf(w.y), b2 = f2bf(w.z), b3 = f2bf(w.w);
+        *(uint2*)((bf16*)e.sh + bz * e.ssh + shrow * e.ldsh + n) =
+            make_uint2((uint32_t)b0.x | ((uint32_t)b1.x << 16), (uint32_t)b2.x | ((uint32_t)b3.x << 16));
+        tr[(nl + 0) * TLD + ml] = b0;
+        tr[(nl + 1) * TLD + ml] = b1;
+        tr[(nl + 2) * TLD + ml] = b2;
+        tr[(nl + 3) * TLD + ml] = b3;
+      }
+  }
+  __syncthreads();
+  bf16* dst = (bf16*)e.shT + bz * e.sshT;
+  constexpr int CH = BM / 8;
+  for (int c = tid; c < BN * CH; c += 256) {
+    const int nl = c / CH, ml = (c % CH) * 8;
+    *(uint4*)(dst + (int64_t)(n0 + nl) * e.ldshT + m0 + ml) = *(const uint4*)(tr + nl * TLD + ml);
+  }
+}
+
 template <int EK, int STAGES, bool SPLIT>
 __global__ __launch_bounds__(256) void k_gemm_dl(GemmArgs g) {
   constexpr int BM = 128, BN = 128, WM = 64, WN = 64, TM = 2, TN = 2;
@@ -375,6 +432,11 @@ __global__ __launch_bounds__(256) void k_gemm_dl(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
 
+  // fused SGD step (no K split): the master values of the tile, loaded ahead of the main loop
+  constexpr bool SGD = EK == EPI_SGD && !SPLIT;
+  float4 pre[SGD ? 2 : 1][SGD ? 2 : 1][SGD ? 4 : 1];
+  if constexpr (SGD) dl_sgd_prefetch(g, pre, m0, n0, wm0, wn0, lane, bz);
+
   const int lr = lane & 31, lk = (lane >> 5) * 8, sw = lr & 7;
   for (int st = 0; st < STAGES - 1 && st < nk; ++st) issue(st);
   for (int kt = 0; kt < nk; ++kt) {
@@ -401,12 +463,16 @@ __global__ __launch_bounds__(256) void k_gemm_dl(GemmArgs g) {
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = SGD ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0)
+                          : __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     }
   }
   WAIT_VM_LDS(0);
   __builtin_amdgcn_s_barrier();  // every wave is done with the operand buffers
-  gemm_epilogue<BM, BN, WM, WN, false, EK, SPLIT>(g, acc, accu, smem_raw, m0, n0, wm0, wn0, tid, bz, split, S);
+  if constexpr (SGD)
+    dl_sgd_epilogue(g, acc, pre, smem_raw, m0, n0, wm0, wn0, tid, bz);
+  else
+    gemm_epilogue<BM, BN, WM, WN, false, EK, SPLIT>(g, acc, accu, smem_raw, m0, n0, wm0, wn0, tid, bz, split, S);
 }
 
 // ------------------------------------------------------------------ wide tiles
