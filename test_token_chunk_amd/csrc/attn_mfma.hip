@@ -83,14 +83,19 @@ __global__ __launch_bounds__(NW * 64) void k_swa_fwd(AttnArgs a, int S) {
   const bf16* Kr = (const bf16*)a.kr + bh * R * HD;
   const bf16* Vt = (const bf16*)a.vtr + bh * HD * R;
 
-  // Q fragments (B operand of S^T = K Q^T): query lane%32, head dims 16*ks + 8g .. +7.
-  // Kept in named registers (an array here ends up in scratch memory).
+  // Q fragments (B operand of S^T = K Q^T): query lane%32, head dims 16*ks + 8g .. +7,
+  // pre-multiplied by log2(e)/sqrt(hd) (rounded to bf16) so that S^T comes out in log2
+  // units.  Kept in named registers (an array here ends up in scratch memory).
+  const float sl2 = 1.4426950408889634f / sqrtf((float)HD);  // log2(e) / sqrt(hd)
   bf16x8 q0, q1, q2, q3, q4, q5, q6, q7;
   {
     const bf16* q = (const bf16*)a.q + (bh * a.n + (qok ? tq : 0)) * HD + g * 8;
     auto ldq = [&](int ks) {
       uint4 v = qok ? *(const uint4*)(q + ks * 16) : make_uint4(0, 0, 0, 0);
-      return __builtin_bit_cast(bf16x8, v);
+      bf16x8 x = __builtin_bit_cast(bf16x8, v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = (__bf16)((float)x[e] * sl2);
+      return x;
     };
     q0 = ldq(0);
     q1 = ldq(1);
@@ -152,7 +157,6 @@ __global__ __launch_bounds__(NW * 64) void k_swa_fwd(AttnArgs a, int S) {
 #pragma unroll
   for (int i = 0; i < HM; ++i) o[i] = f32x16{};
   float mref = -INFINITY, lrun = 0.f;  // reference max (log2 units), this lane's row sum
-  const float sl2 = 1.4426950408889634f / sqrtf((float)HD);  // log2(e) / sqrt(hd)
   const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
 
   // Two wave groups in counter-phase.  The waves of a block move in lockstep between the
@@ -162,7 +166,6 @@ __global__ __launch_bounds__(NW * 64) void k_swa_fwd(AttnArgs a, int S) {
   // a SIMD works through its softmax on the vector ALUs, the other issues MFMAs.  V^T tiles
   // live in a ring of 3 (group B reads them one iteration late).
   const bool late = wid >= NW / 2;
-  uint32_t qa[8], qb[8];  // group B: probabilities of the previous tile
   if (it_beg < ntiles) {
     LOAD_TILE(it_beg)
     STORE_TILE(it_beg & 1, it_beg % 3)
@@ -186,16 +189,6 @@ __global__ __launch_bounds__(NW * 64) void k_swa_fwd(AttnArgs a, int S) {
       }                                                                                          \
     }                                                                                            \
   }
-  for (int it = it_beg; it < ntiles; ++it) {
-    const int cur = it & 1;
-    if (it + 1 < ntiles) LOAD_TILE(it + 1)
-    const int64_t kp0 = ktile0 + (int64_t)it * KT;
-    if (late && it > it_beg) PV((it - 1) % 3, qa, qb)
-    // S^T for the two 32-key halves of the tile
-    f32x16 s0 = f32x16{}, s1 = f32x16{};
-    {
-      const bf16* k0p = &sm.k[cur][(lane & 31)][g * 8];
-      const bf16* k1p = &sm.k[cur][32 + (lane & 31)][g * 8];
 #define SSTEP(ks, qv)                                                         \
   if constexpr (KS > ks) {                                                    \
     bf16x8 k0 = *(const bf16x8*)(k0p + ks * 16);                              \
@@ -203,65 +196,101 @@ __global__ __launch_bounds__(NW * 64) void k_swa_fwd(AttnArgs a, int S) {
     s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qv, s0, 0, 0, 0);       \
     s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qv, s1, 0, 0, 0);       \
   }
-      SSTEP(0, q0) SSTEP(1, q1) SSTEP(2, q2) SSTEP(3, q3) SSTEP(4, q4) SSTEP(5, q5) SSTEP(6, q6) SSTEP(7, q7)
-#undef SSTEP
-    }
-    // register 4j+i of half mt holds key kp0 + 32 mt + 8 j + 4 g + i.  Visible keys:
-    // qpos - window < key <= qpos.  Only tiles that cut a window edge for some query of
-    // this wave (or waves with out-of-range queries) need the per-element mask.
-    const bool full = wfull && kp0 >= wpos_hi - a.window + 1 && kp0 + KT - 1 <= wpos_lo;
-    if (!full) {
-      const int64_t hi64 = qpos - kp0, lo64 = qpos - a.window - kp0;
-      const int hi = !qok ? -1 : hi64 < -1 ? -1 : hi64 > 64 ? 64 : (int)hi64;
-      const int lo = lo64 < -2 ? -2 : lo64 > 64 ? 64 : (int)lo64;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int off = 8 * (r >> 2) + 4 * g + (r & 3);
-        if (!(off <= hi && off > lo)) s0[r] = -INFINITY;
-        if (!(off + 32 <= hi && off + 32 > lo)) s1[r] = -INFINITY;
-      }
-    }
-    // lazy reference max (log2 units): it moves only when the tile's max passes it by more
-    // than 8, so exponentials stay <= 2^8 and O is rarely rescaled (the result does not
-    // depend on the reference); the pair of lanes of a query shares it
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, fmaxf(s0[r], s1[r]));
-    float corr = 1.f;
-    if (__any(tmax * sl2 > mref + 8.f)) {
-      const float pmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * sl2;
-      const float mnew = pmax > mref + 8.f ? pmax : mref;
-      corr = mnew == mref ? 1.f : exp2f(mref - mnew);
-      mref = mnew;
-#pragma unroll
-      for (int i = 0; i < HM; ++i) o[i] *= corr;
-    }
-    const float nb = mref == -INFINITY ? 0.f : -mref;
-    // row sums: dot products of the bf16 probabilities that feed the PV product, per lane
-    // (the pair's sums are added at the end)
-    float psum = 0.f;
-    uint32_t pa[8], pb[8];
-#pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-      pa[r >> 1] = pk2(ex2(fmaf(s0[r], sl2, nb)), ex2(fmaf(s0[r + 1], sl2, nb)));
-      pb[r >> 1] = pk2(ex2(fmaf(s1[r], sl2, nb)), ex2(fmaf(s1[r + 1], sl2, nb)));
-      psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pa[r >> 1]), ones, psum, false);
-      psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pb[r >> 1]), ones, psum, false);
-    }
-    lrun = lrun * corr + psum;
-    if (late) {
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        qa[r] = pa[r];
-        qb[r] = pb[r];
-      }
-    } else {
-      PV(it % 3, pa, pb)
-    }
-    if (it + 1 < ntiles) STORE_TILE(cur ^ 1, (it + 1) % 3)
-    __syncthreads();
+#define FWD_TILE(it, PA, PB, QA, QB) \
+  { \
+    const int cur = it & 1; \
+    if (it + 1 < ntiles) LOAD_TILE(it + 1) \
+    const int64_t kp0 = ktile0 + (int64_t)it * KT; \
+    if (late && it > it_beg) PV((it - 1) % 3, QA, QB) \
+    /* S^T - reference for the two 32-key halves of the tile: the accumulators start at */ \
+    /* minus this lane's (this query's) reference, so the exponent needs no extra operation */ \
+    const float nb0 = mref == -INFINITY ? 0.f : -mref; \
+    f32x16 s0, s1; \
+_Pragma("unroll") \
+    for (int r = 0; r < 16; ++r) { \
+      s0[r] = nb0; \
+      s1[r] = nb0; \
+    } \
+    { \
+      const bf16* k0p = &sm.k[cur][(lane & 31)][g * 8]; \
+      const bf16* k1p = &sm.k[cur][32 + (lane & 31)][g * 8]; \
+      SSTEP(0, q0) SSTEP(1, q1) SSTEP(2, q2) SSTEP(3, q3) SSTEP(4, q4) SSTEP(5, q5) SSTEP(6, q6) SSTEP(7, q7) \
+    } \
+    /* register 4j+i of half mt holds key kp0 + 32 mt + 8 j + 4 g + i.  Visible keys: */ \
+    /* qpos - window < key <= qpos.  Only tiles that cut a window edge for some query of */ \
+    /* this wave (or waves with out-of-range queries) need the per-element mask. */ \
+    const bool full = wfull && kp0 >= wpos_hi - a.window + 1 && kp0 + KT - 1 <= wpos_lo; \
+    if (!full) { \
+      const int64_t hi64 = qpos - kp0, lo64 = qpos - a.window - kp0; \
+      const int hi = !qok ? -1 : hi64 < -1 ? -1 : hi64 > 64 ? 64 : (int)hi64; \
+      const int lo = lo64 < -2 ? -2 : lo64 > 64 ? 64 : (int)lo64; \
+_Pragma("unroll") \
+      for (int r = 0; r < 16; ++r) { \
+        const int off = 8 * (r >> 2) + 4 * g + (r & 3); \
+        if (!(off <= hi && off > lo)) s0[r] = -INFINITY; \
+        if (!(off + 32 <= hi && off + 32 > lo)) s1[r] = -INFINITY; \
+      } \
+    } \
+    /* lazy reference max (log2 units): it moves only when the tile's max passes it by more */ \
+    /* than 8, so exponentials stay <= 2^8 and O is rarely rescaled (the result does not */ \
+    /* depend on the reference); the pair of lanes of a query shares it.  The first tile */ \
+    /* (no reference yet) always sets it. */ \
+    float tmax = -INFINITY; \
+_Pragma("unroll") \
+    for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, fmaxf(s0[r], s1[r])); \
+    float corr = 1.f; \
+    if (__any(tmax > 8.f || mref == -INFINITY)) { \
+      /* what the accumulators had subtracted */ \
+      const float base = mref == -INFINITY ? 0.f : mref; \
+      const float pmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) + base; \
+      const float mnew = (mref == -INFINITY || pmax > mref + 8.f) ? pmax : mref; \
+      corr = mnew == mref ? 1.f : exp2f(mref - mnew); \
+      mref = mnew; \
+      const float shift = mnew == -INFINITY ? 0.f : base - mnew; \
+_Pragma("unroll") \
+      for (int r = 0; r < 16; ++r) { \
+        s0[r] += shift; \
+        s1[r] += shift; \
+      } \
+_Pragma("unroll") \
+      for (int i = 0; i < HM; ++i) o[i] *= corr; \
+    } \
+    /* row sums: dot products of the bf16 probabilities that feed the PV product, per lane */ \
+    /* (the pair's sums are added at the end) */ \
+    float psum = 0.f; \
+_Pragma("unroll") \
+    for (int r = 0; r < 16; r += 2) { \
+      PA[r >> 1] = pk2(ex2(s0[r]), ex2(s0[r + 1])); \
+      PB[r >> 1] = pk2(ex2(s1[r]), ex2(s1[r + 1])); \
+      psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, PA[r >> 1]), ones, psum, false); \
+      psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, PB[r >> 1]), ones, psum, false); \
+    } \
+    lrun = lrun * corr + psum; \
+    if (!late) PV(it % 3, PA, PB) \
+    if (it + 1 < ntiles) STORE_TILE(cur ^ 1, (it + 1) % 3) \
+    __syncthreads(); \
   }
-  if (late && it_beg < ntiles) PV((ntiles - 1) % 3, qa, qb)
+  // P of a tile in (pa, pb) or (qa, qb), alternating, so that group B keeps the previous
+  // tile's probabilities without copying them
+  uint32_t pa[8], pb[8], qa[8], qb[8];
+  for (int it2 = it_beg; it2 < ntiles; it2 += 2) {
+    {
+      const int it = it2;
+      FWD_TILE(it, pa, pb, qa, qb)
+    }
+    if (it2 + 1 < ntiles) {
+      const int it = it2 + 1;
+      FWD_TILE(it, qa, qb, pa, pb)
+    }
+  }
+#undef FWD_TILE
+#undef SSTEP
+  if (late && it_beg < ntiles) {
+    if ((ntiles - it_beg) & 1)
+      PV((ntiles - 1) % 3, pa, pb)
+    else
+      PV((ntiles - 1) % 3, qa, qb)
+  }
 #undef PV
 
 #undef LOADK
