@@ -845,6 +845,177 @@ __global__ __launch_bounds__(256) void k_heads_transpose(const bf16* __restrict_
   }
 }
 
+// dQ with the K, V and K^T tiles copied straight from global memory into LDS
+// (global_load_lds: lane L of a wave writes 16 bytes at the wave's LDS address + 16 L), two
+// stages, no staging registers.  Rows are unpadded; the 16-byte chunks of a K or V row are
+// XOR-swizzled by row % (hd/8) and those of a K^T row by row % 8, which keeps the fragment
+// reads of a wave on distinct banks.  Needs the transposed key ring; otherwise as k_swa_dq.
+template <int HD>
+constexpr int dq2_stage_bytes() { return 3 * KT * HD * 2; }
+
+template <int HD, bool SPLIT>
+__global__ __launch_bounds__(512) void k_swa_dq2(AttnBwdArgs a, int S) {
+  constexpr int NW = 8, BQn = NW * QW;
+  constexpr int KS = HD / 16, HM = HD / 32;
+  constexpr int CPR = HD / 8;              // 16-byte chunks per K / V row
+  constexpr int RPK = 1024 / (HD * 2);     // K / V rows per 1 KB copy
+  constexpr int TB = KT * HD * 2 / 1024;   // 1 KB copies per tile (K, V and K^T each)
+  constexpr int TBW = TB / NW;             // per wave
+  constexpr int SB = dq2_stage_bytes<HD>();
+  constexpr int VOFF = KT * HD * 2, TOFF = 2 * KT * HD * 2;
+  static_assert(TB % NW == 0 && CPR * 16 == HD * 2 && 32 % CPR == 0, "tile copy layout");
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, g = lane >> 5, l32 = lane & 31;
+  const int b = SPLIT ? blockIdx.z / S : blockIdx.z, h = blockIdx.y;
+  const int sp = SPLIT ? blockIdx.z % S : 0;
+  const int64_t bh = (int64_t)b * a.H + h;
+  const int R = a.R, d = a.H * HD;
+  const int t0 = blockIdx.x * BQn;
+  const int tq = t0 + wid * QW + l32;
+  const bool qok = tq < a.n;
+  const int64_t qpos = a.pos0 + tq;
+  const int tw0 = t0 + wid * QW;
+  const bool wfull = tw0 + QW <= a.n;
+  const int64_t wpos_lo = a.pos0 + tw0, wpos_hi = wpos_lo + QW - 1;
+  const bf16* Kr = (const bf16*)a.kr + bh * R * HD;
+  const bf16* Vr = (const bf16*)a.vr + bh * R * HD;
+  const bf16* Kt = (const bf16*)a.ktr + bh * HD * R;
+
+  bf16x8 q0, q1, q2, q3, q4, q5, q6, q7, e0, e1, e2, e3, e4, e5, e6, e7;
+  {
+    const bf16* q = (const bf16*)a.q + (bh * a.n + (qok ? tq : 0)) * HD + g * 8;
+    const bf16* dO = (const bf16*)a.dout + ((int64_t)b * a.n + (qok ? tq : 0)) * d + (int64_t)h * HD + g * 8;
+    auto ld8 = [&](const bf16* p, int ks) {
+      uint4 v = qok ? *(const uint4*)(p + ks * 16) : make_uint4(0, 0, 0, 0);
+      return __builtin_bit_cast(bf16x8, v);
+    };
+    q0 = ld8(q, 0); q1 = ld8(q, 1); e0 = ld8(dO, 0); e1 = ld8(dO, 1);
+    if constexpr (KS > 2) { q2 = ld8(q, 2); q3 = ld8(q, 3); e2 = ld8(dO, 2); e3 = ld8(dO, 3); }
+    if constexpr (KS > 4) { q4 = ld8(q, 4); q5 = ld8(q, 5); e4 = ld8(dO, 4); e5 = ld8(dO, 5); }
+    if constexpr (KS > 6) { q6 = ld8(q, 6); q7 = ld8(q, 7); e6 = ld8(dO, 6); e7 = ld8(dO, 7); }
+  }
+  const float LOG2E = 1.4426950408889634f;
+  const float sl2 = LOG2E / sqrtf((float)HD);
+  const float nlse2 = qok ? -a.lse[bh * a.n + tq] * LOG2E : 0.f;
+  const float Dq = qok ? a.dvec[bh * a.n + tq] : 0.f;
+
+  const int tlast = min(t0 + BQn, a.n) - 1;
+  const int64_t kbeg = max((int64_t)0, a.pos0 + t0 - a.window + 1);
+  const int64_t kend = a.pos0 + tlast;
+  const int64_t ktile0 = (kbeg / KT) * KT;
+  const int ntiles_all = (int)((kend - ktile0) / KT) + 1;
+  const int per = SPLIT ? (ntiles_all + S - 1) / S : ntiles_all;
+  const int it_beg = SPLIT ? min(ntiles_all, sp * per) : 0;
+  const int ntiles = SPLIT ? min(ntiles_all, it_beg + per) : ntiles_all;
+  const int sbase = (int)(ktile0 % R);
+
+  // copies of tile it_ into stage st: K and V rows by ring slot, K^T rows (head dims) of
+  // 64 consecutive slots (tiles start at multiples of 64 positions and R % 8 == 0, so an
+  // 8-key chunk never wraps)
+  auto issue = [&](int it_, int st) {
+    const int slot0 = (sbase + it_ * KT) % R;
+    unsigned char* base = smem_raw + st * SB;
+#pragma unroll
+    for (int u = 0; u < TBW; ++u) {
+      const int j = wid * TBW + u;
+      const int row = j * RPK + lane / CPR, c = (lane % CPR) ^ (row % CPR);
+      const int64_t off = (int64_t)ring_add(slot0, row, R) * HD + c * 8;
+      __builtin_amdgcn_global_load_lds(Kr + off, LDSP(base + j * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(Vr + off, LDSP(base + VOFF + j * 1024), 16, 0, 0);
+      const int trow = j * 8 + (lane >> 3), tc = (lane & 7) ^ (trow & 7);
+      __builtin_amdgcn_global_load_lds(Kt + (int64_t)trow * R + ring_add(slot0, tc * 8, R),
+                                       LDSP(base + TOFF + j * 1024), 16, 0, 0);
+    }
+  };
+
+  f32x16 acc[HM];
+#pragma unroll
+  for (int i = 0; i < HM; ++i) acc[i] = f32x16{};
+  const int xr = l32 % CPR, xt = l32 & 7;
+  if (it_beg < ntiles) issue(it_beg, it_beg & 1);
+  WAIT_VM_LDS(0);
+  __syncthreads();
+  for (int it = it_beg; it < ntiles; ++it) {
+    const int cur = it & 1;
+    if (it + 1 < ntiles) issue(it + 1, cur ^ 1);
+    const unsigned char* stg = smem_raw + cur * SB;
+    const int64_t kp0 = ktile0 + (int64_t)it * KT;
+    const bool full = wfull && kp0 >= wpos_hi - a.window + 1 && kp0 + KT - 1 <= wpos_lo;
+    const int64_t hi64 = qpos - kp0, lo64 = qpos - a.window - kp0;
+    const int hi = !qok ? -1 : hi64 < -1 ? -1 : hi64 > 64 ? 64 : (int)hi64;
+    const int lo = lo64 < -2 ? -2 : lo64 > 64 ? 64 : (int)lo64;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      f32x16 s0 = f32x16{}, p0 = f32x16{};
+      const unsigned char* krow = stg + (hf * 32 + l32) * (HD * 2);
+#define SSTEP(ks, qv, ev)                                                                          \
+  if constexpr (KS > ks) {                                                                         \
+    const int co = (((2 * ks + g) ^ xr) << 4);                                                     \
+    s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(krow + co), qv, s0, 0, 0, 0);    \
+    p0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(krow + VOFF + co), ev, p0, 0, 0, 0); \
+  }
+      SSTEP(0, q0, e0) SSTEP(1, q1, e1) SSTEP(2, q2, e2) SSTEP(3, q3, e3)
+      SSTEP(4, q4, e4) SSTEP(5, q5, e5) SSTEP(6, q6, e6) SSTEP(7, q7, e7)
+#undef SSTEP
+      if (!full) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int off = hf * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+          if (!(off <= hi && off > lo)) s0[r] = -INFINITY;
+        }
+      }
+      uint32_t da[8];
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const float x0 = ex2(fmaf(s0[r], sl2, nlse2)) * (p0[r] - Dq);
+        const float x1 = ex2(fmaf(s0[r + 1], sl2, nlse2)) * (p0[r + 1] - Dq);
+        da[r >> 1] = pk2(x0, x1);
+      }
+      const bf16x8 ds0 = __builtin_bit_cast(bf16x8, make_uint4(da[0], da[1], da[2], da[3]));
+      const bf16x8 ds1 = __builtin_bit_cast(bf16x8, make_uint4(da[4], da[5], da[6], da[7]));
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const int ch = hf * 4 + st * 2;  // 16-byte chunk of keys hf*32 + st*16 .. +7
+#pragma unroll
+        for (int hm = 0; hm < HM; ++hm) {
+          const unsigned char* trow = stg + TOFF + (hm * 32 + l32) * (KT * 2) + 8 * g;
+          const uint2 lo2 = *(const uint2*)(trow + ((ch ^ xt) << 4));
+          const uint2 hi2 = *(const uint2*)(trow + (((ch + 1) ^ xt) << 4));
+          const bf16x8 kf = __builtin_bit_cast(bf16x8, make_uint4(lo2.x, lo2.y, hi2.x, hi2.y));
+          acc[hm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, st ? ds1 : ds0, acc[hm], 0, 0, 0);
+        }
+      }
+    }
+    WAIT_VM_LDS(0);
+    __syncthreads();
+  }
+  if (!qok) return;
+  const float sc = 1.f / sqrtf((float)HD);
+  float* out = (SPLIT ? a.ws + (int64_t)sp * a.B * a.n * d : a.dq) + ((int64_t)b * a.n + tq) * d + (int64_t)h * HD;
+#pragma unroll
+  for (int hm = 0; hm < HM; ++hm)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int d0 = hm * 32 + 8 * j + 4 * g;
+      *(float4*)(out + d0) = make_float4(acc[hm][4 * j] * sc, acc[hm][4 * j + 1] * sc, acc[hm][4 * j + 2] * sc,
+                                         acc[hm][4 * j + 3] * sc);
+    }
+}
+
+template <int HD, bool SPLIT>
+hipError_t launch_dq2(const AttnBwdArgs& a, int S, hipStream_t s) {
+  static bool attr = false;
+  if (!attr) {
+    hipError_t e = hipFuncSetAttribute((const void*)k_swa_dq2<HD, SPLIT>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       2 * dq2_stage_bytes<HD>());
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  hipLaunchKernelGGL((k_swa_dq2<HD, SPLIT>), dim3(cdiv(a.n, 8 * QW), a.H, a.B * S), dim3(512),
+                     2 * dq2_stage_bytes<HD>(), s, a, S);
+  return hipGetLastError();
+}
+
 template <int HD, int NW, bool SPLIT, bool TR>
 hipError_t launch_dq(const AttnBwdArgs& a, int S, hipStream_t s) {
   static bool attr = false;
@@ -886,13 +1057,17 @@ hipError_t launch_bwd(const AttnBwdArgs& a, hipStream_t s) {
   const int64_t ntiles = (std::min<int64_t>(a.window, a.pos0 + 1) + 8 * QW) / KT + 1;
   const int64_t total = (int64_t)a.B * a.n * a.H * HD;
   const int S = attn_splits(blocks8, ntiles, total, a.ws, a.ws_floats);
+  // the direct-to-LDS form (measured faster at head dim 128, slower at 64)
+  constexpr bool DQ2 = HD == 128;
   if (S > 1) {
-    e = tr ? launch_dq<HD, 8, true, true>(a, S, s) : launch_dq<HD, 8, true, false>(a, S, s);
+    if constexpr (DQ2) e = tr ? launch_dq2<HD, true>(a, S, s) : launch_dq<HD, 8, true, false>(a, S, s);
+    else e = tr ? launch_dq<HD, 8, true, true>(a, S, s) : launch_dq<HD, 8, true, false>(a, S, s);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_dq_reduce, dim3((unsigned)std::min<int64_t>(cdiv(total / 4, 256), 8192)), dim3(256), 0, s,
                        a.ws, S, total, a.dq);
   } else {
-    e = tr ? launch_dq<HD, 8, false, true>(a, 1, s) : launch_dq<HD, 8, false, false>(a, 1, s);
+    if constexpr (DQ2) e = tr ? launch_dq2<HD, false>(a, 1, s) : launch_dq<HD, 8, false, false>(a, 1, s);
+    else e = tr ? launch_dq<HD, 8, false, true>(a, 1, s) : launch_dq<HD, 8, false, false>(a, 1, s);
     if (e != hipSuccess) return e;
   }
   // dK/dV: split each key block's query range when the grid is small (ordered sum after);
