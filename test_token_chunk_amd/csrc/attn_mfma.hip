@@ -848,7 +848,7 @@ __global__ __launch_bounds__(256) void k_heads_transpose(const bf16* __restrict_
 // dQ with the K, V and K^T tiles copied straight from global memory into LDS
 // (global_load_lds: lane L of a wave writes 16 bytes at the wave's LDS address + 16 L), two
 // stages, no staging registers.  Rows are unpadded; the 16-byte chunks of a K or V row are
-// XOR-swizzled by row % (hd/8) and those of a K^T row by row % 8, which keeps the fragment
+// XOR-swizzled by row % (hd/8) and those of a K^T row by (row / 2) % 8, which keeps the fragment
 // reads of a wave on distinct banks.  Needs the transposed key ring; otherwise as k_swa_dq.
 template <int HD>
 constexpr int dq2_stage_bytes() { return 3 * KT * HD * 2; }
@@ -922,7 +922,7 @@ __global__ __launch_bounds__(512) void k_swa_dq2(AttnBwdArgs a, int S) {
       const int64_t off = (int64_t)ring_add(slot0, row, R) * HD + c * 8;
       __builtin_amdgcn_global_load_lds(Kr + off, LDSP(base + j * 1024), 16, 0, 0);
       __builtin_amdgcn_global_load_lds(Vr + off, LDSP(base + VOFF + j * 1024), 16, 0, 0);
-      const int trow = j * 8 + (lane >> 3), tc = (lane & 7) ^ (trow & 7);
+      const int trow = j * 8 + (lane >> 3), tc = (lane & 7) ^ ((trow >> 1) & 7);
       __builtin_amdgcn_global_load_lds(Kt + (int64_t)trow * R + ring_add(slot0, tc * 8, R),
                                        LDSP(base + TOFF + j * 1024), 16, 0, 0);
     }
@@ -931,7 +931,7 @@ __global__ __launch_bounds__(512) void k_swa_dq2(AttnBwdArgs a, int S) {
   f32x16 acc[HM];
 #pragma unroll
   for (int i = 0; i < HM; ++i) acc[i] = f32x16{};
-  const int xr = l32 % CPR, xt = l32 & 7;
+  const int xr = l32 % CPR, xt = (l32 >> 1) & 7;
   if (it_beg < ntiles) issue(it_beg, it_beg & 1);
   WAIT_VM_LDS(0);
   __syncthreads();
