@@ -635,6 +635,8 @@ __global__ __launch_bounds__(256) void k_swa_dkv(AttnBwdArgs a, int P) {
   const int s0blk = blockIdx.x * BQ;
   const int sk = s0blk + wid * QW + (lane & 31);  // this lane's key (chunk-local)
   const bool kok = sk < a.n;
+  const int wsk_hi = s0blk + wid * QW + QW - 1;    // last key of this wave
+  const bool wkok = wsk_hi < a.n;                   // all 32 keys of the wave exist
   const float LOG2E = 1.4426950408889634f;
   const float sl2 = LOG2E / sqrtf((float)HD);
 
@@ -664,13 +666,14 @@ __global__ __launch_bounds__(256) void k_swa_dkv(AttnBwdArgs a, int P) {
   const int per = (ntq + P - 1) / P;
   const int tbeg = tfirst + part * per * KT;
   const int tstop = min(a.n, tfirst + (part + 1) * per * KT);
-  for (int tq0 = tbeg; tq0 < tstop; tq0 += KT) {
-    uint4 rq0, rq1, rq2, rq3, ro0, ro1, ro2, ro3, tq_0, tq_1, tq_2, tq_3, to_0, to_1, to_2, to_3;
-    // Q^T / dO^T chunk c (TR): head-dim row c / 8, queries (c % 8) * 8 .. +7
+  // the next query tile is loaded into registers while the current one is computed
+  uint4 rq0, rq1, rq2, rq3, ro0, ro1, ro2, ro3, tq_0, tq_1, tq_2, tq_3, to_0, to_1, to_2, to_3;
+  float nl2 = 0.f, ndd = 0.f;
+  // Q^T / dO^T chunk c (TR): head-dim row c / 8, queries (c % 8) * 8 .. +7
 #define LD(i, dq_, do_, tq_, to_)                                                           \
   if constexpr (KCH > i) {                                                                  \
     const int c = tid + i * 256, r = c / (HD / 8), col = (c % (HD / 8)) * 8;                \
-    const int t = tq0 + r;                                                                  \
+    const int t = tl0 + r;                                                                  \
     if (t < a.n) {                                                                          \
       dq_ = *(const uint4*)((const bf16*)a.q + (bh * a.n + t) * HD + col);                  \
       do_ = *(const uint4*)((const bf16*)a.dout + ((int64_t)b * a.n + t) * d + (int64_t)h * HD + col); \
@@ -679,7 +682,7 @@ __global__ __launch_bounds__(256) void k_swa_dkv(AttnBwdArgs a, int P) {
       do_ = make_uint4(0, 0, 0, 0);                                                         \
     }                                                                                       \
     if constexpr (TR) {                                                                     \
-      const int tt = tq0 + (c % (KT / 8)) * 8;                                              \
+      const int tt = tl0 + (c % (KT / 8)) * 8;                                              \
       const int64_t toff = (bh * HD + c / (KT / 8)) * a.n + tt;                             \
       if (tt < a.n) {                                                                       \
         tq_ = *(const uint4*)((const bf16*)a.qt + toff);                                    \
@@ -690,9 +693,20 @@ __global__ __launch_bounds__(256) void k_swa_dkv(AttnBwdArgs a, int P) {
       }                                                                                     \
     }                                                                                       \
   }
-    LD(0, rq0, ro0, tq_0, to_0) LD(1, rq1, ro1, tq_1, to_1) LD(2, rq2, ro2, tq_2, to_2) LD(3, rq3, ro3, tq_3, to_3)
-#undef LD
-    __syncthreads();
+#define LOAD_QTILE(T)                                                                       \
+  {                                                                                         \
+    const int tl0 = (T);                                                                    \
+    LD(0, rq0, ro0, tq_0, to_0) LD(1, rq1, ro1, tq_1, to_1) LD(2, rq2, ro2, tq_2, to_2)     \
+    LD(3, rq3, ro3, tq_3, to_3)                                                             \
+    if (tid < KT) {                                                                         \
+      const int t = tl0 + tid;                                                              \
+      nl2 = t < a.n ? a.lse[bh * a.n + t] * LOG2E : 0.f;                                    \
+      ndd = t < a.n ? a.dvec[bh * a.n + t] : 0.f;                                           \
+    }                                                                                       \
+  }
+  if (tbeg < tstop) LOAD_QTILE(tbeg)
+  for (int tq0 = tbeg; tq0 < tstop; tq0 += KT) {
+    __syncthreads();  // the previous tile's reads of LDS are done
 #define ST(i, sq, so, tq_, to_)                                                             \
   if constexpr (KCH > i) {                                                                  \
     const int c = tid + i * 256, r = c / (HD / 8), col = (c % (HD / 8)) * 8;                \
@@ -713,11 +727,11 @@ __global__ __launch_bounds__(256) void k_swa_dkv(AttnBwdArgs a, int P) {
     ST(0, rq0, ro0, tq_0, to_0) ST(1, rq1, ro1, tq_1, to_1) ST(2, rq2, ro2, tq_2, to_2) ST(3, rq3, ro3, tq_3, to_3)
 #undef ST
     if (tid < KT) {
-      const int t = tq0 + tid;
-      sm.lse2[tid] = t < a.n ? a.lse[bh * a.n + t] * LOG2E : 0.f;
-      sm.dd[tid] = t < a.n ? a.dvec[bh * a.n + t] : 0.f;
+      sm.lse2[tid] = nl2;
+      sm.dd[tid] = ndd;
     }
     __syncthreads();
+    if (tq0 + KT < tstop) LOAD_QTILE(tq0 + KT)
     // the 64-query tile in two halves of 32 queries (keeps the score registers to one half)
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
@@ -733,22 +747,30 @@ __global__ __launch_bounds__(256) void k_swa_dkv(AttnBwdArgs a, int P) {
       SSTEP(4, k4, v4) SSTEP(5, k5, v5) SSTEP(6, k6, v6) SSTEP(7, k7, v7)
 #undef SSTEP
       // rows = queries tq0 + 32 hf + 8 j + 4 g + i; visible iff sk <= t < n and t - sk < window
+      // (window >= n here, so the last condition always holds).  Only halves that reach the
+      // chunk end or the diagonal of this wave's keys need the per-element test.
+      const int th0 = tq0 + hf * 32;
+      const bool full = wkok && th0 + 31 < a.n && th0 >= wsk_hi;
       uint32_t pa[8], da[8];
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        float pv[2], dsv[2];
+      for (int j4 = 0; j4 < 4; ++j4) {
+        const float4 l4 = *(const float4*)&sm.lse2[hf * 32 + 8 * j4 + 4 * g];
+        const float4 d4 = *(const float4*)&sm.dd[hf * 32 + 8 * j4 + 4 * g];
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dvv[4] = {d4.x, d4.y, d4.z, d4.w};
+        float pv[4], dsv[4];
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int rr = r + u;
-          const int row = hf * 32 + 8 * (rr >> 2) + 4 * g + (rr & 3);
-          const int t = tq0 + row;
-          const bool ok = kok && t < a.n && t >= sk && t - sk < a.window;
-          const float p = ok ? ex2(s0[rr] * sl2 - sm.lse2[row]) : 0.f;
-          pv[u] = p;
-          dsv[u] = p * (p0[rr] - sm.dd[row]);
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int rr = 4 * j4 + i4;
+          const int t = th0 + 8 * j4 + 4 * g + i4;
+          const bool ok = full || (kok && t < a.n && t >= sk);
+          const float p = ok ? ex2(fmaf(s0[rr], sl2, -lv[i4])) : 0.f;
+          pv[i4] = p;
+          dsv[i4] = p * (p0[rr] - dvv[i4]);
         }
-        pa[r >> 1] = pk2(pv[0], pv[1]);
-        da[r >> 1] = pk2(dsv[0], dsv[1]);
+        pa[2 * j4] = pk2(pv[0], pv[1]);
+        pa[2 * j4 + 1] = pk2(pv[2], pv[3]);
+        da[2 * j4] = pk2(dsv[0], dsv[1]);
+        da[2 * j4 + 1] = pk2(dsv[2], dsv[3]);
       }
       const bf16x8 pf0 = __builtin_bit_cast(bf16x8, make_uint4(pa[0], pa[1], pa[2], pa[3]));
       const bf16x8 pf1 = __builtin_bit_cast(bf16x8, make_uint4(pa[4], pa[5], pa[6], pa[7]));
@@ -771,6 +793,8 @@ __global__ __launch_bounds__(256) void k_swa_dkv(AttnBwdArgs a, int P) {
       }
     }
   }
+#undef LD
+#undef LOAD_QTILE
   if (!kok) return;
   const float sc = 1.f / sqrtf((float)HD);
   const int64_t plane = (int64_t)a.B * a.n * d;
