@@ -460,8 +460,11 @@ int top_chunk(ttt_ctx* c, const int32_t* tgt, int64_t ld, const float* hsrc, int
     // overlapping the rest of the backward: their inputs (dy^T, dz^T of this block, act^T,
     // m^T) stay untouched until the next chunk, and the GEMMs above that read the old
     // W_down^T and W_gu^T have been enqueued before them.
-    hipStream_t sg = c->overlap ? c->side : c->stream;
-    if (c->overlap) {
+    // (the lowest block's update is the chunk's critical path: it runs on the main stream,
+    // next to the side stream's remaining updates)
+    const bool on_side = c->overlap && j > 0;
+    hipStream_t sg = on_side ? c->side : c->stream;
+    if (on_side) {
       CK(hipEventRecord(c->ev_m2s, c->stream));
       CK(hipStreamWaitEvent(c->side, c->ev_m2s, 0));
     }
