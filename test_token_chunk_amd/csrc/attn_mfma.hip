@@ -921,7 +921,25 @@ __global__ __launch_bounds__(512) void k_swa_dq2(AttnBwdArgs a, int S) {
   const float LOG2E = 1.4426950408889634f;
   const float sl2 = LOG2E / sqrtf((float)HD);
   const float nlse2 = qok ? -a.lse[bh * a.n + tq] * LOG2E : 0.f;
-  const float Dq = qok ? a.dvec[bh * a.n + tq] : 0.f;
+  // D = rowsum(dO * O) of this lane's query from its own dO fragments and the matching O
+  // fragments (the lane pair holds the two halves of the head dim); written for the dK/dV
+  // kernel by the first key-range part
+  float Dq;
+  {
+    const bf16* op = (const bf16*)a.o + ((int64_t)b * a.n + (qok ? tq : 0)) * d + (int64_t)h * HD + g * 8;
+    float part = 0.f;
+    auto dot8 = [&](const bf16x8& e, int ks) {
+      const bf16x8 o = __builtin_bit_cast(bf16x8, qok ? *(const uint4*)(op + ks * 16) : make_uint4(0, 0, 0, 0));
+#pragma unroll
+      for (int u = 0; u < 8; ++u) part = fmaf((float)e[u], (float)o[u], part);
+    };
+    dot8(e0, 0); dot8(e1, 1);
+    if constexpr (KS > 2) { dot8(e2, 2); dot8(e3, 3); }
+    if constexpr (KS > 4) { dot8(e4, 4); dot8(e5, 5); }
+    if constexpr (KS > 6) { dot8(e6, 6); dot8(e7, 7); }
+    Dq = part + __shfl_xor(part, 32, 64);
+    if (qok && g == 0 && sp == 0) a.dvec[bh * a.n + tq] = Dq;
+  }
 
   const int tlast = min(t0 + BQn, a.n) - 1;
   const int64_t kbeg = max((int64_t)0, a.pos0 + t0 - a.window + 1);
@@ -1068,12 +1086,18 @@ hipError_t launch_dkv(const AttnBwdArgs& a, int P, hipStream_t s) {
 
 template <int HD>
 hipError_t launch_bwd(const AttnBwdArgs& a, hipStream_t s) {
-  hipError_t e = swa_dvec_bf16(a, s);
-  if (e != hipSuccess) return e;
+  // the direct-to-LDS dQ form (head dim 128, transposed key ring) computes D = rowsum(dO * O)
+  // itself and stores it for dK/dV; otherwise a separate pass does
+  const bool tr = a.ktr && a.dot && a.R % 8 == 0 && a.n % 8 == 0 && (a.H * HD) % 8 == 0;
+  constexpr bool DQ2 = HD == 128;
+  hipError_t e = hipSuccess;
+  if (!(DQ2 && tr)) {
+    e = swa_dvec_bf16(a, s);
+    if (e != hipSuccess) return e;
+  }
   // transposed tiles are read with 16-byte copies when the caller provides the
   // transposed key ring and a dO^T scratch, 8-key groups stay inside the ring
   // (R % 8 == 0) and 8-query groups inside the chunk (n % 8 == 0)
-  const bool tr = a.ktr && a.dot && a.R % 8 == 0 && a.n % 8 == 0 && (a.H * HD) % 8 == 0;
   if (tr)
     hipLaunchKernelGGL(k_heads_transpose, dim3(cdiv(a.n, 64), cdiv(a.H * HD, 64), a.B), dim3(256), 0, s,
                        (const bf16*)a.dout, (bf16*)a.dot, a.n, a.H, HD);
@@ -1081,8 +1105,7 @@ hipError_t launch_bwd(const AttnBwdArgs& a, hipStream_t s) {
   const int64_t ntiles = (std::min<int64_t>(a.window, a.pos0 + 1) + 8 * QW) / KT + 1;
   const int64_t total = (int64_t)a.B * a.n * a.H * HD;
   const int S = attn_splits(blocks8, ntiles, total, a.ws, a.ws_floats);
-  // the direct-to-LDS form (measured faster at head dim 128, slower at 64)
-  constexpr bool DQ2 = HD == 128;
+  // (the direct-to-LDS dQ form: measured faster at head dim 128, slower at 64)
   if (S > 1) {
     if constexpr (DQ2) e = tr ? launch_dq2<HD, true>(a, S, s) : launch_dq<HD, 8, true, false>(a, S, s);
     else e = tr ? launch_dq<HD, 8, true, true>(a, S, s) : launch_dq<HD, 8, true, false>(a, S, s);
