@@ -82,61 +82,129 @@ __device__ __forceinline__ void store4<bf16>(bf16* p, float a, float b, float c,
                           (uint32_t)f2bf(c).x | ((uint32_t)f2bf(d).x << 16));
 }
 
-// Vector forms of the row kernels above: one wave per row, 16-byte loads (d % 4 == 0,
-// 16-byte aligned rows); transposed outputs are written by k_transpose_rows afterwards.
+// Vector forms of the row kernels above: one 256-thread block per row, 16-byte access
+// (d % 4 == 0, d <= 4096, 16-byte aligned rows); transposed outputs are written by
+// k_transpose_rows afterwards.  With `parts`, the S fp32 parts of a K-split GEMM
+// ([S][M][d], plane = M * d floats apart) are summed in order inside the row kernel
+// instead of by a separate pass: the forward adds them to h (and rewrites h), the backward
+// uses their sum as dy.
 template <typename T>
-__global__ __launch_bounds__(256) void k_rmsnorm_fwd4(const float* x, int64_t M, int d, const float* g, float eps,
-                                                      T* y, float* rstd, float* xcopy) {
-  const int64_t m = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (m >= M) return;
-  const int lane = threadIdx.x & 63, d4 = d / 4;
-  const float4* xr = (const float4*)(x + m * d);
-  float ss = 0.f;
-  for (int i = lane; i < d4; i += 64) {
-    const float4 v = xr[i];
-    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
-    if (xcopy) ((float4*)(xcopy + m * d))[i] = v;
+__global__ __launch_bounds__(256) void k_rmsnorm_fwd_row(float* h, const float* __restrict__ parts, int S, int64_t plane,
+                                                         int d, const float* __restrict__ g, float eps,
+                                                         T* __restrict__ y, float* __restrict__ rstd,
+                                                         float* __restrict__ xcopy) {
+  __shared__ float sh[16];
+  const int64_t m = blockIdx.x;
+  const int tid = threadIdx.x, d4 = d / 4;
+  float4* hr = (float4*)(h + m * d);
+  float4 v[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int i = tid + 256 * k;
+    if (i < d4) v[k] = hr[i];
   }
-  ss = warp_sum(ss);
+  if (parts) {
+    const float4* pr = (const float4*)(parts + m * d);
+    const int64_t pl4 = plane / 4;
+    for (int sp = 0; sp < S; ++sp) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int i = tid + 256 * k;
+        if (i < d4) {
+          const float4 q = pr[sp * pl4 + i];
+          v[k].x += q.x;
+          v[k].y += q.y;
+          v[k].z += q.z;
+          v[k].w += q.w;
+        }
+      }
+    }
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int i = tid + 256 * k;
+    if (i < d4) {
+      if (parts) hr[i] = v[k];
+      if (xcopy) ((float4*)(xcopy + m * d))[i] = v[k];
+      ss += v[k].x * v[k].x + v[k].y * v[k].y + v[k].z * v[k].z + v[k].w * v[k].w;
+    }
+  }
+  ss = block_sum(ss, sh);
   const float r = 1.f / sqrtf(ss / (float)d + eps);
-  if (lane == 0 && rstd) rstd[m] = r;
-  for (int i = lane; i < d4; i += 64) {
-    const float4 v = xr[i], w = ((const float4*)g)[i];
-    store4<T>(y + m * d + 4 * i, w.x * v.x * r, w.y * v.y * r, w.z * v.z * r, w.w * v.w * r);
+  if (tid == 0 && rstd) rstd[m] = r;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int i = tid + 256 * k;
+    if (i < d4) {
+      const float4 w = ((const float4*)g)[i];
+      store4<T>(y + m * d + 4 * i, w.x * v[k].x * r, w.y * v[k].y * r, w.z * v[k].z * r, w.w * v[k].w * r);
+    }
   }
 }
 
 template <typename T>
-__global__ __launch_bounds__(256) void k_rmsnorm_bwd4(const float* x, const float* rstd, int64_t M, int d,
-                                                      const float* g, const float* dy, const float* resid, float* out,
-                                                      T* outT) {
-  const int64_t m = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (m >= M) return;
-  const int lane = threadIdx.x & 63, d4 = d / 4;
+__global__ __launch_bounds__(256) void k_rmsnorm_bwd_row(const float* __restrict__ x, const float* __restrict__ rstd,
+                                                         int d, const float* __restrict__ g, const float* dy,
+                                                         const float* __restrict__ parts, int S, int64_t plane,
+                                                         const float* resid, float* out, T* outT) {
+  __shared__ float sh[16];
+  const int64_t m = blockIdx.x;
+  const int tid = threadIdx.x, d4 = d / 4;
   const float4* xr = (const float4*)(x + m * d);
-  const float4* dr = (const float4*)(dy + m * d);
   const float4* g4 = (const float4*)g;
-  float dot = 0.f;
-  for (int i = lane; i < d4; i += 64) {
-    const float4 v = xr[i], e = dr[i], w = g4[i];
-    dot += w.x * e.x * v.x + w.y * e.y * v.y + w.z * e.z * v.z + w.w * e.w * v.w;
+  const float4* er = (const float4*)((parts ? parts : dy) + m * d);
+  float4 e[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int i = tid + 256 * k;
+    if (i < d4) e[k] = er[i];
   }
-  dot = warp_sum(dot);
+  if (parts) {
+    const int64_t pl4 = plane / 4;
+    for (int sp = 1; sp < S; ++sp) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int i = tid + 256 * k;
+        if (i < d4) {
+          const float4 q = er[sp * pl4 + i];
+          e[k].x += q.x;
+          e[k].y += q.y;
+          e[k].z += q.z;
+          e[k].w += q.w;
+        }
+      }
+    }
+  }
+  float dot = 0.f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int i = tid + 256 * k;
+    if (i < d4) {
+      const float4 v = xr[i], w = g4[i];
+      dot += w.x * e[k].x * v.x + w.y * e[k].y * v.y + w.z * e[k].z * v.z + w.w * e[k].w * v.w;
+    }
+  }
+  dot = block_sum(dot, sh);
   const float r = rstd[m];
   const float c = r * r * r * dot / (float)d;
-  for (int i = lane; i < d4; i += 64) {
-    const float4 v = xr[i], e = dr[i], w = g4[i];
-    float4 o = make_float4(r * w.x * e.x - v.x * c, r * w.y * e.y - v.y * c, r * w.z * e.z - v.z * c,
-                           r * w.w * e.w - v.w * c);
-    if (resid) {
-      const float4 q = ((const float4*)(resid + m * d))[i];
-      o.x += q.x;
-      o.y += q.y;
-      o.z += q.z;
-      o.w += q.w;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int i = tid + 256 * k;
+    if (i < d4) {
+      const float4 v = xr[i], w = g4[i];
+      float4 o = make_float4(r * w.x * e[k].x - v.x * c, r * w.y * e[k].y - v.y * c, r * w.z * e[k].z - v.z * c,
+                             r * w.w * e[k].w - v.w * c);
+      if (resid) {
+        const float4 q = ((const float4*)(resid + m * d))[i];
+        o.x += q.x;
+        o.y += q.y;
+        o.z += q.z;
+        o.w += q.w;
+      }
+      ((float4*)(out + m * d))[i] = o;
+      if (outT) store4<T>(outT + m * d + 4 * i, o.x, o.y, o.z, o.w);
     }
-    ((float4*)(out + m * d))[i] = o;
-    if (outT) store4<T>(outT + m * d + 4 * i, o.x, o.y, o.z, o.w);
   }
 }
 
@@ -608,9 +676,10 @@ template <typename T>
 hipError_t rmsnorm_fwd(const float* x, int64_t M, int d, const float* g, float eps, T* y, float* rstd, T* yT, int rpb,
                        int64_t ldT, float* xcopy, hipStream_t s) {
   if (M == 0) return hipSuccess;
-  if (y && d % 4 == 0 && al16(x) && al16(g) && al16(y) && al16(xcopy) &&
+  if (y && d % 4 == 0 && d <= 4096 && al16(x) && al16(g) && al16(y) && al16(xcopy) &&
       (!yT || transpose_ok(y, yT, M, d, rpb, ldT))) {
-    hipLaunchKernelGGL(k_rmsnorm_fwd4<T>, dim3(cdiv(M, 4)), dim3(256), 0, s, x, M, d, g, eps, y, rstd, xcopy);
+    hipLaunchKernelGGL(k_rmsnorm_fwd_row<T>, dim3((unsigned)M), dim3(256), 0, s, const_cast<float*>(x), nullptr, 0,
+                       (int64_t)0, d, g, eps, y, rstd, xcopy);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !yT) return e;
     return transpose_rows(y, yT, M, d, rpb, ldT, s);
@@ -627,13 +696,44 @@ template <typename T>
 hipError_t rmsnorm_bwd(const float* x, const float* rstd, int64_t M, int d, const float* g, const float* dy,
                        const float* resid, float* out, T* outT, hipStream_t s) {
   if (M == 0) return hipSuccess;
-  if (d % 4 == 0 && al16(x) && al16(g) && al16(dy) && al16(resid) && al16(out) && al16(outT)) {
-    hipLaunchKernelGGL(k_rmsnorm_bwd4<T>, dim3(cdiv(M, 4)), dim3(256), 0, s, x, rstd, M, d, g, dy, resid, out, outT);
+  if (d % 4 == 0 && d <= 4096 && al16(x) && al16(g) && al16(dy) && al16(resid) && al16(out) && al16(outT)) {
+    hipLaunchKernelGGL(k_rmsnorm_bwd_row<T>, dim3((unsigned)M), dim3(256), 0, s, x, rstd, d, g, dy, nullptr, 0,
+                       (int64_t)0, resid, out, outT);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(k_rmsnorm_bwd<T>, dim3(M), dim3(row_threads(d)), 0, s, x, rstd, d, g, dy, resid, out, outT);
   return hipGetLastError();
 }
+
+static bool parts_ok(int d, const void* a, const void* b, const void* c2, const void* d2, const void* e2) {
+  return d % 4 == 0 && d <= 4096 && al16(a) && al16(b) && al16(c2) && al16(d2) && al16(e2);
+}
+
+template <typename T>
+hipError_t add_rmsnorm_fwd_parts(float* h, const float* parts, int S, int64_t plane, int64_t M, int d, const float* g,
+                                 float eps, T* y, float* rstd, T* yT, int rpb, int64_t ldT, float* xcopy,
+                                 hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  if (!(y && parts_ok(d, h, parts, g, y, xcopy) && plane % 4 == 0 && (!yT || transpose_ok(y, yT, M, d, rpb, ldT))))
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_rmsnorm_fwd_row<T>, dim3((unsigned)M), dim3(256), 0, s, h, parts, S, plane, d, g, eps, y, rstd,
+                     xcopy);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !yT) return e;
+  return transpose_rows(y, yT, M, d, rpb, ldT, s);
+}
+
+template <typename T>
+hipError_t rmsnorm_bwd_parts(const float* x, const float* rstd, int64_t M, int d, const float* g, const float* parts,
+                             int S, int64_t plane, const float* resid, float* out, T* outT, hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  if (!(parts_ok(d, x, g, parts, resid, out) && al16(outT) && plane % 4 == 0)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_rmsnorm_bwd_row<T>, dim3((unsigned)M), dim3(256), 0, s, x, rstd, d, g, nullptr, parts, S,
+                     plane, resid, out, outT);
+  return hipGetLastError();
+}
+
+bool row_parts_ok(int d) { return d % 4 == 0 && d <= 4096; }
 
 template <typename T>
 hipError_t convert_rows(const float* x, int64_t M, int d, T* y, T* yT, int rpb, int64_t ldT, hipStream_t s) {
@@ -729,6 +829,10 @@ hipError_t refresh_shadows(const float* master, int rows, int cols, int batch, i
                                          hipStream_t);                                                              \
   template hipError_t rmsnorm_fwd<T>(const float*, int64_t, int, const float*, float, T*, float*, T*, int, int64_t, \
                                      float*, hipStream_t);                                                                  \
+  template hipError_t add_rmsnorm_fwd_parts<T>(float*, const float*, int, int64_t, int64_t, int, const float*,  \
+                                               float, T*, float*, T*, int, int64_t, float*, hipStream_t);         \
+  template hipError_t rmsnorm_bwd_parts<T>(const float*, const float*, int64_t, int, const float*, const float*,  \
+                                           int, int64_t, const float*, float*, T*, hipStream_t);                   \
   template hipError_t rmsnorm_bwd<T>(const float*, const float*, int64_t, int, const float*, const float*,          \
                                      const float*, float*, T*, hipStream_t);                                        \
   template hipError_t convert_rows<T>(const float*, int64_t, int, T*, T*, int, int64_t, hipStream_t);               \

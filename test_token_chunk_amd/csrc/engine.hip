@@ -111,6 +111,9 @@ struct ttt_ctx {
   std::string err;
   float* pending_loss = nullptr;  // device losses of async work, checked by ttt_sync
   int64_t pending_n = 0;
+  // K-split parts of the last residual-stream GEMM left in ws, summed into the residual
+  // stream by the next RMSNorm forward (0: none)
+  int pend_parts = 0;
 
   // per-kernel-class device time (HIP events around each launch) while profiling is on
   uint32_t prof = 0;  // bit i: time launches of class i
@@ -214,6 +217,10 @@ struct Ops<float> {
     if (!st) st = c->stream;
     return timed(c, g.e.kind, gemm_flops(g), st, [&] { return gemm_simt_f32(g, st); });
   }
+  static hipError_t gemm_parts(ttt_ctx* c, const GemmArgs& g, int& S) {
+    S = 1;
+    return gemm(c, g);
+  }
   static hipError_t fwd(ttt_ctx* c, const AttnArgs& a) {
     double fl = 4.0 * a.hd * a.H * a.B * attn_pairs(c, a.n, a.pos0);
     return timed(c, PC_SWA_FWD, fl, c->stream, [&] { return swa_fwd_simt<float>(a, c->stream); });
@@ -229,6 +236,7 @@ template <>
 struct Ops<bf16> {
   // st: the side stream (no workspace there: the split workspace belongs to the main stream)
   static hipError_t gemm(ttt_ctx* c, const GemmArgs& g0, hipStream_t st = nullptr) {
+    if (c->pend_parts && !st) return hipErrorIllegalState;  // the workspace still holds parts to sum
     GemmArgs g = g0;
     g.ws = st ? nullptr : c->ws;
     g.ws_floats = st ? 0 : c->ws_floats;
@@ -238,7 +246,21 @@ struct Ops<bf16> {
     return timed(c, cls, gemm_flops(g), st,
                  [&] { return c->mfma ? gemm_mfma_bf16(g, st) : gemm_simt_bf16(g, st); });
   }
+  // a GEMM whose fp32 result [M][N] feeds a row kernel next: if it splits K, its S parts stay
+  // in the workspace for that kernel to sum (S > 1); otherwise it writes g.e.c (S = 1)
+  static hipError_t gemm_parts(ttt_ctx* c, const GemmArgs& g0, int& S) {
+    GemmArgs g = g0;
+    g.ws = c->ws;
+    g.ws_floats = c->ws_floats;
+    S = (c->mfma && (int64_t)g.M * g.batch >= 128 && row_parts_ok(g.N) && g.e.ldc == g.N &&
+         g.e.sc == (g.batch > 1 ? (int64_t)g.M * g.N : g.e.sc))
+            ? gemm_mfma_splits(g, nullptr)
+            : 1;
+    g.defer = S > 1;
+    return gemm(c, g);
+  }
   static hipError_t fwd(ttt_ctx* c, const AttnArgs& a0) {
+    if (c->pend_parts) return hipErrorIllegalState;
     AttnArgs a = a0;
     a.ws = c->ws;
     a.ws_floats = c->ws_floats;
@@ -248,6 +270,7 @@ struct Ops<bf16> {
                  [&] { return c->mfma ? swa_fwd_mfma(a, c->stream) : swa_fwd_simt<bf16>(a, c->stream); });
   }
   static hipError_t bwd(ttt_ctx* c, const AttnBwdArgs& a0) {
+    if (c->pend_parts) return hipErrorIllegalState;
     AttnBwdArgs a = a0;
     a.ws = c->ws;
     a.ws_floats = c->ws_floats;
@@ -276,14 +299,36 @@ T* tp(void* p, int64_t off = 0) {
 
 // forward of block l over n tokens per row at positions [p0, p0+n); h is the
 // fp32 residual stream [B*n][d], updated in place.
+// RMSNorm forward of the residual stream h [M][d]; parts of a preceding K-split GEMM that
+// are still in the workspace are added to h first (in order, in the same kernel)
+template <typename T>
+hipError_t norm_fwd(ttt_ctx* c, float* h, int64_t M, const float* g, T* y, float* rstd, T* yT, int rpb, int64_t ldT,
+                    float* xcopy) {
+  const float eps = (float)c->cfg.rms_eps;
+  if (c->pend_parts > 1) {
+    const int S = c->pend_parts;
+    c->pend_parts = 0;
+    return add_rmsnorm_fwd_parts<T>(h, c->ws, S, M * c->d, M, c->d, g, eps, y, rstd, yT, rpb, ldT, xcopy, c->stream);
+  }
+  return rmsnorm_fwd<T>(h, M, c->d, g, eps, y, rstd, yT, rpb, ldT, xcopy, c->stream);
+}
+
+// RMSNorm backward with dy from a GEMM that may have left S > 1 K-split parts in the workspace
+template <typename T>
+hipError_t norm_bwd(ttt_ctx* c, int S, const float* x, const float* rstd, int64_t M, const float* g, const float* dy,
+                    const float* resid, float* out, T* outT) {
+  if (S > 1) return rmsnorm_bwd_parts<T>(x, rstd, M, c->d, g, c->ws, S, M * c->d, resid, out, outT, c->stream);
+  return rmsnorm_bwd<T>(x, rstd, M, c->d, g, dy, resid, out, outT, c->stream);
+}
+
 template <typename T>
 int layer_fwd(ttt_ctx* c, int l, float* h, int n, int64_t p0, int mode, TopActs* sv) {
   const int B = c->B, d = c->d, f = c->f;
   const int64_t M = (int64_t)B * n;
   const LayerW& w = c->lw[l];
   if (mode != MLP_ONLY) {
-    CK(rmsnorm_fwd<T>(h, M, d, w.attn_norm, (float)c->cfg.rms_eps, tp<T>(c->ub), sv ? sv->rstd1 : c->rstd_tmp,
-                      (T*)nullptr, n, 0, sv ? sv->h_in : nullptr, c->stream));
+    CK(norm_fwd<T>(c, h, M, w.attn_norm, tp<T>(c->ub), sv ? sv->rstd1 : c->rstd_tmp, (T*)nullptr, n, 0,
+                   sv ? sv->h_in : nullptr));
     GemmArgs g = mk(c->ub, d, w.wqkv, d, (int)M, 3 * d, d);
     g.e.kind = EPI_F32;
     g.e.c = c->qkvb;
@@ -323,11 +368,16 @@ int layer_fwd(ttt_ctx* c, int l, float* h, int n, int64_t p0, int mode, TopActs*
     go.e.kind = EPI_ADD_F32;
     go.e.c = h;
     go.e.ldc = d;
-    CK(Ops<T>::gemm(c, go));
-    if (mode == ATTN_ONLY) return TTT_OK;
+    if (mode == ATTN_ONLY) {
+      CK(Ops<T>::gemm(c, go));
+      return TTT_OK;
+    }
+    int So = 1;  // the MLP norm below sums a K split of the output projection
+    CK(Ops<T>::gemm_parts(c, go, So));
+    c->pend_parts = So > 1 ? So : 0;
   }
-  CK(rmsnorm_fwd<T>(h, M, d, w.mlp_norm, (float)c->cfg.rms_eps, tp<T>(c->ub), sv ? sv->rstd2 : c->rstd_tmp,
-                    sv ? tp<T>(sv->mT) : (T*)nullptr, n, c->b, sv ? sv->h_mid : nullptr, c->stream));
+  CK(norm_fwd<T>(c, h, M, w.mlp_norm, tp<T>(c->ub), sv ? sv->rstd2 : c->rstd_tmp, sv ? tp<T>(sv->mT) : (T*)nullptr,
+                 n, c->b, sv ? sv->h_mid : nullptr));
   if (l >= c->l0) {
     const FastW& fw = c->fw[l - c->l0];
     GemmArgs g = mk(c->ub, d, fw.wgu, d, n, c->il ? 2 * f : f, d);
@@ -357,7 +407,9 @@ int layer_fwd(ttt_ctx* c, int l, float* h, int n, int64_t p0, int mode, TopActs*
     gd.e.c = h;
     gd.e.ldc = d;
     gd.e.sc = (int64_t)n * d;
-    CK(Ops<T>::gemm(c, gd));
+    int Sd = 1;  // summed by the next norm forward (next block's attention norm or the final norm)
+    CK(Ops<T>::gemm_parts(c, gd, Sd));
+    c->pend_parts = Sd > 1 ? Sd : 0;
   } else {
     GemmArgs g = mk(c->ub, d, w.wgu, d, (int)M, c->il ? 2 * f : f, d);
     g.dual_off = c->il ? 0 : f;
@@ -369,7 +421,9 @@ int layer_fwd(ttt_ctx* c, int l, float* h, int n, int64_t p0, int mode, TopActs*
     gd.e.kind = EPI_ADD_F32;
     gd.e.c = h;
     gd.e.ldc = d;
-    CK(Ops<T>::gemm(c, gd));
+    int Sd = 1;
+    CK(Ops<T>::gemm_parts(c, gd, Sd));
+    c->pend_parts = Sd > 1 ? Sd : 0;
   }
   return TTT_OK;
 }
@@ -400,8 +454,7 @@ int top_chunk(ttt_ctx* c, const int32_t* tgt, int64_t ld, const float* hsrc, int
     rc = layer_fwd<T>(c, c->l0 + j, c->htop, n, p0, FULL, &c->acts[j]);
     if (rc) return rc;
   }
-  CK(rmsnorm_fwd<T>(c->htop, M, d, c->final_norm, (float)c->cfg.rms_eps, tp<T>(c->hf), c->rstdf, (T*)nullptr, n, 0,
-                    nullptr, c->stream));
+  CK(norm_fwd<T>(c, c->htop, M, c->final_norm, tp<T>(c->hf), c->rstdf, (T*)nullptr, n, 0, nullptr));
   GemmArgs gl = mk(c->hf, d, c->lm_head, d, (int)M, V, d);
   gl.e.kind = EPI_F32;
   gl.e.c = c->logits;
@@ -416,8 +469,9 @@ int top_chunk(ttt_ctx* c, const int32_t* tgt, int64_t ld, const float* hsrc, int
   gx.e.kind = EPI_F32;
   gx.e.c = c->tmpf;
   gx.e.ldc = d;
-  CK(Ops<T>::gemm(c, gx));
-  CK(rmsnorm_bwd<T>(c->htop, c->rstdf, M, d, c->final_norm, c->tmpf, nullptr, c->dh, (T*)nullptr, c->stream));
+  int Sx = 1;
+  CK(Ops<T>::gemm_parts(c, gx, Sx));
+  CK(norm_bwd<T>(c, Sx, c->htop, c->rstdf, M, c->final_norm, c->tmpf, nullptr, c->dh, (T*)nullptr));
   const float lr = c->cfg.lr;
   const int64_t fsz = 3LL * f * d;
   for (int j = c->Lq - 1; j >= 0; --j) {
@@ -445,6 +499,7 @@ int top_chunk(ttt_ctx* c, const int32_t* tgt, int64_t ld, const float* hsrc, int
     g1.e.st = 2LL * f * b;
     g1.e.f = f;
     CK(Ops<T>::gemm(c, g1));
+    int S3 = 1;   // K-split parts of dm left for the MLP norm's backward
     if (j > 0) {  // dm = dz_g W_gate + dz_u W_up  (before W_gate/W_up change)
       GemmArgs g3 = mk(c->dz, 2 * f, w.wguT, 2 * f, n, d, 2 * f);
       g3.batch = B;
@@ -454,7 +509,7 @@ int top_chunk(ttt_ctx* c, const int32_t* tgt, int64_t ld, const float* hsrc, int
       g3.e.c = c->tmpf;
       g3.e.ldc = d;
       g3.e.sc = (int64_t)n * d;
-      CK(Ops<T>::gemm(c, g3));
+      CK(Ops<T>::gemm_parts(c, g3, S3));
     }
     // The weight gradients of this block with the fused SGD step run on the side stream,
     // overlapping the rest of the backward: their inputs (dy^T, dz^T of this block, act^T,
@@ -506,7 +561,7 @@ int top_chunk(ttt_ctx* c, const int32_t* tgt, int64_t ld, const float* hsrc, int
     if (j == 0) break;
     const LayerW& lw = c->lw[l];
     // through the MLP norm and the residual: dh <- d h_mid
-    CK(rmsnorm_bwd<T>(a.h_mid, a.rstd2, M, d, lw.mlp_norm, c->tmpf, c->dh, c->dh, tp<T>(c->dhT), c->stream));
+    CK(norm_bwd<T>(c, S3, a.h_mid, a.rstd2, M, lw.mlp_norm, c->tmpf, c->dh, c->dh, tp<T>(c->dhT)));
     // attention output projection
     GemmArgs g5 = mk(c->dhT, d, lw.woT, d, (int)M, d, d);
     g5.e.kind = EPI_T;
@@ -541,8 +596,9 @@ int top_chunk(ttt_ctx* c, const int32_t* tgt, int64_t ld, const float* hsrc, int
     g6.e.kind = EPI_F32;
     g6.e.c = c->tmpf;
     g6.e.ldc = d;
-    CK(Ops<T>::gemm(c, g6));
-    CK(rmsnorm_bwd<T>(a.h_in, a.rstd1, M, d, lw.attn_norm, c->tmpf, c->dh, c->dh, (T*)nullptr, c->stream));
+    int S6 = 1;
+    CK(Ops<T>::gemm_parts(c, g6, S6));
+    CK(norm_bwd<T>(c, S6, a.h_in, a.rstd1, M, lw.attn_norm, c->tmpf, c->dh, c->dh, (T*)nullptr));
   }
   // the next chunk reads the updated fast weights and rewrites the saved activations
   if (c->overlap) {
@@ -583,8 +639,7 @@ int decode_step(ttt_ctx* c, int32_t* tok, int64_t ld) {
     int rc = layer_fwd<T>(c, l, c->hb, 1, c->pos, FULL, nullptr);
     if (rc) return rc;
   }
-  CK(rmsnorm_fwd<T>(c->hb, B, d, c->final_norm, (float)c->cfg.rms_eps, tp<T>(c->hf), c->rstd_tmp, (T*)nullptr, 1, 0,
-                    nullptr, c->stream));
+  CK(norm_fwd<T>(c, c->hb, B, c->final_norm, tp<T>(c->hf), c->rstd_tmp, (T*)nullptr, 1, 0, nullptr));
   GemmArgs gl = mk(c->hf, d, c->lm_head, d, B, c->V, d);
   gl.e.kind = EPI_F32;
   gl.e.c = c->logits;
@@ -828,6 +883,7 @@ int build(ttt_ctx* c, const ttt_weights* w) {
 }
 
 int reset_state(ttt_ctx* c) {
+  c->pend_parts = 0;
   const int64_t fsz = 3LL * c->f * c->d;
   for (int j = 0; j < c->Lq; ++j) {
     FastW& fw = c->fw[j];

@@ -927,6 +927,7 @@ hipError_t launch_splitk(const GemmArgs& g0, int S, int Ks, bool wide, hipStream
     dim3 grid(cdiv(g.N, 128), cdiv(g.M, 128), g.batch * S);
     hipLaunchKernelGGL(kern, grid, dim3(256), shm, s, g);
   }
+  if (g0.defer) return hipGetLastError();  // the caller sums the parts
   const int64_t total = (int64_t)g.batch * g.M * g.N;
   const bool vec = g.N % 4 == 0 && g.e.ldc % 4 == 0 && g.e.sc % 4 == 0 && ((uintptr_t)g.e.c % 16) == 0 &&
                    ((uintptr_t)g.ws % 16) == 0;

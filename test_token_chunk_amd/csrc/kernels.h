@@ -73,6 +73,7 @@ struct GemmArgs {
   Epi e;
   float* ws = nullptr;    // optional fp32 workspace: lets small-grid GEMMs split K (EPI_F32/EPI_T/EPI_ADD_F32)
   int64_t ws_floats = 0;
+  bool defer = false;     // a K split leaves its fp32 parts in ws ([S][batch][M][N]) for the caller to sum
 };
 
 hipError_t gemm_simt_f32(const GemmArgs& g, hipStream_t s);   // fp32 operands
@@ -95,6 +96,18 @@ template <typename T>
 hipError_t rmsnorm_bwd(const float* x, const float* rstd, int64_t M, int d, const float* g, const float* dy,
                        const float* resid, float* out, T* outT, hipStream_t s);
 // fp32 [B*n][d] -> T copy [B*n][d] (optional) and transposed T [B][d][ldT] (optional)
+// consumers of a K-split GEMM's fp32 parts ([S][M][d], plane = M * d floats apart), summed
+// in order in the row kernel: h += sum, then RMSNorm forward (as rmsnorm_fwd); RMSNorm
+// backward with dy = sum (as rmsnorm_bwd).  d % 4 == 0, d <= 4096 (row_parts_ok), 16-byte
+// aligned rows; hipErrorInvalidValue otherwise.
+bool row_parts_ok(int d);
+template <typename T>
+hipError_t add_rmsnorm_fwd_parts(float* h, const float* parts, int S, int64_t plane, int64_t M, int d, const float* g,
+                                 float eps, T* y, float* rstd, T* yT, int rows_per_batch, int64_t ldT, float* xcopy,
+                                 hipStream_t s);
+template <typename T>
+hipError_t rmsnorm_bwd_parts(const float* x, const float* rstd, int64_t M, int d, const float* g, const float* parts,
+                             int S, int64_t plane, const float* resid, float* out, T* outT, hipStream_t s);
 template <typename T>
 hipError_t convert_rows(const float* x, int64_t M, int d, T* y, T* yT, int rows_per_batch, int64_t ldT,
                         hipStream_t s);
