@@ -31,7 +31,11 @@ constexpr int BQ = NW * QW;
 template <int HD>
 struct FwdSmem {
   bf16 k[2][KT][HD + 8];   // K tile, row = key
-  bf16 vt[3][HD][KT + 8];  // V^T tile, row = head dim (ring of 3: read one and two tiles late)
+  // V^T tile, row = head dim (ring of 3: read one and two tiles late).  Rows are 34 dwords
+  // apart: the 8-byte fragment reads of 32 lanes (32 consecutive rows, one column) then fall
+  // on 32 distinct bank pairs (17 r mod 32 is a permutation), where a 36-dword stride repeats
+  // every 16 rows and conflicts two ways.
+  bf16 vt[3][HD][KT + 4];
 };
 
 // two floats -> packed bf16 pair, round to nearest even (one v_cvt_pk_bf16_f32 on gfx950)
@@ -144,7 +148,11 @@ __global__ __launch_bounds__(NW * 64) void k_swa_fwd(AttnArgs a, int S) {
 #define STV(i, src)                                                                \
   if constexpr (VCH > i) {                                                         \
     const int c = tid + i * NT, r = c / (KT / 8), col = (c % (KT / 8)) * 8;        \
-    if (c < KT * HD / 8) *(uint4*)&sm.vt[vbuf][r][col] = src;                      \
+    if (c < KT * HD / 8) { /* rows are 8-byte aligned only */                      \
+      uint2* d = (uint2*)&sm.vt[vbuf][r][col];                                     \
+      d[0] = make_uint2(src.x, src.y);                                             \
+      d[1] = make_uint2(src.z, src.w);                                             \
+    }                                                                              \
   }
 #define STORE_TILE(buf_, vbuf_)                                                    \
   {                                                                                \
@@ -196,6 +204,14 @@ __global__ __launch_bounds__(NW * 64) void k_swa_fwd(AttnArgs a, int S) {
     s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qv, s0, 0, 0, 0);       \
     s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qv, s1, 0, 0, 0);       \
   }
+#define EXP_TILE(PA, PB) \
+_Pragma("unroll") \
+    for (int r = 0; r < 16; r += 2) { \
+      PA[r >> 1] = pk2(ex2(s0[r]), ex2(s0[r + 1])); \
+      PB[r >> 1] = pk2(ex2(s1[r]), ex2(s1[r + 1])); \
+      psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, PA[r >> 1]), ones, psum, false); \
+      psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, PB[r >> 1]), ones, psum, false); \
+    }
 #define FWD_TILE(it, PA, PB, QA, QB) \
   { \
     const int cur = it & 1; \
@@ -231,15 +247,21 @@ _Pragma("unroll") \
         if (!(off + 32 <= hi && off + 32 > lo)) s1[r] = -INFINITY; \
       } \
     } \
-    /* lazy reference max (log2 units): it moves only when the tile's max passes it by more */ \
-    /* than 8, so exponentials stay <= 2^8 and O is rarely rescaled (the result does not */ \
-    /* depend on the reference); the pair of lanes of a query shares it.  The first tile */ \
-    /* (no reference yet) always sets it. */ \
-    float tmax = -INFINITY; \
-_Pragma("unroll") \
-    for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, fmaxf(s0[r], s1[r])); \
+    /* probabilities against the current reference, and their row sums: dot products of the */ \
+    /* bf16 values that feed the PV product, per lane (the pair's sums are added at the end) */ \
+    float psum = 0.f; \
+    EXP_TILE(PA, PB) \
+    /* lazy reference max (log2 units): it stays while every lane's sum of the tile's */ \
+    /* probabilities is at most 2^12 (so each is), which needs no maximum over the tile; */ \
+    /* otherwise (and on the first tile, with no reference yet) the tile's maximum moves it */ \
+    /* when it passes the reference by more than 8, O is rescaled and the probabilities */ \
+    /* are redone.  The result does not depend on the reference; the pair of lanes of a */ \
+    /* query shares it. */ \
     float corr = 1.f; \
-    if (__any(tmax > 8.f || mref == -INFINITY)) { \
+    if (__any(!(psum <= 4096.f) || mref == -INFINITY)) { \
+      float tmax = -INFINITY; \
+_Pragma("unroll") \
+      for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, fmaxf(s0[r], s1[r])); \
       /* what the accumulators had subtracted */ \
       const float base = mref == -INFINITY ? 0.f : mref; \
       const float pmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) + base; \
@@ -254,16 +276,8 @@ _Pragma("unroll") \
       } \
 _Pragma("unroll") \
       for (int i = 0; i < HM; ++i) o[i] *= corr; \
-    } \
-    /* row sums: dot products of the bf16 probabilities that feed the PV product, per lane */ \
-    /* (the pair's sums are added at the end) */ \
-    float psum = 0.f; \
-_Pragma("unroll") \
-    for (int r = 0; r < 16; r += 2) { \
-      PA[r >> 1] = pk2(ex2(s0[r]), ex2(s0[r + 1])); \
-      PB[r >> 1] = pk2(ex2(s1[r]), ex2(s1[r + 1])); \
-      psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, PA[r >> 1]), ones, psum, false); \
-      psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, PB[r >> 1]), ones, psum, false); \
+      psum = 0.f; \
+      EXP_TILE(PA, PB) \
     } \
     lrun = lrun * corr + psum; \
     if (!late) PV(it % 3, PA, PB) \
@@ -284,6 +298,7 @@ _Pragma("unroll") \
     }
   }
 #undef FWD_TILE
+#undef EXP_TILE
 #undef SSTEP
   if (late && it_beg < ntiles) {
     if ((ntiles - it_beg) & 1)

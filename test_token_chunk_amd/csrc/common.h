@@ -90,3 +90,6 @@ static inline unsigned cdiv(int64_t a, int64_t b) { return (unsigned)((a + b - 1
 // wait until at most n vector-memory operations are outstanding and all LDS operations are
 // done (gfx9 s_waitcnt: vmcnt in bits 15:14 and 3:0, expcnt 6:4, lgkmcnt 11:8)
 #define WAIT_VM_LDS(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4))
+// wait until at most n vector-memory operations are outstanding, LDS operations untouched
+// (direct-to-LDS loads count as vector-memory operations until their data is in LDS)
+#define WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))

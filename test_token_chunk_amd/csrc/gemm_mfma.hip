@@ -442,11 +442,11 @@ __global__ __launch_bounds__(256) void k_gemm_dl(GemmArgs g) {
   for (int kt = 0; kt < nk; ++kt) {
     const int later = min(STAGES - 2, nk - 1 - kt);  // tiles issued after tile kt
     if (later >= 2)
-      WAIT_VM_LDS(2 * LPT);
+      WAIT_VM(2 * LPT);
     else if (later == 1)
-      WAIT_VM_LDS(LPT);
+      WAIT_VM(LPT);
     else
-      WAIT_VM_LDS(0);
+      WAIT_VM(0);
     __builtin_amdgcn_s_barrier();  // tile kt is in LDS for all waves; stage of tile kt-1 is free
     if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1);
     const unsigned char* a_base = smem_raw + (kt % STAGES) * DL_TILE_BYTES;
@@ -477,14 +477,14 @@ __global__ __launch_bounds__(256) void k_gemm_dl(GemmArgs g) {
 
 // ------------------------------------------------------------------ wide tiles
 // BM x 256 block tile, 8 waves in a 2 x 4 grid, each wave (BM/2) x 64 = (BM/64) x 2 MFMA
-// tiles; one block (two waves per SIMD) per CU.  Two configurations:
-//   BM = 256: K steps of 32 through a ring of 4 stages (32 KB each), wave tile 128 x 64;
-//   BM = 128: K steps of 64 through a ring of 3 stages (48 KB each), wave tile 64 x 64.
-// A wave tile of 128 x 64 reads 0.75 KB of operands from LDS per MFMA instead of the
-// 1 KB of a 64 x 64 one; on CDNA4 the 64 x 64 tile is bound by LDS bandwidth.
+// tiles, one block (two waves per SIMD) per CU (NW = 4, a 2 x 2 grid of (BM/2) x 128 wave
+// tiles at one wave per SIMD, halves the LDS reads per MFMA but measured no faster: LDS
+// reads are conflict-free and rarely waited on).  Two configurations:
+//   BM = 256: K steps of 32 through a ring of 4 stages (32 KB each; 5 measured no faster);
+//   BM = 128: K steps of 64 through a ring of 3 stages (48 KB each).
 //
-// Operands go straight from global memory to LDS (global_load_lds), a step WST - 2 steps
-// ahead of its use.  LDS rows hold one K step of one operand row (64 or 128 bytes) with the
+// Operands go straight from global memory to LDS (global_load_lds), WST - 2 steps ahead of
+// the step being published.  LDS rows hold one K step of one operand row (64 or 128 bytes) with the
 // 16-byte chunks XOR-swizzled by (row / 4) % 4 or (row / 2) % 8, which puts the 16 rows read
 // by a quarter-wave on distinct banks.  Inside a step the fragments of the next 16-deep
 // slice are read while the MFMAs of the current one run, across the step boundary too:
@@ -506,7 +506,6 @@ struct WideCfg {
   static constexpr int ST = BM == 256 ? 4 : 3;       // ring stages
   static constexpr int RB = BK * 2;                  // LDS row bytes
   static constexpr int SBYTES = (BM + 256) * RB;     // one stage
-  static constexpr int LPT = (BM + 256) * RB / 1024 / 8;  // 1 KB DMA blocks per wave per step
 };
 
 template <int BM, int EK>
@@ -524,10 +523,10 @@ __device__ __forceinline__ int wide_swz(int row) {
 
 // Epilogue of the wide tiles: lane holds C[m][n .. n+3] with m = m0 + wm0 + 32 i + (l % 32),
 // n = n0 + wn0 + 32 j + 8 q + 4 (l / 32) in acc[i][j][4q .. 4q+3].
-template <int BM, int EK, bool SPLIT, int TM, int TN>
+template <int BM, int EK, bool SPLIT, int TM, int TN, int NT>
 __device__ __forceinline__ void wide_epilogue(const GemmArgs& g, f32x16 (&acc)[TM][TN], unsigned char* smem_raw,
                                               int m0, int n0, int wm0, int wn0, int tid, int bz, int split) {
-  constexpr int BN = 256, NT = 512;
+  constexpr int BN = 256;
   const int lane = tid & 63, lr = lane & 31, hi = lane >> 5;
   const Epi& e = g.e;
   constexpr bool TR = EK == EPI_SGD || EK == EPI_SWIGLU_IL || EK == EPI_SWIGLU_BWD;
@@ -542,15 +541,17 @@ __device__ __forceinline__ void wide_epilogue(const GemmArgs& g, f32x16 (&acc)[T
   for (int i = 0; i < TM; ++i) {
     const int ml = wm0 + i * 32 + lr, m = m0 + ml;
     if constexpr (EK == EPI_SWIGLU_IL) {
-      static_assert(TN == 2, "gate and up halves of one 64-column group");
+      static_assert(TN % 2 == 0, "gate and up halves of 64-column groups");
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int fl = wn0 / 2 + 8 * q + 4 * hi, fi = n0 / 2 + fl;
+      for (int pq = 0; pq < 2 * TN; ++pq) {
+        // column group pq / 4 of the wave: accumulators 2 (pq / 4) (gate) and 2 (pq / 4) + 1 (up)
+        const int q = pq % 4, jg = 2 * (pq / 4);
+        const int fl = (wn0 + 32 * jg) / 2 + 8 * q + 4 * hi, fi = n0 / 2 + fl;
         float x[4], u[4], a[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          x[r] = acc[i][0][4 * q + r];
-          u[r] = acc[i][1][4 * q + r];
+          x[r] = acc[i][jg][4 * q + r];
+          u[r] = acc[i][jg + 1][4 * q + r];
           a[r] = x[r] / (1.f + __expf(-x[r])) * u[r];
           tr0[(fl + r) * TLD + ml] = f2bf(a[r]);
         }
@@ -654,13 +655,16 @@ __device__ __forceinline__ void wide_epilogue(const GemmArgs& g, f32x16 (&acc)[T
   }
 }
 
-template <int BM, int EK, bool SPLIT>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_gemm_wide(GemmArgs g) {
+template <int BM, int EK, bool SPLIT, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void k_gemm_wide(GemmArgs g) {
   using C = WideCfg<BM>;
-  constexpr int BN = 256, BK = C::BK, WST = C::ST, RB = C::RB, SBYTES = C::SBYTES, LPT = C::LPT;
-  constexpr int WM = BM / 2, WN = 64, TM = WM / 32, TN = WN / 32;
+  constexpr int BN = 256, BK = C::BK, WST = C::ST, RB = C::RB, SBYTES = C::SBYTES;
+  // NW = 8: 2 x 4 waves of (BM / 2) x 64; NW = 4: 2 x 2 waves of (BM / 2) x 128 (half the
+  // fragment reads from LDS per MFMA, one wave per SIMD)
+  constexpr int WM = BM / 2, WN = 2 * BN / NW, TM = WM / 32, TN = WN / 32;
   constexpr int RPB = 1024 / RB, CPR = RB / 16, NH = BK / 16;
-  constexpr int ABYTES = BM * RB, ABLK = BM / RPB / 8, BBLK = BN / RPB / 8;
+  constexpr int ABYTES = BM * RB, ABLK = BM / RPB / NW, BBLK = BN / RPB / NW;
+  constexpr int LPT = ABLK + BBLK;  // 1 KB DMA blocks per wave per step
   extern __shared__ __align__(16) unsigned char smem_raw[];
   const int S = SPLIT ? (int)g.e.ldt : 1;
   const int tiles_m = g.M / BM, tiles_n = g.N / BN, tiles = tiles_m * tiles_n;
@@ -679,7 +683,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const bf16* A = (const bf16*)g.A + bz * g.sA;
   const bf16* B = (const bf16*)g.B + bz * g.sB;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int wm0 = (wid >> 2) * WM, wn0 = (wid & 3) * WN;
+  const int wm0 = (wid / (NW / 2)) * WM, wn0 = (wid % (NW / 2)) * WN;
   const int nk = (kend - kbeg) / BK;
   // 1 KB DMA block = RPB rows; lane L lands at row L / CPR, physical chunk L % CPR and
   // fetches the logical chunk the swizzle puts there.  Wave w copies A blocks
@@ -728,14 +732,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     _Pragma("unroll") for (int j = 0; j < TN; ++j)                                             \
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
 #define SB() __builtin_amdgcn_sched_barrier(0)
-  // waits until at most `later` steps of DMA are outstanding (later <= 2 here)
+  // waits until at most `later` steps of DMA are outstanding (later <= 3 here)
 #define WAIT_STEPS(later)                                                                      \
   {                                                                                            \
-    if ((later) >= 2) WAIT_VM_LDS(2 * LPT);                                                    \
-    else if ((later) == 1) WAIT_VM_LDS(LPT);                                                   \
-    else WAIT_VM_LDS(0);                                                                       \
+    if ((later) >= 3) WAIT_VM(3 * LPT);                                                        \
+    else if ((later) == 2) WAIT_VM(2 * LPT);                                                   \
+    else if ((later) == 1) WAIT_VM(LPT);                                                       \
+    else WAIT_VM(0);                                                                           \
   }
-  static_assert(WST - 2 <= 2 && WST >= 3, "ring depth");
+  static_assert(WST - 2 <= 3 && WST >= 3, "ring depth");
 
   // prologue: steps 0 .. WST-2 in flight, step 0 published, its first slice in registers
   for (int st = 0; st < WST - 1 && st < nk; ++st) issue(st);
@@ -786,12 +791,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #undef WAIT_STEPS
   WAIT_VM_LDS(0);
   __syncthreads();  // every wave is done with the operand buffers
-  wide_epilogue<BM, EK, SPLIT, TM, TN>(g, acc, smem_raw, m0, n0, wm0, wn0, tid, bz, split);
+  wide_epilogue<BM, EK, SPLIT, TM, TN, 64 * NW>(g, acc, smem_raw, m0, n0, wm0, wn0, tid, bz, split);
 }
 
-template <int BM, int EK, bool SPLIT>
+template <int BM, int EK, bool SPLIT, int NW = 8>
 hipError_t launch_wide(const GemmArgs& g, int S, hipStream_t s) {
-  auto kern = k_gemm_wide<BM, EK, SPLIT>;
+  auto kern = k_gemm_wide<BM, EK, SPLIT, NW>;
   constexpr size_t shm = wide_lds_bytes<BM, EK>();
   static bool attr_set = false;
   if (!attr_set) {
@@ -800,7 +805,7 @@ hipError_t launch_wide(const GemmArgs& g, int S, hipStream_t s) {
     attr_set = true;
   }
   const int64_t tiles = (int64_t)(g.M / BM) * (g.N / 256) * g.batch * S;
-  hipLaunchKernelGGL(kern, dim3((unsigned)(8 * cdiv(tiles, 8))), dim3(512), shm, s, g);
+  hipLaunchKernelGGL(kern, dim3((unsigned)(8 * cdiv(tiles, 8))), dim3(64 * NW), shm, s, g);
   return hipGetLastError();
 }
 
