@@ -1113,7 +1113,7 @@ hipError_t launch_bwd(const AttnBwdArgs& a, hipStream_t s) {
   // transposed tiles are read with 16-byte copies when the caller provides the
   // transposed key ring and a dO^T scratch, 8-key groups stay inside the ring
   // (R % 8 == 0) and 8-query groups inside the chunk (n % 8 == 0)
-  if (tr)
+  if (tr && !a.dot_ready)
     hipLaunchKernelGGL(k_heads_transpose, dim3(cdiv(a.n, 64), cdiv(a.H * HD, 64), a.B), dim3(256), 0, s,
                        (const bf16*)a.dout, (bf16*)a.dot, a.n, a.H, HD);
   const int64_t blocks8 = (int64_t)cdiv(a.n, 8 * QW) * a.H * a.B;

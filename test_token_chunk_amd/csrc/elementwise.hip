@@ -243,6 +243,53 @@ __global__ __launch_bounds__(256) void k_transpose_rows(const bf16* __restrict__
   }
 }
 
+// sum of S fp32 parts [S][B*n][d] (plane floats apart, in order) -> y [B][n][d] and
+// yT [B][d][n] (bf16), 64 rows x 64 columns per block through the same LDS tile as above
+// (d % 4 == 0, n % 8 == 0)
+__global__ __launch_bounds__(256) void k_parts_rows_t(const float* __restrict__ parts, int S, int64_t plane, int n,
+                                                      int d, bf16* __restrict__ y, bf16* __restrict__ yt) {
+  __shared__ __align__(16) uint16_t tile[64][72];  // [token][column]
+  const int t0 = blockIdx.x * 64, c0 = blockIdx.y * 64, b = blockIdx.z;
+  const int tid = threadIdx.x, c4 = tid & 15, r0 = tid >> 4, c = c0 + 4 * c4;
+  float4 acc[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) acc[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int sp = 0; sp < S; ++sp) {
+    float4 v[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int t = t0 + r0 + 16 * k;
+      v[k] = (t < n && c < d) ? *(const float4*)(parts + sp * plane + ((int64_t)b * n + t) * d + c)
+                              : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      acc[k].x += v[k].x;
+      acc[k].y += v[k].y;
+      acc[k].z += v[k].z;
+      acc[k].w += v[k].w;
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int r = r0 + 16 * k, t = t0 + r;
+    const uint2 w = make_uint2((uint32_t)f2bf(acc[k].x).x | ((uint32_t)f2bf(acc[k].y).x << 16),
+                               (uint32_t)f2bf(acc[k].z).x | ((uint32_t)f2bf(acc[k].w).x << 16));
+    if (t < n && c < d) *(uint2*)(y + ((int64_t)b * n + t) * d + c) = w;
+    *(uint2*)&tile[r][4 * c4] = w;
+  }
+  __syncthreads();
+  for (int e = tid; e < 64 * 8; e += 256) {
+    const int cr = e >> 3, tch = (e & 7) * 8, cc = c0 + cr, t = t0 + tch;
+    if (cc < d && t < n) {
+      uint32_t w[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) w[k] = (uint32_t)tile[tch + 2 * k][cr] | ((uint32_t)tile[tch + 2 * k + 1][cr] << 16);
+      *(uint4*)(yt + ((int64_t)b * d + cc) * n + t) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  }
+}
+
 __global__ void k_count_valid(const int32_t* tgt, int64_t ld, int n, int* nvalid) {
   __shared__ float sh[16];
   int b = blockIdx.x;
@@ -824,6 +871,17 @@ hipError_t refresh_shadows(const float* master, int rows, int cols, int batch, i
   return hipGetLastError();
 }
 
+template <typename T>
+hipError_t parts_rows_t(const float* parts, int S, int64_t plane, int64_t M, int d, int rpb, T* y, T* yT,
+                        hipStream_t s) {
+  if (sizeof(T) != 2 || S < 1 || rpb <= 0 || M % rpb != 0 || rpb % 8 != 0 || d % 4 != 0 || plane % 4 != 0 ||
+      !al16(parts) || !al16(y) || !al16(yT))
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_parts_rows_t, dim3(cdiv(rpb, 64), cdiv(d, 64), (unsigned)(M / rpb)), dim3(256), 0, s, parts,
+                     S, plane, rpb, d, (bf16*)y, (bf16*)yT);
+  return hipGetLastError();
+}
+
 #define INST(T)                                                                                                      \
   template hipError_t embed_gather_ld<T>(const int32_t*, int64_t, int, int, const T*, int, int, float*, int*,       \
                                          hipStream_t);                                                              \
@@ -836,6 +894,7 @@ hipError_t refresh_shadows(const float* master, int rows, int cols, int batch, i
   template hipError_t rmsnorm_bwd<T>(const float*, const float*, int64_t, int, const float*, const float*,          \
                                      const float*, float*, T*, hipStream_t);                                        \
   template hipError_t convert_rows<T>(const float*, int64_t, int, T*, T*, int, int64_t, hipStream_t);               \
+  template hipError_t parts_rows_t<T>(const float*, int, int64_t, int64_t, int, int, T*, T*, hipStream_t);          \
   template hipError_t ce_rows_ld<T>(const float*, int64_t, int, const int32_t*, int64_t, const int*, int, float*,   \
                                     T*, int*, hipStream_t);                                                         \
   template hipError_t rope_bwd_pack<T>(const float*, const float*, const float*, const float*, const float*,        \

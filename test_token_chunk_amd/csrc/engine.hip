@@ -567,8 +567,14 @@ int top_chunk(ttt_ctx* c, const int32_t* tgt, int64_t ld, const float* hsrc, int
     g5.e.kind = EPI_T;
     g5.e.c = c->dO;
     g5.e.ldc = d;
-    CK(Ops<T>::gemm(c, g5));
+    int S5 = 1;
+    CK(Ops<T>::gemm_parts(c, g5, S5));
     AttnBwdArgs ab;
+    if (S5 > 1) {
+      // one pass sums the K-split parts into dO and its per-head transpose for the backward
+      CK(parts_rows_t<T>(c->ws, S5, M * d, M, d, n, tp<T>(c->dO), tp<T>(c->dOT), c->stream));
+      ab.dot_ready = true;
+    }
     ab.q = a.q;
     ab.qt = a.qt;
     ab.kr = lw.kr;

@@ -95,7 +95,6 @@ hipError_t rmsnorm_fwd(const float* x, int64_t M, int d, const float* g, float e
 template <typename T>
 hipError_t rmsnorm_bwd(const float* x, const float* rstd, int64_t M, int d, const float* g, const float* dy,
                        const float* resid, float* out, T* outT, hipStream_t s);
-// fp32 [B*n][d] -> T copy [B*n][d] (optional) and transposed T [B][d][ldT] (optional)
 // consumers of a K-split GEMM's fp32 parts ([S][M][d], plane = M * d floats apart), summed
 // in order in the row kernel: h += sum, then RMSNorm forward (as rmsnorm_fwd); RMSNorm
 // backward with dy = sum (as rmsnorm_bwd).  d % 4 == 0, d <= 4096 (row_parts_ok), 16-byte
@@ -108,6 +107,13 @@ hipError_t add_rmsnorm_fwd_parts(float* h, const float* parts, int S, int64_t pl
 template <typename T>
 hipError_t rmsnorm_bwd_parts(const float* x, const float* rstd, int64_t M, int d, const float* g, const float* parts,
                              int S, int64_t plane, const float* resid, float* out, T* outT, hipStream_t s);
+// the sum of a K-split GEMM's fp32 parts ([S][M][d], plane = M * d floats apart, summed in
+// order) as y [M][d] and, transposed per batch of rpb rows, yT [M/rpb][d][rpb] (bf16 only;
+// d % 4 == 0, rpb % 8 == 0, 16-byte aligned; hipErrorInvalidValue otherwise)
+template <typename T>
+hipError_t parts_rows_t(const float* parts, int S, int64_t plane, int64_t M, int d, int rpb, T* y, T* yT,
+                        hipStream_t s);
+// fp32 [B*n][d] -> T copy [B*n][d] (optional) and transposed T [B][d][ldT] (optional)
 template <typename T>
 hipError_t convert_rows(const float* x, int64_t M, int d, T* y, T* yT, int rows_per_batch, int64_t ldT,
                         hipStream_t s);
@@ -158,6 +164,7 @@ struct AttnBwdArgs {
   int64_t pos0;
   float* ws = nullptr;  // optional fp32 workspace: lets small grids split the key range of dq
   int64_t ws_floats = 0;
+  bool dot_ready = false;  // dot already holds dO^T (written by the producer of dout)
 };
 template <typename T>
 hipError_t swa_bwd_simt(const AttnBwdArgs& a, hipStream_t s);
