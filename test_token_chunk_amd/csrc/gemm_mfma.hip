@@ -693,21 +693,24 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
   const bf16* Ag = A + (int64_t)(m0 + arow) * g.lda;
   const bf16* Bg = B + (int64_t)(n0 + brow) * g.ldb;
 
-  auto issue = [&](int kt) {
+  // DMA block i (0 .. LPT-1: A blocks, then B blocks) of step kt
+  auto issue_one = [&](int kt, int i) {
     unsigned char* base = smem_raw + (kt % WST) * SBYTES;
     const int k0 = kbeg + kt * BK;
-#pragma unroll
-    for (int i = 0; i < ABLK; ++i) {
+    if (i < ABLK) {
       const int lc = lpc ^ wide_swz<BK>(arow + i * RPB);
       __builtin_amdgcn_global_load_lds(Ag + (int64_t)(i * RPB) * g.lda + k0 + lc * 8,
                                        LDSP(base + (wid * ABLK + i) * 1024), 16, 0, 0);
+    } else {
+      const int ib = i - ABLK;
+      const int lc = lpc ^ wide_swz<BK>(brow + ib * RPB);
+      __builtin_amdgcn_global_load_lds(Bg + (int64_t)(ib * RPB) * g.ldb + k0 + lc * 8,
+                                       LDSP(base + ABYTES + (wid * BBLK + ib) * 1024), 16, 0, 0);
     }
+  };
+  auto issue = [&](int kt) {
 #pragma unroll
-    for (int i = 0; i < BBLK; ++i) {
-      const int lc = lpc ^ wide_swz<BK>(brow + i * RPB);
-      __builtin_amdgcn_global_load_lds(Bg + (int64_t)(i * RPB) * g.ldb + k0 + lc * 8,
-                                       LDSP(base + ABYTES + (wid * BBLK + i) * 1024), 16, 0, 0);
-    }
+    for (int i = 0; i < LPT; ++i) issue_one(kt, i);
   };
 
   f32x16 acc[TM][TN];
@@ -732,6 +735,15 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
     _Pragma("unroll") for (int j = 0; j < TN; ++j)                                             \
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
 #define SB() __builtin_amdgcn_sched_barrier(0)
+  // The DMA of step kt + WST - 1 is spread over the MFMA rows that follow the barrier (2 TM - 1
+  // slots: rows 1 .. TM-1 of half-step NH-2, rows 0 .. TM-1 of half-step NH-1): issued in one
+  // burst, the queue of vector-memory instructions stalls the wave in front of its MFMAs.
+  // DMA block i goes after slot i (2 TM - 1) / LPT.
+  constexpr int NSLOT = 2 * TM - 1;
+#define DMA_SLOT(slot)                                                                         \
+  if (pend) {                                                                                  \
+    _Pragma("unroll") for (int i = 0; i < LPT; ++i) if (i * NSLOT / LPT == (slot)) issue_one(kt + WST - 1, i); \
+  }
   // waits until at most `later` steps of DMA are outstanding (later <= 3 here)
 #define WAIT_STEPS(later)                                                                      \
   {                                                                                            \
@@ -754,6 +766,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
     // invariant: f0 holds slice 0 of step kt; step kt is published; every wave has finished
     // reading step kt - 1
     const bool more = kt + 1 < nk;
+    const bool pend = kt + WST - 1 < nk;
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
       if ((h & 1) == 0) {
@@ -766,13 +779,18 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
           // tells that every wave is past its reads of step kt - 1, whose stage is reused next
           WAIT_STEPS(min(WST - 3, nk - 2 - kt));
           __builtin_amdgcn_s_barrier();
-          if (kt + WST - 1 < nk) issue(kt + WST - 1);
         }
         SB();
-        MFMA_ROWS(f0a, f0b, 1, TM)
-        SB();
+        _Pragma("unroll") for (int r = 1; r < TM; ++r) {
+          MFMA_ROWS(f0a, f0b, r, r + 1)
+          SB();
+          if (h == NH - 2) DMA_SLOT(r - 1)
+          SB();
+        }
       } else {
         MFMA_ROWS(f1a, f1b, 0, 1)
+        SB();
+        if (h == NH - 1) DMA_SLOT(TM - 1)
         SB();
         if (h + 1 < NH) {
           FRAGS(f0a, f0b, kt, h + 1)
@@ -780,13 +798,18 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
           FRAGS(f0a, f0b, kt + 1, 0)
         }
         SB();
-        MFMA_ROWS(f1a, f1b, 1, TM)
-        SB();
+        _Pragma("unroll") for (int r = 1; r < TM; ++r) {
+          MFMA_ROWS(f1a, f1b, r, r + 1)
+          SB();
+          if (h == NH - 1) DMA_SLOT(TM - 1 + r)
+          SB();
+        }
       }
     }
   }
 #undef FRAGS
 #undef MFMA_ROWS
+#undef DMA_SLOT
 #undef SB
 #undef WAIT_STEPS
   WAIT_VM_LDS(0);
