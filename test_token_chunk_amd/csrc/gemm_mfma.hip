@@ -411,18 +411,20 @@ __global__ __launch_bounds__(256) void k_gemm_dl(GemmArgs g) {
   const int wm0 = (wid >> 1) * WM, wn0 = (wid & 1) * WN;
   const int nk = (kend - kbeg) / BK;
 
-  auto issue = [&](int kt) {
+  // 1 KB blocks i = 0..3 of the A and B tiles of step kt (8 rows each)
+  auto issue_one = [&](int kt, int i) {
     unsigned char* base = smem_raw + (kt % STAGES) * DL_TILE_BYTES;
     const int k0 = kbeg + kt * BK;
+    const int blk = wid * 4 + i;          // 8-row block of the tile (1 KB)
+    const int r = blk * 8 + (lane >> 3);  // tile row of this lane
+    const int c = (lane & 7) ^ (r & 7);   // logical chunk that lands at physical chunk lane & 7
+    __builtin_amdgcn_global_load_lds(A + (int64_t)(m0 + r) * g.lda + k0 + c * 8, LDSP(base + blk * 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(B + (int64_t)(n0 + r) * g.ldb + k0 + c * 8,
+                                     LDSP(base + BM * BK * 2 + blk * 1024), 16, 0, 0);
+  };
+  auto issue = [&](int kt) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int blk = wid * 4 + i;          // 8-row block of the tile (1 KB)
-      const int r = blk * 8 + (lane >> 3);  // tile row of this lane
-      const int c = (lane & 7) ^ (r & 7);   // logical chunk that lands at physical chunk lane & 7
-      __builtin_amdgcn_global_load_lds(A + (int64_t)(m0 + r) * g.lda + k0 + c * 8, LDSP(base + blk * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(B + (int64_t)(n0 + r) * g.ldb + k0 + c * 8,
-                                       LDSP(base + BM * BK * 2 + blk * 1024), 16, 0, 0);
-    }
+    for (int i = 0; i < 4; ++i) issue_one(kt, i);
   };
 
   f32x16 acc[TM][TN];
@@ -448,23 +450,48 @@ __global__ __launch_bounds__(256) void k_gemm_dl(GemmArgs g) {
     else
       WAIT_VM(0);
     __builtin_amdgcn_s_barrier();  // tile kt is in LDS for all waves; stage of tile kt-1 is free
-    if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1);
+    // the DMA of tile kt + STAGES - 1 goes out between the MFMAs of this step, a block pair per
+    // 16-deep slice (in one burst the vector-memory queue stalls the wave in front of them)
+    const bool pend = kt + STAGES - 1 < nk;
     const unsigned char* a_base = smem_raw + (kt % STAGES) * DL_TILE_BYTES;
     const unsigned char* b_base = a_base + BM * BK * 2;
-#pragma unroll
-    for (int kk = 0; kk < BK; kk += 16) {
-      const int p = (((kk + lk) >> 3) ^ sw) << 4;  // physical byte offset of the logical chunk
-      bf16x8 af[TM], bfr[TN];
+    // fragments of the 16-deep slice kk (logical chunk (kk + lk) / 8 at its swizzled place);
+    // those of the next slice are read while the MFMAs of this one run
+    auto frags = [&](int kk, bf16x8 (&af)[TM], bf16x8 (&bfr)[TN]) {
+      const int p = (((kk + lk) >> 3) ^ sw) << 4;
 #pragma unroll
       for (int i = 0; i < TM; ++i) af[i] = *(const bf16x8*)(a_base + (wm0 + i * 32 + lr) * 128 + p);
 #pragma unroll
       for (int j = 0; j < TN; ++j) bfr[j] = *(const bf16x8*)(b_base + (wn0 + j * 32 + lr) * 128 + p);
+    };
+    bf16x8 af0[TM], bf0[TN], af1[TM], bf1[TN];
+    frags(0, af0, bf0);
+#pragma unroll
+    for (int kk = 0; kk < BK; kk += 16) {
+      bf16x8 (&af)[TM] = (kk / 16) % 2 ? af1 : af0;
+      bf16x8 (&bfr)[TN] = (kk / 16) % 2 ? bf1 : bf0;
+      if (kk + 16 < BK) {
+        if ((kk / 16) % 2) frags(kk + 16, af0, bf0);
+        else frags(kk + 16, af1, bf1);
+      }
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
           acc[i][j] = SGD ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0)
                           : __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+      // (with 2 stages the next tile is waited for at the top of the next step: its DMA goes
+      // out over the first half of this one)
+      if (pend) {
+        if constexpr (STAGES == 2) {
+          if (kk < BK / 2) {
+            issue_one(kt + 1, 2 * (kk / 16));
+            issue_one(kt + 1, 2 * (kk / 16) + 1);
+          }
+        } else {
+          issue_one(kt + STAGES - 1, kk / 16);
+        }
+      }
     }
   }
   WAIT_VM_LDS(0);
