@@ -39,3 +39,7 @@ MID_T = 680
 MIDK = dict(n_layers=2, d_model=1024, n_heads=8, d_ff=1024, vocab=512, window=256, chunk=128, n_fast=1, batch=1,
             rope_theta=1e4, rms_eps=1e-5, lr=1e-2, dtype="bf16")
 MIDK_T = 256
+# the same width with two fast blocks: the upper block's attention backward runs, its dO comes
+# from the K-split W_o^T product (parts summed together with dO's per-head transpose) and the
+# RMSNorm backward kernels sum K-split parts
+MIDK2 = dict(MIDK, n_layers=3, n_fast=2)

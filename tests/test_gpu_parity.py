@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 
 from oracle import Oracle
-from tests.cfgs import MID, MID_T, MIDK, MIDK_T, TOY, cfg as mkcfg
+from tests.cfgs import MID, MID_T, MIDK, MIDK2, MIDK_T, TOY, cfg as mkcfg
 from test_token_chunk_amd import synth
 
 pytestmark = pytest.mark.gpu
@@ -102,6 +102,20 @@ def test_midk_split_k_epilogues_parity():
     print(f"midk: max loss rel err {rel:.3e}")
     assert rel <= tl
     compare_fast(ctx.fast_weights(0), o.get_fast(0), _w0(w, c), tw, "midk")
+
+
+def test_midk_two_fast_blocks_split_k_consumers_parity():
+    """d=1024, two fast blocks, b=128: the row kernels that sum K-split parts (RMSNorm forward
+    and backward) and the kernel that sums the W_o^T product's parts into dO and its per-head
+    transpose for the attention backward of the upper fast block."""
+    c = mkcfg(**MIDK2)
+    print("case midk2", flush=True)
+    w, o, ctx, ref, got = run_pair(c, MIDK_T, dist="zipf")
+    tl, tw = TOL["bf16"]
+    rel = np.max(np.abs(got - ref) / np.abs(ref))
+    print(f"midk2: max loss rel err {rel:.3e}")
+    assert rel <= tl
+    compare_fast(ctx.fast_weights(0), o.get_fast(0), _w0(w, c), tw, "midk2")
 
 
 def test_toy_more_fast_blocks_and_ragged_tail():
