@@ -217,7 +217,8 @@ struct Ops<float> {
     if (!st) st = c->stream;
     return timed(c, g.e.kind, gemm_flops(g), st, [&] { return gemm_simt_f32(g, st); });
   }
-  static hipError_t gemm_parts(ttt_ctx* c, const GemmArgs& g, int& S) {
+  static hipError_t gemm_parts(ttt_ctx* c, const GemmArgs& g, int rpb, int& S) {
+    (void)rpb;
     S = 1;
     return gemm(c, g);
   }
@@ -246,13 +247,14 @@ struct Ops<bf16> {
     return timed(c, cls, gemm_flops(g), st,
                  [&] { return c->mfma ? gemm_mfma_bf16(g, st) : gemm_simt_bf16(g, st); });
   }
-  // a GEMM whose fp32 result [M][N] feeds a row kernel next: if it splits K, its S parts stay
-  // in the workspace for that kernel to sum (S > 1); otherwise it writes g.e.c (S = 1)
-  static hipError_t gemm_parts(ttt_ctx* c, const GemmArgs& g0, int& S) {
+  // a GEMM whose fp32 result [M][N] (batches of rpb rows) feeds a row kernel next: if it
+  // splits K, its S parts stay in the workspace for that kernel to sum (S > 1); otherwise it
+  // writes g.e.c (S = 1).  The consumers' transposed copies move 8-row groups: rpb % 8 == 0.
+  static hipError_t gemm_parts(ttt_ctx* c, const GemmArgs& g0, int rpb, int& S) {
     GemmArgs g = g0;
     g.ws = c->ws;
     g.ws_floats = c->ws_floats;
-    S = (c->mfma && (int64_t)g.M * g.batch >= 128 && row_parts_ok(g.N) && g.e.ldc == g.N &&
+    S = (c->mfma && rpb % 8 == 0 && (int64_t)g.M * g.batch >= 128 && row_parts_ok(g.N) && g.e.ldc == g.N &&
          g.e.sc == (g.batch > 1 ? (int64_t)g.M * g.N : g.e.sc))
             ? gemm_mfma_splits(g, nullptr)
             : 1;
@@ -373,7 +375,7 @@ int layer_fwd(ttt_ctx* c, int l, float* h, int n, int64_t p0, int mode, TopActs*
       return TTT_OK;
     }
     int So = 1;  // the MLP norm below sums a K split of the output projection
-    CK(Ops<T>::gemm_parts(c, go, So));
+    CK(Ops<T>::gemm_parts(c, go, n, So));
     c->pend_parts = So > 1 ? So : 0;
   }
   CK(norm_fwd<T>(c, h, M, w.mlp_norm, tp<T>(c->ub), sv ? sv->rstd2 : c->rstd_tmp, sv ? tp<T>(sv->mT) : (T*)nullptr,
@@ -408,7 +410,7 @@ int layer_fwd(ttt_ctx* c, int l, float* h, int n, int64_t p0, int mode, TopActs*
     gd.e.ldc = d;
     gd.e.sc = (int64_t)n * d;
     int Sd = 1;  // summed by the next norm forward (next block's attention norm or the final norm)
-    CK(Ops<T>::gemm_parts(c, gd, Sd));
+    CK(Ops<T>::gemm_parts(c, gd, n, Sd));
     c->pend_parts = Sd > 1 ? Sd : 0;
   } else {
     GemmArgs g = mk(c->ub, d, w.wgu, d, (int)M, c->il ? 2 * f : f, d);
@@ -422,7 +424,7 @@ int layer_fwd(ttt_ctx* c, int l, float* h, int n, int64_t p0, int mode, TopActs*
     gd.e.c = h;
     gd.e.ldc = d;
     int Sd = 1;
-    CK(Ops<T>::gemm_parts(c, gd, Sd));
+    CK(Ops<T>::gemm_parts(c, gd, n, Sd));
     c->pend_parts = Sd > 1 ? Sd : 0;
   }
   return TTT_OK;
@@ -470,7 +472,7 @@ int top_chunk(ttt_ctx* c, const int32_t* tgt, int64_t ld, const float* hsrc, int
   gx.e.c = c->tmpf;
   gx.e.ldc = d;
   int Sx = 1;
-  CK(Ops<T>::gemm_parts(c, gx, Sx));
+  CK(Ops<T>::gemm_parts(c, gx, n, Sx));
   CK(norm_bwd<T>(c, Sx, c->htop, c->rstdf, M, c->final_norm, c->tmpf, nullptr, c->dh, (T*)nullptr));
   const float lr = c->cfg.lr;
   const int64_t fsz = 3LL * f * d;
@@ -509,7 +511,7 @@ int top_chunk(ttt_ctx* c, const int32_t* tgt, int64_t ld, const float* hsrc, int
       g3.e.c = c->tmpf;
       g3.e.ldc = d;
       g3.e.sc = (int64_t)n * d;
-      CK(Ops<T>::gemm_parts(c, g3, S3));
+      CK(Ops<T>::gemm_parts(c, g3, n, S3));
     }
     // The weight gradients of this block with the fused SGD step run on the side stream,
     // overlapping the rest of the backward: their inputs (dy^T, dz^T of this block, act^T,
@@ -567,11 +569,11 @@ int top_chunk(ttt_ctx* c, const int32_t* tgt, int64_t ld, const float* hsrc, int
     g5.e.kind = EPI_T;
     g5.e.c = c->dO;
     g5.e.ldc = d;
+    // one pass sums K-split parts into dO and its per-head transpose for the backward
     int S5 = 1;
-    CK(Ops<T>::gemm_parts(c, g5, S5));
+    CK(Ops<T>::gemm_parts(c, g5, n, S5));
     AttnBwdArgs ab;
     if (S5 > 1) {
-      // one pass sums the K-split parts into dO and its per-head transpose for the backward
       CK(parts_rows_t<T>(c->ws, S5, M * d, M, d, n, tp<T>(c->dO), tp<T>(c->dOT), c->stream));
       ab.dot_ready = true;
     }
@@ -603,7 +605,7 @@ int top_chunk(ttt_ctx* c, const int32_t* tgt, int64_t ld, const float* hsrc, int
     g6.e.c = c->tmpf;
     g6.e.ldc = d;
     int S6 = 1;
-    CK(Ops<T>::gemm_parts(c, g6, S6));
+    CK(Ops<T>::gemm_parts(c, g6, n, S6));
     CK(norm_bwd<T>(c, S6, a.h_in, a.rstd1, M, lw.attn_norm, c->tmpf, c->dh, c->dh, (T*)nullptr));
   }
   // the next chunk reads the updated fast weights and rewrites the saved activations

@@ -118,6 +118,20 @@ def test_midk_two_fast_blocks_split_k_consumers_parity():
     compare_fast(ctx.fast_weights(0), o.get_fast(0), _w0(w, c), tw, "midk2")
 
 
+def test_midk_two_fast_blocks_ragged_chunk_parity():
+    """As above with chunks of 136 and a ragged last chunk of 130 rows (not a multiple of 8):
+    the K-split GEMMs of that chunk take the register-staged loop and dO is summed without
+    the transposed copy."""
+    c = mkcfg(**dict(MIDK2, chunk=136))
+    print("case midk2 ragged", flush=True)
+    w, o, ctx, ref, got = run_pair(c, 266, dist="zipf")
+    tl, tw = TOL["bf16"]
+    rel = np.max(np.abs(got - ref) / np.abs(ref))
+    print(f"midk2 ragged: max loss rel err {rel:.3e}")
+    assert rel <= tl
+    compare_fast(ctx.fast_weights(0), o.get_fast(0), _w0(w, c), tw, "midk2 ragged")
+
+
 def test_toy_more_fast_blocks_and_ragged_tail():
     """Two fast blocks (attention backward exercised), window 96 not a
     multiple of the chunk 40, T=300 (ragged last chunk), some targets ignored."""
