@@ -249,12 +249,14 @@ struct Ops<bf16> {
   }
   // a GEMM whose fp32 result [M][N] (batches of rpb rows) feeds a row kernel next: if it
   // splits K, its S parts stay in the workspace for that kernel to sum (S > 1); otherwise it
-  // writes g.e.c (S = 1).  The consumers' transposed copies move 8-row groups: rpb % 8 == 0.
+  // writes g.e.c (S = 1).  The consumers' transposed copies move 8-row groups into rows of
+  // rpb (dO^T) or of the chunk length b (the MLP input of the weight gradients): both % 8 == 0.
   static hipError_t gemm_parts(ttt_ctx* c, const GemmArgs& g0, int rpb, int& S) {
     GemmArgs g = g0;
     g.ws = c->ws;
     g.ws_floats = c->ws_floats;
-    S = (c->mfma && rpb % 8 == 0 && (int64_t)g.M * g.batch >= 128 && row_parts_ok(g.N) && g.e.ldc == g.N &&
+    S = (c->mfma && rpb % 8 == 0 && c->b % 8 == 0 && (int64_t)g.M * g.batch >= 128 && row_parts_ok(g.N) &&
+         g.e.ldc == g.N &&
          g.e.sc == (g.batch > 1 ? (int64_t)g.M * g.N : g.e.sc))
             ? gemm_mfma_splits(g, nullptr)
             : 1;

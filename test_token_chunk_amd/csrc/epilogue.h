@@ -46,7 +46,10 @@ __device__ __forceinline__ void epi_apply_k(const Epi& e, int bz, int m, int n, 
       float* p = e.master + bz * e.sm + (int64_t)m * e.ldm + n;
       float w = *p - e.lr * acc;
       *p = w;
-      ((T*)e.sh)[bz * e.ssh + (int64_t)m * e.ldsh + n] = from_f<T>(w);
+      // (il_f > 0: the row-major shadow keeps gate/up rows interleaved, as the SwiGLU
+      // epilogue of the forward reads them)
+      const int64_t shrow = e.il_f ? swiglu_il_row(m, e.il_f) : (int64_t)m;
+      ((T*)e.sh)[bz * e.ssh + shrow * e.ldsh + n] = from_f<T>(w);
       ((T*)e.shT)[bz * e.sshT + (int64_t)n * e.ldshT + m] = from_f<T>(w);
       break;
     }

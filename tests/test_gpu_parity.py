@@ -118,13 +118,14 @@ def test_midk_two_fast_blocks_split_k_consumers_parity():
     compare_fast(ctx.fast_weights(0), o.get_fast(0), _w0(w, c), tw, "midk2")
 
 
-def test_midk_two_fast_blocks_ragged_chunk_parity():
-    """As above with chunks of 136 and a ragged last chunk of 130 rows (not a multiple of 8):
-    the K-split GEMMs of that chunk take the register-staged loop and dO is summed without
-    the transposed copy."""
-    c = mkcfg(**dict(MIDK2, chunk=136))
-    print("case midk2 ragged", flush=True)
-    w, o, ctx, ref, got = run_pair(c, 266, dist="zipf")
+@pytest.mark.parametrize("chunk,T", [(136, 266), (132, 260)])
+def test_midk_two_fast_blocks_ragged_chunk_parity(chunk, T):
+    """As above with chunk lengths or a ragged last chunk that are not multiples of 8 (chunks
+    of 136 and a last one of 130 rows; chunks of 132 and a last one of 128): the K-split
+    products of those chunks are summed by their own pass, not left for the row kernels."""
+    c = mkcfg(**dict(MIDK2, chunk=chunk))
+    print(f"case midk2 ragged chunk {chunk} T {T}", flush=True)
+    w, o, ctx, ref, got = run_pair(c, T, dist="zipf")
     tl, tw = TOL["bf16"]
     rel = np.max(np.abs(got - ref) / np.abs(ref))
     print(f"midk2 ragged: max loss rel err {rel:.3e}")
