@@ -133,6 +133,37 @@ def test_midk_two_fast_blocks_ragged_chunk_parity(chunk, T):
     compare_fast(ctx.fast_weights(0), o.get_fast(0), _w0(w, c), tw, "midk2 ragged")
 
 
+# bf16 engine (matrix-core path) at shapes off the main workloads: name -> (config, T, mask)
+EDGE = {
+    # two batch rows, ragged last chunk (300 = 7 x 40 + 20), every 7th target masked
+    "batch2_ragged_masked": (dict(TOY, dtype="bf16", batch=2, n_fast=2, window=96, chunk=40, lr=3e-2), 300, True),
+    # head dim 64, every block fast (no frozen lower blocks), chunk 48 with a ragged tail
+    "hd64_all_fast": (dict(TOY, dtype="bf16", n_layers=3, d_model=192, n_heads=3, d_ff=384, window=64, chunk=48,
+                           n_fast=3), 250, False),
+    # head dim 96, window barely above the chunk (72 of 100), ragged tail
+    "hd96_tight_window": (dict(TOY, dtype="bf16", n_layers=3, d_model=384, n_heads=4, d_ff=640, window=100,
+                               chunk=72, n_fast=2), 200, False),
+}
+
+
+@pytest.mark.parametrize("name", sorted(EDGE))
+def test_bf16_edge_configurations_parity(name):
+    cfgd, T, masked = EDGE[name]
+    c = mkcfg(**cfgd)
+    print(f"case edge {name}", flush=True)
+    mask = None
+    if masked:
+        mask = np.zeros((c.batch, T), dtype=bool)
+        mask[:, ::7] = True
+    w, o, ctx, ref, got = run_pair(c, T, dist="zipf", targets_mask=mask)
+    tl, tw = TOL["bf16"]
+    rel = np.max(np.abs(got - ref) / np.abs(ref))
+    print(f"edge {name}: max loss rel err {rel:.3e}")
+    assert rel <= tl
+    for b in range(c.batch):
+        compare_fast(ctx.fast_weights(b), o.get_fast(b), _w0(w, c), tw, f"edge {name} row {b}")
+
+
 def test_toy_more_fast_blocks_and_ragged_tail():
     """Two fast blocks (attention backward exercised), window 96 not a
     multiple of the chunk 40, T=300 (ragged last chunk), some targets ignored."""
