@@ -76,6 +76,14 @@ struct ttt_ctx {
   // second stream for the fused-SGD weight-gradient GEMMs, which only the next chunk depends on
   hipStream_t side = nullptr;
   hipEvent_t ev_m2s = nullptr, ev_s2m = nullptr;
+  // the batched lower-block pass of the next lookahead group runs on its own stream beside the
+  // current group's chunks, with its own scratch buffers and an h' buffer per group parity
+  // (TTT_NO_BOTTOM_OVERLAP=1: in line on the main stream)
+  bool bot_overlap = true;
+  hipStream_t bstream = nullptr;
+  hipEvent_t ev_bdone[2] = {nullptr, nullptr}, ev_cdone[2] = {nullptr, nullptr}, ev_c2b = nullptr;
+  float *hb2 = nullptr, *b_qkvb = nullptr, *b_rstd = nullptr, *b_ws = nullptr;
+  void *b_ub = nullptr, *b_qb = nullptr, *b_ob = nullptr, *b_actb = nullptr;
   ttt_free_fn free_fn = nullptr;
   void* free_user = nullptr;
   std::vector<void*> allocs;
@@ -125,6 +133,20 @@ struct ttt_ctx {
     hipEvent_t a, b;
   };
   std::vector<ProfRec> prof_recs;
+
+  // the streams and events this context created (null ones skipped)
+  void destroy_streams() {
+    for (hipEvent_t* e : {&ev_m2s, &ev_s2m, &ev_c2b, &ev_bdone[0], &ev_bdone[1], &ev_cdone[0], &ev_cdone[1]})
+      if (*e) {
+        (void)hipEventDestroy(*e);
+        *e = nullptr;
+      }
+    for (hipStream_t* st : {&side, &bstream})
+      if (*st) {
+        (void)hipStreamDestroy(*st);
+        *st = nullptr;
+      }
+  }
 
   void* alloc(size_t bytes) {
     if (bytes == 0) bytes = 256;
@@ -619,8 +641,80 @@ int top_chunk(ttt_ctx* c, const int32_t* tgt, int64_t ld, const float* hsrc, int
 }
 
 // the chunk loop over n_tokens tokens per row, starting at c->pos
+// While alive, the context's stream, scratch buffers and workspace are those of the batched
+// pass, and c->hb is the given h' buffer; the destructor restores them.
+struct BottomScope {
+  ttt_ctx* c;
+  float* hb_main;
+  BottomScope(ttt_ctx* c_, float* hbuf) : c(c_), hb_main(c_->hb) {
+    swap_all();
+    c->hb = hbuf;
+  }
+  ~BottomScope() {
+    c->hb = hb_main;
+    swap_all();
+  }
+  void swap_all() {
+    std::swap(c->stream, c->bstream);
+    std::swap(c->qkvb, c->b_qkvb);
+    std::swap(c->rstd_tmp, c->b_rstd);
+    std::swap(c->ws, c->b_ws);
+    std::swap(c->ub, c->b_ub);
+    std::swap(c->qb, c->b_qb);
+    std::swap(c->ob, c->b_ob);
+    std::swap(c->actb, c->b_actb);
+  }
+};
+
+// Lookahead groups of G chunks: the batched pass of group i + 1 (batched stream, h' buffer
+// (i + 1) % 2) is issued before the chunks of group i (main stream, buffer i % 2), so the two
+// run side by side; events order each buffer's writer after its previous readers.
+template <typename T>
+int run_tokens_overlap(ttt_ctx* c, const int32_t* tok, const int32_t* tgt, int64_t ld, int64_t n_tokens,
+                       float* loss_dev) {
+  const int64_t gmax = (int64_t)c->G * c->b;
+  const int ng = (int)((n_tokens + gmax - 1) / gmax);
+  float* hbuf[2] = {c->hb, c->hb2};
+  auto group_len = [&](int gi) { return (int)std::min<int64_t>(n_tokens - gi * gmax, gmax); };
+  auto bottom = [&](int gi) -> int {
+    BottomScope scope(c, hbuf[gi & 1]);
+    int rc = bottom_pass<T>(c, tok + gi * gmax, ld, group_len(gi), c->pos + gi * gmax);
+    if (rc) return rc;
+    CK(hipEventRecord(c->ev_bdone[gi & 1], c->stream));  // (the batched stream in this scope)
+    return TTT_OK;
+  };
+  // the batched stream starts after the main stream's earlier work, which may still read h'
+  CK(hipEventRecord(c->ev_c2b, c->stream));
+  CK(hipStreamWaitEvent(c->bstream, c->ev_c2b, 0));
+  int rc = bottom(0);
+  if (rc) return rc;
+  int64_t ci = 0;
+  for (int gi = 0; gi < ng; ++gi) {
+    if (gi + 1 < ng) {
+      // buffer (gi + 1) % 2 was last read by the chunks of group gi - 1
+      if (gi >= 1) CK(hipStreamWaitEvent(c->bstream, c->ev_cdone[(gi + 1) & 1], 0));
+      rc = bottom(gi + 1);
+      if (rc) return rc;
+    }
+    CK(hipStreamWaitEvent(c->stream, c->ev_bdone[gi & 1], 0));
+    const int g = group_len(gi);
+    const int64_t s = gi * gmax;
+    for (int cs = 0; cs < g; cs += c->b) {
+      const int n = std::min(c->b, g - cs);
+      rc = top_chunk<T>(c, tgt + s + cs, ld, hbuf[gi & 1] + (int64_t)cs * c->d, (int64_t)g * c->d, n,
+                        c->pos + s + cs, loss_dev + ci * c->B);
+      if (rc) return rc;
+      ++ci;
+    }
+    CK(hipEventRecord(c->ev_cdone[gi & 1], c->stream));
+  }
+  c->pos += n_tokens;
+  return TTT_OK;
+}
+
 template <typename T>
 int run_tokens(ttt_ctx* c, const int32_t* tok, const int32_t* tgt, int64_t ld, int64_t n_tokens, float* loss_dev) {
+  if (c->bot_overlap) return run_tokens_overlap<T>(c, tok, tgt, ld, n_tokens, loss_dev);
   int64_t done = 0, ci = 0;
   const int64_t gmax = (int64_t)c->G * c->b;
   while (done < n_tokens) {
@@ -837,6 +931,15 @@ int build(ttt_ctx* c, const ttt_weights* w) {
   }
   // work buffers
   AL(c->hb, rows_bot * d * 4);
+  if (c->bot_overlap) {
+    AL(c->hb2, rows_bot * d * 4);
+    AL(c->b_qkvb, rows_bot * 3 * d * 4);
+    AL(c->b_rstd, rows_bot * 4);
+    AL(c->b_ub, rows_bot * d * es);
+    AL(c->b_qb, rows_bot * d * es);
+    AL(c->b_ob, rows_bot * d * es);
+    AL(c->b_actb, rows_bot * f * es);
+  }
   AL(c->qkvb, rows_bot * 3 * d * 4);
   AL(c->rstd_tmp, rows_bot * 4);
   AL(c->ub, rows_bot * d * es);
@@ -871,6 +974,7 @@ int build(ttt_ctx* c, const ttt_weights* w) {
   AL(c->err_dev, 256);
   c->ws_floats = 8 * rows_top * (int64_t)(d + 2 * H);
   AL(c->ws, c->ws_floats * 4);
+  if (c->bot_overlap) AL(c->b_ws, c->ws_floats * 4);
   CK(hipMemset(c->err_dev, 0, 4));
   c->acts.resize(c->Lq);
   for (int j = 0; j < c->Lq; ++j) {
@@ -893,6 +997,8 @@ int build(ttt_ctx* c, const ttt_weights* w) {
 }
 
 int reset_state(ttt_ctx* c) {
+  // (a failed call may have left a batched pass in flight on the batched stream)
+  if (c->bstream) CK(hipStreamSynchronize(c->bstream));
   c->pend_parts = 0;
   const int64_t fsz = 3LL * c->f * c->d;
   for (int j = 0; j < c->Lq; ++j) {
@@ -1009,11 +1115,21 @@ int ttt_create(const ttt_config* cfg, const ttt_weights* w, void* hip_stream, tt
   const char* noside = getenv("TTT_NO_SIDE");
   c->overlap = !(noside && noside[0] == '1');
   c->il = c->bf16 && c->mfma && c0.d_ff % 32 == 0 && c0.d_model % 8 == 0;
-  if (hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking) != hipSuccess ||
-      hipEventCreateWithFlags(&c->ev_m2s, hipEventDisableTiming) != hipSuccess ||
-      hipEventCreateWithFlags(&c->ev_s2m, hipEventDisableTiming) != hipSuccess) {
+  const char* nobot = getenv("TTT_NO_BOTTOM_OVERLAP");
+  c->bot_overlap = !(nobot && nobot[0] == '1');
+  bool ok = hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking) == hipSuccess &&
+            hipEventCreateWithFlags(&c->ev_m2s, hipEventDisableTiming) == hipSuccess &&
+            hipEventCreateWithFlags(&c->ev_s2m, hipEventDisableTiming) == hipSuccess;
+  if (ok && c->bot_overlap) {
+    ok = hipStreamCreateWithFlags(&c->bstream, hipStreamNonBlocking) == hipSuccess &&
+         hipEventCreateWithFlags(&c->ev_c2b, hipEventDisableTiming) == hipSuccess;
+    for (int i = 0; i < 2 && ok; ++i)
+      ok = hipEventCreateWithFlags(&c->ev_bdone[i], hipEventDisableTiming) == hipSuccess &&
+           hipEventCreateWithFlags(&c->ev_cdone[i], hipEventDisableTiming) == hipSuccess;
+  }
+  if (!ok) {
     g_create_err = "stream/event creation failed";
-    if (c->side) (void)hipStreamDestroy(c->side);
+    c->destroy_streams();
     delete c;
     return TTT_EDEVICE;
   }
@@ -1022,9 +1138,7 @@ int ttt_create(const ttt_config* cfg, const ttt_weights* w, void* hip_stream, tt
   if (rc != TTT_OK) {
     g_create_err = c->err;
     c->release_all();
-    (void)hipEventDestroy(c->ev_m2s);
-    (void)hipEventDestroy(c->ev_s2m);
-    (void)hipStreamDestroy(c->side);
+    c->destroy_streams();
     delete c;
     return rc;
   }
@@ -1065,9 +1179,8 @@ void ttt_destroy(ttt_ctx* c) {
   (void)hipStreamSynchronize(c->stream);
   for (hipEvent_t e : c->ev_pool) (void)hipEventDestroy(e);
   (void)hipStreamSynchronize(c->side);
-  (void)hipEventDestroy(c->ev_m2s);
-  (void)hipEventDestroy(c->ev_s2m);
-  (void)hipStreamDestroy(c->side);
+  if (c->bstream) (void)hipStreamSynchronize(c->bstream);
+  c->destroy_streams();
   c->release_all();
   delete c;
 }
