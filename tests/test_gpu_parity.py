@@ -164,6 +164,20 @@ def test_bf16_edge_configurations_parity(name):
         compare_fast(ctx.fast_weights(b), o.get_fast(b), _w0(w, c), tw, f"edge {name} row {b}")
 
 
+def test_default_fast_set_is_last_quarter():
+    """n_fast = 0 takes the last max(1, L/4) blocks (tests/golden/fast_set.txt): with 8 layers the
+    library holds two fast blocks (ttt_get_fast_weights rejects any other size), initialised from
+    the given MLP weights of blocks 6 and 7."""
+    c = mkcfg(**dict(TOY, n_layers=8, n_fast=0))
+    w = synth.weights(synth.Shape(8, c.d_model, c.n_heads, c.d_ff, c.vocab), bf16=False)
+    ctx = _ctx(c, w, 256)
+    fw = ctx.fast_weights(0)
+    assert len(fw) == 2
+    for j, l in enumerate((6, 7)):
+        for a, key in enumerate(("w_gate", "w_up", "w_down")):
+            np.testing.assert_array_equal(fw[j][a], np.asarray(w[key][l], dtype=np.float32))
+
+
 def test_toy_more_fast_blocks_and_ragged_tail():
     """Two fast blocks (attention backward exercised), window 96 not a
     multiple of the chunk 40, T=300 (ragged last chunk), some targets ignored."""

@@ -6,6 +6,8 @@ cross-entropy / autograd), closed forms and invariances.
 """
 import math
 
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -281,3 +283,24 @@ def test_rejects_bad_ids_and_window_smaller_than_chunk():
         o.prefill_chunk(np.array([[0, 1, 11, 2]]), np.array([[1, 2, 3, 4]]))
     with pytest.raises(ValueError):
         o.prefill_chunk(np.array([[0, 1, 2, 3]]), np.array([[1, 2, -2, 4]]))
+
+
+def test_fast_set_is_the_last_quarter_of_the_blocks():
+    """tests/golden/fast_set.txt (the pages' fast-set rule, cited there): every configuration of the
+    tests and the benchmark updates the MLPs of its last max(1, L/4) blocks, and the fast parameter
+    count is 3 d f of each of them."""
+    from tests import cfgs
+    rows = {}
+    with open(os.path.join(os.path.dirname(__file__), "golden", "fast_set.txt")) as fh:
+        for line in fh:
+            if line.strip() and not line.startswith("#"):
+                name, L, d, f, nf, npar = line.split()
+                rows[name] = tuple(int(x) for x in (L, d, f, nf, npar))
+    assert set(rows) == {"toy", "125M", "760M", "3B"}
+    for name, (L, d, f, nf, npar) in rows.items():
+        assert nf == max(1, L // 4), name
+        assert npar == 3 * d * f * nf, name
+    for name, c in (("toy", cfgs.TOY), ("125M", cfgs.M125), ("760M", cfgs.M760), ("3B", cfgs.M3B)):
+        L, d, f, nf, _ = rows[name]
+        assert (c["n_layers"], c["d_model"], c["d_ff"], c["n_fast"]) == (L, d, f, nf), name
+
