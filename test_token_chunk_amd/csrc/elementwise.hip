@@ -106,18 +106,25 @@ __global__ __launch_bounds__(256) void k_rmsnorm_fwd_row(float* h, const float* 
   if (parts) {
     const float4* pr = (const float4*)(parts + m * d);
     const int64_t pl4 = plane / 4;
-    for (int sp = 0; sp < S; ++sp) {
+    // up to four parts' loads in flight at once, then added in order (an absent part adds 0)
+    for (int sp0 = 0; sp0 < S; sp0 += 4) {
+      float4 q[4][4];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int i = tid + 256 * k;
-        if (i < d4) {
-          const float4 q = pr[sp * pl4 + i];
-          v[k].x += q.x;
-          v[k].y += q.y;
-          v[k].z += q.z;
-          v[k].w += q.w;
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int i = tid + 256 * k;
+          q[u][k] = (sp0 + u < S && i < d4) ? pr[(sp0 + u) * pl4 + i] : make_float4(0.f, 0.f, 0.f, 0.f);
         }
-      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          v[k].x += q[u][k].x;
+          v[k].y += q[u][k].y;
+          v[k].z += q[u][k].z;
+          v[k].w += q[u][k].w;
+        }
     }
   }
   float ss = 0.f;
@@ -162,18 +169,25 @@ __global__ __launch_bounds__(256) void k_rmsnorm_bwd_row(const float* __restrict
   }
   if (parts) {
     const int64_t pl4 = plane / 4;
-    for (int sp = 1; sp < S; ++sp) {
+    // (parts 1.. as in the forward kernel: four parts' loads in flight, added in order)
+    for (int sp0 = 1; sp0 < S; sp0 += 4) {
+      float4 q[4][4];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int i = tid + 256 * k;
-        if (i < d4) {
-          const float4 q = er[sp * pl4 + i];
-          e[k].x += q.x;
-          e[k].y += q.y;
-          e[k].z += q.z;
-          e[k].w += q.w;
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int i = tid + 256 * k;
+          q[u][k] = (sp0 + u < S && i < d4) ? er[(sp0 + u) * pl4 + i] : make_float4(0.f, 0.f, 0.f, 0.f);
         }
-      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          e[k].x += q[u][k].x;
+          e[k].y += q[u][k].y;
+          e[k].z += q[u][k].z;
+          e[k].w += q[u][k].w;
+        }
     }
   }
   float dot = 0.f;
@@ -254,21 +268,27 @@ __global__ __launch_bounds__(256) void k_parts_rows_t(const float* __restrict__ 
   float4 acc[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) acc[k] = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int sp = 0; sp < S; ++sp) {
-    float4 v[4];
+  // up to four parts' loads in flight at once, then added in order (an absent part adds 0)
+  for (int sp0 = 0; sp0 < S; sp0 += 4) {
+    float4 v[4][4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int t = t0 + r0 + 16 * k;
-      v[k] = (t < n && c < d) ? *(const float4*)(parts + sp * plane + ((int64_t)b * n + t) * d + c)
-                              : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
+    for (int u = 0; u < 4; ++u)
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      acc[k].x += v[k].x;
-      acc[k].y += v[k].y;
-      acc[k].z += v[k].z;
-      acc[k].w += v[k].w;
-    }
+      for (int k = 0; k < 4; ++k) {
+        const int t = t0 + r0 + 16 * k;
+        v[u][k] = (sp0 + u < S && t < n && c < d)
+                      ? *(const float4*)(parts + (sp0 + u) * plane + ((int64_t)b * n + t) * d + c)
+                      : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        acc[k].x += v[u][k].x;
+        acc[k].y += v[u][k].y;
+        acc[k].z += v[u][k].z;
+        acc[k].w += v[u][k].w;
+      }
   }
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
