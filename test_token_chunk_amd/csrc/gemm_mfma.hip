@@ -17,6 +17,11 @@
 
 namespace {
 
+// 1 / (1 + e^-x), the logistic function, with the hardware reciprocal (v_rcp_f32, about 1 ulp):
+// the bf16 outputs of the matrix-core epilogues do not resolve the difference from a correctly
+// rounded division, which takes about ten instructions.  Large negative x: e^-x = inf, 1/inf = 0.
+__device__ __forceinline__ float sigmoid_fast(float x) { return __builtin_amdgcn_rcpf(1.f + __expf(-x)); }
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
@@ -84,7 +89,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, f32x16 (&acc)[T
           for (int r = 0; r < 4; ++r) {
             const int ml = wm0 + i * 32 + 8 * q + 4 * hi + r, m = m0 + ml;
             const float x = acc[i][2 * jp][4 * q + r], u = acc[i][2 * jp + 1][4 * q + r];
-            const float act = x / (1.f + __expf(-x)) * u;
+            const float act = x * sigmoid_fast(x) * u;
             if (m < g.M && 2 * fi < g.N) {
               ((bf16*)e.c)[bz * e.sc + (int64_t)m * e.ldc + fi] = f2bf(act);
               if (e.zg) {
@@ -132,7 +137,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, f32x16 (&acc)[T
           const float x = acc[i][j][4 * q + r];
           if constexpr (DUAL) {
             const float u = accu[i][j][4 * q + r];
-            const float act = x / (1.f + __expf(-x)) * u;
+            const float act = x * sigmoid_fast(x) * u;
             if (in) {
               ((bf16*)e.c)[bz * e.sc + (int64_t)m * e.ldc + n] = f2bf(act);
               if (e.zg) {
@@ -153,7 +158,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, f32x16 (&acc)[T
             if (in) {
               const float zg = bf2f(((const bf16*)e.zg)[bz * e.sz + (int64_t)m * e.ldz + n]);
               const float zu = bf2f(((const bf16*)e.zu)[bz * e.sz + (int64_t)m * e.ldz + n]);
-              const float sg = 1.f / (1.f + __expf(-zg));
+              const float sg = sigmoid_fast(zg);
               const float dzu = x * zg * sg;
               const float dzg = x * zu * sg * (1.f + zg * (1.f - sg));
               bf16* c = (bf16*)e.c + bz * e.sc + (int64_t)m * e.ldc;
@@ -579,7 +584,7 @@ __device__ __forceinline__ void wide_epilogue(const GemmArgs& g, f32x16 (&acc)[T
         for (int r = 0; r < 4; ++r) {
           x[r] = acc[i][jg][4 * q + r];
           u[r] = acc[i][jg + 1][4 * q + r];
-          a[r] = x[r] / (1.f + __expf(-x[r])) * u[r];
+          a[r] = x[r] * sigmoid_fast(x[r]) * u[r];
           tr0[(fl + r) * TLD + ml] = f2bf(a[r]);
         }
         *(uint2*)((bf16*)e.c + bz * e.sc + (int64_t)m * e.ldc + fi) = pk4(a[0], a[1], a[2], a[3]);
@@ -642,7 +647,7 @@ __device__ __forceinline__ void wide_epilogue(const GemmArgs& g, f32x16 (&acc)[T
             float dg[4], du[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-              const float sg = 1.f / (1.f + __expf(-zg[r]));
+              const float sg = sigmoid_fast(zg[r]);
               du[r] = x[r] * zg[r] * sg;
               dg[r] = x[r] * zu[r] * sg * (1.f + zg[r] * (1.f - sg));
               tr0[(nl + r) * TLD + ml] = f2bf(dg[r]);
