@@ -1100,7 +1100,7 @@ hipError_t launch_dkv(const AttnBwdArgs& a, int P, hipStream_t s) {
 }
 
 template <int HD>
-hipError_t launch_bwd(const AttnBwdArgs& a, hipStream_t s) {
+hipError_t launch_bwd(const AttnBwdArgs& a, hipStream_t s, AttnBwdParts* parts) {
   // the direct-to-LDS dQ form (head dim 128, transposed key ring) computes D = rowsum(dO * O)
   // itself and stores it for dK/dV; otherwise a separate pass does
   const bool tr = a.ktr && a.dot && a.R % 8 == 0 && a.n % 8 == 0 && (a.H * HD) % 8 == 0;
@@ -1125,21 +1125,28 @@ hipError_t launch_bwd(const AttnBwdArgs& a, hipStream_t s) {
     if constexpr (DQ2) e = tr ? launch_dq2<HD, true>(a, S, s) : launch_dq<HD, 8, true, false>(a, S, s);
     else e = tr ? launch_dq<HD, 8, true, true>(a, S, s) : launch_dq<HD, 8, true, false>(a, S, s);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_dq_reduce, dim3((unsigned)std::min<int64_t>(cdiv(total / 4, 256), 8192)), dim3(256), 0, s,
-                       a.ws, S, total, a.dq);
+    if (!parts)
+      hipLaunchKernelGGL(k_dq_reduce, dim3((unsigned)std::min<int64_t>(cdiv(total / 4, 256), 8192)), dim3(256), 0, s,
+                         a.ws, S, total, a.dq);
   } else {
     if constexpr (DQ2) e = tr ? launch_dq2<HD, false>(a, 1, s) : launch_dq<HD, 8, false, false>(a, 1, s);
     else e = tr ? launch_dq<HD, 8, false, true>(a, 1, s) : launch_dq<HD, 8, false, false>(a, 1, s);
     if (e != hipSuccess) return e;
   }
   // dK/dV: split each key block's query range when the grid is small (ordered sum after);
-  // one 4-wave block per CU, so pick the P <= 4 with the fewest rounds of 256 blocks per part
+  // one 4-wave block per CU, so pick the P <= 4 with the fewest rounds of 256 blocks per part.
+  // Parts left to the caller go after the dQ parts in the workspace.
+  AttnBwdArgs kv = a;
+  if (parts && S > 1) {
+    kv.ws = a.ws + S * total;
+    kv.ws_floats = a.ws_floats - S * total;
+  }
   const int64_t kblocks = (int64_t)cdiv(a.n, BQ) * a.H * a.B;
   int P = 1;
-  if (a.ws && kblocks < 256) {
+  if (kv.ws && kblocks < 256) {
     double best = 1e30;
     for (int p = 1; p <= std::min(4, (int)cdiv(a.n, KT)); ++p) {
-      if (p > 1 && 2LL * p * total > a.ws_floats) break;
+      if (p > 1 && 2LL * p * total > kv.ws_floats) break;
       const double cost = (double)cdiv(kblocks * p, 256) / p;
       if (cost < best - 1e-9) {
         best = cost;
@@ -1147,11 +1154,19 @@ hipError_t launch_bwd(const AttnBwdArgs& a, hipStream_t s) {
       }
     }
   }
-  e = tr ? launch_dkv<HD, true>(a, P, s) : launch_dkv<HD, false>(a, P, s);
+  e = tr ? launch_dkv<HD, true>(kv, P, s) : launch_dkv<HD, false>(kv, P, s);
   if (e != hipSuccess) return e;
-  if (P > 1)
+  if (parts) {
+    parts->dq = S > 1 ? a.ws : a.dq;
+    parts->sq = S;
+    parts->dk = P > 1 ? kv.ws : a.dk;
+    parts->dv = P > 1 ? kv.ws + P * total : a.dv;
+    parts->pkv = P;
+    parts->plane = total;
+  } else if (P > 1) {
     hipLaunchKernelGGL(k_dkv_reduce, dim3((unsigned)std::min<int64_t>(cdiv(total / 4, 256), 8192)), dim3(256), 0, s,
                        a.ws, P, total, a.dk, a.dv);
+  }
   return hipGetLastError();
 }
 
@@ -1176,14 +1191,15 @@ hipError_t swa_fwd_mfma(const AttnArgs& a, hipStream_t s) {
   }
 }
 
-hipError_t swa_bwd_mfma(const AttnBwdArgs& a, hipStream_t s) {
+hipError_t swa_bwd_mfma(const AttnBwdArgs& a, hipStream_t s, AttnBwdParts* parts) {
+  if (parts) *parts = AttnBwdParts{a.dq, 1, a.dk, a.dv, 1, (int64_t)a.B * a.n * a.H * a.hd};
   if (a.n == 0) return hipSuccess;
   if (a.window < a.n) return swa_bwd_simt<bf16>(a, s);
   switch (a.hd) {
-    case 32: return launch_bwd<32>(a, s);
-    case 64: return launch_bwd<64>(a, s);
-    case 96: return launch_bwd<96>(a, s);
-    case 128: return launch_bwd<128>(a, s);
+    case 32: return launch_bwd<32>(a, s, parts);
+    case 64: return launch_bwd<64>(a, s, parts);
+    case 96: return launch_bwd<96>(a, s, parts);
+    case 128: return launch_bwd<128>(a, s, parts);
     default: return swa_bwd_simt<bf16>(a, s);
   }
 }

@@ -625,24 +625,48 @@ __global__ __launch_bounds__(256) void k_rope_qkv4(const float* __restrict__ qkv
   }
 }
 
-// vector form of k_rope_bwd_pack: 4 consecutive pairs per thread (hd % 8 == 0, aligned rows)
+// the ordered sums from zero of cnt parts (plane floats apart) of the float4s at p and
+// p + half, with up to four parts' loads in flight
+__device__ inline void sum_parts_pair(const float* p, int half, int cnt, int64_t plane, float4& x, float4& y) {
+  x = make_float4(0.f, 0.f, 0.f, 0.f);
+  y = x;
+  for (int i = 0; i < cnt; i += 4) {
+    float4 u[4], v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (i + j < cnt) {
+        u[j] = *(const float4*)(p + (i + j) * plane);
+        v[j] = *(const float4*)(p + (i + j) * plane + half);
+      }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (i + j < cnt) {
+        x.x += u[j].x; x.y += u[j].y; x.z += u[j].z; x.w += u[j].w;
+        y.x += v[j].x; y.y += v[j].y; y.z += v[j].z; y.w += v[j].w;
+      }
+  }
+}
+
+// vector form of k_rope_bwd_pack: 4 consecutive pairs per thread (hd % 8 == 0, aligned rows
+// and planes)
 template <typename T>
-__global__ __launch_bounds__(256) void k_rope_bwd_pack4(const float* dq, const float* dk, const float* dv,
-                                                        const float* cos_t, const float* sin_t, int64_t pos0,
-                                                        int64_t M, int n, int H, int hd, T* dqkv) {
+__global__ __launch_bounds__(256) void k_rope_bwd_pack4(AttnBwdParts g, const float* cos_t, const float* sin_t,
+                                                        int64_t pos0, int64_t M, int n, int H, int hd, T* dqkv) {
   const int half = hd / 2, q4 = half / 4, d = H * hd;
   const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (e >= M * H * q4) return;
   const int64_t m = e / (H * q4);
   const int h = (int)((e / q4) % H), i = (int)(e % q4) * 4;
-  const int64_t pos = pos0 + m % n;
+  const int64_t pos = pos0 + m % n, off = m * d + h * hd + i;
   const float4 c = *(const float4*)(cos_t + pos * half + i), sn = *(const float4*)(sin_t + pos * half + i);
   const float cc[4] = {c.x, c.y, c.z, c.w}, ss[4] = {sn.x, sn.y, sn.z, sn.w};
   T* o = dqkv + m * 3 * d + h * hd;
-  const float* src[2] = {dq + m * d + h * hd, dk + m * d + h * hd};
+  const float* src[2] = {g.dq + off, g.dk + off};
+  const int cnt[2] = {g.sq, g.pkv};
 #pragma unroll
   for (int w = 0; w < 2; ++w) {
-    const float4 a = *(const float4*)(src[w] + i), bb = *(const float4*)(src[w] + half + i);
+    float4 a, bb;
+    sum_parts_pair(src[w], half, cnt[w], g.plane, a, bb);
     const float av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {bb.x, bb.y, bb.z, bb.w};
     float lo[4], hi[4];
 #pragma unroll
@@ -653,36 +677,39 @@ __global__ __launch_bounds__(256) void k_rope_bwd_pack4(const float* dq, const f
     store4<T>(o + w * d + i, lo[0], lo[1], lo[2], lo[3]);
     store4<T>(o + w * d + half + i, hi[0], hi[1], hi[2], hi[3]);
   }
-  const float* v = dv + m * d + h * hd;
-  const float4 a = *(const float4*)(v + i), bb = *(const float4*)(v + half + i);
+  float4 a, bb;
+  sum_parts_pair(g.dv + off, half, g.pkv, g.plane, a, bb);
   store4<T>(o + 2 * d + i, a.x, a.y, a.z, a.w);
   store4<T>(o + 2 * d + half + i, bb.x, bb.y, bb.z, bb.w);
 }
 
 // inverse rotation of dq, dk (gradients w.r.t. rotated q, k) and packing [dq|dk|dv]
 template <typename T>
-__global__ void k_rope_bwd_pack(const float* dq, const float* dk, const float* dv, const float* cos_t,
-                                const float* sin_t, int64_t pos0, int n, int H, int hd, T* dqkv) {
+__global__ void k_rope_bwd_pack(AttnBwdParts g, const float* cos_t, const float* sin_t, int64_t pos0, int n, int H,
+                                int hd, T* dqkv) {
   int64_t m = blockIdx.x;
   int h = blockIdx.y;
   int t = (int)(m % n);
   int half = hd / 2, d = H * hd;
   int64_t pos = pos0 + t;
-  const float* q = dq + m * d + h * hd;
-  const float* k = dk + m * d + h * hd;
-  const float* v = dv + m * d + h * hd;
+  const int64_t off = m * d + h * hd;
+  auto sum = [&](const float* p, int cnt) {
+    float acc = 0.f;
+    for (int j = 0; j < cnt; ++j) acc += p[j * g.plane];
+    return acc;
+  };
   T* o = dqkv + m * 3 * d + h * hd;
   for (int i = threadIdx.x; i < half; i += blockDim.x) {
     float c = cos_t[pos * half + i], s = sin_t[pos * half + i];
-    float a = q[i], bb = q[i + half];
+    float a = sum(g.dq + off + i, g.sq), bb = sum(g.dq + off + i + half, g.sq);
     o[i] = from_f<T>(a * c + bb * s);
     o[i + half] = from_f<T>(bb * c - a * s);
-    a = k[i];
-    bb = k[i + half];
+    a = sum(g.dk + off + i, g.pkv);
+    bb = sum(g.dk + off + i + half, g.pkv);
     o[d + i] = from_f<T>(a * c + bb * s);
     o[d + i + half] = from_f<T>(bb * c - a * s);
-    o[2 * d + i] = from_f<T>(v[i]);
-    o[2 * d + i + half] = from_f<T>(v[i + half]);
+    o[2 * d + i] = from_f<T>(sum(g.dv + off + i, g.pkv));
+    o[2 * d + i + half] = from_f<T>(sum(g.dv + off + i + half, g.pkv));
   }
 }
 
@@ -864,18 +891,20 @@ hipError_t rope_qkv_f32in(const float* qkv, int B, const RopeRing& rr, int is_bf
 }
 
 template <typename T>
-hipError_t rope_bwd_pack(const float* dq, const float* dk, const float* dv, const float* cos_t, const float* sin_t,
-                         int64_t pos0, int B, int n, int H, int hd, T* dqkv, hipStream_t s) {
+hipError_t rope_bwd_pack(const AttnBwdParts& g, const float* cos_t, const float* sin_t, int64_t pos0, int B, int n,
+                         int H, int hd, T* dqkv, hipStream_t s) {
   if (B * n == 0) return hipSuccess;
-  if (hd % 8 == 0 && al16(dq) && al16(dk) && al16(dv) && al16(cos_t) && al16(sin_t) && al16(dqkv)) {
+  if (g.sq < 1 || g.pkv < 1 || ((g.sq > 1 || g.pkv > 1) && g.plane < (int64_t)B * n * H * hd))
+    return hipErrorInvalidValue;
+  if (hd % 8 == 0 && g.plane % 4 == 0 && al16(g.dq) && al16(g.dk) && al16(g.dv) && al16(cos_t) && al16(sin_t) &&
+      al16(dqkv)) {
     const int64_t M = (int64_t)B * n, items = M * H * (hd / 8);
-    hipLaunchKernelGGL(k_rope_bwd_pack4<T>, dim3(cdiv(items, 256)), dim3(256), 0, s, dq, dk, dv, cos_t, sin_t, pos0, M,
-                       n, H, hd, dqkv);
+    hipLaunchKernelGGL(k_rope_bwd_pack4<T>, dim3(cdiv(items, 256)), dim3(256), 0, s, g, cos_t, sin_t, pos0, M, n, H,
+                       hd, dqkv);
     return hipGetLastError();
   }
   int th = hd / 2 >= 64 ? 64 : 32;
-  hipLaunchKernelGGL(k_rope_bwd_pack<T>, dim3(B * n, H), dim3(th), 0, s, dq, dk, dv, cos_t, sin_t, pos0, n, H, hd,
-                     dqkv);
+  hipLaunchKernelGGL(k_rope_bwd_pack<T>, dim3(B * n, H), dim3(th), 0, s, g, cos_t, sin_t, pos0, n, H, hd, dqkv);
   return hipGetLastError();
 }
 
@@ -917,7 +946,7 @@ hipError_t parts_rows_t(const float* parts, int S, int64_t plane, int64_t M, int
   template hipError_t parts_rows_t<T>(const float*, int, int64_t, int64_t, int, int, T*, T*, hipStream_t);          \
   template hipError_t ce_rows_ld<T>(const float*, int64_t, int, const int32_t*, int64_t, const int*, int, float*,   \
                                     T*, int*, hipStream_t);                                                         \
-  template hipError_t rope_bwd_pack<T>(const float*, const float*, const float*, const float*, const float*,        \
-                                       int64_t, int, int, int, int, T*, hipStream_t);
+  template hipError_t rope_bwd_pack<T>(const AttnBwdParts&, const float*, const float*, int64_t, int, int, int, int, \
+                                       T*, hipStream_t);
 INST(float)
 INST(bf16)

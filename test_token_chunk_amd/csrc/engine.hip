@@ -108,7 +108,8 @@ struct ttt_ctx {
   std::vector<void*> dyT, dzT;  // per fast block: inputs of its weight-gradient GEMMs (side stream)
   int* err_dev = nullptr;
   float* ws = nullptr;  // split-K / split-key workspace (used by one launch at a time)
-  int64_t ws_floats = 0;
+  int64_t ws_floats = 0;        // what GEMM splits and the attention forward may use
+  int64_t ws_alloc_floats = 0;  // allocated: also dQ and dK/dV parts of the attention backward side by side
   int32_t* d_tok = nullptr;
   int64_t d_tok_cap = 0;
   float* d_loss = nullptr;
@@ -248,7 +249,8 @@ struct Ops<float> {
     double fl = 4.0 * a.hd * a.H * a.B * attn_pairs(c, a.n, a.pos0);
     return timed(c, PC_SWA_FWD, fl, c->stream, [&] { return swa_fwd_simt<float>(a, c->stream); });
   }
-  static hipError_t bwd(ttt_ctx* c, const AttnBwdArgs& a) {
+  static hipError_t bwd(ttt_ctx* c, const AttnBwdArgs& a, AttnBwdParts* parts) {
+    *parts = AttnBwdParts{a.dq, 1, a.dk, a.dv, 1, (int64_t)a.B * a.n * a.H * a.hd};
     double fl = 4.0 * a.hd * a.H * a.B * (attn_pairs(c, a.n, a.pos0) + 0.5 * a.n * (a.n + 1.0));
     return timed(c, PC_SWA_BWD, fl, c->stream, [&] { return swa_bwd_simt<float>(a, c->stream); });
   }
@@ -295,14 +297,16 @@ struct Ops<bf16> {
     return timed(c, cls, fl, c->stream,
                  [&] { return c->mfma ? swa_fwd_mfma(a, c->stream) : swa_fwd_simt<bf16>(a, c->stream); });
   }
-  static hipError_t bwd(ttt_ctx* c, const AttnBwdArgs& a0) {
+  // the split sums of dQ, dK, dV are left to the consumer as described in *parts
+  static hipError_t bwd(ttt_ctx* c, const AttnBwdArgs& a0, AttnBwdParts* parts) {
     if (c->pend_parts) return hipErrorIllegalState;
     AttnBwdArgs a = a0;
     a.ws = c->ws;
-    a.ws_floats = c->ws_floats;
+    a.ws_floats = c->ws_alloc_floats;
+    *parts = AttnBwdParts{a.dq, 1, a.dk, a.dv, 1, (int64_t)a.B * a.n * a.H * a.hd};
     double fl = 4.0 * a.hd * a.H * a.B * (attn_pairs(c, a.n, a.pos0) + 0.5 * a.n * (a.n + 1.0));
     return timed(c, PC_SWA_BWD, fl, c->stream,
-                 [&] { return c->mfma ? swa_bwd_mfma(a, c->stream) : swa_bwd_simt<bf16>(a, c->stream); });
+                 [&] { return c->mfma ? swa_bwd_mfma(a, c->stream, parts) : swa_bwd_simt<bf16>(a, c->stream); });
   }
 };
 
@@ -622,8 +626,9 @@ int top_chunk(ttt_ctx* c, const int32_t* tgt, int64_t ld, const float* hsrc, int
     ab.R = c->R;
     ab.window = c->k;
     ab.pos0 = p0;
-    CK(Ops<T>::bwd(c, ab));
-    CK(rope_bwd_pack<T>(c->dq, c->dk, c->dv, c->cos_t, c->sin_t, p0, B, n, c->H, c->hd, tp<T>(c->dqkv), c->stream));
+    AttnBwdParts bp;
+    CK(Ops<T>::bwd(c, ab, &bp));
+    CK(rope_bwd_pack<T>(bp, c->cos_t, c->sin_t, p0, B, n, c->H, c->hd, tp<T>(c->dqkv), c->stream));
     GemmArgs g6 = mk(c->dqkv, 3 * d, lw.wqkvT, 3 * d, (int)M, d, 3 * d);
     g6.e.kind = EPI_F32;
     g6.e.c = c->tmpf;
@@ -973,8 +978,9 @@ int build(ttt_ctx* c, const ttt_weights* w) {
   AL(c->dqkv, rows_top * 3 * d * es);
   AL(c->err_dev, 256);
   c->ws_floats = 8 * rows_top * (int64_t)(d + 2 * H);
-  AL(c->ws, c->ws_floats * 4);
-  if (c->bot_overlap) AL(c->b_ws, c->ws_floats * 4);
+  c->ws_alloc_floats = 2 * c->ws_floats;
+  AL(c->ws, c->ws_alloc_floats * 4);
+  if (c->bot_overlap) AL(c->b_ws, c->ws_alloc_floats * 4);
   CK(hipMemset(c->err_dev, 0, 4));
   c->acts.resize(c->Lq);
   for (int j = 0; j < c->Lq; ++j) {

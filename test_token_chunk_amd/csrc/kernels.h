@@ -168,12 +168,25 @@ struct AttnBwdArgs {
 };
 template <typename T>
 hipError_t swa_bwd_simt(const AttnBwdArgs& a, hipStream_t s);
-hipError_t swa_bwd_mfma(const AttnBwdArgs& a, hipStream_t s);  // bf16
+// where a backward left dQ, dK, dV: sq (pkv) fp32 parts, plane floats apart, that the consumer
+// sums in order from zero; a count of 1 means the arrays hold the finished sums
+struct AttnBwdParts {
+  const float* dq = nullptr;
+  int sq = 1;
+  const float* dk = nullptr;
+  const float* dv = nullptr;
+  int pkv = 1;
+  int64_t plane = 0;
+};
+// bf16; with parts != null, split sums are not taken but described in *parts (dK/dV parts
+// are placed after the dQ parts in ws)
+hipError_t swa_bwd_mfma(const AttnBwdArgs& a, hipStream_t s, AttnBwdParts* parts = nullptr);
 
 // RoPE of q, k from a fp32 [B*n][3d] projection; q -> rr.q (and rr.qt), k, v -> rings
 hipError_t rope_qkv_f32in(const float* qkv, int B, const RopeRing& rr, int is_bf16, hipStream_t s);
 
-// RoPE backward of dq, dk (fp32, rotated frame) and packing [dq | dk | dv] into T [B*n][3d]
+// RoPE backward of dq, dk (fp32, rotated frame; each the ordered sum of its parts) and
+// packing [dq | dk | dv] into T [B*n][3d]
 template <typename T>
-hipError_t rope_bwd_pack(const float* dq, const float* dk, const float* dv, const float* cos_t, const float* sin_t,
-                         int64_t pos0, int B, int n, int H, int hd, T* dqkv, hipStream_t s);
+hipError_t rope_bwd_pack(const AttnBwdParts& g, const float* cos_t, const float* sin_t, int64_t pos0, int B, int n,
+                         int H, int hd, T* dqkv, hipStream_t s);

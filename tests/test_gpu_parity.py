@@ -118,6 +118,22 @@ def test_midk_two_fast_blocks_split_k_consumers_parity():
     compare_fast(ctx.fast_weights(0), o.get_fast(0), _w0(w, c), tw, "midk2")
 
 
+@pytest.mark.parametrize("window,T", [(1024, 1536), (2048, 2560)])
+def test_mid_long_window_split_attention_backward_parity(window, T):
+    """d=256 (two heads of 128), b=128, windows of 1024 and 2048 keys: the attention
+    backward of a chunk splits the key range of dQ (2 and 4 parts) and the query range of
+    dK/dV (2 parts) and leaves the parts side by side in the workspace; the RoPE backward
+    pass sums them in order while it packs [dq | dk | dv]."""
+    c = mkcfg(**dict(MID, window=window))
+    print(f"case mid window {window} T {T}", flush=True)
+    w, o, ctx, ref, got = run_pair(c, T, dist="zipf")
+    tl, tw = TOL["bf16"]
+    rel = np.max(np.abs(got - ref) / np.abs(ref))
+    print(f"mid window {window}: max loss rel err {rel:.3e}")
+    assert rel <= tl
+    compare_fast(ctx.fast_weights(0), o.get_fast(0), _w0(w, c), tw, f"mid window {window}")
+
+
 @pytest.mark.parametrize("chunk,T", [(136, 266), (132, 260)])
 def test_midk_two_fast_blocks_ragged_chunk_parity(chunk, T):
     """As above with chunk lengths or a ragged last chunk that are not multiples of 8 (chunks
