@@ -7,8 +7,10 @@ fallback: without the built library, or without a gfx950 GPU, calls fail.
 """
 from __future__ import annotations
 
+import atexit
 import ctypes
 import os
+import weakref
 from dataclasses import dataclass
 
 import numpy as np
@@ -81,6 +83,10 @@ def load_library():
         return _lib
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(f"{LIB_PATH} is not built; run test_token_chunk_amd/build_lib.py")
+    # torch first: it carries its own HIP runtime, and the library's HIP dependency must resolve
+    # to the runtime torch's memory and streams belong to (opened the other way round, the
+    # library saw no device)
+    import torch  # noqa: F401
     lib = ctypes.CDLL(LIB_PATH)
     vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
     lib.ttt_set_allocator.argtypes = [_ALLOC_FN, _FREE_FN, vp]
@@ -125,6 +131,28 @@ def _install_torch_allocator(lib):
     rc = lib.ttt_set_allocator(_hooks[0], _hooks[1], None)
     if rc:
         raise TTTError(rc, "ttt_set_allocator")
+
+
+# Contexts still open when the interpreter exits are destroyed by an exit handler, while the
+# allocator callbacks and torch are intact: at finalization, a context held in a module global
+# would otherwise free its memory through callbacks whose objects may already be gone.  The
+# handler is registered with the first context, after torch is imported, so it runs before
+# torch's own exit handlers.
+_LIVE = weakref.WeakSet()
+_exit_hook = False
+
+
+def _close_live():
+    for ctx in list(_LIVE):
+        ctx.close()
+
+
+def _track(ctx):
+    global _exit_hook
+    if not _exit_hook:
+        atexit.register(_close_live)
+        _exit_hook = True
+    _LIVE.add(ctx)
 
 
 @dataclass
@@ -194,6 +222,7 @@ class TTTContext:
         self._h = h
         self._lib = lib
         self.n_fast = cfg.n_fast or max(1, L // 4)
+        _track(self)
 
     def _check(self, rc):
         if rc:

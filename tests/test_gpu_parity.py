@@ -294,3 +294,28 @@ def test_generate_teacher_forced_against_oracle():
     assert np.array_equal(lg.argmax(axis=1)[clear], toks[0][clear])
     np.testing.assert_allclose(upd, oupd, rtol=1e-5)
     compare_fast(ctx.fast_weights(0), o.get_fast(0), _w0(w, c), 1e-4, "decode f32")
+
+
+def test_context_held_in_a_module_global_exits_cleanly():
+    """A context that is still open when the interpreter exits (held in a module global) is
+    destroyed by the binding's exit handler while its allocator callbacks still work: the
+    process ends with status 0."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    script = (
+        "import sys; sys.path.insert(0, %r)\n"
+        "from tests.cfgs import TOY, cfg\n"
+        "from test_token_chunk_amd import TTTConfig, TTTContext, synth\n"
+        "c = cfg(**dict(TOY, dtype='bf16'))\n"
+        "w = synth.weights(synth.Shape(c.n_layers, c.d_model, c.n_heads, c.d_ff, c.vocab), bf16=True)\n"
+        "seq = synth.tokens(1, 129, c.vocab, 'uniform', seed=2)\n"
+        "ctx = TTTContext(TTTConfig.from_dict(vars(c), max_positions=136), w)\n"
+        "ctx.prefill_seq(seq)\n"
+        "print('prefill ok', flush=True)\n" % root)
+    print("case module-global context exit", flush=True)
+    r = subprocess.run([sys.executable, "-c", script], capture_output=True, text=True, timeout=110)
+    print(r.stdout[-500:], r.stderr[-1500:])
+    assert "prefill ok" in r.stdout
+    assert r.returncode == 0
