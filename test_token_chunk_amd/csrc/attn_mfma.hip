@@ -1170,16 +1170,162 @@ hipError_t launch_bwd(const AttnBwdArgs& a, hipStream_t s, AttnBwdParts* parts) 
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- decode
+//
+// One query per (row, head) at position pos0 (n == 1), as in greedy generation: the window's
+// keys and values are read once, so the kernel is bound by HBM.  A block takes 256 keys of
+// the window (64 per wave) and the grid covers the window with S blocks per (row, head); the
+// parts are merged by k_swa_combine.  The HD/8 lanes of one key row each load a 16-byte piece
+// (a wave load covers 64/(HD/8) whole rows), the piece's dot product with the query (bf16 pairs
+// into fp32) is summed over those lanes with DPP moves, so every lane holds the scores of the
+// keys whose value pieces it loads; softmax weights use the wave's maximum, and the four waves
+// merge through LDS.
+
+typedef __bf16 bf16x2d __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dec_dot8(const uint4& a, const uint4& b) {
+  auto d2 = [](uint32_t x, uint32_t y, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2d, x), __builtin_bit_cast(bf16x2d, y), c, false);
+  };
+  return d2(a.w, b.w, d2(a.z, b.z, d2(a.y, b.y, d2(a.x, b.x, 0.f))));
+}
+
+// sum over the LPK (8 or 16) adjacent lanes of a key row: quad swaps, then the mirrored half
+// rows and rows of 16 (each step pairs lanes whose partial sums cover disjoint lanes)
+template <int LPK>
+__device__ __forceinline__ float dec_sum_lanes(float v) {
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));  // quad [1,0,3,2]
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));  // quad [2,3,0,1]
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false)); // half-row mirror
+  if constexpr (LPK == 16)
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false));  // row mirror
+  return v;
+}
+
+constexpr int DEC_KB = 256;  // keys per block
+
+template <int HD>
+__global__ __launch_bounds__(256) void k_swa_decode(AttnArgs a, int S) {
+  constexpr int LPK = HD / 8;       // lanes per key row
+  constexpr int KPR = 64 / LPK;     // keys per load round
+  constexpr int ROUNDS = 64 / KPR;  // rounds per wave (64 keys)
+  __shared__ float sm_o[4][HD];
+  __shared__ float sm_m[4], sm_l[4];
+  const int sp = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, dg = lane % LPK, sub = lane / LPK;
+  const int64_t pos = a.pos0;
+  const int64_t lo = pos - a.window + 1 > 0 ? pos - a.window + 1 : 0;
+  const int64_t blo = lo + (int64_t)sp * DEC_KB;
+  const int64_t bhi = blo + DEC_KB < pos + 1 ? blo + DEC_KB : pos + 1;  // this block's keys [blo, bhi)
+  const int64_t bh = (int64_t)b * a.H + h;
+  const uint4 qv = *(const uint4*)((const bf16*)a.q + bh * HD + dg * 8);
+  const bf16* Kb = (const bf16*)a.kr + bh * a.R * HD + dg * 8;
+  const bf16* Vb = (const bf16*)a.vr + bh * a.R * HD + dg * 8;
+  const int64_t wlo = blo + 64 * w;  // this wave's first key
+  const int s0 = (int)(wlo % a.R);    // its ring slot; 64 <= R, so one wrap at most
+  uint4 kv[ROUNDS], vv[ROUNDS];
+#pragma unroll
+  for (int i = 0; i < ROUNDS; ++i) {
+    const int kk = i * KPR + sub;
+    int slot = s0 + kk;
+    if (slot >= a.R) slot -= a.R;
+    const bool ok = wlo + kk < bhi;
+    kv[i] = ok ? *(const uint4*)(Kb + (int64_t)slot * HD) : make_uint4(0u, 0u, 0u, 0u);
+    vv[i] = ok ? *(const uint4*)(Vb + (int64_t)slot * HD) : make_uint4(0u, 0u, 0u, 0u);
+  }
+  float sc[ROUNDS];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < ROUNDS; ++i) {
+    sc[i] = dec_sum_lanes<LPK>(dec_dot8(kv[i], qv));
+    if (wlo + i * KPR + sub < bhi) mx = fmaxf(mx, sc[i]);
+  }
+#pragma unroll
+  for (int o = LPK; o < 64; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+  const float sl2 = 1.4426950408889634f / sqrtf((float)HD);
+  float l = 0.f, o8[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) o8[j] = 0.f;
+#pragma unroll
+  for (int i = 0; i < ROUNDS; ++i) {
+    const float pw = wlo + i * KPR + sub < bhi ? exp2f((sc[i] - mx) * sl2) : 0.f;
+    l += pw;
+    const uint32_t u[4] = {vv[i].x, vv[i].y, vv[i].z, vv[i].w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      o8[2 * j] += pw * __uint_as_float(u[j] << 16);
+      o8[2 * j + 1] += pw * __uint_as_float(u[j] & 0xffff0000u);
+    }
+  }
+#pragma unroll
+  for (int o = LPK; o < 64; o <<= 1) {
+    l += __shfl_xor(l, o, 64);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) o8[j] += __shfl_xor(o8[j], o, 64);
+  }
+  if (sub == 0) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) sm_o[w][dg * 8 + j] = o8[j];
+  }
+  if (lane == 0) {
+    sm_m[w] = mx;
+    sm_l[w] = l;
+  }
+  __syncthreads();
+  if (threadIdx.x >= HD) return;
+  const int d = threadIdx.x;
+  float M = fmaxf(fmaxf(sm_m[0], sm_m[1]), fmaxf(sm_m[2], sm_m[3]));
+  float L = 0.f, O = 0.f;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const float wt = sm_m[v] == -INFINITY ? 0.f : exp2f((sm_m[v] - M) * sl2);
+    L += wt * sm_l[v];
+    O += wt * sm_o[v][d];
+  }
+  if (S == 1) {
+    ((bf16*)a.o)[(int64_t)b * a.H * HD + (int64_t)h * HD + d] = f2bf(O / L);
+    if (a.lse && d == 0) a.lse[bh] = M * (sl2 * 0.6931471805599453f) + logf(L);
+    return;
+  }
+  const int64_t plane = (int64_t)a.B * a.H;  // n == 1
+  const int64_t row = (int64_t)sp * plane + bh;
+  a.ws[row * HD + d] = O;
+  if (d == 0) {
+    float* pm = a.ws + (int64_t)S * plane * HD;
+    pm[row] = M;
+    pm[(int64_t)S * plane + row] = L;
+  }
+}
+
+template <int HD>
+hipError_t launch_decode(const AttnArgs& a, int S, hipStream_t s) {
+  hipLaunchKernelGGL(k_swa_decode<HD>, dim3(S, a.H, a.B), dim3(256), 0, s, a, S);
+  if (S > 1) hipLaunchKernelGGL(k_swa_combine, dim3(cdiv((int64_t)a.B * a.H, 4)), dim3(256), 0, s, a, S);
+  return hipGetLastError();
+}
+
+// blocks of 256 keys over the window of the single query, or 0 when the decode kernel does not apply
+int decode_splits(const AttnArgs& a) {
+  if (a.n != 1 || (a.hd != 64 && a.hd != 128) || a.R < 64 || a.window < 1) return 0;
+  if (((uintptr_t)a.q | (uintptr_t)a.kr | (uintptr_t)a.vr) & 15) return 0;
+  const int64_t nkeys = std::min<int64_t>(a.window, a.pos0 + 1);
+  const int S = (int)cdiv(nkeys, DEC_KB);
+  if (S > 1 && (!a.ws || (int64_t)S * a.B * a.H * (a.hd + 2) > a.ws_floats)) return 0;
+  return S;
+}
+
 }  // namespace
 
 // key-range parts the forward would use for this call (1: single kernel)
 int swa_fwd_mfma_splits(const AttnArgs& a) {
+  if (const int S = decode_splits(a)) return S;
   if (a.n == 0 || a.R % 8 != 0 || (a.hd != 32 && a.hd != 64 && a.hd != 96 && a.hd != 128)) return 1;
   return fwd_splits(a);
 }
 
 hipError_t swa_fwd_mfma(const AttnArgs& a, hipStream_t s) {
   if (a.n == 0) return hipSuccess;
+  if (const int S = decode_splits(a)) return a.hd == 128 ? launch_decode<128>(a, S, s) : launch_decode<64>(a, S, s);
   // 64-key tiles read 8-key groups of the transposed value ring: R % 8 == 0
   if (a.R % 8 != 0) return swa_fwd_simt<bf16>(a, s);
   switch (a.hd) {

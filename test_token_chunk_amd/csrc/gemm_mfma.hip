@@ -1058,6 +1058,8 @@ bool wide_ok(const GemmArgs& g) {
 }
 
 GemmPlan gemm_plan(const GemmArgs& g) {
+  // a handful of rows: the matrix-vector kernel, one pass over the weights, no K split
+  if (gemv_ok(g)) return {4, 1, g.K};
   const bool splittable = g.e.kind == EPI_F32 || g.e.kind == EPI_T || g.e.kind == EPI_ADD_F32;
   // short K (the weight gradients over one chunk): the prologue and the epilogue weigh as much as
   // the main loop, and two 128 x 128 blocks per CU overlap them better than one wide block
@@ -1108,6 +1110,7 @@ hipError_t gemm_mfma_bf16(const GemmArgs& g, hipStream_t s) {
   if (!ok) return g.e.kind == EPI_SWIGLU_IL ? hipErrorInvalidValue : gemm_simt_bf16(g, s);
   if (g.e.kind == EPI_SWIGLU_IL && (g.N % 64 != 0)) return hipErrorInvalidValue;
   const GemmPlan p = gemm_plan(g);
+  if (p.kern == 4) return gemv_bf16(g, s);
   if (p.S > 1) return launch_splitk(g, p.S, p.Ks, p.kern >= 2, s);
   if (p.kern >= 2) {
     const int bm = p.kern == 3 ? 256 : 128;

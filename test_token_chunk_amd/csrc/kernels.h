@@ -80,6 +80,12 @@ hipError_t gemm_simt_f32(const GemmArgs& g, hipStream_t s);   // fp32 operands
 hipError_t gemm_simt_bf16(const GemmArgs& g, hipStream_t s);  // bf16 operands, SIMT
 hipError_t gemm_mfma_bf16(const GemmArgs& g, hipStream_t s);  // bf16 operands, MFMA
 int gemm_mfma_splits(const GemmArgs& g, int* ks_out);          // split-K parts gemm_mfma_bf16 would use
+// M <= 8 rows per batch (decode), bf16 operands: one read of the weight rows per product;
+// kinds EPI_F32, EPI_T, EPI_ADD_F32 and the SwiGLU kinds without z_g / z_u / act^T outputs,
+// K % 8 == 0, 16-byte aligned operands and 8-element strides (gemv_ok); gemm_mfma_bf16 takes
+// it by itself for such products
+bool gemv_ok(const GemmArgs& g);
+hipError_t gemv_bf16(const GemmArgs& g, hipStream_t s);
 
 // ------------------------------------------------------------------ elementwise
 // Token arrays are [B][ld] int32 (row stride ld); activations are [B*n][d] rows.

@@ -21,7 +21,9 @@ def _torch():
 GEMM_SHAPES = [(128, 128, 64), (300, 200, 72), (1, 512, 128), (1000, 384, 40), (257, 129, 1000), (64, 96, 8),
                (1024, 2560, 256), (1000, 384, 4100), (256, 640, 2056),
                # wide tiles: 128-row (small grid), 128-row split K, 256-row (large grid)
-               (512, 512, 256), (512, 1024, 2048), (4096, 4096, 256)]
+               (512, 512, 256), (512, 1024, 2048), (4096, 4096, 256),
+               # a handful of rows (decode): the matrix-vector kernel, K in whole and partial 512-element steps
+               (1, 7680, 2560), (2, 300, 520), (3, 1000, 2056), (5, 129, 40), (8, 2560, 6912), (2, 32000, 2560)]
 
 
 def _workspace(torch, use):
@@ -82,6 +84,11 @@ ATTN_CASES = [
     (1, 1, 128, 1, 64, 5000, 128),
     (1, 2, 96, 70, 150, 77, 224),
     (1, 2, 128, 300, 1024, 2000, 1344),
+    # one query per head (decode): blocks of 256 window keys, merged when there are several
+    (1, 2, 128, 1, 1000, 700, 1100),
+    (2, 3, 128, 1, 2048, 5000, 2100),
+    (1, 2, 64, 1, 300, 1234, 320),
+    (1, 4, 128, 1, 8192, 20000, 9216),
 ]
 
 

@@ -296,6 +296,42 @@ def test_generate_teacher_forced_against_oracle():
     compare_fast(ctx.fast_weights(0), o.get_fast(0), _w0(w, c), 1e-4, "decode f32")
 
 
+def test_generate_bf16_two_rows_teacher_forced_against_oracle():
+    """bf16 greedy decode of two rows (d=256, two heads of 128, window 640, updates every 64
+    tokens): every product of a decode step has one or two rows, so it runs the
+    matrix-vector kernel (fp32 and residual-add outputs, SwiGLU with the interleaved
+    per-row fast weights), and attention of the single query runs the decode kernel with
+    up to 3 blocks of window keys.  Replaying the GPU's tokens in the oracle: each GPU token's
+    logit is within the bf16 tolerance of the oracle's maximum, ids agree wherever the
+    oracle's top-2 margin is clear, and the update losses and fast weights match."""
+    c = mkcfg(**dict(MID, window=640, batch=2))
+    w = synth.weights(_shape(c), bf16=True)
+    T, n_new = 384, 160
+    seq = synth.tokens(2, T + 1, c.vocab, "zipf", seed=9)
+    print("case generate bf16 two rows", flush=True)
+    ctx = _ctx(c, w, T + n_new + 8)
+    ctx.prefill_seq(seq)
+    toks, upd = ctx.generate(seq[:, T], n_new, 64)
+    o = Oracle(c, w, T + n_new + 8)
+    o.prefill(seq)
+    ot, oupd, logits = o.generate(seq[:, T], n_new, 64, forced=toks, want_logits=True)
+    tl, tw = TOL["bf16"]
+    for r in range(2):
+        lg = logits[r]
+        top = lg.max(axis=1)
+        chosen = lg[np.arange(n_new), toks[r]]
+        tol = tl * np.max(np.abs(lg))
+        print(f"row {r}: worst logit gap {np.max(top - chosen):.3e} (tol {tol:.3e})")
+        assert np.all(top - chosen <= tol)
+        srt = np.sort(lg, axis=1)
+        clear = (srt[:, -1] - srt[:, -2]) > tol
+        assert clear.sum() > n_new // 4
+        assert np.array_equal(lg.argmax(axis=1)[clear], toks[r][clear])
+    np.testing.assert_allclose(upd, oupd, rtol=tl)
+    for r in range(2):
+        compare_fast(ctx.fast_weights(r), o.get_fast(r), _w0(w, c), tw, f"decode bf16 row {r}")
+
+
 def test_context_held_in_a_module_global_exits_cleanly():
     """A context that is still open when the interpreter exits (held in a module global) is
     destroyed by the binding's exit handler while its allocator callbacks still work: the
