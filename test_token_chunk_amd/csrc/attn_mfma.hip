@@ -1297,10 +1297,49 @@ __global__ __launch_bounds__(256) void k_swa_decode(AttnArgs a, int S) {
   }
 }
 
+// merge of the S key-block parts of one (row, head): a block per (row, head) loads all parts
+// at once (thread t: parts t / (HD/8) + k * 256 / (HD/8), dims (t % (HD/8)) * 8 ..+8) and sums
+// them through LDS, so the many parts of a long window cost one round of loads
+template <int HD>
+__global__ __launch_bounds__(256) void k_swa_dec_combine(AttnArgs a, int S) {
+  constexpr int DG = HD / 8, PS = 256 / DG;
+  __shared__ float red[PS][HD];
+  __shared__ float sh[16];
+  const int64_t bh = blockIdx.x, plane = (int64_t)a.B * a.H;
+  const float* pm = a.ws + (int64_t)S * plane * HD;
+  const float* pl = pm + (int64_t)S * plane;
+  const int t = threadIdx.x, dg = t % DG, ps = t / DG;
+  const float sl2 = 1.4426950408889634f / sqrtf((float)HD);
+  float mloc = -INFINITY;
+  for (int sp = t; sp < S; sp += 256) mloc = fmaxf(mloc, pm[sp * plane + bh]);
+  const float M = block_max(mloc, sh);
+  float o[8], l = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) o[j] = 0.f;
+  for (int sp = ps; sp < S; sp += PS) {
+    const int64_t row = sp * plane + bh;
+    const float w = pm[row] == -INFINITY ? 0.f : exp2f((pm[row] - M) * sl2);
+    if (dg == 0) l += w * pl[row];
+    const float4 x0 = *(const float4*)(a.ws + row * HD + dg * 8), x1 = *(const float4*)(a.ws + row * HD + dg * 8 + 4);
+    o[0] += w * x0.x; o[1] += w * x0.y; o[2] += w * x0.z; o[3] += w * x0.w;
+    o[4] += w * x1.x; o[5] += w * x1.y; o[6] += w * x1.z; o[7] += w * x1.w;
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) red[ps][dg * 8 + j] = o[j];
+  const float L = block_sum(l, sh);  // (its barriers also order the LDS writes above)
+  if (t >= HD) return;
+  float O = 0.f;
+#pragma unroll
+  for (int p = 0; p < PS; ++p) O += red[p][t];
+  const int64_t b = bh / a.H, h = bh % a.H;
+  ((bf16*)a.o)[b * a.H * HD + h * HD + t] = f2bf(O / L);
+  if (a.lse && t == 0) a.lse[bh] = M * (sl2 * 0.6931471805599453f) + logf(L);
+}
+
 template <int HD>
 hipError_t launch_decode(const AttnArgs& a, int S, hipStream_t s) {
   hipLaunchKernelGGL(k_swa_decode<HD>, dim3(S, a.H, a.B), dim3(256), 0, s, a, S);
-  if (S > 1) hipLaunchKernelGGL(k_swa_combine, dim3(cdiv((int64_t)a.B * a.H, 4)), dim3(256), 0, s, a, S);
+  if (S > 1) hipLaunchKernelGGL(k_swa_dec_combine<HD>, dim3(a.B * a.H), dim3(256), 0, s, a, S);
   return hipGetLastError();
 }
 

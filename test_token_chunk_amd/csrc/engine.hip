@@ -266,7 +266,8 @@ struct Ops<bf16> {
     g.ws = st ? nullptr : c->ws;
     g.ws_floats = st ? 0 : c->ws_floats;
     if (!st) st = c->stream;
-    const int kind_cls = g.e.kind == EPI_SWIGLU_IL ? (int)EPI_SWIGLU : g.e.kind;  // one SwiGLU class
+    // one SwiGLU class; the q|k|v product with RoPE counts as the fp32-output product it replaces
+    const int kind_cls = g.e.kind == EPI_SWIGLU_IL ? (int)EPI_SWIGLU : g.e.kind == EPI_QKV_ROPE ? (int)EPI_F32 : g.e.kind;
     const int cls = (c->mfma && gemm_mfma_splits(g, nullptr) > 1) ? PC_GEMM_SPLITK : kind_cls;
     return timed(c, cls, gemm_flops(g), st,
                  [&] { return c->mfma ? gemm_mfma_bf16(g, st) : gemm_simt_bf16(g, st); });
@@ -363,7 +364,6 @@ int layer_fwd(ttt_ctx* c, int l, float* h, int n, int64_t p0, int mode, TopActs*
     g.e.kind = EPI_F32;
     g.e.c = c->qkvb;
     g.e.ldc = 3 * d;
-    CK(Ops<T>::gemm(c, g));
     RopeRing rr;
     rr.cos_t = c->cos_t;
     rr.sin_t = c->sin_t;
@@ -378,7 +378,16 @@ int layer_fwd(ttt_ctx* c, int l, float* h, int n, int64_t p0, int mode, TopActs*
     rr.vr = w.vr;
     rr.vtr = w.vtr;
     rr.ktr = w.ktr;
-    CK(rope_qkv_f32in(c->qkvb, B, rr, c->bf16 ? 1 : 0, c->stream));
+    // a handful of rows (decode): RoPE and the ring writes in the matrix-vector product itself
+    GemmArgs gr = g;
+    gr.e.kind = EPI_QKV_ROPE;
+    gr.e.rr = rr;
+    if (c->mfma && c->bf16 && gemv_ok(gr)) {
+      CK(Ops<T>::gemm(c, gr));
+    } else {
+      CK(Ops<T>::gemm(c, g));
+      CK(rope_qkv_f32in(c->qkvb, B, rr, c->bf16 ? 1 : 0, c->stream));
+    }
     AttnArgs a;
     a.q = rr.q;
     a.kr = w.kr;

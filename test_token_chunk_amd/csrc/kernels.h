@@ -14,7 +14,9 @@ enum EpiKind {
   EPI_SWIGLU = 3,  // dual: act = silu(acc_g) * acc_u -> c (T); zg, zu (T) and act^T (T) optional
   EPI_SWIGLU_BWD = 4, // acc = d act: dz_g, dz_u -> c = dz (T, [m][2f]) and dz^T (T, [2f][ldt])
   EPI_SGD = 5,     // acc = gradient: master (fp32) -= lr * acc; shadow (T) and shadow^T (T) refreshed
-  EPI_QKV_ROPE = 6, // acc = [q|k|v] row: RoPE of q, k; q -> c, k,v -> rings (see RopeRing)
+  EPI_QKV_ROPE = 6, // acc = [q|k|v] row (N = 3 H hd, row m = token m % n of batch row m / n): RoPE of q, k
+                    // at pos0 + m % n; q (q^T) and the ring slots of k (K^T), v, V^T written as in
+                    // rope_qkv_f32in; matrix-vector kernel only (gemv_ok)
   EPI_SWIGLU_IL = 7 // single operand with gate/up rows interleaved in groups of 32 (see swiglu_il_row):
                     // columns 64g..64g+31 are gate rows 32g.., 64g+32..64g+63 the matching up rows;
                     // outputs as EPI_SWIGLU with N = 2f (act, z_g, z_u [m][f], act^T)
