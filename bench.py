@@ -103,6 +103,9 @@ def main():
     ap.add_argument("--tokens", type=int, default=0, help="override T (tokens per row)")
     ap.add_argument("--cpu-sample", type=int, default=32, help="oracle sample size in tokens (0 = skip)")
     ap.add_argument("--lookahead", type=int, default=0, help="chunks per batched lower-block pass (0 = library default)")
+    ap.add_argument("--workload", default="prefill", choices=("prefill", "decode"),
+                    help="decode: greedy generation after a full window, an inner-loop update every chunk")
+    ap.add_argument("--decode-tokens", type=int, default=1024, help="decode: generated tokens per step")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device-to-device copy 3 times (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -124,6 +127,8 @@ def main():
 
     from test_token_chunk_amd import TTTConfig, TTTContext, synth
 
+    if args.workload == "decode":
+        return decode_bench(args)
     c = dict(CONFIGS[args.config])
     T = args.tokens or c.pop("T")
     c.pop("T", None)
@@ -206,6 +211,78 @@ def main():
     }
     if args.cpu_sample > 0:
         out["cpu_baseline"] = cpu_baseline(c, w, seq, args.cpu_sample)
+    print(json.dumps(out))
+
+
+def decode_bench(args):
+    """Greedy generation of one row with test-time training: the window is filled by a prefill of
+    window + chunk tokens, then a step generates --decode-tokens tokens with an inner-loop update
+    after every chunk of them (forward of those positions again, loss, backward, SGD).  The roofline
+    kernel is the attention of the single query over its window blocks, bound by reading the
+    window's keys and values from HBM."""
+    import torch
+
+    from test_token_chunk_amd import PROFILE_KERNELS, TTTConfig, TTTContext, synth
+
+    c = dict(CONFIGS[args.config])
+    c.pop("T")
+    dist = c.pop("dist")
+    n_new, b, k = args.decode_tokens, c["chunk"], c["window"]
+    P = k + b
+    upd = min(b, n_new)
+    torch.cuda.set_device(0)
+    w = synth.weights(synth.Shape(c["n_layers"], c["d_model"], c["n_heads"], c["d_ff"], c["vocab"]),
+                      bf16=c["dtype"] == "bf16")
+    seq = synth.tokens(1, P + 1, c["vocab"], dist)
+    max_pos = P + (max(args.warmup, args.steps) + args.steps + 1) * n_new + 8
+    ctx = TTTContext(TTTConfig(batch=1, max_positions=max_pos, **c), w)
+    ctx.prefill(seq[:, :P], seq[:, 1:])
+    last = seq[:, P]
+    print(f"decode: config {args.config}, window filled by {P} tokens, {n_new} tokens per step, update every {upd}",
+          file=sys.stderr, flush=True)
+    # warm-up steps run with the attention launches timed as well, at least as many as the timed
+    # steps, so that the library's pool already holds every event the timed region records
+    ctx.profile_begin(["swa_decode"])
+    for i in range(max(args.warmup, args.steps)):
+        toks, _ = ctx.generate(last, n_new, upd)
+        last = toks[:, -1]
+        print(f"warmup step {i} done", file=sys.stderr, flush=True)
+    ctx.profile_end()
+    ctx.profile_begin(["swa_decode"])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    losses = []
+    for i in range(args.steps):
+        toks, ul = ctx.generate(last, n_new, upd)
+        last = toks[:, -1]
+        losses.append(float(ul[0, -1]) if ul.size else None)
+        print(f"step {i} done", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    st = ctx.profile_end().get("swa_decode")
+    ms = dt / args.steps * 1e3
+    H, hd = c["n_heads"], c["d_model"] // c["n_heads"]
+    roof = None
+    if st and st["count"]:
+        # algorithmic bytes of one launch (position >= window - 1, so every query sees k keys): the
+        # window's keys and values (bf16), the query, and the fp32 parts of S = k/256 blocks per head
+        S = -(-k // 256)
+        byts = 2 * k * H * hd * 2 + H * hd * 2 + S * H * (hd + 2) * 4
+        avg_s = st["ms"] / st["count"] / 1e3
+        roof = {"kernel": PROFILE_KERNELS["swa_decode"][0].replace("hd", str(hd)), "class": "swa_decode",
+                "bound": "hbm", "achieved": round(byts / avg_s / 1e9, 1), "peak": 8000.0, "unit": "GB/s",
+                "frac": round(byts / avg_s / 8e12, 4), "traffic": None, "avg_launch_us": round(avg_s * 1e6, 2),
+                "launches_per_step": st["count"] // args.steps, "mb_per_launch": round(byts / 1e6, 2)}
+    out = {
+        "metric": "TTT greedy decode tokens/s (update every chunk)", "value": round(args.steps * n_new / dt, 1),
+        "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 2),
+        "ms_per_token": round(ms / n_new, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": c["dtype"], "data": "synthetic",
+        "config": {"workload": f"ttt-decode-{args.config}", "layers": c["n_layers"], "d_model": c["d_model"],
+                   "window": k, "chunk": b, "fast_blocks": c["n_fast"], "batch": 1, "tokens_per_step": n_new,
+                   "update_every": upd, "prefill_tokens": P, "token_dist": dist},
+        "last_update_loss": losses[-1], "roofline": roof,
+    }
     print(json.dumps(out))
 
 

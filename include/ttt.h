@@ -168,11 +168,13 @@ int64_t ttt_position(const ttt_ctx* ctx);
  * 2 residual add, 3 SwiGLU (gate and up), 4 SwiGLU backward, 5 weight gradient
  * with the fused SGD step (one kernel each) -- 6 K-split GEMMs (kernel + ordered
  * sum), 7 sliding-window attention forward (one kernel), 8 the same with a split
- * key range (kernel + merge), 9 attention backward (all its kernels). */
+ * key range (kernel + merge), 9 attention backward (all its kernels), 10 attention
+ * of one query per head in generation (the kernel over blocks of window keys; their
+ * merge is not timed). */
 enum {
   TTT_PROF_GEMM_F32 = 0, TTT_PROF_GEMM_BF16 = 1, TTT_PROF_GEMM_RESID = 2, TTT_PROF_GEMM_SWIGLU = 3,
   TTT_PROF_GEMM_SWIGLU_BWD = 4, TTT_PROF_GEMM_SGD = 5, TTT_PROF_GEMM_SPLITK = 6, TTT_PROF_SWA_FWD = 7,
-  TTT_PROF_SWA_FWD_SPLIT = 8, TTT_PROF_SWA_BWD = 9, TTT_PROF_CLASSES = 10
+  TTT_PROF_SWA_FWD_SPLIT = 8, TTT_PROF_SWA_BWD = 9, TTT_PROF_SWA_DECODE = 10, TTT_PROF_CLASSES = 11
 };
 int ttt_profile_enable(ttt_ctx* ctx, int32_t on);
 int ttt_profile_read(ttt_ctx* ctx, int32_t n_classes, double* ms, int64_t* counts, double* flops);

@@ -28,7 +28,7 @@ EXPORTS = ("ttt_set_allocator", "ttt_create", "ttt_prefill_chunk", "ttt_prefill"
            "ttt_generate", "ttt_get_fast_weights", "ttt_reset", "ttt_position", "ttt_destroy", "ttt_last_error",
            "ttt_profile_enable", "ttt_profile_read")
 PROFILE_CLASSES = ("gemm_f32out", "gemm_bf16out", "gemm_resid", "gemm_swiglu", "gemm_swiglu_bwd", "gemm_sgd",
-                   "gemm_splitk", "swa_fwd", "swa_fwd_split", "swa_bwd")
+                   "gemm_splitk", "swa_fwd", "swa_fwd_split", "swa_bwd", "swa_decode")
 # kernels behind each class (rocprofv3 names); classes marked single=True are one kernel
 PROFILE_KERNELS = {  # class: (kernels, one kernel per launch)
     "gemm_f32out": ("k_gemm_wide<256|128, 0, false> (k_gemm_dl / k_gemm_mfma off the wide-tile shapes)", False),
@@ -41,8 +41,9 @@ PROFILE_KERNELS = {  # class: (kernels, one kernel per launch)
     "gemm_splitk": ("k_gemm_wide<128, 0, true> + k_splitk_reduce4<0>", False),
     "swa_fwd": ("k_swa_fwd<hd, 8, false>", True),
     "swa_fwd_split": ("k_swa_fwd<hd, 8, true> + k_swa_combine", False),
-    "swa_bwd": ("k_dvec + k_heads_transpose + k_swa_dq<hd, 8, *> (+ k_dq_reduce) + k_swa_dkv<hd, *> "
-                "(+ k_dkv_reduce)", False),
+    "swa_bwd": ("k_swa_dq2<hd, *> (k_dvec + k_swa_dq<hd, 8, *> off hd 128) + k_swa_dkv<hd, *>; split parts "
+                "are summed by k_rope_bwd_pack4 outside the class", False),
+    "swa_decode": ("k_swa_decode<hd>", True),
 }
 
 

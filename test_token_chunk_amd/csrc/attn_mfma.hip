@@ -1362,6 +1362,26 @@ int swa_fwd_mfma_splits(const AttnArgs& a) {
   return fwd_splits(a);
 }
 
+int swa_decode_splits(const AttnArgs& a) { return decode_splits(a); }
+
+hipError_t swa_decode_blocks(const AttnArgs& a, int S, hipStream_t s) {
+  if (S < 1 || S != decode_splits(a)) return hipErrorInvalidValue;
+  if (a.hd == 128)
+    hipLaunchKernelGGL(k_swa_decode<128>, dim3(S, a.H, a.B), dim3(256), 0, s, a, S);
+  else
+    hipLaunchKernelGGL(k_swa_decode<64>, dim3(S, a.H, a.B), dim3(256), 0, s, a, S);
+  return hipGetLastError();
+}
+
+hipError_t swa_decode_merge(const AttnArgs& a, int S, hipStream_t s) {
+  if (S <= 1) return hipSuccess;
+  if (a.hd == 128)
+    hipLaunchKernelGGL(k_swa_dec_combine<128>, dim3(a.B * a.H), dim3(256), 0, s, a, S);
+  else
+    hipLaunchKernelGGL(k_swa_dec_combine<64>, dim3(a.B * a.H), dim3(256), 0, s, a, S);
+  return hipGetLastError();
+}
+
 hipError_t swa_fwd_mfma(const AttnArgs& a, hipStream_t s) {
   if (a.n == 0) return hipSuccess;
   if (const int S = decode_splits(a)) return a.hd == 128 ? launch_decode<128>(a, S, s) : launch_decode<64>(a, S, s);

@@ -193,7 +193,7 @@ int fail(ttt_ctx* c, int code, const std::string& msg) {
 // Classes: GEMMs without split by epilogue kind (EPI_F32 .. EPI_SGD; one kernel each),
 // split-K GEMMs (kernel + ordered reduce), attention forward (one kernel), split-key
 // attention forward (kernel + combine), attention backward (dvec + dq + dk/dv)
-enum { PC_GEMM_SPLITK = 6, PC_SWA_FWD = 7, PC_SWA_FWD_SPLIT = 8, PC_SWA_BWD = 9, PC_N = 10 };
+enum { PC_GEMM_SPLITK = 6, PC_SWA_FWD = 7, PC_SWA_FWD_SPLIT = 8, PC_SWA_BWD = 9, PC_SWA_DEC = 10, PC_N = 11 };
 
 hipEvent_t next_event(ttt_ctx* c) {
   if (c->ev_used == c->ev_pool.size()) {
@@ -294,6 +294,14 @@ struct Ops<bf16> {
     a.ws = c->ws;
     a.ws_floats = c->ws_floats;
     double fl = 4.0 * a.hd * a.H * a.B * attn_pairs(c, a.n, a.pos0);
+    if (c->mfma) {
+      // one query per head (decode): the window-block kernel is timed on its own, the merge after it
+      if (const int S = swa_decode_splits(a)) {
+        hipError_t e = timed(c, PC_SWA_DEC, fl, c->stream,
+                             [&] { return swa_decode_blocks(a, S, c->stream); });
+        return e != hipSuccess ? e : swa_decode_merge(a, S, c->stream);
+      }
+    }
     const int cls = (c->mfma && swa_fwd_mfma_splits(a) > 1) ? PC_SWA_FWD_SPLIT : PC_SWA_FWD;
     return timed(c, cls, fl, c->stream,
                  [&] { return c->mfma ? swa_fwd_mfma(a, c->stream) : swa_fwd_simt<bf16>(a, c->stream); });
