@@ -265,8 +265,8 @@ def decode_bench(args):
     roof = None
     if st and st["count"]:
         # algorithmic bytes of one launch (position >= window - 1, so every query sees k keys): the
-        # window's keys and values (bf16), the query, and the fp32 parts of S = k/256 blocks per head
-        S = -(-k // 256)
+        # window's keys and values (bf16), the query, and the fp32 parts of S = k/128 blocks per head
+        S = -(-k // 128)
         byts = 2 * k * H * hd * 2 + H * hd * 2 + S * H * (hd + 2) * 4
         avg_s = st["ms"] / st["count"] / 1e3
         roof = {"kernel": PROFILE_KERNELS["swa_decode"][0].replace("hd", str(hd)), "class": "swa_decode",

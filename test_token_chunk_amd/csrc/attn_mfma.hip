@@ -1173,9 +1173,9 @@ hipError_t launch_bwd(const AttnBwdArgs& a, hipStream_t s, AttnBwdParts* parts) 
 // ---------------------------------------------------------------- decode
 //
 // One query per (row, head) at position pos0 (n == 1), as in greedy generation: the window's
-// keys and values are read once, so the kernel is bound by HBM.  A block takes 256 keys of
-// the window (64 per wave) and the grid covers the window with S blocks per (row, head); the
-// parts are merged by k_swa_combine.  The HD/8 lanes of one key row each load a 16-byte piece
+// keys and values are read once, so the kernel is bound by HBM.  A block takes 128 keys of
+// the window (32 per wave) and the grid covers the window with S blocks per (row, head); the
+// parts are merged by k_swa_dec_combine.  The HD/8 lanes of one key row each load a 16-byte piece
 // (a wave load covers 64/(HD/8) whole rows), the piece's dot product with the query (bf16 pairs
 // into fp32) is summed over those lanes with DPP moves, so every lane holds the scores of the
 // keys whose value pieces it loads; softmax weights use the wave's maximum, and the four waves
@@ -1202,13 +1202,13 @@ __device__ __forceinline__ float dec_sum_lanes(float v) {
   return v;
 }
 
-constexpr int DEC_KB = 256;  // keys per block
+constexpr int DEC_KB = 128;  // keys per block (measured: 128 beats 256 and 64)
 
 template <int HD>
 __global__ __launch_bounds__(256) void k_swa_decode(AttnArgs a, int S) {
   constexpr int LPK = HD / 8;       // lanes per key row
   constexpr int KPR = 64 / LPK;     // keys per load round
-  constexpr int ROUNDS = 64 / KPR;  // rounds per wave (64 keys)
+  constexpr int ROUNDS = 32 / KPR;  // rounds per wave (32 keys)
   __shared__ float sm_o[4][HD];
   __shared__ float sm_m[4], sm_l[4];
   const int sp = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -1221,7 +1221,7 @@ __global__ __launch_bounds__(256) void k_swa_decode(AttnArgs a, int S) {
   const uint4 qv = *(const uint4*)((const bf16*)a.q + bh * HD + dg * 8);
   const bf16* Kb = (const bf16*)a.kr + bh * a.R * HD + dg * 8;
   const bf16* Vb = (const bf16*)a.vr + bh * a.R * HD + dg * 8;
-  const int64_t wlo = blo + 64 * w;  // this wave's first key
+  const int64_t wlo = blo + 32 * w;  // this wave's first key
   const int s0 = (int)(wlo % a.R);    // its ring slot; 64 <= R, so one wrap at most
   uint4 kv[ROUNDS], vv[ROUNDS];
 #pragma unroll
@@ -1343,7 +1343,7 @@ hipError_t launch_decode(const AttnArgs& a, int S, hipStream_t s) {
   return hipGetLastError();
 }
 
-// blocks of 256 keys over the window of the single query, or 0 when the decode kernel does not apply
+// blocks of DEC_KB keys over the window of the single query, or 0 when the decode kernel does not apply
 int decode_splits(const AttnArgs& a) {
   if (a.n != 1 || (a.hd != 64 && a.hd != 128) || a.R < 64 || a.window < 1) return 0;
   if (((uintptr_t)a.q | (uintptr_t)a.kr | (uintptr_t)a.vr) & 15) return 0;

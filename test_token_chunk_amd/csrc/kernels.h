@@ -153,7 +153,7 @@ hipError_t swa_fwd_simt(const AttnArgs& a, hipStream_t s);
 hipError_t swa_fwd_mfma(const AttnArgs& a, hipStream_t s);  // bf16
 int swa_fwd_mfma_splits(const AttnArgs& a);                  // key-range parts it would use
 // the two launches swa_fwd_mfma makes for one query per (row, head) (n == 1, hd 64 or 128):
-// S blocks of 256 window keys per (row, head) (S = swa_decode_splits, 0 when that form does
+// S blocks of 128 window keys per (row, head) (S = swa_decode_splits, 0 when that form does
 // not apply; parts in ws when S > 1), then their merge into o and lse
 int swa_decode_splits(const AttnArgs& a);
 hipError_t swa_decode_blocks(const AttnArgs& a, int S, hipStream_t s);

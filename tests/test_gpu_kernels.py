@@ -84,7 +84,7 @@ ATTN_CASES = [
     (1, 1, 128, 1, 64, 5000, 128),
     (1, 2, 96, 70, 150, 77, 224),
     (1, 2, 128, 300, 1024, 2000, 1344),
-    # one query per head (decode): blocks of 256 window keys, merged when there are several
+    # one query per head (decode): blocks of 128 window keys (6, 16, 3 and 64 here), merged
     (1, 2, 128, 1, 1000, 700, 1100),
     (2, 3, 128, 1, 2048, 5000, 2100),
     (1, 2, 64, 1, 300, 1234, 320),

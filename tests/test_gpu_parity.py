@@ -301,7 +301,7 @@ def test_generate_bf16_two_rows_teacher_forced_against_oracle():
     tokens): every product of a decode step has one or two rows, so it runs the
     matrix-vector kernel (fp32 and residual-add outputs, SwiGLU with the interleaved
     per-row fast weights), and attention of the single query runs the decode kernel with
-    up to 3 blocks of window keys.  Replaying the GPU's tokens in the oracle: each GPU token's
+    up to 5 blocks of 128 window keys.  Replaying the GPU's tokens in the oracle: each GPU token's
     logit is within the bf16 tolerance of the oracle's maximum, ids agree wherever the
     oracle's top-2 margin is clear, and the update losses and fast weights match."""
     c = mkcfg(**dict(MID, window=640, batch=2))
