@@ -149,6 +149,29 @@ int ttt_generate(ttt_ctx* ctx, const int32_t* first_input, int32_t n_new, int32_
  * must equal 3 * d * f * n_fast. */
 int ttt_get_fast_weights(ttt_ctx* ctx, int32_t row, float* dst, int64_t n_floats);
 
+/* Per-session snapshot and resume (page "突破大语言模型上下文限制的新范式": a
+ * per-session parameter snapshot; resuming also needs the window and the position).
+ *
+ * ttt_set_fast_weights: host `src` (layout of ttt_get_fast_weights, n_floats = 3 * d
+ * * f * n_fast) becomes the fp32 fast weights of row `row`; its bf16 copies are
+ * refreshed.  Synchronous.  TTT_EINVAL on a bad row, size or NULL, TTT_ESTATE when
+ * poisoned.
+ *
+ * ttt_state_size: bytes of a whole-context snapshot: a header of 16 int64 (magic,
+ * version, batch, n_layers, n_heads, head dim, ring slots, element bytes, fast blocks,
+ * d_ff, d_model, position, 4 reserved), then the fp32 fast weights of every block
+ * ([n_fast][batch][3 d f]), then per layer its key/value ring arrays as stored on the
+ * device (K, V, V^T, and K^T where the layer keeps it).  -1 for a NULL context.
+ * ttt_save_state writes it to host `dst` (nbytes >= ttt_state_size; synchronous;
+ * TTT_ESTATE when poisoned).  ttt_load_state reads one back into a context of the same
+ * configuration (TTT_EINVAL when the header does not match or nbytes is short): fast
+ * weights, window, position; bf16 weight copies refreshed, poisoning and pending device
+ * work of ttt_prefill_device cleared.  The caller owns both buffers. */
+int ttt_set_fast_weights(ttt_ctx* ctx, int32_t row, const float* src, int64_t n_floats);
+int64_t ttt_state_size(const ttt_ctx* ctx);
+int ttt_save_state(ttt_ctx* ctx, void* dst, int64_t nbytes);
+int ttt_load_state(ttt_ctx* ctx, const void* src, int64_t nbytes);
+
 /* Fast weights back to their initial values, window cleared, pos = 0,
  * poisoning cleared. */
 int ttt_reset(ttt_ctx* ctx);

@@ -26,7 +26,8 @@ _NAMES = {-1: "TTT_EINVAL", -2: "TTT_ENOMEM", -3: "TTT_EDEVICE", -4: "TTT_ESTATE
 # every symbol include/ttt.h declares
 EXPORTS = ("ttt_set_allocator", "ttt_create", "ttt_prefill_chunk", "ttt_prefill", "ttt_prefill_device", "ttt_sync",
            "ttt_generate", "ttt_get_fast_weights", "ttt_reset", "ttt_position", "ttt_destroy", "ttt_last_error",
-           "ttt_profile_enable", "ttt_profile_read")
+           "ttt_profile_enable", "ttt_profile_read", "ttt_set_fast_weights", "ttt_state_size", "ttt_save_state",
+           "ttt_load_state")
 PROFILE_CLASSES = ("gemm_f32out", "gemm_bf16out", "gemm_resid", "gemm_swiglu", "gemm_swiglu_bwd", "gemm_sgd",
                    "gemm_splitk", "swa_fwd", "swa_fwd_split", "swa_bwd", "swa_decode")
 # kernels behind each class (rocprofv3 names); classes marked single=True are one kernel
@@ -103,6 +104,11 @@ def load_library():
     lib.ttt_position.restype = i64
     lib.ttt_destroy.argtypes = [vp]
     lib.ttt_destroy.restype = None
+    lib.ttt_set_fast_weights.argtypes = [vp, i32, vp, i64]
+    lib.ttt_state_size.argtypes = [vp]
+    lib.ttt_state_size.restype = i64
+    lib.ttt_save_state.argtypes = [vp, vp, i64]
+    lib.ttt_load_state.argtypes = [vp, vp, i64]
     lib.ttt_profile_enable.argtypes = [vp, i32]
     lib.ttt_profile_read.argtypes = [vp, i32, vp, vp, vp]
     lib.ttt_last_error.argtypes = [vp]
@@ -292,6 +298,22 @@ class TTTContext:
         out = np.zeros(n, dtype=np.float32)
         self._check(self._lib.ttt_get_fast_weights(self._h, row, out.ctypes.data, n))
         return out
+
+    def set_fast_weights_flat(self, row: int, flat) -> None:
+        """fp32 fast weights of `row` in the layout of fast_weights_flat."""
+        flat = np.ascontiguousarray(flat, dtype=np.float32)
+        self._check(self._lib.ttt_set_fast_weights(self._h, row, flat.ctypes.data, flat.size))
+
+    def save_state(self) -> np.ndarray:
+        """Snapshot of fast weights, window and position (bytes, see ttt_state_size)."""
+        n = int(self._lib.ttt_state_size(self._h))
+        buf = np.empty(n, dtype=np.uint8)
+        self._check(self._lib.ttt_save_state(self._h, buf.ctypes.data, n))
+        return buf
+
+    def load_state(self, blob) -> None:
+        blob = np.ascontiguousarray(blob, dtype=np.uint8)
+        self._check(self._lib.ttt_load_state(self._h, blob.ctypes.data, blob.size))
 
     def fast_weights(self, row: int = 0) -> list:
         """[(W_gate [f,d], W_up [f,d], W_down [d,f]) per fast block, ascending]"""

@@ -1019,6 +1019,48 @@ int build(ttt_ctx* c, const ttt_weights* w) {
   return TTT_OK;
 }
 
+// bf16 copies (row-major, transposed, interleaved gate/up) of every row's fp32 fast weights
+hipError_t refresh_fast_shadows(ttt_ctx* c) {
+  const int64_t fsz = 3LL * c->f * c->d;
+  for (int j = 0; j < c->Lq; ++j) {
+    FastW& fw = c->fw[j];
+    hipError_t e = refresh_shadows(fw.master, 2 * c->f, c->d, c->B, fsz, fw.wgu, 2LL * c->f * c->d, fw.wguT,
+                                   2LL * c->f * c->d, c->bf16, c->il ? c->f : 0, c->stream);
+    if (e != hipSuccess) return e;
+    e = refresh_shadows(fw.master + 2LL * c->f * c->d, c->d, c->f, c->B, fsz, fw.wd, (int64_t)c->d * c->f, fw.wdT,
+                        (int64_t)c->d * c->f, c->bf16, 0, c->stream);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+constexpr int64_t STATE_MAGIC = 0x5354544E49545454LL, STATE_VERSION = 1, STATE_HDR = 16;
+
+void state_header(const ttt_ctx* c, int64_t* h) {
+  const int64_t v[STATE_HDR] = {STATE_MAGIC, STATE_VERSION, c->B, c->L, c->H, c->hd, c->R, (int64_t)c->es, c->Lq, c->f,
+                                c->d, c->pos, 0, 0, 0, 0};
+  for (int i = 0; i < STATE_HDR; ++i) h[i] = v[i];
+}
+
+// the device arrays of a snapshot after the header, in order: fast weights, then each layer's rings
+template <typename F>
+hipError_t for_state_arrays(ttt_ctx* c, F&& f) {
+  const int64_t fsz = 3LL * c->f * c->d, ring = (int64_t)c->B * c->H * c->R * c->hd * c->es;
+  for (int j = 0; j < c->Lq; ++j) {
+    hipError_t e = f((void*)c->fw[j].master, fsz * c->B * 4);
+    if (e != hipSuccess) return e;
+  }
+  for (int l = 0; l < c->L; ++l) {
+    void* arr[4] = {c->lw[l].kr, c->lw[l].vr, c->lw[l].vtr, c->lw[l].ktr};
+    for (void* p : arr) {
+      if (!p) continue;
+      hipError_t e = f(p, ring);
+      if (e != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
+}
+
 int reset_state(ttt_ctx* c) {
   // (a failed call may have left a batched pass in flight on the batched stream)
   if (c->bstream) CK(hipStreamSynchronize(c->bstream));
@@ -1311,6 +1353,74 @@ int ttt_generate(ttt_ctx* c, const int32_t* first_input, int32_t n_new, int32_t 
   if (update_losses)
     for (int u = 0; u < nu; ++u)
       for (int r = 0; r < c->B; ++r) update_losses[(int64_t)r * nu + u] = tmp[(size_t)u * c->B + r];
+  return TTT_OK;
+}
+
+int ttt_set_fast_weights(ttt_ctx* c, int32_t row, const float* src, int64_t n_floats) {
+  if (!c) return TTT_EINVAL;
+  if (c->poisoned) return fail(c, TTT_ESTATE, "context poisoned; call ttt_reset");
+  if (!src || row < 0 || row >= c->B) return fail(c, TTT_EINVAL, "bad row or NULL src");
+  const int64_t fsz = 3LL * c->f * c->d;
+  if (n_floats != fsz * c->Lq) return fail(c, TTT_EINVAL, "n_floats must be 3*d*f*n_fast");
+  if (c->bstream) CK(hipStreamSynchronize(c->bstream));
+  for (int j = 0; j < c->Lq; ++j)
+    CK(hipMemcpyAsync(c->fw[j].master + row * fsz, src + j * fsz, fsz * 4, hipMemcpyHostToDevice, c->stream));
+  CK(refresh_fast_shadows(c));
+  CK(hipStreamSynchronize(c->stream));
+  return TTT_OK;
+}
+
+int64_t ttt_state_size(const ttt_ctx* c) {
+  if (!c) return -1;
+  int64_t n = STATE_HDR * 8;
+  (void)for_state_arrays(const_cast<ttt_ctx*>(c), [&](void*, int64_t bytes) {
+    n += bytes;
+    return hipSuccess;
+  });
+  return n;
+}
+
+int ttt_save_state(ttt_ctx* c, void* dst, int64_t nbytes) {
+  if (!c) return TTT_EINVAL;
+  if (c->poisoned) return fail(c, TTT_ESTATE, "context poisoned; call ttt_reset");
+  if (!dst || nbytes < ttt_state_size(c)) return fail(c, TTT_EINVAL, "NULL dst or nbytes below ttt_state_size");
+  if (c->bstream) CK(hipStreamSynchronize(c->bstream));
+  CK(hipStreamSynchronize(c->stream));
+  state_header(c, (int64_t*)dst);
+  char* p = (char*)dst + STATE_HDR * 8;
+  CK(for_state_arrays(c, [&](void* a, int64_t bytes) {
+    hipError_t e = hipMemcpy(p, a, bytes, hipMemcpyDeviceToHost);
+    p += bytes;
+    return e;
+  }));
+  return TTT_OK;
+}
+
+int ttt_load_state(ttt_ctx* c, const void* src, int64_t nbytes) {
+  if (!c) return TTT_EINVAL;
+  if (!src || nbytes < ttt_state_size(c)) return fail(c, TTT_EINVAL, "NULL src or nbytes below ttt_state_size");
+  int64_t want[STATE_HDR];
+  state_header(c, want);
+  const int64_t* got = (const int64_t*)src;
+  for (int i = 0; i < STATE_HDR; ++i)
+    if (i != 11 && got[i] != want[i]) return fail(c, TTT_EINVAL, "snapshot of another configuration");
+  if (got[11] < 0 || got[11] > c->cfg.max_positions) return fail(c, TTT_EINVAL, "snapshot position out of range");
+  if (c->bstream) CK(hipStreamSynchronize(c->bstream));
+  CK(hipStreamSynchronize(c->stream));
+  const char* p = (const char*)src + STATE_HDR * 8;
+  CK(for_state_arrays(c, [&](void* a, int64_t bytes) {
+    hipError_t e = hipMemcpy(a, p, bytes, hipMemcpyHostToDevice);
+    p += bytes;
+    return e;
+  }));
+  CK(refresh_fast_shadows(c));
+  CK(hipMemsetAsync(c->err_dev, 0, 4, c->stream));
+  CK(hipStreamSynchronize(c->stream));
+  c->pos = got[11];
+  c->pend_parts = 0;
+  c->poisoned = false;
+  c->pending_loss = nullptr;
+  c->pending_n = 0;
   return TTT_OK;
 }
 

@@ -332,6 +332,67 @@ def test_generate_bf16_two_rows_teacher_forced_against_oracle():
         compare_fast(ctx.fast_weights(r), o.get_fast(r), _w0(w, c), tw, f"decode bf16 row {r}")
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_set_fast_weights_against_oracle(dtype):
+    """Fast weights set from the host (per row, as a per-session snapshot would restore them):
+    the following chunks' losses and final fast weights match the oracle given the same
+    weights (toy shape, two rows with different snapshots)."""
+    c = mkcfg(**dict(TOY, dtype=dtype, batch=2, n_fast=2))
+    w = synth.weights(_shape(c), bf16=dtype == "bf16")
+    T = 256
+    seq = synth.tokens(2, T + 1, c.vocab, "uniform", seed=11)
+    print(f"case set fast weights {dtype}", flush=True)
+    ctx = _ctx(c, w, T + 8)
+    o = Oracle(c, w, T + 8)
+    rng = np.random.default_rng(5)
+    for r in range(2):
+        flat = ctx.fast_weights_flat(r).astype(np.float64)
+        flat = (flat + 0.02 * rng.standard_normal(flat.size)).astype(np.float32)
+        ctx.set_fast_weights_flat(r, flat)
+        o.set_fast_flat(r, flat.astype(np.float64))
+        assert np.array_equal(ctx.fast_weights_flat(r), flat)
+    got = ctx.prefill(seq[:, :T], seq[:, 1:])
+    ref = np.stack([o.prefill_chunk(seq[:, s:s + c.chunk], seq[:, s + 1:s + 1 + c.chunk])
+                    for s in range(0, T, c.chunk)], axis=1)
+    tl, tw = TOL[dtype]
+    rel = np.max(np.abs(got - ref) / np.abs(ref))
+    print(f"set fast weights {dtype}: max loss rel err {rel:.3e}")
+    assert rel <= tl
+    for r in range(2):
+        g, rf = ctx.fast_weights_flat(r), o.get_fast_flat(r)
+        assert np.max(np.abs(g - rf)) / np.max(np.abs(rf)) <= tw
+
+
+def test_save_and_load_state_resume_bit_exact():
+    """A snapshot taken after some chunks (fast weights, window, position) loaded into a fresh
+    context of the same configuration: the following chunks and a greedy generation give
+    bit-identical losses, tokens and fast weights to the context that was never interrupted;
+    a snapshot of another configuration is refused."""
+    from test_token_chunk_amd import TTTError
+    c = mkcfg(**dict(MID, batch=2))
+    w = synth.weights(_shape(c), bf16=True)
+    T1, T2 = 256, 256
+    seq = synth.tokens(2, T1 + T2 + 1, c.vocab, "zipf", seed=12)
+    print("case save/load state", flush=True)
+    a = _ctx(c, w, T1 + T2 + 80)
+    a.prefill(seq[:, :T1], seq[:, 1:T1 + 1])
+    blob = a.save_state()
+    la = a.prefill(seq[:, T1:T1 + T2], seq[:, T1 + 1:])
+    ta, _ = a.generate(seq[:, T1 + T2], 40, 20)
+    b = _ctx(c, w, T1 + T2 + 80)
+    b.load_state(blob)
+    assert b.position == T1
+    lb = b.prefill(seq[:, T1:T1 + T2], seq[:, T1 + 1:])
+    tb, _ = b.generate(seq[:, T1 + T2], 40, 20)
+    assert np.array_equal(la, lb)
+    assert np.array_equal(ta, tb)
+    for r in range(2):
+        assert np.array_equal(a.fast_weights_flat(r), b.fast_weights_flat(r))
+    other = _ctx(mkcfg(**dict(MID, batch=1)), w, T1 + T2 + 80)
+    with pytest.raises(TTTError):
+        other.load_state(blob)
+
+
 def test_context_held_in_a_module_global_exits_cleanly():
     """A context that is still open when the interpreter exits (held in a module global) is
     destroyed by the binding's exit handler while its allocator callbacks still work: the
