@@ -1297,9 +1297,10 @@ __global__ __launch_bounds__(256) void k_swa_decode(AttnArgs a, int S) {
   }
 }
 
-// merge of the S key-block parts of one (row, head): a block per (row, head) loads all parts
-// at once (thread t: parts t / (HD/8) + k * 256 / (HD/8), dims (t % (HD/8)) * 8 ..+8) and sums
-// them through LDS, so the many parts of a long window cost one round of loads
+// merge of the S key-block parts of one (row, head): a block per (row, head); thread t takes parts
+// t / (HD/8) + k * 256 / (HD/8) and dims (t % (HD/8)) * 8 ..+8, issues the loads of four parts at
+// once and merges them against its own running maximum, so a window of up to 64 parts costs one
+// round of loads; the threads' results are rescaled to the block maximum and summed through LDS
 template <int HD>
 __global__ __launch_bounds__(256) void k_swa_dec_combine(AttnArgs a, int S) {
   constexpr int DG = HD / 8, PS = 256 / DG;
@@ -1310,23 +1311,43 @@ __global__ __launch_bounds__(256) void k_swa_dec_combine(AttnArgs a, int S) {
   const float* pl = pm + (int64_t)S * plane;
   const int t = threadIdx.x, dg = t % DG, ps = t / DG;
   const float sl2 = 1.4426950408889634f / sqrtf((float)HD);
-  float mloc = -INFINITY;
-  for (int sp = t; sp < S; sp += 256) mloc = fmaxf(mloc, pm[sp * plane + bh]);
-  const float M = block_max(mloc, sh);
-  float o[8], l = 0.f;
+  float mt = -INFINITY, lt = 0.f, o[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) o[j] = 0.f;
-  for (int sp = ps; sp < S; sp += PS) {
-    const int64_t row = sp * plane + bh;
-    const float w = pm[row] == -INFINITY ? 0.f : exp2f((pm[row] - M) * sl2);
-    if (dg == 0) l += w * pl[row];
-    const float4 x0 = *(const float4*)(a.ws + row * HD + dg * 8), x1 = *(const float4*)(a.ws + row * HD + dg * 8 + 4);
-    o[0] += w * x0.x; o[1] += w * x0.y; o[2] += w * x0.z; o[3] += w * x0.w;
-    o[4] += w * x1.x; o[5] += w * x1.y; o[6] += w * x1.z; o[7] += w * x1.w;
-  }
+  for (int base = ps; base < S; base += 4 * PS) {
+    float pmv[4], plv[4];
+    float4 xa[4], xb[4];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) red[ps][dg * 8 + j] = o[j];
-  const float L = block_sum(l, sh);  // (its barriers also order the LDS writes above)
+    for (int u = 0; u < 4; ++u) {
+      const int sp = base + u * PS;
+      const int64_t row = (int64_t)(sp < S ? sp : 0) * plane + bh;
+      pmv[u] = sp < S ? pm[row] : -INFINITY;
+      plv[u] = pl[row];
+      xa[u] = *(const float4*)(a.ws + row * HD + dg * 8);
+      xb[u] = *(const float4*)(a.ws + row * HD + dg * 8 + 4);
+    }
+    float mn = mt;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) mn = fmaxf(mn, pmv[u]);
+    if (mn == -INFINITY) continue;
+    const float sc = mt == -INFINITY ? 0.f : exp2f((mt - mn) * sl2);
+    lt *= sc;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) o[j] *= sc;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float w = pmv[u] == -INFINITY ? 0.f : exp2f((pmv[u] - mn) * sl2);
+      lt += w * plv[u];
+      o[0] += w * xa[u].x; o[1] += w * xa[u].y; o[2] += w * xa[u].z; o[3] += w * xa[u].w;
+      o[4] += w * xb[u].x; o[5] += w * xb[u].y; o[6] += w * xb[u].z; o[7] += w * xb[u].w;
+    }
+    mt = mn;
+  }
+  const float M = block_max(mt, sh);
+  const float f = mt == -INFINITY ? 0.f : exp2f((mt - M) * sl2);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) red[ps][dg * 8 + j] = o[j] * f;
+  const float L = block_sum(dg == 0 ? lt * f : 0.f, sh);  // (its barriers also order the LDS writes above)
   if (t >= HD) return;
   float O = 0.f;
 #pragma unroll
