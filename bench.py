@@ -58,8 +58,27 @@ def flops_per_row(c: dict, T: int) -> dict:
     return out
 
 
+def host_cpu() -> tuple:
+    """(CPU model from lscpu, CPUs this process may run on)."""
+    import subprocess
+    model = "unknown"
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except (OSError, subprocess.SubprocessError):
+        pass
+    return model, len(os.sched_getaffinity(0))
+
+
 def cpu_baseline(c: dict, w: dict, seq: np.ndarray, sample_tokens: int) -> dict:
-    """The fp64 oracle on the first `sample_tokens` positions (one chunk) of the same workload."""
+    """The fp64 oracle on the first `sample_tokens` positions (one chunk) of the same workload.
+
+    At position 0 a query sees at most `sample_tokens` keys instead of the window's k, so the
+    measured rate flatters the oracle; the steady-state figure scales it by the FLOPs of a token
+    with a full window over the FLOPs of the sample's tokens (labelled as extrapolated)."""
     from types import SimpleNamespace
 
     from oracle import Oracle
@@ -70,11 +89,22 @@ def cpu_baseline(c: dict, w: dict, seq: np.ndarray, sample_tokens: int) -> dict:
     t0 = time.perf_counter()
     o.prefill_chunk(seq[:1, :n], seq[:1, 1:n + 1])
     dt = time.perf_counter() - t0
-    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    model, nproc = host_cpu()
+    threads = int(os.environ.get("OMP_NUM_THREADS", nproc))
     o.close()
-    return {"value": n / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"first {n} positions of the sequence as one inner-loop step (forward, backward, SGD), "
-                      f"fp64, {dt:.1f} s"}
+    sample_flops = flops_per_row(dict(c, chunk=n), n)["total"]
+    k, b = c["window"], c["chunk"]
+    steady = flops_per_row(c, k + b)
+    steady_tok = (steady["total"] - flops_per_row(c, k)["total"]) / b  # FLOPs of one chunk past the window fill
+    rate = sample_flops / dt
+    return {"value": n / dt, "unit": "tokens/s", "cores": min(threads, nproc), "kind": "oracle",
+            "cpu_model": model, "nproc": nproc,
+            "sample": f"positions 0..{n - 1} of the sequence as one inner-loop step (forward, backward, SGD), "
+                      f"fp64, {dt:.1f} s; at position 0 each query sees <= {n} keys, not the window's {k}",
+            "fp64_gflops": round(rate / 1e9, 2),
+            "steady_state_extrapolated": {"value": round(rate / steady_tok, 4), "unit": "tokens/s",
+                                          "basis": "the sample's fp64 FLOP rate applied to the FLOPs of a token "
+                                                   f"with a full {k}-key window (extrapolated, not measured)"}}
 
 
 def measured_traffic(kernel: str, config: str):
@@ -101,6 +131,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--config", default="3b", choices=sorted(CONFIGS))
     ap.add_argument("--tokens", type=int, default=0, help="override T (tokens per row)")
+    ap.add_argument("--window", type=int, default=0, help="override the attention window k (keys per query)")
     ap.add_argument("--cpu-sample", type=int, default=32, help="oracle sample size in tokens (0 = skip)")
     ap.add_argument("--lookahead", type=int, default=0, help="chunks per batched lower-block pass (0 = library default)")
     ap.add_argument("--workload", default="prefill", choices=("prefill", "decode"),
@@ -133,6 +164,8 @@ def main():
     T = args.tokens or c.pop("T")
     c.pop("T", None)
     dist = c.pop("dist")
+    if args.window:
+        c["window"] = args.window
     torch.cuda.set_device(0)
     t_setup = time.perf_counter()
     w = synth.weights(synth.Shape(c["n_layers"], c["d_model"], c["n_heads"], c["d_ff"], c["vocab"]),
@@ -158,13 +191,12 @@ def main():
         step()
         print(f"warmup step {i}: {time.perf_counter() - t0:.3f} s", file=sys.stderr, flush=True)
     # per-class device time of one untimed step (HIP events around every GEMM / attention launch);
-    # it picks the roofline kernel: the one-kernel class with the most device time
+    # it picks the roofline kernel: the class with the most device time in the step
     from test_token_chunk_amd import PROFILE_KERNELS
     ctx.profile_begin()
     step()
     kstats = ctx.profile_end()
-    single = {k: v for k, v in kstats.items() if PROFILE_KERNELS.get(k, ("", False))[1]}
-    roof_cls = max(single.items(), key=lambda kv: kv[1]["ms"])[0] if single else None
+    roof_cls = max(kstats.items(), key=lambda kv: kv[1]["ms"])[0] if kstats else None
 
     # timed region: only the roofline kernel's launches carry events
     ctx.profile_begin([roof_cls] if roof_cls else [])
@@ -182,19 +214,28 @@ def main():
     F = flops_per_row(c, T)
     peak = PEAK_BF16 if c["dtype"] == "bf16" else PEAK_F32
 
-    # roofline of the dominant single kernel, from its launches inside the timed region
+    # roofline of the class with the most device time, from its launches inside the timed region:
+    # achieved = its algorithmic FLOPs (summed over the shapes it runs) / its summed duration
+    hd = c["d_model"] // c["n_heads"]
     roof = None
     if roof_cls and roof_cls in rstats:
         name, st = roof_cls, rstats[roof_cls]
         flops_per_launch = st["flops"] / max(st["count"], 1)
         avg_s = st["ms"] / max(st["count"], 1) / 1e3
         achieved = flops_per_launch / avg_s / 1e12
-        kname = PROFILE_KERNELS[name][0].replace("hd", str(c["d_model"] // c["n_heads"]))
+        kname = PROFILE_KERNELS[name][0].replace("hd", str(hd))
         roof = {"kernel": kname, "class": name, "bound": "mfma", "achieved": round(achieved, 1),
                 "peak": peak / 1e12, "unit": "TFLOP/s", "frac": round(achieved / (peak / 1e12), 4),
                 "traffic": measured_traffic(kname, args.config),
                 "avg_launch_us": round(avg_s * 1e6, 2), "launches_per_step": st["count"] // args.steps,
-                "gflop_per_launch": round(flops_per_launch / 1e9, 3)}
+                "gflop_per_launch": round(flops_per_launch / 1e9, 3),
+                "share_of_device_time": round(kstats[name]["ms"] / sum(v["ms"] for v in kstats.values()), 4)}
+    total_dev = sum(v["ms"] for v in kstats.values())
+    top = sorted(kstats.items(), key=lambda kv: -kv[1]["ms"])[:6]
+    kernel_top = [{"class": k, "kernels": PROFILE_KERNELS[k][0].replace("hd", str(hd)),
+                   "ms_per_step": round(v["ms"], 2), "share": round(v["ms"] / total_dev, 4),
+                   "tflops": round(v["flops"] / max(v["ms"], 1e-9) / 1e9, 1),
+                   "frac": round(v["flops"] / max(v["ms"], 1e-9) / 1e9 / (peak / 1e12), 4)} for k, v in top]
     out = {
         "metric": "TTT prefill tokens/s (fwd+inner-loop bwd+update) and % bf16 MFMA peak",
         "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -206,8 +247,10 @@ def main():
         "flops_per_step": F["total"], "mfma_peak_frac": round(F["total"] / (ms / 1e3) / peak, 4),
         "final_chunk_loss": float(losses[-1]), "first_chunk_loss": float(losses[0]),
         "roofline": roof,
+        "kernel_top": kernel_top,
         "kernel_classes": {k: {"ms_per_step": round(v["ms"], 3), "tflops": round(
             v["flops"] / max(v["ms"], 1e-9) / 1e9, 1)} for k, v in kstats.items()},
+        "device_ms_per_step_all_streams": round(total_dev, 1),
     }
     if args.cpu_sample > 0:
         out["cpu_baseline"] = cpu_baseline(c, w, seq, args.cpu_sample)
@@ -227,6 +270,8 @@ def decode_bench(args):
     c = dict(CONFIGS[args.config])
     c.pop("T")
     dist = c.pop("dist")
+    if args.window:
+        c["window"] = args.window
     n_new, b, k = args.decode_tokens, c["chunk"], c["window"]
     P = k + b
     upd = min(b, n_new)

@@ -97,10 +97,18 @@ typedef void* (*ttt_alloc_fn)(size_t bytes, void* user);
 typedef void (*ttt_free_fn)(void* ptr, void* user);
 int ttt_set_allocator(ttt_alloc_fn alloc, ttt_free_fn free_fn, void* user);
 
-/* Create a context on the current HIP device.  `hip_stream` (hipStream_t,
- * may be NULL for the null stream) is the stream every call enqueues on.
- * Fast weights start as copies of the given MLP weights of the last n_fast
- * blocks; the key/value window is empty and the position is 0. */
+/* Create a context on the current HIP device (page "TTT-E2E 如何让大模型边用
+ * 边学", §9: a model is made from a checkpoint together with the window size
+ * and the inner batch b; here the checkpoint is the host weight arrays `w`
+ * and window / chunk are fields of `cfg`).  `hip_stream` (hipStream_t, may be
+ * NULL for the null stream) is the stream every call enqueues on.  Fast
+ * weights start as copies of the given MLP weights of the last n_fast blocks;
+ * the key/value window is empty and the position is 0.
+ * Errors: TTT_EINVAL for a NULL argument or an invalid configuration (k < b,
+ * d % H, head_dim odd or > 128, n_fast out of range, non-finite lr ...),
+ * TTT_ENODEV without a gfx950 device, TTT_ENOMEM when the allocator (or the
+ * installed hook) returns NULL, TTT_EDEVICE for other HIP failures.  On error
+ * *out is NULL, nothing stays allocated and ttt_last_error(NULL) says why. */
 int ttt_create(const ttt_config* cfg, const ttt_weights* w, void* hip_stream, ttt_ctx** out);
 
 /* One inner-loop step for every row on n (1..chunk) new tokens (page "TTT-E2E
@@ -128,8 +136,24 @@ int ttt_prefill_device(ttt_ctx* ctx, const int32_t* d_tokens, const int32_t* d_t
                        float* d_losses);
 
 /* Wait for the context's stream; report device-side errors (bad ids,
- * non-finite losses of ttt_prefill_device work). */
+ * non-finite losses of ttt_prefill_device / ttt_score_device work). */
 int ttt_sync(ttt_ctx* ctx);
+
+/* Forward and loss only: the chunk losses that ttt_prefill would report for
+ * the same tokens, without the backward pass and without any update (the fast
+ * weights stay as they are), so the chunks are independent and every block
+ * runs as one batch over up to `lookahead` chunks.  The window's keys/values
+ * are written and pos advances, exactly as in ttt_prefill.  With window >=
+ * the number of positions this is the plain causal transformer, i.e. the
+ * full-attention model that page "TTT-E2E 如何让大模型边用边学" §5.1 compares
+ * TTT-E2E's latency with; it also scores a text under frozen weights.
+ * ttt_score: host arrays and losses as ttt_prefill (synchronous).
+ * ttt_score_device: device arrays as ttt_prefill_device (asynchronous; errors
+ * and non-finite losses reported by ttt_sync).  Argument errors and poisoning
+ * as for ttt_prefill. */
+int ttt_score(ttt_ctx* ctx, const int32_t* tokens, const int32_t* targets, int64_t n_tokens, float* losses);
+int ttt_score_device(ttt_ctx* ctx, const int32_t* d_tokens, const int32_t* d_targets, int64_t n_tokens,
+                     float* d_losses);
 
 /* Greedy generation with test-time training (page "突破大语言模型上下文限制
  * 的新范式", §2.2: an update after every block of generated tokens).  Step j
@@ -146,7 +170,12 @@ int ttt_generate(ttt_ctx* ctx, const int32_t* first_input, int32_t n_new, int32_
 
 /* Copy the fp32 fast weights of row `row` to host `dst`: for each fast block
  * in ascending order, W_gate [f, d], W_up [f, d], W_down [d, f].  n_floats
- * must equal 3 * d * f * n_fast. */
+ * must equal 3 * d * f * n_fast.  These are the parameters the inner loop
+ * changes (page "TTT-E2E 如何让大模型边用边学", §4.2: only the MLPs of the last
+ * quarter of the blocks), i.e. the per-session parameter snapshot of page
+ * "突破大语言模型上下文限制的新范式", §5.1.  Waits for the context's stream;
+ * works on a poisoned context (it returns what the device holds).  TTT_EINVAL
+ * for a bad row, a NULL dst or a size mismatch. */
 int ttt_get_fast_weights(ttt_ctx* ctx, int32_t row, float* dst, int64_t n_floats);
 
 /* Per-session snapshot and resume (page "突破大语言模型上下文限制的新范式": a
@@ -159,11 +188,12 @@ int ttt_get_fast_weights(ttt_ctx* ctx, int32_t row, float* dst, int64_t n_floats
  *
  * ttt_state_size: bytes of a whole-context snapshot: a header of 16 int64 (magic,
  * version, batch, n_layers, n_heads, head dim, ring slots, element bytes, fast blocks,
- * d_ff, d_model, position, 4 reserved), then the fp32 fast weights of every block
+ * d_ff, d_model, position, window, chunk, vocab, bit pattern of rope_theta), then the fp32 fast weights of every block
  * ([n_fast][batch][3 d f]), then per layer its key/value ring arrays as stored on the
  * device (K, V, V^T, and K^T where the layer keeps it).  -1 for a NULL context.
  * ttt_save_state writes it to host `dst` (nbytes >= ttt_state_size; synchronous;
- * TTT_ESTATE when poisoned).  ttt_load_state reads one back into a context of the same
+ * TTT_ESTATE when poisoned; a device-side error of earlier ttt_prefill_device work is
+ * reported as ttt_sync would, and poisons, before anything is written).  ttt_load_state reads one back into a context of the same
  * configuration (TTT_EINVAL when the header does not match or nbytes is short): fast
  * weights, window, position; bf16 weight copies refreshed, poisoning and pending device
  * work of ttt_prefill_device cleared.  The caller owns both buffers. */
@@ -172,8 +202,9 @@ int64_t ttt_state_size(const ttt_ctx* ctx);
 int ttt_save_state(ttt_ctx* ctx, void* dst, int64_t nbytes);
 int ttt_load_state(ttt_ctx* ctx, const void* src, int64_t nbytes);
 
-/* Fast weights back to their initial values, window cleared, pos = 0,
- * poisoning cleared. */
+/* Start a new text (page "TTT-E2E 如何让大模型边用边学", §4.2: every new text
+ * starts from the trained initial weights): fast weights back to their initial
+ * values, window cleared, pos = 0, poisoning cleared.  Synchronous. */
 int ttt_reset(ttt_ctx* ctx);
 
 /* Current absolute position of every row (rows advance together). */

@@ -27,7 +27,7 @@ _NAMES = {-1: "TTT_EINVAL", -2: "TTT_ENOMEM", -3: "TTT_EDEVICE", -4: "TTT_ESTATE
 EXPORTS = ("ttt_set_allocator", "ttt_create", "ttt_prefill_chunk", "ttt_prefill", "ttt_prefill_device", "ttt_sync",
            "ttt_generate", "ttt_get_fast_weights", "ttt_reset", "ttt_position", "ttt_destroy", "ttt_last_error",
            "ttt_profile_enable", "ttt_profile_read", "ttt_set_fast_weights", "ttt_state_size", "ttt_save_state",
-           "ttt_load_state")
+           "ttt_load_state", "ttt_score", "ttt_score_device")
 PROFILE_CLASSES = ("gemm_f32out", "gemm_bf16out", "gemm_resid", "gemm_swiglu", "gemm_swiglu_bwd", "gemm_sgd",
                    "gemm_splitk", "swa_fwd", "swa_fwd_split", "swa_bwd", "swa_decode")
 # kernels behind each class (rocprofv3 names); classes marked single=True are one kernel
@@ -96,6 +96,8 @@ def load_library():
     lib.ttt_prefill_chunk.argtypes = [vp, vp, vp, i32, vp]
     lib.ttt_prefill.argtypes = [vp, vp, vp, i64, vp]
     lib.ttt_prefill_device.argtypes = [vp, vp, vp, i64, vp]
+    lib.ttt_score.argtypes = [vp, vp, vp, i64, vp]
+    lib.ttt_score_device.argtypes = [vp, vp, vp, i64, vp]
     lib.ttt_sync.argtypes = [vp]
     lib.ttt_generate.argtypes = [vp, vp, i32, i32, vp, vp]
     lib.ttt_get_fast_weights.argtypes = [vp, i32, vp, i64]
@@ -279,6 +281,23 @@ class TTTContext:
                                                  ctypes.c_void_p(d_targets.data_ptr()), n,
                                                  ctypes.c_void_p(d_losses.data_ptr()) if d_losses is not None
                                                  else None))
+
+    def score(self, tokens, targets) -> np.ndarray:
+        """Forward and loss only (no update): host arrays [B, n_tokens]; losses [B, n_chunks]."""
+        tokens, targets = _i32(tokens), _i32(targets)
+        B, n = tokens.shape
+        nch = (n + self.cfg.chunk - 1) // self.cfg.chunk
+        losses = np.zeros((B, nch), dtype=np.float32)
+        self._check(self._lib.ttt_score(self._h, tokens.ctypes.data, targets.ctypes.data, n, losses.ctypes.data))
+        return losses
+
+    def score_device(self, d_tokens, d_targets, d_losses=None):
+        """As prefill_device, forward and loss only (no update). Async."""
+        n = d_tokens.shape[1]
+        self._check(self._lib.ttt_score_device(self._h, ctypes.c_void_p(d_tokens.data_ptr()),
+                                               ctypes.c_void_p(d_targets.data_ptr()), n,
+                                               ctypes.c_void_p(d_losses.data_ptr()) if d_losses is not None
+                                               else None))
 
     def sync(self):
         self._check(self._lib.ttt_sync(self._h))

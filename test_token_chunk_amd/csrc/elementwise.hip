@@ -341,6 +341,7 @@ __global__ void k_ce_rows(const float* logits, int V, const int32_t* tgt, int64_
   int nv = nvalid[b];
   float inv = nv > 0 ? 1.f / (float)nv : 0.f;
   if (threadIdx.x == 0) loss_tok[m] = (y >= 0) ? lse - z[y] : 0.f;
+  if (!dlogits) return;  // loss only (scoring without an update)
   T* dz = dlogits + m * V;
   for (int v = threadIdx.x; v < V; v += blockDim.x) {
     float p = (y >= 0) ? (expf(z[v] - lse) - (v == y ? 1.f : 0.f)) * inv : 0.f;
@@ -379,6 +380,7 @@ __global__ __launch_bounds__(512) void k_ce_rows4(const float* logits, int V, co
   const int nv = nvalid[b];
   const float inv = nv > 0 ? 1.f / (float)nv : 0.f;
   if (threadIdx.x == 0) loss_tok[m] = (y >= 0) ? lse - logits[m * V + y] : 0.f;
+  if (!dlogits) return;  // loss only (scoring without an update)
   T* dz = dlogits + m * V;
   for (int v = threadIdx.x; v < V4; v += blockDim.x) {
     const float4 z = z4[v];

@@ -756,6 +756,49 @@ int run_tokens(ttt_ctx* c, const int32_t* tok, const int32_t* tgt, int64_t ld, i
   return TTT_OK;
 }
 
+// Forward and loss only over n_tokens tokens per row from c->pos (no backward, no update):
+// while nothing changes the fast weights every block is frozen, so all L blocks run over
+// groups of up to G chunks at once; then final norm, lm_head and the cross-entropy of each
+// chunk (the loss a prefill of the same chunk would report).  The window's keys and values
+// are written as by a prefill.
+template <typename T>
+int run_score(ttt_ctx* c, const int32_t* tok, const int32_t* tgt, int64_t ld, int64_t n_tokens, float* loss_dev) {
+  const int B = c->B, d = c->d, V = c->V, b = c->b;
+  const int64_t gmax = (int64_t)c->G * b;
+  int64_t done = 0, ci = 0;
+  while (done < n_tokens) {
+    const int g = (int)std::min<int64_t>(n_tokens - done, gmax);
+    CK(embed_gather_ld<T>(tok + done, ld, B, g, tp<T>(c->embed), d, V, c->hb, c->err_dev, c->stream));
+    for (int l = 0; l < c->L; ++l) {
+      int rc = layer_fwd<T>(c, l, c->hb, g, c->pos + done, FULL, nullptr);
+      if (rc) return rc;
+    }
+    // final norm of the whole group into ub ([B][g][d]); sums K-split parts still pending
+    CK(norm_fwd<T>(c, c->hb, (int64_t)B * g, c->final_norm, tp<T>(c->ub), c->rstd_tmp, (T*)nullptr, g, 0, nullptr));
+    for (int cs = 0; cs < g; cs += b) {
+      const int n = std::min(b, g - cs);
+      GemmArgs gl = mk(tp<T>(c->ub, (int64_t)cs * d), d, c->lm_head, d, n, V, d);
+      gl.batch = B;
+      gl.sA = (int64_t)g * d;
+      gl.sB = 0;
+      gl.e.kind = EPI_F32;
+      gl.e.c = c->logits;
+      gl.e.ldc = V;
+      gl.e.sc = (int64_t)n * V;
+      CK(Ops<T>::gemm(c, gl));
+      const int32_t* t0 = tgt + done + cs;
+      CK(count_valid_ld(t0, ld, B, n, c->nvalid, c->stream));
+      CK(ce_rows_ld<T>(c->logits, (int64_t)B * n, V, t0, ld, c->nvalid, n, c->loss_tok, (T*)nullptr, c->err_dev,
+                       c->stream));
+      CK(reduce_loss(c->loss_tok, c->nvalid, B, n, loss_dev + ci * B, c->stream));
+      ++ci;
+    }
+    done += g;
+  }
+  c->pos += n_tokens;
+  return TTT_OK;
+}
+
 // one greedy decode step: input tok[r*ld], output arg-max to tok[r*ld + 1]
 template <typename T>
 int decode_step(ttt_ctx* c, int32_t* tok, int64_t ld) {
@@ -823,6 +866,10 @@ int sync_and_check(ttt_ctx* c, const float* dloss, int64_t nloss, float* host_co
 
 int run_dispatch(ttt_ctx* c, const int32_t* tok, const int32_t* tgt, int64_t ld, int64_t n, float* loss_dev) {
   return c->bf16 ? run_tokens<bf16>(c, tok, tgt, ld, n, loss_dev) : run_tokens<float>(c, tok, tgt, ld, n, loss_dev);
+}
+
+int score_dispatch(ttt_ctx* c, const int32_t* tok, const int32_t* tgt, int64_t ld, int64_t n, float* loss_dev) {
+  return c->bf16 ? run_score<bf16>(c, tok, tgt, ld, n, loss_dev) : run_score<float>(c, tok, tgt, ld, n, loss_dev);
 }
 
 int decode_dispatch(ttt_ctx* c, int32_t* tok, int64_t ld) {
@@ -1034,11 +1081,16 @@ hipError_t refresh_fast_shadows(ttt_ctx* c) {
   return hipSuccess;
 }
 
-constexpr int64_t STATE_MAGIC = 0x5354544E49545454LL, STATE_VERSION = 1, STATE_HDR = 16;
+constexpr int64_t STATE_MAGIC = 0x5354544E49545454LL, STATE_VERSION = 2, STATE_HDR = 16;
 
+// Everything a snapshot's contents depend on: the ring keys are stored RoPE-rotated at their
+// absolute positions (theta) in slots pos mod R, so window, chunk and theta must match as well
+// as the array sizes; slot 11 is the position.
 void state_header(const ttt_ctx* c, int64_t* h) {
+  int64_t theta_bits = 0;
+  memcpy(&theta_bits, &c->cfg.rope_theta, 8);
   const int64_t v[STATE_HDR] = {STATE_MAGIC, STATE_VERSION, c->B, c->L, c->H, c->hd, c->R, (int64_t)c->es, c->Lq, c->f,
-                                c->d, c->pos, 0, 0, 0, 0};
+                                c->d, c->pos, c->k, c->b, c->V, theta_bits};
   for (int i = 0; i < STATE_HDR; ++i) h[i] = v[i];
 }
 
@@ -1282,6 +1334,56 @@ int ttt_prefill(ttt_ctx* c, const int32_t* tokens, const int32_t* targets, int64
   return TTT_OK;
 }
 
+int ttt_score(ttt_ctx* c, const int32_t* tokens, const int32_t* targets, int64_t n_tokens, float* losses) {
+  if (!c) return TTT_EINVAL;
+  if (c->poisoned) return fail(c, TTT_ESTATE, "context poisoned; call ttt_reset");
+  if (!tokens || !targets || n_tokens <= 0) return fail(c, TTT_EINVAL, "NULL tokens/targets or n_tokens <= 0");
+  if (c->pos + n_tokens > c->cfg.max_positions) return fail(c, TTT_EINVAL, "beyond max_positions");
+  const int64_t cnt = (int64_t)c->B * n_tokens;
+  if (!check_ids(c, tokens, cnt, false)) return fail(c, TTT_EINVAL, "token id out of range");
+  if (!check_ids(c, targets, cnt, true)) return fail(c, TTT_EINVAL, "target id out of range");
+  const int64_t nch = (n_tokens + c->b - 1) / c->b;
+  int rc;
+  if ((rc = ensure_tok(c, 2 * cnt))) return rc;
+  if ((rc = ensure_loss(c, nch * c->B))) return rc;
+  if (c->bstream) CK(hipStreamSynchronize(c->bstream));
+  CK(hipMemcpyAsync(c->d_tok, tokens, cnt * 4, hipMemcpyHostToDevice, c->stream));
+  CK(hipMemcpyAsync(c->d_tok + cnt, targets, cnt * 4, hipMemcpyHostToDevice, c->stream));
+  rc = score_dispatch(c, c->d_tok, c->d_tok + cnt, n_tokens, n_tokens, c->d_loss);
+  if (rc) return rc;
+  std::vector<float> tmp(nch * c->B);
+  rc = sync_and_check(c, c->d_loss, nch * c->B, tmp.data());
+  if (rc) return rc;
+  if (losses)
+    for (int64_t ch = 0; ch < nch; ++ch)
+      for (int r = 0; r < c->B; ++r) losses[(int64_t)r * nch + ch] = tmp[ch * c->B + r];
+  return TTT_OK;
+}
+
+int ttt_score_device(ttt_ctx* c, const int32_t* d_tokens, const int32_t* d_targets, int64_t n_tokens,
+                     float* d_losses) {
+  if (!c) return TTT_EINVAL;
+  if (c->poisoned) return fail(c, TTT_ESTATE, "context poisoned; call ttt_reset");
+  if (!d_tokens || !d_targets || n_tokens <= 0) return fail(c, TTT_EINVAL, "NULL tokens/targets or n_tokens <= 0");
+  if (c->pos + n_tokens > c->cfg.max_positions) return fail(c, TTT_EINVAL, "beyond max_positions");
+  const int64_t nch = (n_tokens + c->b - 1) / c->b;
+  if (!d_losses) {
+    int rc = ensure_loss(c, nch * c->B);
+    if (rc) return rc;
+    d_losses = c->d_loss;
+  }
+  // (a batched pass of an earlier prefill may still be writing the shared buffers)
+  if (c->bstream) {
+    CK(hipEventRecord(c->ev_c2b, c->bstream));
+    CK(hipStreamWaitEvent(c->stream, c->ev_c2b, 0));
+  }
+  int rc = score_dispatch(c, d_tokens, d_targets, n_tokens, n_tokens, d_losses);
+  if (rc) return rc;
+  c->pending_loss = d_losses;
+  c->pending_n = nch * c->B;
+  return TTT_OK;
+}
+
 int ttt_prefill_chunk(ttt_ctx* c, const int32_t* tokens, const int32_t* targets, int32_t n, float* loss_out) {
   if (!c) return TTT_EINVAL;
   if (n <= 0 || n > c->b) return fail(c, TTT_EINVAL, "n must be in 1..chunk");
@@ -1385,7 +1487,14 @@ int ttt_save_state(ttt_ctx* c, void* dst, int64_t nbytes) {
   if (c->poisoned) return fail(c, TTT_ESTATE, "context poisoned; call ttt_reset");
   if (!dst || nbytes < ttt_state_size(c)) return fail(c, TTT_EINVAL, "NULL dst or nbytes below ttt_state_size");
   if (c->bstream) CK(hipStreamSynchronize(c->bstream));
-  CK(hipStreamSynchronize(c->stream));
+  // device-side errors of earlier asynchronous work (a bad id, a non-finite loss) poison the
+  // context here instead of travelling inside the snapshot
+  {
+    int rc = sync_and_check(c, c->pending_loss, c->pending_n, nullptr);
+    c->pending_loss = nullptr;
+    c->pending_n = 0;
+    if (rc) return rc;
+  }
   state_header(c, (int64_t*)dst);
   char* p = (char*)dst + STATE_HDR * 8;
   CK(for_state_arrays(c, [&](void* a, int64_t bytes) {

@@ -126,7 +126,8 @@ template <typename T>
 hipError_t convert_rows(const float* x, int64_t M, int d, T* y, T* yT, int rows_per_batch, int64_t ldT,
                         hipStream_t s);
 hipError_t count_valid_ld(const int32_t* tgt, int64_t ld, int B, int n, int* nvalid, hipStream_t s);
-// cross-entropy of full logit rows: loss_tok[m] and dlogits = (softmax - onehot) / nvalid (T)
+// cross-entropy of full logit rows: loss_tok[m] and dlogits = (softmax - onehot) / nvalid (T;
+// dlogits == nullptr: the losses only)
 template <typename T>
 hipError_t ce_rows_ld(const float* logits, int64_t M, int V, const int32_t* tgt, int64_t ld, const int* nvalid,
                       int rows_per_batch, float* loss_tok, T* dlogits, int* err, hipStream_t s);

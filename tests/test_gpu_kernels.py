@@ -89,6 +89,10 @@ ATTN_CASES = [
     (2, 3, 128, 1, 2048, 5000, 2100),
     (1, 2, 64, 1, 300, 1234, 320),
     (1, 4, 128, 1, 8192, 20000, 9216),
+    # more window blocks than one round of the merge holds (64 parts at head dim 128, 128 at
+    # 64), so the running maximum is rescaled across rounds: windows of 32768 and 20000 keys
+    (1, 2, 128, 1, 32768, 40000, 33024),
+    (1, 2, 64, 1, 20000, 30000, 20480),
 ]
 
 

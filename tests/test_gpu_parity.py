@@ -416,3 +416,65 @@ def test_context_held_in_a_module_global_exits_cleanly():
     print(r.stdout[-500:], r.stderr[-1500:])
     assert "prefill ok" in r.stdout
     assert r.returncode == 0
+
+
+def _oracle_losses(c, w, seq, tg, T):
+    o = Oracle(c, w, T + 8)
+    out = [o.prefill_chunk(seq[:, s:min(T, s + c.chunk)], tg[:, s:min(T, s + c.chunk)]) for s in range(0, T, c.chunk)]
+    return o, np.stack(out, axis=1)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_score_equals_oracle_without_update(dtype):
+    """Forward and loss only (ttt_score): the toy workload against the oracle with lr = 0 (whose
+    chunk losses are then exactly the forward losses), ring wrapping; the fast weights stay
+    bit for bit what they were."""
+    c = mkcfg(**dict(TOY, dtype=dtype, n_fast=2))
+    w = synth.weights(_shape(c), bf16=dtype == "bf16")
+    T = 1000
+    seq = synth.tokens(1, T + 1, c.vocab, "uniform", seed=12)
+    _, ref = _oracle_losses(mkcfg(**dict(vars(c), lr=0.0)), w, seq, seq[:, 1:], T)
+    ctx = _ctx(c, w, T + 8)
+    before = ctx.fast_weights_flat(0).copy()
+    got = ctx.score(seq[:, :T], seq[:, 1:])
+    rel = np.max(np.abs(got - ref) / np.abs(ref))
+    print(f"score toy {dtype}: max loss rel err {rel:.3e}")
+    assert rel <= TOL[dtype][0]
+    assert np.array_equal(ctx.fast_weights_flat(0), before)
+    assert ctx.position == T
+
+
+def test_score_full_attention_two_rows_bf16():
+    """Window >= T (full causal attention, the comparator of the TTT-E2E latency claim) on the
+    bf16 matrix-core path with two rows, a ragged last chunk and masked targets: every chunk
+    loss against the oracle with lr = 0."""
+    c = mkcfg(**dict(MID, batch=2, window=1024))
+    w = synth.weights(_shape(c), bf16=True)
+    T = 700
+    seq = synth.tokens(2, T + 1, c.vocab, "zipf", seed=13)
+    tg = seq[:, 1:].copy()
+    tg[:, ::5] = -1
+    _, ref = _oracle_losses(mkcfg(**dict(vars(c), lr=0.0)), w, seq, tg, T)
+    ctx = _ctx(c, w, T + 8)
+    got = ctx.score(seq[:, :T], tg)
+    rel = np.max(np.abs(got - ref) / np.abs(ref))
+    print(f"score full attention bf16: max loss rel err {rel:.3e}")
+    assert rel <= TOL["bf16"][0]
+
+
+def test_score_after_prefill_is_the_pre_update_loss():
+    """After a prefill of 4 chunks, scoring chunk 5 gives the loss a prefill of chunk 5 reports
+    (its loss before the update), and leaves the weights and position as a prefill of it
+    would leave position (weights untouched)."""
+    c = mkcfg(**dict(TOY, n_fast=2))
+    w = synth.weights(_shape(c), bf16=False)
+    seq = synth.tokens(1, 321, c.vocab, "uniform", seed=14)
+    a, b = _ctx(c, w, 400), _ctx(c, w, 400)
+    a.prefill(seq[:, :256], seq[:, 1:257])
+    b.prefill(seq[:, :256], seq[:, 1:257])
+    fa = a.fast_weights_flat(0).copy()
+    ls = a.score(seq[:, 256:320], seq[:, 257:321])
+    lp = b.prefill_chunk(seq[:, 256:320], seq[:, 257:321])
+    np.testing.assert_allclose(ls[:, 0], lp, rtol=1e-5)
+    assert a.position == b.position == 320
+    assert np.array_equal(a.fast_weights_flat(0), fa)
