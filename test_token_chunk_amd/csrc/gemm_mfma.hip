@@ -341,6 +341,23 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(GemmArgs g) {
 
 constexpr int DL_TILE_BYTES = (128 + 128) * BK * 2;  // one stage: A and B tiles
 
+// Tile of a block of the 128 x 128 loop (grid: n tiles, m tiles, batch).  Consecutive
+// workgroups of a launch go round-robin to the 8 XCDs, each with its own 4 MB L2: block b of a
+// z slice takes logical tile (b % 8) * (nt / 8) + b / 8, so an XCD works through a contiguous
+// run of logical tiles, and the logical order walks groups of 8 m tiles column by column, so
+// the 64 blocks an XCD holds at a time (two per CU) cover about 8 x 8 tiles and share 8 panels
+// of each operand in its L2 instead of fetching a panel per tile.
+__device__ __forceinline__ void dl_tile(int& m0, int& n0) {
+  const int ntn = gridDim.x, ntm = gridDim.y, nt = ntn * ntm;
+  const int lin = blockIdx.y * ntn + blockIdx.x;
+  const int lg = nt % 8 == 0 ? (lin % 8) * (nt / 8) + lin / 8 : lin;
+  const int GM = min(8, ntm);
+  const int grp = lg / (GM * ntn), first = grp * GM, gm = min(ntm - first, GM);
+  const int rr = lg - grp * GM * ntn;
+  m0 = (first + rr % gm) * 128;
+  n0 = (rr / gm) * 128;
+}
+
 // Fused SGD step of the 128 x 128 loop with the MFMA operands swapped (lane = output row m,
 // four consecutive columns n per register group): the fp32 master values of the tile are
 // loaded into registers before the main loop (their latency hides behind it), then
@@ -409,7 +426,8 @@ __global__ __launch_bounds__(256) void k_gemm_dl(GemmArgs g) {
   const int split = SPLIT ? blockIdx.z % S : 0;
   const int kbeg = SPLIT ? split * (int)g.e.st : 0;
   const int kend = SPLIT ? min(g.K, kbeg + (int)g.e.st) : g.K;
-  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+  int m0, n0;
+  dl_tile(m0, n0);
   const bf16* A = (const bf16*)g.A + bz * g.sA;
   const bf16* B = (const bf16*)g.B + bz * g.sB;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
