@@ -36,6 +36,23 @@ int tttk_swa_fwd(int dtype, const void* q, const void* kr, const void* vr, const
                  int32_t B, int32_t H, int32_t hd, int32_t n, int32_t R, int32_t window, int64_t pos0, float* ws,
                  int64_t ws_floats, void* stream);
 
+/* tttk_swa_fwd for callers that cannot allocate device memory (code under HIP
+ * graph capture, serving loops, harnesses that forbid allocation): no workspace
+ * argument, and the call allocates nothing.  Where tttk_swa_fwd would split the
+ * key range (small grids, bf16), the parts go to a static fp32 array of the
+ * library, TTTK_NOALLOC_SCRATCH_FLOATS floats (32 MiB) per device, which every
+ * device the library runs on holds until the process ends.  Results are those of
+ * tttk_swa_fwd with a workspace of that many floats.  TTT_EINVAL (nothing is
+ * launched) when the split the call would take needs more floats than that, e.g.
+ * one 1024-query chunk of 16 heads of 128 (4 parts of 2.1 M floats); the
+ * smaller-split forms are not substituted.  Every call on a device shares that
+ * device's array and leaves its parts there: calls that overlap on one device
+ * (on different streams, or from different threads) race. */
+#define TTTK_NOALLOC_SCRATCH_FLOATS (8 * 1024 * 1024)
+int tttk_swa_fwd_noalloc(int dtype, const void* q, const void* kr, const void* vr, const void* vtr, void* o,
+                         float* lse, int32_t B, int32_t H, int32_t hd, int32_t n, int32_t R, int32_t window,
+                         int64_t pos0, void* stream);
+
 /* Backward of tttk_swa_fwd for a chunk whose keys are ring slots of
  * positions pos0 .. pos0+n-1; keys before pos0 are constants (same page,
  * §8 Q1).  qt [B][H][hd][n] (q transposed), o, dout [B*n][H*hd] in dtype,

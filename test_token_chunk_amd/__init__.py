@@ -366,7 +366,8 @@ class TTTContext:
 
 
 # ---------------------------------------------------------------- kernel level
-KERNEL_EXPORTS = ("tttk_gemm", "tttk_swa_fwd", "tttk_swa_bwd")
+KERNEL_EXPORTS = ("tttk_gemm", "tttk_swa_fwd", "tttk_swa_bwd", "tttk_swa_fwd_noalloc")
+NOALLOC_SCRATCH_FLOATS = 8 * 1024 * 1024  # TTTK_NOALLOC_SCRATCH_FLOATS of include/ttt_kernels.h
 
 
 def _klib():
@@ -378,6 +379,8 @@ def _klib():
                                      vp]
         lib.tttk_swa_bwd.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                      i32, i32, i32, i32, i32, i32, i64, vp, i64, vp]
+        lib.tttk_swa_fwd_noalloc.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i64,
+                                             vp]
         lib._k_ready = True
     return lib
 
@@ -426,6 +429,16 @@ def swa_fwd(q, kr, vr, vtr, o, lse, pos0: int, window: int, ws=None):
                               *_ws(ws), _stream())
     if rc:
         raise TTTError(rc, "tttk_swa_fwd")
+
+
+def swa_fwd_noalloc(q, kr, vr, vtr, o, lse, pos0: int, window: int):
+    """tttk_swa_fwd_noalloc: as swa_fwd, with the split parts in the library's static scratch."""
+    B, H, n, hd = q.shape
+    R = kr.shape[2]
+    rc = _klib().tttk_swa_fwd_noalloc(_dt(q), _p(q), _p(kr), _p(vr), _p(vtr), _p(o), _p(lse), B, H, hd, n, R, window,
+                                      pos0, _stream())
+    if rc:
+        raise TTTError(rc, "tttk_swa_fwd_noalloc")
 
 
 def swa_bwd(q, qt, kr, vr, vtr, o, dout, lse, dvec, dq, dk, dv, pos0: int, window: int, ws=None, ktr=None,

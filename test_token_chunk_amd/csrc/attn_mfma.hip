@@ -1385,6 +1385,17 @@ int swa_fwd_mfma_splits(const AttnArgs& a) {
 
 int swa_decode_splits(const AttnArgs& a) { return decode_splits(a); }
 
+int64_t swa_fwd_mfma_ws_need(const AttnArgs& a0) {
+  if (a0.n == 0) return 0;
+  AttnArgs a = a0;
+  a.ws = reinterpret_cast<float*>(static_cast<uintptr_t>(256));  // any non-null workspace: only sizes are computed
+  a.ws_floats = INT64_MAX;
+  if (const int S = decode_splits(a)) return S > 1 ? (int64_t)S * a.B * a.H * (a.hd + 2) : 0;
+  if (a.R % 8 != 0 || (a.hd != 32 && a.hd != 64 && a.hd != 96 && a.hd != 128)) return 0;
+  const int S = fwd_splits(a);
+  return S > 1 ? (int64_t)S * a.B * a.H * a.n * (a.hd + 2) : 0;
+}
+
 hipError_t swa_decode_blocks(const AttnArgs& a, int S, hipStream_t s) {
   if (S < 1 || S != decode_splits(a)) return hipErrorInvalidValue;
   if (a.hd == 128)

@@ -1,4 +1,6 @@
 // Kernel-level C entry points (include/ttt_kernels.h).
+#include <atomic>
+
 #include "kernels.h"
 #include "ttt.h"
 #include "ttt_kernels.h"
@@ -36,6 +38,58 @@ extern "C" int tttk_swa_fwd(int dtype, const void* q, const void* kr, const void
   if (dtype == TTT_F32) return code(swa_fwd_simt<float>(a, (hipStream_t)stream));
   if (dtype == TTT_BF16) return code(swa_fwd_mfma(a, (hipStream_t)stream));
   return TTT_EINVAL;
+}
+
+// ------------------------------------------------------------ no-allocation variant
+// The split key-range parts of tttk_swa_fwd_noalloc live in this array (one copy per device,
+// loaded with the code object and kept until the process ends).  Host code never uses the
+// array's name as an address: the device address comes from hipGetSymbolAddress, once per
+// device, and is what the kernels receive.
+static __device__ __align__(256) float scratch[TTTK_NOALLOC_SCRATCH_FLOATS];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<float*> g_scratch[kMaxDevices];
+
+// Nothing in the array needs clearing between calls: every part the merge kernels read is
+// written by the same call's split kernel first.
+// device address of `scratch` on the current device (looked up on the first call there)
+hipError_t scratch_ptr(float** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  float* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    void* addr = nullptr;
+    e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!addr) return hipErrorInvalidSymbol;
+    p = static_cast<float*>(addr);
+    g_scratch[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return hipSuccess;
+}
+}  // namespace
+
+extern "C" int tttk_swa_fwd_noalloc(int dtype, const void* q, const void* kr, const void* vr, const void* vtr,
+                                    void* o, float* lse, int32_t B, int32_t H, int32_t hd, int32_t n, int32_t R,
+                                    int32_t window, int64_t pos0, void* stream) {
+  if (!q || !kr || !vr || !vtr || !o || B < 1 || H < 1 || hd < 2 || hd % 2 || hd > 128 || n < 0 || window < 1 ||
+      pos0 < 0 || R < window + n - 1)
+    return TTT_EINVAL;
+  if (dtype == TTT_F32) {  // the fp32 kernels take no workspace
+    AttnArgs a{q, kr, vr, vtr, o, lse, B, H, hd, n, R, window, pos0, nullptr, 0};
+    return code(swa_fwd_simt<float>(a, (hipStream_t)stream));
+  }
+  if (dtype != TTT_BF16) return TTT_EINVAL;
+  float* ws = nullptr;
+  if (scratch_ptr(&ws) != hipSuccess) return TTT_EDEVICE;
+  AttnArgs a{q, kr, vr, vtr, o, lse, B, H, hd, n, R, window, pos0, ws, TTTK_NOALLOC_SCRATCH_FLOATS};
+  // the split this call would take must fit the static array: no smaller split is substituted
+  if (swa_fwd_mfma_ws_need(a) > TTTK_NOALLOC_SCRATCH_FLOATS) return TTT_EINVAL;
+  return code(swa_fwd_mfma(a, (hipStream_t)stream));
 }
 
 extern "C" int tttk_swa_bwd(int dtype, const void* q, const void* qt, const void* kr, const void* vr, const void* vtr,

@@ -153,6 +153,8 @@ template <typename T>
 hipError_t swa_fwd_simt(const AttnArgs& a, hipStream_t s);
 hipError_t swa_fwd_mfma(const AttnArgs& a, hipStream_t s);  // bf16
 int swa_fwd_mfma_splits(const AttnArgs& a);                  // key-range parts it would use
+// fp32 workspace floats the split it prefers takes when the workspace does not limit it (0: none)
+int64_t swa_fwd_mfma_ws_need(const AttnArgs& a);
 // the two launches swa_fwd_mfma makes for one query per (row, head) (n == 1, hd 64 or 128):
 // S blocks of 128 window keys per (row, head) (S = swa_decode_splits, 0 when that form does
 // not apply; parts in ws when S > 1), then their merge into o and lse
