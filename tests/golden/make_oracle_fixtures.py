@@ -86,6 +86,8 @@ def main(argv=None) -> int:
     ap.add_argument("workload", choices=sorted(WORKLOADS))
     args = ap.parse_args(argv)
     from oracle import Oracle
+    with open(os.path.join(ROOT, "oracle", "ttt_oracle.c"), "rb") as fh:  # the source the library is built from
+        sha = hashlib.sha256(fh.read()).hexdigest()
     spec = WORKLOADS[args.workload]
     c = dict(spec["cfg"])
     chunks, b = spec["chunks"], c["chunk"]
@@ -121,8 +123,6 @@ def main(argv=None) -> int:
         dw_argmax[t], dw_at_argmax[t], dw_absmax[t] = i, dw[i], abs(dw[i])
         dw_samples[t] = dw[sample_indices(t, sizes[t])]
         off += sizes[t]
-    with open(os.path.join(ROOT, "oracle", "ttt_oracle.c"), "rb") as fh:
-        sha = hashlib.sha256(fh.read()).hexdigest()
     meta = dict(workload=args.workload, config=c, chunks=chunks, tokens=T, token_dist="zipf",
                 token_seed=TOKEN_SEED, weight_seed=synth.WEIGHT_SEED, samples=SAMPLES, sample_seed=SAMPLE_SEED,
                 oracle_sha256=sha, oracle_seconds=round(time.time() - t0, 1))

@@ -104,45 +104,49 @@ def forward_full(W: Weights, ids, causal_only: bool = False) -> torch.Tensor:
     return hf @ W.Wlm.T
 
 
-def chunk_loop(W: Weights, seq, lr: float, chunk: int):
+def chunk_loop(W: Weights, seq, lr: float, chunk: int, n_steps: int = 1):
     """TTT chunk loop with autograd: keys/values of earlier chunks are kept
-    (detached) and attended to through the band mask; per chunk: mean CE,
-    gradient w.r.t. the fast weights, one SGD step.  Returns (losses [C],
-    per-chunk logits list)."""
+    (detached) and attended to through the band mask; per chunk, n_steps times:
+    forward at the current fast weights, mean CE, gradient w.r.t. the fast
+    weights, one SGD step.  The keys/values cached for the chunk are those of
+    its last forward; the loss reported is that of its first.  Returns
+    (losses [C], per-chunk logits of the first forward)."""
     cfg = W.cfg
     seq = torch.as_tensor(np.asarray(seq), dtype=torch.long)
     T = seq.shape[0] - 1
     cacheK = [None] * cfg.n_layers
     cacheV = [None] * cfg.n_layers
     losses, all_logits = [], []
+    params = [p for blk in W.fast for p in blk]
     for p0 in range(0, T, chunk):
         p1 = min(T, p0 + chunk)
         ids, tgt = seq[p0:p1], seq[p0 + 1:p1 + 1]
         pos = torch.arange(p0, p1)
-        h = W.E[ids]
-        newK, newV = [], []
-        for l in range(cfg.n_layers):
-            q, k, v = _block_attn_inputs(W, l, h, pos)
-            Kall = k if cacheK[l] is None else torch.cat([cacheK[l], k], dim=1)
-            Vall = v if cacheV[l] is None else torch.cat([cacheV[l], v], dim=1)
-            mask = band_mask(pos, torch.arange(0, p1), cfg.window)
-            att = F.scaled_dot_product_attention(q, Kall, Vall, attn_mask=mask)
-            newK.append(k.detach())
-            newV.append(v.detach())
-            h = _block_rest(W, l, h, att)
-        hf = F.rms_norm(h, (cfg.d_model,), weight=W.gf, eps=cfg.rms_eps)
-        logits = hf @ W.Wlm.T
-        loss = F.cross_entropy(logits, tgt, ignore_index=-1)
-        params = [p for blk in W.fast for p in blk]
-        grads = torch.autograd.grad(loss, params)
-        with torch.no_grad():
-            for p, g in zip(params, grads):
-                p -= lr * g
+        for step in range(n_steps):
+            h = W.E[ids]
+            newK, newV = [], []
+            for l in range(cfg.n_layers):
+                q, k, v = _block_attn_inputs(W, l, h, pos)
+                Kall = k if cacheK[l] is None else torch.cat([cacheK[l], k], dim=1)
+                Vall = v if cacheV[l] is None else torch.cat([cacheV[l], v], dim=1)
+                mask = band_mask(pos, torch.arange(0, p1), cfg.window)
+                att = F.scaled_dot_product_attention(q, Kall, Vall, attn_mask=mask)
+                newK.append(k.detach())
+                newV.append(v.detach())
+                h = _block_rest(W, l, h, att)
+            hf = F.rms_norm(h, (cfg.d_model,), weight=W.gf, eps=cfg.rms_eps)
+            logits = hf @ W.Wlm.T
+            loss = F.cross_entropy(logits, tgt, ignore_index=-1)
+            grads = torch.autograd.grad(loss, params)
+            with torch.no_grad():
+                for p, g in zip(params, grads):
+                    p -= lr * g
+            if step == 0:
+                losses.append(float(loss))
+                all_logits.append(logits.detach())
         for l in range(cfg.n_layers):
             cacheK[l] = newK[l] if cacheK[l] is None else torch.cat([cacheK[l], newK[l]], dim=1)
             cacheV[l] = newV[l] if cacheV[l] is None else torch.cat([cacheV[l], newV[l]], dim=1)
-        losses.append(float(loss))
-        all_logits.append(logits.detach())
     return np.array(losses), all_logits
 
 
