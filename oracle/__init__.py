@@ -5,7 +5,8 @@ of the benchmark use it.  The product path never imports this package; the
 oracle shares no code with the HIP path.
 
 The configuration is any object with the attributes n_layers, d_model,
-n_heads, d_ff, vocab, window, chunk, n_fast, batch, rope_theta, rms_eps, lr.
+n_heads, d_ff, vocab, window, chunk, n_fast, batch, rope_theta, rms_eps, lr
+(and optionally n_steps, SGD steps per chunk, default 1).
 Weights are the dict of fp32 numpy arrays produced by the seeded generator
 (row-major [out, in]); they must stay alive as long as the Oracle does.
 """
@@ -33,7 +34,7 @@ def build_lib(force: bool = False) -> str:
 
 class _Cfg(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
-                ("n_layers", "d_model", "n_heads", "d_ff", "vocab", "window", "chunk", "n_fast", "batch", "pad_")] + \
+                ("n_layers", "d_model", "n_heads", "d_ff", "vocab", "window", "chunk", "n_fast", "batch", "n_steps")] + \
                [("rope_theta", ctypes.c_double), ("rms_eps", ctypes.c_double), ("lr", ctypes.c_double)]
 
 
@@ -106,7 +107,7 @@ class Oracle:
         self.L = cfg.n_layers
         c = _Cfg(*(int(getattr(cfg, n)) for n in
                    ("n_layers", "d_model", "n_heads", "d_ff", "vocab", "window", "chunk", "n_fast", "batch")),
-                 0, float(cfg.rope_theta), float(cfg.rms_eps), float(cfg.lr))
+                 int(getattr(cfg, "n_steps", 1)), float(cfg.rope_theta), float(cfg.rms_eps), float(cfg.lr))
         self._keep = []
         arrs = {}
         for key in ("attn_norm", "wq", "wk", "wv", "wo", "mlp_norm", "w_gate", "w_up", "w_down"):

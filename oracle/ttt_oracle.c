@@ -47,7 +47,7 @@
 
 typedef struct {
   int32_t n_layers, d_model, n_heads, d_ff, vocab, window, chunk, n_fast, batch;
-  int32_t pad_;
+  int32_t n_steps; /* SGD steps per chunk; 0 and 1 both mean one */
   double rope_theta, rms_eps, lr;
 } oracle_cfg;
 
@@ -212,7 +212,7 @@ oracle_state* oracle_create(const oracle_cfg* cfg, const oracle_weights* w, int6
   const oracle_cfg c = *cfg;
   if (c.n_layers <= 0 || c.d_model <= 0 || c.n_heads <= 0 || c.d_model % c.n_heads || (c.d_model / c.n_heads) % 2 ||
       c.d_ff <= 0 || c.vocab <= 0 || c.chunk <= 0 || c.window < c.chunk || c.n_fast < 1 || c.n_fast > c.n_layers ||
-      c.batch <= 0)
+      c.batch <= 0 || c.n_steps < 0)
     return NULL;
   oracle_state* s = (oracle_state*)xcalloc(1, sizeof(oracle_state));
   s->c = c;
@@ -617,19 +617,31 @@ int oracle_eval_chunk(oracle_state* s, const int32_t* tokens, const int32_t* tar
  * One step of the inner loop for every row: chunk loss at the current fast
  * weights, its gradient, one SGD step  phi <- phi - lr * grad, pos += n.
  * loss_out[batch] receives the loss before the step.
+ *
+ * With n_steps > 1 (page "从KV Cache到权重压缩：大模型持续学习的新范式", §2.2:
+ * one to three gradient steps on what has been read before the next
+ * prediction) the chunk is processed n_steps times in a row, each time as
+ * above at the weights the previous step left: loss, gradient, SGD.  The
+ * chunk's own key/value entries are those of its last forward; loss_out is
+ * the loss of the first.
  */
 int oracle_prefill_chunk(oracle_state* s, const int32_t* tokens, const int32_t* targets, int n, double* loss_out) {
   int64_t F = oracle_fast_size(s);
+  const int steps = s->c.n_steps > 1 ? s->c.n_steps : 1;
   double* grad = xcalloc((size_t)(F * s->c.batch), 8);
-  int rc = oracle_eval_chunk(s, tokens, targets, n, loss_out, grad);
-  if (rc == 0) {
-    for (int r = 0; r < s->c.batch; ++r) {
-      double* phi = s->rows[r].fast;
-      const double* g = grad + (int64_t)r * F;
-      for (int64_t i = 0; i < F; ++i) phi[i] -= s->c.lr * g[i];
-      s->rows[r].pos += n;
+  int rc = 0;
+  for (int st = 0; st < steps && rc == 0; ++st) {
+    rc = oracle_eval_chunk(s, tokens, targets, n, st == 0 ? loss_out : NULL, grad);
+    if (rc == 0) {
+      for (int r = 0; r < s->c.batch; ++r) {
+        double* phi = s->rows[r].fast;
+        const double* g = grad + (int64_t)r * F;
+        for (int64_t i = 0; i < F; ++i) phi[i] -= s->c.lr * g[i];
+      }
     }
   }
+  if (rc == 0)
+    for (int r = 0; r < s->c.batch; ++r) s->rows[r].pos += n;
   free(grad);
   return rc;
 }

@@ -156,6 +156,46 @@ def test_chunk_loop_equals_autograd_chunk_loop(n_fast):
             assert np.max(np.abs(d_got - d_ref)) <= 1e-9 * np.max(np.abs(d_ref))
 
 
+@pytest.mark.parametrize("n_fast,n_steps", [(1, 2), (2, 3)])
+def test_several_sgd_steps_per_chunk_equal_autograd_chunk_loop(n_fast, n_steps):
+    """n SGD steps per chunk (forward at the weights the previous step left, loss, gradient,
+    step; first loss reported; the chunk's keys/values from its last forward) against the
+    autograd chunk loop doing the same with library routines."""
+    c = cfg(window=6, chunk=4, lr=0.2, n_fast=n_fast, n_steps=n_steps)
+    w = tiny_weights(c)
+    seq = seq_for(c, 14)
+    o = Oracle(c, w, 20)
+    losses = o.prefill(seq)[0]
+    W = tp.Weights(w, c)
+    ref_losses, _ = tp.chunk_loop(W, seq[0], c.lr, c.chunk, n_steps=n_steps)
+    np.testing.assert_allclose(losses, ref_losses, rtol=1e-11)
+    got, ref = o.get_fast(0), tp.fast_numpy(W)
+    w0 = [(w["w_gate"][l], w["w_up"][l], w["w_down"][l]) for l in range(c.n_layers - n_fast, c.n_layers)]
+    for j in range(n_fast):
+        for a in range(3):
+            d_ref = ref[j][a] - w0[j][a]
+            assert np.max(np.abs((got[j][a] - w0[j][a]) - d_ref)) <= 1e-9 * np.max(np.abs(d_ref))
+    # more steps move the weights further than one step does
+    one = Oracle(cfg(window=6, chunk=4, lr=0.2, n_fast=n_fast), w, 20)
+    one.prefill(seq)
+    assert not np.allclose(one.get_fast_flat(0), o.get_fast_flat(0))
+
+
+def test_one_step_is_the_default_and_lr0_steps_change_nothing():
+    """n_steps = 1 is exactly the single-step loop; with lr = 0 three steps report the same
+    losses as one and leave the fast weights bit for bit unchanged."""
+    c = cfg(window=6, chunk=4, lr=0.2, n_fast=2)
+    w = tiny_weights(c)
+    seq = seq_for(c, 12)
+    a, b = Oracle(c, w, 16), Oracle(cfg(window=6, chunk=4, lr=0.2, n_fast=2, n_steps=1), w, 16)
+    np.testing.assert_array_equal(a.prefill(seq), b.prefill(seq))
+    np.testing.assert_array_equal(a.get_fast_flat(0), b.get_fast_flat(0))
+    z1, z3 = Oracle(cfg(window=6, chunk=4, lr=0.0, n_fast=2), w, 16), \
+        Oracle(cfg(window=6, chunk=4, lr=0.0, n_fast=2, n_steps=3), w, 16)
+    np.testing.assert_array_equal(z1.prefill(seq), z3.prefill(seq))
+    np.testing.assert_array_equal(z3.get_fast_flat(0), z1.get_fast_flat(0))
+
+
 def test_ignored_targets_and_empty_chunk():
     """Targets -1 are left out of the mean; a chunk with none valid has loss 0
     and leaves the fast weights unchanged."""
