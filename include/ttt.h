@@ -65,7 +65,10 @@ typedef struct {
                          fp32 residual stream and fp32 master copy of the fast weights */
   int32_t lookahead;  /* chunks whose frozen lower blocks run as one batch (0 = default: 32, at most
                          ceil(max_positions / chunk)); costs (window + lookahead * chunk) ring slots */
-  int32_t reserved_;
+  int32_t n_steps;    /* SGD steps per chunk (0 = 1): each chunk is processed n_steps times in a row at the
+                         weights the previous step left -- forward, loss, gradient, SGD -- and the loss of
+                         the first is reported (page "从KV Cache到权重压缩：大模型持续学习的新范式",
+                         §2.2: one to three gradient steps before the next prediction) */
   int64_t max_positions; /* largest absolute position + 1 that will be processed (RoPE table size) */
   double rope_theta;  /* RoPE base; rotate-half pairing (i, i + head_dim/2) */
   double rms_eps;     /* RMSNorm epsilon: g * x / sqrt(mean(x^2) + eps) */

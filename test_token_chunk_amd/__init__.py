@@ -57,7 +57,7 @@ class TTTError(RuntimeError):
 class _Config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("n_layers", "d_model", "n_heads", "d_ff", "vocab", "window", "chunk", "n_fast", "batch", "dtype",
-                 "lookahead", "reserved_")] + \
+                 "lookahead", "n_steps")] + \
                [("max_positions", ctypes.c_int64), ("rope_theta", ctypes.c_double), ("rms_eps", ctypes.c_double),
                 ("lr", ctypes.c_float), ("reserved2_", ctypes.c_float)]
 
@@ -177,6 +177,7 @@ class TTTConfig:
     batch: int = 1
     dtype: str = "bf16"  # "bf16" or "f32"
     lookahead: int = 0
+    n_steps: int = 0  # SGD steps per chunk (0 = 1)
     max_positions: int = 1 << 17
     rope_theta: float = 1e4
     rms_eps: float = 1e-5
@@ -190,7 +191,8 @@ class TTTConfig:
 
     def _c(self) -> _Config:
         return _Config(self.n_layers, self.d_model, self.n_heads, self.d_ff, self.vocab, self.window, self.chunk,
-                       self.n_fast, self.batch, TTT_BF16 if self.dtype == "bf16" else TTT_F32, self.lookahead, 0,
+                       self.n_fast, self.batch, TTT_BF16 if self.dtype == "bf16" else TTT_F32, self.lookahead,
+                       self.n_steps,
                        self.max_positions, self.rope_theta, self.rms_eps, self.lr, 0.0)
 
 

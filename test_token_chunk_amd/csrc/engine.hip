@@ -67,6 +67,7 @@ struct TopActs {
 struct ttt_ctx {
   ttt_config cfg;
   int L, d, H, hd, f, V, k, b, Lq, l0, B, R, G;
+  int n_steps = 1;  // SGD steps per chunk
   bool bf16;
   size_t es;  // element size of T
   bool mfma = true;
@@ -114,6 +115,7 @@ struct ttt_ctx {
   int64_t d_tok_cap = 0;
   float* d_loss = nullptr;
   int64_t d_loss_cap = 0;
+  float* loss_later = nullptr;  // [B]: losses of a chunk's steps after the first (not reported)
 
   int64_t pos = 0;
   bool poisoned = false;
@@ -723,9 +725,11 @@ int run_tokens_overlap(ttt_ctx* c, const int32_t* tok, const int32_t* tgt, int64
     const int64_t s = gi * gmax;
     for (int cs = 0; cs < g; cs += c->b) {
       const int n = std::min(c->b, g - cs);
-      rc = top_chunk<T>(c, tgt + s + cs, ld, hbuf[gi & 1] + (int64_t)cs * c->d, (int64_t)g * c->d, n,
-                        c->pos + s + cs, loss_dev + ci * c->B);
-      if (rc) return rc;
+      for (int st = 0; st < c->n_steps; ++st) {
+        rc = top_chunk<T>(c, tgt + s + cs, ld, hbuf[gi & 1] + (int64_t)cs * c->d, (int64_t)g * c->d, n,
+                          c->pos + s + cs, st == 0 ? loss_dev + ci * c->B : c->loss_later);
+        if (rc) return rc;
+      }
       ++ci;
     }
     CK(hipEventRecord(c->ev_cdone[gi & 1], c->stream));
@@ -745,9 +749,11 @@ int run_tokens(ttt_ctx* c, const int32_t* tok, const int32_t* tgt, int64_t ld, i
     if (rc) return rc;
     for (int cs = 0; cs < g; cs += c->b) {
       int n = std::min(c->b, g - cs);
-      rc = top_chunk<T>(c, tgt + done + cs, ld, c->hb + (int64_t)cs * c->d, (int64_t)g * c->d, n, c->pos + done + cs,
-                        loss_dev + ci * c->B);
-      if (rc) return rc;
+      for (int st = 0; st < c->n_steps; ++st) {
+        rc = top_chunk<T>(c, tgt + done + cs, ld, c->hb + (int64_t)cs * c->d, (int64_t)g * c->d, n,
+                          c->pos + done + cs, st == 0 ? loss_dev + ci * c->B : c->loss_later);
+        if (rc) return rc;
+      }
       ++ci;
     }
     done += g;
@@ -1022,6 +1028,7 @@ int build(ttt_ctx* c, const ttt_weights* w) {
   AL(c->hf, rows_top * d * es);
   AL(c->dlogits, rows_top * V * es);
   AL(c->nvalid, B * 4);
+  AL(c->loss_later, B * 4);
   AL(c->dh, rows_top * d * 4);
   AL(c->tmpf, rows_top * d * 4);
   AL(c->dq, rows_top * d * 4);
@@ -1187,6 +1194,7 @@ int ttt_create(const ttt_config* cfg, const ttt_weights* w, void* hip_stream, tt
   if (c0.n_fast < 1 || c0.n_fast > c0.n_layers) return bad("n_fast out of range");
   if (c0.dtype != TTT_F32 && c0.dtype != TTT_BF16) return bad("dtype must be TTT_F32 or TTT_BF16");
   if (c0.max_positions <= 0) return bad("max_positions must be positive");
+  if (c0.n_steps < 0) return bad("n_steps must be >= 0");
   if (!(c0.rope_theta > 0) || !(c0.rms_eps >= 0) || !std::isfinite(c0.lr)) return bad("bad theta/eps/lr");
   if (!w->embed || !w->final_norm || !w->lm_head || !w->attn_norm || !w->wq || !w->wk || !w->wv || !w->wo ||
       !w->mlp_norm || !w->w_gate || !w->w_up || !w->w_down)
@@ -1221,6 +1229,7 @@ int ttt_create(const ttt_config* cfg, const ttt_weights* w, void* hip_stream, tt
   c->l0 = c0.n_layers - c0.n_fast;
   c->B = c0.batch;
   c->G = c0.lookahead;
+  c->n_steps = std::max(1, c0.n_steps);
   c->R = c0.window + c0.lookahead * c0.chunk;
   c->bf16 = c0.dtype == TTT_BF16;
   c->es = c->bf16 ? 2 : 4;

@@ -478,3 +478,24 @@ def test_score_after_prefill_is_the_pre_update_loss():
     np.testing.assert_allclose(ls[:, 0], lp, rtol=1e-5)
     assert a.position == b.position == 320
     assert np.array_equal(a.fast_weights_flat(0), fa)
+
+
+@pytest.mark.parametrize("dtype,n_steps", [("f32", 2), ("f32", 3), ("bf16", 2)])
+def test_several_sgd_steps_per_chunk_against_oracle(dtype, n_steps):
+    """n SGD steps per chunk (the chunk processed n times in a row, first loss reported): the toy
+    shape with two fast blocks (f32) and the d = 256 matrix-core shape (bf16), ring wrapping,
+    against the oracle with the same n."""
+    base = dict(TOY, dtype=dtype, n_fast=2) if dtype == "f32" else dict(MID)
+    c = mkcfg(**dict(base, n_steps=n_steps))
+    T = 640 if dtype == "f32" else MID_T
+    print(f"case {dtype} n_steps {n_steps}", flush=True)
+    w, o, ctx, ref, got = run_pair(c, T, dist="uniform" if dtype == "f32" else "zipf")
+    tl, tw = TOL[dtype]
+    rel = np.max(np.abs(got - ref) / np.abs(ref))
+    print(f"{dtype} n_steps {n_steps}: max loss rel err {rel:.3e}")
+    assert rel <= tl
+    compare_fast(ctx.fast_weights(0), o.get_fast(0), _w0(w, c), tw, f"{dtype} n_steps {n_steps}")
+    one = _ctx(mkcfg(**dict(base, n_steps=1)), w, T + 8)
+    seq = synth.tokens(c.batch, T + 1, c.vocab, "uniform" if dtype == "f32" else "zipf", seed=1)
+    l1 = one.prefill(seq[:, :T], seq[:, 1:])
+    assert got[0, 0] == l1[0, 0] and not np.allclose(got, l1)
