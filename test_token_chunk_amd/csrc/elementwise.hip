@@ -478,15 +478,17 @@ __global__ __launch_bounds__(256) void k_rope_qkv(const float* __restrict__ qkv,
     const int slot = (int)(pos % rr.R);
     const float* row = qkv + ((int64_t)b * rr.n + t) * 3 * d + h * hd;
     const float c = rr.cos_t[pos * half + i], s = rr.sin_t[pos * half + i];
-    float a = row[i], bb = row[i + half];
+    // dims i and i + half: natural columns, or adjacent ones when q/k are pair-interleaved
+    const int ca = rr.perm ? 2 * i : i, cb = rr.perm ? 2 * i + 1 : i + half;
+    float a = row[ca], bb = row[cb];
     const float q0 = a * c - bb * s, q1 = bb * c + a * s;
     T* qrow = Q + (bh * rr.n + t) * hd;
     qrow[i] = from_f<T>(q0);
     qrow[i + half] = from_f<T>(q1);
     qs[i][tt] = from_f<T>(q0);
     qs[i + half][tt] = from_f<T>(q1);
-    a = row[d + i];
-    bb = row[d + i + half];
+    a = row[d + ca];
+    bb = row[d + cb];
     T* krow = Kr + (bh * rr.R + slot) * hd;
     const T k0 = from_f<T>(a * c - bb * s), k1 = from_f<T>(bb * c + a * s);
     krow[i] = k0;
@@ -546,8 +548,21 @@ __global__ __launch_bounds__(256) void k_rope_qkv4(const float* __restrict__ qkv
     const float4 c = *(const float4*)(rr.cos_t + pos * half + i), sn = *(const float4*)(rr.sin_t + pos * half + i);
     const float cc[4] = {c.x, c.y, c.z, c.w}, ss[4] = {sn.x, sn.y, sn.z, sn.w};
     float lo[4], hi[4];
+    // dims i..i+3 and i+half..i+half+3 of a q or k head (natural columns, or pair-interleaved:
+    // columns 2i..2i+7 hold dim i, i+half, i+1, i+1+half, ...)
+    auto pairs4 = [&](const float* hrow, float4& lo4, float4& hi4) {
+      if (rr.perm) {
+        const float4 x0 = *(const float4*)(hrow + 2 * i), x1 = *(const float4*)(hrow + 2 * i + 4);
+        lo4 = make_float4(x0.x, x0.z, x1.x, x1.z);
+        hi4 = make_float4(x0.y, x0.w, x1.y, x1.w);
+      } else {
+        lo4 = *(const float4*)(hrow + i);
+        hi4 = *(const float4*)(hrow + half + i);
+      }
+    };
     // q
-    float4 a = *(const float4*)(row + i), bb = *(const float4*)(row + half + i);
+    float4 a, bb;
+    pairs4(row, a, bb);
     float av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {bb.x, bb.y, bb.z, bb.w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -560,8 +575,7 @@ __global__ __launch_bounds__(256) void k_rope_qkv4(const float* __restrict__ qkv
     store4<T>(qrow + i, lo[0], lo[1], lo[2], lo[3]);
     store4<T>(qrow + half + i, hi[0], hi[1], hi[2], hi[3]);
     // k
-    a = *(const float4*)(row + d + i);
-    bb = *(const float4*)(row + d + half + i);
+    pairs4(row + d, a, bb);
     av[0] = a.x; av[1] = a.y; av[2] = a.z; av[3] = a.w;
     bv[0] = bb.x; bv[1] = bb.y; bv[2] = bb.z; bv[3] = bb.w;
 #pragma unroll

@@ -73,6 +73,9 @@ struct ttt_ctx {
   bool mfma = true;
   bool overlap = true;  // weight-gradient GEMMs on the side stream (TTT_NO_SIDE=1: on the main stream)
   bool il = false;  // gate/up rows interleaved for the single-operand SwiGLU GEMM (bf16 matrix-core path)
+  // q/k rows of the forward W_qkv pair-interleaved within each head (RopeRing::perm), so the
+  // projection's epilogue applies RoPE and writes q and the rings (bf16 matrix-core path)
+  bool rope_perm = false;
   hipStream_t stream = nullptr;
   // second stream for the fused-SGD weight-gradient GEMMs, which only the next chunk depends on
   hipStream_t side = nullptr;
@@ -388,11 +391,14 @@ int layer_fwd(ttt_ctx* c, int l, float* h, int n, int64_t p0, int mode, TopActs*
     rr.vr = w.vr;
     rr.vtr = w.vtr;
     rr.ktr = w.ktr;
-    // a handful of rows (decode): RoPE and the ring writes in the matrix-vector product itself
+    rr.perm = c->rope_perm ? 1 : 0;
+    // RoPE and the ring writes in the product's epilogue: the matrix-vector kernel for a handful
+    // of rows (decode), the wide matrix-core tiles for chunks whose shape allows it; otherwise
+    // an fp32 product and a separate RoPE pass
     GemmArgs gr = g;
     gr.e.kind = EPI_QKV_ROPE;
     gr.e.rr = rr;
-    if (c->mfma && c->bf16 && gemv_ok(gr)) {
+    if (c->mfma && c->bf16 && gemm_mfma_fuses_qkv_rope(gr)) {
       CK(Ops<T>::gemm(c, gr));
     } else {
       CK(Ops<T>::gemm(c, g));
@@ -934,7 +940,14 @@ int build(ttt_ctx* c, const ttt_weights* w) {
     memcpy(qkv.data() + 2 * (size_t)d * d, w->wv[l], (size_t)d * d * 4);
     AL(lw.wqkv, 3LL * d * d * es);
     AL(lw.wo, (int64_t)d * d * es);
-    if ((rc = upload(c, lw.wqkv, qkv.data(), 3LL * d * d))) return rc;
+    if (c->rope_perm) {  // forward copy with the q/k rows of each head pair-interleaved
+      std::vector<float> perm((size_t)3 * d * d);
+      for (int64_t r = 0; r < 3LL * d; ++r)
+        memcpy(perm.data() + qkv_perm_row(r, d, hd) * d, qkv.data() + r * d, (size_t)d * 4);
+      if ((rc = upload(c, lw.wqkv, perm.data(), 3LL * d * d))) return rc;
+    } else if ((rc = upload(c, lw.wqkv, qkv.data(), 3LL * d * d))) {
+      return rc;
+    }
     if ((rc = upload(c, lw.wo, w->wo[l], (int64_t)d * d))) return rc;
     if (l > c->l0) {
       AL(lw.wqkvT, 3LL * d * d * es);
@@ -1241,6 +1254,7 @@ int ttt_create(const ttt_config* cfg, const ttt_weights* w, void* hip_stream, tt
   const char* noside = getenv("TTT_NO_SIDE");
   c->overlap = !(noside && noside[0] == '1');
   c->il = c->bf16 && c->mfma && c0.d_ff % 32 == 0 && c0.d_model % 8 == 0;
+  c->rope_perm = c->bf16 && c->mfma;
   const char* nobot = getenv("TTT_NO_BOTTOM_OVERLAP");
   c->bot_overlap = !(nobot && nobot[0] == '1');
   bool ok = hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking) == hipSuccess &&

@@ -561,7 +561,7 @@ struct WideCfg {
 template <int BM, int EK>
 constexpr size_t wide_lds_bytes() {
   const size_t ops = (size_t)WideCfg<BM>::ST * WideCfg<BM>::SBYTES;
-  const int ntr = EK == EPI_SWIGLU_BWD ? 2 : (EK == EPI_SGD || EK == EPI_SWIGLU_IL) ? 1 : 0;
+  const int ntr = EK == EPI_SWIGLU_BWD ? 2 : (EK == EPI_SGD || EK == EPI_SWIGLU_IL || EK == EPI_QKV_ROPE) ? 1 : 0;
   const size_t trb = (size_t)ntr * 256 * (BM + 8) * 2;
   return ops > trb ? ops : trb;
 }
@@ -587,6 +587,70 @@ __device__ __forceinline__ void wide_epilogue(const GemmArgs& g, f32x16 (&acc)[T
     return make_uint2((uint32_t)f2bf(a).x | ((uint32_t)f2bf(b).x << 16),
                       (uint32_t)f2bf(c).x | ((uint32_t)f2bf(d).x << 16));
   };
+  if constexpr (EK == EPI_QKV_ROPE) {
+    // [q|k|v] product with pair-interleaved q/k columns (a tile lies in one part): a lane's four
+    // columns of a q or k head are dims (i, i + hd/2, i + 1, i + 1 + hd/2), rotated in registers at
+    // the row's position and stored as bf16 pairs; v columns are natural.  Rows go to q
+    // [B][H][n][hd] or to ring slot pos % R of K / V [B][H][R][hd]; the transposed copy (q^T, K^T,
+    // V^T, where wanted) is staged through LDS by tile column and stored as 8-token segments.
+    const RopeRing& rr = e.rr;
+    const int hd = rr.hd, half = hd / 2, dm = rr.H * hd;
+    const int part = n0 / dm;
+    bf16* const rows = (bf16*)(part == 0 ? rr.q : part == 1 ? rr.kr : rr.vr);
+    bf16* const tdst = (bf16*)(part == 0 ? rr.qt : part == 1 ? rr.ktr : rr.vtr);
+    const int s0 = (int)(rr.pos0 % rr.R);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int ml = wm0 + i * 32 + lr, m = m0 + ml;
+      const int b = m / rr.n, t = m % rr.n;
+      const int64_t pos = rr.pos0 + t;
+      const int slot = s0 + t >= rr.R ? s0 + t - rr.R : s0 + t;  // t < n <= R
+      const float* cs = rr.cos_t + pos * half;
+      const float* sn = rr.sin_t + pos * half;
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int nl = wn0 + j * 32 + 8 * q + 4 * hi, c = n0 + nl - part * dm;
+          const int h = c / hd, jj = c % hd;
+          const int64_t bh = (int64_t)b * rr.H + h;
+          bf16* row = rows + (part == 0 ? bh * rr.n + t : bh * rr.R + slot) * hd;
+          float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+          if (part < 2) {
+            const int i0 = jj / 2;
+            const float2 cc = *(const float2*)(cs + i0), ss = *(const float2*)(sn + i0);
+            const float lo0 = v[0] * cc.x - v[1] * ss.x, hi0 = v[1] * cc.x + v[0] * ss.x;
+            const float lo1 = v[2] * cc.y - v[3] * ss.y, hi1 = v[3] * cc.y + v[2] * ss.y;
+            *(uint32_t*)(row + i0) = (uint32_t)f2bf(lo0).x | ((uint32_t)f2bf(lo1).x << 16);
+            *(uint32_t*)(row + i0 + half) = (uint32_t)f2bf(hi0).x | ((uint32_t)f2bf(hi1).x << 16);
+            v[0] = lo0;
+            v[1] = hi0;
+            v[2] = lo1;
+            v[3] = hi1;
+          } else {
+            *(uint2*)(row + jj) = pk4(v[0], v[1], v[2], v[3]);
+          }
+          if (tdst) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) tr0[(nl + r) * TLD + ml] = f2bf(v[r]);
+          }
+        }
+    }
+    if (!tdst) return;  // (the same for the whole block)
+    __syncthreads();
+    constexpr int CH = BM / 8;
+    for (int cidx = tid; cidx < BN * CH; cidx += NT) {
+      const int lc = cidx / CH, ml = (cidx % CH) * 8;
+      const int c = n0 + lc - part * dm, h = c / hd, jj = c % hd;
+      const int dim = part < 2 ? ((jj & 1) ? jj / 2 + half : jj / 2) : jj;
+      const int m = m0 + ml, b = m / rr.n, t = m % rr.n;
+      const int64_t bh = (int64_t)b * rr.H + h;
+      const int sl = s0 + t >= rr.R ? s0 + t - rr.R : s0 + t;
+      const int64_t off = part == 0 ? (bh * hd + dim) * rr.n + t : (bh * hd + dim) * rr.R + sl;
+      *(uint4*)(tdst + off) = *(const uint4*)(tr0 + lc * TLD + ml);
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
     const int ml = wm0 + i * 32 + lr, m = m0 + ml;
@@ -1071,6 +1135,16 @@ bool wide_ok(const GemmArgs& g) {
     case EPI_SWIGLU_BWD:
       return e.ldc % 4 == 0 && e.sc % 4 == 0 && e.f % 4 == 0 && al(e.c, 8) && e.ldz % 4 == 0 && e.sz % 4 == 0 &&
              al(e.zg, 8) && al(e.zu, 8) && e.t && e.ldt % 8 == 0 && e.st % 8 == 0 && al(e.t, 16);
+    case EPI_QKV_ROPE: {
+      // a 256-column tile inside one of q, k, v; RoPE pairs in a lane's 4-column group; 8-token
+      // groups of a tile inside one batch row and one run of ring slots (16-byte transposed stores)
+      const RopeRing& r = e.rr;
+      const int64_t dm = (int64_t)r.H * r.hd;
+      return g.batch == 1 && r.perm && r.hd % 4 == 0 && r.hd <= 256 && dm % 256 == 0 && g.N == 3 * dm && r.n > 0 &&
+             r.n % 8 == 0 && g.M % r.n == 0 && r.n <= r.R && r.pos0 % 8 == 0 && r.R % 8 == 0 && r.q && r.kr &&
+             r.vr && r.vtr && r.cos_t && r.sin_t && al(r.q, 8) && al(r.kr, 8) && al(r.vr, 8) && al(r.vtr, 16) &&
+             al(r.ktr, 16) && al(r.qt, 16) && al(r.cos_t, 8) && al(r.sin_t, 8);
+    }
     default: return false;
   }
 }
@@ -1112,6 +1186,12 @@ GemmPlan gemm_plan(const GemmArgs& g) {
 
 }  // namespace
 
+bool gemm_mfma_fuses_qkv_rope(const GemmArgs& g) {
+  if (g.e.kind != EPI_QKV_ROPE || g.M <= 0) return false;
+  if (!(aligned16(g.A) && aligned16(g.B) && g.lda % 8 == 0 && g.ldb % 8 == 0)) return false;
+  return gemv_ok(g) || wide_ok(g);
+}
+
 // split-K parts for this GEMM (1: no split)
 int gemm_mfma_splits(const GemmArgs& g, int* ks_out) {
   if (g.M <= 0 || g.N <= 0 || g.batch <= 0) return 1;
@@ -1139,9 +1219,11 @@ hipError_t gemm_mfma_bf16(const GemmArgs& g, hipStream_t s) {
       case EPI_ADD_F32: return launch_wide_bm<EPI_ADD_F32>(g, bm, s);
       case EPI_SGD: return launch_wide_bm<EPI_SGD>(g, bm, s);
       case EPI_SWIGLU_BWD: return launch_wide<128, EPI_SWIGLU_BWD, false>(g, 1, s);
+      case EPI_QKV_ROPE: return launch_wide_bm<EPI_QKV_ROPE>(g, bm, s);
       default: break;
     }
   }
+  if (g.e.kind == EPI_QKV_ROPE) return hipErrorInvalidValue;  // (gemm_mfma_fuses_qkv_rope said no)
   if (p.kern == 1) {
     switch (g.e.kind) {
       case EPI_SWIGLU_IL: return launch_dl<EPI_SWIGLU_IL, false>(g, 1, s);

@@ -86,8 +86,14 @@ __global__ __launch_bounds__(256) void k_gemv(GemmArgs g, int ncols, int f) {
     ph = (int)(j0 % hpart) / half;
     pi = (int)(j0 % hpart) % half;
     const int64_t c0 = (int64_t)part * g.e.rr.H * g.e.rr.hd + (int64_t)ph * g.e.rr.hd + pi;
-    wr[0] = W + c0 * g.ldb;
-    wr[1] = W + (c0 + half) * g.ldb;
+    if (g.e.rr.perm && part < 2) {  // pair-interleaved q/k rows: dims pi and pi + hd/2 are adjacent
+      const int64_t r0 = (int64_t)part * g.e.rr.H * g.e.rr.hd + (int64_t)ph * g.e.rr.hd + 2 * pi;
+      wr[0] = W + r0 * g.ldb;
+      wr[1] = W + (r0 + 1) * g.ldb;
+    } else {
+      wr[0] = W + c0 * g.ldb;
+      wr[1] = W + (c0 + half) * g.ldb;
+    }
   }
   if constexpr (!RP) {
 #pragma unroll

@@ -16,7 +16,8 @@ enum EpiKind {
   EPI_SGD = 5,     // acc = gradient: master (fp32) -= lr * acc; shadow (T) and shadow^T (T) refreshed
   EPI_QKV_ROPE = 6, // acc = [q|k|v] row (N = 3 H hd, row m = token m % n of batch row m / n): RoPE of q, k
                     // at pos0 + m % n; q (q^T) and the ring slots of k (K^T), v, V^T written as in
-                    // rope_qkv_f32in; matrix-vector kernel only (gemv_ok)
+                    // rope_qkv_f32in; the matrix-vector kernel (gemv_ok) or, with pair-interleaved
+                    // q/k columns (rr.perm), the wide matrix-core tiles (gemm_mfma_fuses_qkv_rope)
   EPI_SWIGLU_IL = 7 // single operand with gate/up rows interleaved in groups of 32 (see swiglu_il_row):
                     // columns 64g..64g+31 are gate rows 32g.., 64g+32..64g+63 the matching up rows;
                     // outputs as EPI_SWIGLU with N = 2f (act, z_g, z_u [m][f], act^T)
@@ -40,7 +41,18 @@ struct RopeRing {
   void* vr;            // ring V [B][H][R][hd] T
   void* vtr;           // ring V^T [B][H][hd][R] T
   void* ktr = nullptr; // ring K^T [B][H][hd][R] T, or null (needed only where the backward runs)
+  // 1: the q and k columns of the [q|k|v] product are pair-interleaved within each head (the
+  // weight rows are stored that way): column 2i of a head holds dim i, column 2i + 1 holds dim
+  // i + hd/2, so a RoPE pair sits in adjacent columns; the v columns keep their natural order
+  int perm = 0;
 };
+// weight row that holds natural row r (< 3 d) of [W_q; W_k; W_v] when the q and k rows are
+// pair-interleaved within each head of hd rows (RopeRing::perm)
+__host__ __device__ inline int64_t qkv_perm_row(int64_t r, int64_t d, int hd) {
+  const int64_t part = r / d, c = r % d, h = c / hd, dim = c % hd, half = hd / 2;
+  if (part == 2) return r;
+  return part * d + h * hd + (dim < half ? 2 * dim : 2 * (dim - half) + 1);
+}
 
 struct Epi {
   int kind = EPI_F32;
@@ -82,6 +94,9 @@ hipError_t gemm_simt_f32(const GemmArgs& g, hipStream_t s);   // fp32 operands
 hipError_t gemm_simt_bf16(const GemmArgs& g, hipStream_t s);  // bf16 operands, SIMT
 hipError_t gemm_mfma_bf16(const GemmArgs& g, hipStream_t s);  // bf16 operands, MFMA
 int gemm_mfma_splits(const GemmArgs& g, int* ks_out);          // split-K parts gemm_mfma_bf16 would use
+// whether gemm_mfma_bf16 runs this EPI_QKV_ROPE product in one kernel (matrix-vector form for a
+// handful of rows; wide tiles with rr.perm, d % 256 == 0, n, pos0 and R multiples of 8, hd % 4 == 0)
+bool gemm_mfma_fuses_qkv_rope(const GemmArgs& g);
 // M <= 8 rows per batch (decode), bf16 operands: one read of the weight rows per product;
 // kinds EPI_F32, EPI_T, EPI_ADD_F32 and the SwiGLU kinds without z_g / z_u / act^T outputs,
 // K % 8 == 0, 16-byte aligned operands and 8-element strides (gemv_ok); gemm_mfma_bf16 takes
