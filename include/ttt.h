@@ -227,11 +227,14 @@ int64_t ttt_position(const ttt_ctx* ctx);
  * sum), 7 sliding-window attention forward (one kernel), 8 the same with a split
  * key range (kernel + merge), 9 attention backward (all its kernels), 10 attention
  * of one query per head in generation (the kernel over blocks of window keys; their
- * merge is not timed). */
+ * merge is not timed), 11 the q|k|v product with RoPE and the key/value ring writes in its
+ * epilogue, 12 the lm_head product with the vocabulary-tiled softmax statistics in its
+ * epilogue (the per-row merge after it is not timed). */
 enum {
   TTT_PROF_GEMM_F32 = 0, TTT_PROF_GEMM_BF16 = 1, TTT_PROF_GEMM_RESID = 2, TTT_PROF_GEMM_SWIGLU = 3,
   TTT_PROF_GEMM_SWIGLU_BWD = 4, TTT_PROF_GEMM_SGD = 5, TTT_PROF_GEMM_SPLITK = 6, TTT_PROF_SWA_FWD = 7,
-  TTT_PROF_SWA_FWD_SPLIT = 8, TTT_PROF_SWA_BWD = 9, TTT_PROF_SWA_DECODE = 10, TTT_PROF_CLASSES = 11
+  TTT_PROF_SWA_FWD_SPLIT = 8, TTT_PROF_SWA_BWD = 9, TTT_PROF_SWA_DECODE = 10, TTT_PROF_GEMM_QKV_ROPE = 11,
+  TTT_PROF_GEMM_LM_CE = 12, TTT_PROF_CLASSES = 13
 };
 int ttt_profile_enable(ttt_ctx* ctx, int32_t on);
 int ttt_profile_read(ttt_ctx* ctx, int32_t n_classes, double* ms, int64_t* counts, double* flops);

@@ -29,7 +29,8 @@ EXPORTS = ("ttt_set_allocator", "ttt_create", "ttt_prefill_chunk", "ttt_prefill"
            "ttt_profile_enable", "ttt_profile_read", "ttt_set_fast_weights", "ttt_state_size", "ttt_save_state",
            "ttt_load_state", "ttt_score", "ttt_score_device")
 PROFILE_CLASSES = ("gemm_f32out", "gemm_bf16out", "gemm_resid", "gemm_swiglu", "gemm_swiglu_bwd", "gemm_sgd",
-                   "gemm_splitk", "swa_fwd", "swa_fwd_split", "swa_bwd", "swa_decode")
+                   "gemm_splitk", "swa_fwd", "swa_fwd_split", "swa_bwd", "swa_decode", "gemm_qkv_rope",
+                   "gemm_lm_ce")
 # kernels behind each class (rocprofv3 names); classes marked single=True are one kernel
 PROFILE_KERNELS = {  # class: (kernels, one kernel per launch)
     "gemm_f32out": ("k_gemm_wide<256|128, 0, false> (k_gemm_dl / k_gemm_mfma off the wide-tile shapes)", False),
@@ -45,6 +46,10 @@ PROFILE_KERNELS = {  # class: (kernels, one kernel per launch)
     "swa_bwd": ("k_swa_dq2<hd, *> (k_dvec + k_swa_dq<hd, 8, *> off hd 128) + k_swa_dkv<hd, *>; split parts "
                 "are summed by k_rope_bwd_pack4 outside the class", False),
     "swa_decode": ("k_swa_decode<hd>", True),
+    "gemm_qkv_rope": ("k_gemm_wide<256|128, 6, false> (q|k|v product, RoPE and ring writes in the epilogue; "
+                      "k_gemv for a handful of rows)", False),
+    "gemm_lm_ce": ("k_gemm_wide<256|128, 8, false> (lm_head, vocabulary-tile softmax statistics in the epilogue)",
+                   False),
 }
 
 

@@ -399,6 +399,55 @@ __global__ __launch_bounds__(512) void k_ce_rows4(const float* logits, int V, co
   }
 }
 
+// Rest of the vocabulary-tiled cross-entropy of one row (after an EPI_LM_CE lm_head product):
+// merge the tiles' statistics (maxima m_t, sums s_t of exp(z - m_t)) into lse = M + log sum_t
+// s_t e^(m_t - M), loss = lse - z_y, and rescale the row's exp(z - m_t) in place into
+// dlogits = (e^(z - lse) - [v == y]) / nvalid.  Grid: one block per row.
+template <typename T>
+__global__ __launch_bounds__(256) void k_ce_finalize(const float* part, const float* zt, int64_t M, int V,
+                                                     const int32_t* tgt, int64_t ld, const int* nvalid, int rpb,
+                                                     float* loss_tok, T* e, int* err) {
+  __shared__ float sh[16];
+  __shared__ float scale[1024];  // e^(m_t - lse) / nvalid per vocabulary tile
+  const int64_t m = blockIdx.x;
+  const int b = (int)(m / rpb), t = (int)(m % rpb);
+  const int ntile = (V + 255) / 256;
+  int y = tgt[b * ld + t];
+  if (y < -1 || y >= V) {
+    if (threadIdx.x == 0) atomicOr(err, 2);
+    y = -1;
+  }
+  float mx = -INFINITY;
+  for (int i = threadIdx.x; i < ntile; i += blockDim.x) mx = fmaxf(mx, part[(int64_t)i * 2 * M + m]);
+  const float Mx = block_max(mx, sh);
+  float sm = 0.f;
+  for (int i = threadIdx.x; i < ntile; i += blockDim.x)
+    sm += part[(int64_t)i * 2 * M + M + m] * __expf(part[(int64_t)i * 2 * M + m] - Mx);
+  const float lse = Mx + logf(block_sum(sm, sh));
+  if (threadIdx.x == 0) loss_tok[m] = y >= 0 ? lse - zt[m] : 0.f;
+  if (!e) return;
+  const int nv = nvalid[b];
+  const float inv = nv > 0 ? 1.f / (float)nv : 0.f;
+  for (int i = threadIdx.x; i < ntile; i += blockDim.x)
+    scale[i] = y >= 0 ? __expf(part[(int64_t)i * 2 * M + m] - lse) * inv : 0.f;
+  __syncthreads();
+  T* row = e + m * V;
+  for (int v = 8 * threadIdx.x; v < V; v += 8 * blockDim.x) {  // 8 columns of one tile (V % 8 == 0)
+    const float sc = scale[v / 256];
+    const uint4 in = *(const uint4*)(row + v);
+    const uint32_t w[4] = {in.x, in.y, in.z, in.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      float x0 = bf2f(bf16{(uint16_t)(w[k] & 0xffff)}) * sc, x1 = bf2f(bf16{(uint16_t)(w[k] >> 16)}) * sc;
+      if (v + 2 * k == y) x0 -= inv;
+      if (v + 2 * k + 1 == y) x1 -= inv;
+      o[k] = (uint32_t)f2bf(x0).x | ((uint32_t)f2bf(x1).x << 16);
+    }
+    *(uint4*)(row + v) = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
 __global__ void k_reduce_loss(const float* loss_tok, const int* nvalid, int n, float* out) {
   __shared__ float sh[16];
   int b = blockIdx.x;
@@ -875,6 +924,20 @@ hipError_t ce_rows_ld(const float* logits, int64_t M, int V, const int32_t* tgt,
                        err);
   return hipGetLastError();
 }
+
+template <typename T>
+hipError_t ce_finalize(const float* part, const float* zt, int64_t M, int V, const int32_t* tgt, int64_t ld,
+                       const int* nvalid, int rpb, float* loss_tok, T* e, int* err, hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  if (sizeof(T) != 2 || V % 8 != 0 || (V + 255) / 256 > 1024 || (e && !al16(e))) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_ce_finalize<T>, dim3((unsigned)M), dim3(256), 0, s, part, zt, M, V, tgt, ld, nvalid, rpb,
+                     loss_tok, e, err);
+  return hipGetLastError();
+}
+template hipError_t ce_finalize<bf16>(const float*, const float*, int64_t, int, const int32_t*, int64_t, const int*,
+                                      int, float*, bf16*, int*, hipStream_t);
+template hipError_t ce_finalize<float>(const float*, const float*, int64_t, int, const int32_t*, int64_t,
+                                       const int*, int, float*, float*, int*, hipStream_t);
 
 hipError_t reduce_loss(const float* loss_tok, const int* nvalid, int B, int n, float* loss_out, hipStream_t s) {
   hipLaunchKernelGGL(k_reduce_loss, dim3(B), dim3(256), 0, s, loss_tok, nvalid, n, loss_out);

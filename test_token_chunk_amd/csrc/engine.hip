@@ -105,6 +105,7 @@ struct ttt_ctx {
   float *hb = nullptr, *qkvb = nullptr, *rstd_tmp = nullptr;
   void *ub = nullptr, *qb = nullptr, *ob = nullptr, *actb = nullptr;
   float *htop = nullptr, *rstdf = nullptr, *logits = nullptr, *loss_tok = nullptr;
+  float *ce_part = nullptr, *ce_zt = nullptr;  // vocabulary-tile softmax statistics, target logits
   void *hf = nullptr, *dlogits = nullptr;
   int* nvalid = nullptr;
   float *dh = nullptr, *tmpf = nullptr, *dq = nullptr, *dk = nullptr, *dv = nullptr, *dvec = nullptr;
@@ -198,7 +199,10 @@ int fail(ttt_ctx* c, int code, const std::string& msg) {
 // Classes: GEMMs without split by epilogue kind (EPI_F32 .. EPI_SGD; one kernel each),
 // split-K GEMMs (kernel + ordered reduce), attention forward (one kernel), split-key
 // attention forward (kernel + combine), attention backward (dvec + dq + dk/dv)
-enum { PC_GEMM_SPLITK = 6, PC_SWA_FWD = 7, PC_SWA_FWD_SPLIT = 8, PC_SWA_BWD = 9, PC_SWA_DEC = 10, PC_N = 11 };
+enum {
+  PC_GEMM_SPLITK = 6, PC_SWA_FWD = 7, PC_SWA_FWD_SPLIT = 8, PC_SWA_BWD = 9, PC_SWA_DEC = 10, PC_QKV_ROPE = 11,
+  PC_LM_CE = 12, PC_N = 13
+};
 
 hipEvent_t next_event(ttt_ctx* c) {
   if (c->ev_used == c->ev_pool.size()) {
@@ -271,8 +275,11 @@ struct Ops<bf16> {
     g.ws = st ? nullptr : c->ws;
     g.ws_floats = st ? 0 : c->ws_floats;
     if (!st) st = c->stream;
-    // one SwiGLU class; the q|k|v product with RoPE counts as the fp32-output product it replaces
-    const int kind_cls = g.e.kind == EPI_SWIGLU_IL ? (int)EPI_SWIGLU : g.e.kind == EPI_QKV_ROPE ? (int)EPI_F32 : g.e.kind;
+    // one SwiGLU class; the products with the RoPE and cross-entropy epilogues have their own
+    const int kind_cls = g.e.kind == EPI_SWIGLU_IL  ? (int)EPI_SWIGLU
+                         : g.e.kind == EPI_QKV_ROPE ? (int)PC_QKV_ROPE
+                         : g.e.kind == EPI_LM_CE    ? (int)PC_LM_CE
+                                                    : g.e.kind;
     const int cls = (c->mfma && gemm_mfma_splits(g, nullptr) > 1) ? PC_GEMM_SPLITK : kind_cls;
     return timed(c, cls, gemm_flops(g), st,
                  [&] { return c->mfma ? gemm_mfma_bf16(g, st) : gemm_simt_bf16(g, st); });
@@ -363,6 +370,40 @@ hipError_t norm_bwd(ttt_ctx* c, int S, const float* x, const float* rstd, int64_
                     const float* resid, float* out, T* outT) {
   if (S > 1) return rmsnorm_bwd_parts<T>(x, rstd, M, c->d, g, c->ws, S, M * c->d, resid, out, outT, c->stream);
   return rmsnorm_bwd<T>(x, rstd, M, c->d, g, dy, resid, out, outT, c->stream);
+}
+
+// lm_head over M rows of x (rows of rpb per batch row, targets tgt [B][ld]) and the chunk's
+// cross-entropy per row into loss_tok, with dlogits (T [M][V]) when dl != nullptr; nvalid must
+// be counted.  bf16 matrix cores: one GEMM whose epilogue keeps the softmax statistics of each
+// 256-column vocabulary tile and exp(z - tile max) in dl (or the logits buffer), then a per-row
+// merge that writes the loss and rescales dl in place; otherwise fp32 logits and a row pass.
+template <typename T>
+hipError_t lmhead_ce(ttt_ctx* c, const void* x, int64_t M, const int32_t* tgt, int64_t ld, int rpb, T* dl) {
+  const int d = c->d, V = c->V;
+  GemmArgs gl = mk(x, d, c->lm_head, d, (int)M, V, d);
+  if (c->mfma && c->bf16) {
+    GemmArgs gf = gl;
+    gf.e.kind = EPI_LM_CE;
+    gf.e.c = dl ? (void*)dl : c->logits;  // exp(z - m_t) as bf16 (the fp32 logits buffer is big enough)
+    gf.e.ldc = V;
+    gf.e.tgt = tgt;
+    gf.e.ldtg = ld;
+    gf.e.rpb = rpb;
+    gf.e.ce_part = c->ce_part;
+    gf.e.ce_zt = c->ce_zt;
+    if (gemm_mfma_fuses_lm_ce(gf)) {
+      hipError_t e = Ops<T>::gemm(c, gf);
+      if (e != hipSuccess) return e;
+      return ce_finalize<T>(c->ce_part, c->ce_zt, M, V, tgt, ld, c->nvalid, rpb, c->loss_tok, dl, c->err_dev,
+                            c->stream);
+    }
+  }
+  gl.e.kind = EPI_F32;
+  gl.e.c = c->logits;
+  gl.e.ldc = V;
+  hipError_t e = Ops<T>::gemm(c, gl);
+  if (e != hipSuccess) return e;
+  return ce_rows_ld<T>(c->logits, M, V, tgt, ld, c->nvalid, rpb, c->loss_tok, dl, c->err_dev, c->stream);
 }
 
 template <typename T>
@@ -510,13 +551,8 @@ int top_chunk(ttt_ctx* c, const int32_t* tgt, int64_t ld, const float* hsrc, int
     if (rc) return rc;
   }
   CK(norm_fwd<T>(c, c->htop, M, c->final_norm, tp<T>(c->hf), c->rstdf, (T*)nullptr, n, 0, nullptr));
-  GemmArgs gl = mk(c->hf, d, c->lm_head, d, (int)M, V, d);
-  gl.e.kind = EPI_F32;
-  gl.e.c = c->logits;
-  gl.e.ldc = V;
-  CK(Ops<T>::gemm(c, gl));
   CK(count_valid_ld(tgt, ld, B, n, c->nvalid, c->stream));
-  CK(ce_rows_ld<T>(c->logits, M, V, tgt, ld, c->nvalid, n, c->loss_tok, tp<T>(c->dlogits), c->err_dev, c->stream));
+  CK(lmhead_ce<T>(c, c->hf, M, tgt, ld, n, tp<T>(c->dlogits)));
   CK(reduce_loss(c->loss_tok, c->nvalid, B, n, loss_dev, c->stream));
 
   // backward
@@ -789,19 +825,23 @@ int run_score(ttt_ctx* c, const int32_t* tok, const int32_t* tgt, int64_t ld, in
     CK(norm_fwd<T>(c, c->hb, (int64_t)B * g, c->final_norm, tp<T>(c->ub), c->rstd_tmp, (T*)nullptr, g, 0, nullptr));
     for (int cs = 0; cs < g; cs += b) {
       const int n = std::min(b, g - cs);
-      GemmArgs gl = mk(tp<T>(c->ub, (int64_t)cs * d), d, c->lm_head, d, n, V, d);
-      gl.batch = B;
-      gl.sA = (int64_t)g * d;
-      gl.sB = 0;
-      gl.e.kind = EPI_F32;
-      gl.e.c = c->logits;
-      gl.e.ldc = V;
-      gl.e.sc = (int64_t)n * V;
-      CK(Ops<T>::gemm(c, gl));
       const int32_t* t0 = tgt + done + cs;
       CK(count_valid_ld(t0, ld, B, n, c->nvalid, c->stream));
-      CK(ce_rows_ld<T>(c->logits, (int64_t)B * n, V, t0, ld, c->nvalid, n, c->loss_tok, (T*)nullptr, c->err_dev,
-                       c->stream));
+      if (B == 1) {  // the chunk's rows are contiguous: lm_head and the tiled cross-entropy in one product
+        CK(lmhead_ce<T>(c, tp<T>(c->ub, (int64_t)cs * d), n, t0, ld, n, (T*)nullptr));
+      } else {
+        GemmArgs gl = mk(tp<T>(c->ub, (int64_t)cs * d), d, c->lm_head, d, n, V, d);
+        gl.batch = B;
+        gl.sA = (int64_t)g * d;
+        gl.sB = 0;
+        gl.e.kind = EPI_F32;
+        gl.e.c = c->logits;
+        gl.e.ldc = V;
+        gl.e.sc = (int64_t)n * V;
+        CK(Ops<T>::gemm(c, gl));
+        CK(ce_rows_ld<T>(c->logits, (int64_t)B * n, V, t0, ld, c->nvalid, n, c->loss_tok, (T*)nullptr, c->err_dev,
+                         c->stream));
+      }
       CK(reduce_loss(c->loss_tok, c->nvalid, B, n, loss_dev + ci * B, c->stream));
       ++ci;
     }
@@ -1040,6 +1080,8 @@ int build(ttt_ctx* c, const ttt_weights* w) {
   AL(c->loss_tok, rows_top * 4);
   AL(c->hf, rows_top * d * es);
   AL(c->dlogits, rows_top * V * es);
+  AL(c->ce_part, rows_top * 2 * cdiv(V, 256) * 4);
+  AL(c->ce_zt, rows_top * 4);
   AL(c->nvalid, B * 4);
   AL(c->loss_later, B * 4);
   AL(c->dh, rows_top * d * 4);

@@ -562,6 +562,7 @@ template <int BM, int EK>
 constexpr size_t wide_lds_bytes() {
   const size_t ops = (size_t)WideCfg<BM>::ST * WideCfg<BM>::SBYTES;
   const int ntr = EK == EPI_SWIGLU_BWD ? 2 : (EK == EPI_SGD || EK == EPI_SWIGLU_IL || EK == EPI_QKV_ROPE) ? 1 : 0;
+  // (EPI_LM_CE reduces through 2 x 4 x BM floats, well within the operand ring)
   const size_t trb = (size_t)ntr * 256 * (BM + 8) * 2;
   return ops > trb ? ops : trb;
 }
@@ -587,6 +588,62 @@ __device__ __forceinline__ void wide_epilogue(const GemmArgs& g, f32x16 (&acc)[T
     return make_uint2((uint32_t)f2bf(a).x | ((uint32_t)f2bf(b).x << 16),
                       (uint32_t)f2bf(c).x | ((uint32_t)f2bf(d).x << 16));
   };
+  if constexpr (EK == EPI_LM_CE) {
+    // Vocabulary tile n0 / 256 of the lm_head logits: for each row the maximum m_t of its 256
+    // columns and the sum of exp(z - m_t) (fp32, reduced over the lane pair and the 4 column
+    // waves through LDS), exp(z - m_t) stored as T, and the fp32 logit of the row's target if
+    // it falls in this tile.  Waves: wid / 4 picks the row half, wid % 4 the 64-column group.
+    static_assert(NT == 512, "2 x 4 waves");
+    float* red = reinterpret_cast<float*>(smem_raw);  // [2][4][BM]: column-group maxima, then sums
+    const int wc = wn0 / 64, tn = n0 / BN;
+    float mx[TM];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      float v = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) v = fmaxf(v, acc[i][j][r]);
+      v = fmaxf(v, __shfl_xor(v, 32, 64));
+      if (hi == 0) red[wc * BM + wm0 + i * 32 + lr] = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int ml = wm0 + i * 32 + lr, m = m0 + ml;
+      mx[i] = fmaxf(fmaxf(red[ml], red[BM + ml]), fmaxf(red[2 * BM + ml], red[3 * BM + ml]));
+      const int y = e.tgt[(int64_t)(m / e.rpb) * e.ldtg + m % e.rpb];
+      float sum = 0.f;
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int n = n0 + wn0 + j * 32 + 8 * q + 4 * hi;
+          float x[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float z = acc[i][j][4 * q + r];
+            x[r] = __expf(z - mx[i]);
+            sum += x[r];
+            if (n + r == y) e.ce_zt[m] = z;
+          }
+          *(uint2*)((bf16*)e.c + (int64_t)m * e.ldc + n) = pk4(x[0], x[1], x[2], x[3]);
+        }
+      sum += __shfl_xor(sum, 32, 64);
+      if (hi == 0) red[4 * BM + wc * BM + ml] = sum;
+    }
+    __syncthreads();
+    if (wc == 0 && hi == 0) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int ml = wm0 + i * 32 + lr, m = m0 + ml;
+        const float sm = (red[4 * BM + ml] + red[5 * BM + ml]) + (red[6 * BM + ml] + red[7 * BM + ml]);
+        e.ce_part[(int64_t)tn * 2 * g.M + m] = mx[i];
+        e.ce_part[(int64_t)tn * 2 * g.M + g.M + m] = sm;
+      }
+    }
+    return;
+  }
   if constexpr (EK == EPI_QKV_ROPE) {
     // [q|k|v] product with pair-interleaved q/k columns (a tile lies in one part): a lane's four
     // columns of a q or k head are dims (i, i + hd/2, i + 1, i + 1 + hd/2), rotated in registers at
@@ -1135,6 +1192,9 @@ bool wide_ok(const GemmArgs& g) {
     case EPI_SWIGLU_BWD:
       return e.ldc % 4 == 0 && e.sc % 4 == 0 && e.f % 4 == 0 && al(e.c, 8) && e.ldz % 4 == 0 && e.sz % 4 == 0 &&
              al(e.zg, 8) && al(e.zu, 8) && e.t && e.ldt % 8 == 0 && e.st % 8 == 0 && al(e.t, 16);
+    case EPI_LM_CE:
+      return g.batch == 1 && e.ldc % 4 == 0 && al(e.c, 8) && e.tgt && e.rpb > 0 && g.M % e.rpb == 0 && e.ce_part &&
+             e.ce_zt;
     case EPI_QKV_ROPE: {
       // a 256-column tile inside one of q, k, v; RoPE pairs in a lane's 4-column group; 8-token
       // groups of a tile inside one batch row and one run of ring slots (16-byte transposed stores)
@@ -1186,6 +1246,12 @@ GemmPlan gemm_plan(const GemmArgs& g) {
 
 }  // namespace
 
+bool gemm_mfma_fuses_lm_ce(const GemmArgs& g) {
+  if (g.e.kind != EPI_LM_CE || g.M <= 0) return false;
+  if (!(aligned16(g.A) && aligned16(g.B) && g.lda % 8 == 0 && g.ldb % 8 == 0)) return false;
+  return wide_ok(g);
+}
+
 bool gemm_mfma_fuses_qkv_rope(const GemmArgs& g) {
   if (g.e.kind != EPI_QKV_ROPE || g.M <= 0) return false;
   if (!(aligned16(g.A) && aligned16(g.B) && g.lda % 8 == 0 && g.ldb % 8 == 0)) return false;
@@ -1220,10 +1286,12 @@ hipError_t gemm_mfma_bf16(const GemmArgs& g, hipStream_t s) {
       case EPI_SGD: return launch_wide_bm<EPI_SGD>(g, bm, s);
       case EPI_SWIGLU_BWD: return launch_wide<128, EPI_SWIGLU_BWD, false>(g, 1, s);
       case EPI_QKV_ROPE: return launch_wide_bm<EPI_QKV_ROPE>(g, bm, s);
+      case EPI_LM_CE: return launch_wide_bm<EPI_LM_CE>(g, bm, s);
       default: break;
     }
   }
-  if (g.e.kind == EPI_QKV_ROPE) return hipErrorInvalidValue;  // (gemm_mfma_fuses_qkv_rope said no)
+  // (gemm_mfma_fuses_qkv_rope / gemm_mfma_fuses_lm_ce said no)
+  if (g.e.kind == EPI_QKV_ROPE || g.e.kind == EPI_LM_CE) return hipErrorInvalidValue;
   if (p.kern == 1) {
     switch (g.e.kind) {
       case EPI_SWIGLU_IL: return launch_dl<EPI_SWIGLU_IL, false>(g, 1, s);

@@ -18,9 +18,14 @@ enum EpiKind {
                     // at pos0 + m % n; q (q^T) and the ring slots of k (K^T), v, V^T written as in
                     // rope_qkv_f32in; the matrix-vector kernel (gemv_ok) or, with pair-interleaved
                     // q/k columns (rr.perm), the wide matrix-core tiles (gemm_mfma_fuses_qkv_rope)
-  EPI_SWIGLU_IL = 7 // single operand with gate/up rows interleaved in groups of 32 (see swiglu_il_row):
+  EPI_SWIGLU_IL = 7, // single operand with gate/up rows interleaved in groups of 32 (see swiglu_il_row):
                     // columns 64g..64g+31 are gate rows 32g.., 64g+32..64g+63 the matching up rows;
                     // outputs as EPI_SWIGLU with N = 2f (act, z_g, z_u [m][f], act^T)
+  EPI_LM_CE = 8     // acc = logits z [m][v] of the lm_head (wide tiles, batch 1, N % 256 == 0): the
+                    // softmax statistics of each row over each 256-column vocabulary tile (max m_t
+                    // and sum of exp(z - m_t): ce_part [N/256][2][M]), exp(z - m_t) as T in c, and the
+                    // target's logit z[m][y_m] in ce_zt [M] (targets tgt [B][ldtg], rows of rpb);
+                    // ce_finalize turns c into dlogits in place
 };
 
 // row of the interleaved [gate; up] weight that holds row r (< 2f) of the stacked [W_gate; W_up]
@@ -75,6 +80,12 @@ struct Epi {
   float lr = 0.f;
   int64_t il_f = 0;  // EPI_SGD: > 0 writes the row-major shadow with gate/up rows interleaved (f = il_f)
   RopeRing rr;
+  // EPI_LM_CE extras
+  const int32_t* tgt = nullptr;
+  int64_t ldtg = 0;
+  int rpb = 0;
+  float* ce_part = nullptr;
+  float* ce_zt = nullptr;
 };
 
 struct GemmArgs {
@@ -141,6 +152,15 @@ template <typename T>
 hipError_t convert_rows(const float* x, int64_t M, int d, T* y, T* yT, int rows_per_batch, int64_t ldT,
                         hipStream_t s);
 hipError_t count_valid_ld(const int32_t* tgt, int64_t ld, int B, int n, int* nvalid, hipStream_t s);
+// whether gemm_mfma_bf16 runs this lm_head product with the EPI_LM_CE epilogue
+bool gemm_mfma_fuses_lm_ce(const GemmArgs& g);
+// the rest of the vocabulary-tiled cross-entropy after an EPI_LM_CE product: per row, merges the
+// tiles' (max, exp-sum) into logsumexp (online softmax), loss_tok[m] = lse - z[m][y] (0 for an
+// ignored target), and turns the row of exp(z - m_t) in e into dlogits = (softmax - onehot) /
+// nvalid in place (e == nullptr: the losses only)
+template <typename T>
+hipError_t ce_finalize(const float* part, const float* zt, int64_t M, int V, const int32_t* tgt, int64_t ld,
+                       const int* nvalid, int rows_per_batch, float* loss_tok, T* e, int* err, hipStream_t s);
 // cross-entropy of full logit rows: loss_tok[m] and dlogits = (softmax - onehot) / nvalid (T;
 // dlogits == nullptr: the losses only)
 template <typename T>
