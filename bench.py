@@ -58,6 +58,18 @@ def flops_per_row(c: dict, T: int) -> dict:
     return out
 
 
+def flops_forward(c: dict, T: int) -> int:
+    """Algorithmic FLOPs of the forward only (every block, lm_head) over T tokens: the comparator
+    with no test-time training."""
+    L, d, f, V, k, b = c["n_layers"], c["d_model"], c["d_ff"], c["vocab"], c["window"], c["chunk"]
+    total = 0
+    for p0 in range(0, T, b):
+        n = min(b, T - p0)
+        A = sum(min(k, t + 1) for t in range(p0, p0 + n))
+        total += n * (L * (8 * d * d + 6 * d * f) + 2 * d * V) + 4 * L * d * A
+    return total
+
+
 def host_cpu() -> tuple:
     """(CPU model from lscpu, CPUs this process may run on)."""
     import subprocess
@@ -134,8 +146,11 @@ def main():
     ap.add_argument("--window", type=int, default=0, help="override the attention window k (keys per query)")
     ap.add_argument("--cpu-sample", type=int, default=32, help="oracle sample size in tokens (0 = skip)")
     ap.add_argument("--lookahead", type=int, default=0, help="chunks per batched lower-block pass (0 = library default)")
-    ap.add_argument("--workload", default="prefill", choices=("prefill", "decode"),
-                    help="decode: greedy generation after a full window, an inner-loop update every chunk")
+    ap.add_argument("--workload", default="prefill", choices=("prefill", "decode", "full-attention"),
+                    help="decode: greedy generation after a full window, an inner-loop update every chunk; "
+                         "full-attention: forward and loss only with the window covering the whole sequence "
+                         "(no test-time training), timed beside the TTT prefill step")
+    ap.add_argument("--n-steps", type=int, default=0, help="SGD steps per chunk (0 = library default, one)")
     ap.add_argument("--decode-tokens", type=int, default=1024, help="decode: generated tokens per step")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device-to-device copy 3 times (reference for HBM byte counters)")
@@ -160,6 +175,8 @@ def main():
 
     if args.workload == "decode":
         return decode_bench(args)
+    if args.workload == "full-attention":
+        return full_attention_bench(args)
     c = dict(CONFIGS[args.config])
     T = args.tokens or c.pop("T")
     c.pop("T", None)
@@ -171,7 +188,7 @@ def main():
     w = synth.weights(synth.Shape(c["n_layers"], c["d_model"], c["n_heads"], c["d_ff"], c["vocab"]),
                       bf16=c["dtype"] == "bf16")
     seq = synth.tokens(1, T + 1, c["vocab"], dist)
-    cfg = TTTConfig(batch=1, max_positions=T + 8, lookahead=args.lookahead, **c)
+    cfg = TTTConfig(batch=1, max_positions=T + 8, lookahead=args.lookahead, n_steps=args.n_steps, **c)
     ctx = TTTContext(cfg, w)
     d_tok = torch.tensor(seq[:, :T], dtype=torch.int32, device="cuda")
     d_tgt = torch.tensor(seq[:, 1:], dtype=torch.int32, device="cuda")
@@ -212,6 +229,14 @@ def main():
     ms = dt / args.steps * 1e3
     tok_s = T / (ms / 1e3)
     F = flops_per_row(c, T)
+    if args.n_steps > 1:
+        # each further step repeats the chunk's forward from block l0's MLP up (the attention half of
+        # block l0 and everything below it is not recomputed), the lm_head, the backward and the update
+        top = flops_per_row(dict(c, n_layers=c["n_fast"]), T)
+        d, k, b = c["d_model"], c["window"], c["chunk"]
+        l0_attn = sum(8 * d * d * min(b, T - p0) + 4 * d * sum(min(k, t + 1) for t in range(p0, min(T, p0 + b)))
+                      for p0 in range(0, T, b))
+        F["total"] += (args.n_steps - 1) * (top["total"] - l0_attn)
     peak = PEAK_BF16 if c["dtype"] == "bf16" else PEAK_F32
 
     # roofline of the class with the most device time, from its launches inside the timed region:
@@ -241,9 +266,11 @@ def main():
         "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms, 2), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": c["dtype"], "data": "synthetic",
-        "config": {"workload": f"ttt-prefill-{args.config}", "layers": c["n_layers"], "d_model": c["d_model"],
-                   "tokens": T, "window": c["window"], "chunk": c["chunk"], "fast_blocks": c["n_fast"], "batch": 1,
-                   "token_dist": dist},
+        "config": {"workload": f"ttt-prefill-{args.config}" + (f"-k{c['window']}" if args.window else "") +
+                   (f"-steps{args.n_steps}" if args.n_steps > 1 else ""), "layers": c["n_layers"],
+                   "d_model": c["d_model"], "tokens": T, "window": c["window"], "chunk": c["chunk"],
+                   "fast_blocks": c["n_fast"], "batch": 1, "token_dist": dist,
+                   "sgd_steps_per_chunk": max(1, args.n_steps)},
         "flops_per_step": F["total"], "mfma_peak_frac": round(F["total"] / (ms / 1e3) / peak, 4),
         "final_chunk_loss": float(losses[-1]), "first_chunk_loss": float(losses[0]),
         "roofline": roof,
@@ -254,6 +281,79 @@ def main():
     }
     if args.cpu_sample > 0:
         out["cpu_baseline"] = cpu_baseline(c, w, seq, args.cpu_sample)
+    print(json.dumps(out))
+
+
+def full_attention_bench(args):
+    """The comparator of the pages' latency claim: the same model and sequence with the window
+    covering every position (full causal attention) and no test-time training -- forward and
+    loss only (ttt_score_device) -- timed beside the TTT prefill step at the configuration's
+    window.  value = tokens/s of the full-attention forward; ttt_over_full = the TTT step's time
+    over the full-attention forward's."""
+    import torch
+
+    from test_token_chunk_amd import TTTConfig, TTTContext, synth
+
+    c = dict(CONFIGS[args.config])
+    T = args.tokens or c.pop("T")
+    c.pop("T", None)
+    dist = c.pop("dist")
+    if args.window:
+        c["window"] = args.window
+    torch.cuda.set_device(0)
+    w = synth.weights(synth.Shape(c["n_layers"], c["d_model"], c["n_heads"], c["d_ff"], c["vocab"]),
+                      bf16=c["dtype"] == "bf16")
+    seq = synth.tokens(1, T + 1, c["vocab"], dist)
+    d_tok = torch.tensor(seq[:, :T], dtype=torch.int32, device="cuda")
+    d_tgt = torch.tensor(seq[:, 1:], dtype=torch.int32, device="cuda")
+    nch = (T + c["chunk"] - 1) // c["chunk"]
+    d_loss = torch.zeros(nch, 1, dtype=torch.float32, device="cuda")
+
+    def timed(ctx, fn, label):
+        def step():
+            ctx.reset()
+            fn(ctx)
+            ctx.sync()
+        for i in range(args.warmup):
+            step()
+            print(f"{label} warmup step {i} done", file=sys.stderr, flush=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step()
+            print(f"{label} step {i} done", file=sys.stderr, flush=True)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / args.steps
+
+    full = dict(c, window=T)
+    ctx = TTTContext(TTTConfig(batch=1, max_positions=T + 8, lookahead=args.lookahead, **full), w)
+    t_full = timed(ctx, lambda x: x.score_device(d_tok, d_tgt, d_loss), "full-attention")
+    full_losses = d_loss[:, 0].cpu().numpy()
+    ctx.close()
+    del ctx
+    torch.cuda.empty_cache()
+    ctx = TTTContext(TTTConfig(batch=1, max_positions=T + 8, lookahead=args.lookahead, **c), w)
+    t_ttt = timed(ctx, lambda x: x.prefill_device(d_tok, d_tgt, d_loss), "ttt")
+    ttt_losses = d_loss[:, 0].cpu().numpy()
+    ctx.close()
+    F_full = flops_forward(full, T)
+    F_ttt = flops_per_row(c, T)["total"]
+    out = {
+        "metric": "full-attention forward tokens/s (no test-time training) and TTT/full latency ratio",
+        "value": round(T / t_full, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(t_full * 1e3, 2), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": c["dtype"], "data": "synthetic",
+        "config": {"workload": f"full-attention-vs-ttt-{args.config}", "layers": c["n_layers"],
+                   "d_model": c["d_model"], "tokens": T, "ttt_window": c["window"], "chunk": c["chunk"],
+                   "fast_blocks": c["n_fast"], "batch": 1, "token_dist": dist},
+        "full_attention": {"ms": round(t_full * 1e3, 2), "flops": F_full,
+                           "mfma_peak_frac": round(F_full / t_full / PEAK_BF16, 4),
+                           "mean_chunk_loss": float(full_losses.mean())},
+        "ttt_prefill": {"ms": round(t_ttt * 1e3, 2), "flops": F_ttt, "mfma_peak_frac": round(F_ttt / t_ttt / PEAK_BF16, 4),
+                        "mean_chunk_loss": float(ttt_losses.mean())},
+        "ttt_over_full_latency": round(t_ttt / t_full, 4),
+        "ttt_over_full_flops": round(F_ttt / F_full, 4),
+    }
     print(json.dumps(out))
 
 
@@ -323,7 +423,8 @@ def decode_bench(args):
         "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 2),
         "ms_per_token": round(ms / n_new, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": c["dtype"], "data": "synthetic",
-        "config": {"workload": f"ttt-decode-{args.config}", "layers": c["n_layers"], "d_model": c["d_model"],
+        "config": {"workload": f"ttt-decode-{args.config}" + (f"-k{k}" if args.window else ""), "layers": c["n_layers"],
+                   "d_model": c["d_model"],
                    "window": k, "chunk": b, "fast_blocks": c["n_fast"], "batch": 1, "tokens_per_step": n_new,
                    "update_every": upd, "prefill_tokens": P, "token_dist": dist},
         "last_update_loss": losses[-1], "roofline": roof,
