@@ -630,6 +630,7 @@ int top_chunk(ttt_ctx* c, const int32_t* tgt, int64_t ld, const float* hsrc, int
     g2.e.ldshT = d;
     g2.e.sshT = (int64_t)f * d;
     g2.e.lr = lr;
+    g2.background = on_side;
     CK(Ops<T>::gemm(c, g2, sg));
     // [dW_gate; dW_up] = dz^T m, fused SGD step
     GemmArgs g4 = mk(dzT, b, a.mT, b, 2 * f, d, n);
@@ -648,6 +649,7 @@ int top_chunk(ttt_ctx* c, const int32_t* tgt, int64_t ld, const float* hsrc, int
     g4.e.sshT = 2LL * d * f;
     g4.e.lr = lr;
     g4.e.il_f = c->il ? f : 0;
+    g4.background = on_side;
     CK(Ops<T>::gemm(c, g4, sg));
     if (j == 0) break;
     const LayerW& lw = c->lw[l];

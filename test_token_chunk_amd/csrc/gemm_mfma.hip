@@ -647,15 +647,21 @@ __device__ __forceinline__ void wide_epilogue(const GemmArgs& g, f32x16 (&acc)[T
   if constexpr (EK == EPI_QKV_ROPE) {
     // [q|k|v] product with pair-interleaved q/k columns (a tile lies in one part): a lane's four
     // columns of a q or k head are dims (i, i + hd/2, i + 1, i + 1 + hd/2), rotated in registers at
-    // the row's position and stored as bf16 pairs; v columns are natural.  Rows go to q
-    // [B][H][n][hd] or to ring slot pos % R of K / V [B][H][R][hd]; the transposed copy (q^T, K^T,
-    // V^T, where wanted) is staged through LDS by tile column and stored as 8-token segments.
+    // the row's position; v columns are natural.  Rows go to q [B][H][n][hd] or to ring slot
+    // pos % R of K / V [B][H][R][hd]; the transposed copy (q^T, K^T, V^T, where wanted) is staged
+    // through LDS by tile column and stored as 8-token segments.  When the tile holds whole heads
+    // (hd divides 256) the rows are staged through LDS too and stored as 16-byte segments of whole
+    // rows (written directly, a 128-byte line of a q or k row would collect 4-byte pieces from two
+    // waves: partial-line writes that the L2 fetches and writes back).
     const RopeRing& rr = e.rr;
     const int hd = rr.hd, half = hd / 2, dm = rr.H * hd;
     const int part = n0 / dm;
     bf16* const rows = (bf16*)(part == 0 ? rr.q : part == 1 ? rr.kr : rr.vr);
     bf16* const tdst = (bf16*)(part == 0 ? rr.qt : part == 1 ? rr.ktr : rr.vtr);
     const int s0 = (int)(rr.pos0 % rr.R);
+    const bool staged = BN % hd == 0;
+    constexpr int SLD = BN + 8;
+    bf16* const st = reinterpret_cast<bf16*>(smem_raw);  // staged rows [BM][SLD], by natural tile column
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       const int ml = wm0 + i * 32 + lr, m = m0 + ml;
@@ -670,30 +676,70 @@ __device__ __forceinline__ void wide_epilogue(const GemmArgs& g, f32x16 (&acc)[T
         for (int q = 0; q < 4; ++q) {
           const int nl = wn0 + j * 32 + 8 * q + 4 * hi, c = n0 + nl - part * dm;
           const int h = c / hd, jj = c % hd;
-          const int64_t bh = (int64_t)b * rr.H + h;
-          bf16* row = rows + (part == 0 ? bh * rr.n + t : bh * rr.R + slot) * hd;
           float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-          if (part < 2) {
+          if (part < 2) {  // rotate; the pairs become (lo0, hi0, lo1, hi1), kept in acc for the transposed copy
             const int i0 = jj / 2;
             const float2 cc = *(const float2*)(cs + i0), ss = *(const float2*)(sn + i0);
             const float lo0 = v[0] * cc.x - v[1] * ss.x, hi0 = v[1] * cc.x + v[0] * ss.x;
             const float lo1 = v[2] * cc.y - v[3] * ss.y, hi1 = v[3] * cc.y + v[2] * ss.y;
-            *(uint32_t*)(row + i0) = (uint32_t)f2bf(lo0).x | ((uint32_t)f2bf(lo1).x << 16);
-            *(uint32_t*)(row + i0 + half) = (uint32_t)f2bf(hi0).x | ((uint32_t)f2bf(hi1).x << 16);
             v[0] = lo0;
             v[1] = hi0;
             v[2] = lo1;
             v[3] = hi1;
-          } else {
-            *(uint2*)(row + jj) = pk4(v[0], v[1], v[2], v[3]);
+            acc[i][j][4 * q] = lo0;
+            acc[i][j][4 * q + 1] = hi0;
+            acc[i][j][4 * q + 2] = lo1;
+            acc[i][j][4 * q + 3] = hi1;
           }
-          if (tdst) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) tr0[(nl + r) * TLD + ml] = f2bf(v[r]);
+          const uint32_t plo = (uint32_t)f2bf(v[0]).x | ((uint32_t)f2bf(v[2]).x << 16);
+          const uint32_t phi = (uint32_t)f2bf(v[1]).x | ((uint32_t)f2bf(v[3]).x << 16);
+          if (staged) {
+            bf16* srow = st + ml * SLD + (nl - jj);
+            if (part < 2) {
+              *(uint32_t*)(srow + jj / 2) = plo;
+              *(uint32_t*)(srow + jj / 2 + half) = phi;
+            } else {
+              *(uint2*)(srow + jj) = pk4(v[0], v[1], v[2], v[3]);
+            }
+          } else {
+            const int64_t bh = (int64_t)b * rr.H + h;
+            bf16* row = rows + (part == 0 ? bh * rr.n + t : bh * rr.R + slot) * hd;
+            if (part < 2) {
+              *(uint32_t*)(row + jj / 2) = plo;
+              *(uint32_t*)(row + jj / 2 + half) = phi;
+            } else {
+              *(uint2*)(row + jj) = pk4(v[0], v[1], v[2], v[3]);
+            }
           }
         }
     }
+    if (staged) {
+      __syncthreads();
+      constexpr int SEG = BN / 8;  // 16-byte segments per staged row
+      const int h0 = (n0 - part * dm) / hd;
+      for (int cidx = tid; cidx < BM * SEG; cidx += NT) {
+        const int ml = cidx / SEG, cs8 = (cidx % SEG) * 8;
+        const int m = m0 + ml, b = m / rr.n, t = m % rr.n;
+        const int sl = s0 + t >= rr.R ? s0 + t - rr.R : s0 + t;
+        const int64_t bh = (int64_t)b * rr.H + h0 + cs8 / hd;
+        bf16* row = rows + (part == 0 ? bh * rr.n + t : bh * rr.R + sl) * hd + cs8 % hd;
+        *(uint4*)row = *(const uint4*)(st + ml * SLD + cs8);
+      }
+    }
     if (!tdst) return;  // (the same for the whole block)
+    if (staged) __syncthreads();  // the staged rows have been read: the LDS takes the transposed tile
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int ml = wm0 + i * 32 + lr;
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int nl = wn0 + j * 32 + 8 * q + 4 * hi;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) tr0[(nl + r) * TLD + ml] = f2bf(acc[i][j][4 * q + r]);  // pair-interleaved order
+        }
+    }
     __syncthreads();
     constexpr int CH = BM / 8;
     for (int cidx = tid; cidx < BN * CH; cidx += NT) {
@@ -1025,11 +1071,15 @@ hipError_t launch_dl_st(const GemmArgs& g, int S, hipStream_t s) {
 
 template <int EK, bool SPLIT>
 hipError_t launch_dl(const GemmArgs& g, int S, hipStream_t s) {
-  static int stages = -1;
+  static int stages = -1;  // TTT_GEMM_STAGES (tuning switch) or 0 = by role
   if (stages < 0) {
     const char* e = getenv("TTT_GEMM_STAGES");
-    stages = e ? atoi(e) : 2;
+    stages = e ? atoi(e) : 0;
   }
+  // background work: three stages (96 KB of LDS, one block per CU), which leaves the other
+  // half of each CU's block slots to the latency-bound kernels of the main stream (3B step, same
+  // box: 2016 -> 1970 ms although the weight-gradient GEMMs themselves take twice as long)
+  if (stages == 0 && g.background) return launch_dl_st<EK, SPLIT, 3>(g, S, s);
   if (stages == 4) return launch_dl_st<EK, SPLIT, 4>(g, S, s);
   if (stages == 3) return launch_dl_st<EK, SPLIT, 3>(g, S, s);
   return launch_dl_st<EK, SPLIT, 2>(g, S, s);

@@ -99,6 +99,9 @@ struct GemmArgs {
   float* ws = nullptr;    // optional fp32 workspace: lets small-grid GEMMs split K (EPI_F32/EPI_T/EPI_ADD_F32)
   int64_t ws_floats = 0;
   bool defer = false;     // a K split leaves its fp32 parts in ws ([S][batch][M][N]) for the caller to sum
+  // runs on a side stream beside latency-bound work: take the form that holds fewer resources per
+  // CU (the fused-SGD 128 x 128 loop with three LDS stages: one block per CU instead of two)
+  bool background = false;
 };
 
 hipError_t gemm_simt_f32(const GemmArgs& g, hipStream_t s);   // fp32 operands
