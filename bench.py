@@ -39,6 +39,7 @@ CONFIGS = {
 }
 PEAK_BF16 = 2.5e15  # MI355X dense bf16 MFMA, FLOP/s
 PEAK_F32 = 157.3e12
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, GB/s
 
 
 def flops_per_row(c: dict, T: int) -> dict:
@@ -56,6 +57,23 @@ def flops_per_row(c: dict, T: int) -> dict:
         out["upd"] += 6 * d * f * Lq
     out["total"] = sum(out.values())
     return out
+
+
+def sgd_bytes_per_row(c: dict, T: int, n_steps: int = 1) -> int:
+    """Algorithmic HBM bytes of the weight-gradient products with the fused SGD step over T tokens:
+    per fast parameter and step the fp32 master is read and written and one bf16 copy written
+    (10 B); the operands (the chunk's output gradients and the saved inputs of the three fast
+    matrices, bf16) are read once.  This work is below the ridge point (about 205 FLOP/B at the
+    3B shape), so it is priced against HBM bandwidth."""
+    d, f, b, Lq = c["d_model"], c["d_ff"], c["chunk"], c["n_fast"]
+    total = 0
+    for p0 in range(0, T, b):
+        n = min(b, T - p0)
+        total += Lq * (3 * d * f * 10 + (3 * f + 2 * d) * n * 2)
+    return total * max(1, n_steps)
+
+
+HBM_CLASSES = ("gemm_sgd",)  # profile classes priced in bytes, not FLOPs
 
 
 def flops_forward(c: dict, T: int) -> int:
@@ -255,12 +273,24 @@ def main():
                 "avg_launch_us": round(avg_s * 1e6, 2), "launches_per_step": st["count"] // args.steps,
                 "gflop_per_launch": round(flops_per_launch / 1e9, 3),
                 "share_of_device_time": round(kstats[name]["ms"] / sum(v["ms"] for v in kstats.values()), 4)}
+        if name in HBM_CLASSES:
+            # bytes per launch: the step's algorithmic bytes of the class over its launches per step
+            bytes_per_launch = sgd_bytes_per_row(c, T, args.n_steps) / max(st["count"] // args.steps, 1)
+            gbs = bytes_per_launch / avg_s / 1e9
+            roof.update({"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4), "mb_per_launch": round(bytes_per_launch / 1e6, 2),
+                         "mfma_tflops": round(achieved, 1)})
     total_dev = sum(v["ms"] for v in kstats.values())
     top = sorted(kstats.items(), key=lambda kv: -kv[1]["ms"])[:6]
     kernel_top = [{"class": k, "kernels": PROFILE_KERNELS[k][0].replace("hd", str(hd)),
                    "ms_per_step": round(v["ms"], 2), "share": round(v["ms"] / total_dev, 4),
                    "tflops": round(v["flops"] / max(v["ms"], 1e-9) / 1e9, 1),
                    "frac": round(v["flops"] / max(v["ms"], 1e-9) / 1e9 / (peak / 1e12), 4)} for k, v in top]
+    for e in kernel_top:
+        if e["class"] in HBM_CLASSES:
+            gbs = sgd_bytes_per_row(c, T, args.n_steps) / (e["ms_per_step"] / 1e3) / 1e9
+            e.update({"bound": "hbm", "gbps": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4),
+                      "mfma_frac": e["frac"]})
     out = {
         "metric": "TTT prefill tokens/s (fwd+inner-loop bwd+update) and % bf16 MFMA peak",
         "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -415,7 +445,7 @@ def decode_bench(args):
         byts = 2 * k * H * hd * 2 + H * hd * 2 + S * H * (hd + 2) * 4
         avg_s = st["ms"] / st["count"] / 1e3
         roof = {"kernel": PROFILE_KERNELS["swa_decode"][0].replace("hd", str(hd)), "class": "swa_decode",
-                "bound": "hbm", "achieved": round(byts / avg_s / 1e9, 1), "peak": 8000.0, "unit": "GB/s",
+                "bound": "hbm", "achieved": round(byts / avg_s / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(byts / avg_s / 8e12, 4), "traffic": None, "avg_launch_us": round(avg_s * 1e6, 2),
                 "launches_per_step": st["count"] // args.steps, "mb_per_launch": round(byts / 1e6, 2)}
     out = {

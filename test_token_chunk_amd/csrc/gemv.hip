@@ -70,6 +70,7 @@ __global__ __launch_bounds__(256) void k_gemv(GemmArgs g, int ncols, int f) {
   constexpr bool SW = KIND == EPI_SWIGLU || KIND == EPI_SWIGLU_IL;
   constexpr bool RP = KIND == EPI_QKV_ROPE;  // NR == 2: the pair (i, i + hd/2); ncols = pairs
   constexpr int RW = SW ? 2 * NR : NR;  // weight rows per wave
+  static_assert(!RP || NR == 2, "a RoPE wave holds the two rows of one rotation pair");
   constexpr int U = MR <= 2 ? 4 : 2;    // 512-element steps per trip
   const int lane = threadIdx.x & 63;
   const int64_t wv = (int64_t)blockIdx.x * GW + (threadIdx.x >> 6);
@@ -178,6 +179,9 @@ hipError_t launch_gemv(const GemmArgs& g, int ncols, int f, hipStream_t s) {
 }
 
 template <int KIND>
+hipError_t gemv_cols(const GemmArgs& g, hipStream_t s);
+
+template <int KIND>
 hipError_t gemv_kind(const GemmArgs& g, hipStream_t s) {
   if constexpr (KIND == EPI_QKV_ROPE) {
     const int pairs = g.N / 2;
@@ -185,7 +189,13 @@ hipError_t gemv_kind(const GemmArgs& g, hipStream_t s) {
     if (g.M == 2) return launch_gemv<2, 2, KIND>(g, pairs, 0, s);
     if (g.M <= 4) return launch_gemv<4, 2, KIND>(g, pairs, 0, s);
     return launch_gemv<8, 2, KIND>(g, pairs, 0, s);
+  } else {
+    return gemv_cols<KIND>(g, s);
   }
+}
+
+template <int KIND>
+hipError_t gemv_cols(const GemmArgs& g, hipStream_t s) {
   const bool sw = KIND == EPI_SWIGLU || KIND == EPI_SWIGLU_IL;
   const int ncols = KIND == EPI_SWIGLU_IL ? g.N / 2 : g.N;
   const int f = sw ? ncols : 0;
