@@ -6,9 +6,12 @@ oracle shares no code with the HIP path.
 
 The configuration is any object with the attributes n_layers, d_model,
 n_heads, d_ff, vocab, window, chunk, n_fast, batch, rope_theta, rms_eps, lr
-(and optionally n_steps, SGD steps per chunk, default 1).
+(and optionally n_steps, SGD steps per chunk, default 1, and dual_mlp, a static
+plus a dynamic MLP in every updated block, default 0).
 Weights are the dict of fp32 numpy arrays produced by the seeded generator
-(row-major [out, in]); they must stay alive as long as the Oracle does.
+(row-major [out, in]); with dual_mlp it also holds dyn_gate, dyn_up, dyn_down,
+lists of n_fast arrays (the dynamic MLPs' initial weights).  They must stay
+alive as long as the Oracle does.
 """
 from __future__ import annotations
 
@@ -34,7 +37,8 @@ def build_lib(force: bool = False) -> str:
 
 class _Cfg(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
-                ("n_layers", "d_model", "n_heads", "d_ff", "vocab", "window", "chunk", "n_fast", "batch", "n_steps")] + \
+                ("n_layers", "d_model", "n_heads", "d_ff", "vocab", "window", "chunk", "n_fast", "batch", "n_steps",
+                "dual_mlp")] + \
                [("rope_theta", ctypes.c_double), ("rms_eps", ctypes.c_double), ("lr", ctypes.c_double)]
 
 
@@ -44,7 +48,8 @@ _FPP = ctypes.POINTER(_FP)
 
 class _W(ctypes.Structure):
     _fields_ = [("embed", _FP), ("final_norm", _FP), ("lm_head", _FP)] + \
-               [(n, _FPP) for n in ("attn_norm", "wq", "wk", "wv", "wo", "mlp_norm", "w_gate", "w_up", "w_down")]
+               [(n, _FPP) for n in ("attn_norm", "wq", "wk", "wv", "wo", "mlp_norm", "w_gate", "w_up", "w_down",
+                                    "dyn_gate", "dyn_up", "dyn_down")]
 
 
 def _load():
@@ -107,7 +112,8 @@ class Oracle:
         self.L = cfg.n_layers
         c = _Cfg(*(int(getattr(cfg, n)) for n in
                    ("n_layers", "d_model", "n_heads", "d_ff", "vocab", "window", "chunk", "n_fast", "batch")),
-                 int(getattr(cfg, "n_steps", 1)), float(cfg.rope_theta), float(cfg.rms_eps), float(cfg.lr))
+                 int(getattr(cfg, "n_steps", 1)), int(getattr(cfg, "dual_mlp", 0)), float(cfg.rope_theta),
+                 float(cfg.rms_eps), float(cfg.lr))
         self._keep = []
         arrs = {}
         for key in ("attn_norm", "wq", "wk", "wv", "wo", "mlp_norm", "w_gate", "w_up", "w_down"):
@@ -116,6 +122,15 @@ class Oracle:
             arr = (_FP * self.L)(*[_fp(a) for a in lst])
             self._keep.append(arr)
             arrs[key] = ctypes.cast(arr, _FPP)
+        if int(getattr(cfg, "dual_mlp", 0)):
+            nf = int(cfg.n_fast)
+            for key in ("dyn_gate", "dyn_up", "dyn_down"):
+                lst = [np.ascontiguousarray(a, dtype=np.float32) for a in weights[key]]
+                assert len(lst) == nf, f"{key}: {len(lst)} arrays for {nf} updated blocks"
+                self._keep.extend(lst)
+                arr = (_FP * nf)(*[_fp(a) for a in lst])
+                self._keep.append(arr)
+                arrs[key] = ctypes.cast(arr, _FPP)
         glob = {k: np.ascontiguousarray(weights[k], dtype=np.float32) for k in ("embed", "final_norm", "lm_head")}
         self._keep.extend(glob.values())
         w = _W(_fp(glob["embed"]), _fp(glob["final_norm"]), _fp(glob["lm_head"]), **arrs)

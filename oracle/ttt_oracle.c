@@ -22,6 +22,11 @@
  *    every ~1000 generated tokens.
  *  - "测试时训练：长上下文的持续学习" §2.1.2: the training signal is
  *    -log p(x_{t+1} | x_<=t) and the step is theta <- theta - eta * grad.
+ *  - "从KV Cache到权重压缩：大模型持续学习的新范式" §2.2: 1-3 gradient steps per
+ *    update (n_steps), and optionally two MLPs in each updated block, a static
+ *    one that keeps what pretraining stored and a dynamic one that adapts
+ *    (dual_mlp: both read the block's MLP RMSNorm output and their outputs
+ *    add; only the dynamic one is updated).
  *
  * Readings where the pages are silent (each is listed in the design notes):
  *  window = k keys including the query itself (t-k < s <= t); Llama-style
@@ -48,6 +53,7 @@
 typedef struct {
   int32_t n_layers, d_model, n_heads, d_ff, vocab, window, chunk, n_fast, batch;
   int32_t n_steps; /* SGD steps per chunk; 0 and 1 both mean one */
+  int32_t dual_mlp; /* 1: static + dynamic MLP in every updated block */
   double rope_theta, rms_eps, lr;
 } oracle_cfg;
 
@@ -64,11 +70,17 @@ typedef struct {
   const float* const* w_gate;    /* L x [f, d] */
   const float* const* w_up;      /* L x [f, d] */
   const float* const* w_down;    /* L x [d, f] */
+  /* dual_mlp only: initial weights of the dynamic MLP of updated block j (layer L - n_fast + j),
+     n_fast entries each; the static MLP of those blocks is w_gate / w_up / w_down above */
+  const float* const* dyn_gate;  /* n_fast x [f, d] */
+  const float* const* dyn_up;    /* n_fast x [f, d] */
+  const float* const* dyn_down;  /* n_fast x [d, f] */
 } oracle_weights;
 
 /* saved activations of one layer for the current chunk */
 typedef struct {
   double *h_in, *u, *rstd1, *q, *k, *v, *att, *h_mid, *m, *rstd2, *zg, *zu, *act;
+  double *zg_s, *zu_s; /* static MLP of an updated block (dual_mlp), else NULL */
 } layer_acts;
 
 typedef struct {
@@ -212,8 +224,9 @@ oracle_state* oracle_create(const oracle_cfg* cfg, const oracle_weights* w, int6
   const oracle_cfg c = *cfg;
   if (c.n_layers <= 0 || c.d_model <= 0 || c.n_heads <= 0 || c.d_model % c.n_heads || (c.d_model / c.n_heads) % 2 ||
       c.d_ff <= 0 || c.vocab <= 0 || c.chunk <= 0 || c.window < c.chunk || c.n_fast < 1 || c.n_fast > c.n_layers ||
-      c.batch <= 0 || c.n_steps < 0)
+      c.batch <= 0 || c.n_steps < 0 || c.dual_mlp < 0 || c.dual_mlp > 1)
     return NULL;
+  if (c.dual_mlp && (!w->dyn_gate || !w->dyn_up || !w->dyn_down)) return NULL;
   oracle_state* s = (oracle_state*)xcalloc(1, sizeof(oracle_state));
   s->c = c;
   s->max_pos = max_positions;
@@ -235,16 +248,23 @@ oracle_state* oracle_create(const oracle_cfg* cfg, const oracle_weights* w, int6
   s->w.w_gate = p + 6 * L;
   s->w.w_up = p + 7 * L;
   s->w.w_down = p + 8 * L;
+  s->w.dyn_gate = w->dyn_gate;
+  s->w.dyn_up = w->dyn_up;
+  s->w.dyn_down = w->dyn_down;
 
   int64_t fd = (int64_t)c.d_ff * c.d_model, blk = fast_block(&c);
   s->fast0 = (double*)xcalloc((size_t)(blk * c.n_fast), sizeof(double));
   for (int j = 0; j < c.n_fast; ++j) {
+    /* the updated MLP: the block's own, or its dynamic one */
     int l = l0_of(&c) + j;
+    const float* gsrc = c.dual_mlp ? w->dyn_gate[j] : w->w_gate[l];
+    const float* usrc = c.dual_mlp ? w->dyn_up[j] : w->w_up[l];
+    const float* dsrc = c.dual_mlp ? w->dyn_down[j] : w->w_down[l];
     double* dst = s->fast0 + j * blk;
     for (int64_t i = 0; i < fd; ++i) {
-      dst[i] = w->w_gate[l][i];
-      dst[fd + i] = w->w_up[l][i];
-      dst[2 * fd + i] = w->w_down[l][i];
+      dst[i] = gsrc[i];
+      dst[fd + i] = usrc[i];
+      dst[2 * fd + i] = dsrc[i];
     }
   }
   s->rows = (row_state*)xcalloc((size_t)c.batch, sizeof(row_state));
@@ -302,7 +322,7 @@ typedef struct {
   double *h_final, *hf, *rstdf, *logits;
 } chunk_work;
 
-static void acts_alloc(layer_acts* a, int n, int d, int f) {
+static void acts_alloc(layer_acts* a, int n, int d, int f, int dual) {
   a->h_in = xcalloc((size_t)n * d, 8);
   a->u = xcalloc((size_t)n * d, 8);
   a->rstd1 = xcalloc((size_t)n, 8);
@@ -316,11 +336,14 @@ static void acts_alloc(layer_acts* a, int n, int d, int f) {
   a->zg = xcalloc((size_t)n * f, 8);
   a->zu = xcalloc((size_t)n * f, 8);
   a->act = xcalloc((size_t)n * f, 8);
+  a->zg_s = dual ? xcalloc((size_t)n * f, 8) : NULL;
+  a->zu_s = dual ? xcalloc((size_t)n * f, 8) : NULL;
 }
 
 static void acts_free(layer_acts* a) {
   free(a->h_in); free(a->u); free(a->rstd1); free(a->q); free(a->k); free(a->v); free(a->att);
   free(a->h_mid); free(a->m); free(a->rstd2); free(a->zg); free(a->zu); free(a->act);
+  free(a->zg_s); free(a->zu_s);
 }
 
 /* first key position visible from query position t: window of k keys incl. t */
@@ -392,6 +415,18 @@ static void forward_chunk(const oracle_state* s, row_state* rs, const int32_t* i
       mm_xwt_d(a->m, n, d, wg + fd, f, a->zu);
       for (int64_t i = 0; i < (int64_t)n * f; ++i) a->act[i] = silu(a->zg[i]) * a->zu[i];
       mm_xwt_d(a->act, n, f, wg + 2 * fd, d, tmp);
+      if (c->dual_mlp) {
+        /* the static MLP reads the same normed input; the two outputs add */
+        double* act_s = xcalloc((size_t)n * f, 8);
+        double* y_s = xcalloc((size_t)n * d, 8);
+        mm_xwt_f(a->m, n, d, s->w.w_gate[l], f, a->zg_s);
+        mm_xwt_f(a->m, n, d, s->w.w_up[l], f, a->zu_s);
+        for (int64_t i = 0; i < (int64_t)n * f; ++i) act_s[i] = silu(a->zg_s[i]) * a->zu_s[i];
+        mm_xwt_f(act_s, n, f, s->w.w_down[l], d, y_s);
+        for (int64_t i = 0; i < (int64_t)n * d; ++i) tmp[i] += y_s[i];
+        free(act_s);
+        free(y_s);
+      }
     } else {
       mm_xwt_f(a->m, n, d, s->w.w_gate[l], f, a->zg);
       mm_xwt_f(a->m, n, d, s->w.w_up[l], f, a->zu);
@@ -474,6 +509,19 @@ static void backward_chunk(const oracle_state* s, row_state* rs, const chunk_wor
     mm_dyw_d(dzg, n, f, wg, d, tmp);
     mm_dyw_d(dzu, n, f, wg + fd, d, dmid);
     for (int64_t i = 0; i < (int64_t)n * d; ++i) tmp[i] += dmid[i];
+    if (c->dual_mlp) {
+      /* the frozen static MLP passes its input gradient on too (its weights get none) */
+      mm_dyw_f(dh, n, d, s->w.w_down[l], f, dact);
+      for (int64_t i = 0; i < (int64_t)n * f; ++i) {
+        double sg = sigmoid(a->zg_s[i]);
+        dzu[i] = dact[i] * a->zg_s[i] * sg;
+        dzg[i] = dact[i] * a->zu_s[i] * sg * (1.0 + a->zg_s[i] * (1.0 - sg));
+      }
+      mm_dyw_f(dzg, n, f, s->w.w_gate[l], d, dmid);
+      for (int64_t i = 0; i < (int64_t)n * d; ++i) tmp[i] += dmid[i];
+      mm_dyw_f(dzu, n, f, s->w.w_up[l], d, dmid);
+      for (int64_t i = 0; i < (int64_t)n * d; ++i) tmp[i] += dmid[i];
+    }
     rmsnorm_bwd(a->h_mid, a->rstd2, n, d, s->w.mlp_norm[l], tmp, dmid);
     for (int64_t i = 0; i < (int64_t)n * d; ++i) dmid[i] += dh[i]; /* d h_mid */
     /* attention: h_mid = h_in + att W_o^T */
@@ -559,7 +607,7 @@ static void work_alloc(const oracle_cfg* c, chunk_work* wk, int n) {
   int d = c->d_model, f = c->d_ff, V = c->vocab;
   wk->n = n;
   wk->acts = (layer_acts*)xcalloc((size_t)c->n_layers, sizeof(layer_acts));
-  for (int l = 0; l < c->n_layers; ++l) acts_alloc(&wk->acts[l], n, d, f);
+  for (int l = 0; l < c->n_layers; ++l) acts_alloc(&wk->acts[l], n, d, f, c->dual_mlp && l >= l0_of(c));
   wk->h_final = xcalloc((size_t)n * d, 8);
   wk->hf = xcalloc((size_t)n * d, 8);
   wk->rstdf = xcalloc((size_t)n, 8);

@@ -113,6 +113,21 @@ def weight_stream(name: str, layer: int = -1) -> int:
     return 16 + 8 * layer + per[name]
 
 
+def dynamic_mlp_stream(name: str, block: int) -> int:
+    """Stream id of a dynamic-MLP tensor of updated block `block` (0 = the lowest updated block)."""
+    return (1 << 20) + 4 * block + {"dyn_gate": 0, "dyn_up": 1, "dyn_down": 2}[name]
+
+
+def dynamic_mlp(shape, n_fast: int, bf16: bool, seed: int = WEIGHT_SEED, std: float = WEIGHT_STD) -> dict:
+    """Initial weights of the dynamic MLPs of the n_fast updated blocks, for the variant with a
+    static and a dynamic MLP in each of them: {"dyn_gate": [f, d] x n_fast, "dyn_up": [f, d] x
+    n_fast, "dyn_down": [d, f] x n_fast}, N(0, std) from streams of their own."""
+    d, f = shape.d_model, shape.d_ff
+    return {"dyn_gate": [normal(seed, dynamic_mlp_stream("dyn_gate", j), (f, d), std, bf16) for j in range(n_fast)],
+            "dyn_up": [normal(seed, dynamic_mlp_stream("dyn_up", j), (f, d), std, bf16) for j in range(n_fast)],
+            "dyn_down": [normal(seed, dynamic_mlp_stream("dyn_down", j), (d, f), std, bf16) for j in range(n_fast)]}
+
+
 def weights(shape, bf16: bool, seed: int = WEIGHT_SEED, std: float = WEIGHT_STD,
             zero_lm_head: bool = False) -> dict:
     """All model weights as fp32 numpy arrays, row-major [out, in]."""

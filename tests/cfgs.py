@@ -4,7 +4,7 @@ from types import SimpleNamespace
 
 def cfg(**kw):
     base = dict(n_layers=4, d_model=16, n_heads=2, d_ff=24, vocab=11, window=5, chunk=4, n_fast=1, batch=1,
-                rope_theta=1e4, rms_eps=1e-5, lr=0.1, dtype="f32", n_steps=1)
+                rope_theta=1e4, rms_eps=1e-5, lr=0.1, dtype="f32", n_steps=1, dual_mlp=0)
     base.update(kw)
     return SimpleNamespace(**base)
 

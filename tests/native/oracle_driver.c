@@ -7,6 +7,7 @@
  *
  * Covered: creation (and the rejected configurations), chunks of the full size,
  * a ragged last chunk and chunks with ignored targets, two SGD steps per chunk,
+ * the static + dynamic MLP variant,
  * the gradient of one chunk, greedy generation with an update and per-step
  * logits, teacher forcing, reading and writing fast weights, the RoPE and
  * RMSNorm helpers.  Exit status 0 when every call returned what it should.
@@ -43,6 +44,8 @@ typedef struct {
   float *embed, *final_norm, *lm_head;
   float* per_layer[9][L];
   const float* ptrs[9][L];
+  float* dyn[3][2];           /* dynamic MLPs of the two updated blocks */
+  const float* dyn_ptrs[3][2];
 } weights;
 
 static void make_weights(weights* w) {
@@ -56,6 +59,11 @@ static void make_weights(weights* w) {
       w->per_layer[a][l] = filled(sizes[a], gain ? 0.1f : 0.3f, gain ? 1.f : 0.f);
       w->ptrs[a][l] = w->per_layer[a][l];
     }
+  for (int a = 0; a < 3; ++a)
+    for (int j = 0; j < 2; ++j) {
+      w->dyn[a][j] = filled((size_t)F * D, 0.3f, 0.f);
+      w->dyn_ptrs[a][j] = w->dyn[a][j];
+    }
 }
 
 static void free_weights(weights* w) {
@@ -64,6 +72,8 @@ static void free_weights(weights* w) {
   free(w->lm_head);
   for (int a = 0; a < 9; ++a)
     for (int l = 0; l < L; ++l) free(w->per_layer[a][l]);
+  for (int a = 0; a < 3; ++a)
+    for (int j = 0; j < 2; ++j) free(w->dyn[a][j]);
 }
 
 static oracle_weights view(const weights* w) {
@@ -81,6 +91,9 @@ static oracle_weights view(const weights* w) {
   o.w_gate = w->ptrs[6];
   o.w_up = w->ptrs[7];
   o.w_down = w->ptrs[8];
+  o.dyn_gate = w->dyn_ptrs[0];
+  o.dyn_up = w->dyn_ptrs[1];
+  o.dyn_down = w->dyn_ptrs[2];
   return o;
 }
 
@@ -155,9 +168,18 @@ int main(void) {
   CHECK(oracle_create(NULL, &ow, MAXPOS) == NULL);
   CHECK(oracle_create(&bad, &ow, 0) == NULL);
 
-  for (int steps = 1; steps <= 2; ++steps) {
+  /* a dual configuration without its dynamic weights is refused */
+  bad = base_cfg();
+  bad.dual_mlp = 1;
+  oracle_weights nodyn = ow;
+  nodyn.dyn_up = NULL;
+  CHECK(oracle_create(&bad, &nodyn, MAXPOS) == NULL);
+
+  /* one SGD step, two SGD steps, static + dynamic MLP */
+  for (int variant = 0; variant < 3; ++variant) {
     oracle_cfg c = base_cfg();
-    c.n_steps = steps;
+    c.n_steps = variant == 1 ? 2 : 1;
+    c.dual_mlp = variant == 2;
     oracle_state* s = oracle_create(&c, &ow, MAXPOS);
     CHECK(s != NULL);
     if (!s) break;

@@ -344,3 +344,133 @@ def test_fast_set_is_the_last_quarter_of_the_blocks():
         L, d, f, nf, _ = rows[name]
         assert (c["n_layers"], c["d_model"], c["d_ff"], c["n_fast"]) == (L, d, f, nf), name
 
+
+
+# ------------------------------------------------- static + dynamic MLP (dual)
+
+def dual_weights(c, std=0.3, seed=7, static_down_zero=False, dyn_from_static=False):
+    """tiny_weights plus the dynamic MLPs of the updated blocks (their own seeded draws)."""
+    w = tiny_weights(c, std=std, seed=seed)
+    shape = synth.Shape(c.n_layers, c.d_model, c.n_heads, c.d_ff, c.vocab)
+    w.update(synth.dynamic_mlp(shape, c.n_fast, bf16=False, seed=seed + 1, std=std))
+    l0 = c.n_layers - c.n_fast
+    if dyn_from_static:
+        for j in range(c.n_fast):
+            w["dyn_gate"][j] = w["w_gate"][l0 + j].copy()
+            w["dyn_up"][j] = w["w_up"][l0 + j].copy()
+    if static_down_zero:
+        for l in range(l0, c.n_layers):
+            w["w_down"][l] = np.zeros_like(w["w_down"][l])
+    return w
+
+
+@pytest.mark.parametrize("n_fast", [1, 2])
+def test_dual_mlp_equals_autograd_chunk_loop(n_fast):
+    """Static + dynamic MLP in the updated blocks (the static one frozen, the dynamic one
+    updated; one RMSNorm feeds both, their outputs add): losses and final dynamic weights of a
+    several-chunk loop equal the autograd chunk loop of the same model."""
+    c = cfg(window=6, chunk=4, lr=0.2, n_fast=n_fast, dual_mlp=1)
+    w = dual_weights(c)
+    seq = seq_for(c, 14)
+    o = Oracle(c, w, 20)
+    losses = o.prefill(seq)[0]
+    W = tp.Weights(w, c)
+    ref_losses, _ = tp.chunk_loop(W, seq[0], c.lr, c.chunk)
+    np.testing.assert_allclose(losses, ref_losses, rtol=1e-11)
+    got, ref = o.get_fast(0), tp.fast_numpy(W)
+    for j in range(n_fast):
+        for a, key in enumerate(("dyn_gate", "dyn_up", "dyn_down")):
+            d_ref = ref[j][a] - w[key][j]
+            assert np.max(np.abs((got[j][a] - w[key][j]) - d_ref)) <= 1e-9 * np.max(np.abs(d_ref))
+
+
+def test_dual_mlp_with_shared_gate_up_equals_single_mlp_with_summed_down():
+    """SwiGLU is linear in its down projection: when every dynamic MLP has the static one's
+    gate and up weights, the model equals the single-MLP model whose down projection is the sum
+    of the two.  So the losses agree, and the gradient w.r.t. the dynamic W_down equals the
+    single model's gradient w.r.t. its W_down in every updated block -- in the lower one only if
+    the static MLP's input gradient reaches the blocks below."""
+    c2 = cfg(window=6, chunk=4, lr=0.0, n_fast=2, dual_mlp=1)
+    c1 = cfg(window=6, chunk=4, lr=0.0, n_fast=2)
+    w = dual_weights(c2, dyn_from_static=True)
+    l0 = c2.n_layers - c2.n_fast
+    # both down projections on a grid of 2^-12 (|w| < 2), so their sum is exact in fp32
+    for j in range(c2.n_fast):
+        w["w_down"][l0 + j] = (np.round(w["w_down"][l0 + j] * 4096) / 4096).astype(np.float32)
+        w["dyn_down"][j] = (np.round(w["dyn_down"][j] * 4096) / 4096).astype(np.float32)
+    w1 = {k: (list(v) if isinstance(v, list) else v) for k, v in w.items()}
+    for j in range(c2.n_fast):
+        s64 = w["w_down"][l0 + j].astype(np.float64) + w["dyn_down"][j].astype(np.float64)
+        w1["w_down"][l0 + j] = s64.astype(np.float32)
+        assert np.array_equal(w1["w_down"][l0 + j].astype(np.float64), s64)
+    seq = seq_for(c2, 12)
+    od, os_ = Oracle(c2, w, 16), Oracle(c1, w1, 16)
+    np.testing.assert_allclose(od.prefill(seq, 2), os_.prefill(seq, 2), rtol=1e-12)
+    toks, tgts = seq[:, 8:12], seq[:, 9:13]
+    ld, gd = od.eval_chunk(toks, tgts, grad=True)
+    ls, gs = os_.eval_chunk(toks, tgts, grad=True)
+    np.testing.assert_allclose(ld, ls, rtol=1e-12)
+    fd = c2.d_ff * c2.d_model
+    for j in range(c2.n_fast):
+        dn = slice(j * 3 * fd + 2 * fd, (j + 1) * 3 * fd)
+        err = np.max(np.abs(gd[0, dn] - gs[0, dn])) / np.max(np.abs(gs[0, dn]))
+        assert err < 1e-10, (j, err)
+        assert np.max(np.abs(gs[0, dn])) > 1e-4
+
+
+def test_dual_mlp_with_zero_static_down_equals_single_mlp():
+    """With the static MLPs' down projections zero the static branch adds nothing and passes
+    no gradient: the dual model equals the single-MLP model whose updated MLPs start at the
+    dynamic weights, losses and updated weights alike over several updated chunks."""
+    c2 = cfg(window=6, chunk=4, lr=0.2, n_fast=2, dual_mlp=1)
+    c1 = cfg(window=6, chunk=4, lr=0.2, n_fast=2)
+    w = dual_weights(c2, static_down_zero=True)
+    l0 = c2.n_layers - c2.n_fast
+    w1 = {k: (list(v) if isinstance(v, list) else v) for k, v in w.items()}
+    for j in range(c2.n_fast):
+        w1["w_gate"][l0 + j], w1["w_up"][l0 + j], w1["w_down"][l0 + j] = \
+            w["dyn_gate"][j], w["dyn_up"][j], w["dyn_down"][j]
+    seq = seq_for(c2, 14)
+    od, os_ = Oracle(c2, w, 20), Oracle(c1, w1, 20)
+    np.testing.assert_allclose(od.prefill(seq), os_.prefill(seq), rtol=1e-12)
+    np.testing.assert_allclose(od.get_fast_flat(0), os_.get_fast_flat(0), rtol=0, atol=1e-13)
+    assert not np.allclose(od.get_fast_flat(0), np.concatenate(
+        [np.concatenate([w[k][j].ravel() for k in ("dyn_gate", "dyn_up", "dyn_down")]) for j in range(2)]))
+
+
+def test_dual_mlp_gradient_matches_central_differences():
+    """Chunk-loss gradient w.r.t. the dynamic MLPs against central finite differences (two
+    updated blocks, cached keys/values from two earlier updated chunks)."""
+    c = cfg(n_fast=2, lr=0.1, dual_mlp=1)
+    w = dual_weights(c)
+    seq = seq_for(c, 12)
+    o = Oracle(c, w, 16)
+    for ch in range(2):
+        o.prefill_chunk(seq[:, ch * 4:(ch + 1) * 4], seq[:, ch * 4 + 1:(ch + 1) * 4 + 1])
+    toks, tgts = seq[:, 8:12], seq[:, 9:13]
+    _, g = o.eval_chunk(toks, tgts, grad=True)
+    g = g[0]
+    phi = o.get_fast_flat(0)
+    idx = np.random.default_rng(1).choice(phi.size, size=300, replace=False)
+    h = 1e-5
+    fd = np.empty(idx.size)
+    for j, i in enumerate(idx):
+        p = phi.copy()
+        p[i] += h
+        o.set_fast_flat(0, p)
+        lp, _ = o.eval_chunk(toks, tgts)
+        p[i] -= 2 * h
+        o.set_fast_flat(0, p)
+        lm, _ = o.eval_chunk(toks, tgts)
+        fd[j] = (lp[0] - lm[0]) / (2 * h)
+    o.set_fast_flat(0, phi)
+    err = np.max(np.abs(fd - g[idx])) / np.max(np.abs(g[idx]))
+    assert err < 1e-6, err
+
+
+def test_dual_mlp_requires_the_dynamic_weights():
+    c = cfg(n_fast=2, dual_mlp=1)
+    w = tiny_weights(c)
+    w.update({"dyn_gate": [], "dyn_up": [], "dyn_down": []})
+    with pytest.raises(AssertionError):
+        Oracle(c, w, 16)

@@ -42,10 +42,17 @@ class Weights:
             self.layers.append({k: t64(w[k][l]) for k in
                                 ("attn_norm", "wq", "wk", "wv", "wo", "mlp_norm", "w_gate", "w_up", "w_down")})
         l0 = L - cfg.n_fast
-        # fast weights as leaf tensors (the MLP matrices of blocks l0..L-1)
+        # dual: blocks l0..L-1 keep their own MLP frozen (static) and add a dynamic one
+        self.dual = bool(getattr(cfg, "dual_mlp", 0))
+        # fast weights as leaf tensors (the updated MLP matrices of blocks l0..L-1)
         self.fast = []
         for j, l in enumerate(range(l0, L)):
-            src = fast[j] if fast is not None else (w["w_gate"][l], w["w_up"][l], w["w_down"][l])
+            if fast is not None:
+                src = fast[j]
+            elif self.dual:
+                src = (w["dyn_gate"][j], w["dyn_up"][j], w["dyn_down"][j])
+            else:
+                src = (w["w_gate"][l], w["w_up"][l], w["w_down"][l])
             self.fast.append([t64(a).clone().requires_grad_(True) for a in src])
         self.l0 = l0
 
@@ -76,7 +83,10 @@ def _block_rest(W: Weights, l: int, h: torch.Tensor, att: torch.Tensor):
     hm = h + att.transpose(0, 1).reshape(T, cfg.d_model) @ lay["wo"].T
     m = F.rms_norm(hm, (cfg.d_model,), weight=lay["mlp_norm"], eps=cfg.rms_eps)
     wg, wu, wd = W.mlp(l)
-    return hm + (F.silu(m @ wg.T) * (m @ wu.T)) @ wd.T
+    y = (F.silu(m @ wg.T) * (m @ wu.T)) @ wd.T
+    if W.dual and l >= W.l0:
+        y = y + (F.silu(m @ lay["w_gate"].T) * (m @ lay["w_up"].T)) @ lay["w_down"].T
+    return hm + y
 
 
 def band_mask(q_pos: torch.Tensor, k_pos: torch.Tensor, window: int) -> torch.Tensor:
