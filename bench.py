@@ -43,7 +43,9 @@ PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, GB/s
 
 
 def flops_per_row(c: dict, T: int) -> dict:
-    """Algorithmic FLOPs (matmul = 2 M N K) of the inner loop over T tokens."""
+    """Algorithmic FLOPs (matmul = 2 M N K) of the inner loop over T tokens.  With dual_mlp the
+    updated blocks also run their frozen static MLP forward (6 d f per token) and, above the
+    lowest updated block, its input-gradient products (6 d f per token)."""
     L, d, f, V, k, b, Lq = c["n_layers"], c["d_model"], c["d_ff"], c["vocab"], c["window"], c["chunk"], c["n_fast"]
     out = {"fwd_gemm": 0, "fwd_attn": 0, "bwd_gemm": 0, "bwd_attn": 0, "upd": 0}
     for p0 in range(0, T, b):
@@ -55,6 +57,9 @@ def flops_per_row(c: dict, T: int) -> dict:
         out["bwd_gemm"] += 2 * n * d * V + (Lq - 1) * n * (12 * d * f + 8 * d * d) + 8 * n * d * f
         out["bwd_attn"] += (Lq - 1) * (4 * d * A + 4 * d * I)
         out["upd"] += 6 * d * f * Lq
+        if c.get("dual_mlp"):
+            out["fwd_gemm"] += n * Lq * 6 * d * f
+            out["bwd_gemm"] += (Lq - 1) * n * 6 * d * f
     out["total"] = sum(out.values())
     return out
 
@@ -113,7 +118,8 @@ def cpu_baseline(c: dict, w: dict, seq: np.ndarray, sample_tokens: int) -> dict:
 
     from oracle import Oracle
     oc = SimpleNamespace(**{k: c[k] for k in ("n_layers", "d_model", "n_heads", "d_ff", "vocab", "window", "chunk",
-                                              "n_fast", "rope_theta", "lr")}, batch=1, rms_eps=1e-5)
+                                              "n_fast", "rope_theta", "lr")}, batch=1, rms_eps=1e-5,
+                         dual_mlp=int(c.get("dual_mlp", 0)))
     n = min(sample_tokens, c["chunk"])
     o = Oracle(oc, w, n)
     t0 = time.perf_counter()
@@ -169,6 +175,8 @@ def main():
                          "full-attention: forward and loss only with the window covering the whole sequence "
                          "(no test-time training), timed beside the TTT prefill step")
     ap.add_argument("--n-steps", type=int, default=0, help="SGD steps per chunk (0 = library default, one)")
+    ap.add_argument("--dual-mlp", action="store_true",
+                    help="static + dynamic MLP in every updated block (the dynamic one is updated)")
     ap.add_argument("--decode-tokens", type=int, default=1024, help="decode: generated tokens per step")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device-to-device copy 3 times (reference for HBM byte counters)")
@@ -203,8 +211,11 @@ def main():
         c["window"] = args.window
     torch.cuda.set_device(0)
     t_setup = time.perf_counter()
-    w = synth.weights(synth.Shape(c["n_layers"], c["d_model"], c["n_heads"], c["d_ff"], c["vocab"]),
-                      bf16=c["dtype"] == "bf16")
+    shape = synth.Shape(c["n_layers"], c["d_model"], c["n_heads"], c["d_ff"], c["vocab"])
+    w = synth.weights(shape, bf16=c["dtype"] == "bf16")
+    if args.dual_mlp:
+        c["dual_mlp"] = 1
+        w.update(synth.dynamic_mlp(shape, c["n_fast"], bf16=c["dtype"] == "bf16"))
     seq = synth.tokens(1, T + 1, c["vocab"], dist)
     cfg = TTTConfig(batch=1, max_positions=T + 8, lookahead=args.lookahead, n_steps=args.n_steps, **c)
     ctx = TTTContext(cfg, w)
@@ -297,10 +308,11 @@ def main():
         "ms_per_step": round(ms, 2), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": c["dtype"], "data": "synthetic",
         "config": {"workload": f"ttt-prefill-{args.config}" + (f"-k{c['window']}" if args.window else "") +
-                   (f"-steps{args.n_steps}" if args.n_steps > 1 else ""), "layers": c["n_layers"],
+                   (f"-steps{args.n_steps}" if args.n_steps > 1 else "") + ("-dual-mlp" if args.dual_mlp else ""),
+                   "layers": c["n_layers"],
                    "d_model": c["d_model"], "tokens": T, "window": c["window"], "chunk": c["chunk"],
                    "fast_blocks": c["n_fast"], "batch": 1, "token_dist": dist,
-                   "sgd_steps_per_chunk": max(1, args.n_steps)},
+                   "sgd_steps_per_chunk": max(1, args.n_steps), "dual_mlp": bool(args.dual_mlp)},
         "flops_per_step": F["total"], "mfma_peak_frac": round(F["total"] / (ms / 1e3) / peak, 4),
         "final_chunk_loss": float(losses[-1]), "first_chunk_loss": float(losses[0]),
         "roofline": roof,

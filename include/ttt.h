@@ -73,11 +73,17 @@ typedef struct {
   double rope_theta;  /* RoPE base; rotate-half pairing (i, i + head_dim/2) */
   double rms_eps;     /* RMSNorm epsilon: g * x / sqrt(mean(x^2) + eps) */
   float lr;           /* SGD step size of the inner loop */
-  float reserved2_;
+  int32_t dual_mlp;   /* 0: the updated blocks' own MLPs are the fast weights.  1: each updated block keeps
+                         its MLP frozen (static) and adds a dynamic SwiGLU MLP of the same width, whose
+                         weights (ttt_weights.dyn_*) are the fast weights; both read the block's MLP
+                         RMSNorm output and their outputs add (page "从KV Cache到权重压缩：大模型持续学习的新范式",
+                         §2.2: a static MLP keeps pretrained knowledge, a dynamic MLP adapts) */
 } ttt_config;
 
 /* Host fp32 weight arrays (copied by ttt_create; bf16 contexts round them to
- * nearest-even bf16).  Per-layer fields are arrays of L pointers. */
+ * nearest-even bf16).  Per-layer fields are arrays of L pointers; the dyn_*
+ * fields (read only when cfg.dual_mlp = 1, may be NULL otherwise) are arrays of
+ * n_fast pointers, entry j for block L - n_fast + j. */
 typedef struct {
   const float* embed;      /* [V, d] */
   const float* final_norm; /* [d] */
@@ -91,6 +97,9 @@ typedef struct {
   const float* const* w_gate;    /* [f, d] */
   const float* const* w_up;      /* [f, d] */
   const float* const* w_down;    /* [d, f] */
+  const float* const* dyn_gate;  /* [f, d] initial dynamic MLP of each updated block (dual_mlp) */
+  const float* const* dyn_up;    /* [f, d] */
+  const float* const* dyn_down;  /* [d, f] */
 } ttt_weights;
 
 /* Optional device allocator (e.g. PyTorch's caching allocator).  Install it
@@ -108,7 +117,8 @@ int ttt_set_allocator(ttt_alloc_fn alloc, ttt_free_fn free_fn, void* user);
  * weights start as copies of the given MLP weights of the last n_fast blocks;
  * the key/value window is empty and the position is 0.
  * Errors: TTT_EINVAL for a NULL argument or an invalid configuration (k < b,
- * d % H, head_dim odd or > 128, n_fast out of range, non-finite lr ...),
+ * d % H, head_dim odd or > 128, n_fast out of range, non-finite lr, dual_mlp
+ * without its dyn_* arrays ...),
  * TTT_ENODEV without a gfx950 device, TTT_ENOMEM when the allocator (or the
  * installed hook) returns NULL, TTT_EDEVICE for other HIP failures.  On error
  * *out is NULL, nothing stays allocated and ttt_last_error(NULL) says why. */
@@ -172,7 +182,8 @@ int ttt_generate(ttt_ctx* ctx, const int32_t* first_input, int32_t n_new, int32_
                  int32_t* out_tokens, float* update_losses);
 
 /* Copy the fp32 fast weights of row `row` to host `dst`: for each fast block
- * in ascending order, W_gate [f, d], W_up [f, d], W_down [d, f].  n_floats
+ * in ascending order, W_gate [f, d], W_up [f, d], W_down [d, f] (with dual_mlp,
+ * those of the dynamic MLP).  n_floats
  * must equal 3 * d * f * n_fast.  These are the parameters the inner loop
  * changes (page "TTT-E2E 如何让大模型边用边学", §4.2: only the MLPs of the last
  * quarter of the blocks), i.e. the per-session parameter snapshot of page
@@ -189,9 +200,10 @@ int ttt_get_fast_weights(ttt_ctx* ctx, int32_t row, float* dst, int64_t n_floats
  * refreshed.  Synchronous.  TTT_EINVAL on a bad row, size or NULL, TTT_ESTATE when
  * poisoned.
  *
- * ttt_state_size: bytes of a whole-context snapshot: a header of 16 int64 (magic,
+ * ttt_state_size: bytes of a whole-context snapshot: a header of 17 int64 (magic,
  * version, batch, n_layers, n_heads, head dim, ring slots, element bytes, fast blocks,
- * d_ff, d_model, position, window, chunk, vocab, bit pattern of rope_theta), then the fp32 fast weights of every block
+ * d_ff, d_model, position, window, chunk, vocab, bit pattern of rope_theta, dual_mlp),
+ * then the fp32 fast weights of every block
  * ([n_fast][batch][3 d f]), then per layer its key/value ring arrays as stored on the
  * device (K, V, V^T, and K^T where the layer keeps it).  -1 for a NULL context.
  * ttt_save_state writes it to host `dst` (nbytes >= ttt_state_size; synchronous;

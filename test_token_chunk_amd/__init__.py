@@ -64,7 +64,7 @@ class _Config(ctypes.Structure):
                 ("n_layers", "d_model", "n_heads", "d_ff", "vocab", "window", "chunk", "n_fast", "batch", "dtype",
                  "lookahead", "n_steps")] + \
                [("max_positions", ctypes.c_int64), ("rope_theta", ctypes.c_double), ("rms_eps", ctypes.c_double),
-                ("lr", ctypes.c_float), ("reserved2_", ctypes.c_float)]
+                ("lr", ctypes.c_float), ("dual_mlp", ctypes.c_int32)]
 
 
 _FP = ctypes.POINTER(ctypes.c_float)
@@ -73,7 +73,8 @@ _FPP = ctypes.POINTER(_FP)
 
 class _Weights(ctypes.Structure):
     _fields_ = [("embed", _FP), ("final_norm", _FP), ("lm_head", _FP)] + \
-               [(n, _FPP) for n in ("attn_norm", "wq", "wk", "wv", "wo", "mlp_norm", "w_gate", "w_up", "w_down")]
+               [(n, _FPP) for n in ("attn_norm", "wq", "wk", "wv", "wo", "mlp_norm", "w_gate", "w_up", "w_down",
+                                    "dyn_gate", "dyn_up", "dyn_down")]
 
 
 _ALLOC_FN = ctypes.CFUNCTYPE(ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p)
@@ -183,6 +184,7 @@ class TTTConfig:
     dtype: str = "bf16"  # "bf16" or "f32"
     lookahead: int = 0
     n_steps: int = 0  # SGD steps per chunk (0 = 1)
+    dual_mlp: int = 0  # 1: static + dynamic MLP in every updated block (weights dyn_gate/dyn_up/dyn_down)
     max_positions: int = 1 << 17
     rope_theta: float = 1e4
     rms_eps: float = 1e-5
@@ -198,7 +200,7 @@ class TTTConfig:
         return _Config(self.n_layers, self.d_model, self.n_heads, self.d_ff, self.vocab, self.window, self.chunk,
                        self.n_fast, self.batch, TTT_BF16 if self.dtype == "bf16" else TTT_F32, self.lookahead,
                        self.n_steps,
-                       self.max_positions, self.rope_theta, self.rms_eps, self.lr, 0.0)
+                       self.max_positions, self.rope_theta, self.rms_eps, self.lr, int(self.dual_mlp))
 
 
 def _i32(a) -> np.ndarray:
@@ -228,6 +230,14 @@ class TTTContext:
             arr = (_FP * L)(*[fp(x) for x in weights[key]])
             keep.append(arr)
             arrs[key] = ctypes.cast(arr, _FPP)
+        if cfg.dual_mlp:  # the dynamic MLPs of the updated blocks, n_fast arrays each
+            nf = cfg.n_fast or max(1, L // 4)
+            for key in ("dyn_gate", "dyn_up", "dyn_down"):
+                if len(weights[key]) != nf:
+                    raise ValueError(f"{key}: {len(weights[key])} arrays for {nf} updated blocks")
+                arr = (_FP * nf)(*[fp(x) for x in weights[key]])
+                keep.append(arr)
+                arrs[key] = ctypes.cast(arr, _FPP)
         w = _Weights(fp(weights["embed"]), fp(weights["final_norm"]), fp(weights["lm_head"]), **arrs)
         h = ctypes.c_void_p()
         self._c = cfg._c()

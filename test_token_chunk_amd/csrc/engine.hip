@@ -60,6 +60,7 @@ struct FastW {
 struct TopActs {
   float *h_in = nullptr, *rstd1 = nullptr, *h_mid = nullptr, *rstd2 = nullptr, *lse = nullptr;
   void *q = nullptr, *qt = nullptr, *o = nullptr, *mT = nullptr, *zg = nullptr, *zu = nullptr, *actT = nullptr;
+  void *zg_s = nullptr, *zu_s = nullptr;  // static MLP pre-activations (dual MLP, blocks above l0)
 };
 
 }  // namespace
@@ -68,6 +69,9 @@ struct ttt_ctx {
   ttt_config cfg;
   int L, d, H, hd, f, V, k, b, Lq, l0, B, R, G;
   int n_steps = 1;  // SGD steps per chunk
+  // static + dynamic MLP in every fast block: sw holds the frozen static MLPs in the fast
+  // weights' layouts (one copy, all rows share it), fw the dynamic ones
+  bool dual = false;
   bool bf16;
   size_t es;  // element size of T
   bool mfma = true;
@@ -95,6 +99,7 @@ struct ttt_ctx {
 
   std::vector<LayerW> lw;
   std::vector<FastW> fw;
+  std::vector<FastW> sw;  // dual MLP: static MLPs of the fast blocks (batch 1, master kept)
   std::vector<TopActs> acts;
   void *embed = nullptr, *lm_head = nullptr, *lm_headT = nullptr;
   float* final_norm = nullptr;
@@ -110,6 +115,7 @@ struct ttt_ctx {
   int* nvalid = nullptr;
   float *dh = nullptr, *tmpf = nullptr, *dq = nullptr, *dk = nullptr, *dv = nullptr, *dvec = nullptr;
   void *dyN = nullptr, *dz = nullptr, *dhT = nullptr, *dO = nullptr, *dOT = nullptr, *dqkv = nullptr;
+  void* dzT_s = nullptr;  // dual MLP: transposed dz of the static MLP's backward (written, never read)
   std::vector<void*> dyT, dzT;  // per fast block: inputs of its weight-gradient GEMMs (side stream)
   int* err_dev = nullptr;
   float* ws = nullptr;  // split-K / split-key workspace (used by one launch at a time)
@@ -475,6 +481,27 @@ int layer_fwd(ttt_ctx* c, int l, float* h, int n, int64_t p0, int mode, TopActs*
   CK(norm_fwd<T>(c, h, M, w.mlp_norm, tp<T>(c->ub), sv ? sv->rstd2 : c->rstd_tmp, sv ? tp<T>(sv->mT) : (T*)nullptr,
                  n, c->b, sv ? sv->h_mid : nullptr));
   if (l >= c->l0) {
+    if (c->dual) {
+      // the frozen static MLP on the same normed input, all rows at once; its output is added to
+      // the residual stream here, the dynamic MLP's below
+      const FastW& st = c->sw[l - c->l0];
+      GemmArgs gs = mk(c->ub, d, st.wgu, d, (int)M, c->il ? 2 * f : f, d);
+      gs.dual_off = c->il ? 0 : f;
+      gs.e.kind = c->il ? EPI_SWIGLU_IL : EPI_SWIGLU;
+      gs.e.c = c->actb;
+      gs.e.ldc = f;
+      if (sv && sv->zg_s) {  // pre-activations for the backward of blocks above l0
+        gs.e.zg = sv->zg_s;
+        gs.e.zu = sv->zu_s;
+        gs.e.ldz = f;
+      }
+      CK(Ops<T>::gemm(c, gs));
+      GemmArgs gds = mk(c->actb, f, st.wd, f, (int)M, d, f);
+      gds.e.kind = EPI_ADD_F32;
+      gds.e.c = h;
+      gds.e.ldc = d;
+      CK(Ops<T>::gemm(c, gds));
+    }
     const FastW& fw = c->fw[l - c->l0];
     GemmArgs g = mk(c->ub, d, fw.wgu, d, n, c->il ? 2 * f : f, d);
     g.batch = B;
@@ -600,7 +627,10 @@ int top_chunk(ttt_ctx* c, const int32_t* tgt, int64_t ld, const float* hsrc, int
       g3.e.c = c->tmpf;
       g3.e.ldc = d;
       g3.e.sc = (int64_t)n * d;
-      CK(Ops<T>::gemm_parts(c, g3, n, S3));
+      if (c->dual)
+        CK(Ops<T>::gemm(c, g3));  // the static MLP's part is added to tmpf below
+      else
+        CK(Ops<T>::gemm_parts(c, g3, n, S3));
     }
     // The weight gradients of this block with the fused SGD step run on the side stream,
     // overlapping the rest of the backward: their inputs (dy^T, dz^T of this block, act^T,
@@ -652,6 +682,28 @@ int top_chunk(ttt_ctx* c, const int32_t* tgt, int64_t ld, const float* hsrc, int
     g4.background = on_side;
     CK(Ops<T>::gemm(c, g4, sg));
     if (j == 0) break;
+    if (c->dual) {
+      // the frozen static MLP passes its input gradient on as well: d act_s = dy W_down_s ->
+      // dz_s, then dm += dz_s,g W_gate_s + dz_s,u W_up_s (c->dz is free again: the dynamic dm
+      // product that read it is ahead on this stream, the SGD products read dzT)
+      const FastW& st = c->sw[j];
+      GemmArgs s1 = mk(c->dyN, d, st.wdT, d, (int)M, f, d);
+      s1.e.kind = EPI_SWIGLU_BWD;
+      s1.e.zg = a.zg_s;
+      s1.e.zu = a.zu_s;
+      s1.e.ldz = f;
+      s1.e.c = c->dz;
+      s1.e.ldc = 2 * f;
+      s1.e.t = c->dzT_s;
+      s1.e.ldt = (int64_t)M;
+      s1.e.f = f;
+      CK(Ops<T>::gemm(c, s1));
+      GemmArgs s3 = mk(c->dz, 2 * f, st.wguT, 2 * f, (int)M, d, 2 * f);
+      s3.e.kind = EPI_ADD_F32;
+      s3.e.c = c->tmpf;
+      s3.e.ldc = d;
+      CK(Ops<T>::gemm(c, s3));
+    }
     const LayerW& lw = c->lw[l];
     // through the MLP norm and the residual: dh <- d h_mid
     CK(norm_bwd<T>(c, S3, a.h_mid, a.rstd2, M, lw.mlp_norm, c->tmpf, c->dh, c->dh, tp<T>(c->dhT)));
@@ -1031,15 +1083,41 @@ int build(ttt_ctx* c, const ttt_weights* w) {
   for (int j = 0; j < c->Lq; ++j) {
     int l = c->l0 + j;
     float* init = c->fast_init + j * fsz;
-    CK(hipMemcpy(init, w->w_gate[l], (size_t)f * d * 4, hipMemcpyHostToDevice));
-    CK(hipMemcpy(init + (int64_t)f * d, w->w_up[l], (size_t)f * d * 4, hipMemcpyHostToDevice));
-    CK(hipMemcpy(init + 2LL * f * d, w->w_down[l], (size_t)d * f * 4, hipMemcpyHostToDevice));
+    // the updated MLP: the block's own, or (dual MLP) its dynamic one
+    const float* gsrc = c->dual ? w->dyn_gate[j] : w->w_gate[l];
+    const float* usrc = c->dual ? w->dyn_up[j] : w->w_up[l];
+    const float* dsrc = c->dual ? w->dyn_down[j] : w->w_down[l];
+    CK(hipMemcpy(init, gsrc, (size_t)f * d * 4, hipMemcpyHostToDevice));
+    CK(hipMemcpy(init + (int64_t)f * d, usrc, (size_t)f * d * 4, hipMemcpyHostToDevice));
+    CK(hipMemcpy(init + 2LL * f * d, dsrc, (size_t)d * f * 4, hipMemcpyHostToDevice));
     FastW& fw = c->fw[j];
     AL(fw.master, fsz * B * 4);
     AL(fw.wgu, 2LL * f * d * B * es);
     AL(fw.wguT, 2LL * f * d * B * es);
     AL(fw.wd, (int64_t)d * f * B * es);
     AL(fw.wdT, (int64_t)d * f * B * es);
+  }
+  // dual MLP: the static MLPs of the fast blocks, frozen, in the same layouts as the dynamic
+  // ones (the transposed copies serve the backward of the blocks above l0)
+  if (c->dual) {
+    c->sw.resize(c->Lq);
+    for (int j = 0; j < c->Lq; ++j) {
+      const int l = c->l0 + j;
+      FastW& sw = c->sw[j];
+      AL(sw.master, fsz * 4);
+      CK(hipMemcpy(sw.master, w->w_gate[l], (size_t)f * d * 4, hipMemcpyHostToDevice));
+      CK(hipMemcpy(sw.master + (int64_t)f * d, w->w_up[l], (size_t)f * d * 4, hipMemcpyHostToDevice));
+      CK(hipMemcpy(sw.master + 2LL * f * d, w->w_down[l], (size_t)d * f * 4, hipMemcpyHostToDevice));
+      AL(sw.wgu, 2LL * f * d * es);
+      AL(sw.wguT, 2LL * f * d * es);
+      AL(sw.wd, (int64_t)d * f * es);
+      AL(sw.wdT, (int64_t)d * f * es);
+      CK(refresh_shadows(sw.master, 2 * f, d, 1, fsz, sw.wgu, 2LL * f * d, sw.wguT, 2LL * f * d, c->bf16,
+                         c->il ? f : 0, c->stream));
+      CK(refresh_shadows(sw.master + 2LL * f * d, d, f, 1, fsz, sw.wd, (int64_t)d * f, sw.wdT, (int64_t)d * f,
+                         c->bf16, 0, c->stream));
+    }
+    CK(hipStreamSynchronize(c->stream));
   }
   // RoPE table in fp64 on the host, stored fp32: angle = pos * theta^(-2i/hd)
   const int half = hd / 2;
@@ -1100,6 +1178,7 @@ int build(ttt_ctx* c, const ttt_weights* w) {
     AL(c->dzT[j], rows_top * 2 * f * es);
   }
   AL(c->dz, rows_top * 2 * f * es);
+  if (c->dual) AL(c->dzT_s, rows_top * 2 * f * es);
   AL(c->dhT, rows_top * d * es);
   AL(c->dO, rows_top * d * es);
   if (c->bf16) AL(c->dOT, rows_top * d * es);
@@ -1125,6 +1204,10 @@ int build(ttt_ctx* c, const ttt_weights* w) {
     AL(a.zg, rows_top * f * es);
     AL(a.zu, rows_top * f * es);
     AL(a.actT, rows_top * f * es);
+    if (c->dual && j > 0) {
+      AL(a.zg_s, rows_top * f * es);
+      AL(a.zu_s, rows_top * f * es);
+    }
   }
 #undef AL
   return TTT_OK;
@@ -1145,16 +1228,17 @@ hipError_t refresh_fast_shadows(ttt_ctx* c) {
   return hipSuccess;
 }
 
-constexpr int64_t STATE_MAGIC = 0x5354544E49545454LL, STATE_VERSION = 2, STATE_HDR = 16;
+constexpr int64_t STATE_MAGIC = 0x5354544E49545454LL, STATE_VERSION = 3, STATE_HDR = 17;
 
 // Everything a snapshot's contents depend on: the ring keys are stored RoPE-rotated at their
 // absolute positions (theta) in slots pos mod R, so window, chunk and theta must match as well
-// as the array sizes; slot 11 is the position.
+// as the array sizes, and the fast weights are the dynamic MLPs' when dual_mlp is set; slot 11
+// is the position.
 void state_header(const ttt_ctx* c, int64_t* h) {
   int64_t theta_bits = 0;
   memcpy(&theta_bits, &c->cfg.rope_theta, 8);
   const int64_t v[STATE_HDR] = {STATE_MAGIC, STATE_VERSION, c->B, c->L, c->H, c->hd, c->R, (int64_t)c->es, c->Lq, c->f,
-                                c->d, c->pos, c->k, c->b, c->V, theta_bits};
+                                c->d, c->pos, c->k, c->b, c->V, theta_bits, c->dual ? 1 : 0};
   for (int i = 0; i < STATE_HDR; ++i) h[i] = v[i];
 }
 
@@ -1253,6 +1337,12 @@ int ttt_create(const ttt_config* cfg, const ttt_weights* w, void* hip_stream, tt
   if (c0.max_positions <= 0) return bad("max_positions must be positive");
   if (c0.n_steps < 0) return bad("n_steps must be >= 0");
   if (!(c0.rope_theta > 0) || !(c0.rms_eps >= 0) || !std::isfinite(c0.lr)) return bad("bad theta/eps/lr");
+  if (c0.dual_mlp != 0 && c0.dual_mlp != 1) return bad("dual_mlp must be 0 or 1");
+  if (c0.dual_mlp) {
+    if (!w->dyn_gate || !w->dyn_up || !w->dyn_down) return bad("dual_mlp needs the dyn_* weight arrays");
+    for (int j = 0; j < c0.n_fast; ++j)
+      if (!w->dyn_gate[j] || !w->dyn_up[j] || !w->dyn_down[j]) return bad("NULL dynamic MLP weight pointer");
+  }
   if (!w->embed || !w->final_norm || !w->lm_head || !w->attn_norm || !w->wq || !w->wk || !w->wv || !w->wo ||
       !w->mlp_norm || !w->w_gate || !w->w_up || !w->w_down)
     return bad("NULL weight pointer");
@@ -1287,6 +1377,7 @@ int ttt_create(const ttt_config* cfg, const ttt_weights* w, void* hip_stream, tt
   c->B = c0.batch;
   c->G = c0.lookahead;
   c->n_steps = std::max(1, c0.n_steps);
+  c->dual = c0.dual_mlp == 1;
   c->R = c0.window + c0.lookahead * c0.chunk;
   c->bf16 = c0.dtype == TTT_BF16;
   c->es = c->bf16 ? 2 : 4;

@@ -132,10 +132,15 @@ int main() {
     }
   }
 
-  // a NULL weight array is refused too
+  // a NULL weight array is refused too, and so is the dual MLP without its dynamic weights
   Weights w2;
   w2.w.wq = nullptr;
   CHECK(create_rc(good_cfg(), w2, &msg) == TTT_EINVAL);
+  ttt_config cd = good_cfg();
+  cd.dual_mlp = 1;
+  CHECK(create_rc(cd, w, &msg) == TTT_EINVAL && msg.find("dyn_") != std::string::npos);
+  cd.dual_mlp = 2;
+  CHECK(create_rc(cd, w, &msg) == TTT_EINVAL && msg.find("dual_mlp") != std::string::npos);
 
   // allocator hook: both or neither
   CHECK(ttt_set_allocator(hook_alloc, nullptr, nullptr) == TTT_EINVAL);

@@ -29,6 +29,9 @@ def _shape(c):
 
 
 def _w0(w, c):
+    """initial fast weights: the updated blocks' MLPs, or their dynamic MLPs (dual MLP)"""
+    if getattr(c, "dual_mlp", 0):
+        return [(w["dyn_gate"][j], w["dyn_up"][j], w["dyn_down"][j]) for j in range(c.n_fast)]
     return [(w["w_gate"][l], w["w_up"][l], w["w_down"][l]) for l in range(c.n_layers - c.n_fast, c.n_layers)]
 
 
@@ -48,6 +51,8 @@ def compare_fast(gpu_fast, ref_fast, w0, tol, label=""):
 def run_pair(c, T, dist="uniform", tok_seed=1, targets_mask=None, **over):
     bf = c.dtype == "bf16"
     w = synth.weights(_shape(c), bf16=bf)
+    if getattr(c, "dual_mlp", 0):
+        w.update(synth.dynamic_mlp(_shape(c), c.n_fast, bf16=bf))
     seq = synth.tokens(c.batch, T + 1, c.vocab, dist, seed=tok_seed)
     tg = seq[:, 1:].copy()
     if targets_mask is not None:
@@ -499,3 +504,80 @@ def test_several_sgd_steps_per_chunk_against_oracle(dtype, n_steps):
     seq = synth.tokens(c.batch, T + 1, c.vocab, "uniform" if dtype == "f32" else "zipf", seed=1)
     l1 = one.prefill(seq[:, :T], seq[:, 1:])
     assert got[0, 0] == l1[0, 0] and not np.allclose(got, l1)
+
+
+DUAL = {
+    # toy shape, fp32, two fast blocks, ragged last chunk
+    "f32-toy": (dict(TOY, n_fast=2), 300, "uniform"),
+    # d = 256 matrix-core tiles, two fast blocks, ragged last chunk
+    "bf16-mid": (dict(MID), MID_T, "zipf"),
+    # d = 1024: the per-chunk N = d products split K, two fast blocks
+    "bf16-midk2": (dict(MIDK2), MIDK_T, "zipf"),
+    # two rows, some targets ignored
+    "bf16-mid-2rows": (dict(MID, batch=2), 512, "zipf"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(DUAL))
+def test_static_plus_dynamic_mlp_against_oracle(name):
+    """Static + dynamic MLP in the updated blocks (the block's MLP frozen, a dynamic SwiGLU MLP
+    of the same width added and updated): chunk losses and the dynamic weights and their update
+    against the oracle of the same variant.  The update is what tells the variant apart: against
+    the oracle of the model without the static MLPs (the single-MLP model starting from the
+    dynamic weights) the GPU's update is off by far more than the tolerance (about 0.3-0.4 of
+    max |dW| at these shapes, while chunk losses move by under 1 %)."""
+    base, T, dist = DUAL[name]
+    c = mkcfg(**dict(base, dual_mlp=1))
+    mask = None
+    if c.batch > 1:
+        mask = np.zeros((c.batch, T), dtype=bool)
+        mask[1, 5:40] = True
+        mask[0, 200:230] = True
+    print(f"case dual MLP {name}: T={T}", flush=True)
+    w, o, ctx, ref, got = run_pair(c, T, dist=dist, targets_mask=mask)
+    tl, tw = TOL[c.dtype]
+    rel = np.max(np.abs(got - ref) / np.abs(ref))
+    print(f"dual {name}: max loss rel err {rel:.3e}")
+    assert rel <= tl
+    for r in range(c.batch):
+        compare_fast(ctx.fast_weights(r), o.get_fast(r), _w0(w, c), tw, f"dual {name} row {r}")
+    # the same inputs through the oracle of the model without the static MLPs
+    l0 = c.n_layers - c.n_fast
+    w_nostatic = {k: (list(v) if isinstance(v, list) else v) for k, v in w.items()}
+    for j in range(c.n_fast):
+        w_nostatic["w_gate"][l0 + j], w_nostatic["w_up"][l0 + j], w_nostatic["w_down"][l0 + j] = _w0(w, c)[j]
+    seq = synth.tokens(c.batch, T + 1, c.vocab, dist, seed=1)
+    tg = seq[:, 1:].copy()
+    if mask is not None:
+        tg[mask] = -1
+    o2 = Oracle(mkcfg(**base), w_nostatic, T + 8)
+    for st in range(0, T, c.chunk):
+        o2.prefill_chunk(seq[:, st:min(T, st + c.chunk)], tg[:, st:min(T, st + c.chunk)])
+    off = 0.0
+    for j, (g, r, z) in enumerate(zip(ctx.fast_weights(0), o2.get_fast(0), _w0(w, c))):
+        for a in range(3):
+            off = max(off, np.max(np.abs((g[a] - z[a]) - (r[a] - z[a]))) / np.max(np.abs(r[a] - z[a])))
+    print(f"dual {name}: update rel err against the model without static MLPs {off:.3e}")
+    assert off > 5 * tw
+
+
+def test_static_plus_dynamic_mlp_generate_teacher_forced():
+    """Greedy decode with the dual MLP (fp32 toy shape, two fast blocks, an update every 64
+    generated tokens) replayed in the oracle: chosen logits at the oracle's maximum, update losses
+    and the dynamic weights after the updates."""
+    c = mkcfg(**dict(TOY, n_fast=2, dual_mlp=1))
+    w = synth.weights(_shape(c), bf16=False)
+    w.update(synth.dynamic_mlp(_shape(c), c.n_fast, bf16=False))
+    T, n_new = 192, 128
+    seq = synth.tokens(1, T + 1, c.vocab, "uniform", seed=9)
+    ctx = _ctx(c, w, T + n_new + 8)
+    ctx.prefill_seq(seq)
+    toks, upd = ctx.generate(seq[:, T], n_new, 64)
+    o = Oracle(c, w, T + n_new + 8)
+    o.prefill(seq)
+    _, oupd, logits = o.generate(seq[:, T], n_new, 64, forced=toks, want_logits=True)
+    lg = logits[0]
+    tol = 1e-4 * np.max(np.abs(lg))
+    assert np.all(lg.max(axis=1) - lg[np.arange(n_new), toks[0]] <= tol)
+    np.testing.assert_allclose(upd, oupd, rtol=1e-5)
+    compare_fast(ctx.fast_weights(0), o.get_fast(0), _w0(w, c), 1e-4, "dual decode f32")
