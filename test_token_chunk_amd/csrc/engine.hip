@@ -116,6 +116,9 @@ struct ttt_ctx {
   float *dh = nullptr, *tmpf = nullptr, *dq = nullptr, *dk = nullptr, *dv = nullptr, *dvec = nullptr;
   void *dyN = nullptr, *dz = nullptr, *dhT = nullptr, *dO = nullptr, *dOT = nullptr, *dqkv = nullptr;
   void* dzT_s = nullptr;  // dual MLP: transposed dz of the static MLP's backward (written, never read)
+  // dual MLP: the static MLP's activations when both MLPs read the residual stream directly
+  // (decode, norm inside the products): [B * chunk][f]
+  void* act_s = nullptr;
   std::vector<void*> dyT, dzT;  // per fast block: inputs of its weight-gradient GEMMs (side stream)
   int* err_dev = nullptr;
   float* ws = nullptr;  // split-K / split-key workspace (used by one launch at a time)
@@ -412,14 +415,33 @@ hipError_t lmhead_ce(ttt_ctx* c, const void* x, int64_t M, const int32_t* tgt, i
   return ce_rows_ld<T>(c->logits, M, V, tgt, ld, c->nvalid, rpb, c->loss_tok, dl, c->err_dev, c->stream);
 }
 
+// A product whose input rows are RMSNorm(h; gain): with a handful of rows (decode) and nothing
+// of the norm to keep for a backward, the matrix-vector kernel normalizes the fp32 rows itself;
+// returns whether g now reads h that way (else g is unchanged and the norm must run first).
+bool norm_in_product(ttt_ctx* c, const TopActs* sv, GemmArgs& g, const float* h, const float* gain) {
+  static int off = -1;  // tuning switch TTT_NO_NORM_IN_PRODUCT=1: separate norm kernels
+  if (off < 0) {
+    const char* e = getenv("TTT_NO_NORM_IN_PRODUCT");
+    off = e && e[0] == '1' ? 1 : 0;
+  }
+  if (off || sv || !c->bf16 || !c->mfma || c->pend_parts) return false;
+  GemmArgs t = g;
+  t.A = nullptr;
+  t.nx = h;
+  t.ng = gain;
+  t.ldnx = c->d;
+  t.neps = (float)c->cfg.rms_eps;
+  if (!gemv_ok(t)) return false;
+  g = t;
+  return true;
+}
+
 template <typename T>
 int layer_fwd(ttt_ctx* c, int l, float* h, int n, int64_t p0, int mode, TopActs* sv) {
   const int B = c->B, d = c->d, f = c->f;
   const int64_t M = (int64_t)B * n;
   const LayerW& w = c->lw[l];
   if (mode != MLP_ONLY) {
-    CK(norm_fwd<T>(c, h, M, w.attn_norm, tp<T>(c->ub), sv ? sv->rstd1 : c->rstd_tmp, (T*)nullptr, n, 0,
-                   sv ? sv->h_in : nullptr));
     GemmArgs g = mk(c->ub, d, w.wqkv, d, (int)M, 3 * d, d);
     g.e.kind = EPI_F32;
     g.e.c = c->qkvb;
@@ -445,7 +467,11 @@ int layer_fwd(ttt_ctx* c, int l, float* h, int n, int64_t p0, int mode, TopActs*
     GemmArgs gr = g;
     gr.e.kind = EPI_QKV_ROPE;
     gr.e.rr = rr;
-    if (c->mfma && c->bf16 && gemm_mfma_fuses_qkv_rope(gr)) {
+    // (decode: the attention norm inside the product)
+    if (!norm_in_product(c, sv, gr, h, w.attn_norm))
+      CK(norm_fwd<T>(c, h, M, w.attn_norm, tp<T>(c->ub), sv ? sv->rstd1 : c->rstd_tmp, (T*)nullptr, n, 0,
+                     sv ? sv->h_in : nullptr));
+    if (c->mfma && c->bf16 && (gr.nx || gemm_mfma_fuses_qkv_rope(gr))) {
       CK(Ops<T>::gemm(c, gr));
     } else {
       CK(Ops<T>::gemm(c, g));
@@ -478,50 +504,89 @@ int layer_fwd(ttt_ctx* c, int l, float* h, int n, int64_t p0, int mode, TopActs*
     CK(Ops<T>::gemm_parts(c, go, n, So));
     c->pend_parts = So > 1 ? So : 0;
   }
-  CK(norm_fwd<T>(c, h, M, w.mlp_norm, tp<T>(c->ub), sv ? sv->rstd2 : c->rstd_tmp, sv ? tp<T>(sv->mT) : (T*)nullptr,
-                 n, c->b, sv ? sv->h_mid : nullptr));
-  if (l >= c->l0) {
+  // the MLP products that read the normed rows m: the static and the dynamic MLP (fast blocks,
+  // dual MLP), the fast MLP (batched over rows: each row has its own weights) or the frozen one
+  const bool fast = l >= c->l0;
+  GemmArgs gs, gu;
+  if (fast && c->dual) {
+    const FastW& st = c->sw[l - c->l0];
+    gs = mk(c->ub, d, st.wgu, d, (int)M, c->il ? 2 * f : f, d);
+    gs.dual_off = c->il ? 0 : f;
+    gs.e.kind = c->il ? EPI_SWIGLU_IL : EPI_SWIGLU;
+    gs.e.c = c->actb;
+    gs.e.ldc = f;
+    if (sv && sv->zg_s) {  // pre-activations for the backward of blocks above l0
+      gs.e.zg = sv->zg_s;
+      gs.e.zu = sv->zu_s;
+      gs.e.ldz = f;
+    }
+  }
+  if (fast) {
+    const FastW& fw = c->fw[l - c->l0];
+    gu = mk(c->ub, d, fw.wgu, d, n, c->il ? 2 * f : f, d);
+    gu.batch = B;
+    gu.sA = (int64_t)n * d;
+    gu.sB = 2LL * f * d;
+    gu.dual_off = c->il ? 0 : f;
+    gu.e.kind = c->il ? EPI_SWIGLU_IL : EPI_SWIGLU;
+    gu.e.c = c->actb;
+    gu.e.ldc = f;
+    gu.e.sc = (int64_t)n * f;
+    if (sv) {
+      gu.e.zg = sv->zg;
+      gu.e.zu = sv->zu;
+      gu.e.ldz = f;
+      gu.e.sz = (int64_t)n * f;
+      gu.e.t = sv->actT;
+      gu.e.ldt = c->b;
+      gu.e.st = (int64_t)f * c->b;
+    }
+  } else {
+    gu = mk(c->ub, d, w.wgu, d, (int)M, c->il ? 2 * f : f, d);
+    gu.dual_off = c->il ? 0 : f;
+    gu.e.kind = c->il ? EPI_SWIGLU_IL : EPI_SWIGLU;
+    gu.e.c = c->actb;
+    gu.e.ldc = f;
+  }
+  // (decode: the MLP norm inside those products when all of them take it)
+  bool in_product = false;
+  {
+    GemmArgs ts = gs, tu = gu;
+    const bool both = fast && c->dual;
+    if (norm_in_product(c, sv, tu, h, w.mlp_norm) && (!both || norm_in_product(c, sv, ts, h, w.mlp_norm))) {
+      gu = tu;
+      gs = ts;
+      in_product = true;
+    } else {
+      CK(norm_fwd<T>(c, h, M, w.mlp_norm, tp<T>(c->ub), sv ? sv->rstd2 : c->rstd_tmp,
+                     sv ? tp<T>(sv->mT) : (T*)nullptr, n, c->b, sv ? sv->h_mid : nullptr));
+    }
+  }
+  if (fast) {
     if (c->dual) {
       // the frozen static MLP on the same normed input, all rows at once; its output is added to
-      // the residual stream here, the dynamic MLP's below
+      // the residual stream after the dynamic MLP's gate/up product has read that stream (when
+      // the norm runs inside the products, both read h itself: the static activations go to
+      // their own buffer), else right away
       const FastW& st = c->sw[l - c->l0];
-      GemmArgs gs = mk(c->ub, d, st.wgu, d, (int)M, c->il ? 2 * f : f, d);
-      gs.dual_off = c->il ? 0 : f;
-      gs.e.kind = c->il ? EPI_SWIGLU_IL : EPI_SWIGLU;
-      gs.e.c = c->actb;
-      gs.e.ldc = f;
-      if (sv && sv->zg_s) {  // pre-activations for the backward of blocks above l0
-        gs.e.zg = sv->zg_s;
-        gs.e.zu = sv->zu_s;
-        gs.e.ldz = f;
-      }
-      CK(Ops<T>::gemm(c, gs));
-      GemmArgs gds = mk(c->actb, f, st.wd, f, (int)M, d, f);
+      GemmArgs gds = mk(in_product ? c->act_s : c->actb, f, st.wd, f, (int)M, d, f);
       gds.e.kind = EPI_ADD_F32;
       gds.e.c = h;
       gds.e.ldc = d;
-      CK(Ops<T>::gemm(c, gds));
+      if (in_product) {
+        gs.e.c = c->act_s;
+        CK(Ops<T>::gemm(c, gs));
+        CK(Ops<T>::gemm(c, gu));
+        CK(Ops<T>::gemm(c, gds));
+      } else {
+        CK(Ops<T>::gemm(c, gs));
+        CK(Ops<T>::gemm(c, gds));
+        CK(Ops<T>::gemm(c, gu));
+      }
+    } else {
+      CK(Ops<T>::gemm(c, gu));
     }
     const FastW& fw = c->fw[l - c->l0];
-    GemmArgs g = mk(c->ub, d, fw.wgu, d, n, c->il ? 2 * f : f, d);
-    g.batch = B;
-    g.sA = (int64_t)n * d;
-    g.sB = 2LL * f * d;
-    g.dual_off = c->il ? 0 : f;
-    g.e.kind = c->il ? EPI_SWIGLU_IL : EPI_SWIGLU;
-    g.e.c = c->actb;
-    g.e.ldc = f;
-    g.e.sc = (int64_t)n * f;
-    if (sv) {
-      g.e.zg = sv->zg;
-      g.e.zu = sv->zu;
-      g.e.ldz = f;
-      g.e.sz = (int64_t)n * f;
-      g.e.t = sv->actT;
-      g.e.ldt = c->b;
-      g.e.st = (int64_t)f * c->b;
-    }
-    CK(Ops<T>::gemm(c, g));
     GemmArgs gd = mk(c->actb, f, fw.wd, f, n, d, f);
     gd.batch = B;
     gd.sA = (int64_t)n * f;
@@ -534,12 +599,7 @@ int layer_fwd(ttt_ctx* c, int l, float* h, int n, int64_t p0, int mode, TopActs*
     CK(Ops<T>::gemm_parts(c, gd, n, Sd));
     c->pend_parts = Sd > 1 ? Sd : 0;
   } else {
-    GemmArgs g = mk(c->ub, d, w.wgu, d, (int)M, c->il ? 2 * f : f, d);
-    g.dual_off = c->il ? 0 : f;
-    g.e.kind = c->il ? EPI_SWIGLU_IL : EPI_SWIGLU;
-    g.e.c = c->actb;
-    g.e.ldc = f;
-    CK(Ops<T>::gemm(c, g));
+    CK(Ops<T>::gemm(c, gu));
     GemmArgs gd = mk(c->actb, f, w.wd, f, (int)M, d, f);
     gd.e.kind = EPI_ADD_F32;
     gd.e.c = h;
@@ -914,11 +974,13 @@ int decode_step(ttt_ctx* c, int32_t* tok, int64_t ld) {
     int rc = layer_fwd<T>(c, l, c->hb, 1, c->pos, FULL, nullptr);
     if (rc) return rc;
   }
-  CK(norm_fwd<T>(c, c->hb, B, c->final_norm, tp<T>(c->hf), c->rstd_tmp, (T*)nullptr, 1, 0, nullptr));
   GemmArgs gl = mk(c->hf, d, c->lm_head, d, B, c->V, d);
   gl.e.kind = EPI_F32;
   gl.e.c = c->logits;
   gl.e.ldc = c->V;
+  // (the final norm inside the lm_head product when it takes it)
+  if (!norm_in_product(c, nullptr, gl, c->hb, c->final_norm))
+    CK(norm_fwd<T>(c, c->hb, B, c->final_norm, tp<T>(c->hf), c->rstd_tmp, (T*)nullptr, 1, 0, nullptr));
   CK(Ops<T>::gemm(c, gl));
   CK(argmax_rows_ld(c->logits, B, c->V, tok + 1, ld, nullptr, 0, c->stream));
   c->pos += 1;
@@ -1178,7 +1240,10 @@ int build(ttt_ctx* c, const ttt_weights* w) {
     AL(c->dzT[j], rows_top * 2 * f * es);
   }
   AL(c->dz, rows_top * 2 * f * es);
-  if (c->dual) AL(c->dzT_s, rows_top * 2 * f * es);
+  if (c->dual) {
+    AL(c->dzT_s, rows_top * 2 * f * es);
+    AL(c->act_s, rows_top * f * es);
+  }
   AL(c->dhT, rows_top * d * es);
   AL(c->dO, rows_top * d * es);
   if (c->bf16) AL(c->dOT, rows_top * d * es);

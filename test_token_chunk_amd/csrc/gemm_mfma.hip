@@ -1304,6 +1304,7 @@ bool gemm_mfma_fuses_lm_ce(const GemmArgs& g) {
 
 bool gemm_mfma_fuses_qkv_rope(const GemmArgs& g) {
   if (g.e.kind != EPI_QKV_ROPE || g.M <= 0) return false;
+  if (g.nx) return gemv_ok(g);
   if (!(aligned16(g.A) && aligned16(g.B) && g.lda % 8 == 0 && g.ldb % 8 == 0)) return false;
   return gemv_ok(g) || wide_ok(g);
 }
@@ -1318,6 +1319,8 @@ int gemm_mfma_splits(const GemmArgs& g, int* ks_out) {
 
 hipError_t gemm_mfma_bf16(const GemmArgs& g, hipStream_t s) {
   if (g.M <= 0 || g.N <= 0 || g.batch <= 0) return hipSuccess;
+  // rows normalized in the kernel: only the matrix-vector form does that
+  if (g.nx) return gemv_ok(g) ? gemv_bf16(g, s) : hipErrorInvalidValue;
   // 16-byte vector loads need 8-element aligned rows and batch strides
   bool ok = aligned16(g.A) && aligned16(g.B) && g.lda % 8 == 0 && g.ldb % 8 == 0 && g.sA % 8 == 0 &&
             g.sB % 8 == 0 && (g.dual_off * g.ldb) % 8 == 0 && g.K >= 1;

@@ -78,5 +78,6 @@ hipError_t launch(const GemmArgs& g, hipStream_t s) {
 
 }  // namespace
 
-hipError_t gemm_simt_f32(const GemmArgs& g, hipStream_t s) { return launch<float>(g, s); }
-hipError_t gemm_simt_bf16(const GemmArgs& g, hipStream_t s) { return launch<bf16>(g, s); }
+// (rows normalized inside the product are a matrix-vector-kernel feature only)
+hipError_t gemm_simt_f32(const GemmArgs& g, hipStream_t s) { return g.nx ? hipErrorInvalidValue : launch<float>(g, s); }
+hipError_t gemm_simt_bf16(const GemmArgs& g, hipStream_t s) { return g.nx ? hipErrorInvalidValue : launch<bf16>(g, s); }

@@ -9,6 +9,12 @@
 // the matrix-core GEMM (fp32, bf16, residual add, SwiGLU with separate or interleaved gate/up
 // rows) and, for the q|k|v projection, RoPE with the writes into the key/value ring
 // (EPI_QKV_ROPE: a wave takes the column pair i, i + hd/2 of one head).
+//
+// NRM: the input rows are the RMSNorm of fp32 residual-stream rows, formed by the block itself:
+// W . (x * rstd * g) = rstd * (W . (x * g)), so the block's threads first write x * g as bf16 to
+// LDS (one pass over the rows for all its waves) and sum x^2 per row, then the waves run their
+// dot products from LDS and scale the sums by rstd = 1 / sqrt(mean(x^2) + eps) at the end -- no
+// separate normalization kernel and no normalized copy of the rows in memory.
 #include "kernels.h"
 
 namespace {
@@ -65,17 +71,23 @@ __device__ __forceinline__ void qkv_rope_store(const RopeRing& rr, int part, int
   }
 }
 
-template <int MR, int NR, int KIND>
+__device__ __forceinline__ uint32_t pkbf(float a, float b) {
+  return (uint32_t)f2bf(a).x | ((uint32_t)f2bf(b).x << 16);
+}
+
+template <int MR, int NR, int KIND, bool NRM>
 __global__ __launch_bounds__(256) void k_gemv(GemmArgs g, int ncols, int f) {
   constexpr bool SW = KIND == EPI_SWIGLU || KIND == EPI_SWIGLU_IL;
   constexpr bool RP = KIND == EPI_QKV_ROPE;  // NR == 2: the pair (i, i + hd/2); ncols = pairs
   constexpr int RW = SW ? 2 * NR : NR;  // weight rows per wave
   static_assert(!RP || NR == 2, "a RoPE wave holds the two rows of one rotation pair");
   constexpr int U = MR <= 2 ? 4 : 2;    // 512-element steps per trip
-  const int lane = threadIdx.x & 63;
-  const int64_t wv = (int64_t)blockIdx.x * GW + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int64_t wv = (int64_t)blockIdx.x * GW + wid;
   const int64_t j0 = RP ? wv : wv * NR;
-  if (j0 >= ncols) return;
+  // (NRM: every wave takes part in staging the rows and reaches the barrier after it)
+  if (!NRM && j0 >= ncols) return;
+  const bool active = j0 < ncols;
   const int64_t bz = blockIdx.y;
   const bf16* A = (const bf16*)g.A + bz * g.sA;
   const bf16* W = (const bf16*)g.B + bz * g.sB;
@@ -83,9 +95,10 @@ __global__ __launch_bounds__(256) void k_gemv(GemmArgs g, int ncols, int f) {
   int part = 0, ph = 0, pi = 0;
   if constexpr (RP) {
     const int half = g.e.rr.hd / 2, hpart = g.e.rr.H * half;
-    part = (int)(j0 / hpart);
-    ph = (int)(j0 % hpart) / half;
-    pi = (int)(j0 % hpart) % half;
+    const int64_t jr = active ? j0 : 0;  // (an idle wave's pointers are never read through)
+    part = (int)(jr / hpart);
+    ph = (int)(jr % hpart) / half;
+    pi = (int)(jr % hpart) % half;
     const int64_t c0 = (int64_t)part * g.e.rr.H * g.e.rr.hd + (int64_t)ph * g.e.rr.hd + pi;
     if (g.e.rr.perm && part < 2) {  // pair-interleaved q/k rows: dims pi and pi + hd/2 are adjacent
       const int64_t r0 = (int64_t)part * g.e.rr.H * g.e.rr.hd + (int64_t)ph * g.e.rr.hd + 2 * pi;
@@ -117,6 +130,43 @@ __global__ __launch_bounds__(256) void k_gemv(GemmArgs g, int ncols, int f) {
   for (int r = 0; r < RW; ++r)
 #pragma unroll
     for (int m = 0; m < MR; ++m) acc[r][m] = 0.f;
+  // NRM: rows m < M of x * g as bf16, [MR][K / 8] pieces of 16 bytes, and the 1 / rms of each row
+  extern __shared__ uint4 xs[];
+  __shared__ float red[GW][MR];
+  float rstd[MR];
+  if constexpr (NRM) {
+    const float* X = g.nx + bz * (int64_t)M * g.ldnx;
+    float ssl[MR];
+#pragma unroll
+    for (int m = 0; m < MR; ++m) ssl[m] = 0.f;
+    for (int k = 8 * (int)threadIdx.x; k < K; k += 8 * 64 * GW) {
+      const float4 g0 = *(const float4*)(g.ng + k), g1 = *(const float4*)(g.ng + k + 4);
+#pragma unroll
+      for (int m = 0; m < MR; ++m) {
+        if (m >= M) break;
+        const float* xr = X + (int64_t)m * g.ldnx + k;
+        const float4 x0 = *(const float4*)xr, x1 = *(const float4*)(xr + 4);
+        ssl[m] += (x0.x * x0.x + x0.y * x0.y) + (x0.z * x0.z + x0.w * x0.w) + (x1.x * x1.x + x1.y * x1.y) +
+                  (x1.z * x1.z + x1.w * x1.w);
+        xs[m * (K / 8) + k / 8] = make_uint4(pkbf(x0.x * g0.x, x0.y * g0.y), pkbf(x0.z * g0.z, x0.w * g0.w),
+                                             pkbf(x1.x * g1.x, x1.y * g1.y), pkbf(x1.z * g1.z, x1.w * g1.w));
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+      const float t = warp_sum(ssl[m]);
+      if (lane == 0) red[wid][m] = t;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+      float t = 0.f;
+#pragma unroll
+      for (int w = 0; w < GW; ++w) t += red[w][m];
+      rstd[m] = rsqrtf(t / (float)K + g.neps);
+    }
+    if (!active) return;
+  }
   for (int k0 = 8 * lane; k0 < K; k0 += 512 * U) {
     uint4 wv[U][RW], xv[U][MR];
 #pragma unroll
@@ -125,9 +175,15 @@ __global__ __launch_bounds__(256) void k_gemv(GemmArgs g, int ncols, int f) {
       // rows m >= M repeat row M - 1 (their sums are not stored); pieces past K add zero
 #pragma unroll
       for (int r = 0; r < RW; ++r) wv[u][r] = k < K ? *(const uint4*)(wr[r] + k) : make_uint4(0u, 0u, 0u, 0u);
+      if constexpr (NRM) {
 #pragma unroll
-      for (int m = 0; m < MR; ++m)
-        xv[u][m] = k < K ? *(const uint4*)(A + (int64_t)(m < M ? m : M - 1) * g.lda + k) : make_uint4(0u, 0u, 0u, 0u);
+        for (int m = 0; m < MR; ++m)
+          xv[u][m] = k < K ? xs[(m < M ? m : M - 1) * (K / 8) + k / 8] : make_uint4(0u, 0u, 0u, 0u);
+      } else {
+#pragma unroll
+        for (int m = 0; m < MR; ++m)
+          xv[u][m] = k < K ? *(const uint4*)(A + (int64_t)(m < M ? m : M - 1) * g.lda + k) : make_uint4(0u, 0u, 0u, 0u);
+      }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u)
@@ -140,6 +196,12 @@ __global__ __launch_bounds__(256) void k_gemv(GemmArgs g, int ncols, int f) {
   for (int r = 0; r < RW; ++r)
 #pragma unroll
     for (int m = 0; m < MR; ++m) acc[r][m] = warp_sum(acc[r][m]);
+  if constexpr (NRM) {
+#pragma unroll
+    for (int m = 0; m < MR; ++m)
+#pragma unroll
+      for (int r = 0; r < RW; ++r) acc[r][m] *= rstd[m];
+  }
   if (lane != 0) return;
   const Epi& e = g.e;
   if constexpr (RP) {
@@ -173,8 +235,11 @@ template <int MR, int NR, int KIND>
 hipError_t launch_gemv(const GemmArgs& g, int ncols, int f, hipStream_t s) {
   // one wave per NR columns, or per column pair (ncols counts pairs) with RoPE
   const int64_t waves = KIND == EPI_QKV_ROPE ? ncols : (ncols + NR - 1) / NR;
-  hipLaunchKernelGGL((k_gemv<MR, NR, KIND>), dim3((unsigned)((waves + GW - 1) / GW), (unsigned)g.batch),
-                     dim3(64 * GW), 0, s, g, ncols, f);
+  const dim3 grid((unsigned)((waves + GW - 1) / GW), (unsigned)g.batch);
+  if (g.nx)  // rows of x * g staged in LDS: MR * K bf16 (gemv_ok keeps it within 64 KB)
+    hipLaunchKernelGGL((k_gemv<MR, NR, KIND, true>), grid, dim3(64 * GW), (size_t)MR * g.K * 2, s, g, ncols, f);
+  else
+    hipLaunchKernelGGL((k_gemv<MR, NR, KIND, false>), grid, dim3(64 * GW), 0, s, g, ncols, f);
   return hipGetLastError();
 }
 
@@ -222,17 +287,22 @@ bool al16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 bool gemv_ok(const GemmArgs& g) {
   const int k = g.e.kind;
   if (g.M < 1 || g.M > 8 || g.N < 1 || g.K < 8 || g.K % 8 != 0 || g.batch < 1) return false;
+  // the input rows: A (bf16), or fp32 rows normalized in the kernel (nx, 16-byte pieces)
+  // (with nx the block stages MR * K bf16 in LDS, MR = M rounded up to 1, 2, 4 or 8)
+  const int mr = g.M <= 1 ? 1 : g.M <= 2 ? 2 : g.M <= 4 ? 4 : 8;
+  const bool in_ok = g.nx ? (g.ng && al16(g.nx) && al16(g.ng) && g.ldnx >= g.K && g.ldnx % 4 == 0 &&
+                             (int64_t)mr * g.K * 2 <= 65536)
+                          : (al16(g.A) && g.lda % 8 == 0 && g.sA % 8 == 0);
+  if (!in_ok) return false;
   if (k == EPI_QKV_ROPE) {
     const RopeRing& r = g.e.rr;
     return g.batch == 1 && r.hd > 0 && r.hd % 2 == 0 && r.H > 0 && g.N == 3 * r.H * r.hd && r.n > 0 &&
-           g.M % r.n == 0 && r.R > 0 && r.q && r.kr && r.vr && r.cos_t && r.sin_t && al16(g.A) && al16(g.B) &&
-           g.lda % 8 == 0 && g.ldb % 8 == 0;
+           g.M % r.n == 0 && r.R > 0 && r.q && r.kr && r.vr && r.cos_t && r.sin_t && al16(g.B) && g.ldb % 8 == 0;
   }
   if (k != EPI_F32 && k != EPI_T && k != EPI_ADD_F32 && k != EPI_SWIGLU && k != EPI_SWIGLU_IL) return false;
   if ((k == EPI_SWIGLU || k == EPI_SWIGLU_IL) && (g.e.zg || g.e.zu || g.e.t)) return false;
   if (k == EPI_SWIGLU_IL && (g.N % 64 != 0 || g.dual_off != 0)) return false;
-  return g.e.c && al16(g.A) && al16(g.B) && g.lda % 8 == 0 && g.ldb % 8 == 0 && g.sA % 8 == 0 && g.sB % 8 == 0 &&
-         (g.dual_off * g.ldb) % 8 == 0;
+  return g.e.c && al16(g.B) && g.ldb % 8 == 0 && g.sB % 8 == 0 && (g.dual_off * g.ldb) % 8 == 0;
 }
 
 hipError_t gemv_bf16(const GemmArgs& g, hipStream_t s) {

@@ -102,6 +102,13 @@ struct GemmArgs {
   // runs on a side stream beside latency-bound work: take the form that holds fewer resources per
   // CU (the fused-SGD 128 x 128 loop with three LDS stages: one block per CU instead of two)
   bool background = false;
+  // input rows normalized inside the product (matrix-vector form only, see gemv_ok): with nx set,
+  // input row m of batch b is RMSNorm(x; ng, neps) of the fp32 row x = nx + (b * M + m) * ldnx
+  // (K elements), and A is not read
+  const float* nx = nullptr;
+  const float* ng = nullptr;
+  int64_t ldnx = 0;
+  float neps = 0.f;
 };
 
 hipError_t gemm_simt_f32(const GemmArgs& g, hipStream_t s);   // fp32 operands
@@ -114,7 +121,8 @@ bool gemm_mfma_fuses_qkv_rope(const GemmArgs& g);
 // M <= 8 rows per batch (decode), bf16 operands: one read of the weight rows per product;
 // kinds EPI_F32, EPI_T, EPI_ADD_F32 and the SwiGLU kinds without z_g / z_u / act^T outputs,
 // K % 8 == 0, 16-byte aligned operands and 8-element strides (gemv_ok); gemm_mfma_bf16 takes
-// it by itself for such products
+// it by itself for such products; with g.nx it normalizes the input rows itself (the product
+// of the RMSNorm of a handful of residual-stream rows, in one kernel)
 bool gemv_ok(const GemmArgs& g);
 hipError_t gemv_bf16(const GemmArgs& g, hipStream_t s);
 
