@@ -336,8 +336,11 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(GemmArgs g) {
 // straight from global memory into LDS (global_load_lds_dwordx4: lane L of a wave writes
 // 16 bytes at the wave's LDS address + 16 L) through a ring of STAGES buffers, so loads run
 // STAGES-1 K steps ahead without staging registers.  LDS rows are 128 bytes with the
-// 16-byte chunks XOR-swizzled by (row & 7), which keeps the operand reads of a wave on
-// distinct banks.  Requires M, N multiples of 128 and a K range that is a multiple of 64.
+// 16-byte chunks XOR-swizzled by (row / 2) % 8: a 16-byte fragment read serves 16 lanes (16
+// consecutive rows) per pass, and rows 2t and 2t + 1 fall into the two 128-byte halves of the
+// banks, so the 16 rows take 16 distinct (half, chunk) places -- no bank conflicts (with
+// row % 8, rows r and r + 8 collided).  Requires M, N multiples of 128 and a K range that is a
+// multiple of 64.
 
 constexpr int DL_TILE_BYTES = (128 + 128) * BK * 2;  // one stage: A and B tiles
 
@@ -439,8 +442,8 @@ __global__ __launch_bounds__(256) void k_gemm_dl(GemmArgs g) {
     unsigned char* base = smem_raw + (kt % STAGES) * DL_TILE_BYTES;
     const int k0 = kbeg + kt * BK;
     const int blk = wid * 4 + i;          // 8-row block of the tile (1 KB)
-    const int r = blk * 8 + (lane >> 3);  // tile row of this lane
-    const int c = (lane & 7) ^ (r & 7);   // logical chunk that lands at physical chunk lane & 7
+    const int r = blk * 8 + (lane >> 3);     // tile row of this lane
+    const int c = (lane & 7) ^ ((r >> 1) & 7);  // logical chunk that lands at physical chunk lane & 7
     __builtin_amdgcn_global_load_lds(A + (int64_t)(m0 + r) * g.lda + k0 + c * 8, LDSP(base + blk * 1024), 16, 0, 0);
     __builtin_amdgcn_global_load_lds(B + (int64_t)(n0 + r) * g.ldb + k0 + c * 8,
                                      LDSP(base + BM * BK * 2 + blk * 1024), 16, 0, 0);
@@ -462,7 +465,7 @@ __global__ __launch_bounds__(256) void k_gemm_dl(GemmArgs g) {
   float4 pre[SGD ? 2 : 1][SGD ? 2 : 1][SGD ? 4 : 1];
   if constexpr (SGD) dl_sgd_prefetch(g, pre, m0, n0, wm0, wn0, lane, bz);
 
-  const int lr = lane & 31, lk = (lane >> 5) * 8, sw = lr & 7;
+  const int lr = lane & 31, lk = (lane >> 5) * 8, sw = (lr >> 1) & 7;  // (wm0 + 32 i keeps the swizzle)
   for (int st = 0; st < STAGES - 1 && st < nk; ++st) issue(st);
   for (int kt = 0; kt < nk; ++kt) {
     const int later = min(STAGES - 2, nk - 1 - kt);  // tiles issued after tile kt
