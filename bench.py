@@ -143,21 +143,23 @@ def cpu_baseline(c: dict, w: dict, seq: np.ndarray, sample_tokens: int) -> dict:
                                                    f"with a full {k}-key window (extrapolated, not measured)"}}
 
 
-def measured_traffic(kernel: str, config: str):
-    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary, or None when
-    there is none for this kernel and workload or the kernel's source changed since it was taken."""
+def measured_traffic(kernel: str, cls: str, config: str):
+    """HBM bytes per launch of the roofline kernel (class `cls`) from a committed rocprofv3 counter
+    summary (profiles/*_hbm_traffic.txt: FETCH_SIZE and WRITE_SIZE scaled by a plain copy of known
+    size), or None when there is none for this kernel and workload or the kernel's source changed
+    since the counters were taken."""
+    import glob
     import hashlib
-    path = os.path.join(ROOT, "profiles", "k_swa_fwd_3b_hbm_traffic.txt")
-    if not os.path.exists(path):
-        return None
-    kv = dict(line.split(": ", 1) for line in open(path).read().splitlines()
-              if ": " in line and not line.startswith("#"))
-    src = os.path.join(ROOT, kv.get("source", "-"))
-    if kv.get("kernel") != kernel or kv.get("config") != config or not os.path.exists(src):
-        return None
-    if hashlib.sha256(open(src, "rb").read()).hexdigest() != kv.get("source_sha256"):
-        return None
-    return float(kv["traffic_bytes_per_launch"])
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*_hbm_traffic.txt"))):
+        kv = dict(line.split(": ", 1) for line in open(path).read().splitlines()
+                  if ": " in line and not line.startswith("#"))
+        if kv.get("config") != config or (kv.get("class") != cls and kv.get("kernel") != kernel):
+            continue
+        src = os.path.join(ROOT, kv.get("source", "-"))
+        if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest() != kv.get("source_sha256"):
+            return None
+        return float(kv["traffic_bytes_per_launch"])
+    return None
 
 
 def main():
@@ -280,7 +282,7 @@ def main():
         kname = PROFILE_KERNELS[name][0].replace("hd", str(hd))
         roof = {"kernel": kname, "class": name, "bound": "mfma", "achieved": round(achieved, 1),
                 "peak": peak / 1e12, "unit": "TFLOP/s", "frac": round(achieved / (peak / 1e12), 4),
-                "traffic": measured_traffic(kname, args.config),
+                "traffic": measured_traffic(kname, name, args.config),
                 "avg_launch_us": round(avg_s * 1e6, 2), "launches_per_step": st["count"] // args.steps,
                 "gflop_per_launch": round(flops_per_launch / 1e9, 3),
                 "share_of_device_time": round(kstats[name]["ms"] / sum(v["ms"] for v in kstats.values()), 4)}
