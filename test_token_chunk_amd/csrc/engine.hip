@@ -1326,9 +1326,18 @@ hipError_t for_state_arrays(ttt_ctx* c, F&& f) {
   return hipSuccess;
 }
 
+// the batched and side streams finished (a failed call may leave work in flight there)
+hipError_t sync_aux(ttt_ctx* c) {
+  if (c->bstream) {
+    hipError_t e = hipStreamSynchronize(c->bstream);
+    if (e != hipSuccess) return e;
+  }
+  return c->side ? hipStreamSynchronize(c->side) : hipSuccess;
+}
+
 int reset_state(ttt_ctx* c) {
-  // (a failed call may have left a batched pass in flight on the batched stream)
-  if (c->bstream) CK(hipStreamSynchronize(c->bstream));
+  // (a failed call may have left a batched pass or updates in flight on the other streams)
+  CK(sync_aux(c));
   c->pend_parts = 0;
   const int64_t fsz = 3LL * c->f * c->d;
   for (int j = 0; j < c->Lq; ++j) {
@@ -1569,7 +1578,7 @@ int ttt_score(ttt_ctx* c, const int32_t* tokens, const int32_t* targets, int64_t
   int rc;
   if ((rc = ensure_tok(c, 2 * cnt))) return rc;
   if ((rc = ensure_loss(c, nch * c->B))) return rc;
-  if (c->bstream) CK(hipStreamSynchronize(c->bstream));
+  CK(sync_aux(c));
   CK(hipMemcpyAsync(c->d_tok, tokens, cnt * 4, hipMemcpyHostToDevice, c->stream));
   CK(hipMemcpyAsync(c->d_tok + cnt, targets, cnt * 4, hipMemcpyHostToDevice, c->stream));
   rc = score_dispatch(c, c->d_tok, c->d_tok + cnt, n_tokens, n_tokens, c->d_loss);
@@ -1687,7 +1696,7 @@ int ttt_set_fast_weights(ttt_ctx* c, int32_t row, const float* src, int64_t n_fl
   if (!src || row < 0 || row >= c->B) return fail(c, TTT_EINVAL, "bad row or NULL src");
   const int64_t fsz = 3LL * c->f * c->d;
   if (n_floats != fsz * c->Lq) return fail(c, TTT_EINVAL, "n_floats must be 3*d*f*n_fast");
-  if (c->bstream) CK(hipStreamSynchronize(c->bstream));
+  CK(sync_aux(c));
   for (int j = 0; j < c->Lq; ++j)
     CK(hipMemcpyAsync(c->fw[j].master + row * fsz, src + j * fsz, fsz * 4, hipMemcpyHostToDevice, c->stream));
   CK(refresh_fast_shadows(c));
@@ -1709,7 +1718,7 @@ int ttt_save_state(ttt_ctx* c, void* dst, int64_t nbytes) {
   if (!c) return TTT_EINVAL;
   if (c->poisoned) return fail(c, TTT_ESTATE, "context poisoned; call ttt_reset");
   if (!dst || nbytes < ttt_state_size(c)) return fail(c, TTT_EINVAL, "NULL dst or nbytes below ttt_state_size");
-  if (c->bstream) CK(hipStreamSynchronize(c->bstream));
+  CK(sync_aux(c));
   // device-side errors of earlier asynchronous work (a bad id, a non-finite loss) poison the
   // context here instead of travelling inside the snapshot
   {
@@ -1737,7 +1746,7 @@ int ttt_load_state(ttt_ctx* c, const void* src, int64_t nbytes) {
   for (int i = 0; i < STATE_HDR; ++i)
     if (i != 11 && got[i] != want[i]) return fail(c, TTT_EINVAL, "snapshot of another configuration");
   if (got[11] < 0 || got[11] > c->cfg.max_positions) return fail(c, TTT_EINVAL, "snapshot position out of range");
-  if (c->bstream) CK(hipStreamSynchronize(c->bstream));
+  CK(sync_aux(c));
   CK(hipStreamSynchronize(c->stream));
   const char* p = (const char*)src + STATE_HDR * 8;
   CK(for_state_arrays(c, [&](void* a, int64_t bytes) {
