@@ -180,6 +180,8 @@ def main():
     ap.add_argument("--dual-mlp", action="store_true",
                     help="static + dynamic MLP in every updated block (the dynamic one is updated)")
     ap.add_argument("--decode-tokens", type=int, default=1024, help="decode: generated tokens per step")
+    ap.add_argument("--no-isolated", action="store_true",
+                    help="skip the extra profiled step with the streams serialized (kernel_top_isolated)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device-to-device copy 3 times (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -304,6 +306,40 @@ def main():
             gbs = sgd_bytes_per_row(c, T, args.n_steps) / (e["ms_per_step"] / 1e3) / 1e9
             e.update({"bound": "hbm", "gbps": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4),
                       "mfma_frac": e["frac"]})
+    iso = None
+    if not args.no_isolated:
+        # One more (untimed) step in a fresh context with every launch on one stream: per-class
+        # device time of each kernel alone on the GPU.  In the measured step the three streams
+        # time-slice the CUs, so a class's event time there includes the other streams' kernels.
+        ctx.close()
+        saved = {k: os.environ.get(k) for k in ("TTT_NO_SIDE", "TTT_NO_BOTTOM_OVERLAP")}
+        os.environ.update(TTT_NO_SIDE="1", TTT_NO_BOTTOM_OVERLAP="1")
+        try:
+            ctx = TTTContext(cfg, w)
+        finally:
+            for k, v in saved.items():
+                if v is None:
+                    os.environ.pop(k, None)
+                else:
+                    os.environ[k] = v
+        ctx.profile_begin()
+        t0 = time.perf_counter()
+        step()
+        iso_ms = (time.perf_counter() - t0) * 1e3
+        istats = ctx.profile_end()
+        ctx.close()
+        iso_top = sorted(istats.items(), key=lambda kv: -kv[1]["ms"])[:8]
+        iso = {"step_ms_serial_with_events": round(iso_ms, 1),
+               "device_ms_per_step": round(sum(v["ms"] for v in istats.values()), 1), "classes": []}
+        for k, v in iso_top:
+            e = {"class": k, "ms_per_step": round(v["ms"], 2),
+                 "tflops": round(v["flops"] / max(v["ms"], 1e-9) / 1e9, 1),
+                 "frac": round(v["flops"] / max(v["ms"], 1e-9) / 1e9 / (peak / 1e12), 4)}
+            if k in HBM_CLASSES:
+                gbs = sgd_bytes_per_row(c, T, args.n_steps) / (v["ms"] / 1e3) / 1e9
+                e.update({"bound": "hbm", "gbps": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4),
+                          "mfma_frac": e["frac"]})
+            iso["classes"].append(e)
     out = {
         "metric": "TTT prefill tokens/s (fwd+inner-loop bwd+update) and % bf16 MFMA peak",
         "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -322,6 +358,7 @@ def main():
         "kernel_classes": {k: {"ms_per_step": round(v["ms"], 3), "tflops": round(
             v["flops"] / max(v["ms"], 1e-9) / 1e9, 1)} for k, v in kstats.items()},
         "device_ms_per_step_all_streams": round(total_dev, 1),
+        "kernel_top_isolated": iso,
     }
     if args.cpu_sample > 0:
         out["cpu_baseline"] = cpu_baseline(c, w, seq, args.cpu_sample)
