@@ -362,18 +362,45 @@ __global__ __launch_bounds__(256) void k_swa_combine(AttnArgs a, int S) {
   const float* pl = pm + (int64_t)S * plane;
   const float sl2 = 1.4426950408889634f / sqrtf((float)hd);
   float M = -INFINITY;
-  for (int sidx = 0; sidx < S; ++sidx) M = fmaxf(M, pm[sidx * plane + qh]);
   float L = 0.f;
   float2 acc = make_float2(0.f, 0.f);
   const bool act = 2 * lane < hd;
-  for (int sidx = 0; sidx < S; ++sidx) {
-    const int64_t row = sidx * plane + qh;
-    const float w = pm[row] == -INFINITY ? 0.f : exp2f((pm[row] - M) * sl2);
-    L += w * pl[row];
-    if (act) {
-      const float2 v = *(const float2*)(a.ws + row * hd + 2 * lane);
-      acc.x += w * v.x;
-      acc.y += w * v.y;
+  constexpr int SMAX = 8;  // (the split takes at most 8 parts): every load of the row in one round
+  if (S <= SMAX) {
+    float pmv[SMAX], plv[SMAX];
+    float2 vv[SMAX];
+#pragma unroll
+    for (int sidx = 0; sidx < SMAX; ++sidx) {
+      pmv[sidx] = -INFINITY;
+      plv[sidx] = 0.f;
+      vv[sidx] = make_float2(0.f, 0.f);
+      if (sidx < S) {
+        const int64_t row = sidx * plane + qh;
+        pmv[sidx] = pm[row];
+        plv[sidx] = pl[row];
+        if (act) vv[sidx] = *(const float2*)(a.ws + row * hd + 2 * lane);
+      }
+    }
+#pragma unroll
+    for (int sidx = 0; sidx < SMAX; ++sidx) M = fmaxf(M, pmv[sidx]);
+#pragma unroll
+    for (int sidx = 0; sidx < SMAX; ++sidx) {
+      const float w = pmv[sidx] == -INFINITY ? 0.f : exp2f((pmv[sidx] - M) * sl2);
+      L += w * plv[sidx];
+      acc.x += w * vv[sidx].x;
+      acc.y += w * vv[sidx].y;
+    }
+  } else {
+    for (int sidx = 0; sidx < S; ++sidx) M = fmaxf(M, pm[sidx * plane + qh]);
+    for (int sidx = 0; sidx < S; ++sidx) {
+      const int64_t row = sidx * plane + qh;
+      const float w = pm[row] == -INFINITY ? 0.f : exp2f((pm[row] - M) * sl2);
+      L += w * pl[row];
+      if (act) {
+        const float2 v = *(const float2*)(a.ws + row * hd + 2 * lane);
+        acc.x += w * v.x;
+        acc.y += w * v.y;
+      }
     }
   }
   if (act) {
