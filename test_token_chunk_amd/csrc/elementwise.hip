@@ -832,6 +832,13 @@ hipError_t transpose_rows(const T* y, T* yT, int64_t M, int d, int rpb, int64_t 
 }  // namespace
 
 template <typename T>
+hipError_t transpose_rows_checked(const T* y, T* yT, int64_t M, int d, int rpb, int64_t ldT, hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  if (!transpose_ok(y, yT, M, d, rpb, ldT)) return hipErrorNotSupported;
+  return transpose_rows(y, yT, M, d, rpb, ldT, s);
+}
+
+template <typename T>
 hipError_t rmsnorm_fwd(const float* x, int64_t M, int d, const float* g, float eps, T* y, float* rstd, T* yT, int rpb,
                        int64_t ldT, float* xcopy, hipStream_t s) {
   if (M == 0) return hipSuccess;
@@ -1022,6 +1029,7 @@ hipError_t parts_rows_t(const float* parts, int S, int64_t plane, int64_t M, int
   template hipError_t rmsnorm_bwd<T>(const float*, const float*, int64_t, int, const float*, const float*,          \
                                      const float*, float*, T*, hipStream_t);                                        \
   template hipError_t convert_rows<T>(const float*, int64_t, int, T*, T*, int, int64_t, hipStream_t);               \
+  template hipError_t transpose_rows_checked<T>(const T*, T*, int64_t, int, int, int64_t, hipStream_t);             \
   template hipError_t parts_rows_t<T>(const float*, int, int64_t, int64_t, int, int, T*, T*, hipStream_t);          \
   template hipError_t ce_rows_ld<T>(const float*, int64_t, int, const int32_t*, int64_t, const int*, int, float*,   \
                                     T*, int*, hipStream_t);                                                         \

@@ -649,7 +649,8 @@ int top_chunk(ttt_ctx* c, const int32_t* tgt, int64_t ld, const float* hsrc, int
   gx.e.ldc = d;
   int Sx = 1;
   CK(Ops<T>::gemm_parts(c, gx, n, Sx));
-  CK(norm_bwd<T>(c, Sx, c->htop, c->rstdf, M, c->final_norm, c->tmpf, nullptr, c->dh, (T*)nullptr));
+  // (dh and its T copy dy for the first block's products)
+  CK(norm_bwd<T>(c, Sx, c->htop, c->rstdf, M, c->final_norm, c->tmpf, nullptr, c->dh, tp<T>(c->dyN)));
   const float lr = c->cfg.lr;
   const int64_t fsz = 3LL * f * d;
   for (int j = c->Lq - 1; j >= 0; --j) {
@@ -658,7 +659,12 @@ int top_chunk(ttt_ctx* c, const int32_t* tgt, int64_t ld, const float* hsrc, int
     FastW& w = c->fw[j];
     void* dyT = c->dyT[j];
     void* dzT = c->dzT[j];
-    CK(convert_rows<T>(c->dh, M, d, tp<T>(c->dyN), tp<T>(dyT), n, b, c->stream));
+    // dy in T (written by the norm backward that produced dh) and transposed for the weight gradients
+    const hipError_t te = transpose_rows_checked<T>(tp<T>(c->dyN), tp<T>(dyT), M, d, n, b, c->stream);
+    if (te == hipErrorNotSupported)
+      CK(convert_rows<T>(c->dh, M, d, tp<T>(c->dyN), tp<T>(dyT), n, b, c->stream));
+    else
+      CK(te);
     // d act = dy W_down  ->  dz_g, dz_u
     GemmArgs g1 = mk(c->dyN, d, w.wdT, d, n, f, d);
     g1.batch = B;
@@ -810,7 +816,7 @@ int top_chunk(ttt_ctx* c, const int32_t* tgt, int64_t ld, const float* hsrc, int
     g6.e.ldc = d;
     int S6 = 1;
     CK(Ops<T>::gemm_parts(c, g6, n, S6));
-    CK(norm_bwd<T>(c, S6, a.h_in, a.rstd1, M, lw.attn_norm, c->tmpf, c->dh, c->dh, (T*)nullptr));
+    CK(norm_bwd<T>(c, S6, a.h_in, a.rstd1, M, lw.attn_norm, c->tmpf, c->dh, c->dh, tp<T>(c->dyN)));
   }
   // the next chunk reads the updated fast weights and rewrites the saved activations
   if (c->overlap) {

@@ -162,6 +162,10 @@ hipError_t parts_rows_t(const float* parts, int S, int64_t plane, int64_t M, int
 template <typename T>
 hipError_t convert_rows(const float* x, int64_t M, int d, T* y, T* yT, int rows_per_batch, int64_t ldT,
                         hipStream_t s);
+// yT = y (T [M][d] in batches of rpb rows) transposed per batch into [d][ldT]; hipErrorNotSupported
+// (nothing launched) for shapes the 16-byte transposing kernel does not take (fp32, rpb % 8 ...)
+template <typename T>
+hipError_t transpose_rows_checked(const T* y, T* yT, int64_t M, int d, int rpb, int64_t ldT, hipStream_t s);
 hipError_t count_valid_ld(const int32_t* tgt, int64_t ld, int B, int n, int* nvalid, hipStream_t s);
 // whether gemm_mfma_bf16 runs this lm_head product with the EPI_LM_CE epilogue
 bool gemm_mfma_fuses_lm_ce(const GemmArgs& g);
