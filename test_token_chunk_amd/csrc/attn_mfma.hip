@@ -38,12 +38,8 @@ struct FwdSmem {
   bf16 vt[3][HD][KT + 4];
 };
 
-// two floats -> packed bf16 pair, round to nearest even (one v_cvt_pk_bf16_f32 on gfx950)
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ uint32_t pk2(float a, float b) {
-  bf16x2 v = {(__bf16)a, (__bf16)b};
-  return __builtin_bit_cast(uint32_t, v);
-}
+__device__ __forceinline__ uint32_t pk2(float a, float b) { return bf16pair(a, b); }
 
 // 2^x with one v_exp_f32 (results below 2^-126 flush to zero, which no probability here
 // resolves anyway); exp2f adds a denormal-range fix-up of five more instructions

@@ -18,11 +18,24 @@ __host__ __device__ __forceinline__ float bf2f(bf16 v) {
 }
 
 __host__ __device__ __forceinline__ bf16 f2bf(float f) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  // gfx950 converts in hardware (v_cvt_pk_bf16_f32, round to nearest even, NaN stays NaN)
+  return bf16{__builtin_bit_cast(uint16_t, (__bf16)f)};
+#else
   uint32_t u;
   __builtin_memcpy(&u, &f, 4);
   if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return bf16{(uint16_t)((u >> 16) | 0x40)};  // NaN
   u += 0x7FFFu + ((u >> 16) & 1u);
   return bf16{(uint16_t)(u >> 16)};
+#endif
+}
+
+// two floats -> packed bf16 pair (a in the low half), round to nearest even: one
+// v_cvt_pk_bf16_f32 on gfx950
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16pair(float a, float b) {
+  bf16x2_t v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 template <typename T>

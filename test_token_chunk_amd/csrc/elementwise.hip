@@ -78,8 +78,7 @@ __device__ __forceinline__ void store4<float>(float* p, float a, float b, float 
 }
 template <>
 __device__ __forceinline__ void store4<bf16>(bf16* p, float a, float b, float c, float d) {
-  *(uint2*)p = make_uint2((uint32_t)f2bf(a).x | ((uint32_t)f2bf(b).x << 16),
-                          (uint32_t)f2bf(c).x | ((uint32_t)f2bf(d).x << 16));
+  *(uint2*)p = make_uint2(bf16pair(a, b), bf16pair(c, d));
 }
 
 // Vector forms of the row kernels above: one 256-thread block per row, 16-byte access
@@ -293,8 +292,7 @@ __global__ __launch_bounds__(256) void k_parts_rows_t(const float* __restrict__ 
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int r = r0 + 16 * k, t = t0 + r;
-    const uint2 w = make_uint2((uint32_t)f2bf(acc[k].x).x | ((uint32_t)f2bf(acc[k].y).x << 16),
-                               (uint32_t)f2bf(acc[k].z).x | ((uint32_t)f2bf(acc[k].w).x << 16));
+    const uint2 w = make_uint2(bf16pair(acc[k].x, acc[k].y), bf16pair(acc[k].z, acc[k].w));
     if (t < n && c < d) *(uint2*)(y + ((int64_t)b * n + t) * d + c) = w;
     *(uint2*)&tile[r][4 * c4] = w;
   }
@@ -391,8 +389,7 @@ __global__ __launch_bounds__(512) void k_ce_rows4(const float* logits, int V, co
       p[k] = (y >= 0) ? p[k] * inv : 0.f;
     }
     if constexpr (sizeof(T) == 2) {
-      *(uint2*)(dz + 4 * v) = make_uint2((uint32_t)f2bf(p[0]).x | ((uint32_t)f2bf(p[1]).x << 16),
-                                         (uint32_t)f2bf(p[2]).x | ((uint32_t)f2bf(p[3]).x << 16));
+      *(uint2*)(dz + 4 * v) = make_uint2(bf16pair(p[0], p[1]), bf16pair(p[2], p[3]));
     } else {
       *(float4*)(dz + 4 * v) = make_float4(p[0], p[1], p[2], p[3]);
     }
@@ -442,7 +439,7 @@ __global__ __launch_bounds__(256) void k_ce_finalize(const float* part, const fl
       float x0 = bf2f(bf16{(uint16_t)(w[k] & 0xffff)}) * sc, x1 = bf2f(bf16{(uint16_t)(w[k] >> 16)}) * sc;
       if (v + 2 * k == y) x0 -= inv;
       if (v + 2 * k + 1 == y) x1 -= inv;
-      o[k] = (uint32_t)f2bf(x0).x | ((uint32_t)f2bf(x1).x << 16);
+      o[k] = bf16pair(x0, x1);
     }
     *(uint4*)(row + v) = make_uint4(o[0], o[1], o[2], o[3]);
   }

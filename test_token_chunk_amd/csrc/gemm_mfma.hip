@@ -400,13 +400,12 @@ __device__ __forceinline__ void dl_sgd_epilogue(const GemmArgs& g, f32x16 (&acc)
                                      pre[i][j][q].z - e.lr * acc[i][j][4 * q + 2],
                                      pre[i][j][q].w - e.lr * acc[i][j][4 * q + 3]);
         *(float4*)(e.master + bz * e.sm + (int64_t)m * e.ldm + n) = w;
-        const bf16 b0 = f2bf(w.x), b1 = f2bf(w.y), b2 = f2bf(w.z), b3 = f2bf(w.w);
-        *(uint2*)((bf16*)e.sh + bz * e.ssh + shrow * e.ldsh + n) =
-            make_uint2((uint32_t)b0.x | ((uint32_t)b1.x << 16), (uint32_t)b2.x | ((uint32_t)b3.x << 16));
-        tr[(nl + 0) * TLD + ml] = b0;
-        tr[(nl + 1) * TLD + ml] = b1;
-        tr[(nl + 2) * TLD + ml] = b2;
-        tr[(nl + 3) * TLD + ml] = b3;
+        const uint32_t p01 = bf16pair(w.x, w.y), p23 = bf16pair(w.z, w.w);
+        *(uint2*)((bf16*)e.sh + bz * e.ssh + shrow * e.ldsh + n) = make_uint2(p01, p23);
+        tr[(nl + 0) * TLD + ml] = bf16{(uint16_t)p01};
+        tr[(nl + 1) * TLD + ml] = bf16{(uint16_t)(p01 >> 16)};
+        tr[(nl + 2) * TLD + ml] = bf16{(uint16_t)p23};
+        tr[(nl + 3) * TLD + ml] = bf16{(uint16_t)(p23 >> 16)};
       }
   }
   __syncthreads();
@@ -588,8 +587,7 @@ __device__ __forceinline__ void wide_epilogue(const GemmArgs& g, f32x16 (&acc)[T
   bf16* tr0 = reinterpret_cast<bf16*>(smem_raw);  // [BN][TLD] (IL: [BN/2][TLD])
   bf16* tr1 = tr0 + BN * TLD;                     // SwiGLU backward: dz_u^T
   auto pk4 = [](float a, float b, float c, float d) {
-    return make_uint2((uint32_t)f2bf(a).x | ((uint32_t)f2bf(b).x << 16),
-                      (uint32_t)f2bf(c).x | ((uint32_t)f2bf(d).x << 16));
+    return make_uint2(bf16pair(a, b), bf16pair(c, d));
   };
   if constexpr (EK == EPI_LM_CE) {
     // Vocabulary tile n0 / 256 of the lm_head logits: for each row the maximum m_t of its 256
@@ -694,8 +692,8 @@ __device__ __forceinline__ void wide_epilogue(const GemmArgs& g, f32x16 (&acc)[T
             acc[i][j][4 * q + 2] = lo1;
             acc[i][j][4 * q + 3] = hi1;
           }
-          const uint32_t plo = (uint32_t)f2bf(v[0]).x | ((uint32_t)f2bf(v[2]).x << 16);
-          const uint32_t phi = (uint32_t)f2bf(v[1]).x | ((uint32_t)f2bf(v[3]).x << 16);
+          const uint32_t plo = bf16pair(v[0], v[2]);
+          const uint32_t phi = bf16pair(v[1], v[3]);
           if (staged) {
             bf16* srow = st + ml * SLD + (nl - jj);
             if (part < 2) {
@@ -848,11 +846,12 @@ __device__ __forceinline__ void wide_epilogue(const GemmArgs& g, f32x16 (&acc)[T
             const float4 p = pre[j * 4 + q];
             const float w0 = p.x - e.lr * v0, w1 = p.y - e.lr * v1, w2 = p.z - e.lr * v2, w3 = p.w - e.lr * v3;
             *(float4*)(e.master + bz * e.sm + (int64_t)m * e.ldm + n) = make_float4(w0, w1, w2, w3);
-            *(uint2*)((bf16*)e.sh + bz * e.ssh + shrow * e.ldsh + n) = pk4(w0, w1, w2, w3);
-            tr0[(nl + 0) * TLD + ml] = f2bf(w0);
-            tr0[(nl + 1) * TLD + ml] = f2bf(w1);
-            tr0[(nl + 2) * TLD + ml] = f2bf(w2);
-            tr0[(nl + 3) * TLD + ml] = f2bf(w3);
+            const uint2 wb = pk4(w0, w1, w2, w3);
+            *(uint2*)((bf16*)e.sh + bz * e.ssh + shrow * e.ldsh + n) = wb;
+            tr0[(nl + 0) * TLD + ml] = bf16{(uint16_t)wb.x};
+            tr0[(nl + 1) * TLD + ml] = bf16{(uint16_t)(wb.x >> 16)};
+            tr0[(nl + 2) * TLD + ml] = bf16{(uint16_t)wb.y};
+            tr0[(nl + 3) * TLD + ml] = bf16{(uint16_t)(wb.y >> 16)};
           }
         }
     }
@@ -1146,8 +1145,7 @@ __global__ __launch_bounds__(256) void k_splitk_reduce4(GemmArgs g, int S) {
     if constexpr (EK == EPI_F32) {
       *(float4*)((float*)e.c + bz * e.sc + m * e.ldc + n) = acc;
     } else if constexpr (EK == EPI_T) {
-      const uint2 w = make_uint2((uint32_t)f2bf(acc.x).x | ((uint32_t)f2bf(acc.y).x << 16),
-                                 (uint32_t)f2bf(acc.z).x | ((uint32_t)f2bf(acc.w).x << 16));
+      const uint2 w = make_uint2(bf16pair(acc.x, acc.y), bf16pair(acc.z, acc.w));
       *(uint2*)((bf16*)e.c + bz * e.sc + m * e.ldc + n) = w;
     } else {
       float* c = (float*)e.c + bz * e.sc + m * e.ldc + n;

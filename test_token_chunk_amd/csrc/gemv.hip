@@ -71,10 +71,6 @@ __device__ __forceinline__ void qkv_rope_store(const RopeRing& rr, int part, int
   }
 }
 
-__device__ __forceinline__ uint32_t pkbf(float a, float b) {
-  return (uint32_t)f2bf(a).x | ((uint32_t)f2bf(b).x << 16);
-}
-
 template <int MR, int NR, int KIND, bool NRM>
 __global__ __launch_bounds__(256) void k_gemv(GemmArgs g, int ncols, int f) {
   constexpr bool SW = KIND == EPI_SWIGLU || KIND == EPI_SWIGLU_IL;
@@ -148,8 +144,8 @@ __global__ __launch_bounds__(256) void k_gemv(GemmArgs g, int ncols, int f) {
         const float4 x0 = *(const float4*)xr, x1 = *(const float4*)(xr + 4);
         ssl[m] += (x0.x * x0.x + x0.y * x0.y) + (x0.z * x0.z + x0.w * x0.w) + (x1.x * x1.x + x1.y * x1.y) +
                   (x1.z * x1.z + x1.w * x1.w);
-        xs[m * (K / 8) + k / 8] = make_uint4(pkbf(x0.x * g0.x, x0.y * g0.y), pkbf(x0.z * g0.z, x0.w * g0.w),
-                                             pkbf(x1.x * g1.x, x1.y * g1.y), pkbf(x1.z * g1.z, x1.w * g1.w));
+        xs[m * (K / 8) + k / 8] = make_uint4(bf16pair(x0.x * g0.x, x0.y * g0.y), bf16pair(x0.z * g0.z, x0.w * g0.w),
+                                             bf16pair(x1.x * g1.x, x1.y * g1.y), bf16pair(x1.z * g1.z, x1.w * g1.w));
       }
     }
 #pragma unroll
