@@ -100,6 +100,17 @@ static inline unsigned cdiv(int64_t a, int64_t b) { return (unsigned)((a + b - 1
 // LDS pointer for global_load_lds (lane L of a wave writes 16 bytes at the wave's LDS
 // address + 16 L)
 #define LDSP(p) ((void __attribute__((address_space(3)))*)(p))
+// raw buffer resource over `bytes` bytes from p (gfx9 data-format word): a buffer load takes
+// a per-lane byte offset and a wave-uniform one, so a loop that advances along K moves only
+// the scalar offset; loads past `bytes` return zero instead of touching memory
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+// 16 bytes per lane from byte offset voff + soff of the buffer into LDS at the wave's
+// address lds + 16 * lane (like global_load_lds)
+__device__ __forceinline__ void buf_lds16(__amdgpu_buffer_rsrc_t r, void* lds, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, LDSP(lds), 16, voff, soff, 0, 0);
+}
 // wait until at most n vector-memory operations are outstanding and all LDS operations are
 // done (gfx9 s_waitcnt: vmcnt in bits 15:14 and 3:0, expcnt 6:4, lgkmcnt 11:8)
 #define WAIT_VM_LDS(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4))

@@ -430,22 +430,30 @@ __global__ __launch_bounds__(256) void k_gemm_dl(GemmArgs g) {
   const int kend = SPLIT ? min(g.K, kbeg + (int)g.e.st) : g.K;
   int m0, n0;
   dl_tile(m0, n0);
-  const bf16* A = (const bf16*)g.A + bz * g.sA;
-  const bf16* B = (const bf16*)g.B + bz * g.sB;
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: LDS addresses stay scalar
   const int wm0 = (wid >> 1) * WM, wn0 = (wid & 1) * WN;
   const int nk = (kend - kbeg) / BK;
 
-  // 1 KB blocks i = 0..3 of the A and B tiles of step kt (8 rows each)
+  // 1 KB blocks i = 0..3 of the A and B tiles of step kt (8 rows each).  The 128-row operand
+  // panels are buffers: each lane keeps the byte offsets of its rows and chunks, a K step
+  // moves only the scalar offset.
+  const __amdgpu_buffer_rsrc_t ra = buf_rsrc((const bf16*)g.A + bz * g.sA + (int64_t)m0 * g.lda, (uint32_t)(BM * g.lda * 2));
+  const __amdgpu_buffer_rsrc_t rb = buf_rsrc((const bf16*)g.B + bz * g.sB + (int64_t)n0 * g.ldb, (uint32_t)(BN * g.ldb * 2));
+  int va[4], vb[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = (wid * 4 + i) * 8 + (lane >> 3);  // tile row of this lane
+    const int c = (lane & 7) ^ ((r >> 1) & 7);      // logical chunk that lands at physical chunk lane & 7
+    va[i] = (r * g.lda + c * 8) * 2;
+    vb[i] = (r * g.ldb + c * 8) * 2;
+  }
   auto issue_one = [&](int kt, int i) {
     unsigned char* base = smem_raw + (kt % STAGES) * DL_TILE_BYTES;
-    const int k0 = kbeg + kt * BK;
-    const int blk = wid * 4 + i;          // 8-row block of the tile (1 KB)
-    const int r = blk * 8 + (lane >> 3);     // tile row of this lane
-    const int c = (lane & 7) ^ ((r >> 1) & 7);  // logical chunk that lands at physical chunk lane & 7
-    __builtin_amdgcn_global_load_lds(A + (int64_t)(m0 + r) * g.lda + k0 + c * 8, LDSP(base + blk * 1024), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(B + (int64_t)(n0 + r) * g.ldb + k0 + c * 8,
-                                     LDSP(base + BM * BK * 2 + blk * 1024), 16, 0, 0);
+    const int k0b = (kbeg + kt * BK) * 2;
+    const int blk = wid * 4 + i;  // 8-row block of the tile (1 KB)
+    buf_lds16(ra, base + blk * 1024, va[i], k0b);
+    buf_lds16(rb, base + BM * BK * 2 + blk * 1024, vb[i], k0b);
   };
   auto issue = [&](int kt) {
 #pragma unroll
@@ -899,33 +907,37 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
   const int split = SPLIT ? zz % S : 0;
   const int kbeg = SPLIT ? split * (int)g.e.st : 0;
   const int kend = SPLIT ? min(g.K, kbeg + (int)g.e.st) : g.K;
-  const bf16* A = (const bf16*)g.A + bz * g.sA;
-  const bf16* B = (const bf16*)g.B + bz * g.sB;
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: LDS addresses stay scalar
   const int wm0 = (wid / (NW / 2)) * WM, wn0 = (wid % (NW / 2)) * WN;
   const int nk = (kend - kbeg) / BK;
   // 1 KB DMA block = RPB rows; lane L lands at row L / CPR, physical chunk L % CPR and
   // fetches the logical chunk the swizzle puts there.  Wave w copies A blocks
-  // [w ABLK, (w+1) ABLK) and B blocks [w BBLK, (w+1) BBLK).
+  // [w ABLK, (w+1) ABLK) and B blocks [w BBLK, (w+1) BBLK).  The operand panels (BM rows of A
+  // from m0, 256 rows of B from n0) are buffers: each lane keeps the byte offsets of its rows and
+  // chunks, and a K step only moves the scalar offset.
   const int lrow = lane / CPR, lpc = lane % CPR;
   const int arow = wid * ABLK * RPB + lrow, brow = wid * BBLK * RPB + lrow;
-  const bf16* Ag = A + (int64_t)(m0 + arow) * g.lda;
-  const bf16* Bg = B + (int64_t)(n0 + brow) * g.ldb;
+  const __amdgpu_buffer_rsrc_t ra = buf_rsrc((const bf16*)g.A + bz * g.sA + (int64_t)m0 * g.lda, (uint32_t)(BM * g.lda * 2));
+  const __amdgpu_buffer_rsrc_t rb = buf_rsrc((const bf16*)g.B + bz * g.sB + (int64_t)n0 * g.ldb, (uint32_t)(BN * g.ldb * 2));
+  int voff[LPT];
+#pragma unroll
+  for (int i = 0; i < LPT; ++i) {
+    if (i < ABLK) {
+      const int r = arow + i * RPB;
+      voff[i] = (r * g.lda + (lpc ^ wide_swz<BK>(r)) * 8) * 2;
+    } else {
+      const int r = brow + (i - ABLK) * RPB;
+      voff[i] = (r * g.ldb + (lpc ^ wide_swz<BK>(r)) * 8) * 2;
+    }
+  }
 
   // DMA block i (0 .. LPT-1: A blocks, then B blocks) of step kt
   auto issue_one = [&](int kt, int i) {
     unsigned char* base = smem_raw + (kt % WST) * SBYTES;
-    const int k0 = kbeg + kt * BK;
-    if (i < ABLK) {
-      const int lc = lpc ^ wide_swz<BK>(arow + i * RPB);
-      __builtin_amdgcn_global_load_lds(Ag + (int64_t)(i * RPB) * g.lda + k0 + lc * 8,
-                                       LDSP(base + (wid * ABLK + i) * 1024), 16, 0, 0);
-    } else {
-      const int ib = i - ABLK;
-      const int lc = lpc ^ wide_swz<BK>(brow + ib * RPB);
-      __builtin_amdgcn_global_load_lds(Bg + (int64_t)(ib * RPB) * g.ldb + k0 + lc * 8,
-                                       LDSP(base + ABYTES + (wid * BBLK + ib) * 1024), 16, 0, 0);
-    }
+    const int k0b = (kbeg + kt * BK) * 2;
+    if (i < ABLK) buf_lds16(ra, base + (wid * ABLK + i) * 1024, voff[i], k0b);
+    else buf_lds16(rb, base + ABYTES + (wid * BBLK + (i - ABLK)) * 1024, voff[i], k0b);
   };
   auto issue = [&](int kt) {
 #pragma unroll
@@ -1092,7 +1104,9 @@ bool dl_ok(const GemmArgs& g, int Ks) {
   const char* off = getenv("TTT_GEMM_NO_DL");
   if (off && off[0] == '1') return false;
   return g.M % 128 == 0 && g.N % 128 == 0 && g.K % BK == 0 && Ks % BK == 0 && g.lda % 8 == 0 && g.ldb % 8 == 0 &&
-         g.e.kind != EPI_SWIGLU;
+         g.e.kind != EPI_SWIGLU &&
+         // 128-row operand panels are buffers with 32-bit byte offsets
+         (int64_t)128 * g.lda * 2 < (1LL << 31) && (int64_t)128 * g.ldb * 2 < (1LL << 31);
 }
 
 template <int BM, int BN, int WM, int WN, bool DUAL, int EK>
@@ -1227,6 +1241,8 @@ bool wide_ok(const GemmArgs& g) {
   }
   if (off) return false;
   if (!(g.M % 128 == 0 && g.N % 256 == 0 && g.K % 64 == 0 && g.lda % 8 == 0 && g.ldb % 8 == 0)) return false;
+  // operand panels of 256 rows are addressed as buffers with 32-bit byte offsets
+  if ((int64_t)256 * g.lda * 2 >= (1LL << 31) || (int64_t)256 * g.ldb * 2 >= (1LL << 31)) return false;
   // the epilogues store 4-element row segments (and 8-element transposed segments)
   const Epi& e = g.e;
   switch (e.kind) {
