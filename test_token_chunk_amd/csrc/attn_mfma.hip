@@ -927,7 +927,8 @@ __global__ __launch_bounds__(512) void k_swa_dq2(AttnBwdArgs a, int S) {
   constexpr int VOFF = KT * HD * 2, TOFF = 2 * KT * HD * 2;
   static_assert(TB % NW == 0 && CPR * 16 == HD * 2 && 32 % CPR == 0, "tile copy layout");
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, g = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: LDS addresses stay scalar
   const int b = SPLIT ? blockIdx.z / S : blockIdx.z, h = blockIdx.y;
   const int sp = SPLIT ? blockIdx.z % S : 0;
   const int64_t bh = (int64_t)b * a.H + h;
@@ -992,6 +993,9 @@ __global__ __launch_bounds__(512) void k_swa_dq2(AttnBwdArgs a, int S) {
   // copies of tile it_ into stage st: K and V rows by ring slot, K^T rows (head dims) of
   // 64 consecutive slots (tiles start at multiples of 64 positions and R % 8 == 0, so an
   // 8-key chunk never wraps)
+  // the head's K, V and K^T rings are buffers (32-bit byte offsets, checked at launch)
+  const __amdgpu_buffer_rsrc_t rk = buf_rsrc(Kr, (uint32_t)(R * HD * 2)), rv = buf_rsrc(Vr, (uint32_t)(R * HD * 2)),
+                               rt = buf_rsrc(Kt, (uint32_t)(R * HD * 2));
   auto issue = [&](int it_, int st) {
     const int slot0 = (sbase + it_ * KT) % R;
     unsigned char* base = smem_raw + st * SB;
@@ -999,12 +1003,11 @@ __global__ __launch_bounds__(512) void k_swa_dq2(AttnBwdArgs a, int S) {
     for (int u = 0; u < TBW; ++u) {
       const int j = wid * TBW + u;
       const int row = j * RPK + lane / CPR, c = (lane % CPR) ^ (row % CPR);
-      const int64_t off = (int64_t)ring_add(slot0, row, R) * HD + c * 8;
-      __builtin_amdgcn_global_load_lds(Kr + off, LDSP(base + j * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(Vr + off, LDSP(base + VOFF + j * 1024), 16, 0, 0);
+      const int off = (ring_add(slot0, row, R) * HD + c * 8) * 2;
+      buf_lds16(rk, base + j * 1024, off, 0);
+      buf_lds16(rv, base + VOFF + j * 1024, off, 0);
       const int trow = j * 8 + (lane >> 3), tc = (lane & 7) ^ ((trow >> 1) & 7);
-      __builtin_amdgcn_global_load_lds(Kt + (int64_t)trow * R + ring_add(slot0, tc * 8, R),
-                                       LDSP(base + TOFF + j * 1024), 16, 0, 0);
+      buf_lds16(rt, base + TOFF + j * 1024, (trow * R + ring_add(slot0, tc * 8, R)) * 2, 0);
     }
   };
 
@@ -1126,7 +1129,9 @@ template <int HD>
 hipError_t launch_bwd(const AttnBwdArgs& a, hipStream_t s, AttnBwdParts* parts) {
   // the direct-to-LDS dQ form (head dim 128, transposed key ring) computes D = rowsum(dO * O)
   // itself and stores it for dK/dV; otherwise a separate pass does
-  const bool tr = a.ktr && a.dot && a.R % 8 == 0 && a.n % 8 == 0 && (a.H * HD) % 8 == 0;
+  // (the direct-to-LDS dQ form addresses a head's ring with 32-bit byte offsets)
+  const bool tr = a.ktr && a.dot && a.R % 8 == 0 && a.n % 8 == 0 && (a.H * HD) % 8 == 0 &&
+                  (int64_t)a.R * HD * 2 < (1LL << 31);
   constexpr bool DQ2 = HD == 128;
   hipError_t e = hipSuccess;
   if (!(DQ2 && tr)) {

@@ -1000,10 +1000,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
     const bool pend = kt + WST - 1 < nk;
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
+      // the fragments of the next slice are read before this slice's MFMAs, so all TM rows of
+      // MFMAs cover the LDS latency
       if ((h & 1) == 0) {
-        MFMA_ROWS(f0a, f0b, 0, 1)
-        SB();
         if (h + 1 < NH) FRAGS(f1a, f1b, kt, h + 1)
+        SB();
+        MFMA_ROWS(f0a, f0b, 0, 1)
         SB();
         if (h == NH - 2 && more) {
           // publish step kt + 1 (issued WST - 2 steps ago) for every wave; the barrier also
@@ -1019,15 +1021,15 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
           SB();
         }
       } else {
-        MFMA_ROWS(f1a, f1b, 0, 1)
-        SB();
-        if (h == NH - 1) DMA_SLOT(TM - 1)
-        SB();
         if (h + 1 < NH) {
           FRAGS(f0a, f0b, kt, h + 1)
         } else if (more) {
           FRAGS(f0a, f0b, kt + 1, 0)
         }
+        SB();
+        MFMA_ROWS(f1a, f1b, 0, 1)
+        SB();
+        if (h == NH - 1) DMA_SLOT(TM - 1)
         SB();
         _Pragma("unroll") for (int r = 1; r < TM; ++r) {
           MFMA_ROWS(f1a, f1b, r, r + 1)
