@@ -657,8 +657,8 @@ struct DkvSmem {
   float dd[KT];
 };
 
-// P > 1: blockIdx.z = b * P + part; the block covers part `part` of its key block's query
-// tiles and writes partial dK / dV to ws[part] / ws[P + part] (each [B*n][H*hd]).
+// P > 1: the block covers part `part` of its key block's query tiles and writes partial
+// dK / dV to ws[part] / ws[P + part] (each [B*n][H*hd]).
 template <int HD, bool TR>
 __global__ __launch_bounds__(256) void k_swa_dkv(AttnBwdArgs a, int P) {
   constexpr int KS = HD / 16, HM = HD / 32;
@@ -667,10 +667,12 @@ __global__ __launch_bounds__(256) void k_swa_dkv(AttnBwdArgs a, int P) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   DkvSmem<HD>& sm = *reinterpret_cast<DkvSmem<HD>*>(smem_raw);
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, g = lane >> 5;
-  const int b = blockIdx.z / P, h = blockIdx.y, part = blockIdx.z % P;
+  // blockIdx.y = key block * P + part: blocks are dispatched head-fastest in that order, so the
+  // early key blocks (the longest query ranges) start first and the short ones fill in behind
+  const int b = blockIdx.z, h = blockIdx.x, part = blockIdx.y % P;
   const int64_t bh = (int64_t)b * a.H + h;
   const int R = a.R, d = a.H * HD;
-  const int s0blk = blockIdx.x * BQ;
+  const int s0blk = (blockIdx.y / P) * BQ;
   const int sk = s0blk + wid * QW + (lane & 31);  // this lane's key (chunk-local)
   const bool kok = sk < a.n;
   const int wsk_hi = s0blk + wid * QW + QW - 1;    // last key of this wave
@@ -1120,7 +1122,8 @@ hipError_t launch_dkv(const AttnBwdArgs& a, int P, hipStream_t s) {
     if (e != hipSuccess) return e;
     attr = true;
   }
-  hipLaunchKernelGGL((k_swa_dkv<HD, TR>), dim3(cdiv(a.n, BQ), a.H, a.B * P), dim3(256), sizeof(DkvSmem<HD>), s, a,
+  if ((int64_t)cdiv(a.n, BQ) * P > 65535) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((k_swa_dkv<HD, TR>), dim3(a.H, cdiv(a.n, BQ) * P, a.B), dim3(256), sizeof(DkvSmem<HD>), s, a,
                      P);
   return hipGetLastError();
 }
