@@ -597,6 +597,28 @@ __device__ __forceinline__ void wide_epilogue(const GemmArgs& g, f32x16 (&acc)[T
   auto pk4 = [](float a, float b, float c, float d) {
     return make_uint2(bf16pair(a, b), bf16pair(c, d));
   };
+  if constexpr (SPLIT) {
+    // fp32 part of a K split: the tile goes through LDS (rows of BN + 4 floats) so that each
+    // wave stores whole 1 KB rows instead of 32-byte pieces of 32 rows
+    static_assert(BM * (BN + 4) * 4 <= wide_lds_bytes<BM, EK>(), "staged part fits the operand ring");
+    constexpr int SLD = BN + 4;
+    float* st = reinterpret_cast<float*>(smem_raw);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          *(float4*)(st + (wm0 + i * 32 + lr) * SLD + wn0 + j * 32 + 8 * q + 4 * hi) =
+              make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+    __syncthreads();
+    float* part = g.ws + (((int64_t)split * g.batch + bz) * g.M + m0) * g.N + n0;
+    for (int c = tid; c < BM * (BN / 4); c += NT) {
+      const int r = c / (BN / 4), c4 = (c % (BN / 4)) * 4;
+      *(float4*)(part + (int64_t)r * g.N + c4) = *(const float4*)(st + r * SLD + c4);
+    }
+    return;
+  }
   if constexpr (EK == EPI_LM_CE) {
     // Vocabulary tile n0 / 256 of the lm_head logits: for each row the maximum m_t of its 256
     // columns and the sum of exp(z - m_t) (fp32, reduced over the lane pair and the 4 column
@@ -820,9 +842,7 @@ __device__ __forceinline__ void wide_epilogue(const GemmArgs& g, f32x16 (&acc)[T
           const int nl = wn0 + j * 32 + 8 * q + 4 * hi, n = n0 + nl;
           const float v0 = acc[i][j][4 * q], v1 = acc[i][j][4 * q + 1], v2 = acc[i][j][4 * q + 2],
                       v3 = acc[i][j][4 * q + 3];
-          if constexpr (SPLIT) {
-            *(float4*)(g.ws + (((int64_t)split * g.batch + bz) * g.M + m) * g.N + n) = make_float4(v0, v1, v2, v3);
-          } else if constexpr (EK == EPI_F32) {
+          if constexpr (EK == EPI_F32) {
             *(float4*)((float*)e.c + bz * e.sc + (int64_t)m * e.ldc + n) = make_float4(v0, v1, v2, v3);
           } else if constexpr (EK == EPI_T) {
             *(uint2*)((bf16*)e.c + bz * e.sc + (int64_t)m * e.ldc + n) = pk4(v0, v1, v2, v3);
