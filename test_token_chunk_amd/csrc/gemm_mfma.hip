@@ -571,9 +571,12 @@ struct WideCfg {
 template <int BM, int EK>
 constexpr size_t wide_lds_bytes() {
   const size_t ops = (size_t)WideCfg<BM>::ST * WideCfg<BM>::SBYTES;
-  const int ntr = EK == EPI_SWIGLU_BWD ? 2 : (EK == EPI_SGD || EK == EPI_SWIGLU_IL || EK == EPI_QKV_ROPE) ? 1 : 0;
+  const int ntr = EK == EPI_SWIGLU_BWD ? 2 : (EK == EPI_SGD || EK == EPI_QKV_ROPE) ? 1 : 0;
   // (EPI_LM_CE reduces through 2 x 4 x BM floats, well within the operand ring)
-  const size_t trb = (size_t)ntr * 256 * (BM + 8) * 2;
+  // EPI_SWIGLU_IL: the transposed activations (128 rows of BM + 8) and the activation rows
+  // (BM rows of 128 + 8) side by side
+  const size_t trb = EK == EPI_SWIGLU_IL ? (size_t)128 * (BM + 8) * 2 + (size_t)BM * 136 * 2
+                                         : (size_t)ntr * 256 * (BM + 8) * 2;
   return ops > trb ? ops : trb;
 }
 
@@ -801,9 +804,15 @@ __device__ __forceinline__ void wide_epilogue(const GemmArgs& g, f32x16 (&acc)[T
           x[r] = acc[i][jg][4 * q + r];
           u[r] = acc[i][jg + 1][4 * q + r];
           a[r] = x[r] * sigmoid_fast(x[r]) * u[r];
-          tr0[(fl + r) * TLD + ml] = f2bf(a[r]);
         }
-        *(uint2*)((bf16*)e.c + bz * e.sc + (int64_t)m * e.ldc + fi) = pk4(a[0], a[1], a[2], a[3]);
+        const uint2 ab = pk4(a[0], a[1], a[2], a[3]);
+        if (e.t) {
+          tr0[(fl + 0) * TLD + ml] = bf16{(uint16_t)ab.x};
+          tr0[(fl + 1) * TLD + ml] = bf16{(uint16_t)(ab.x >> 16)};
+          tr0[(fl + 2) * TLD + ml] = bf16{(uint16_t)ab.y};
+          tr0[(fl + 3) * TLD + ml] = bf16{(uint16_t)(ab.y >> 16)};
+        }
+        *(uint2*)(tr0 + (BN / 2) * TLD + ml * 136 + fl) = ab;  // activation rows, stored below
         if (e.zg) {
           *(uint2*)((bf16*)e.zg + bz * e.sz + (int64_t)m * e.ldz + fi) = pk4(x[0], x[1], x[2], x[3]);
           *(uint2*)((bf16*)e.zu + bz * e.sz + (int64_t)m * e.ldz + fi) = pk4(u[0], u[1], u[2], u[3]);
@@ -882,6 +891,16 @@ __device__ __forceinline__ void wide_epilogue(const GemmArgs& g, f32x16 (&acc)[T
             tr0[(nl + 3) * TLD + ml] = bf16{(uint16_t)(wb.y >> 16)};
           }
         }
+    }
+  }
+  if constexpr (EK == EPI_SWIGLU_IL) {
+    // the activation tile (BM rows of 128) leaves LDS as whole 256-byte row segments
+    __syncthreads();
+    const bf16* sa = tr0 + (BN / 2) * TLD;
+    bf16* cb = (bf16*)e.c + bz * e.sc + (int64_t)m0 * e.ldc + n0 / 2;
+    for (int c = tid; c < BM * 16; c += NT) {
+      const int r = c / 16, s8 = (c % 16) * 8;
+      *(uint4*)(cb + (int64_t)r * e.ldc + s8) = *(const uint4*)(sa + r * 136 + s8);
     }
   }
   if constexpr (TR) {
@@ -1272,7 +1291,7 @@ bool wide_ok(const GemmArgs& g) {
     case EPI_ADD_F32: return e.ldc % 4 == 0 && e.sc % 4 == 0 && al(e.c, 16);
     case EPI_T: return e.ldc % 4 == 0 && e.sc % 4 == 0 && al(e.c, 8);
     case EPI_SWIGLU_IL:
-      return e.ldc % 4 == 0 && e.sc % 4 == 0 && al(e.c, 8) &&
+      return e.ldc % 8 == 0 && e.sc % 8 == 0 && al(e.c, 16) &&
              (!e.zg || (e.ldz % 4 == 0 && e.sz % 4 == 0 && al(e.zg, 8) && al(e.zu, 8))) &&
              (!e.t || (e.ldt % 8 == 0 && e.st % 8 == 0 && al(e.t, 16)));
     case EPI_SGD:
