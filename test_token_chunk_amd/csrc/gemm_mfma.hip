@@ -575,7 +575,9 @@ constexpr size_t wide_lds_bytes() {
   // (EPI_LM_CE reduces through 2 x 4 x BM floats, well within the operand ring)
   // EPI_SWIGLU_IL: the transposed activations (128 rows of BM + 8) and the activation rows
   // (BM rows of 128 + 8) side by side
+  // EPI_ADD_F32: 128 rows of 256 + 4 floats (the residual rows are updated 128 at a time)
   const size_t trb = EK == EPI_SWIGLU_IL ? (size_t)128 * (BM + 8) * 2 + (size_t)BM * 136 * 2
+                     : EK == EPI_ADD_F32 ? (size_t)128 * 260 * 4
                                          : (size_t)ntr * 256 * (BM + 8) * 2;
   return ops > trb ? ops : trb;
 }
@@ -619,6 +621,35 @@ __device__ __forceinline__ void wide_epilogue(const GemmArgs& g, f32x16 (&acc)[T
     for (int c = tid; c < BM * (BN / 4); c += NT) {
       const int r = c / (BN / 4), c4 = (c % (BN / 4)) * 4;
       *(float4*)(part + (int64_t)r * g.N + c4) = *(const float4*)(st + r * SLD + c4);
+    }
+    return;
+  }
+  if constexpr (EK == EPI_ADD_F32) {
+    // residual update c += acc, 128 rows at a time through LDS: each wave reads and writes whole
+    // 1 KB rows of c instead of 32-byte pieces of 32 rows
+    constexpr int SLD = BN + 4, HR = BM < 128 ? BM : 128;
+    float* st = reinterpret_cast<float*>(smem_raw);
+    float* cb = (float*)e.c + bz * e.sc + (int64_t)m0 * e.ldc + n0;
+#pragma unroll
+    for (int h0 = 0; h0 < BM; h0 += HR) {
+      if (h0 > 0) __syncthreads();  // the previous rows have been read out of LDS
+      if (wm0 >= h0 && wm0 < h0 + HR) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              *(float4*)(st + (wm0 - h0 + i * 32 + lr) * SLD + wn0 + j * 32 + 8 * q + 4 * hi) =
+                  make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+      }
+      __syncthreads();
+      for (int c = tid; c < HR * (BN / 4); c += NT) {
+        const int r = c / (BN / 4), c4 = (c % (BN / 4)) * 4;
+        float* p = cb + (int64_t)(h0 + r) * e.ldc + c4;
+        const float4 v = *(const float4*)(st + r * SLD + c4), o = *(const float4*)p;
+        *(float4*)p = make_float4(o.x + v.x, o.y + v.y, o.z + v.z, o.w + v.w);
+      }
     }
     return;
   }
