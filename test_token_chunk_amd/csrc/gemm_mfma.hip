@@ -364,8 +364,8 @@ __device__ __forceinline__ void dl_tile(int& m0, int& n0) {
 // Fused SGD step of the 128 x 128 loop with the MFMA operands swapped (lane = output row m,
 // four consecutive columns n per register group): the fp32 master values of the tile are
 // loaded into registers before the main loop (their latency hides behind it), then
-// master -= lr * acc is stored as 16-byte row segments, the row-major shadow as 8-byte
-// segments and the transposed shadow through LDS as 16-byte segments.
+// master -= lr * acc, its row-major bf16 shadow and the transposed shadow go through LDS and
+// leave as whole rows (the master and the shadow a quarter of the tile at a time).
 __device__ __forceinline__ void dl_sgd_prefetch(const GemmArgs& g, float4 (&pre)[2][2][4], int m0, int n0, int wm0,
                                                 int wn0, int lane, int bz) {
   const int lr = lane & 31, hi = lane >> 5;
@@ -383,30 +383,48 @@ __device__ __forceinline__ void dl_sgd_prefetch(const GemmArgs& g, float4 (&pre)
 __device__ __forceinline__ void dl_sgd_epilogue(const GemmArgs& g, f32x16 (&acc)[2][2], const float4 (&pre)[2][2][4],
                                                 unsigned char* smem_raw, int m0, int n0, int wm0, int wn0, int tid,
                                                 int bz) {
-  constexpr int BM = 128, BN = 128, TLD = BM + 8;
+  constexpr int BM = 128, BN = 128, TLD = BM + 8, SLD = BN + 4, BLD = BN + 8;
   const int lane = tid & 63, lr = lane & 31, hi = lane >> 5;
   const Epi& e = g.e;
-  bf16* tr = reinterpret_cast<bf16*>(smem_raw);  // [BN][TLD]: tile row n holds BM consecutive m
+  // LDS: the transposed shadow tile [BN][TLD], then one quarter (32 rows) of the updated master
+  // [32][SLD] and of the row-major shadow [32][BLD]; a quarter leaves LDS as whole rows
+  bf16* tr = reinterpret_cast<bf16*>(smem_raw);
+  float* sq = reinterpret_cast<float*>(smem_raw + BN * TLD * 2);
+  bf16* sb = reinterpret_cast<bf16*>(smem_raw + BN * TLD * 2 + 32 * SLD * 4);
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int ml = wm0 + i * 32 + lr, m = m0 + ml;
-    const int64_t shrow = e.il_f ? swiglu_il_row(m, e.il_f) : m;
+  for (int Q = 0; Q < 4; ++Q) {
+    if (Q > 0) __syncthreads();  // the previous quarter has left LDS
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int i = 0; i < 2; ++i) {
+      if (wm0 + 32 * i != 32 * Q) continue;  // (wave-uniform)
+      const int ml = wm0 + i * 32 + lr;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int nl = wn0 + j * 32 + 8 * q + 4 * hi, n = n0 + nl;
-        const float4 w = make_float4(pre[i][j][q].x - e.lr * acc[i][j][4 * q], pre[i][j][q].y - e.lr * acc[i][j][4 * q + 1],
-                                     pre[i][j][q].z - e.lr * acc[i][j][4 * q + 2],
-                                     pre[i][j][q].w - e.lr * acc[i][j][4 * q + 3]);
-        *(float4*)(e.master + bz * e.sm + (int64_t)m * e.ldm + n) = w;
-        const uint32_t p01 = bf16pair(w.x, w.y), p23 = bf16pair(w.z, w.w);
-        *(uint2*)((bf16*)e.sh + bz * e.ssh + shrow * e.ldsh + n) = make_uint2(p01, p23);
-        tr[(nl + 0) * TLD + ml] = bf16{(uint16_t)p01};
-        tr[(nl + 1) * TLD + ml] = bf16{(uint16_t)(p01 >> 16)};
-        tr[(nl + 2) * TLD + ml] = bf16{(uint16_t)p23};
-        tr[(nl + 3) * TLD + ml] = bf16{(uint16_t)(p23 >> 16)};
-      }
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int nl = wn0 + j * 32 + 8 * q + 4 * hi;
+          const float4 w = make_float4(pre[i][j][q].x - e.lr * acc[i][j][4 * q], pre[i][j][q].y - e.lr * acc[i][j][4 * q + 1],
+                                       pre[i][j][q].z - e.lr * acc[i][j][4 * q + 2],
+                                       pre[i][j][q].w - e.lr * acc[i][j][4 * q + 3]);
+          const uint32_t p01 = bf16pair(w.x, w.y), p23 = bf16pair(w.z, w.w);
+          *(float4*)(sq + lr * SLD + nl) = w;
+          *(uint2*)(sb + lr * BLD + nl) = make_uint2(p01, p23);
+          tr[(nl + 0) * TLD + ml] = bf16{(uint16_t)p01};
+          tr[(nl + 1) * TLD + ml] = bf16{(uint16_t)(p01 >> 16)};
+          tr[(nl + 2) * TLD + ml] = bf16{(uint16_t)p23};
+          tr[(nl + 3) * TLD + ml] = bf16{(uint16_t)(p23 >> 16)};
+        }
+    }
+    __syncthreads();
+    for (int c = tid; c < 32 * (BN / 4); c += 256) {
+      const int r = c / (BN / 4), c4 = (c % (BN / 4)) * 4, m = m0 + 32 * Q + r;
+      *(float4*)(e.master + bz * e.sm + (int64_t)m * e.ldm + n0 + c4) = *(const float4*)(sq + r * SLD + c4);
+    }
+    for (int c = tid; c < 32 * (BN / 8); c += 256) {
+      const int r = c / (BN / 8), c8 = (c % (BN / 8)) * 8, m = m0 + 32 * Q + r;
+      const int64_t shrow = e.il_f ? swiglu_il_row(m, e.il_f) : m;
+      *(uint4*)((bf16*)e.sh + bz * e.ssh + shrow * e.ldsh + n0 + c8) = *(const uint4*)(sb + r * BLD + c8);
+    }
   }
   __syncthreads();
   bf16* dst = (bf16*)e.shT + bz * e.sshT;
@@ -416,6 +434,8 @@ __device__ __forceinline__ void dl_sgd_epilogue(const GemmArgs& g, f32x16 (&acc)
     *(uint4*)(dst + (int64_t)(n0 + nl) * e.ldshT + m0 + ml) = *(const uint4*)(tr + nl * TLD + ml);
   }
 }
+
+static_assert(128 * 136 * 2 + 32 * 132 * 4 + 32 * 136 * 2 <= 2 * DL_TILE_BYTES, "SGD epilogue staging fits two stages");
 
 template <int EK, int STAGES, bool SPLIT>
 __global__ __launch_bounds__(256) void k_gemm_dl(GemmArgs g) {
