@@ -1,7 +1,8 @@
 /*
  * ttt_kernels.h -- kernel-level entry points of the MI355X TTT-E2E library,
  * for unit tests and micro-benchmarks of single kernels.  All pointers are
- * DEVICE pointers owned by the caller; every call is asynchronous on
+ * DEVICE pointers owned by the caller, 16-byte aligned (as hipMalloc and torch
+ * allocations are); every call is asynchronous on
  * `stream` (hipStream_t, may be NULL) and returns 0 or a negative TTT_E* code
  * (include/ttt.h) for a bad argument or a launch failure.  dtype is TTT_F32
  * (fp32 operands, SIMT kernels) or TTT_BF16 (bf16 operands, matrix cores).

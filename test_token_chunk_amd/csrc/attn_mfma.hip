@@ -311,37 +311,64 @@ _Pragma("unroll") \
 #undef STV
 #undef STORE_TILE
   lrun += __shfl_xor(lrun, 32, 64);
-  if (!qok) return;
+  // The block's output rows leave through LDS as whole rows (queries past the chunk end are not
+  // written): every wave is done with the K and V^T tiles first.
+  __syncthreads();
+  const int qr = wid * QW + (lane & 31);  // the lane's query row in the block
   if constexpr (SPLIT) {
-    const int64_t row = ((int64_t)sp * a.B * a.H + bh) * a.n + tq;  // [S][B][H][n]
-    float* po = a.ws + row * HD;
+    // fp32 part [S][B][H][n][HD] of this key range (the block's rows are consecutive), half the
+    // block's queries at a time; the reference and the row sum per query beside it
+    constexpr int SLD = HD + 4, HQ = BQ / 2;
+    static_assert(HQ * SLD * 4 <= sizeof(FwdSmem<HD>), "staged part rows fit");
+    float* st = reinterpret_cast<float*>(smem_raw);
+    const int64_t row0 = ((int64_t)sp * a.B * a.H + bh) * a.n + t0;
     float* pm = a.ws + (int64_t)S * a.B * a.H * a.n * HD;
     float* pl = pm + (int64_t)S * a.B * a.H * a.n;
+    if (qok && g == 0) {
+      pm[row0 + qr] = mref == -INFINITY ? -INFINITY : mref / sl2;  // raw score units
+      pl[row0 + qr] = lrun;
+    }
 #pragma unroll
-    for (int hm = 0; hm < HM; ++hm)
+    for (int half = 0; half < 2; ++half) {
+      if (half > 0) __syncthreads();  // the first half's rows have left LDS
+      if (qr / HQ == half) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int d0 = hm * 32 + 8 * j + 4 * g;
-        *(float4*)(po + d0) = make_float4(o[hm][4 * j], o[hm][4 * j + 1], o[hm][4 * j + 2], o[hm][4 * j + 3]);
+        for (int hm = 0; hm < HM; ++hm)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int d0 = hm * 32 + 8 * j + 4 * g;
+            *(float4*)(st + (qr - half * HQ) * SLD + d0) = make_float4(o[hm][4 * j], o[hm][4 * j + 1], o[hm][4 * j + 2], o[hm][4 * j + 3]);
+          }
       }
-    if (g == 0) {
-      pm[row] = mref == -INFINITY ? -INFINITY : mref / sl2;  // raw score units
-      pl[row] = lrun;
+      __syncthreads();
+      float* po = a.ws + (row0 + half * HQ) * HD;
+      for (int c = tid; c < HQ * (HD / 4); c += NT) {
+        const int r = c / (HD / 4), c4 = (c % (HD / 4)) * 4;
+        if (t0 + half * HQ + r < a.n) *(float4*)(po + (int64_t)r * HD + c4) = *(const float4*)(st + r * SLD + c4);
+      }
     }
     return;
   }
+  // bf16 rows of O [B n][H HD] (head h's HD columns), all BQ queries at once
+  constexpr int OLD = HD + 8;
+  static_assert(BQ * OLD * 2 <= sizeof(FwdSmem<HD>), "staged output rows fit");
+  bf16* so = reinterpret_cast<bf16*>(smem_raw);
   const float inv = 1.f / lrun;
-  bf16* out = (bf16*)a.o + ((int64_t)b * a.n + tq) * ((int64_t)a.H * HD) + (int64_t)h * HD;
 #pragma unroll
   for (int hm = 0; hm < HM; ++hm)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int d0 = hm * 32 + 8 * j + 4 * g;
-      uint2 w = make_uint2(pk2(o[hm][4 * j] * inv, o[hm][4 * j + 1] * inv),
-                           pk2(o[hm][4 * j + 2] * inv, o[hm][4 * j + 3] * inv));
-      *(uint2*)(out + d0) = w;
+      *(uint2*)(so + qr * OLD + d0) = make_uint2(pk2(o[hm][4 * j] * inv, o[hm][4 * j + 1] * inv),
+                                                 pk2(o[hm][4 * j + 2] * inv, o[hm][4 * j + 3] * inv));
     }
-  if (a.lse && g == 0) a.lse[bh * a.n + tq] = (mref + log2f(lrun)) * 0.6931471805599453f;
+  if (a.lse && qok && g == 0) a.lse[bh * a.n + tq] = (mref + log2f(lrun)) * 0.6931471805599453f;
+  __syncthreads();
+  bf16* ob = (bf16*)a.o + ((int64_t)b * a.n + t0) * ((int64_t)a.H * HD) + (int64_t)h * HD;
+  for (int c = tid; c < BQ * (HD / 8); c += NT) {
+    const int r = c / (HD / 8), c8 = (c % (HD / 8)) * 8;
+    if (t0 + r < a.n) *(uint4*)(ob + (int64_t)r * (a.H * HD) + c8) = *(const uint4*)(so + r * OLD + c8);
+  }
 }
 
 // merge the key-range parts of a split forward: O = sum_s w_s O_s / sum_s w_s l_s with
@@ -835,20 +862,34 @@ __global__ __launch_bounds__(256) void k_swa_dkv(AttnBwdArgs a, int P) {
   }
 #undef LD
 #undef LOAD_QTILE
-  if (!kok) return;
+  // dK (scaled) and then dV of the block's keys leave through LDS as whole rows of HD floats
+  // (keys past the chunk end hold zeros and are not written)
   const float sc = 1.f / sqrtf((float)HD);
   const int64_t plane = (int64_t)a.B * a.n * d;
-  float* ok_ = (P > 1 ? a.ws + part * plane : a.dk) + ((int64_t)b * a.n + sk) * d + (int64_t)h * HD;
-  float* ov_ = (P > 1 ? a.ws + (P + part) * plane : a.dv) + ((int64_t)b * a.n + sk) * d + (int64_t)h * HD;
+  constexpr int SLD = HD + 4;
+  static_assert(BQ * SLD * 4 <= sizeof(DkvSmem<HD>), "staged dK / dV rows fit");
+  float* st = reinterpret_cast<float*>(smem_raw);
+  const int kr = wid * QW + (lane & 31);  // the lane's key row in the block
 #pragma unroll
-  for (int hm = 0; hm < HM; ++hm)
+  for (int which = 0; which < 2; ++which) {
+    __syncthreads();  // the last tile's (then the dK rows') reads of LDS are done
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int d0 = hm * 32 + 8 * j + 4 * g;
-      *(float4*)(ok_ + d0) = make_float4(dk[hm][4 * j] * sc, dk[hm][4 * j + 1] * sc, dk[hm][4 * j + 2] * sc,
-                                         dk[hm][4 * j + 3] * sc);
-      *(float4*)(ov_ + d0) = make_float4(dv[hm][4 * j], dv[hm][4 * j + 1], dv[hm][4 * j + 2], dv[hm][4 * j + 3]);
+    for (int hm = 0; hm < HM; ++hm)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d0 = hm * 32 + 8 * j + 4 * g;
+        *(float4*)(st + kr * SLD + d0) =
+            which == 0 ? make_float4(dk[hm][4 * j] * sc, dk[hm][4 * j + 1] * sc, dk[hm][4 * j + 2] * sc, dk[hm][4 * j + 3] * sc)
+                       : make_float4(dv[hm][4 * j], dv[hm][4 * j + 1], dv[hm][4 * j + 2], dv[hm][4 * j + 3]);
+      }
+    __syncthreads();
+    float* base = (P > 1 ? a.ws + (which * P + part) * plane : (which ? a.dv : a.dk)) + ((int64_t)b * a.n + s0blk) * d +
+                  (int64_t)h * HD;
+    for (int c = tid; c < BQ * (HD / 4); c += 256) {
+      const int r = c / (HD / 4), c4 = (c % (HD / 4)) * 4;
+      if (s0blk + r < a.n) *(float4*)(base + (int64_t)r * d + c4) = *(const float4*)(st + r * SLD + c4);
     }
+  }
 }
 
 template <typename Smem, typename K>
@@ -1074,17 +1115,33 @@ __global__ __launch_bounds__(512) void k_swa_dq2(AttnBwdArgs a, int S) {
     WAIT_VM_LDS(0);
     __syncthreads();
   }
-  if (!qok) return;
+  // dQ rows leave through LDS as whole rows of HD floats, half the block's queries at a time
+  // (queries past the chunk end hold zeros and are not written)
   const float sc = 1.f / sqrtf((float)HD);
-  float* out = (SPLIT ? a.ws + (int64_t)sp * a.B * a.n * d : a.dq) + ((int64_t)b * a.n + tq) * d + (int64_t)h * HD;
+  constexpr int SLD = HD + 4, HQ = BQn / 2;
+  static_assert(HQ * SLD * 4 <= 2 * SB, "staged dQ rows fit");
+  float* st = reinterpret_cast<float*>(smem_raw);
+  float* outb = (SPLIT ? a.ws + (int64_t)sp * a.B * a.n * d : a.dq) + ((int64_t)b * a.n + t0) * d + (int64_t)h * HD;
 #pragma unroll
-  for (int hm = 0; hm < HM; ++hm)
+  for (int half = 0; half < 2; ++half) {
+    if (half > 0) __syncthreads();  // the first half's rows have left LDS
+    if (wid / (NW / 2) == half) {
+      const int r = (wid % (NW / 2)) * QW + l32;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int d0 = hm * 32 + 8 * j + 4 * g;
-      *(float4*)(out + d0) = make_float4(acc[hm][4 * j] * sc, acc[hm][4 * j + 1] * sc, acc[hm][4 * j + 2] * sc,
-                                         acc[hm][4 * j + 3] * sc);
+      for (int hm = 0; hm < HM; ++hm)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int d0 = hm * 32 + 8 * j + 4 * g;
+          *(float4*)(st + r * SLD + d0) = make_float4(acc[hm][4 * j] * sc, acc[hm][4 * j + 1] * sc,
+                                                      acc[hm][4 * j + 2] * sc, acc[hm][4 * j + 3] * sc);
+        }
     }
+    __syncthreads();
+    for (int c = tid; c < HQ * (HD / 4); c += NW * 64) {
+      const int r = c / (HD / 4), c4 = (c % (HD / 4)) * 4, tq_ = half * HQ + r;
+      if (t0 + tq_ < a.n) *(float4*)(outb + (int64_t)tq_ * d + c4) = *(const float4*)(st + r * SLD + c4);
+    }
+  }
 }
 
 template <int HD, bool SPLIT>
