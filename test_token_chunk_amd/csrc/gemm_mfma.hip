@@ -365,7 +365,11 @@ __device__ __forceinline__ void dl_tile(int& m0, int& n0) {
 // four consecutive columns n per register group): the fp32 master values of the tile are
 // loaded into registers before the main loop (their latency hides behind it), then
 // master -= lr * acc, its row-major bf16 shadow and the transposed shadow go through LDS and
-// leave as whole rows (the master and the shadow a quarter of the tile at a time).
+// leave as whole rows (the master and the shadow a quarter of the tile at a time), with
+// non-temporal stores: the next chunk reads them, so they need not displace the operand panels
+// (and what the kernels of the other streams hold) from the L2s.
+typedef float nt_f4 __attribute__((ext_vector_type(4)));
+typedef unsigned nt_u4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ void dl_sgd_prefetch(const GemmArgs& g, float4 (&pre)[2][2][4], int m0, int n0, int wm0,
                                                 int wn0, int lane, int bz) {
   const int lr = lane & 31, hi = lane >> 5;
@@ -418,12 +422,12 @@ __device__ __forceinline__ void dl_sgd_epilogue(const GemmArgs& g, f32x16 (&acc)
     __syncthreads();
     for (int c = tid; c < 32 * (BN / 4); c += 256) {
       const int r = c / (BN / 4), c4 = (c % (BN / 4)) * 4, m = m0 + 32 * Q + r;
-      *(float4*)(e.master + bz * e.sm + (int64_t)m * e.ldm + n0 + c4) = *(const float4*)(sq + r * SLD + c4);
+      __builtin_nontemporal_store(*(const nt_f4*)(sq + r * SLD + c4), (nt_f4*)(e.master + bz * e.sm + (int64_t)m * e.ldm + n0 + c4));
     }
     for (int c = tid; c < 32 * (BN / 8); c += 256) {
       const int r = c / (BN / 8), c8 = (c % (BN / 8)) * 8, m = m0 + 32 * Q + r;
       const int64_t shrow = e.il_f ? swiglu_il_row(m, e.il_f) : m;
-      *(uint4*)((bf16*)e.sh + bz * e.ssh + shrow * e.ldsh + n0 + c8) = *(const uint4*)(sb + r * BLD + c8);
+      __builtin_nontemporal_store(*(const nt_u4*)(sb + r * BLD + c8), (nt_u4*)((bf16*)e.sh + bz * e.ssh + shrow * e.ldsh + n0 + c8));
     }
   }
   __syncthreads();
@@ -431,7 +435,7 @@ __device__ __forceinline__ void dl_sgd_epilogue(const GemmArgs& g, f32x16 (&acc)
   constexpr int CH = BM / 8;
   for (int c = tid; c < BN * CH; c += 256) {
     const int nl = c / CH, ml = (c % CH) * 8;
-    *(uint4*)(dst + (int64_t)(n0 + nl) * e.ldshT + m0 + ml) = *(const uint4*)(tr + nl * TLD + ml);
+    __builtin_nontemporal_store(*(const nt_u4*)(tr + nl * TLD + ml), (nt_u4*)(dst + (int64_t)(n0 + nl) * e.ldshT + m0 + ml));
   }
 }
 
