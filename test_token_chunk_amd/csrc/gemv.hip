@@ -19,7 +19,10 @@
 
 namespace {
 
-constexpr int GW = 4;  // waves per block
+// waves per block: 4, or 8 when the block first stages the normalized rows in LDS (the staging
+// pass reads x and the gains once per block, so more waves share it)
+template <bool NRM>
+constexpr int gemv_waves() { return NRM ? 8 : 4; }
 
 typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 
@@ -72,7 +75,8 @@ __device__ __forceinline__ void qkv_rope_store(const RopeRing& rr, int part, int
 }
 
 template <int MR, int NR, int KIND, bool NRM>
-__global__ __launch_bounds__(256) void k_gemv(GemmArgs g, int ncols, int f) {
+__global__ __launch_bounds__(64 * gemv_waves<NRM>()) void k_gemv(GemmArgs g, int ncols, int f) {
+  constexpr int GW = gemv_waves<NRM>();
   constexpr bool SW = KIND == EPI_SWIGLU || KIND == EPI_SWIGLU_IL;
   constexpr bool RP = KIND == EPI_QKV_ROPE;  // NR == 2: the pair (i, i + hd/2); ncols = pairs
   constexpr int RW = SW ? 2 * NR : NR;  // weight rows per wave
@@ -231,11 +235,15 @@ template <int MR, int NR, int KIND>
 hipError_t launch_gemv(const GemmArgs& g, int ncols, int f, hipStream_t s) {
   // one wave per NR columns, or per column pair (ncols counts pairs) with RoPE
   const int64_t waves = KIND == EPI_QKV_ROPE ? ncols : (ncols + NR - 1) / NR;
-  const dim3 grid((unsigned)((waves + GW - 1) / GW), (unsigned)g.batch);
-  if (g.nx)  // rows of x * g staged in LDS: MR * K bf16 (gemv_ok keeps it within 64 KB)
+  if (g.nx) {  // rows of x * g staged in LDS: MR * K bf16 (gemv_ok keeps it within 64 KB)
+    constexpr int GW = gemv_waves<true>();
+    const dim3 grid((unsigned)((waves + GW - 1) / GW), (unsigned)g.batch);
     hipLaunchKernelGGL((k_gemv<MR, NR, KIND, true>), grid, dim3(64 * GW), (size_t)MR * g.K * 2, s, g, ncols, f);
-  else
+  } else {
+    constexpr int GW = gemv_waves<false>();
+    const dim3 grid((unsigned)((waves + GW - 1) / GW), (unsigned)g.batch);
     hipLaunchKernelGGL((k_gemv<MR, NR, KIND, false>), grid, dim3(64 * GW), 0, s, g, ncols, f);
+  }
   return hipGetLastError();
 }
 
