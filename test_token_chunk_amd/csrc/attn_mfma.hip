@@ -892,6 +892,234 @@ __global__ __launch_bounds__(256) void k_swa_dkv(AttnBwdArgs a, int P) {
   }
 }
 
+// dK/dV with the query tiles copied straight from global memory into LDS (buffer loads to
+// LDS, two stages, no staging registers, no per-row bounds tests): the Q and dO tiles
+// [64 queries][hd] with the 16-byte chunks of a row XOR-swizzled by row % (hd/8), the
+// transposed Q^T and dO^T tiles [hd][64 queries] swizzled by (row / 2) % 8, and the tile's
+// 64 log-sum-exp and D values.  Otherwise as k_swa_dkv (TR form): every query tile of the
+// chunk is whole (n % 64 == 0), head dim 128, 32-bit byte offsets within a head's arrays.
+template <int HD>
+constexpr int dkv2_stage_bytes() { return 4 * KT * HD * 2 + 2 * 1024; }
+
+template <int HD>
+__global__ __launch_bounds__(256) void k_swa_dkv2(AttnBwdArgs a, int P) {
+  constexpr int KS = HD / 16, HM = HD / 32;
+  constexpr int CPR = HD / 8;             // 16-byte chunks per Q / dO row
+  constexpr int RPK = 1024 / (HD * 2);    // Q / dO rows per 1 KB copy
+  constexpr int TB = KT * HD * 2 / 1024;  // 1 KB copies per tile (each of the four)
+  constexpr int TBW = TB / 4;             // per wave
+  constexpr int SB = dkv2_stage_bytes<HD>();
+  constexpr int OOFF = KT * HD * 2, QTOFF = 2 * KT * HD * 2, OTOFF = 3 * KT * HD * 2;
+  constexpr int LOFF = 4 * KT * HD * 2, DOFF = LOFF + 1024;
+  static_assert(TB % 4 == 0 && CPR == 16 && KT == 64, "tile copy layout");
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: LDS addresses stay scalar
+  const int b = blockIdx.z, h = blockIdx.x, part = blockIdx.y % P;
+  const int64_t bh = (int64_t)b * a.H + h;
+  const int R = a.R, d = a.H * HD, n = a.n;
+  const int s0blk = (blockIdx.y / P) * BQ;
+  const int sk = s0blk + wid * QW + l32;  // this lane's key (chunk-local)
+  const bool kok = sk < n;
+  const int wsk_hi = s0blk + wid * QW + QW - 1;
+  const bool wkok = wsk_hi < n;
+  const float LOG2E = 1.4426950408889634f;
+  const float sl2 = LOG2E / sqrtf((float)HD);
+
+  bf16x8 k0, k1, k2, k3, k4, k5, k6, k7, v0, v1, v2, v3, v4, v5, v6, v7;
+  {
+    const int slot = (int)((a.pos0 + (kok ? sk : 0)) % R);
+    const bf16* kp = (const bf16*)a.kr + (bh * R + slot) * HD + g * 8;
+    const bf16* vp = (const bf16*)a.vr + (bh * R + slot) * HD + g * 8;
+    auto ld8 = [&](const bf16* p, int ks) {
+      uint4 v = kok ? *(const uint4*)(p + ks * 16) : make_uint4(0, 0, 0, 0);
+      return __builtin_bit_cast(bf16x8, v);
+    };
+    k0 = ld8(kp, 0); k1 = ld8(kp, 1); v0 = ld8(vp, 0); v1 = ld8(vp, 1);
+    if constexpr (KS > 2) { k2 = ld8(kp, 2); k3 = ld8(kp, 3); v2 = ld8(vp, 2); v3 = ld8(vp, 3); }
+    if constexpr (KS > 4) { k4 = ld8(kp, 4); k5 = ld8(kp, 5); v4 = ld8(vp, 4); v5 = ld8(vp, 5); }
+    if constexpr (KS > 6) { k6 = ld8(kp, 6); k7 = ld8(kp, 7); v6 = ld8(vp, 6); v7 = ld8(vp, 7); }
+  }
+  f32x16 dk[HM], dv[HM];
+#pragma unroll
+  for (int i = 0; i < HM; ++i) {
+    dk[i] = f32x16{};
+    dv[i] = f32x16{};
+  }
+  const int tfirst = (s0blk / KT) * KT;
+  const int ntq = (n - tfirst + KT - 1) / KT;
+  const int per = (ntq + P - 1) / P;
+  const int tbeg = tfirst + part * per * KT;
+  const int tstop = min(n, tfirst + (part + 1) * per * KT);
+
+  // the head's Q, Q^T, dO^T, lse and D and the row's dO are buffers (32-bit byte offsets,
+  // checked at launch); each lane keeps the byte offsets of its rows and chunks, a query tile
+  // moves only the scalar offset
+  const __amdgpu_buffer_rsrc_t rq = buf_rsrc((const bf16*)a.q + bh * n * HD, (uint32_t)(n * HD * 2));
+  const __amdgpu_buffer_rsrc_t rqt = buf_rsrc((const bf16*)a.qt + bh * HD * n, (uint32_t)(n * HD * 2));
+  const __amdgpu_buffer_rsrc_t rot = buf_rsrc((const bf16*)a.dot + bh * HD * n, (uint32_t)(n * HD * 2));
+  const __amdgpu_buffer_rsrc_t ro =
+      buf_rsrc((const bf16*)a.dout + (int64_t)b * n * d + (int64_t)h * HD, (uint32_t)((int64_t)n * d * 2));
+  const __amdgpu_buffer_rsrc_t rl = buf_rsrc(a.lse + bh * n, (uint32_t)(n * 4));
+  const __amdgpu_buffer_rsrc_t rd = buf_rsrc(a.dvec + bh * n, (uint32_t)(n * 4));
+  int oq[TBW], oo[TBW], ot[TBW];
+#pragma unroll
+  for (int u = 0; u < TBW; ++u) {
+    const int j = wid * TBW + u;
+    const int row = j * RPK + lane / CPR, c = (lane % CPR) ^ (row % CPR);
+    oq[u] = (row * HD + c * 8) * 2;
+    oo[u] = (row * d + c * 8) * 2;
+    const int trow = j * 8 + (lane >> 3), tc = (lane & 7) ^ ((trow >> 1) & 7);
+    ot[u] = (trow * n + tc * 8) * 2;
+  }
+  const int ol = (lane & 15) * 16;  // lanes 16..63 copy the same 256 bytes again
+  auto issue = [&](int t0, int st) {
+    unsigned char* base = smem_raw + st * SB;
+#pragma unroll
+    for (int u = 0; u < TBW; ++u) {
+      const int j = wid * TBW + u;
+      buf_lds16(rq, base + j * 1024, oq[u], t0 * HD * 2);
+      buf_lds16(ro, base + OOFF + j * 1024, oo[u], t0 * d * 2);
+      buf_lds16(rqt, base + QTOFF + j * 1024, ot[u], t0 * 2);
+      buf_lds16(rot, base + OTOFF + j * 1024, ot[u], t0 * 2);
+    }
+    if (wid == 0) {
+      buf_lds16(rl, base + LOFF, ol, t0 * 4);
+      buf_lds16(rd, base + DOFF, ol, t0 * 4);
+    }
+  };
+  const int xr = l32 % CPR, xt = (l32 >> 1) & 7;
+  if (tbeg < tstop) issue(tbeg, 0);
+  WAIT_VM_LDS(0);
+  __syncthreads();
+  int it = 0;
+  for (int tq0 = tbeg; tq0 < tstop; tq0 += KT, ++it) {
+    const int cur = it & 1;
+    const unsigned char* stg = smem_raw + cur * SB;
+    const float* lse_t = reinterpret_cast<const float*>(stg + LOFF);
+    const float* dd_t = reinterpret_cast<const float*>(stg + DOFF);
+    // With one wave per SIMD nothing hides an LDS read that an MFMA waits for, so each phase
+    // reads all its fragments first (one LDS latency per phase instead of one per MFMA); the
+    // Q^T / dO^T fragments of a half are read before its softmax, which covers their latency.
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      f32x16 s0 = f32x16{}, p0 = f32x16{};
+      const unsigned char* qrow = stg + (hf * 32 + l32) * (HD * 2);
+      bf16x8 aq[KS], ao[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int co = (((2 * ks + g) ^ xr) << 4);
+        aq[ks] = *(const bf16x8*)(qrow + co);
+        ao[ks] = *(const bf16x8*)(qrow + OOFF + co);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#define SSTEP(ks, kv, vv)                                                               \
+  if constexpr (KS > ks) {                                                              \
+    s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[ks], kv, s0, 0, 0, 0);              \
+    p0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao[ks], vv, p0, 0, 0, 0);              \
+  }
+      SSTEP(0, k0, v0) SSTEP(1, k1, v1) SSTEP(2, k2, v2) SSTEP(3, k3, v3)
+      SSTEP(4, k4, v4) SSTEP(5, k5, v5) SSTEP(6, k6, v6) SSTEP(7, k7, v7)
+#undef SSTEP
+      __builtin_amdgcn_sched_barrier(0);
+      // Q^T / dO^T fragments of this half (k index = the permuted queries, see k_swa_dkv)
+      bf16x8 tqf[2][HM], tof[2][HM];
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const int ch = hf * 4 + st * 2;  // 16-byte chunk of queries hf*32 + st*16 .. +7
+#pragma unroll
+        for (int hm = 0; hm < HM; ++hm) {
+          const unsigned char* trow = stg + QTOFF + (hm * 32 + l32) * (KT * 2) + 8 * g;
+          const unsigned char* orow = stg + OTOFF + (hm * 32 + l32) * (KT * 2) + 8 * g;
+          const uint2 ql = *(const uint2*)(trow + ((ch ^ xt) << 4));
+          const uint2 qh = *(const uint2*)(trow + (((ch + 1) ^ xt) << 4));
+          const uint2 olo = *(const uint2*)(orow + ((ch ^ xt) << 4));
+          const uint2 ohi = *(const uint2*)(orow + (((ch + 1) ^ xt) << 4));
+          tof[st][hm] = __builtin_bit_cast(bf16x8, make_uint4(olo.x, olo.y, ohi.x, ohi.y));
+          tqf[st][hm] = __builtin_bit_cast(bf16x8, make_uint4(ql.x, ql.y, qh.x, qh.y));
+        }
+      }
+      float4 l4s[4], d4s[4];
+#pragma unroll
+      for (int j4 = 0; j4 < 4; ++j4) {
+        l4s[j4] = *(const float4*)&lse_t[hf * 32 + 8 * j4 + 4 * g];
+        d4s[j4] = *(const float4*)&dd_t[hf * 32 + 8 * j4 + 4 * g];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // the copies of the next tile go out after the last LDS reads of this one (the other
+      // stage was released by the previous tile's closing barrier): an LDS read issued after
+      // them would wait for them
+      if (hf == 1 && tq0 + KT < tstop) issue(tq0 + KT, cur ^ 1);
+      // rows = queries tq0 + 32 hf + 8 j + 4 g + i; visible iff sk <= t (window >= n here)
+      const int th0 = tq0 + hf * 32;
+      const bool full = wkok && th0 >= wsk_hi;
+      uint32_t pa[8], da[8];
+#pragma unroll
+      for (int j4 = 0; j4 < 4; ++j4) {
+        const float4 l4 = l4s[j4], d4 = d4s[j4];
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dvv[4] = {d4.x, d4.y, d4.z, d4.w};
+        float pv[4], dsv[4];
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int rr = 4 * j4 + i4;
+          const int t = th0 + 8 * j4 + 4 * g + i4;
+          // masked scores become -inf, so the exponential gives 0 without a branch
+          float x = fmaf(s0[rr], sl2, -LOG2E * lv[i4]);
+          if (!full) x = (kok && t >= sk) ? x : -INFINITY;
+          const float p = ex2(x);
+          pv[i4] = p;
+          dsv[i4] = p * (p0[rr] - dvv[i4]);
+        }
+        pa[2 * j4] = pk2(pv[0], pv[1]);
+        pa[2 * j4 + 1] = pk2(pv[2], pv[3]);
+        da[2 * j4] = pk2(dsv[0], dsv[1]);
+        da[2 * j4 + 1] = pk2(dsv[2], dsv[3]);
+      }
+      const bf16x8 pf0 = __builtin_bit_cast(bf16x8, make_uint4(pa[0], pa[1], pa[2], pa[3]));
+      const bf16x8 pf1 = __builtin_bit_cast(bf16x8, make_uint4(pa[4], pa[5], pa[6], pa[7]));
+      const bf16x8 df0 = __builtin_bit_cast(bf16x8, make_uint4(da[0], da[1], da[2], da[3]));
+      const bf16x8 df1 = __builtin_bit_cast(bf16x8, make_uint4(da[4], da[5], da[6], da[7]));
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int hm = 0; hm < HM; ++hm) {
+          dv[hm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tof[st][hm], st ? pf1 : pf0, dv[hm], 0, 0, 0);
+          dk[hm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tqf[st][hm], st ? df1 : df0, dk[hm], 0, 0, 0);
+        }
+    }
+    WAIT_VM_LDS(0);
+    __syncthreads();  // the next tile is in LDS; every wave is done with this one
+  }
+  // dK (scaled) and then dV of the block's keys leave through LDS as whole rows of HD floats
+  // (keys past the chunk end hold zeros and are not written)
+  const float sc = 1.f / sqrtf((float)HD);
+  const int64_t plane = (int64_t)a.B * n * d;
+  constexpr int SLD = HD + 4;
+  static_assert(BQ * SLD * 4 <= 2 * SB, "staged dK / dV rows fit");
+  float* stf = reinterpret_cast<float*>(smem_raw);
+  const int kr = wid * QW + l32;
+#pragma unroll
+  for (int which = 0; which < 2; ++which) {
+    if (which > 0) __syncthreads();  // the dK rows have left LDS
+#pragma unroll
+    for (int hm = 0; hm < HM; ++hm)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d0 = hm * 32 + 8 * j + 4 * g;
+        *(float4*)(stf + kr * SLD + d0) =
+            which == 0 ? make_float4(dk[hm][4 * j] * sc, dk[hm][4 * j + 1] * sc, dk[hm][4 * j + 2] * sc, dk[hm][4 * j + 3] * sc)
+                       : make_float4(dv[hm][4 * j], dv[hm][4 * j + 1], dv[hm][4 * j + 2], dv[hm][4 * j + 3]);
+      }
+    __syncthreads();
+    float* base = (P > 1 ? a.ws + (which * P + part) * plane : (which ? a.dv : a.dk)) + ((int64_t)b * n + s0blk) * d +
+                  (int64_t)h * HD;
+    for (int c = tid; c < BQ * (HD / 4); c += 256) {
+      const int r = c / (HD / 4), c4 = (c % (HD / 4)) * 4;
+      if (s0blk + r < n) *(float4*)(base + (int64_t)r * d + c4) = *(const float4*)(stf + r * SLD + c4);
+    }
+  }
+}
+
 template <typename Smem, typename K>
 hipError_t set_lds(K kern) {
   return hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(Smem));
@@ -1185,6 +1413,31 @@ hipError_t launch_dkv(const AttnBwdArgs& a, int P, hipStream_t s) {
   return hipGetLastError();
 }
 
+// TTT_NO_DKV2=1 (tuning switch): the register-staged dK/dV kernel everywhere
+bool dkv2_off() {
+  static int off = -1;
+  if (off < 0) {
+    const char* e = getenv("TTT_NO_DKV2");
+    off = e && atoi(e) ? 1 : 0;
+  }
+  return off == 1;
+}
+
+template <int HD>
+hipError_t launch_dkv2(const AttnBwdArgs& a, int P, hipStream_t s) {
+  static bool attr = false;
+  if (!attr) {
+    hipError_t e = hipFuncSetAttribute((const void*)k_swa_dkv2<HD>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       2 * dkv2_stage_bytes<HD>());
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  if ((int64_t)cdiv(a.n, BQ) * P > 65535) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((k_swa_dkv2<HD>), dim3(a.H, cdiv(a.n, BQ) * P, a.B), dim3(256), 2 * dkv2_stage_bytes<HD>(), s,
+                     a, P);
+  return hipGetLastError();
+}
+
 template <int HD>
 hipError_t launch_bwd(const AttnBwdArgs& a, hipStream_t s, AttnBwdParts* parts) {
   // the direct-to-LDS dQ form (head dim 128, transposed key ring) computes D = rowsum(dO * O)
@@ -1242,7 +1495,13 @@ hipError_t launch_bwd(const AttnBwdArgs& a, hipStream_t s, AttnBwdParts* parts) 
       }
     }
   }
-  e = tr ? launch_dkv<HD, true>(kv, P, s) : launch_dkv<HD, false>(kv, P, s);
+  // the direct-to-LDS dK/dV form: head dim 128, transposed tiles, whole 64-query tiles, a head's
+  // arrays and the row's dO within 32-bit byte offsets
+  const bool dkv2 = HD == 128 && tr && a.n % KT == 0 && (int64_t)a.n * a.H * HD * 2 < (1LL << 31) && !dkv2_off();
+  if constexpr (HD == 128) {
+    if (dkv2) e = launch_dkv2<HD>(kv, P, s);
+  }
+  if (!dkv2) e = tr ? launch_dkv<HD, true>(kv, P, s) : launch_dkv<HD, false>(kv, P, s);
   if (e != hipSuccess) return e;
   if (parts) {
     parts->dq = S > 1 ? a.ws : a.dq;

@@ -211,7 +211,10 @@ def ref_attention_bwd(q, kr, vr, dO, pos0, window):
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("B,H,hd,n,window,pos0,R", [(1, 2, 32, 64, 256, 1000, 320), (2, 2, 64, 100, 130, 517, 256),
                                                     (1, 2, 128, 130, 200, 331, 336), (1, 2, 128, 200, 1536, 3000, 1736),
-                                                    (2, 3, 96, 136, 300, 4000, 440)])
+                                                    (2, 3, 96, 136, 300, 4000, 440),
+                                                    # whole 64-query tiles at head dim 128 (the direct-to-LDS dK/dV
+                                                    # form): a half-empty last key block, and two rows of 3 heads
+                                                    (1, 2, 128, 192, 512, 3000, 704), (2, 3, 128, 256, 1024, 5000, 1280)])
 def test_swa_bwd_matches_fp64(dtype, B, H, hd, n, window, pos0, R, use_ws, tr):
     """tr: the transposed key ring and a dO^T scratch are passed (16-byte tile copies when n % 8 == 0)."""
     torch = _torch()
