@@ -1460,7 +1460,13 @@ hipError_t launch_bwd(const AttnBwdArgs& a, hipStream_t s, AttnBwdParts* parts) 
   const int64_t blocks8 = (int64_t)cdiv(a.n, 8 * QW) * a.H * a.B;
   const int64_t ntiles = (std::min<int64_t>(a.window, a.pos0 + 1) + 8 * QW) / KT + 1;
   const int64_t total = (int64_t)a.B * a.n * a.H * HD;
-  const int S = attn_splits(blocks8, ntiles, total, a.ws, a.ws_floats);
+  int S = attn_splits(blocks8, ntiles, total, a.ws, a.ws_floats);
+  static int force_s = -1;  // TTT_DQ_SPLITS (tuning switch): key-range parts of dQ
+  if (force_s < 0) {
+    const char* ev = getenv("TTT_DQ_SPLITS");
+    force_s = ev ? std::max(0, atoi(ev)) : 0;
+  }
+  if (force_s > 0 && a.ws && (int64_t)force_s * total <= a.ws_floats / 2) S = force_s;
   // (the direct-to-LDS dQ form: measured faster at head dim 128, slower at 64)
   if (S > 1) {
     if constexpr (DQ2) e = tr ? launch_dq2<HD, true>(a, S, s) : launch_dq<HD, 8, true, false>(a, S, s);
@@ -1484,7 +1490,14 @@ hipError_t launch_bwd(const AttnBwdArgs& a, hipStream_t s, AttnBwdParts* parts) 
   }
   const int64_t kblocks = (int64_t)cdiv(a.n, BQ) * a.H * a.B;
   int P = 1;
-  if (kv.ws && kblocks < 256) {
+  static int force_p = -1;  // TTT_DKV_PARTS (tuning switch): query-range parts of dK/dV
+  if (force_p < 0) {
+    const char* ev = getenv("TTT_DKV_PARTS");
+    force_p = ev ? std::max(0, atoi(ev)) : 0;
+  }
+  if (force_p > 0 && kv.ws && 2LL * force_p * total <= kv.ws_floats) {
+    P = std::min(force_p, (int)cdiv(a.n, KT));
+  } else if (kv.ws && kblocks < 256) {
     double best = 1e30;
     for (int p = 1; p <= std::min(4, (int)cdiv(a.n, KT)); ++p) {
       if (p > 1 && 2LL * p * total > kv.ws_floats) break;
@@ -1496,8 +1509,12 @@ hipError_t launch_bwd(const AttnBwdArgs& a, hipStream_t s, AttnBwdParts* parts) 
     }
   }
   // the direct-to-LDS dK/dV form: head dim 128, transposed tiles, whole 64-query tiles, a head's
-  // arrays and the row's dO within 32-bit byte offsets
+  // arrays and the row's dO within 32-bit byte offsets.  It takes at most two parts: at the 3B
+  // chunk shape (160 key blocks) two parts beat the three that the model above picks, inside the
+  // step (1843 against 1853 ms, same box), where fewer parts also mean fewer fp32 planes
+  // written here and summed by the consumer
   const bool dkv2 = HD == 128 && tr && a.n % KT == 0 && (int64_t)a.n * a.H * HD * 2 < (1LL << 31) && !dkv2_off();
+  if (dkv2 && force_p == 0) P = std::min(P, 2);
   if constexpr (HD == 128) {
     if (dkv2) e = launch_dkv2<HD>(kv, P, s);
   }
