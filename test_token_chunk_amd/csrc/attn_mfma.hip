@@ -463,7 +463,14 @@ int attn_splits(int64_t blocks, int64_t ntiles, int64_t need_per_split, const fl
 int fwd_splits(const AttnArgs& a) {
   const int64_t blocks = (int64_t)cdiv(a.n, 8 * QW) * a.H * a.B;
   const int64_t ntiles = (std::min<int64_t>(a.window, a.pos0 + 1) + 8 * QW) / KT + 1;
-  return attn_splits(blocks, ntiles, (int64_t)a.B * a.H * a.n * (a.hd + 2), a.ws, a.ws_floats);
+  const int64_t need = (int64_t)a.B * a.H * a.n * (a.hd + 2);
+  static int force_s = -1;  // TTT_FWD_SPLITS (tuning switch): key-range parts of a small-grid forward
+  if (force_s < 0) {
+    const char* ev = getenv("TTT_FWD_SPLITS");
+    force_s = ev ? std::max(0, atoi(ev)) : 0;
+  }
+  if (force_s > 0 && a.ws && blocks < 128 && force_s * need <= a.ws_floats) return force_s;
+  return attn_splits(blocks, ntiles, need, a.ws, a.ws_floats);
 }
 
 template <int HD>
