@@ -946,6 +946,15 @@ __global__ __launch_bounds__(256) void k_swa_dkv2(AttnBwdArgs a, int P) {
     if constexpr (KS > 2) { k2 = ld8(kp, 2); k3 = ld8(kp, 3); v2 = ld8(vp, 2); v3 = ld8(vp, 3); }
     if constexpr (KS > 4) { k4 = ld8(kp, 4); k5 = ld8(kp, 5); v4 = ld8(vp, 4); v5 = ld8(vp, 5); }
     if constexpr (KS > 6) { k6 = ld8(kp, 6); k7 = ld8(kp, 7); v6 = ld8(vp, 6); v7 = ld8(vp, 7); }
+    // K pre-multiplied by log2(e)/sqrt(hd) (rounded to bf16): S comes out in log2 units
+    auto sc8 = [&](bf16x8& x) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = (__bf16)((float)x[e] * sl2);
+    };
+    sc8(k0); sc8(k1);
+    if constexpr (KS > 2) { sc8(k2); sc8(k3); }
+    if constexpr (KS > 4) { sc8(k4); sc8(k5); }
+    if constexpr (KS > 6) { sc8(k6); sc8(k7); }
   }
   f32x16 dk[HM], dv[HM];
 #pragma unroll
@@ -1010,7 +1019,17 @@ __global__ __launch_bounds__(256) void k_swa_dkv2(AttnBwdArgs a, int P) {
     // Q^T / dO^T fragments of a half are read before its softmax, which covers their latency.
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
-      f32x16 s0 = f32x16{}, p0 = f32x16{};
+      // S accumulators start at minus the row's log-sum-exp (log2 units) and dP at minus its D, so
+      // P = exp2(S) and dS = P * dP need one operation each
+      f32x16 s0, p0;
+#pragma unroll
+      for (int j4 = 0; j4 < 4; ++j4) {
+        const float4 l4 = *(const float4*)&lse_t[hf * 32 + 8 * j4 + 4 * g];
+        const float4 d4 = *(const float4*)&dd_t[hf * 32 + 8 * j4 + 4 * g];
+        s0[4 * j4] = -LOG2E * l4.x; s0[4 * j4 + 1] = -LOG2E * l4.y;
+        s0[4 * j4 + 2] = -LOG2E * l4.z; s0[4 * j4 + 3] = -LOG2E * l4.w;
+        p0[4 * j4] = -d4.x; p0[4 * j4 + 1] = -d4.y; p0[4 * j4 + 2] = -d4.z; p0[4 * j4 + 3] = -d4.w;
+      }
       const unsigned char* qrow = stg + (hf * 32 + l32) * (HD * 2);
       bf16x8 aq[KS], ao[KS];
 #pragma unroll
@@ -1046,12 +1065,6 @@ __global__ __launch_bounds__(256) void k_swa_dkv2(AttnBwdArgs a, int P) {
           tqf[st][hm] = __builtin_bit_cast(bf16x8, make_uint4(ql.x, ql.y, qh.x, qh.y));
         }
       }
-      float4 l4s[4], d4s[4];
-#pragma unroll
-      for (int j4 = 0; j4 < 4; ++j4) {
-        l4s[j4] = *(const float4*)&lse_t[hf * 32 + 8 * j4 + 4 * g];
-        d4s[j4] = *(const float4*)&dd_t[hf * 32 + 8 * j4 + 4 * g];
-      }
       __builtin_amdgcn_sched_barrier(0);
       // the copies of the next tile go out after the last LDS reads of this one (the other
       // stage was released by the previous tile's closing barrier): an LDS read issued after
@@ -1063,19 +1076,17 @@ __global__ __launch_bounds__(256) void k_swa_dkv2(AttnBwdArgs a, int P) {
       uint32_t pa[8], da[8];
 #pragma unroll
       for (int j4 = 0; j4 < 4; ++j4) {
-        const float4 l4 = l4s[j4], d4 = d4s[j4];
-        const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dvv[4] = {d4.x, d4.y, d4.z, d4.w};
         float pv[4], dsv[4];
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
           const int rr = 4 * j4 + i4;
           const int t = th0 + 8 * j4 + 4 * g + i4;
           // masked scores become -inf, so the exponential gives 0 without a branch
-          float x = fmaf(s0[rr], sl2, -LOG2E * lv[i4]);
+          float x = s0[rr];
           if (!full) x = (kok && t >= sk) ? x : -INFINITY;
           const float p = ex2(x);
           pv[i4] = p;
-          dsv[i4] = p * (p0[rr] - dvv[i4]);
+          dsv[i4] = p * p0[rr];
         }
         pa[2 * j4] = pk2(pv[0], pv[1]);
         pa[2 * j4 + 1] = pk2(pv[2], pv[3]);
