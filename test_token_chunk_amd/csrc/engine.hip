@@ -1355,12 +1355,20 @@ int reset_state(ttt_ctx* c) {
     CK(refresh_shadows(fw.master + 2LL * c->f * c->d, c->d, c->f, c->B, fsz, fw.wd, (int64_t)c->d * c->f, fw.wdT,
                        (int64_t)c->d * c->f, c->bf16, 0, c->stream));
   }
-  const int64_t ring = (int64_t)c->B * c->H * c->R * c->hd * c->es;
-  for (int l = 0; l < c->L; ++l) {
-    CK(hipMemsetAsync(c->lw[l].kr, 0, ring, c->stream));
-    CK(hipMemsetAsync(c->lw[l].vr, 0, ring, c->stream));
-    CK(hipMemsetAsync(c->lw[l].vtr, 0, ring, c->stream));
-    if (c->lw[l].ktr) CK(hipMemsetAsync(c->lw[l].ktr, 0, ring, c->stream));
+  // The key/value rings need no clearing: a query at position t reads only slots of positions
+  // max(0, t - window + 1) .. t, all written by the new sequence before; the other slots of a
+  // 64-key tile are masked to probability 0, which needs only that they hold finite values, as
+  // the previous sequence leaves them (they are zero from creation).  After a failure (the context
+  // was poisoned: a non-finite value may sit in a ring), or when the last asynchronous call was
+  // never checked by ttt_sync, they are cleared.
+  if (c->poisoned || c->pending_loss) {
+    const int64_t ring = (int64_t)c->B * c->H * c->R * c->hd * c->es;
+    for (int l = 0; l < c->L; ++l) {
+      CK(hipMemsetAsync(c->lw[l].kr, 0, ring, c->stream));
+      CK(hipMemsetAsync(c->lw[l].vr, 0, ring, c->stream));
+      CK(hipMemsetAsync(c->lw[l].vtr, 0, ring, c->stream));
+      if (c->lw[l].ktr) CK(hipMemsetAsync(c->lw[l].ktr, 0, ring, c->stream));
+    }
   }
   CK(hipMemsetAsync(c->err_dev, 0, 4, c->stream));
   CK(hipStreamSynchronize(c->stream));
