@@ -219,7 +219,9 @@ int ttt_load_state(ttt_ctx* ctx, const void* src, int64_t nbytes);
 
 /* Start a new text (page "TTT-E2E 如何让大模型边用边学", §4.2: every new text
  * starts from the trained initial weights): fast weights back to their initial
- * values, window cleared, pos = 0, poisoning cleared.  Synchronous. */
+ * values, window emptied (pos = 0: no earlier key is visible to the new text; the
+ * ring memory is zeroed only after a failure or an unchecked ttt_prefill_device, since
+ * the new text reads only slots it writes itself), poisoning cleared.  Synchronous. */
 int ttt_reset(ttt_ctx* ctx);
 
 /* Current absolute position of every row (rows advance together). */
