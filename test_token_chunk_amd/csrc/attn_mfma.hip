@@ -901,10 +901,11 @@ __global__ __launch_bounds__(256) void k_swa_dkv(AttnBwdArgs a, int P) {
 
 // dK/dV with the query tiles copied straight from global memory into LDS (buffer loads to
 // LDS, two stages, no staging registers, no per-row bounds tests): the Q and dO tiles
-// [64 queries][hd] with the 16-byte chunks of a row XOR-swizzled by row % (hd/8), the
+// [64 queries][hd] with the 16-byte chunks of a row XOR-swizzled (by row % 16 at hd 128, by
+// (row / 2) % 8 at hd 64), the
 // transposed Q^T and dO^T tiles [hd][64 queries] swizzled by (row / 2) % 8, and the tile's
 // 64 log-sum-exp and D values.  Otherwise as k_swa_dkv (TR form): every query tile of the
-// chunk is whole (n % 64 == 0), head dim 128, 32-bit byte offsets within a head's arrays.
+// chunk is whole (n % 64 == 0), head dim 128 or 64, 32-bit byte offsets within a head's arrays.
 template <int HD>
 constexpr int dkv2_stage_bytes() { return 4 * KT * HD * 2 + 2 * 1024; }
 
@@ -918,7 +919,11 @@ __global__ __launch_bounds__(256) void k_swa_dkv2(AttnBwdArgs a, int P) {
   constexpr int SB = dkv2_stage_bytes<HD>();
   constexpr int OOFF = KT * HD * 2, QTOFF = 2 * KT * HD * 2, OTOFF = 3 * KT * HD * 2;
   constexpr int LOFF = 4 * KT * HD * 2, DOFF = LOFF + 1024;
-  static_assert(TB % 4 == 0 && CPR == 16 && KT == 64, "tile copy layout");
+  static_assert(TB % 4 == 0 && (CPR == 16 || CPR == 8) && KT == 64, "tile copy layout");
+  // 16-byte chunk swizzle of a Q / dO row: by row % 16 for 256-byte rows; by (row / 2) % 8 for
+  // 128-byte rows (two rows share the 64 banks), so the 16 rows a quarter-wave reads hit
+  // distinct banks
+  auto qswz = [](int row) { return CPR == 16 ? row % 16 : (row >> 1) & 7; };
   extern __shared__ __align__(16) unsigned char smem_raw[];
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: LDS addresses stay scalar
@@ -982,7 +987,7 @@ __global__ __launch_bounds__(256) void k_swa_dkv2(AttnBwdArgs a, int P) {
 #pragma unroll
   for (int u = 0; u < TBW; ++u) {
     const int j = wid * TBW + u;
-    const int row = j * RPK + lane / CPR, c = (lane % CPR) ^ (row % CPR);
+    const int row = j * RPK + lane / CPR, c = (lane % CPR) ^ qswz(row);
     oq[u] = (row * HD + c * 8) * 2;
     oo[u] = (row * d + c * 8) * 2;
     const int trow = j * 8 + (lane >> 3), tc = (lane & 7) ^ ((trow >> 1) & 7);
@@ -1004,7 +1009,7 @@ __global__ __launch_bounds__(256) void k_swa_dkv2(AttnBwdArgs a, int P) {
       buf_lds16(rd, base + DOFF, ol, t0 * 4);
     }
   };
-  const int xr = l32 % CPR, xt = (l32 >> 1) & 7;
+  const int xr = qswz(l32), xt = (l32 >> 1) & 7;  // (rows hf * 32 + l32 keep the swizzle of l32)
   if (tbeg < tstop) issue(tbeg, 0);
   WAIT_VM_LDS(0);
   __syncthreads();
@@ -1526,14 +1531,15 @@ hipError_t launch_bwd(const AttnBwdArgs& a, hipStream_t s, AttnBwdParts* parts) 
       }
     }
   }
-  // the direct-to-LDS dK/dV form: head dim 128, transposed tiles, whole 64-query tiles, a head's
+  // the direct-to-LDS dK/dV form: head dim 128 or 64, transposed tiles, whole 64-query tiles, a head's
   // arrays and the row's dO within 32-bit byte offsets.  It takes at most two parts: at the 3B
   // chunk shape (160 key blocks) two parts beat the three that the model above picks, inside the
   // step (1843 against 1853 ms, same box), where fewer parts also mean fewer fp32 planes
   // written here and summed by the consumer
-  const bool dkv2 = HD == 128 && tr && a.n % KT == 0 && (int64_t)a.n * a.H * HD * 2 < (1LL << 31) && !dkv2_off();
+  const bool dkv2 = (HD == 128 || HD == 64) && tr && a.n % KT == 0 && (int64_t)a.n * a.H * HD * 2 < (1LL << 31) &&
+                    !dkv2_off();
   if (dkv2 && force_p == 0) P = std::min(P, 2);
-  if constexpr (HD == 128) {
+  if constexpr (HD == 128 || HD == 64) {
     if (dkv2) e = launch_dkv2<HD>(kv, P, s);
   }
   if (!dkv2) e = tr ? launch_dkv<HD, true>(kv, P, s) : launch_dkv<HD, false>(kv, P, s);

@@ -214,7 +214,8 @@ def ref_attention_bwd(q, kr, vr, dO, pos0, window):
                                                     (2, 3, 96, 136, 300, 4000, 440),
                                                     # whole 64-query tiles at head dim 128 (the direct-to-LDS dK/dV
                                                     # form): a half-empty last key block, and two rows of 3 heads
-                                                    (1, 2, 128, 192, 512, 3000, 704), (2, 3, 128, 256, 1024, 5000, 1280)])
+                                                    (1, 2, 128, 192, 512, 3000, 704), (2, 3, 128, 256, 1024, 5000, 1280),
+                                                    (1, 2, 64, 192, 512, 3000, 704), (2, 3, 64, 128, 300, 4000, 448)])
 def test_swa_bwd_matches_fp64(dtype, B, H, hd, n, window, pos0, R, use_ws, tr):
     """tr: the transposed key ring and a dO^T scratch are passed (16-byte tile copies when n % 8 == 0)."""
     torch = _torch()
