@@ -43,7 +43,8 @@ PROFILE_KERNELS = {  # class: (kernels, one kernel per launch)
     "gemm_splitk": ("k_gemm_wide<128, 0, true> + k_splitk_reduce4<0>", False),
     "swa_fwd": ("k_swa_fwd<hd, 8, false>", True),
     "swa_fwd_split": ("k_swa_fwd<hd, 8, true> + k_swa_combine", False),
-    "swa_bwd": ("k_swa_dq2<hd, *> (k_dvec + k_swa_dq<hd, 8, *> off hd 128) + k_swa_dkv<hd, *>; split parts "
+    "swa_bwd": ("k_swa_dq2<hd, *> (k_dvec + k_swa_dq<hd, 8, *> off hd 128) + k_swa_dkv3<hd> (k_swa_dkv<hd, *> off "
+                "hd 128 / 64 with whole 64-query tiles); split parts "
                 "are summed by k_rope_bwd_pack4 outside the class", False),
     "swa_decode": ("k_swa_decode<hd>", True),
     "gemm_qkv_rope": ("k_gemm_wide<256|128, 6, false> (q|k|v product, RoPE and ring writes in the epilogue; "

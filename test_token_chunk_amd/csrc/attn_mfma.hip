@@ -899,73 +899,74 @@ __global__ __launch_bounds__(256) void k_swa_dkv(AttnBwdArgs a, int P) {
   }
 }
 
-// dK/dV with the query tiles copied straight from global memory into LDS (buffer loads to
-// LDS, two stages, no staging registers, no per-row bounds tests): the Q and dO tiles
-// [64 queries][hd] with the 16-byte chunks of a row XOR-swizzled (by row % 16 at hd 128, by
-// (row / 2) % 8 at hd 64), the
-// transposed Q^T and dO^T tiles [hd][64 queries] swizzled by (row / 2) % 8, and the tile's
-// 64 log-sum-exp and D values.  Otherwise as k_swa_dkv (TR form): every query tile of the
-// chunk is whole (n % 64 == 0), head dim 128 or 64, 32-bit byte offsets within a head's arrays.
+// One stage of the direct-to-LDS dK/dV kernel below: the Q and dO tiles [64 queries][hd] (the
+// 16-byte chunks of a row XOR-swizzled by row % 16 at hd 128, by (row / 2) % 8 at hd 64), the
+// transposed Q^T and dO^T tiles [hd][64 queries] (chunks swizzled by (row / 2) % 8), and the tile's
+// 64 log-sum-exp and D values (1 KB each).
 template <int HD>
 constexpr int dkv2_stage_bytes() { return 4 * KT * HD * 2 + 2 * 1024; }
 
+// dK/dV for the chunk's own keys with the query tiles copied straight from global memory into
+// LDS (buffer loads to LDS, two stages, per-lane offsets precomputed, no per-row bounds tests:
+// every query tile of the chunk is whole, n % 64 == 0; head dim 128 or 64; 32-bit byte offsets
+// within a head's arrays), 16 keys per wave on the 16 x 16 x 32 matrix instructions: 8 waves
+// (two per SIMD at hd 128) cover the 128 keys of a block, and the two waves of a SIMD hide each
+// other's latencies (a 32-key wave needs about 400 registers, one wave per SIMD).  The fragments
+// of a phase are read in one group before its MFMAs, and the next tile's copies go out after the
+// tile's last LDS read.  Otherwise as k_swa_dkv (TR form).  In
+// the 16 x 16 x 32 product a lane supplies row (or column) l % 16 and k indices 8 (l / 16) .. +7,
+// and holds rows 4 (l / 16) .. +3 of column l % 16 of the result; P and dS feed the dV and dK
+// products from registers with the k index over the 32 queries of a half-tile permuted so that
+// k slot e of lane group G is query 16 (e / 4) + 4 G + e % 4 -- the rows the lane holds.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
 template <int HD>
-__global__ __launch_bounds__(256) void k_swa_dkv2(AttnBwdArgs a, int P) {
-  constexpr int KS = HD / 16, HM = HD / 32;
-  constexpr int CPR = HD / 8;             // 16-byte chunks per Q / dO row
-  constexpr int RPK = 1024 / (HD * 2);    // Q / dO rows per 1 KB copy
-  constexpr int TB = KT * HD * 2 / 1024;  // 1 KB copies per tile (each of the four)
-  constexpr int TBW = TB / 4;             // per wave
+__global__ __launch_bounds__(512) void k_swa_dkv3(AttnBwdArgs a, int P) {
+  constexpr int NWV = 8, KW = 16;          // waves, keys per wave
+  constexpr int KS = HD / 32, HB = HD / 16;
+  constexpr int CPR = HD / 8;
+  constexpr int RPK = 1024 / (HD * 2);
+  constexpr int TB = KT * HD * 2 / 1024;
+  constexpr int TBW = TB / NWV;
   constexpr int SB = dkv2_stage_bytes<HD>();
   constexpr int OOFF = KT * HD * 2, QTOFF = 2 * KT * HD * 2, OTOFF = 3 * KT * HD * 2;
   constexpr int LOFF = 4 * KT * HD * 2, DOFF = LOFF + 1024;
-  static_assert(TB % 4 == 0 && (CPR == 16 || CPR == 8) && KT == 64, "tile copy layout");
-  // 16-byte chunk swizzle of a Q / dO row: by row % 16 for 256-byte rows; by (row / 2) % 8 for
-  // 128-byte rows (two rows share the 64 banks), so the 16 rows a quarter-wave reads hit
-  // distinct banks
+  static_assert(TB % NWV == 0 && (CPR == 16 || CPR == 8) && KT == 64 && NWV * KW == BQ, "tile copy layout");
   auto qswz = [](int row) { return CPR == 16 ? row % 16 : (row >> 1) & 7; };
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
-  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: LDS addresses stay scalar
+  const int tid = threadIdx.x, lane = tid & 63, G = lane >> 4, l16 = lane & 15;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int b = blockIdx.z, h = blockIdx.x, part = blockIdx.y % P;
   const int64_t bh = (int64_t)b * a.H + h;
   const int R = a.R, d = a.H * HD, n = a.n;
   const int s0blk = (blockIdx.y / P) * BQ;
-  const int sk = s0blk + wid * QW + l32;  // this lane's key (chunk-local)
+  const int sk = s0blk + wid * KW + l16;  // this lane's key (chunk-local)
   const bool kok = sk < n;
-  const int wsk_hi = s0blk + wid * QW + QW - 1;
+  const int wsk_hi = s0blk + wid * KW + KW - 1;
   const bool wkok = wsk_hi < n;
   const float LOG2E = 1.4426950408889634f;
   const float sl2 = LOG2E / sqrtf((float)HD);
 
-  bf16x8 k0, k1, k2, k3, k4, k5, k6, k7, v0, v1, v2, v3, v4, v5, v6, v7;
+  // K (pre-multiplied by log2(e)/sqrt(hd)) and V fragments of this lane's key: head dims
+  // 32 ks + 8 G .. +7
+  bf16x8 kf[KS], vf[KS];
   {
     const int slot = (int)((a.pos0 + (kok ? sk : 0)) % R);
-    const bf16* kp = (const bf16*)a.kr + (bh * R + slot) * HD + g * 8;
-    const bf16* vp = (const bf16*)a.vr + (bh * R + slot) * HD + g * 8;
-    auto ld8 = [&](const bf16* p, int ks) {
-      uint4 v = kok ? *(const uint4*)(p + ks * 16) : make_uint4(0, 0, 0, 0);
-      return __builtin_bit_cast(bf16x8, v);
-    };
-    k0 = ld8(kp, 0); k1 = ld8(kp, 1); v0 = ld8(vp, 0); v1 = ld8(vp, 1);
-    if constexpr (KS > 2) { k2 = ld8(kp, 2); k3 = ld8(kp, 3); v2 = ld8(vp, 2); v3 = ld8(vp, 3); }
-    if constexpr (KS > 4) { k4 = ld8(kp, 4); k5 = ld8(kp, 5); v4 = ld8(vp, 4); v5 = ld8(vp, 5); }
-    if constexpr (KS > 6) { k6 = ld8(kp, 6); k7 = ld8(kp, 7); v6 = ld8(vp, 6); v7 = ld8(vp, 7); }
-    // K pre-multiplied by log2(e)/sqrt(hd) (rounded to bf16): S comes out in log2 units
-    auto sc8 = [&](bf16x8& x) {
+    const bf16* kp = (const bf16*)a.kr + (bh * R + slot) * HD + G * 8;
+    const bf16* vp = (const bf16*)a.vr + (bh * R + slot) * HD + G * 8;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = (__bf16)((float)x[e] * sl2);
-    };
-    sc8(k0); sc8(k1);
-    if constexpr (KS > 2) { sc8(k2); sc8(k3); }
-    if constexpr (KS > 4) { sc8(k4); sc8(k5); }
-    if constexpr (KS > 6) { sc8(k6); sc8(k7); }
+    for (int ks = 0; ks < KS; ++ks) {
+      kf[ks] = __builtin_bit_cast(bf16x8, kok ? *(const uint4*)(kp + ks * 32) : make_uint4(0, 0, 0, 0));
+      vf[ks] = __builtin_bit_cast(bf16x8, kok ? *(const uint4*)(vp + ks * 32) : make_uint4(0, 0, 0, 0));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) kf[ks][e] = (__bf16)((float)kf[ks][e] * sl2);
+    }
   }
-  f32x16 dk[HM], dv[HM];
+  f32x4 dk[HB], dv[HB];
 #pragma unroll
-  for (int i = 0; i < HM; ++i) {
-    dk[i] = f32x16{};
-    dv[i] = f32x16{};
+  for (int i = 0; i < HB; ++i) {
+    dk[i] = f32x4{};
+    dv[i] = f32x4{};
   }
   const int tfirst = (s0blk / KT) * KT;
   const int ntq = (n - tfirst + KT - 1) / KT;
@@ -973,9 +974,6 @@ __global__ __launch_bounds__(256) void k_swa_dkv2(AttnBwdArgs a, int P) {
   const int tbeg = tfirst + part * per * KT;
   const int tstop = min(n, tfirst + (part + 1) * per * KT);
 
-  // the head's Q, Q^T, dO^T, lse and D and the row's dO are buffers (32-bit byte offsets,
-  // checked at launch); each lane keeps the byte offsets of its rows and chunks, a query tile
-  // moves only the scalar offset
   const __amdgpu_buffer_rsrc_t rq = buf_rsrc((const bf16*)a.q + bh * n * HD, (uint32_t)(n * HD * 2));
   const __amdgpu_buffer_rsrc_t rqt = buf_rsrc((const bf16*)a.qt + bh * HD * n, (uint32_t)(n * HD * 2));
   const __amdgpu_buffer_rsrc_t rot = buf_rsrc((const bf16*)a.dot + bh * HD * n, (uint32_t)(n * HD * 2));
@@ -993,7 +991,7 @@ __global__ __launch_bounds__(256) void k_swa_dkv2(AttnBwdArgs a, int P) {
     const int trow = j * 8 + (lane >> 3), tc = (lane & 7) ^ ((trow >> 1) & 7);
     ot[u] = (trow * n + tc * 8) * 2;
   }
-  const int ol = (lane & 15) * 16;  // lanes 16..63 copy the same 256 bytes again
+  const int ol = (lane & 15) * 16;
   auto issue = [&](int t0, int st) {
     unsigned char* base = smem_raw + st * SB;
 #pragma unroll
@@ -1009,7 +1007,7 @@ __global__ __launch_bounds__(256) void k_swa_dkv2(AttnBwdArgs a, int P) {
       buf_lds16(rd, base + DOFF, ol, t0 * 4);
     }
   };
-  const int xr = qswz(l32), xt = (l32 >> 1) & 7;  // (rows hf * 32 + l32 keep the swizzle of l32)
+  const int xr = qswz(l16), xt = (l16 >> 1) & 7;  // (rows r * 16 + l16 keep the swizzle of l16)
   if (tbeg < tstop) issue(tbeg, 0);
   WAIT_VM_LDS(0);
   __syncthreads();
@@ -1019,128 +1017,120 @@ __global__ __launch_bounds__(256) void k_swa_dkv2(AttnBwdArgs a, int P) {
     const unsigned char* stg = smem_raw + cur * SB;
     const float* lse_t = reinterpret_cast<const float*>(stg + LOFF);
     const float* dd_t = reinterpret_cast<const float*>(stg + DOFF);
-    // With one wave per SIMD nothing hides an LDS read that an MFMA waits for, so each phase
-    // reads all its fragments first (one LDS latency per phase instead of one per MFMA); the
-    // Q^T / dO^T fragments of a half are read before its softmax, which covers their latency.
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
-      // S accumulators start at minus the row's log-sum-exp (log2 units) and dP at minus its D, so
-      // P = exp2(S) and dS = P * dP need one operation each
-      f32x16 s0, p0;
+      // S and dP of the half-tile's two 16-query row blocks, started at minus the row's
+      // log-sum-exp (log2 units) and minus its D
+      f32x4 sc[2], pc[2];
 #pragma unroll
-      for (int j4 = 0; j4 < 4; ++j4) {
-        const float4 l4 = *(const float4*)&lse_t[hf * 32 + 8 * j4 + 4 * g];
-        const float4 d4 = *(const float4*)&dd_t[hf * 32 + 8 * j4 + 4 * g];
-        s0[4 * j4] = -LOG2E * l4.x; s0[4 * j4 + 1] = -LOG2E * l4.y;
-        s0[4 * j4 + 2] = -LOG2E * l4.z; s0[4 * j4 + 3] = -LOG2E * l4.w;
-        p0[4 * j4] = -d4.x; p0[4 * j4 + 1] = -d4.y; p0[4 * j4 + 2] = -d4.z; p0[4 * j4 + 3] = -d4.w;
+      for (int rb = 0; rb < 2; ++rb) {
+        const float4 l4 = *(const float4*)&lse_t[hf * 32 + rb * 16 + 4 * G];
+        const float4 d4 = *(const float4*)&dd_t[hf * 32 + rb * 16 + 4 * G];
+        sc[rb] = f32x4{-LOG2E * l4.x, -LOG2E * l4.y, -LOG2E * l4.z, -LOG2E * l4.w};
+        pc[rb] = f32x4{-d4.x, -d4.y, -d4.z, -d4.w};
       }
-      const unsigned char* qrow = stg + (hf * 32 + l32) * (HD * 2);
-      bf16x8 aq[KS], ao[KS];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const int co = (((2 * ks + g) ^ xr) << 4);
-        aq[ks] = *(const bf16x8*)(qrow + co);
-        ao[ks] = *(const bf16x8*)(qrow + OOFF + co);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#define SSTEP(ks, kv, vv)                                                               \
-  if constexpr (KS > ks) {                                                              \
-    s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[ks], kv, s0, 0, 0, 0);              \
-    p0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao[ks], vv, p0, 0, 0, 0);              \
-  }
-      SSTEP(0, k0, v0) SSTEP(1, k1, v1) SSTEP(2, k2, v2) SSTEP(3, k3, v3)
-      SSTEP(4, k4, v4) SSTEP(5, k5, v5) SSTEP(6, k6, v6) SSTEP(7, k7, v7)
-#undef SSTEP
-      __builtin_amdgcn_sched_barrier(0);
-      // Q^T / dO^T fragments of this half (k index = the permuted queries, see k_swa_dkv)
-      bf16x8 tqf[2][HM], tof[2][HM];
+      for (int rb = 0; rb < 2; ++rb) {
+        const unsigned char* qrow = stg + (hf * 32 + rb * 16 + l16) * (HD * 2);
+        bf16x8 aq[KS], ao[KS];
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        const int ch = hf * 4 + st * 2;  // 16-byte chunk of queries hf*32 + st*16 .. +7
+        for (int ks = 0; ks < KS; ++ks) {
+          const int co = (((4 * ks + G) ^ xr) << 4);
+          aq[ks] = *(const bf16x8*)(qrow + co);
+          ao[ks] = *(const bf16x8*)(qrow + OOFF + co);
+        }
 #pragma unroll
-        for (int hm = 0; hm < HM; ++hm) {
-          const unsigned char* trow = stg + QTOFF + (hm * 32 + l32) * (KT * 2) + 8 * g;
-          const unsigned char* orow = stg + OTOFF + (hm * 32 + l32) * (KT * 2) + 8 * g;
-          const uint2 ql = *(const uint2*)(trow + ((ch ^ xt) << 4));
-          const uint2 qh = *(const uint2*)(trow + (((ch + 1) ^ xt) << 4));
-          const uint2 olo = *(const uint2*)(orow + ((ch ^ xt) << 4));
-          const uint2 ohi = *(const uint2*)(orow + (((ch + 1) ^ xt) << 4));
-          tof[st][hm] = __builtin_bit_cast(bf16x8, make_uint4(olo.x, olo.y, ohi.x, ohi.y));
-          tqf[st][hm] = __builtin_bit_cast(bf16x8, make_uint4(ql.x, ql.y, qh.x, qh.y));
+        for (int ks = 0; ks < KS; ++ks) {
+          sc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[ks], kf[ks], sc[rb], 0, 0, 0);
+          pc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ao[ks], vf[ks], pc[rb], 0, 0, 0);
         }
       }
-      __builtin_amdgcn_sched_barrier(0);
-      // the copies of the next tile go out after the last LDS reads of this one (the other
-      // stage was released by the previous tile's closing barrier): an LDS read issued after
-      // them would wait for them
-      if (hf == 1 && tq0 + KT < tstop) issue(tq0 + KT, cur ^ 1);
-      // rows = queries tq0 + 32 hf + 8 j + 4 g + i; visible iff sk <= t (window >= n here)
+      // rows = queries tq0 + 32 hf + 16 rb + 4 G + i; visible iff sk <= t (window >= n here)
       const int th0 = tq0 + hf * 32;
       const bool full = wkok && th0 >= wsk_hi;
-      uint32_t pa[8], da[8];
+      uint32_t pa[4], da[4];
 #pragma unroll
-      for (int j4 = 0; j4 < 4; ++j4) {
+      for (int rb = 0; rb < 2; ++rb) {
         float pv[4], dsv[4];
 #pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const int rr = 4 * j4 + i4;
-          const int t = th0 + 8 * j4 + 4 * g + i4;
-          // masked scores become -inf, so the exponential gives 0 without a branch
-          float x = s0[rr];
+        for (int i = 0; i < 4; ++i) {
+          const int t = th0 + rb * 16 + 4 * G + i;
+          float x = sc[rb][i];
           if (!full) x = (kok && t >= sk) ? x : -INFINITY;
-          const float p = ex2(x);
-          pv[i4] = p;
-          dsv[i4] = p * p0[rr];
+          const float pp = ex2(x);
+          pv[i] = pp;
+          dsv[i] = pp * pc[rb][i];
         }
-        pa[2 * j4] = pk2(pv[0], pv[1]);
-        pa[2 * j4 + 1] = pk2(pv[2], pv[3]);
-        da[2 * j4] = pk2(dsv[0], dsv[1]);
-        da[2 * j4 + 1] = pk2(dsv[2], dsv[3]);
+        pa[2 * rb] = pk2(pv[0], pv[1]);
+        pa[2 * rb + 1] = pk2(pv[2], pv[3]);
+        da[2 * rb] = pk2(dsv[0], dsv[1]);
+        da[2 * rb + 1] = pk2(dsv[2], dsv[3]);
       }
-      const bf16x8 pf0 = __builtin_bit_cast(bf16x8, make_uint4(pa[0], pa[1], pa[2], pa[3]));
-      const bf16x8 pf1 = __builtin_bit_cast(bf16x8, make_uint4(pa[4], pa[5], pa[6], pa[7]));
-      const bf16x8 df0 = __builtin_bit_cast(bf16x8, make_uint4(da[0], da[1], da[2], da[3]));
-      const bf16x8 df1 = __builtin_bit_cast(bf16x8, make_uint4(da[4], da[5], da[6], da[7]));
+      const bf16x8 pf = __builtin_bit_cast(bf16x8, make_uint4(pa[0], pa[1], pa[2], pa[3]));
+      const bf16x8 df = __builtin_bit_cast(bf16x8, make_uint4(da[0], da[1], da[2], da[3]));
+      // dV^T += dO^T P, dK^T += Q^T dS over the half's 32 queries: the A fragments are queries
+      // 32 hf + 4 G .. +3 and 32 hf + 16 + 4 G .. +3 of head-dim row 16 hb + l16
+      const int c0 = hf * 4 + (G >> 1), c1 = c0 + 2, bo = 8 * (G & 1);
 #pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int hm = 0; hm < HM; ++hm) {
-          dv[hm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tof[st][hm], st ? pf1 : pf0, dv[hm], 0, 0, 0);
-          dk[hm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tqf[st][hm], st ? df1 : df0, dk[hm], 0, 0, 0);
-        }
+      for (int hb = 0; hb < HB; ++hb) {
+        const unsigned char* trow = stg + QTOFF + (hb * 16 + l16) * (KT * 2) + bo;
+        const unsigned char* orow = stg + OTOFF + (hb * 16 + l16) * (KT * 2) + bo;
+        const uint2 ql = *(const uint2*)(trow + ((c0 ^ xt) << 4));
+        const uint2 qh = *(const uint2*)(trow + ((c1 ^ xt) << 4));
+        const uint2 olo = *(const uint2*)(orow + ((c0 ^ xt) << 4));
+        const uint2 ohi = *(const uint2*)(orow + ((c1 ^ xt) << 4));
+        const bf16x8 ofr = __builtin_bit_cast(bf16x8, make_uint4(olo.x, olo.y, ohi.x, ohi.y));
+        const bf16x8 qfr = __builtin_bit_cast(bf16x8, make_uint4(ql.x, ql.y, qh.x, qh.y));
+        dv[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ofr, pf, dv[hb], 0, 0, 0);
+        dk[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qfr, df, dk[hb], 0, 0, 0);
+      }
+      // the next tile's copies go out after this tile's last LDS reads (an LDS read issued
+      // after them would wait for them)
+      __builtin_amdgcn_sched_barrier(0);
+      if (hf == 1 && tq0 + KT < tstop) issue(tq0 + KT, cur ^ 1);
     }
     WAIT_VM_LDS(0);
     __syncthreads();  // the next tile is in LDS; every wave is done with this one
   }
-  // dK (scaled) and then dV of the block's keys leave through LDS as whole rows of HD floats
-  // (keys past the chunk end hold zeros and are not written)
-  const float sc = 1.f / sqrtf((float)HD);
+  // dK (scaled) and then dV leave through LDS as whole rows of HD floats: the lane holds head
+  // dims 16 hb + 4 G .. +3 of key wid * 16 + l16
+  const float scl = 1.f / sqrtf((float)HD);
   const int64_t plane = (int64_t)a.B * n * d;
   constexpr int SLD = HD + 4;
   static_assert(BQ * SLD * 4 <= 2 * SB, "staged dK / dV rows fit");
   float* stf = reinterpret_cast<float*>(smem_raw);
-  const int kr = wid * QW + l32;
+  const int kr = wid * KW + l16;
 #pragma unroll
   for (int which = 0; which < 2; ++which) {
-    if (which > 0) __syncthreads();  // the dK rows have left LDS
+    if (which > 0) __syncthreads();
 #pragma unroll
-    for (int hm = 0; hm < HM; ++hm)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int d0 = hm * 32 + 8 * j + 4 * g;
-        *(float4*)(stf + kr * SLD + d0) =
-            which == 0 ? make_float4(dk[hm][4 * j] * sc, dk[hm][4 * j + 1] * sc, dk[hm][4 * j + 2] * sc, dk[hm][4 * j + 3] * sc)
-                       : make_float4(dv[hm][4 * j], dv[hm][4 * j + 1], dv[hm][4 * j + 2], dv[hm][4 * j + 3]);
-      }
+    for (int hb = 0; hb < HB; ++hb) {
+      const f32x4 v = which == 0 ? dk[hb] * scl : dv[hb];
+      *(float4*)(stf + kr * SLD + hb * 16 + 4 * G) = make_float4(v[0], v[1], v[2], v[3]);
+    }
     __syncthreads();
     float* base = (P > 1 ? a.ws + (which * P + part) * plane : (which ? a.dv : a.dk)) + ((int64_t)b * n + s0blk) * d +
                   (int64_t)h * HD;
-    for (int c = tid; c < BQ * (HD / 4); c += 256) {
+    for (int c = tid; c < BQ * (HD / 4); c += NWV * 64) {
       const int r = c / (HD / 4), c4 = (c % (HD / 4)) * 4;
       if (s0blk + r < n) *(float4*)(base + (int64_t)r * d + c4) = *(const float4*)(stf + r * SLD + c4);
     }
   }
+}
+
+template <int HD>
+hipError_t launch_dkv3(const AttnBwdArgs& a, int P, hipStream_t s) {
+  static bool attr = false;
+  if (!attr) {
+    hipError_t e = hipFuncSetAttribute((const void*)k_swa_dkv3<HD>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       2 * dkv2_stage_bytes<HD>());
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  if ((int64_t)cdiv(a.n, BQ) * P > 65535) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((k_swa_dkv3<HD>), dim3(a.H, cdiv(a.n, BQ) * P, a.B), dim3(512), 2 * dkv2_stage_bytes<HD>(), s,
+                     a, P);
+  return hipGetLastError();
 }
 
 template <typename Smem, typename K>
@@ -1436,7 +1426,7 @@ hipError_t launch_dkv(const AttnBwdArgs& a, int P, hipStream_t s) {
   return hipGetLastError();
 }
 
-// TTT_NO_DKV2=1 (tuning switch): the register-staged dK/dV kernel everywhere
+// TTT_NO_DKV2=1 (tuning switch): the register-staged dK/dV kernel everywhere (not the direct-to-LDS one)
 bool dkv2_off() {
   static int off = -1;
   if (off < 0) {
@@ -1444,21 +1434,6 @@ bool dkv2_off() {
     off = e && atoi(e) ? 1 : 0;
   }
   return off == 1;
-}
-
-template <int HD>
-hipError_t launch_dkv2(const AttnBwdArgs& a, int P, hipStream_t s) {
-  static bool attr = false;
-  if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void*)k_swa_dkv2<HD>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       2 * dkv2_stage_bytes<HD>());
-    if (e != hipSuccess) return e;
-    attr = true;
-  }
-  if ((int64_t)cdiv(a.n, BQ) * P > 65535) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((k_swa_dkv2<HD>), dim3(a.H, cdiv(a.n, BQ) * P, a.B), dim3(256), 2 * dkv2_stage_bytes<HD>(), s,
-                     a, P);
-  return hipGetLastError();
 }
 
 template <int HD>
@@ -1534,13 +1509,13 @@ hipError_t launch_bwd(const AttnBwdArgs& a, hipStream_t s, AttnBwdParts* parts) 
   // the direct-to-LDS dK/dV form: head dim 128 or 64, transposed tiles, whole 64-query tiles, a head's
   // arrays and the row's dO within 32-bit byte offsets.  It takes at most two parts: at the 3B
   // chunk shape (160 key blocks) two parts beat the three that the model above picks, inside the
-  // step (1843 against 1853 ms, same box), where fewer parts also mean fewer fp32 planes
-  // written here and summed by the consumer
+  // step (1828 against 1837 ms, same box; one part 1828), where fewer parts also mean fewer fp32
+  // planes written here and summed by the consumer
   const bool dkv2 = (HD == 128 || HD == 64) && tr && a.n % KT == 0 && (int64_t)a.n * a.H * HD * 2 < (1LL << 31) &&
                     !dkv2_off();
   if (dkv2 && force_p == 0) P = std::min(P, 2);
   if constexpr (HD == 128 || HD == 64) {
-    if (dkv2) e = launch_dkv2<HD>(kv, P, s);
+    if (dkv2) e = launch_dkv3<HD>(kv, P, s);
   }
   if (!dkv2) e = tr ? launch_dkv<HD, true>(kv, P, s) : launch_dkv<HD, false>(kv, P, s);
   if (e != hipSuccess) return e;
