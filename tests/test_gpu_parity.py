@@ -258,6 +258,25 @@ def test_chunk_calls_equal_sequence_call_and_reset():
     np.testing.assert_array_equal(la, lc)
 
 
+def test_reset_after_another_text_equals_fresh_context():
+    """ttt_reset keeps the key/value ring memory (a new text reads only slots it writes itself;
+    the masked slots of a 64-key tile only need finite values): a context that read another
+    text first and was reset repeats a fresh context bit for bit.  bf16 matrix-core path, a
+    ragged last chunk (tiles that reach past the text's end) and a window over several tiles."""
+    c = mkcfg(**dict(MID, window=512))
+    w = synth.weights(_shape(c), bf16=True)
+    other = synth.tokens(1, MID_T + 1, c.vocab, "zipf", seed=11)
+    seq = synth.tokens(1, 601, c.vocab, "zipf", seed=12)
+    a = _ctx(c, w, MID_T)
+    a.prefill_seq(other)
+    a.reset()
+    la = a.prefill_seq(seq)
+    b = _ctx(c, w, MID_T)
+    lb = b.prefill_seq(seq)
+    np.testing.assert_array_equal(la, lb)
+    assert np.array_equal(a.fast_weights_flat(), b.fast_weights_flat())
+
+
 def test_device_entry_point_matches_host_entry_point():
     import torch
     c = mkcfg(**dict(TOY, n_fast=2))
