@@ -455,35 +455,52 @@ __global__ void k_reduce_loss(const float* loss_tok, const int* nvalid, int n, f
 }
 
 // arg-max of each row, lowest index on ties; written to out[b*ld_out] and out2[b*ld_out2] (if given)
-__global__ void k_argmax(const float* logits, int V, int32_t* out, int64_t ld_out, int32_t* out2, int64_t ld_out2) {
-  __shared__ float sv[1024];
-  __shared__ int si[1024];
-  int b = blockIdx.x;
+// arg-max of each logits row (ties to the lowest id; NaNs are never taken): 16-byte loads, each
+// thread keeping its running best in id order, then a shuffle reduction per wave and one across
+// the block's waves
+__device__ __forceinline__ void argmax_merge(float& bv, int& bi, float x, int i) {
+  if (x > bv || (x == bv && i < bi)) {
+    bv = x;
+    bi = i;
+  }
+}
+
+__global__ __launch_bounds__(1024) void k_argmax(const float* logits, int V, int32_t* out, int64_t ld_out,
+                                                 int32_t* out2, int64_t ld_out2) {
+  __shared__ float sv[16];
+  __shared__ int si[16];
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, nw = blockDim.x >> 6;
   const float* z = logits + (int64_t)b * V;
   float bv = -INFINITY;
   int bi = 0x7fffffff;
-  for (int v = threadIdx.x; v < V; v += blockDim.x) {
-    float x = z[v];
-    if (x > bv || (x == bv && v < bi)) { bv = x; bi = v; }
-  }
-  sv[threadIdx.x] = bv;
-  si[threadIdx.x] = bi;
-  __syncthreads();
-  for (int o = blockDim.x / 2; o > 0; o >>= 1) {
-    if (threadIdx.x < o) {
-      float x = sv[threadIdx.x + o];
-      int i = si[threadIdx.x + o];
-      if (x > sv[threadIdx.x] || (x == sv[threadIdx.x] && i < si[threadIdx.x])) {
-        sv[threadIdx.x] = x;
-        si[threadIdx.x] = i;
-      }
+  if (V % 4 == 0 && ((uintptr_t)z & 15) == 0) {
+    for (int v = 4 * tid; v < V; v += 4 * blockDim.x) {
+      const float4 x = *(const float4*)(z + v);
+      argmax_merge(bv, bi, x.x, v);
+      argmax_merge(bv, bi, x.y, v + 1);
+      argmax_merge(bv, bi, x.z, v + 2);
+      argmax_merge(bv, bi, x.w, v + 3);
     }
-    __syncthreads();
+  } else {
+    for (int v = tid; v < V; v += blockDim.x) argmax_merge(bv, bi, z[v], v);
   }
-  if (threadIdx.x == 0) {
-    int r = si[0] == 0x7fffffff ? 0 : si[0];
-    out[b * ld_out] = r;
-    if (out2) out2[b * ld_out2] = r;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) argmax_merge(bv, bi, __shfl_xor(bv, o, 64), __shfl_xor(bi, o, 64));
+  if (lane == 0) {
+    sv[wid] = bv;
+    si[wid] = bi;
+  }
+  __syncthreads();
+  if (wid == 0) {
+    bv = lane < nw ? sv[lane] : -INFINITY;
+    bi = lane < nw ? si[lane] : 0x7fffffff;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) argmax_merge(bv, bi, __shfl_xor(bv, o, 64), __shfl_xor(bi, o, 64));
+    if (lane == 0) {
+      const int r = bi == 0x7fffffff ? 0 : bi;
+      out[b * ld_out] = r;
+      if (out2) out2[b * ld_out2] = r;
+    }
   }
 }
 
