@@ -82,7 +82,7 @@ __global__ __launch_bounds__(64 * gemv_waves<NRM>()) void k_gemv(GemmArgs g, int
   constexpr int RW = SW ? 2 * NR : NR;  // weight rows per wave
   static_assert(!RP || NR == 2, "a RoPE wave holds the two rows of one rotation pair");
   constexpr int U = MR <= 2 ? 4 : 2;    // 512-element steps per trip
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wid = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const int64_t wv = (int64_t)blockIdx.x * GW + wid;
   const int64_t j0 = RP ? wv : wv * NR;
   // (NRM: every wave takes part in staging the rows and reaches the barrier after it)
@@ -134,23 +134,66 @@ __global__ __launch_bounds__(64 * gemv_waves<NRM>()) void k_gemv(GemmArgs g, int
   extern __shared__ uint4 xs[];
   __shared__ float red[GW][MR];
   float rstd[MR];
+  // weight pieces of one trip (U steps of 512 elements from k0) as buffer loads over the wave's
+  // rows (K elements each): pieces past K read as zero without a branch, so the loads of a trip
+  // are one uninterrupted group
+  __amdgpu_buffer_rsrc_t wrs[RW];
+#pragma unroll
+  for (int r = 0; r < RW; ++r) wrs[r] = buf_rsrc(wr[r], (uint32_t)K * 2u);
+  auto load_w = [&](int k0, uint4 (&wv)[U][RW]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+      for (int r = 0; r < RW; ++r) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(wrs[r], (k0 + 512 * u) * 2, 0, 0);
+        wv[u][r] = make_uint4(v[0], v[1], v[2], v[3]);
+      }
+    }
+  };
+  uint4 wfirst[U][RW];
   if constexpr (NRM) {
     const float* X = g.nx + bz * (int64_t)M * g.ldnx;
     float ssl[MR];
 #pragma unroll
     for (int m = 0; m < MR; ++m) ssl[m] = 0.f;
-    for (int k = 8 * (int)threadIdx.x; k < K; k += 8 * 64 * GW) {
-      const float4 g0 = *(const float4*)(g.ng + k), g1 = *(const float4*)(g.ng + k + 4);
+    auto stage = [&](int k, const float4& g0, const float4& g1, const float4 (&x0)[MR], const float4 (&x1)[MR]) {
 #pragma unroll
       for (int m = 0; m < MR; ++m) {
         if (m >= M) break;
-        const float* xr = X + (int64_t)m * g.ldnx + k;
-        const float4 x0 = *(const float4*)xr, x1 = *(const float4*)(xr + 4);
-        ssl[m] += (x0.x * x0.x + x0.y * x0.y) + (x0.z * x0.z + x0.w * x0.w) + (x1.x * x1.x + x1.y * x1.y) +
-                  (x1.z * x1.z + x1.w * x1.w);
-        xs[m * (K / 8) + k / 8] = make_uint4(bf16pair(x0.x * g0.x, x0.y * g0.y), bf16pair(x0.z * g0.z, x0.w * g0.w),
-                                             bf16pair(x1.x * g1.x, x1.y * g1.y), bf16pair(x1.z * g1.z, x1.w * g1.w));
+        ssl[m] += (x0[m].x * x0[m].x + x0[m].y * x0[m].y) + (x0[m].z * x0[m].z + x0[m].w * x0[m].w) +
+                  (x1[m].x * x1[m].x + x1[m].y * x1[m].y) + (x1[m].z * x1[m].z + x1[m].w * x1[m].w);
+        xs[m * (K / 8) + k / 8] =
+            make_uint4(bf16pair(x0[m].x * g0.x, x0[m].y * g0.y), bf16pair(x0[m].z * g0.z, x0[m].w * g0.w),
+                       bf16pair(x1[m].x * g1.x, x1[m].y * g1.y), bf16pair(x1[m].z * g1.z, x1[m].w * g1.w));
       }
+    };
+    auto load_x = [&](int k, float4& g0, float4& g1, float4 (&x0)[MR], float4 (&x1)[MR]) {
+      g0 = *(const float4*)(g.ng + k);
+      g1 = *(const float4*)(g.ng + k + 4);
+#pragma unroll
+      for (int m = 0; m < MR; ++m) {
+        const float* xr = X + (int64_t)(m < M ? m : M - 1) * g.ldnx + k;
+        x0[m] = *(const float4*)xr;
+        x1[m] = *(const float4*)(xr + 4);
+      }
+    };
+    // The first trip's weight pieces do not depend on the rows: they are requested right after
+    // this thread's first piece of the rows and arrive while the block stages them (one memory
+    // round trip before the dot products instead of two).  An idle wave's row pointers are
+    // valid (clamped), so every wave issues them.
+    const int kst = 8 * (int)threadIdx.x;
+    {
+      float4 g0, g1, x0[MR], x1[MR];
+      if (kst < K) load_x(kst, g0, g1, x0, x1);
+      __builtin_amdgcn_sched_barrier(0);
+      load_w(8 * lane, wfirst);
+      __builtin_amdgcn_sched_barrier(0);
+      if (kst < K) stage(kst, g0, g1, x0, x1);
+    }
+    for (int k = kst + 8 * 64 * GW; k < K; k += 8 * 64 * GW) {
+      float4 g0, g1, x0[MR], x1[MR];
+      load_x(k, g0, g1, x0, x1);
+      stage(k, g0, g1, x0, x1);
     }
 #pragma unroll
     for (int m = 0; m < MR; ++m) {
@@ -167,14 +210,11 @@ __global__ __launch_bounds__(64 * gemv_waves<NRM>()) void k_gemv(GemmArgs g, int
     }
     if (!active) return;
   }
-  for (int k0 = 8 * lane; k0 < K; k0 += 512 * U) {
-    uint4 wv[U][RW], xv[U][MR];
+  auto trip = [&](int k0, const uint4 (&wv)[U][RW]) {
+    uint4 xv[U][MR];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int k = k0 + 512 * u;
-      // rows m >= M repeat row M - 1 (their sums are not stored); pieces past K add zero
-#pragma unroll
-      for (int r = 0; r < RW; ++r) wv[u][r] = k < K ? *(const uint4*)(wr[r] + k) : make_uint4(0u, 0u, 0u, 0u);
       if constexpr (NRM) {
 #pragma unroll
         for (int m = 0; m < MR; ++m)
@@ -191,6 +231,16 @@ __global__ __launch_bounds__(64 * gemv_waves<NRM>()) void k_gemv(GemmArgs g, int
       for (int r = 0; r < RW; ++r)
 #pragma unroll
         for (int m = 0; m < MR; ++m) acc[r][m] = dot8(wv[u][r], xv[u][m], acc[r][m]);
+  };
+  int k0 = 8 * lane;
+  if constexpr (NRM) {
+    if (k0 < K) trip(k0, wfirst);
+    k0 += 512 * U;
+  }
+  for (; k0 < K; k0 += 512 * U) {
+    uint4 wv[U][RW];
+    load_w(k0, wv);
+    trip(k0, wv);
   }
 #pragma unroll
   for (int r = 0; r < RW; ++r)
