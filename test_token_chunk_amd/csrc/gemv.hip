@@ -81,7 +81,9 @@ __global__ __launch_bounds__(64 * gemv_waves<NRM>()) void k_gemv(GemmArgs g, int
   constexpr bool RP = KIND == EPI_QKV_ROPE;  // NR == 2: the pair (i, i + hd/2); ncols = pairs
   constexpr int RW = SW ? 2 * NR : NR;  // weight rows per wave
   static_assert(!RP || NR == 2, "a RoPE wave holds the two rows of one rotation pair");
-  constexpr int U = MR <= 2 ? 4 : 2;    // 512-element steps per trip
+  // 512-element steps per trip: 8 where the wave reads one or two weight rows (the loads in
+  // flight are what keeps HBM busy), 4 for more rows, 2 for more input rows
+  constexpr int U = MR > 2 ? 2 : RW <= 2 ? 8 : 4;
   const int lane = threadIdx.x & 63, wid = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const int64_t wv = (int64_t)blockIdx.x * GW + wid;
   const int64_t j0 = RP ? wv : wv * NR;
