@@ -320,8 +320,9 @@ hipError_t gemv_cols(const GemmArgs& g, hipStream_t s) {
   const bool sw = KIND == EPI_SWIGLU || KIND == EPI_SWIGLU_IL;
   const int ncols = KIND == EPI_SWIGLU_IL ? g.N / 2 : g.N;
   const int f = sw ? ncols : 0;
-  // columns per wave: enough waves to fill the chip, more loads in flight per wave for wide outputs
-  const int nr = g.M > 2 ? 1 : (ncols >= 16384 ? 4 : (ncols >= 4096 ? 2 : 1));
+  // columns per wave: enough waves to fill the chip, more loads in flight per wave for wide outputs;
+  // a SwiGLU column is already two weight rows, and one of them per wave takes the deeper trips
+  const int nr = g.M > 2 || (sw && g.M == 1) ? 1 : (ncols >= 16384 ? 4 : (ncols >= 4096 ? 2 : 1));
   if (g.M == 1) {
     if (nr == 4) return launch_gemv<1, 4, KIND>(g, ncols, f, s);
     if (nr == 2) return launch_gemv<1, 2, KIND>(g, ncols, f, s);
