@@ -32,7 +32,8 @@ int tttk_gemm(int dtype, const void* A, int64_t lda, const void* B, int64_t ldb,
  * keys t-window < s <= t, s >= 0, key s at ring slot s mod R.
  * q [B][H][n][hd] (rotated), kr, vr [B][H][R][hd], vtr [B][H][hd][R] (V
  * transposed), o [B*n][H*hd], lse [B][H][n] fp32 (natural log) or NULL.
- * Scale 1/sqrt(hd). */
+ * Scale 1/sqrt(hd).  Every ring slot must hold finite values: slots next to
+ * a query's window are read with the tile and weighted by exactly zero. */
 int tttk_swa_fwd(int dtype, const void* q, const void* kr, const void* vr, const void* vtr, void* o, float* lse,
                  int32_t B, int32_t H, int32_t hd, int32_t n, int32_t R, int32_t window, int64_t pos0, float* ws,
                  int64_t ws_floats, void* stream);

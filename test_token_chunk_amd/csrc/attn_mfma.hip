@@ -1592,10 +1592,14 @@ __global__ __launch_bounds__(256) void k_swa_decode(AttnArgs a, int S) {
     const int kk = i * KPR + sub;
     int slot = s0 + kk;
     if (slot >= a.R) slot -= a.R;
-    const bool ok = wlo + kk < bhi;
-    kv[i] = ok ? *(const uint4*)(Kb + (int64_t)slot * HD) : make_uint4(0u, 0u, 0u, 0u);
-    vv[i] = ok ? *(const uint4*)(Vb + (int64_t)slot * HD) : make_uint4(0u, 0u, 0u, 0u);
+    // every slot is a valid ring row, so the loads are unconditional (a branch per load, with
+    // zeros on the other path, made the wave wait for the loads in flight before issuing the
+    // next); keys past the block are left out of the maximum and get weight 0, which needs only
+    // that their slots hold finite values
+    kv[i] = *(const uint4*)(Kb + (int64_t)slot * HD);
+    vv[i] = *(const uint4*)(Vb + (int64_t)slot * HD);
   }
+  __builtin_amdgcn_sched_barrier(0);  // all of the wave's loads go out before its first product
   float sc[ROUNDS];
   float mx = -INFINITY;
 #pragma unroll
