@@ -1688,15 +1688,19 @@ __global__ __launch_bounds__(256) void k_swa_dec_combine(AttnArgs a, int S) {
     for (int u = 0; u < 4; ++u) {
       const int sp = base + u * PS;
       const int64_t row = (int64_t)(sp < S ? sp : 0) * plane + bh;
-      pmv[u] = sp < S ? pm[row] : -INFINITY;
+      // an absent part reads part 0 and gets maximum -inf (its weight is 0); written as an add so
+      // the load stays unconditional (a select made it a branch that serialized the load groups)
+      pmv[u] = pm[row] + (sp < S ? 0.f : -INFINITY);
       plv[u] = pl[row];
       xa[u] = *(const float4*)(a.ws + row * HD + dg * 8);
       xb[u] = *(const float4*)(a.ws + row * HD + dg * 8 + 4);
     }
+    __builtin_amdgcn_sched_barrier(0);  // the group's loads all go out before the first wait
     float mn = mt;
 #pragma unroll
     for (int u = 0; u < 4; ++u) mn = fmaxf(mn, pmv[u]);
-    if (mn == -INFINITY) continue;
+    // (no early exit when every maximum is -inf: then nothing was accumulated, the scale and the
+    // weights are 0 and the sums stay 0, and all loads of the group stay unconditional)
     const float sc = mt == -INFINITY ? 0.f : exp2f((mt - mn) * sl2);
     lt *= sc;
 #pragma unroll
